@@ -1,0 +1,354 @@
+"""Oracle draft -> verify -> accept loop, greedy autoregressive decoding.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+What it follows:
+  * CLaSp article, section 三 (three stages): the draft runs the model with
+    some intermediate layers skipped and produces candidate tokens; the full
+    model checks all of them in one forward pass; at the first rejected draft
+    token the full model's own prediction replaces it and drafting restarts
+    from there.  Section 一: autoregressive decoding emits one token per full
+    forward (the baseline).
+  * CAS-Spec blog, section 2.1: layer sparsity and early exit (an early exit
+    after layer e is the same as skipping layers e..L-1), 8-bit dynamic
+    activation quantization; section 2.2: several draft levels in one window.
+  * CLaSp article, section 四: a draft exit threshold (readings below).
+
+Readings where the pages are silent (each listed in the design doc):
+  * greedy decoding, argmax ties to the lowest index;
+  * a skipped layer is the identity on the residual stream and writes no KV;
+  * draft rows attend to the committed prefix plus those window positions
+    whose KV this layer wrote during drafting (per-layer valid bits);
+  * verify rows are [t0, d1..dk] at positions p..p+k, row i predicts d_{i+1},
+    row k yields the bonus token; verify overwrites the window's KV;
+  * the exit threshold compares the draft's top-1 softmax probability with
+    tau; the low-confidence token is kept, then drafting stops;
+  * the quantized draft quantizes the inputs of all seven projections of an
+    executed layer (q/k/v share one input), never the LM head.
+
+Every decode row goes through ``forward_row`` one row at a time, so verify
+row i and the autoregressive step at the same position are the same
+computation; only the prompt prefill runs as a block.
+
+Pins (tests/test_oracle_decode.py): greedy prefix property, incremental
+decode equal to full recompute, speculative output equal to greedy output
+for every policy, accepted length in [0, k], forced wrong drafts, empty-mask
+drafts accepted in full, all-skipped draft closed form.
+"""
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .model import rms_norm, rope, silu, attend, fake_quant, argmax_first
+
+WINDOW_MAX = 32
+
+
+class DecodeState:
+    """KV cache and committed length of one sequence."""
+
+    def __init__(self, model, max_seq):
+        L, Hkv, hd = model.L, model.Hkv, model.hd
+        self.max_seq = max_seq
+        self.k = np.zeros((L, max_seq, Hkv, hd), model.dt)
+        self.v = np.zeros((L, max_seq, Hkv, hd), model.dt)
+        self.p = 0                 # committed length (KV rows [0, p) are final)
+        self.t0 = None             # pending token, input of the row at position p
+        self.window = []           # drafted tokens d1..dk (positions p+1..p+k as inputs)
+        self.valid = [0] * L       # per layer: bit j set = KV at p+j written by a draft
+        self.target_states = None  # full states H*[0..L] of the last accepted token
+        self.target_pos = None     # its position t*
+
+
+def _project(W, x):
+    return W @ x
+
+
+def layer_row(model, l, h, pos, st, mode, quant=False):
+    """One decoder layer on one residual row ``h`` at position ``pos``.
+
+    mode "full":  writes its k, v at ``pos``; attends to cache rows [0, pos].
+    mode "draft": writes its k, v at ``pos`` (a window slot) and sets the
+                  layer's valid bit; attends to [0, p) plus valid window slots.
+    mode "dp":    writes nothing; attends to [0, pos) plus its own k, v.
+    """
+    m = model
+    lw = m.layer(l)
+    dt = m.dt
+    x = rms_norm(h, lw["attn_norm"], m.eps)
+    if quant:
+        x = fake_quant(x, dt)
+    q = _project(lw["wq"], x).reshape(m.Hq, m.hd)
+    k = _project(lw["wk"], x).reshape(m.Hkv, m.hd)
+    v = _project(lw["wv"], x).reshape(m.Hkv, m.hd)
+    q = rope(q, pos, m.theta)
+    k = rope(k, pos, m.theta)
+    if mode == "full":
+        st.k[l, pos], st.v[l, pos] = k, v
+        keys, vals = st.k[l, :pos + 1], st.v[l, :pos + 1]
+    elif mode == "draft":
+        st.k[l, pos], st.v[l, pos] = k, v
+        slot = pos - st.p
+        assert 0 <= slot < WINDOW_MAX
+        st.valid[l] |= 1 << slot
+        idx = list(range(st.p)) + [st.p + j for j in range(WINDOW_MAX) if (st.valid[l] >> j) & 1]
+        keys, vals = st.k[l, idx], st.v[l, idx]
+    elif mode == "dp":
+        keys = np.concatenate([st.k[l, :pos], k[None]], axis=0)
+        vals = np.concatenate([st.v[l, :pos], v[None]], axis=0)
+    else:
+        raise ValueError(mode)
+    group = m.Hq // m.Hkv
+    o = np.concatenate([attend(q[hh], keys[:, hh // group], vals[:, hh // group])
+                        for hh in range(m.Hq)])
+    if quant:
+        o = fake_quant(o, dt)
+    h = h + _project(lw["wo"], o)
+    x = rms_norm(h, lw["ffn_norm"], m.eps)
+    if quant:
+        x = fake_quant(x, dt)
+    a = silu(_project(lw["w_gate"], x)) * _project(lw["w_up"], x)
+    if quant:
+        a = fake_quant(a, dt)
+    return h + _project(lw["w_down"], a)
+
+
+def forward_row(model, st, tok, pos, mode, skip=None, quant=False):
+    """Embed ``tok`` and run every layer not in ``skip``; returns (logits, states).
+
+    ``states[0]`` is the embedding, ``states[l+1]`` the residual after layer l
+    (a skipped layer repeats its input).
+    """
+    h = model.embed_row(tok)
+    states = [h]
+    for l in range(model.L):
+        if skip is None or not skip[l]:
+            h = layer_row(model, l, h, pos, st, mode, quant)
+        states.append(h)
+    return model.head(h), states
+
+
+def prefill(model, tokens, max_seq):
+    """Causal full-model pass over the prompt, as one block of rows.
+
+    Returns (state, logits of the last row, states of the last row).  The
+    pending token t0 is the argmax of the last row; the last prompt row is the
+    first layer-selection target (its own KV stays committed at P-1).
+    """
+    m = model
+    tokens = np.asarray(tokens)
+    P = len(tokens)
+    assert 1 <= P <= max_seq
+    st = DecodeState(m, max_seq)
+    H = np.stack([m.embed_row(t) for t in tokens])
+    last_states = [H[-1].copy()]
+    pos = np.arange(P)
+    group = m.Hq // m.Hkv
+    causal = pos[None, :] <= pos[:, None]
+    for l in range(m.L):
+        lw = m.layer(l)
+        X = np.stack([rms_norm(h, lw["attn_norm"], m.eps) for h in H])
+        Q = (X @ lw["wq"].T).reshape(P, m.Hq, m.hd)
+        K = (X @ lw["wk"].T).reshape(P, m.Hkv, m.hd)
+        Vv = (X @ lw["wv"].T).reshape(P, m.Hkv, m.hd)
+        Q = np.stack([rope(Q[t], t, m.theta) for t in range(P)])
+        K = np.stack([rope(K[t], t, m.theta) for t in range(P)])
+        st.k[l, :P], st.v[l, :P] = K, Vv
+        O = np.empty((P, m.Hq, m.hd), m.dt)
+        for hh in range(m.Hq):
+            kh = hh // group
+            S = (Q[:, hh] @ K[:, kh].T) / np.sqrt(m.hd)
+            S = np.where(causal, S, -np.inf)
+            S = S - S.max(axis=1, keepdims=True)
+            Pm = np.exp(S)
+            Pm = Pm / Pm.sum(axis=1, keepdims=True)
+            O[:, hh] = Pm @ Vv[:, kh]
+        H = H + O.reshape(P, -1) @ lw["wo"].T
+        X = np.stack([rms_norm(h, lw["ffn_norm"], m.eps) for h in H])
+        A = silu(X @ lw["w_gate"].T) * (X @ lw["w_up"].T)
+        H = H + A @ lw["w_down"].T
+        last_states.append(H[-1].copy())
+    z = m.head(H[-1])
+    st.p = P
+    st.t0 = argmax_first(z)
+    st.target_states = last_states
+    st.target_pos = P - 1
+    return st, z, last_states
+
+
+def draft(model, st, skip, quant, k, tau=0.0):
+    """Draft up to ``k`` tokens into the window with a skip mask.
+
+    Returns (tokens drafted by this call, top-1 probabilities).  Appends to
+    any tokens already in the window (several draft levels may share one
+    window).  With ``tau > 0`` drafting stops after the first token whose
+    top-1 softmax probability is below ``tau``.
+    """
+    out, pmax = [], []
+    for _ in range(k):
+        if len(st.window) >= WINDOW_MAX - 1:
+            break
+        tok = st.t0 if not st.window else st.window[-1]
+        pos = st.p + len(st.window)
+        z, _ = forward_row(model, st, tok, pos, "draft", skip, quant)
+        d = argmax_first(z)
+        st.window.append(d)
+        out.append(d)
+        zs = z - np.max(z)
+        pm = 1.0 / float(np.sum(np.exp(zs)))
+        pmax.append(pm)
+        if tau > 0 and pm < tau:
+            break
+    return out, pmax
+
+
+def verify(model, st, drafts=None):
+    """Full model over rows [t0, d1..dk] at positions p..p+k, row by row.
+
+    ``drafts`` overrides the window (a host-forced draft).  Returns (logits
+    [k+1][V], states [k+1][L+1][d], the draft tokens verified).
+    """
+    d = list(st.window if drafts is None else drafts)
+    rows = [st.t0] + d
+    logits, states = [], []
+    for i, tok in enumerate(rows):
+        z, s = forward_row(model, st, tok, st.p + i, "full")
+        logits.append(z)
+        states.append(s)
+    return np.stack(logits), states, d
+
+
+def accept(st, logits, states, drafts):
+    """Greedy acceptance and rollback.
+
+    a_i = argmax of verify row i; n = length of the longest prefix of the
+    drafts that equals a_0..a_{n-1}; bonus = a_n.  The committed length moves
+    to p + n + 1 (rows past it are stale and never read); the window is
+    cleared; row n becomes the next layer-selection target.
+    Returns (n, bonus, emitted tokens d_1..d_n + [bonus]).
+    """
+    k = len(drafts)
+    a = [argmax_first(z) for z in logits]
+    n = 0
+    while n < k and a[n] == drafts[n]:
+        n += 1
+    bonus = a[n]
+    emitted = list(drafts[:n]) + [bonus]
+    st.target_states = states[n]
+    st.target_pos = st.p + n
+    st.p = st.p + n + 1
+    st.t0 = bonus
+    st.window = []
+    st.valid = [0] * len(st.valid)
+    return n, bonus, emitted
+
+
+def ar_generate(model, prompt, G, max_seq=None):
+    """Greedy autoregressive decoding: G tokens (t0 included)."""
+    max_seq = max_seq or len(prompt) + G + 1
+    st, z, _ = prefill(model, prompt, max_seq)
+    out = [st.t0]
+    while len(out) < G:
+        zz, s = forward_row(model, st, st.t0, st.p, "full")
+        st.target_states, st.target_pos = s, st.p
+        st.p += 1
+        st.t0 = argmax_first(zz)
+        out.append(st.t0)
+    return out
+
+
+@dataclass
+class Policy:
+    """Draft policy of one speculative run.
+
+    skip: static skip set (layer indices); dp_skip: number of layers the
+    CLaSp DP chooses (overrides ``skip``), re-run every ``interval`` verify
+    rounds; tau: draft exit threshold (0 = off); cascade: a list of levels
+    ``[(n_skip_by_dp, exit_layers, quant)]`` ordered fast -> precise, routed
+    by the DyTC heuristics with at most ``K`` drafts per round.
+    """
+    K: int = 4
+    skip: tuple = ()
+    dp_skip: int = None
+    interval: int = 32
+    tau: float = 0.0
+    quant: bool = False
+    cascade: list = None
+    latency_beta: tuple = (1.0, 0.0, 1.0)
+    forced_drafts: dict = field(default_factory=dict)
+
+
+def _mask_from_set(L, s):
+    m = [0] * L
+    for l in s:
+        m[l] = 1
+    return m
+
+
+def speculative_generate(model, prompt, G, policy, max_seq=None, log=None):
+    """Self-speculative greedy decoding of G tokens (t0 included).
+
+    Returns (tokens, per-round records).  The DP (if any) runs once after the
+    prefill and again after every ``interval``-th verify round.
+    """
+    from .clasp import clasp_dp
+    from .dytc import A_INIT, plan_cascade, update_cascade, predict_latency
+    L = model.L
+    max_seq = max_seq or len(prompt) + G + WINDOW_MAX + 1
+    st, _, _ = prefill(model, prompt, max_seq)
+    out = [st.t0]
+    records = []
+
+    def select_masks():
+        if policy.cascade is not None:
+            ms = []
+            for n_skip, exit_layers, _q in policy.cascade:
+                le = L - exit_layers
+                mask, _, _ = clasp_dp(model, st, n_skip - exit_layers, n_layers=le)
+                ms.append(mask)
+            return ms
+        if policy.dp_skip is not None:
+            return [clasp_dp(model, st, policy.dp_skip)[0]]
+        return [_mask_from_set(L, policy.skip)]
+
+    masks = select_masks()
+    a = [A_INIT] * (len(policy.cascade) if policy.cascade else 0)
+    rounds = 0
+    while len(out) < G:
+        budget = G - len(out) - 1
+        if policy.cascade is not None:
+            depth = [L - sum(mk) for mk in masks]
+            t_hat = [predict_latency(policy.latency_beta, st.p, dp) for dp in depth]
+            t_ver = predict_latency(policy.latency_beta, st.p, L)
+            plan = plan_cascade(a, t_hat, t_ver, policy.K)
+            steps = []          # window order: most precise level first
+            for lev in reversed(range(len(masks))):
+                kk = min(plan[lev], budget - sum(s[2] for s in steps))
+                steps.append((lev, masks[lev], kk))
+            drafted_levels = []
+            for lev, mk, kk in steps:
+                toks, _ = draft(model, st, mk, policy.cascade[lev][2], kk, 0.0)
+                drafted_levels += [lev] * len(toks)
+        else:
+            kk = min(policy.K, budget)
+            if rounds in policy.forced_drafts:
+                d = list(policy.forced_drafts[rounds])[:kk]
+                st.window = d
+            else:
+                draft(model, st, masks[0], policy.quant, kk, policy.tau)
+            drafted_levels = None
+        logits, states, d = verify(model, st)
+        n, bonus, emitted = accept(st, logits, states, d)
+        out += emitted
+        rounds += 1
+        rec = {"k": len(d), "n": n, "bonus": bonus}
+        if drafted_levels is not None:
+            a = update_cascade(a, drafted_levels, n)
+            rec["levels"] = drafted_levels
+            rec["a"] = list(a)
+        records.append(rec)
+        if (policy.dp_skip is not None or policy.cascade is not None) and rounds % policy.interval == 0:
+            masks = select_masks()
+        if log is not None:
+            log.append(rec)
+    return out[:G], records

@@ -1,0 +1,133 @@
+"""Oracle decoder forward (Llama-style), one layer at a time.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+What it follows:
+  * The target model is a LLaMA-family decoder (CLaSp article, section 四:
+    LLaMA3 series; CAS-Spec blog, section 2.1: Llama-2 7B).  The pages give no
+    layer equations, so the standard Llama block is written out: pre-RMSNorm,
+    rotary position embedding (rotate-half pairing), grouped-query softmax
+    attention, residual add, pre-RMSNorm, SwiGLU FFN, residual add; final
+    RMSNorm and an untied LM head.
+  * Dynamic 8-bit activation quantization (CAS-Spec blog, section 2.1, item 3;
+    CAS-Spec abstract: "activation quantization"): symmetric per-token int8.
+
+Pins (tests/test_oracle_model.py): an independent float64 torch re-expression
+(``scaled_dot_product_attention``, complex-multiply RoPE); closed forms (RoPE at
+position 0 is the identity and preserves norms, a single key returns its
+value, equal scores average the values, zeroed output projections make a layer
+the identity, all-skipped gives head(norm(embedding))); hand-computed int8
+codes in tests/golden; incremental decode equals full recompute.
+"""
+import numpy as np
+
+
+class OracleModel:
+    """Weights (exact float32 values) viewed in the oracle's dtype.
+
+    ``weights``: mapping name -> float32 ndarray, canonical names
+    (``embed``, ``final_norm``, ``lm_head``, ``layers.{l}.{wq,...}``).
+    ``shape``: an object with the model-shape fields (n_layers, d_model, ...).
+    """
+
+    def __init__(self, shape, weights, dtype=np.float64, cache_layers=None):
+        self.shape = shape
+        self.w = weights
+        self.dt = np.dtype(dtype)
+        self.L = shape.n_layers
+        self.d = shape.d_model
+        self.Hq = shape.n_heads
+        self.Hkv = shape.n_kv_heads
+        self.hd = shape.head_dim
+        self.V = shape.vocab
+        self.eps = shape.rms_eps
+        self.theta = shape.rope_theta
+        if cache_layers is None:
+            cache_layers = shape.total_params() * self.dt.itemsize < 2e9
+        self._cache = {} if cache_layers else None
+
+    def _get(self, name):
+        if self._cache is not None and name in self._cache:
+            return self._cache[name]
+        a = np.asarray(self.w[name]).astype(self.dt)
+        if self._cache is not None:
+            self._cache[name] = a
+        return a
+
+    def layer(self, l):
+        names = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+        return {n: self._get(f"layers.{l}.{n}") for n in names}
+
+    def embed_row(self, tok):
+        return np.asarray(self.w["embed"][int(tok)]).astype(self.dt)
+
+    def head(self, h):
+        """Final RMSNorm + LM head of one residual row -> logits [V]."""
+        x = rms_norm(h, self._get("final_norm"), self.eps)
+        return self._get("lm_head") @ x
+
+    def head_rows(self, H):
+        X = np.stack([rms_norm(h, self._get("final_norm"), self.eps) for h in H])
+        return X @ self._get("lm_head").T
+
+
+def rms_norm(h, g, eps):
+    """x = h / sqrt(mean(h^2) + eps) * g  (one row)."""
+    return h / np.sqrt(np.mean(h * h) + eps) * g
+
+
+def rope(x, pos, theta):
+    """Rotate-half rotary embedding of ``x`` [n_heads][hd] at position ``pos``.
+
+    Pair (i, i + hd/2) is rotated by angle pos * theta^(-2i/hd); the angles are
+    formed in float64 whatever the oracle dtype.
+    """
+    hd = x.shape[-1]
+    half = hd // 2
+    i = np.arange(half, dtype=np.float64)
+    ang = float(pos) * np.power(float(theta), -2.0 * i / hd)
+    c = np.cos(ang).astype(x.dtype)
+    s = np.sin(ang).astype(x.dtype)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def attend(q, keys, vals):
+    """Softmax attention of one query [hd] over keys/vals [n][hd]."""
+    s = (keys @ q) / np.sqrt(q.shape[-1])
+    s = s - np.max(s)
+    p = np.exp(s)
+    p = p / np.sum(p)
+    return p @ vals
+
+
+def quantize_row(x):
+    """Dynamic symmetric per-token int8 quantization of one activation row.
+
+    amax = max|x|; q = clamp(rint(x * (127 / amax)), -127, 127); scale = amax/127.
+    Every decision is taken in float32 (127/amax is one correctly rounded
+    float32 division; rint rounds half to even).  amax == 0 gives q = 0 and
+    scale 0.  Returns (int8 codes, float32 scale).
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(x32.shape, np.int8), np.float32(0)
+    inv = np.float32(127.0) / amax
+    q = np.clip(np.rint(x32 * inv), -127, 127).astype(np.int8)
+    return q, np.float32(amax / np.float32(127.0))
+
+
+def fake_quant(x, dt):
+    """The value the draft uses for a quantized input: scale * code."""
+    q, s = quantize_row(x)
+    return q.astype(dt) * dt.type(s)
+
+
+def argmax_first(z):
+    """Index of the maximum; the lowest index wins ties."""
+    return int(np.argmax(z))

@@ -1,0 +1,86 @@
+"""Pins of the oracle's DyTC router (CPU only).
+
+CAS-Spec blog, section 3.1 (EMA with alpha = 0.2), section 3.2 (latency
+model), section 4.1 (initial acceptance); CAS-Spec abstract (routing and
+draft-length assignment from acceptance and latency heuristics).
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import dytc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_ema_golden():
+    a = oracle.A_INIT
+    assert a == 0.65
+    with open(os.path.join(GOLDEN, "ema.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            r, want = (float(t) for t in line.split(";"))
+            a = oracle.ema_update(a, r)
+            assert a == pytest.approx(want, abs=1e-15)
+
+
+def test_ema_closed_form():
+    # constant rate r: a_n = r + 0.8^n (a_0 - r)
+    for r in (0.0, 0.3, 1.0):
+        a = 0.65
+        for n in range(1, 30):
+            a = oracle.ema_update(a, r)
+            assert a == pytest.approx(r + 0.8 ** n * (0.65 - r), abs=1e-12)
+
+
+def test_zero_acceptance_gives_empty_plan():
+    assert oracle.plan_cascade([0.0, 0.0, 0.0], [1.0, 2.0, 3.0], 5.0, 8) == [0, 0, 0]
+
+
+def test_free_certain_drafts_fill_the_window_with_precise_level():
+    # a = 1 everywhere and zero draft cost: score = (K + 1) / t_verify, ties on the
+    # total broken toward the most precise level
+    assert oracle.plan_cascade([1.0, 1.0, 1.0], [0.0, 0.0, 0.0], 1.0, 8) == [0, 0, 8]
+
+
+def test_single_level_matches_geometric_series():
+    """One usable level (others certain to fail): expected accepted length of k
+    drafts at rate a is the geometric sum a (1 - a^k) / (1 - a)."""
+    for a, t, tv in [(0.5, 0.3, 1.0), (0.8, 0.5, 1.0), (0.95, 0.1, 1.0), (0.3, 0.6, 1.0)]:
+        best_k = max(range(9), key=lambda k: ((a * (1 - a ** k) / (1 - a)) + 1) / (tv + k * t))
+        plan = oracle.plan_cascade([0.0, a, 0.0], [9.0, t, 9.0], tv, 8)
+        assert plan == [0, best_k, 0]
+
+
+def test_plan_total_bounded_and_enumerates_165_options():
+    n = sum(1 for p in itertools.product(range(9), repeat=3) if sum(p) <= 8)
+    assert n == 165
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        a = list(rng.uniform(0, 1, 3))
+        t = list(rng.uniform(0.1, 1, 3))
+        plan = oracle.plan_cascade(a, t, 2.0, 8)
+        assert sum(plan) <= 8 and min(plan) >= 0
+
+
+def test_update_counts_reached_slots():
+    # window [L3, L3, L2, L1], n = 1: L3 slot 1 accepted, L3 slot 2 reached and rejected
+    a = oracle.update_cascade([0.5, 0.5, 0.5], [2, 2, 1, 0], 1)
+    assert a[2] == pytest.approx(0.2 * 0.5 + 0.8 * 0.5)
+    assert a[1] == 0.5 and a[0] == 0.5
+    a = oracle.update_cascade([0.5, 0.5, 0.5], [2, 1, 0], 3)      # all accepted
+    assert a == pytest.approx([0.6, 0.6, 0.6])
+
+
+def test_latency_fit_recovers_linear_model():
+    beta = (0.4, 1e-3, 0.05)
+    samples = [(s, d, beta[0] + beta[1] * s + beta[2] * d)
+               for s in (128, 512, 1024, 2048) for d in (10, 22, 32)]
+    got = oracle.fit_latency(samples)
+    np.testing.assert_allclose(got, beta, rtol=1e-9, atol=1e-12)
+    assert oracle.predict_latency(got, 700, 16) == pytest.approx(0.4 + 0.7 + 0.8)
