@@ -1,0 +1,195 @@
+/*
+ * lss.h -- C ABI of the layer-skip self-speculative decoding engine (gfx950).
+ *
+ * The engine runs the draft -> verify -> accept -> layer-selection loop of
+ * on-the-fly self-speculative greedy decoding for one sequence of a
+ * Llama-style decoder on one GPU.  Sources of the method:
+ *   - CLaSp article (news.43b.com.cn/a/479818), section 3 "workflow": draft
+ *     with intermediate layers skipped, verify all drafts in one full-model
+ *     pass, replace the first rejected draft with the full model's token and
+ *     restart drafting there; choose the next skip set by a dynamic program
+ *     over (i layers, j skipped) that maximizes cosine similarity to the last
+ *     accepted token's full hidden states, all j of one i batched with a
+ *     special attention mask instead of copied KV.
+ *   - CAS-Spec summary page (arXiv 2510.26843), abstract, and the CAS-Spec
+ *     blog (intelliparadigm.com 2260101), sections 2.1-3.2: draft models built
+ *     from layer sparsity, early exit and dynamic 8-bit activation
+ *     quantization; several draft levels routed by an EMA acceptance
+ *     predictor (alpha = 0.2) and a linear latency model.
+ *
+ * Conventions for every entry point:
+ *   - Return 0 on success or a negative lss_status.  On an argument or state
+ *     error nothing is launched and the engine's committed state (length,
+ *     window, skip bits, pending token) is unchanged.  lss_last_error()
+ *     gives a message for the last failure of that engine.
+ *   - Pointers named *_dev are device pointers; everything else is host
+ *     memory owned by the caller and only read/written during the call.
+ *   - All device work is enqueued on the stream given to lss_create.  Calls
+ *     that return host values (tokens, counts) synchronize that stream.
+ *   - One engine is not thread-safe; separate engines are independent.
+ */
+#ifndef LSS_H
+#define LSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum lss_status {
+  LSS_OK = 0,
+  LSS_EINVAL = -1,     /* bad argument (sizes, null pointers, ranges) */
+  LSS_ESTATE = -2,     /* call out of order (e.g. accept without verify) */
+  LSS_ECAPACITY = -3,  /* KV capacity, window or row-block limit exceeded */
+  LSS_EHIP = -4,       /* a HIP runtime call failed; see lss_last_error */
+  LSS_ENOTIMPL = -5
+};
+
+enum lss_dtype { LSS_F32 = 0, LSS_BF16 = 1 };
+
+/* Largest number of draft tokens a window can hold. */
+#define LSS_WINDOW_MAX 31
+/* Largest row block of one forward (verify rows, DP rows, prefill chunk). */
+#define LSS_ROWS_MAX 64
+
+/* Model and capacity description.  Weights and the KV cache use `dtype`;
+ * activations and the residual stream are float32.  head_dim must be a
+ * multiple of 64 and at most 256; d_model, ffn_dim, n_heads*head_dim and
+ * n_kv_heads*head_dim must be multiples of 16; d_model <= 8192. */
+typedef struct lss_config {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  float rope_theta; /* rotary base; pairs (i, i + head_dim/2) */
+  float rms_eps;    /* RMSNorm epsilon */
+  int32_t dtype;    /* lss_dtype */
+  int32_t max_seq;  /* KV capacity in positions (prompt + generated + window) */
+  int32_t max_rows; /* row-block limit, 1..LSS_ROWS_MAX */
+} lss_config;
+
+typedef struct lss_engine lss_engine;
+
+/* Bytes of device workspace lss_create needs for `cfg` (KV cache, residual
+ * stash, activations, partial results).  0 if cfg is invalid. */
+size_t lss_workspace_bytes(const lss_config* cfg);
+
+/* load_weights: create an engine over caller-owned device tensors.
+ * tensors_dev: n_tensors = 3 + 9*n_layers device pointers in the order
+ *   embed [V][d], final_norm [d], lm_head [V][d], then per layer
+ *   attn_norm [d], wq [Hq*hd][d], wk [Hkv*hd][d], wv [Hkv*hd][d],
+ *   wo [d][Hq*hd], ffn_norm [d], w_gate [F][d], w_up [F][d], w_down [d][F];
+ *   matrices row-major [out][in] in cfg->dtype, norm gains float32.
+ * workspace_dev: >= lss_workspace_bytes(cfg) bytes of device memory.
+ * Both are borrowed (never freed) and must outlive the engine.  The engine
+ * allocates only a small pinned host buffer of its own.
+ * hip_stream: a hipStream_t (NULL = the null stream). */
+int lss_create(const lss_config* cfg, const void* const* tensors_dev, int32_t n_tensors,
+               void* workspace_dev, size_t workspace_bytes, void* hip_stream, lss_engine** out);
+void lss_destroy(lss_engine* e);
+const char* lss_last_error(const lss_engine* e);
+
+/* Full-model causal pass over the prompt (row blocks of max_rows).  Resets
+ * the sequence.  *t0_out = greedy next token, which becomes the pending
+ * token; the last prompt row becomes the layer-selection target. */
+int lss_prefill(lss_engine* e, const int32_t* tokens, int32_t n, int32_t* t0_out);
+
+/* Draft up to k tokens with the layers where skip_mask[l] != 0 skipped
+ * (CLaSp section 3, draft stage; an early exit is a mask whose tail is
+ * skipped).  quant != 0 quantizes every projection input of an executed
+ * layer to int8 per token (CAS-Spec blog section 2.1).  exit_tau > 0 stops
+ * after the first token whose top-1 softmax probability is below exit_tau
+ * (CLaSp section 4, draft exit threshold).  Appends to the pending window
+ * (several levels may draft into one window).  tokens_out[k] receives the
+ * drafted tokens, *k_done their count.  LSS_ECAPACITY if the window would
+ * exceed LSS_WINDOW_MAX or max_rows - 1 tokens or the KV capacity. */
+int lss_draft(lss_engine* e, const uint8_t* skip_mask, int32_t quant, int32_t k, float exit_tau,
+              int32_t* tokens_out, int32_t* k_done);
+
+/* Verify the window in one full-model pass over rows [t0, d1..dk] at
+ * positions p..p+k (CLaSp section 3, verification).  drafts == NULL
+ * verifies the pending window; otherwise the k host tokens replace it (a
+ * host-forced draft).  Acceptance is computed on the device; results are
+ * read by lss_accept_and_rollback. */
+int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k);
+
+/* Greedy acceptance and O(1) rollback: n = longest prefix of the drafts that
+ * equals the full model's argmax tokens, bonus = the full model's token
+ * after it.  The committed length becomes p + n + 1 (later KV rows are stale
+ * and never read), the window is cleared, the bonus token is pending, and
+ * verify row n becomes the layer-selection target.  accepted_out (may be
+ * NULL) receives the n + 1 emitted tokens d1..dn, bonus. */
+int lss_accept_and_rollback(lss_engine* e, int32_t* n_accepted, int32_t* bonus,
+                            int32_t* accepted_out);
+
+/* CLaSp layer selection (section 3): skip exactly n_skip of the first
+ * n_layers_eff layers (n_layers_eff <= n_layers; layers past it are marked
+ * skipped, an early exit) by the batched cosine-similarity DP against the
+ * target's full hidden states.  mask_out[n_layers] gets 1 = skip; score_out
+ * (may be NULL) the final cosine similarity. */
+int lss_select_layers_dp(lss_engine* e, int32_t n_skip, int32_t n_layers_eff, uint8_t* mask_out,
+                         float* score_out);
+
+/* Committed sequence length p. */
+int32_t lss_seq_len(const lss_engine* e);
+
+/* Parity helpers: logits [rows][vocab] of the last verify / draft step /
+ * prefill row; residual states [n_layers + 1][d] of verify row `row`; the
+ * DP's per-(i, j) decisions [(n_layers+1) * (max_rows)] as
+ * {skip_bit, cos_skip, cos_exec} float triples (unused slots NaN). */
+int lss_read_logits(lss_engine* e, int32_t rows, float* host_out);
+int lss_read_states(lss_engine* e, int32_t row, float* host_out);
+int lss_read_dp_decisions(lss_engine* e, float* host_out);
+
+/* Draft policy of lss_generate. */
+enum lss_mode { LSS_MODE_AR = 0, LSS_MODE_STATIC = 1, LSS_MODE_DP = 2, LSS_MODE_CASCADE = 3 };
+#define LSS_LEVELS_MAX 4
+typedef struct lss_policy {
+  int32_t mode;              /* lss_mode */
+  int32_t k_max;             /* draft tokens per round (cascade: total) */
+  float exit_tau;            /* draft exit threshold, <= 0 off */
+  int32_t quant;             /* STATIC / DP drafts: int8 activations */
+  const uint8_t* static_mask;/* STATIC: [n_layers] 1 = skip */
+  int32_t n_skip;            /* DP: layers to skip */
+  int32_t interval;          /* DP / CASCADE: re-run the DP every `interval` verify rounds */
+  int32_t n_levels;          /* CASCADE: levels, index 0 = fastest */
+  int32_t level_skip[LSS_LEVELS_MAX];  /* total skipped layers per level (incl. exit tail) */
+  int32_t level_exit[LSS_LEVELS_MAX];  /* early-exit tail length per level */
+  int32_t level_quant[LSS_LEVELS_MAX]; /* int8 activations per level */
+  double beta[3];            /* CASCADE latency model b0 + b1*seq_len + b2*executed_layers */
+} lss_policy;
+
+typedef struct lss_stats {
+  int32_t rounds, drafted, accepted, dp_runs, emitted;
+} lss_stats;
+
+/* Prefill `prompt`, then decode until n_gen tokens (t0 included) are
+ * emitted into out_tokens[n_gen] with the given policy; LSS_MODE_AR is the
+ * greedy autoregressive baseline (verify of the pending token alone). */
+int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t n_gen,
+                 const lss_policy* policy, int32_t* out_tokens, lss_stats* stats);
+
+/* DyTC router on the host (CAS-Spec blog sections 3.1-3.2, CAS-Spec
+ * abstract).  plan: draft length per level (index 0 = fastest) maximizing
+ * (E + 1) / (t_verify + sum k_l t_hat_l), E the expected accepted length of
+ * the window ordered most precise level first, total <= k_max.  update:
+ * EMA (alpha 0.2) of each level's accepted/reached ratio after a round
+ * whose window slots had levels slot_levels[k] and n were accepted.
+ * fit: least squares b for samples [n][3] = {seq_len, depth, seconds}. */
+int lss_router_plan(const double* accept_rate, const double* t_hat, int32_t n_levels,
+                    double t_verify, int32_t k_max, int32_t* plan_out);
+int lss_router_update(double* accept_rate, int32_t n_levels, const int32_t* slot_levels,
+                      int32_t k, int32_t n_accepted);
+int lss_latency_fit(const double* samples, int32_t n, double* beta_out);
+
+/* Stand-alone dynamic per-token int8 quantization (CAS-Spec blog section
+ * 2.1): for each of `rows` rows of x_dev[rows][n] (float32), codes q_dev
+ * [rows][n] = clamp(rint(x * fl(127/amax)), -127, 127) and scale_dev[rows]
+ * = amax/127, all in float32, amax = 0 giving codes 0 and scale 0.
+ * Enqueued on hip_stream; no synchronization. */
+int lss_op_quantize_rows(const float* x_dev, int32_t rows, int32_t n, int8_t* q_dev,
+                         float* scale_dev, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSS_H */

@@ -1,0 +1,757 @@
+// Engine of layer-skip self-speculative greedy decoding on one gfx950 GPU,
+// and its C ABI (include/lss.h).
+//
+// One forward code path serves every row block: prefill chunks, draft steps
+// (one row, skip mask, optional int8 activations), verify (k + 1 causal
+// rows), the autoregressive baseline (verify of one row) and the CLaSp
+// layer-selection rows (all at one position, each seeing the committed prefix
+// plus its own key/value).  Because every kernel is row-independent with a
+// fixed reduction order, verify rows equal autoregressive steps bit for bit.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/lss.h"
+#include "lss_kernels.h"
+#include "lss_router.h"
+
+using namespace lss;
+
+namespace {
+
+constexpr int kWinMax = LSS_WINDOW_MAX;
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t kc, vc, hs, hmid, xn, xs, qkv, qrot, selfkv, apart, aout, act, logits, hpart, rope, target,
+      dpg0, dpg1, dpx, dpdec, tok, seqtok, res, total;
+  int xld, nch_max, ntile;
+};
+
+bool cfg_valid(const lss_config* c, std::string* why) {
+  auto fail = [&](const char* m) { if (why) *why = m; return false; };
+  if (!c) return fail("null config");
+  if (c->n_layers < 1 || c->d_model < 16 || c->n_heads < 1 || c->n_kv_heads < 1 || c->ffn_dim < 16 ||
+      c->vocab < 1)
+    return fail("non-positive model dimension");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail("head_dim must be 64 or 128");
+  if (c->n_heads % c->n_kv_heads) return fail("n_heads must be a multiple of n_kv_heads");
+  if (c->d_model % 16 || c->ffn_dim % 16 || c->vocab % 16) return fail("d_model, ffn_dim, vocab must be multiples of 16");
+  if (c->d_model > 8192) return fail("d_model > 8192");
+  if (c->dtype != LSS_F32 && c->dtype != LSS_BF16) return fail("dtype must be LSS_F32 or LSS_BF16");
+  if (c->max_rows < 1 || c->max_rows > LSS_ROWS_MAX) return fail("max_rows out of [1, 64]");
+  if (c->max_seq < 2) return fail("max_seq < 2");
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail("bad rms_eps / rope_theta");
+  return true;
+}
+
+Layout make_layout(const lss_config* c) {
+  Layout L{};
+  const size_t elt = c->dtype == LSS_BF16 ? 2 : 4;
+  const size_t R = c->max_rows, d = c->d_model, F = c->ffn_dim, hd = c->head_dim;
+  const size_t Hq = c->n_heads, Hkv = c->n_kv_heads, V = c->vocab, NL = c->n_layers;
+  L.xld = (int)std::max({d, F, Hq * hd});
+  L.nch_max = (c->max_seq + ATT_CH - 1) / ATT_CH;
+  L.ntile = (int)((V + 15) / 16);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  L.kc = take(NL * Hkv * (size_t)c->max_seq * hd * elt);
+  L.vc = take(NL * Hkv * (size_t)c->max_seq * hd * elt);
+  L.hs = take((NL + 1) * R * d * 4);
+  L.hmid = take(R * d * 4);
+  L.xn = take(R * L.xld * 4);
+  L.xs = take(R * 4);
+  L.qkv = take(R * (Hq + 2 * Hkv) * hd * 4);
+  L.qrot = take(R * Hq * hd * 4);
+  L.selfkv = take(R * 2 * Hkv * hd * 4);
+  L.apart = take(R * Hq * (size_t)L.nch_max * (hd + 2) * 4);
+  L.aout = take(R * Hq * hd * 4);
+  L.act = take(R * F * 4);
+  L.logits = take(R * V * 4);
+  L.hpart = take(R * (size_t)L.ntile * 3 * 4);
+  L.rope = take((size_t)c->max_seq * (hd / 2) * 8);
+  L.target = take((NL + 1) * d * 4);
+  L.dpg0 = take(R * d * 4);
+  L.dpg1 = take(R * d * 4);
+  L.dpx = take(R * d * 4);
+  L.dpdec = take((NL + 1) * (NL + 1) * 3 * 4);
+  L.tok = take(64 * 4);
+  L.seqtok = take((size_t)c->max_seq * 4);
+  L.res = take(sizeof(HeadRes));
+  L.total = off;
+  return L;
+}
+
+struct LayerW {
+  const float* attn_norm;
+  const void *wq, *wk, *wv, *wo;
+  const float* ffn_norm;
+  const void *wg, *wu, *wd;
+};
+
+enum RowMode { MODE_CAUSAL = 0, MODE_DRAFT = 1, MODE_DP = 2 };
+
+}  // namespace
+
+struct lss_engine {
+  lss_config cfg{};
+  Layout lay{};
+  hipStream_t stream = nullptr;
+  bool bf16 = false;
+  const void* embed = nullptr;
+  const float* final_norm = nullptr;
+  const void* lm_head = nullptr;
+  std::vector<LayerW> layers;
+  char* ws = nullptr;
+  // device buffers
+  void *kc = nullptr, *vc = nullptr;
+  float *hs, *hmid, *xn, *xs, *qkv, *qrot, *selfkv, *apart, *aout, *act, *logits, *hpart, *target, *dpg[2],
+      *dpx, *dpdec;
+  float2* rope;
+  int32_t *tok, *seqtok;
+  HeadRes* res;
+  // pinned host mirrors
+  HeadRes* hres = nullptr;
+  int32_t* hstage = nullptr;
+  // sequence state
+  int p = 0;                  // committed length
+  int win = 0;                // drafted tokens in the window
+  std::vector<uint32_t> valid;  // per layer: window slots whose KV this layer wrote
+  bool have_seq = false;
+  bool pending_accept = false;
+  int verify_rows = 0;
+  int logits_rows = 0;
+  bool have_target = false;
+  int target_pos = 0;
+  std::string err;
+};
+
+namespace {
+
+int fail(lss_engine* e, int code, const std::string& msg) {
+  if (e) e->err = msg;
+  return code;
+}
+
+#define HIPCHK(expr)                                                                    \
+  do {                                                                                  \
+    hipError_t _s = (expr);                                                             \
+    if (_s != hipSuccess)                                                               \
+      return fail(e, LSS_EHIP, std::string(#expr) + ": " + hipGetErrorString(_s));     \
+  } while (0)
+
+int check_launch(lss_engine* e, const char* what) {
+  hipError_t s = hipGetLastError();
+  if (s != hipSuccess) return fail(e, LSS_EHIP, std::string(what) + ": " + hipGetErrorString(s));
+  return LSS_OK;
+}
+
+size_t kv_layer_elems(const lss_engine* e) {
+  return (size_t)e->cfg.n_kv_heads * e->cfg.max_seq * e->cfg.head_dim;
+}
+void* kc_layer(lss_engine* e, int l) {
+  const size_t elt = e->bf16 ? 2 : 4;
+  return (char*)e->kc + (size_t)l * kv_layer_elems(e) * elt;
+}
+void* vc_layer(lss_engine* e, int l) {
+  const size_t elt = e->bf16 ? 2 : 4;
+  return (char*)e->vc + (size_t)l * kv_layer_elems(e) * elt;
+}
+float* hs_row(lss_engine* e, int l, int m) {
+  return e->hs + ((size_t)l * e->cfg.max_rows + m) * e->cfg.d_model;
+}
+
+// ------------------------------------------------------------------ launches
+template <typename WT, int EPI>
+void gemm_mt(const GemmArgs& ga, hipStream_t s) {
+  const dim3 grid((ga.N + 15) / 16), block(64 * GEMM_WAVES);
+  const int mt = (ga.M + 15) / 16;
+  switch (mt) {
+    case 1: hipLaunchKernelGGL((k_gemm<WT, 1, EPI>), grid, block, 0, s, ga); break;
+    case 2: hipLaunchKernelGGL((k_gemm<WT, 2, EPI>), grid, block, 0, s, ga); break;
+    case 3: hipLaunchKernelGGL((k_gemm<WT, 3, EPI>), grid, block, 0, s, ga); break;
+    default: hipLaunchKernelGGL((k_gemm<WT, 4, EPI>), grid, block, 0, s, ga); break;
+  }
+}
+
+template <int EPI>
+void gemm(lss_engine* e, const GemmArgs& ga) {
+  if (e->bf16) gemm_mt<uint16_t, EPI>(ga, e->stream);
+  else gemm_mt<float, EPI>(ga, e->stream);
+}
+
+GemmArgs gemm_args(const void* w, int N, int K, const float* X, int ldx, int M, const float* xs, float* Y,
+                   int ldy) {
+  GemmArgs ga{};
+  ga.w[0] = w; ga.w[1] = w; ga.w[2] = w;
+  ga.nseg[0] = N; ga.nseg[1] = 0; ga.nseg[2] = 0;
+  ga.N = N; ga.K = K; ga.X = X; ga.ldx = ldx; ga.M = M; ga.xs = xs; ga.Y = Y; ga.ldy = ldy;
+  return ga;
+}
+
+void rmsnorm(lss_engine* e, const float* h, int M, const float* g, int quant) {
+  const auto& c = e->cfg;
+  hipLaunchKernelGGL(k_rmsnorm<float>, dim3(M), dim3(LSS_NORM_THREADS), 0, e->stream, h, c.d_model, g, c.d_model,
+                     c.rms_eps, e->xn, e->lay.xld, e->xs, quant);
+}
+
+template <typename KT>
+void attention(lss_engine* e, int l, int M, int mode, int pos0) {
+  const auto& c = e->cfg;
+  const int hd = c.head_dim;
+  AttnArgs a{};
+  a.kc = kc_layer(e, l);
+  a.vc = vc_layer(e, l);
+  a.max_seq = c.max_seq; a.Hq = c.n_heads; a.Hkv = c.n_kv_heads; a.hd = hd; a.M = M;
+  a.qrot = e->qrot;
+  a.part = e->apart; a.nch_max = e->lay.nch_max;
+  a.scale = (float)(1.0 / std::sqrt((double)hd));
+  int kmax;
+  if (mode == MODE_CAUSAL) { a.lim_base = pos0 + 1; a.lim_step = 1; a.wbase = 0; a.wmask = 0; kmax = pos0 + M; }
+  else if (mode == MODE_DRAFT) { a.lim_base = e->p; a.lim_step = 0; a.wbase = e->p; a.wmask = e->valid[l]; kmax = pos0 + 1; }
+  else { a.lim_base = pos0; a.lim_step = 0; a.wbase = 0; a.wmask = 0; kmax = pos0; }
+  a.nch = (kmax + ATT_CH - 1) / ATT_CH;
+  const int G = c.n_heads / c.n_kv_heads;
+  if (a.nch > 0) {
+    const dim3 grid(a.nch, c.n_kv_heads, (G * M + ATT_QB - 1) / ATT_QB);
+    if (hd == 128) hipLaunchKernelGGL((k_attn_partial<KT, 128>), grid, dim3(ATT_THREADS), 0, e->stream, a);
+    else hipLaunchKernelGGL((k_attn_partial<KT, 64>), grid, dim3(ATT_THREADS), 0, e->stream, a);
+  }
+  const float* self = mode == MODE_DP ? e->selfkv : nullptr;
+  if (hd == 128)
+    hipLaunchKernelGGL(k_attn_combine<128>, dim3(M * c.n_heads), dim3(128), 0, e->stream, e->apart, a.nch,
+                       e->lay.nch_max, c.n_heads, c.n_kv_heads, e->qrot, self, a.scale, e->aout);
+  else
+    hipLaunchKernelGGL(k_attn_combine<64>, dim3(M * c.n_heads), dim3(64), 0, e->stream, e->apart, a.nch,
+                       e->lay.nch_max, c.n_heads, c.n_kv_heads, e->qrot, self, a.scale, e->aout);
+}
+
+// One decoder layer on M rows: h_out = layer(h_in).  Rows are consecutive
+// positions pos0.. (causal), the single draft slot at pos0, or all at pos0
+// (layer selection).
+void layer_forward(lss_engine* e, int l, int M, const float* h_in, float* h_out, int mode, int pos0, int quant) {
+  const auto& c = e->cfg;
+  const LayerW& w = e->layers[l];
+  const int d = c.d_model, F = c.ffn_dim, hd = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
+  const int qd = Hq * hd, kvd = Hkv * hd;
+  rmsnorm(e, h_in, M, w.attn_norm, quant);
+  {
+    GemmArgs ga = gemm_args(w.wq, qd + 2 * kvd, d, e->xn, e->lay.xld, M, quant ? e->xs : nullptr, e->qkv,
+                            qd + 2 * kvd);
+    ga.w[0] = w.wq; ga.nseg[0] = qd;
+    ga.w[1] = w.wk; ga.nseg[1] = kvd;
+    ga.w[2] = w.wv; ga.nseg[2] = kvd;
+    gemm<EPI_STORE>(e, ga);
+  }
+  const int pos_step = mode == MODE_DP ? 0 : 1;
+  float* self = mode == MODE_DP ? e->selfkv : nullptr;
+  if (e->bf16)
+    hipLaunchKernelGGL(k_rope_kv<uint16_t>, dim3(M, Hq + 2 * Hkv), dim3(hd / 2), 0, e->stream, e->qkv,
+                       qd + 2 * kvd, Hq, Hkv, hd, e->rope, pos0, pos_step, e->qrot, (uint16_t*)kc_layer(e, l),
+                       (uint16_t*)vc_layer(e, l), c.max_seq, self);
+  else
+    hipLaunchKernelGGL(k_rope_kv<float>, dim3(M, Hq + 2 * Hkv), dim3(hd / 2), 0, e->stream, e->qkv,
+                       qd + 2 * kvd, Hq, Hkv, hd, e->rope, pos0, pos_step, e->qrot, (float*)kc_layer(e, l),
+                       (float*)vc_layer(e, l), c.max_seq, self);
+  if (e->bf16) attention<uint16_t>(e, l, M, mode, pos0);
+  else attention<float>(e, l, M, mode, pos0);
+  if (quant)
+    hipLaunchKernelGGL(k_quant_rows, dim3(M), dim3(256), 0, e->stream, e->aout, qd, qd, e->xs, (int8_t*)nullptr);
+  {
+    GemmArgs ga = gemm_args(w.wo, d, qd, e->aout, qd, M, quant ? e->xs : nullptr, e->hmid, d);
+    ga.R = h_in; ga.ldr = d;
+    gemm<EPI_RESID>(e, ga);
+  }
+  rmsnorm(e, e->hmid, M, w.ffn_norm, quant);
+  {
+    GemmArgs ga = gemm_args(w.wg, F, d, e->xn, e->lay.xld, M, quant ? e->xs : nullptr, e->act, F);
+    ga.w2 = w.wu;
+    gemm<EPI_SWIGLU>(e, ga);
+  }
+  if (quant)
+    hipLaunchKernelGGL(k_quant_rows, dim3(M), dim3(256), 0, e->stream, e->act, F, F, e->xs, (int8_t*)nullptr);
+  {
+    GemmArgs ga = gemm_args(w.wd, d, F, e->act, F, M, quant ? e->xs : nullptr, h_out, d);
+    ga.R = e->hmid; ga.ldr = d;
+    gemm<EPI_RESID>(e, ga);
+  }
+}
+
+// Final norm + LM head on M rows of h (row stride d); per-row argmax and top-1
+// probability land in res->argmax/pmax[row0 + m].
+void head(lss_engine* e, const float* h, int M, int row0) {
+  const auto& c = e->cfg;
+  rmsnorm(e, h, M, e->final_norm, 0);
+  GemmArgs ga = gemm_args(e->lm_head, c.vocab, c.d_model, e->xn, e->lay.xld, M, nullptr, e->logits, c.vocab);
+  ga.part = e->hpart;
+  gemm<EPI_LOGITS>(e, ga);
+  hipLaunchKernelGGL(k_head_reduce, dim3(M), dim3(256), 0, e->stream, e->hpart, e->lay.ntile, e->res, row0);
+  e->logits_rows = M;
+}
+
+void embed(lss_engine* e, const int32_t* tok_dev, int M, float* h) {
+  const auto& c = e->cfg;
+  if (e->bf16)
+    hipLaunchKernelGGL(k_embed<uint16_t>, dim3(M), dim3(256), 0, e->stream, (const uint16_t*)e->embed, tok_dev,
+                       c.d_model, h, c.d_model);
+  else
+    hipLaunchKernelGGL(k_embed<float>, dim3(M), dim3(256), 0, e->stream, (const float*)e->embed, tok_dev,
+                       c.d_model, h, c.d_model);
+}
+
+int sync_res(lss_engine* e) {
+  HIPCHK(hipMemcpyAsync(e->hres, e->res, sizeof(HeadRes), hipMemcpyDeviceToHost, e->stream));
+  HIPCHK(hipStreamSynchronize(e->stream));
+  return LSS_OK;
+}
+
+void fill_u32(lss_engine* e, void* p, size_t n, uint32_t v) {
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 65536);
+  if (n) hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, e->stream, (uint32_t*)p, n, v);
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+size_t lss_workspace_bytes(const lss_config* cfg) {
+  if (!cfg_valid(cfg, nullptr)) return 0;
+  return make_layout(cfg).total;
+}
+
+int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tensors, void* workspace,
+               size_t workspace_bytes, void* hip_stream, lss_engine** out) {
+  lss_engine* e = nullptr;
+  std::string why;
+  if (!out) return LSS_EINVAL;
+  *out = nullptr;
+  if (!cfg_valid(cfg, &why)) return LSS_EINVAL;
+  if (!tensors || n_tensors != 3 + 9 * cfg->n_layers || !workspace) return LSS_EINVAL;
+  for (int i = 0; i < n_tensors; ++i)
+    if (!tensors[i] || ((uintptr_t)tensors[i] & 15)) return LSS_EINVAL;
+  if (((uintptr_t)workspace & 255)) return LSS_EINVAL;
+  const Layout lay = make_layout(cfg);
+  if (workspace_bytes < lay.total) return LSS_ECAPACITY;
+
+  e = new lss_engine();
+  e->cfg = *cfg;
+  e->lay = lay;
+  e->stream = (hipStream_t)hip_stream;
+  e->bf16 = cfg->dtype == LSS_BF16;
+  e->embed = tensors[0];
+  e->final_norm = (const float*)tensors[1];
+  e->lm_head = tensors[2];
+  e->layers.resize(cfg->n_layers);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const void* const* t = tensors + 3 + 9 * l;
+    e->layers[l] = LayerW{(const float*)t[0], t[1], t[2], t[3], t[4], (const float*)t[5], t[6], t[7], t[8]};
+  }
+  char* ws = (char*)workspace;
+  e->ws = ws;
+  e->kc = ws + lay.kc; e->vc = ws + lay.vc;
+  e->hs = (float*)(ws + lay.hs); e->hmid = (float*)(ws + lay.hmid); e->xn = (float*)(ws + lay.xn);
+  e->xs = (float*)(ws + lay.xs); e->qkv = (float*)(ws + lay.qkv); e->qrot = (float*)(ws + lay.qrot);
+  e->selfkv = (float*)(ws + lay.selfkv); e->apart = (float*)(ws + lay.apart); e->aout = (float*)(ws + lay.aout);
+  e->act = (float*)(ws + lay.act); e->logits = (float*)(ws + lay.logits); e->hpart = (float*)(ws + lay.hpart);
+  e->rope = (float2*)(ws + lay.rope); e->target = (float*)(ws + lay.target);
+  e->dpg[0] = (float*)(ws + lay.dpg0); e->dpg[1] = (float*)(ws + lay.dpg1); e->dpx = (float*)(ws + lay.dpx);
+  e->dpdec = (float*)(ws + lay.dpdec); e->tok = (int32_t*)(ws + lay.tok); e->seqtok = (int32_t*)(ws + lay.seqtok);
+  e->res = (HeadRes*)(ws + lay.res);
+  e->valid.assign(cfg->n_layers, 0u);
+
+  hipError_t s = hipHostMalloc((void**)&e->hres, sizeof(HeadRes), hipHostMallocDefault);
+  if (s == hipSuccess)
+    s = hipHostMalloc((void**)&e->hstage, ((size_t)cfg->max_seq + 64) * sizeof(int32_t), hipHostMallocDefault);
+  if (s != hipSuccess) {
+    lss_destroy(e);
+    return LSS_EHIP;
+  }
+  // zero the workspace (stale KV rows past the committed length must be finite)
+  fill_u32(e, ws, lay.total / 4, 0u);
+  // rotary table: angle t * theta^(-2i/hd) in double, cos/sin rounded to float
+  {
+    const int half = cfg->head_dim / 2;
+    std::vector<float2> tab((size_t)cfg->max_seq * half);
+    for (int t = 0; t < cfg->max_seq; ++t)
+      for (int i = 0; i < half; ++i) {
+        const double ang = (double)t * std::pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim);
+        tab[(size_t)t * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+      }
+    s = hipMemcpyAsync(e->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice, e->stream);
+    if (s == hipSuccess) s = hipStreamSynchronize(e->stream);
+    if (s == hipSuccess) s = hipGetLastError();
+    if (s != hipSuccess) {
+      lss_destroy(e);
+      return LSS_EHIP;
+    }
+  }
+  *out = e;
+  return LSS_OK;
+}
+
+void lss_destroy(lss_engine* e) {
+  if (!e) return;
+  (void)hipStreamSynchronize(e->stream);
+  if (e->hres) (void)hipHostFree(e->hres);
+  if (e->hstage) (void)hipHostFree(e->hstage);
+  delete e;
+}
+
+const char* lss_last_error(const lss_engine* e) { return e ? e->err.c_str() : "null engine"; }
+
+int32_t lss_seq_len(const lss_engine* e) { return e ? e->p : -1; }
+
+int lss_prefill(lss_engine* e, const int32_t* tokens, int32_t n, int32_t* t0_out) {
+  if (!e) return LSS_EINVAL;
+  const auto& c = e->cfg;
+  if (!tokens || n < 1) return fail(e, LSS_EINVAL, "prefill: empty prompt");
+  if (n + 1 > c.max_seq) return fail(e, LSS_ECAPACITY, "prefill: prompt exceeds max_seq - 1");
+  for (int i = 0; i < n; ++i)
+    if (tokens[i] < 0 || tokens[i] >= c.vocab) return fail(e, LSS_EINVAL, "prefill: token id out of range");
+  std::memcpy(e->hstage, tokens, sizeof(int32_t) * n);
+  HIPCHK(hipMemcpyAsync(e->seqtok, e->hstage, sizeof(int32_t) * n, hipMemcpyHostToDevice, e->stream));
+  const int R = c.max_rows;
+  int last_m = 0;
+  for (int c0 = 0; c0 < n; c0 += R) {
+    const int M = std::min(R, n - c0);
+    embed(e, e->seqtok + c0, M, hs_row(e, 0, 0));
+    for (int l = 0; l < c.n_layers; ++l)
+      layer_forward(e, l, M, hs_row(e, l, 0), hs_row(e, l + 1, 0), MODE_CAUSAL, c0, 0);
+    last_m = M - 1;
+  }
+  head(e, hs_row(e, c.n_layers, last_m), 1, 0);
+  hipLaunchKernelGGL(k_accept, dim3(1), dim3(1), 0, e->stream, e->res, 0, e->tok);  // tok[0] = argmax
+  hipLaunchKernelGGL(k_gather_target, dim3(c.n_layers + 1), dim3(256), 0, e->stream, e->hs, R, c.d_model,
+                     (const HeadRes*)nullptr, last_m, e->target);
+  int rc = check_launch(e, "prefill");
+  if (rc) return rc;
+  rc = sync_res(e);
+  if (rc) return rc;
+  e->p = n;
+  e->win = 0;
+  std::fill(e->valid.begin(), e->valid.end(), 0u);
+  e->have_seq = true;
+  e->pending_accept = false;
+  e->have_target = true;
+  e->target_pos = n - 1;
+  if (t0_out) *t0_out = e->hres->argmax[0];
+  return LSS_OK;
+}
+
+int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, float exit_tau, int32_t* tokens_out,
+              int32_t* k_done) {
+  if (!e) return LSS_EINVAL;
+  const auto& c = e->cfg;
+  if (!e->have_seq || e->pending_accept) return fail(e, LSS_ESTATE, "draft: needs a prefilled sequence and no pending accept");
+  if (!mask || k < 0 || (quant != 0 && quant != 1)) return fail(e, LSS_EINVAL, "draft: bad arguments");
+  if (k > 0 && !tokens_out) return fail(e, LSS_EINVAL, "draft: null tokens_out");
+  const int win_cap = std::min(kWinMax, c.max_rows - 1);
+  if (e->win + k > win_cap) return fail(e, LSS_ECAPACITY, "draft: window would exceed its capacity");
+  if (e->p + e->win + k + 1 > c.max_seq) return fail(e, LSS_ECAPACITY, "draft: KV capacity exceeded");
+  const int start = e->win;
+  int done = 0;
+  for (int s = 0; s < k; ++s) {
+    const int slot = e->win;
+    const int pos = e->p + slot;
+    embed(e, e->tok + slot, 1, hs_row(e, 0, 0));
+    const float* h = hs_row(e, 0, 0);
+    for (int l = 0; l < c.n_layers; ++l) {
+      if (mask[l]) continue;
+      e->valid[l] |= 1u << slot;
+      layer_forward(e, l, 1, h, hs_row(e, l + 1, 0), MODE_DRAFT, pos, quant);
+      h = hs_row(e, l + 1, 0);
+    }
+    head(e, h, 1, slot);
+    hipLaunchKernelGGL(k_draft_commit, dim3(1), dim3(1), 0, e->stream, e->res, slot, e->tok);
+    e->win++;
+    done++;
+    if (exit_tau > 0.f) {
+      int rc = check_launch(e, "draft");
+      if (rc) return rc;
+      rc = sync_res(e);
+      if (rc) return rc;
+      if (e->hres->pmax[slot] < exit_tau) break;
+    }
+  }
+  int rc = check_launch(e, "draft");
+  if (rc) return rc;
+  if (done > 0) {
+    rc = sync_res(e);
+    if (rc) return rc;
+    for (int i = 0; i < done; ++i) tokens_out[i] = e->hres->argmax[start + i];
+  }
+  if (k_done) *k_done = done;
+  return LSS_OK;
+}
+
+int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k) {
+  if (!e) return LSS_EINVAL;
+  const auto& c = e->cfg;
+  if (!e->have_seq || e->pending_accept) return fail(e, LSS_ESTATE, "verify: needs a prefilled sequence and no pending accept");
+  if (drafts) {
+    if (k < 0 || k > std::min(kWinMax, c.max_rows - 1)) return fail(e, LSS_ECAPACITY, "verify: k exceeds the window capacity");
+    for (int i = 0; i < k; ++i)
+      if (drafts[i] < 0 || drafts[i] >= c.vocab) return fail(e, LSS_EINVAL, "verify: token id out of range");
+  } else {
+    if (k != e->win) return fail(e, LSS_EINVAL, "verify: k must equal the pending window length");
+  }
+  if (e->p + k + 1 > c.max_seq) return fail(e, LSS_ECAPACITY, "verify: KV capacity exceeded");
+  if (drafts && k > 0) {
+    std::memcpy(e->hstage, drafts, sizeof(int32_t) * k);
+    HIPCHK(hipMemcpyAsync(e->tok + 1, e->hstage, sizeof(int32_t) * k, hipMemcpyHostToDevice, e->stream));
+  }
+  const int M = k + 1;
+  embed(e, e->tok, M, hs_row(e, 0, 0));
+  for (int l = 0; l < c.n_layers; ++l)
+    layer_forward(e, l, M, hs_row(e, l, 0), hs_row(e, l + 1, 0), MODE_CAUSAL, e->p, 0);
+  head(e, hs_row(e, c.n_layers, 0), M, 0);
+  hipLaunchKernelGGL(k_accept, dim3(1), dim3(1), 0, e->stream, e->res, k, e->tok);
+  hipLaunchKernelGGL(k_gather_target, dim3(c.n_layers + 1), dim3(256), 0, e->stream, e->hs, c.max_rows,
+                     c.d_model, (const HeadRes*)e->res, 0, e->target);
+  const int rc = check_launch(e, "verify");
+  if (rc) return rc;
+  e->win = k;
+  e->verify_rows = M;
+  e->pending_accept = true;
+  return LSS_OK;
+}
+
+int lss_accept_and_rollback(lss_engine* e, int32_t* n_accepted, int32_t* bonus, int32_t* accepted_out) {
+  if (!e) return LSS_EINVAL;
+  if (!e->pending_accept) return fail(e, LSS_ESTATE, "accept: no verify pending");
+  const int rc = sync_res(e);
+  if (rc) return rc;
+  const int n = e->hres->n;
+  if (n_accepted) *n_accepted = n;
+  if (bonus) *bonus = e->hres->bonus;
+  if (accepted_out)
+    for (int i = 0; i <= n; ++i) accepted_out[i] = e->hres->argmax[i];
+  e->target_pos = e->p + n;
+  e->have_target = true;
+  e->p += n + 1;
+  e->win = 0;
+  std::fill(e->valid.begin(), e->valid.end(), 0u);
+  e->pending_accept = false;
+  return LSS_OK;
+}
+
+int lss_select_layers_dp(lss_engine* e, int32_t S, int32_t Le, uint8_t* mask_out, float* score_out) {
+  if (!e) return LSS_EINVAL;
+  const auto& c = e->cfg;
+  const int L = c.n_layers, d = c.d_model;
+  if (!mask_out || Le < 0 || Le > L || S < 0 || S > Le) return fail(e, LSS_EINVAL, "select_layers_dp: bad n_skip / n_layers_eff");
+  if (!e->have_target || e->pending_accept) return fail(e, LSS_ESTATE, "select_layers_dp: no target state");
+  if (std::min(S, Le - S) + 1 > c.max_rows) return fail(e, LSS_ECAPACITY, "select_layers_dp: more DP rows than max_rows");
+  auto lo = [&](int i) { return std::max(0, S - (Le - i)); };
+  auto hi = [&](int i) { return std::min(i, S); };
+  const int tstar = e->target_pos;
+  fill_u32(e, e->dpdec, (size_t)(L + 1) * (L + 1) * 3, 0x7fc00000u);
+  HIPCHK(hipMemcpyAsync(e->dpg[0], e->target, sizeof(float) * d, hipMemcpyDeviceToDevice, e->stream));
+  int cur = 0;
+  for (int i = 1; i <= Le; ++i) {
+    const int lo_p = lo(i - 1), hi_p = hi(i - 1), lo_i = lo(i), hi_i = hi(i);
+    const int ex_lo = std::max(lo_i, lo_p), ex_hi = std::min(hi_i, hi_p);
+    const int ne = ex_hi - ex_lo + 1;
+    if (ne > 0)
+      layer_forward(e, i - 1, ne, e->dpg[cur] + (size_t)(ex_lo - lo_p) * d, e->dpx, MODE_DP, tstar, 0);
+    hipLaunchKernelGGL(k_dp_select, dim3(hi_i - lo_i + 1), dim3(256), 0, e->stream, e->dpx, ex_lo, ex_hi,
+                       e->dpg[cur], lo_p, hi_p, e->target + (size_t)i * d, d, lo_i, e->dpg[cur ^ 1],
+                       e->dpdec + (size_t)i * (L + 1) * 3);
+    cur ^= 1;
+  }
+  int rc = check_launch(e, "select_layers_dp");
+  if (rc) return rc;
+  std::vector<float> dec((size_t)(L + 1) * (L + 1) * 3);
+  HIPCHK(hipMemcpyAsync(dec.data(), e->dpdec, dec.size() * sizeof(float), hipMemcpyDeviceToHost, e->stream));
+  HIPCHK(hipStreamSynchronize(e->stream));
+  for (int l = 0; l < L; ++l) mask_out[l] = l >= Le ? 1 : 0;
+  int j = S;
+  float score = 1.f;
+  if (Le > 0) {
+    const float* f = &dec[((size_t)Le * (L + 1) + S) * 3];
+    score = f[0] != 0.f ? f[1] : f[2];
+  }
+  for (int i = Le; i >= 1; --i) {
+    const float take = dec[((size_t)i * (L + 1) + j) * 3];
+    if (take != 0.f) { mask_out[i - 1] = 1; --j; }
+  }
+  if (j != 0) return fail(e, LSS_EHIP, "select_layers_dp: inconsistent back-pointers");
+  if (score_out) *score_out = score;
+  return LSS_OK;
+}
+
+int lss_read_logits(lss_engine* e, int32_t rows, float* host_out) {
+  if (!e || !host_out || rows < 1 || rows > e->logits_rows) return fail(e, LSS_EINVAL, "read_logits: bad rows");
+  HIPCHK(hipMemcpyAsync(host_out, e->logits, sizeof(float) * rows * (size_t)e->cfg.vocab, hipMemcpyDeviceToHost,
+                        e->stream));
+  HIPCHK(hipStreamSynchronize(e->stream));
+  return LSS_OK;
+}
+
+int lss_read_states(lss_engine* e, int32_t row, float* host_out) {
+  if (!e || !host_out || row < 0 || row >= e->cfg.max_rows) return fail(e, LSS_EINVAL, "read_states: bad row");
+  const auto& c = e->cfg;
+  for (int l = 0; l <= c.n_layers; ++l)
+    HIPCHK(hipMemcpyAsync(host_out + (size_t)l * c.d_model, hs_row(e, l, row), sizeof(float) * c.d_model,
+                          hipMemcpyDeviceToHost, e->stream));
+  HIPCHK(hipStreamSynchronize(e->stream));
+  return LSS_OK;
+}
+
+int lss_read_dp_decisions(lss_engine* e, float* host_out) {
+  if (!e || !host_out) return LSS_EINVAL;
+  const size_t n = (size_t)(e->cfg.n_layers + 1) * (e->cfg.n_layers + 1) * 3;
+  HIPCHK(hipMemcpyAsync(host_out, e->dpdec, n * sizeof(float), hipMemcpyDeviceToHost, e->stream));
+  HIPCHK(hipStreamSynchronize(e->stream));
+  return LSS_OK;
+}
+
+int lss_op_quantize_rows(const float* x, int32_t rows, int32_t n, int8_t* q, float* scale, void* stream) {
+  if (!x || !q || !scale || rows < 0 || n < 0) return LSS_EINVAL;
+  if (rows == 0 || n == 0) {
+    if (rows > 0 && n == 0)
+      hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, (hipStream_t)stream, (uint32_t*)scale, (size_t)rows, 0u);
+    return hipGetLastError() == hipSuccess ? LSS_OK : LSS_EHIP;
+  }
+  hipLaunchKernelGGL(k_quant_rows, dim3(rows), dim3(256), 0, (hipStream_t)stream, const_cast<float*>(x), n, n,
+                     scale, q);
+  return hipGetLastError() == hipSuccess ? LSS_OK : LSS_EHIP;
+}
+
+// ---------------------------------------------------------------- generation loop
+int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t n_gen, const lss_policy* pol,
+                 int32_t* out, lss_stats* stats) {
+  if (!e) return LSS_EINVAL;
+  const auto& c = e->cfg;
+  const int L = c.n_layers;
+  if (!pol || !out || n_gen < 1) return fail(e, LSS_EINVAL, "generate: bad arguments");
+  if (pol->mode < LSS_MODE_AR || pol->mode > LSS_MODE_CASCADE) return fail(e, LSS_EINVAL, "generate: bad mode");
+  if (pol->mode != LSS_MODE_AR && (pol->k_max < 0 || pol->k_max > std::min(kWinMax, c.max_rows - 1)))
+    return fail(e, LSS_EINVAL, "generate: k_max out of range");
+  if (pol->mode == LSS_MODE_STATIC && !pol->static_mask) return fail(e, LSS_EINVAL, "generate: static mask missing");
+  if ((pol->mode == LSS_MODE_DP || pol->mode == LSS_MODE_CASCADE) && pol->interval < 1)
+    return fail(e, LSS_EINVAL, "generate: interval < 1");
+  if (pol->mode == LSS_MODE_CASCADE) {
+    if (pol->n_levels < 1 || pol->n_levels > LSS_LEVELS_MAX) return fail(e, LSS_EINVAL, "generate: n_levels");
+    for (int v = 0; v < pol->n_levels; ++v)
+      if (pol->level_exit[v] < 0 || pol->level_exit[v] > pol->level_skip[v] || pol->level_skip[v] > L)
+        return fail(e, LSS_EINVAL, "generate: level skip / exit out of range");
+  }
+  if ((long)n_prompt + n_gen + std::min(kWinMax, c.max_rows - 1) + 1 > c.max_seq)
+    return fail(e, LSS_ECAPACITY, "generate: prompt + generation + window exceeds max_seq");
+  lss_stats st{};
+  int32_t t0 = 0;
+  int rc = lss_prefill(e, prompt, n_prompt, &t0);
+  if (rc) return rc;
+  int emitted = 0;
+  out[emitted++] = t0;
+  const int nlev = pol->mode == LSS_MODE_CASCADE ? pol->n_levels : 1;
+  std::vector<std::vector<uint8_t>> masks(nlev, std::vector<uint8_t>(L, 0));
+  auto select = [&]() -> int {
+    if (pol->mode == LSS_MODE_STATIC) {
+      std::copy(pol->static_mask, pol->static_mask + L, masks[0].begin());
+    } else if (pol->mode == LSS_MODE_DP) {
+      int r = lss_select_layers_dp(e, pol->n_skip, L, masks[0].data(), nullptr);
+      if (r) return r;
+      st.dp_runs++;
+    } else if (pol->mode == LSS_MODE_CASCADE) {
+      for (int v = 0; v < nlev; ++v) {
+        int r = lss_select_layers_dp(e, pol->level_skip[v] - pol->level_exit[v], L - pol->level_exit[v],
+                                     masks[v].data(), nullptr);
+        if (r) return r;
+        st.dp_runs++;
+      }
+    }
+    return LSS_OK;
+  };
+  if (pol->mode != LSS_MODE_AR) {
+    rc = select();
+    if (rc) return rc;
+  }
+  std::vector<double> acc_rate(nlev, router::kAInit);
+  std::vector<int32_t> slot_levels;
+  std::vector<int32_t> toks(64), acc(64);
+  while (emitted < n_gen) {
+    const int budget = n_gen - emitted - 1;
+    slot_levels.clear();
+    if (pol->mode == LSS_MODE_STATIC || pol->mode == LSS_MODE_DP) {
+      const int k = std::min(pol->k_max, budget);
+      if (k > 0) {
+        int kd = 0;
+        rc = lss_draft(e, masks[0].data(), pol->quant, k, pol->exit_tau, toks.data(), &kd);
+        if (rc) return rc;
+      }
+    } else if (pol->mode == LSS_MODE_CASCADE) {
+      std::vector<double> t_hat(nlev);
+      for (int v = 0; v < nlev; ++v) {
+        int depth = 0;
+        for (int l = 0; l < L; ++l) depth += masks[v][l] ? 0 : 1;
+        t_hat[v] = router::predict(pol->beta, e->p, depth);
+      }
+      const double t_ver = router::predict(pol->beta, e->p, L);
+      std::vector<int32_t> plan(nlev);
+      router::plan(acc_rate.data(), t_hat.data(), nlev, t_ver, pol->k_max, plan.data());
+      int used = 0;
+      for (int v = nlev - 1; v >= 0; --v) {
+        const int k = std::min(plan[v], budget - used);
+        if (k <= 0) continue;
+        int kd = 0;
+        rc = lss_draft(e, masks[v].data(), pol->level_quant[v], k, 0.f, toks.data(), &kd);
+        if (rc) return rc;
+        for (int i = 0; i < kd; ++i) slot_levels.push_back(v);
+        used += kd;
+      }
+    }
+    const int k = e->win;
+    rc = lss_verify(e, nullptr, k);
+    if (rc) return rc;
+    int n = 0, bonus = 0;
+    rc = lss_accept_and_rollback(e, &n, &bonus, acc.data());
+    if (rc) return rc;
+    for (int i = 0; i <= n && emitted < n_gen; ++i) out[emitted++] = acc[i];
+    st.rounds++;
+    st.drafted += k;
+    st.accepted += n;
+    if (pol->mode == LSS_MODE_CASCADE)
+      router::update(acc_rate.data(), nlev, slot_levels.data(), (int)slot_levels.size(), n);
+    if ((pol->mode == LSS_MODE_DP || pol->mode == LSS_MODE_CASCADE) && st.rounds % pol->interval == 0) {
+      rc = select();
+      if (rc) return rc;
+    }
+  }
+  st.emitted = emitted;
+  if (stats) *stats = st;
+  return LSS_OK;
+}
+
+// ---------------------------------------------------------------- router ABI
+int lss_router_plan(const double* a, const double* t_hat, int32_t n_levels, double t_verify, int32_t k_max,
+                    int32_t* plan_out) {
+  if (!a || !t_hat || !plan_out || n_levels < 1 || n_levels > LSS_LEVELS_MAX || k_max < 0 || k_max > kWinMax)
+    return LSS_EINVAL;
+  router::plan(a, t_hat, n_levels, t_verify, k_max, plan_out);
+  return LSS_OK;
+}
+
+int lss_router_update(double* a, int32_t n_levels, const int32_t* slot_levels, int32_t k, int32_t n) {
+  if (!a || n_levels < 1 || n_levels > LSS_LEVELS_MAX || k < 0 || n < 0 || n > k || (k > 0 && !slot_levels))
+    return LSS_EINVAL;
+  for (int i = 0; i < k; ++i)
+    if (slot_levels[i] < 0 || slot_levels[i] >= n_levels) return LSS_EINVAL;
+  router::update(a, n_levels, slot_levels, k, n);
+  return LSS_OK;
+}
+
+int lss_latency_fit(const double* samples, int32_t n, double* beta_out) {
+  if (!samples || !beta_out || n < 3) return LSS_EINVAL;
+  return router::fit(samples, n, beta_out) ? LSS_OK : LSS_EINVAL;
+}
+
+}  // extern "C"

@@ -1,0 +1,229 @@
+"""Python face of the engine: the C-ABI calls of include/lss.h with the same
+names, plus device-memory plumbing (torch allocates the workspace, the stream
+comes from torch).  Every decoding step runs in liblss.so."""
+import ctypes as C
+
+import numpy as np
+
+from . import _native as N
+
+
+class LssError(RuntimeError):
+    def __init__(self, what, rc, msg=""):
+        super().__init__(f"{what}: {N.STATUS_NAMES.get(rc, rc)} {msg}".strip())
+        self.rc = rc
+
+
+def _i32(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return a, a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def _u8(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.uint8))
+    return a, a.ctypes.data_as(C.POINTER(C.c_uint8))
+
+
+def make_config(shape, max_seq, max_rows=16):
+    return N.lss_config(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim,
+                        shape.ffn_dim, shape.vocab, float(shape.rope_theta), float(shape.rms_eps),
+                        N.LSS_BF16 if shape.dtype == "bf16" else N.LSS_F32, int(max_seq), int(max_rows))
+
+
+def workspace_bytes(shape, max_seq, max_rows=16):
+    cfg = make_config(shape, max_seq, max_rows)
+    return int(N.load().lss_workspace_bytes(C.byref(cfg)))
+
+
+class Engine:
+    """One sequence on one GPU.  ``weights``: ``[(name, tensor)]`` in the
+    canonical order on the CUDA device (they are borrowed, not copied)."""
+
+    def __init__(self, shape, weights, max_seq, max_rows=16, stream=None, device="cuda"):
+        import torch
+        self.lib = N.load()
+        self.shape = shape
+        self.cfg = make_config(shape, max_seq, max_rows)
+        self._tensors = [t for _, t in weights]
+        n = len(self._tensors)
+        nbytes = self.lib.lss_workspace_bytes(C.byref(self.cfg))
+        if nbytes == 0:
+            raise LssError("lss_workspace_bytes", N.LSS_EINVAL, "invalid config")
+        self._ws = torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self._ws.device)
+        ptrs = (C.c_void_p * n)(*[t.data_ptr() for t in self._tensors])
+        h = C.c_void_p()
+        rc = self.lib.lss_create(C.byref(self.cfg), ptrs, n, C.c_void_p(self._ws.data_ptr()), nbytes,
+                                 C.c_void_p(self.stream.cuda_stream), C.byref(h))
+        if rc != 0:
+            raise LssError("lss_create", rc)
+        self.h = h
+
+    # -------------------------------------------------------------- helpers
+    def _check(self, rc, what):
+        if rc != 0:
+            msg = self.lib.lss_last_error(self.h)
+            raise LssError(what, rc, msg.decode() if msg else "")
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.lss_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def seq_len(self):
+        return int(self.lib.lss_seq_len(self.h))
+
+    # -------------------------------------------------------------- hot path
+    def prefill(self, tokens):
+        a, p = _i32(tokens)
+        t0 = C.c_int32()
+        self._check(self.lib.lss_prefill(self.h, p, len(a), C.byref(t0)), "lss_prefill")
+        return int(t0.value)
+
+    def draft(self, skip_mask, quant=False, k=1, exit_tau=0.0):
+        m, mp = _u8(skip_mask)
+        out = np.zeros(max(k, 1), np.int32)
+        done = C.c_int32()
+        self._check(self.lib.lss_draft(self.h, mp, int(bool(quant)), int(k), float(exit_tau),
+                                       out.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(done)), "lss_draft")
+        return out[:done.value].tolist()
+
+    def verify(self, drafts=None, k=None):
+        if drafts is None:
+            self._check(self.lib.lss_verify(self.h, None, int(k)), "lss_verify")
+        else:
+            a, p = _i32(drafts)
+            self._check(self.lib.lss_verify(self.h, p, len(a)), "lss_verify")
+
+    def accept(self):
+        n, b = C.c_int32(), C.c_int32()
+        out = np.zeros(N.LSS_ROWS_MAX, np.int32)
+        self._check(self.lib.lss_accept_and_rollback(self.h, C.byref(n), C.byref(b),
+                                                     out.ctypes.data_as(C.POINTER(C.c_int32))),
+                    "lss_accept_and_rollback")
+        return int(n.value), int(b.value), out[:n.value + 1].tolist()
+
+    def select_layers_dp(self, n_skip, n_layers_eff=None):
+        L = self.shape.n_layers
+        mask = np.zeros(L, np.uint8)
+        score = C.c_float()
+        self._check(self.lib.lss_select_layers_dp(self.h, int(n_skip), int(L if n_layers_eff is None else n_layers_eff),
+                                                  mask.ctypes.data_as(C.POINTER(C.c_uint8)), C.byref(score)),
+                    "lss_select_layers_dp")
+        return mask.tolist(), float(score.value)
+
+    def generate(self, prompt, n_gen, policy):
+        a, p = _i32(prompt)
+        pol = make_policy(policy, self.shape.n_layers)
+        out = np.zeros(n_gen, np.int32)
+        st = N.lss_stats()
+        self._check(self.lib.lss_generate(self.h, p, len(a), int(n_gen), C.byref(pol),
+                                          out.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(st)), "lss_generate")
+        return out.tolist(), {f: getattr(st, f) for f, _ in N.lss_stats._fields_}
+
+    # -------------------------------------------------------------- parity helpers
+    def read_logits(self, rows=1):
+        out = np.zeros((rows, self.shape.vocab), np.float32)
+        self._check(self.lib.lss_read_logits(self.h, rows, out.ctypes.data_as(C.POINTER(C.c_float))),
+                    "lss_read_logits")
+        return out
+
+    def read_states(self, row=0):
+        out = np.zeros((self.shape.n_layers + 1, self.shape.d_model), np.float32)
+        self._check(self.lib.lss_read_states(self.h, row, out.ctypes.data_as(C.POINTER(C.c_float))),
+                    "lss_read_states")
+        return out
+
+    def read_dp_decisions(self):
+        L = self.shape.n_layers
+        out = np.zeros((L + 1, L + 1, 3), np.float32)
+        self._check(self.lib.lss_read_dp_decisions(self.h, out.ctypes.data_as(C.POINTER(C.c_float))),
+                    "lss_read_dp_decisions")
+        return out
+
+
+def make_policy(policy, n_layers):
+    """``policy``: dict with ``mode`` in {"ar", "static", "dp", "cascade"} and
+    the matching fields of ``lss_policy``."""
+    pol = N.lss_policy()
+    mode = policy.get("mode", "ar")
+    pol.mode = {"ar": N.LSS_MODE_AR, "static": N.LSS_MODE_STATIC, "dp": N.LSS_MODE_DP,
+                "cascade": N.LSS_MODE_CASCADE}[mode]
+    pol.k_max = int(policy.get("k_max", 0))
+    pol.exit_tau = float(policy.get("exit_tau", 0.0))
+    pol.quant = int(bool(policy.get("quant", False)))
+    if mode == "static":
+        mask = np.zeros(n_layers, np.uint8)
+        for l in policy["skip"]:
+            mask[l] = 1
+        pol._mask_keepalive = mask
+        pol.static_mask = mask.ctypes.data_as(C.POINTER(C.c_uint8))
+    pol.n_skip = int(policy.get("n_skip", 0))
+    pol.interval = int(policy.get("interval", 1))
+    levels = policy.get("levels", [])
+    pol.n_levels = len(levels)
+    for i, (skip, exit_, quant) in enumerate(levels):
+        pol.level_skip[i] = int(skip)
+        pol.level_exit[i] = int(exit_)
+        pol.level_quant[i] = int(bool(quant))
+    beta = policy.get("beta", (0.0, 0.0, 0.0))
+    for i in range(3):
+        pol.beta[i] = float(beta[i])
+    return pol
+
+
+# ------------------------------------------------------------------ host-only entry points
+def router_plan(accept_rate, t_hat, t_verify, k_max):
+    lib = N.load()
+    nl = len(accept_rate)
+    a = (C.c_double * nl)(*accept_rate)
+    t = (C.c_double * nl)(*t_hat)
+    out = (C.c_int32 * nl)()
+    rc = lib.lss_router_plan(a, t, nl, float(t_verify), int(k_max), out)
+    if rc != 0:
+        raise LssError("lss_router_plan", rc)
+    return list(out)
+
+
+def router_update(accept_rate, slot_levels, n_accepted):
+    lib = N.load()
+    nl = len(accept_rate)
+    a = (C.c_double * nl)(*accept_rate)
+    lv = (C.c_int32 * max(1, len(slot_levels)))(*slot_levels)
+    rc = lib.lss_router_update(a, nl, lv, len(slot_levels), int(n_accepted))
+    if rc != 0:
+        raise LssError("lss_router_update", rc)
+    return list(a)
+
+
+def latency_fit(samples):
+    lib = N.load()
+    flat = [float(v) for s in samples for v in s]
+    arr = (C.c_double * len(flat))(*flat)
+    beta = (C.c_double * 3)()
+    rc = lib.lss_latency_fit(arr, len(samples), beta)
+    if rc != 0:
+        raise LssError("lss_latency_fit", rc)
+    return tuple(beta)
+
+
+def quantize_rows(x):
+    """int8 codes and per-row scales of a CUDA float32 tensor [rows][n]."""
+    import torch
+    lib = N.load()
+    x = x.contiguous()
+    rows, n = x.shape
+    q = torch.empty((rows, n), dtype=torch.int8, device=x.device)
+    s = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    rc = lib.lss_op_quantize_rows(C.c_void_p(x.data_ptr()), rows, n, C.c_void_p(q.data_ptr()),
+                                  C.c_void_p(s.data_ptr()), C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise LssError("lss_op_quantize_rows", rc)
+    return q, s

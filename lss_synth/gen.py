@@ -18,6 +18,9 @@ def make_weights(shape: ModelShape, device="cpu", seed=None, planted_identity=()
                  head_scale=1.0):
     """Return ``[(name, tensor)]`` in canonical order, on ``device``.
 
+    Matrices are in the shape's dtype (float32 or bfloat16, rounded to nearest
+    even from a float32 draw); RMSNorm gains are float32 ones.
+
     Each tensor ``i`` is drawn from its own torch generator seeded with
     ``seed * 1_000_003 + i``.  The same seed gives different values on CPU and
     GPU (different generator engines); every comparison in this repository
@@ -51,7 +54,9 @@ def make_weights(shape: ModelShape, device="cpu", seed=None, planted_identity=()
             if base == "lm_head":
                 scale *= head_scale
             t.mul_(scale)
-        out.append((name, t.to(dt).contiguous()))
+        if base not in _NORMS:          # norm gains stay float32 in every config
+            t = t.to(dt)
+        out.append((name, t.contiguous()))
     return out
 
 

@@ -1,0 +1,101 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, validates configurations without touching a GPU, and its host-only
+DyTC router agrees with the oracle's router."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import lss_synth
+import oracle
+from layer_skip_self_amd import _native as N
+import layer_skip_self_amd as lss
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lss.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lss_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = N.load()
+    names = _declared()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(N.SIGNATURES), set(names) ^ set(N.SIGNATURES)
+
+
+def test_workspace_size_and_invalid_configs():
+    sh = lss_synth.SHAPES["llama3_8b"]
+    nb = lss.workspace_bytes(sh, max_seq=1600, max_rows=16)
+    kv = 2 * 32 * 8 * 1600 * 128 * 2
+    assert kv < nb < kv + 200 * 2**20
+    lib = N.load()
+    for field, bad in [("head_dim", 96), ("max_rows", 65), ("max_rows", 0), ("d_model", 8208),
+                       ("n_kv_heads", 5), ("dtype", 7), ("max_seq", 1)]:
+        cfg = lss.make_config(sh, 1600, 16)
+        setattr(cfg, field, bad)
+        assert lib.lss_workspace_bytes(C.byref(cfg)) == 0, field
+        h = C.c_void_p()
+        rc = lib.lss_create(C.byref(cfg), None, 0, None, 0, None, C.byref(h))
+        assert rc == N.LSS_EINVAL and not h.value
+
+
+def test_create_rejects_bad_pointers_without_gpu():
+    sh = lss_synth.SHAPES["tiny"]
+    lib = N.load()
+    cfg = lss.make_config(sh, 64, 8)
+    h = C.c_void_p()
+    n = 3 + 9 * sh.n_layers
+    ptrs = (C.c_void_p * n)(*([0x1000] * n))
+    assert lib.lss_create(C.byref(cfg), ptrs, n - 1, C.c_void_p(0x100000), 1 << 30, None, C.byref(h)) == N.LSS_EINVAL
+    ptrs[5] = 0x1001                      # misaligned tensor
+    assert lib.lss_create(C.byref(cfg), ptrs, n, C.c_void_p(0x100000), 1 << 30, None, C.byref(h)) == N.LSS_EINVAL
+    ptrs[5] = 0x1000
+    assert lib.lss_create(C.byref(cfg), ptrs, n, C.c_void_p(0x100000), 16, None, C.byref(h)) == N.LSS_ECAPACITY
+    assert lib.lss_seq_len(None) == -1
+
+
+def test_router_plan_matches_oracle():
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        nl = int(rng.integers(1, 4))
+        a = list(rng.uniform(0, 1, nl))
+        if rng.uniform() < 0.2:
+            a = [float(round(x, 1)) for x in a]
+        t = list(rng.uniform(0.05, 1.0, nl))
+        tv = float(rng.uniform(0.5, 2.0))
+        k = int(rng.integers(0, 9))
+        assert lss.router_plan(a, t, tv, k) == oracle.plan_cascade(a, t, tv, k)
+
+
+def test_router_update_matches_oracle_bitwise():
+    rng = np.random.default_rng(8)
+    for _ in range(200):
+        nl = 3
+        a = list(rng.uniform(0, 1, nl))
+        k = int(rng.integers(0, 9))
+        levels = sorted((int(x) for x in rng.integers(0, nl, k)), reverse=True)
+        n = int(rng.integers(0, k + 1))
+        assert lss.router_update(a, levels, n) == oracle.update_cascade(a, levels, n)
+
+
+def test_latency_fit_matches_oracle():
+    rng = np.random.default_rng(9)
+    samples = [(s, d, 0.3 + 2e-4 * s + 0.04 * d + rng.normal(0, 0.01))
+               for s in (128, 512, 1024, 2048) for d in (10, 22, 32)]
+    np.testing.assert_allclose(lss.latency_fit(samples), oracle.fit_latency(samples), rtol=1e-9, atol=1e-12)
+
+
+def test_router_rejects_bad_arguments():
+    with pytest.raises(lss.LssError):
+        lss.router_plan([0.5] * 5, [1.0] * 5, 1.0, 8)
+    with pytest.raises(lss.LssError):
+        lss.router_update([0.5, 0.5], [0, 3], 1)
