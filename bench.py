@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark of batch-1 self-speculative greedy decoding on one MI355X.
+
+Default workload (the Llama-3-8B-shaped configuration): 32 layers, d 4096,
+32 query / 8 KV heads, FFN 14336, vocab 128256, bf16 weights drawn N(0, 0.02)
+with residual-branch output projections x0.1; a 1024-token uniform-random
+prompt; 512 generated tokens; the CLaSp DP skips 16 layers and re-runs every
+32 verify rounds; draft exit threshold 0.7; at most 8 drafts per round.
+
+One step = one full generation (prefill + layer selection + draft / verify /
+accept rounds) of that workload; ``value`` = generated tokens / step time.
+The same process also times the GPU's own greedy decoding (speedup), checks
+that both produce identical tokens, times the draft gate/up GEMV launches
+with HIP events on the engine stream (roofline), and times the CPU oracle
+on a bounded sample (cpu_baseline).  Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+WORKLOADS = {
+    "llama3_8b": dict(shape="llama3_8b", prompt=1024, gen=512,
+                      policy={"mode": "dp", "k_max": 8, "n_skip": 16, "interval": 32, "exit_tau": 0.7},
+                      desc="Llama-3-8B shape, prompt 1024, 512 generated, CLaSp DP skip 16 every 32 "
+                           "rounds, exit threshold 0.7, K <= 8"),
+    "llama2_7b": dict(shape="llama2_7b", prompt=512, gen=256,
+                      policy={"mode": "static", "k_max": 6, "skip": tuple(range(1, 32, 2))},
+                      desc="Llama-2-7B shape, prompt 512, 256 generated, static skip of layers 1,3,..,31, K 6"),
+    "tiny": dict(shape="tiny", prompt=32, gen=64, policy={"mode": "static", "k_max": 4, "skip": (1, 2)},
+                 desc="4-layer float32 model, prompt 32, 64 generated, skip {1,2}, K 4"),
+}
+
+
+def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
+    """Time the CPU oracle (float32, as it stands) on a bounded sample."""
+    import numpy as np
+    import lss_synth
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    w_host = [(n, t.to("cpu")) for n, t in w_gpu]
+    model = oracle.OracleModel(shape, lss_synth.LazyF32(w_host), dtype=np.float32, cache_layers=True)
+    for l in range(shape.n_layers):           # widen every weight once (setup, not timed)
+        model.layer(l)
+    model._get("lm_head"); model._get("final_norm")
+    pol = oracle.Policy(K=policy.get("k_max", 4), skip=tuple(policy.get("skip", ())),
+                        dp_skip=policy.get("n_skip") if policy["mode"] == "dp" else None,
+                        interval=policy.get("interval", 32), tau=policy.get("exit_tau", 0.0))
+    sample = np.asarray(prompt[:n_prompt])
+    t0 = time.perf_counter()
+    toks, recs = oracle.speculative_generate(model, sample, n_tokens, pol)
+    dt = time.perf_counter() - t0
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"oracle float32 speculative decoding (same policy) of {len(toks)} tokens after a "
+                      f"{n_prompt}-token prompt of the same workload; prefill + layer selection + "
+                      f"{len(recs)} rounds in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama3_8b", choices=sorted(WORKLOADS))
+    ap.add_argument("--ar-steps", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--cpu-prompt", type=int, default=64)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this engine runs one sequence on one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is a design note only)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import lss_synth
+    from layer_skip_self_amd import Engine
+
+    wl = WORKLOADS[args.workload]
+    shape = lss_synth.SHAPES[wl["shape"]]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    weights = lss_synth.make_weights(shape, device=dev)
+    prompt = lss_synth.make_prompt(shape, wl["prompt"])
+    G = wl["gen"]
+    max_seq = wl["prompt"] + G + 33
+    eng = Engine(shape, weights, max_seq=max_seq, max_rows=64)
+    stream = eng.stream
+
+    def run(policy):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        toks, st = eng.generate(prompt, G, policy)
+        torch.cuda.synchronize()
+        return toks, st, time.perf_counter() - t
+
+    for _ in range(args.warmup):
+        run(wl["policy"])
+    eng.profile_kernel("gate_up", rows=1)
+    times, stats, spec_toks = [], [], None
+    torch.cuda.synchronize()
+    t_all = time.perf_counter()
+    for _ in range(args.steps):
+        toks, st, dt = run(wl["policy"])
+        times.append(dt)
+        stats.append(st)
+        spec_toks = toks
+    torch.cuda.synchronize()
+    t_all = time.perf_counter() - t_all
+    k_ms, k_n, k_bytes = eng.profile_read()
+    eng.profile_kernel("gate_up", enable=False)
+
+    ar_times, ar_toks = [], None
+    run({"mode": "ar"})
+    for _ in range(args.ar_steps):
+        ar_toks, _, dt = run({"mode": "ar"})
+        ar_times.append(dt)
+    pre = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        eng.prefill(prompt)
+        torch.cuda.synchronize()
+        pre.append(time.perf_counter() - t)
+    prefill_s = min(pre)
+
+    step_s = t_all / args.steps
+    value = G / step_s
+    ar_value = G / (sum(ar_times) / len(ar_times))
+    st = stats[-1]
+    rounds = st["rounds"]
+    avg_launch_us = 1e3 * k_ms / max(k_n, 1)
+    bytes_per_launch = k_bytes / max(k_n, 1)
+    achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9 if k_n else None
+    out = {
+        "metric": "gen tokens/s @bs1 (Llama-3-8B shape), speedup vs AR, draft GEMV HBM GB/s",
+        "value": round(value, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * step_s, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic (seeded random-init weights and uniform-random prompt)",
+        "config": {"workload": wl["desc"], "global_batch": 1, "seq_len": wl["prompt"] + G,
+                   "parallelism": "none (1 GPU)"},
+        "speedup_vs_ar": round(value / ar_value, 4),
+        "ar_tokens_per_s": round(ar_value, 3),
+        "lossless": spec_toks == ar_toks,
+        "mean_accepted": round(st["accepted"] / max(rounds, 1), 4),
+        "tokens_per_round": round((st["emitted"] - 1) / max(rounds, 1), 4),
+        "drafted_per_round": round(st["drafted"] / max(rounds, 1), 4),
+        "rounds": rounds,
+        "dp_runs": st["dp_runs"],
+        "prefill_ms": round(1e3 * prefill_s, 3),
+        "decode_tokens_per_s": round((G - 1) / (step_s - prefill_s), 3),
+        "draft_gemv_gbps": round(achieved, 1) if achieved else None,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_gemm<bf16,1,SWIGLU,one-row>: draft gate/up projection + SwiGLU, 1 row",
+            "achieved": round(achieved, 1) if achieved else None,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
+            "traffic": None,
+            "bytes_per_launch": int(bytes_per_launch),
+            "avg_launch_us": round(avg_launch_us, 3),
+            "launches": k_n,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(shape, weights, prompt, wl["policy"], args.cpu_tokens,
+                                           min(args.cpu_prompt, wl["prompt"]))
+    eng.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -54,10 +54,10 @@ enum lss_dtype { LSS_F32 = 0, LSS_BF16 = 1 };
 /* Largest row block of one forward (verify rows, DP rows, prefill chunk). */
 #define LSS_ROWS_MAX 64
 
-/* Model and capacity description.  Weights and the KV cache use `dtype`;
- * activations and the residual stream are float32.  head_dim must be a
- * multiple of 64 and at most 256; d_model, ffn_dim, n_heads*head_dim and
- * n_kv_heads*head_dim must be multiples of 16; d_model <= 8192. */
+/* Model and capacity description.  Weights use `dtype`, the KV cache
+ * `kv_dtype`; activations and the residual stream are float32.  head_dim must be 64 or
+ * 128; n_heads a multiple of n_kv_heads; d_model, ffn_dim and vocab
+ * multiples of 16; d_model <= 8192. */
 typedef struct lss_config {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   float rope_theta; /* rotary base; pairs (i, i + head_dim/2) */
@@ -65,6 +65,7 @@ typedef struct lss_config {
   int32_t dtype;    /* lss_dtype */
   int32_t max_seq;  /* KV capacity in positions (prompt + generated + window) */
   int32_t max_rows; /* row-block limit, 1..LSS_ROWS_MAX */
+  int32_t kv_dtype; /* lss_dtype of the KV cache (float32 keeps keys/values unrounded) */
 } lss_config;
 
 typedef struct lss_engine lss_engine;
@@ -133,9 +134,11 @@ int lss_select_layers_dp(lss_engine* e, int32_t n_skip, int32_t n_layers_eff, ui
 int32_t lss_seq_len(const lss_engine* e);
 
 /* Parity helpers: logits [rows][vocab] of the last verify / draft step /
- * prefill row; residual states [n_layers + 1][d] of verify row `row`; the
- * DP's per-(i, j) decisions [(n_layers+1) * (max_rows)] as
- * {skip_bit, cos_skip, cos_exec} float triples (unused slots NaN). */
+ * prefill row; residual states [n_layers + 1][d] of verify row `row` (valid
+ * until the next draft, verify or prefill); the last DP's decisions
+ * [n_layers + 1][n_layers + 1] (stage i, skipped count j) as float triples
+ * {skip chosen, cos(skip candidate), cos(executed candidate)}, NaN where a
+ * state or candidate does not exist. */
 int lss_read_logits(lss_engine* e, int32_t rows, float* host_out);
 int lss_read_states(lss_engine* e, int32_t row, float* host_out);
 int lss_read_dp_decisions(lss_engine* e, float* host_out);
@@ -180,6 +183,17 @@ int lss_router_plan(const double* accept_rate, const double* t_hat, int32_t n_le
 int lss_router_update(double* accept_rate, int32_t n_levels, const int32_t* slot_levels,
                       int32_t k, int32_t n_accepted);
 int lss_latency_fit(const double* samples, int32_t n, double* beta_out);
+
+/* Measurement: time every launch of one GEMM family with HIP events on the
+ * engine stream.  epilogue: 0 = fused q/k/v projection, 1 = projection +
+ * residual add (attention output, FFN down), 2 = gate/up projection + SwiGLU,
+ * 3 = LM head + argmax partials; rows: match only launches with this many
+ * rows (0 = any).  enable = 0 stops recording.  lss_profile_read syncs the
+ * stream and returns the summed launch time, the launch count and the summed
+ * algorithmic bytes (weights + activation rows read + output rows written)
+ * since profiling was enabled. */
+int lss_profile_kernel(lss_engine* e, int32_t epilogue, int32_t rows, int32_t enable);
+int lss_profile_read(lss_engine* e, double* total_ms, int64_t* launches, int64_t* bytes);
 
 /* Stand-alone dynamic per-token int8 quantization (CAS-Spec blog section
  * 2.1): for each of `rows` rows of x_dev[rows][n] (float32), codes q_dev

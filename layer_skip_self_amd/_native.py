@@ -19,7 +19,8 @@ class lss_config(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_heads", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_dim", C.c_int32),
                 ("vocab", C.c_int32), ("rope_theta", C.c_float), ("rms_eps", C.c_float),
-                ("dtype", C.c_int32), ("max_seq", C.c_int32), ("max_rows", C.c_int32)]
+                ("dtype", C.c_int32), ("max_seq", C.c_int32), ("max_rows", C.c_int32),
+                ("kv_dtype", C.c_int32)]
 
 
 class lss_policy(C.Structure):
@@ -61,6 +62,9 @@ SIGNATURES = {
     "lss_router_update": (C.c_int, [C.POINTER(C.c_double), C.c_int32, C.POINTER(C.c_int32), C.c_int32,
                                     C.c_int32]),
     "lss_latency_fit": (C.c_int, [C.POINTER(C.c_double), C.c_int32, C.POINTER(C.c_double)]),
+    "lss_profile_kernel": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32]),
+    "lss_profile_read": (C.c_int, [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_int64),
+                                   C.POINTER(C.c_int64)]),
     "lss_op_quantize_rows": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                        C.c_void_p]),
 }

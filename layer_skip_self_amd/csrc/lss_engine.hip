@@ -45,6 +45,7 @@ bool cfg_valid(const lss_config* c, std::string* why) {
   if (c->d_model % 16 || c->ffn_dim % 16 || c->vocab % 16) return fail("d_model, ffn_dim, vocab must be multiples of 16");
   if (c->d_model > 8192) return fail("d_model > 8192");
   if (c->dtype != LSS_F32 && c->dtype != LSS_BF16) return fail("dtype must be LSS_F32 or LSS_BF16");
+  if (c->kv_dtype != LSS_F32 && c->kv_dtype != LSS_BF16) return fail("kv_dtype must be LSS_F32 or LSS_BF16");
   if (c->max_rows < 1 || c->max_rows > LSS_ROWS_MAX) return fail("max_rows out of [1, 64]");
   if (c->max_seq < 2) return fail("max_seq < 2");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail("bad rms_eps / rope_theta");
@@ -53,7 +54,7 @@ bool cfg_valid(const lss_config* c, std::string* why) {
 
 Layout make_layout(const lss_config* c) {
   Layout L{};
-  const size_t elt = c->dtype == LSS_BF16 ? 2 : 4;
+  const size_t elt = c->kv_dtype == LSS_BF16 ? 2 : 4;
   const size_t R = c->max_rows, d = c->d_model, F = c->ffn_dim, hd = c->head_dim;
   const size_t Hq = c->n_heads, Hkv = c->n_kv_heads, V = c->vocab, NL = c->n_layers;
   L.xld = (int)std::max({d, F, Hq * hd});
@@ -103,7 +104,8 @@ struct lss_engine {
   lss_config cfg{};
   Layout lay{};
   hipStream_t stream = nullptr;
-  bool bf16 = false;
+  bool bf16 = false;     // weights
+  bool kv16 = false;     // KV cache
   const void* embed = nullptr;
   const float* final_norm = nullptr;
   const void* lm_head = nullptr;
@@ -129,6 +131,12 @@ struct lss_engine {
   int logits_rows = 0;
   bool have_target = false;
   int target_pos = 0;
+  // kernel timing (lss_profile_kernel)
+  int prof_epi = -1, prof_rows = 0;
+  std::vector<hipEvent_t> ev_start, ev_stop;
+  int ev_used = 0;
+  double prof_ms = 0.0;
+  int64_t prof_launches = 0, prof_bytes = 0;
   std::string err;
 };
 
@@ -156,11 +164,11 @@ size_t kv_layer_elems(const lss_engine* e) {
   return (size_t)e->cfg.n_kv_heads * e->cfg.max_seq * e->cfg.head_dim;
 }
 void* kc_layer(lss_engine* e, int l) {
-  const size_t elt = e->bf16 ? 2 : 4;
+  const size_t elt = e->kv16 ? 2 : 4;
   return (char*)e->kc + (size_t)l * kv_layer_elems(e) * elt;
 }
 void* vc_layer(lss_engine* e, int l) {
-  const size_t elt = e->bf16 ? 2 : 4;
+  const size_t elt = e->kv16 ? 2 : 4;
   return (char*)e->vc + (size_t)l * kv_layer_elems(e) * elt;
 }
 float* hs_row(lss_engine* e, int l, int m) {
@@ -172,18 +180,48 @@ template <typename WT, int EPI>
 void gemm_mt(const GemmArgs& ga, hipStream_t s) {
   const dim3 grid((ga.N + 15) / 16), block(64 * GEMM_WAVES);
   const int mt = (ga.M + 15) / 16;
-  switch (mt) {
-    case 1: hipLaunchKernelGGL((k_gemm<WT, 1, EPI>), grid, block, 0, s, ga); break;
-    case 2: hipLaunchKernelGGL((k_gemm<WT, 2, EPI>), grid, block, 0, s, ga); break;
-    case 3: hipLaunchKernelGGL((k_gemm<WT, 3, EPI>), grid, block, 0, s, ga); break;
-    default: hipLaunchKernelGGL((k_gemm<WT, 4, EPI>), grid, block, 0, s, ga); break;
+  if (ga.M == 1) {
+    hipLaunchKernelGGL((k_gemm<WT, 1, EPI, true>), grid, block, 0, s, ga);
+    return;
   }
+  switch (mt) {
+    case 1: hipLaunchKernelGGL((k_gemm<WT, 1, EPI, false>), grid, block, 0, s, ga); break;
+    case 2: hipLaunchKernelGGL((k_gemm<WT, 2, EPI, false>), grid, block, 0, s, ga); break;
+    case 3: hipLaunchKernelGGL((k_gemm<WT, 3, EPI, false>), grid, block, 0, s, ga); break;
+    default: hipLaunchKernelGGL((k_gemm<WT, 4, EPI, false>), grid, block, 0, s, ga); break;
+  }
+}
+
+// Sum the elapsed times of recorded event pairs (the stream must be synced).
+void prof_resolve(lss_engine* e) {
+  for (int i = 0; i < e->ev_used; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, e->ev_start[i], e->ev_stop[i]) == hipSuccess) e->prof_ms += ms;
+  }
+  e->ev_used = 0;
 }
 
 template <int EPI>
 void gemm(lss_engine* e, const GemmArgs& ga) {
+  const bool prof = e->prof_epi == EPI && (e->prof_rows == 0 || e->prof_rows == ga.M);
+  if (prof) {
+    if (e->ev_used == (int)e->ev_start.size()) {
+      (void)hipStreamSynchronize(e->stream);
+      prof_resolve(e);
+    }
+    (void)hipEventRecord(e->ev_start[e->ev_used], e->stream);
+  }
   if (e->bf16) gemm_mt<uint16_t, EPI>(ga, e->stream);
   else gemm_mt<float, EPI>(ga, e->stream);
+  if (prof) {
+    (void)hipEventRecord(e->ev_stop[e->ev_used], e->stream);
+    e->ev_used++;
+    const int64_t elt = e->bf16 ? 2 : 4;
+    const int64_t nw = (EPI == EPI_SWIGLU) ? 2 : 1;
+    e->prof_launches++;
+    e->prof_bytes += nw * (int64_t)ga.N * ga.K * elt + (int64_t)ga.M * ga.K * 4 + (int64_t)ga.M * ga.N * 4 +
+                     (EPI == EPI_RESID ? (int64_t)ga.M * ga.N * 4 : 0);
+  }
 }
 
 GemmArgs gemm_args(const void* w, int N, int K, const float* X, int ldx, int M, const float* xs, float* Y,
@@ -251,7 +289,7 @@ void layer_forward(lss_engine* e, int l, int M, const float* h_in, float* h_out,
   }
   const int pos_step = mode == MODE_DP ? 0 : 1;
   float* self = mode == MODE_DP ? e->selfkv : nullptr;
-  if (e->bf16)
+  if (e->kv16)
     hipLaunchKernelGGL(k_rope_kv<uint16_t>, dim3(M, Hq + 2 * Hkv), dim3(hd / 2), 0, e->stream, e->qkv,
                        qd + 2 * kvd, Hq, Hkv, hd, e->rope, pos0, pos_step, e->qrot, (uint16_t*)kc_layer(e, l),
                        (uint16_t*)vc_layer(e, l), c.max_seq, self);
@@ -259,7 +297,7 @@ void layer_forward(lss_engine* e, int l, int M, const float* h_in, float* h_out,
     hipLaunchKernelGGL(k_rope_kv<float>, dim3(M, Hq + 2 * Hkv), dim3(hd / 2), 0, e->stream, e->qkv,
                        qd + 2 * kvd, Hq, Hkv, hd, e->rope, pos0, pos_step, e->qrot, (float*)kc_layer(e, l),
                        (float*)vc_layer(e, l), c.max_seq, self);
-  if (e->bf16) attention<uint16_t>(e, l, M, mode, pos0);
+  if (e->kv16) attention<uint16_t>(e, l, M, mode, pos0);
   else attention<float>(e, l, M, mode, pos0);
   if (quant)
     hipLaunchKernelGGL(k_quant_rows, dim3(M), dim3(256), 0, e->stream, e->aout, qd, qd, e->xs, (int8_t*)nullptr);
@@ -308,6 +346,7 @@ void embed(lss_engine* e, const int32_t* tok_dev, int M, float* h) {
 int sync_res(lss_engine* e) {
   HIPCHK(hipMemcpyAsync(e->hres, e->res, sizeof(HeadRes), hipMemcpyDeviceToHost, e->stream));
   HIPCHK(hipStreamSynchronize(e->stream));
+  if (e->ev_used) prof_resolve(e);
   return LSS_OK;
 }
 
@@ -345,6 +384,7 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
   e->lay = lay;
   e->stream = (hipStream_t)hip_stream;
   e->bf16 = cfg->dtype == LSS_BF16;
+  e->kv16 = cfg->kv_dtype == LSS_BF16;
   e->embed = tensors[0];
   e->final_norm = (const float*)tensors[1];
   e->lm_head = tensors[2];
@@ -399,6 +439,8 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
 void lss_destroy(lss_engine* e) {
   if (!e) return;
   (void)hipStreamSynchronize(e->stream);
+  for (auto ev : e->ev_start) (void)hipEventDestroy(ev);
+  for (auto ev : e->ev_stop) (void)hipEventDestroy(ev);
   if (e->hres) (void)hipHostFree(e->hres);
   if (e->hstage) (void)hipHostFree(e->hstage);
   delete e;
@@ -728,6 +770,42 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
   }
   st.emitted = emitted;
   if (stats) *stats = st;
+  return LSS_OK;
+}
+
+int lss_profile_kernel(lss_engine* e, int32_t epi, int32_t rows, int32_t enable) {
+  if (!e) return LSS_EINVAL;
+  if (enable && (epi < 0 || epi > 3 || rows < 0)) return fail(e, LSS_EINVAL, "profile_kernel: bad epilogue / rows");
+  HIPCHK(hipStreamSynchronize(e->stream));
+  prof_resolve(e);
+  if (!enable) {
+    e->prof_epi = -1;
+    return LSS_OK;
+  }
+  if (e->ev_start.empty()) {
+    const int n = 2048;
+    e->ev_start.resize(n);
+    e->ev_stop.resize(n);
+    for (int i = 0; i < n; ++i) {
+      HIPCHK(hipEventCreate(&e->ev_start[i]));
+      HIPCHK(hipEventCreate(&e->ev_stop[i]));
+    }
+  }
+  e->prof_epi = epi;
+  e->prof_rows = rows;
+  e->prof_ms = 0.0;
+  e->prof_launches = 0;
+  e->prof_bytes = 0;
+  return LSS_OK;
+}
+
+int lss_profile_read(lss_engine* e, double* total_ms, int64_t* launches, int64_t* bytes) {
+  if (!e) return LSS_EINVAL;
+  HIPCHK(hipStreamSynchronize(e->stream));
+  prof_resolve(e);
+  if (total_ms) *total_ms = e->prof_ms;
+  if (launches) *launches = e->prof_launches;
+  if (bytes) *bytes = e->prof_bytes;
   return LSS_OK;
 }
 

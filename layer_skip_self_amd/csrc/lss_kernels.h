@@ -274,7 +274,9 @@ __device__ __forceinline__ void load_a(float (&a)[MT][GEMM_U][WTr<WT>::EPL], con
   }
 }
 
-template <typename WT, int MT, int EPI>
+// ONE = the launch has exactly one row (draft steps, greedy steps): the same
+// arithmetic as MT = 1, compiled separately so profiles attribute it apart.
+template <typename WT, int MT, int EPI, bool ONE>
 __global__ __launch_bounds__(64 * GEMM_WAVES) void k_gemm(GemmArgs ga) {
   constexpr int EPL = WTr<WT>::EPL;
   constexpr int KS = 4 * EPL * GEMM_U;  // k per wave step
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void k_gemm(GemmArgs ga) {
     load_w<WT>(wc[0], wrow, kb, K, row_ok);
     if constexpr (NACC == 2) load_w<WT>(wc[1], wrow2, kb, K, row_ok);
     for (int s = s0; s < s1; ++s) {
-      load_a<WT, MT>(ac, ga.X, ga.ldx, ga.M, r, kb, K);
+      load_a<WT, MT>(ac, ga.X, ga.ldx, ONE ? 1 : ga.M, r, kb, K);
       const int kn = kb + KS;
       if (s + 1 < s1) {
         load_w<WT>(wn[0], wrow, kn, K, row_ok);

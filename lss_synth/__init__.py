@@ -13,7 +13,7 @@ projections (attention output ``wo`` and FFN ``w_down``) are further scaled
 by 0.1; RMSNorm gains are 1; the LM head is untied from the embedding.
 """
 from .shapes import SHAPES, ModelShape, TENSORS_PER_LAYER, tensor_names
-from .gen import make_weights, make_prompt, bf16_bits_to_f32, weights_to_numpy
+from .gen import make_weights, make_prompt, bf16_bits_to_f32, weights_to_numpy, LazyF32
 
 __all__ = ["SHAPES", "ModelShape", "TENSORS_PER_LAYER", "tensor_names",
-           "make_weights", "make_prompt", "bf16_bits_to_f32", "weights_to_numpy"]
+           "make_weights", "make_prompt", "bf16_bits_to_f32", "weights_to_numpy", "LazyF32"]

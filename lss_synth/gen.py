@@ -81,8 +81,25 @@ def weights_to_numpy(weights):
     out = {}
     for name, t in weights:
         t = t.detach().to("cpu")
-        if t.dtype == torch.bfloat16:
-            out[name] = bf16_bits_to_f32(t.view(torch.int16).numpy())
-        else:
-            out[name] = t.numpy().astype(np.float32, copy=False)
+        # bf16 -> float32 widening is exact (the 16 low bits become zero)
+        out[name] = t.to(torch.float32).numpy() if t.dtype == torch.bfloat16 else \
+            t.numpy().astype(np.float32, copy=False)
     return out
+
+
+class LazyF32:
+    """Read-only mapping name -> float32 ndarray of a weight list, widened on
+    each access (no copy is kept).  For oracle runs on models too large to
+    hold in float32 at once."""
+
+    def __init__(self, weights):
+        self._w = dict(weights)
+
+    def __getitem__(self, name):
+        return weights_to_numpy([(name, self._w[name])])[name]
+
+    def __contains__(self, name):
+        return name in self._w
+
+    def keys(self):
+        return self._w.keys()

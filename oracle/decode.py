@@ -128,7 +128,7 @@ def forward_row(model, st, tok, pos, mode, skip=None, quant=False):
     return model.head(h), states
 
 
-def prefill(model, tokens, max_seq):
+def prefill(model, tokens, max_seq, progress=None):
     """Causal full-model pass over the prompt, as one block of rows.
 
     Returns (state, logits of the last row, states of the last row).  The
@@ -157,7 +157,7 @@ def prefill(model, tokens, max_seq):
         O = np.empty((P, m.Hq, m.hd), m.dt)
         for hh in range(m.Hq):
             kh = hh // group
-            S = (Q[:, hh] @ K[:, kh].T) / np.sqrt(m.hd)
+            S = (Q[:, hh] @ K[:, kh].T) / m.dt.type(np.sqrt(m.hd))
             S = np.where(causal, S, -np.inf)
             S = S - S.max(axis=1, keepdims=True)
             Pm = np.exp(S)
@@ -168,6 +168,8 @@ def prefill(model, tokens, max_seq):
         A = silu(X @ lw["w_gate"].T) * (X @ lw["w_up"].T)
         H = H + A @ lw["w_down"].T
         last_states.append(H[-1].copy())
+        if progress is not None:
+            progress(l)
     z = m.head(H[-1])
     st.p = P
     st.t0 = argmax_first(z)

@@ -49,7 +49,7 @@ class OracleModel:
     def _get(self, name):
         if self._cache is not None and name in self._cache:
             return self._cache[name]
-        a = np.asarray(self.w[name]).astype(self.dt)
+        a = np.asarray(self.w[name]).astype(self.dt, copy=False)
         if self._cache is not None:
             self._cache[name] = a
         return a
@@ -59,6 +59,8 @@ class OracleModel:
         return {n: self._get(f"layers.{l}.{n}") for n in names}
 
     def embed_row(self, tok):
+        if self._cache is not None:
+            return self._get("embed")[int(tok)]
         return np.asarray(self.w["embed"][int(tok)]).astype(self.dt)
 
     def head(self, h):
@@ -98,7 +100,7 @@ def silu(x):
 
 def attend(q, keys, vals):
     """Softmax attention of one query [hd] over keys/vals [n][hd]."""
-    s = (keys @ q) / np.sqrt(q.shape[-1])
+    s = (keys @ q) / q.dtype.type(np.sqrt(q.shape[-1]))
     s = s - np.max(s)
     p = np.exp(s)
     p = p / np.sum(p)

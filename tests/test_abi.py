@@ -35,11 +35,12 @@ def test_library_exports_every_declared_symbol():
 def test_workspace_size_and_invalid_configs():
     sh = lss_synth.SHAPES["llama3_8b"]
     nb = lss.workspace_bytes(sh, max_seq=1600, max_rows=16)
-    kv = 2 * 32 * 8 * 1600 * 128 * 2
+    kv = 2 * 32 * 8 * 1600 * 128 * 4          # float32 KV cache (default)
     assert kv < nb < kv + 200 * 2**20
+    assert lss.workspace_bytes(sh, max_seq=1600, max_rows=16, kv_dtype="bf16") == nb - kv // 2
     lib = N.load()
     for field, bad in [("head_dim", 96), ("max_rows", 65), ("max_rows", 0), ("d_model", 8208),
-                       ("n_kv_heads", 5), ("dtype", 7), ("max_seq", 1)]:
+                       ("n_kv_heads", 5), ("dtype", 7), ("max_seq", 1), ("kv_dtype", 3)]:
         cfg = lss.make_config(sh, 1600, 16)
         setattr(cfg, field, bad)
         assert lib.lss_workspace_bytes(C.byref(cfg)) == 0, field

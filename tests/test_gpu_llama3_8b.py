@@ -1,0 +1,146 @@
+"""GPU parity at the full Llama-3-8B shape (32 layers, d 4096, 32 q / 8 kv
+heads, FFN 14336, vocab 128256, bf16) in the launch configuration bench.py
+times (1024-token prompt, row blocks of 64, KV capacity 1569).
+
+Against the oracle (float32, on the host): prefill logits and residual
+states, teacher-forced verify logits, the CLaSp DP's skip set (bf16 tolerance
+2e-2 on logits; DP decisions equal unless the oracle's skip/execute cosine
+margin is below 1e-3).  Properties that hold at any size: the GPU's
+speculative output equals its greedy output bit for bit, an empty-mask
+draft is accepted in full, planted identity layers are found exactly."""
+import numpy as np
+import pytest
+
+import lss_synth
+import oracle
+from conftest import oracle_gap
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = lss_synth.SHAPES["llama3_8b"]
+P = 1024
+MAX_SEQ = 1024 + 512 + 33
+TOL = 2e-2
+BENCH_POLICY = {"mode": "dp", "k_max": 8, "n_skip": 16, "interval": 32, "exit_tau": 0.7}
+
+
+@pytest.fixture(scope="module")
+def gpu8b():
+    from layer_skip_self_amd import Engine
+    w = lss_synth.make_weights(SHAPE, device="cuda")
+    eng = Engine(SHAPE, w, max_seq=MAX_SEQ, max_rows=64)
+    prompt = lss_synth.make_prompt(SHAPE, P)
+    yield dict(w=w, eng=eng, prompt=prompt)
+    eng.close()
+
+
+@pytest.fixture(scope="module")
+def oracle8b(gpu8b):
+    import time
+    t = time.time()
+    w_host = [(n, t.to("cpu")) for n, t in gpu8b["w"]]
+    model = oracle.OracleModel(SHAPE, lss_synth.LazyF32(w_host), dtype=np.float32, cache_layers=True)
+    for l in range(SHAPE.n_layers):
+        model.layer(l)
+    model.embed_row(0)
+    model.head(np.ones(SHAPE.d_model, np.float32))
+    print(f"\noracle weights widened in {time.time() - t:.1f} s", flush=True)
+    st, z, states = oracle.prefill(model, gpu8b["prompt"], MAX_SEQ,
+                                   progress=lambda l: print(f"oracle prefill layer {l} {time.time() - t:.1f} s",
+                                                            flush=True))
+    return dict(model=model, st=st, z=z, states=states)
+
+
+def test_speculative_equals_greedy_bitwise_8b(gpu8b):
+    eng, prompt = gpu8b["eng"], gpu8b["prompt"]
+    G = 72
+    ar, _ = eng.generate(prompt, G, {"mode": "ar"})
+    for pol in (BENCH_POLICY,
+                {"mode": "static", "k_max": 8, "skip": tuple(range(1, 32, 2)), "quant": True},
+                {"mode": "cascade", "k_max": 8, "interval": 16, "beta": (1.0, 0.0, 0.1),
+                 "levels": [(22, 4, False), (10, 0, True), (0, 0, True)]}):
+        toks, st = eng.generate(prompt, G, pol)
+        assert toks == ar, pol
+        assert 0 <= st["accepted"] <= st["drafted"]
+
+
+def test_empty_mask_draft_accepted_in_full_8b(gpu8b):
+    eng = gpu8b["eng"]
+    eng.prefill(gpu8b["prompt"])
+    d = eng.draft([0] * SHAPE.n_layers, False, 8)
+    assert len(d) == 8
+    eng.verify(None, 8)
+    n, _, _ = eng.accept()
+    assert n == 8
+
+
+def test_prefill_logits_and_states_vs_oracle_8b(gpu8b, oracle8b):
+    eng = gpu8b["eng"]
+    t0 = eng.prefill(gpu8b["prompt"])
+    z = eng.read_logits(1)[0]
+    err = float(np.max(np.abs(z - oracle8b["z"])))
+    print(f"prefill logits max-abs {err:.3e} (logit std {np.std(oracle8b['z']):.3f})")
+    assert err <= TOL
+    if oracle_gap(oracle8b["z"]) >= 1e-2:
+        assert t0 == int(np.argmax(oracle8b["z"]))
+    hs = eng.read_states((P - 1) % 64)
+    ref = np.stack(oracle8b["states"])
+    serr = float(np.max(np.abs(hs - ref)))
+    print(f"prefill last-row residual states max-abs {serr:.3e} (max |h| {np.max(np.abs(ref)):.3f})")
+    assert serr <= TOL
+
+
+def test_teacher_forced_verify_logits_vs_oracle_8b(gpu8b, oracle8b):
+    """Verify rows [t0, o1, o2, o3] (oracle greedy tokens as host-forced drafts)."""
+    eng, model = gpu8b["eng"], oracle8b["model"]
+    st = oracle8b["st"]
+    t0 = eng.prefill(gpu8b["prompt"])
+    if t0 != st.t0:
+        pytest.skip("first token is a near-tie between the two paths")
+    # oracle greedy continuation with logits (on a copy of the committed cache)
+    import copy
+    so = copy.deepcopy(st)
+    toks, zs = [so.t0], []
+    for _ in range(4):
+        zz, _ = oracle.forward_row(model, so, so.t0, so.p, "full")
+        zs.append(zz)
+        so.p += 1
+        so.t0 = int(np.argmax(zz))
+        toks.append(so.t0)
+    eng.verify(toks[1:4])
+    zg = eng.read_logits(4)
+    eng.accept()
+    for i in range(4):
+        err = float(np.max(np.abs(zg[i] - zs[i])))
+        print(f"verify row {i}: max-abs {err:.3e}")
+        assert err <= TOL
+
+
+def test_dp_skip_set_vs_oracle_8b(gpu8b, oracle8b):
+    eng = gpu8b["eng"]
+    eng.prefill(gpu8b["prompt"])
+    mg, sg = eng.select_layers_dp(16)
+    mo, so, dec = oracle.clasp_dp(oracle8b["model"], oracle8b["st"], 16)
+    margins = sorted(abs(cs - ce) for _, cs, ce in dec.values() if cs is not None and ce is not None)
+    diff = [l for l in range(SHAPE.n_layers) if mg[l] != mo[l]]
+    print(f"DP score gpu {sg:.6f} oracle {so:.6f}; smallest oracle margins {margins[:3]}; "
+          f"gpu skip {[l for l in range(32) if mg[l]]}, oracle skip {[l for l in range(32) if mo[l]]}")
+    assert abs(sg - so) <= 1e-3
+    if margins[0] >= 1e-3:
+        assert not diff
+
+
+def test_dp_finds_planted_identity_layers_8b():
+    from layer_skip_self_amd import Engine
+    planted = tuple(sorted(np.random.default_rng(3).choice(32, 16, replace=False).tolist()))
+    w = lss_synth.make_weights(SHAPE, device="cuda", planted_identity=planted)
+    eng = Engine(SHAPE, w, max_seq=MAX_SEQ, max_rows=64)
+    eng.prefill(lss_synth.make_prompt(SHAPE, P))
+    mask, score = eng.select_layers_dp(16)
+    assert tuple(l for l in range(32) if mask[l]) == planted
+    assert score == pytest.approx(1.0, abs=1e-5)
+    d = eng.draft(mask, False, 8)
+    eng.verify(None, len(d))
+    n, _, _ = eng.accept()
+    assert n == len(d) == 8
+    eng.close()
