@@ -56,14 +56,14 @@ enum lss_dtype { LSS_F32 = 0, LSS_BF16 = 1 };
 
 /* Model and capacity description.  Weights use `dtype`, the KV cache
  * `kv_dtype`; activations and the residual stream are float32.  head_dim must be 64 or
- * 128; n_heads a multiple of n_kv_heads; d_model, ffn_dim and vocab
- * multiples of 16; d_model <= 8192. */
+ * 128; n_heads a multiple of n_kv_heads; d_model and ffn_dim multiples of
+ * 32 (bf16) or 16 (float32), vocab a multiple of 16; d_model <= 8192. */
 typedef struct lss_config {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   float rope_theta; /* rotary base; pairs (i, i + head_dim/2) */
   float rms_eps;    /* RMSNorm epsilon */
   int32_t dtype;    /* lss_dtype */
-  int32_t max_seq;  /* KV capacity in positions (prompt + generated + window) */
+  int32_t max_seq;  /* KV capacity in positions (prompt + generated + window), <= 4096 */
   int32_t max_rows; /* row-block limit, 1..LSS_ROWS_MAX */
   int32_t kv_dtype; /* lss_dtype of the KV cache (float32 keeps keys/values unrounded) */
 } lss_config;

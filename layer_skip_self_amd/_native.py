@@ -2,7 +2,8 @@
 import ctypes as C
 import os
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblss.so")
+_LIB_PATH = os.environ.get("LSS_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                             "liblss.so")
 
 LSS_OK, LSS_EINVAL, LSS_ESTATE, LSS_ECAPACITY, LSS_EHIP, LSS_ENOTIMPL = 0, -1, -2, -3, -4, -5
 LSS_F32, LSS_BF16 = 0, 1

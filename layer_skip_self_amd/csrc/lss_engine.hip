@@ -29,9 +29,9 @@ constexpr int kWinMax = LSS_WINDOW_MAX;
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t kc, vc, hs, hmid, xn, xs, qkv, qrot, selfkv, apart, aout, act, logits, hpart, rope, target,
+  size_t kc, vc, hs, hmid, xa, xb, xc, pa, pc, xs, qkv, apart, actr, aout, act, logits, hpart, rope, target,
       dpg0, dpg1, dpx, dpdec, tok, seqtok, res, total;
-  int xld, nch_max, ntile;
+  int xld, nch_max, nz_max, ntile;
 };
 
 bool cfg_valid(const lss_config* c, std::string* why) {
@@ -42,12 +42,15 @@ bool cfg_valid(const lss_config* c, std::string* why) {
     return fail("non-positive model dimension");
   if (c->head_dim != 64 && c->head_dim != 128) return fail("head_dim must be 64 or 128");
   if (c->n_heads % c->n_kv_heads) return fail("n_heads must be a multiple of n_kv_heads");
-  if (c->d_model % 16 || c->ffn_dim % 16 || c->vocab % 16) return fail("d_model, ffn_dim, vocab must be multiples of 16");
+  // whole 4-vector groups of the projection loop: 32 elements (bf16) / 16 (float32)
+  const int kq = c->dtype == LSS_BF16 ? 32 : 16;
+  if (c->d_model % kq || c->ffn_dim % kq || c->vocab % 16)
+    return fail("d_model, ffn_dim must be multiples of 32 (bf16) / 16 (float32), vocab of 16");
   if (c->d_model > 8192) return fail("d_model > 8192");
   if (c->dtype != LSS_F32 && c->dtype != LSS_BF16) return fail("dtype must be LSS_F32 or LSS_BF16");
   if (c->kv_dtype != LSS_F32 && c->kv_dtype != LSS_BF16) return fail("kv_dtype must be LSS_F32 or LSS_BF16");
   if (c->max_rows < 1 || c->max_rows > LSS_ROWS_MAX) return fail("max_rows out of [1, 64]");
-  if (c->max_seq < 2) return fail("max_seq < 2");
+  if (c->max_seq < 2 || c->max_seq > 4096) return fail("max_seq out of [2, 4096]");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail("bad rms_eps / rope_theta");
   return true;
 }
@@ -59,6 +62,7 @@ Layout make_layout(const lss_config* c) {
   const size_t Hq = c->n_heads, Hkv = c->n_kv_heads, V = c->vocab, NL = c->n_layers;
   L.xld = (int)std::max({d, F, Hq * hd});
   L.nch_max = (c->max_seq + ATT_CH - 1) / ATT_CH;
+  L.nz_max = (int)(((Hq / Hkv) * R + ATT_QB - 1) / ATT_QB);
   L.ntile = (int)((V + 15) / 16);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
@@ -66,12 +70,16 @@ Layout make_layout(const lss_config* c) {
   L.vc = take(NL * Hkv * (size_t)c->max_seq * hd * elt);
   L.hs = take((NL + 1) * R * d * 4);
   L.hmid = take(R * d * 4);
-  L.xn = take(R * L.xld * 4);
+  // projection inputs (4 bytes per element in both formats) and partial sums of squares
+  L.xa = take(R * d * 4);
+  L.xb = take(R * (size_t)std::max(F, Hq * hd) * 4);
+  L.xc = take(R * d * 4);
+  L.pa = take(R * (d / 16) * 4);
+  L.pc = take(R * (d / 16) * 4);
   L.xs = take(R * 4);
   L.qkv = take(R * (Hq + 2 * Hkv) * hd * 4);
-  L.qrot = take(R * Hq * hd * 4);
-  L.selfkv = take(R * 2 * Hkv * hd * 4);
-  L.apart = take(R * Hq * (size_t)L.nch_max * (hd + 2) * 4);
+  L.apart = take(Hkv * (size_t)L.nz_max * L.nch_max * ATT_QB * (hd + 2) * 4);
+  L.actr = take(Hkv * (size_t)L.nz_max * 4);
   L.aout = take(R * Hq * hd * 4);
   L.act = take(R * F * 4);
   L.logits = take(R * V * 4);
@@ -113,8 +121,10 @@ struct lss_engine {
   char* ws = nullptr;
   // device buffers
   void *kc = nullptr, *vc = nullptr;
-  float *hs, *hmid, *xn, *xs, *qkv, *qrot, *selfkv, *apart, *aout, *act, *logits, *hpart, *target, *dpg[2],
-      *dpx, *dpdec;
+  float *hs, *hmid, *xs, *qkv, *apart, *aout, *act, *logits, *hpart, *target, *dpg[2], *dpx, *dpdec;
+  void *xa, *xb, *xc;   // projection inputs: layer input (attention-norm gain), attention / FFN output, mid-layer
+  float *pa, *pc;       // partial sums of squares of the residual rows behind xa and xc
+  int* actr;
   float2* rope;
   int32_t *tok, *seqtok;
   HeadRes* res;
@@ -179,16 +189,21 @@ float* hs_row(lss_engine* e, int l, int m) {
 template <typename WT, int EPI>
 void gemm_mt(const GemmArgs& ga, hipStream_t s) {
   const dim3 grid((ga.N + 15) / 16), block(64 * GEMM_WAVES);
-  const int mt = (ga.M + 15) / 16;
+  const size_t a_lds = (size_t)ga.M * a_lds_ld(ga.K) * 4;
+  const bool alds = ga.M <= 16 && a_lds <= GEMM_A_LDS_MAX;
   if (ga.M == 1) {
-    hipLaunchKernelGGL((k_gemm<WT, 1, EPI, true>), grid, block, 0, s, ga);
+    if (alds) hipLaunchKernelGGL((k_gemm<WT, 1, EPI, true, true>), grid, block, a_lds, s, ga);
+    else hipLaunchKernelGGL((k_gemm<WT, 1, EPI, true, false>), grid, block, 0, s, ga);
     return;
   }
-  switch (mt) {
-    case 1: hipLaunchKernelGGL((k_gemm<WT, 1, EPI, false>), grid, block, 0, s, ga); break;
-    case 2: hipLaunchKernelGGL((k_gemm<WT, 2, EPI, false>), grid, block, 0, s, ga); break;
-    case 3: hipLaunchKernelGGL((k_gemm<WT, 3, EPI, false>), grid, block, 0, s, ga); break;
-    default: hipLaunchKernelGGL((k_gemm<WT, 4, EPI, false>), grid, block, 0, s, ga); break;
+  switch ((ga.M + 15) / 16) {
+    case 1:
+      if (alds) hipLaunchKernelGGL((k_gemm<WT, 1, EPI, false, true>), grid, block, a_lds, s, ga);
+      else hipLaunchKernelGGL((k_gemm<WT, 1, EPI, false, false>), grid, block, 0, s, ga);
+      break;
+    case 2: hipLaunchKernelGGL((k_gemm<WT, 2, EPI, false, false>), grid, block, 0, s, ga); break;
+    case 3: hipLaunchKernelGGL((k_gemm<WT, 3, EPI, false, false>), grid, block, 0, s, ga); break;
+    default: hipLaunchKernelGGL((k_gemm<WT, 4, EPI, false, false>), grid, block, 0, s, ga); break;
   }
 }
 
@@ -219,128 +234,184 @@ void gemm(lss_engine* e, const GemmArgs& ga) {
     const int64_t elt = e->bf16 ? 2 : 4;
     const int64_t nw = (EPI == EPI_SWIGLU) ? 2 : 1;
     e->prof_launches++;
-    e->prof_bytes += nw * (int64_t)ga.N * ga.K * elt + (int64_t)ga.M * ga.K * 4 + (int64_t)ga.M * ga.N * 4 +
+    // weights + activation rows read (4 bytes per element) + rows written (float32 and/or projection input)
+    const int64_t outw = (ga.Y && !(EPI == EPI_SWIGLU && ga.xo) ? 4 : 0) + (ga.xo ? 4 : 0);
+    e->prof_bytes += nw * (int64_t)ga.N * ga.K * elt + (int64_t)ga.M * ga.K * 4 + (int64_t)ga.M * ga.N * outw +
                      (EPI == EPI_RESID ? (int64_t)ga.M * ga.N * 4 : 0);
   }
 }
 
-GemmArgs gemm_args(const void* w, int N, int K, const float* X, int ldx, int M, const float* xs, float* Y,
-                   int ldy) {
+GemmArgs gemm_args(const void* w, int N, int K, const void* A, int lda, int M, float* Y, int ldy) {
   GemmArgs ga{};
   ga.w[0] = w; ga.w[1] = w; ga.w[2] = w;
   ga.nseg[0] = N; ga.nseg[1] = 0; ga.nseg[2] = 0;
-  ga.N = N; ga.K = K; ga.X = X; ga.ldx = ldx; ga.M = M; ga.xs = xs; ga.Y = Y; ga.ldy = ldy;
+  ga.N = N; ga.K = K; ga.A = A; ga.lda = lda; ga.M = M; ga.Y = Y; ga.ldy = ldy;
+  ga.scale = SCALE_NONE;
   return ga;
 }
 
-void rmsnorm(lss_engine* e, const float* h, int M, const float* g, int quant) {
-  const auto& c = e->cfg;
-  hipLaunchKernelGGL(k_rmsnorm<float>, dim3(M), dim3(LSS_NORM_THREADS), 0, e->stream, h, c.d_model, g, c.d_model,
-                     c.rms_eps, e->xn, e->lay.xld, e->xs, quant);
-}
+// projection-format row offset (both formats take 4 bytes per element)
+const void* xrow(const void* x, int ld, int m) { return (const char*)x + (size_t)m * ld * 4; }
 
-template <typename KT>
-void attention(lss_engine* e, int l, int M, int mode, int pos0) {
+template <typename KT, typename WT>
+void attention(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
   const auto& c = e->cfg;
   const int hd = c.head_dim;
   AttnArgs a{};
-  a.kc = kc_layer(e, l);
-  a.vc = vc_layer(e, l);
-  a.max_seq = c.max_seq; a.Hq = c.n_heads; a.Hkv = c.n_kv_heads; a.hd = hd; a.M = M;
-  a.qrot = e->qrot;
-  a.part = e->apart; a.nch_max = e->lay.nch_max;
+  a.qkv = e->qkv; a.ldqkv = (c.n_heads + 2 * c.n_kv_heads) * hd;
+  a.cs = e->rope;
+  a.kc = kc_layer(e, l); a.vc = vc_layer(e, l);
+  a.max_seq = c.max_seq; a.Hq = c.n_heads; a.Hkv = c.n_kv_heads; a.M = M;
+  a.pos0 = pos0; a.pos_step = mode == MODE_DP ? 0 : 1;
+  a.part = e->apart; a.nz_max = e->lay.nz_max; a.nch_max = e->lay.nch_max;
+  a.counters = e->actr;
+  a.out = e->aout;
+  a.xo = quant ? nullptr : e->xb;
   a.scale = (float)(1.0 / std::sqrt((double)hd));
   int kmax;
   if (mode == MODE_CAUSAL) { a.lim_base = pos0 + 1; a.lim_step = 1; a.wbase = 0; a.wmask = 0; kmax = pos0 + M; }
   else if (mode == MODE_DRAFT) { a.lim_base = e->p; a.lim_step = 0; a.wbase = e->p; a.wmask = e->valid[l]; kmax = pos0 + 1; }
-  else { a.lim_base = pos0; a.lim_step = 0; a.wbase = 0; a.wmask = 0; kmax = pos0; }
-  a.nch = (kmax + ATT_CH - 1) / ATT_CH;
+  else { a.lim_base = pos0; a.lim_step = 0; a.wbase = 0; a.wmask = 0; a.self_kv = 1; kmax = pos0; }
+  a.nch = std::max(1, (kmax + ATT_CH - 1) / ATT_CH);
   const int G = c.n_heads / c.n_kv_heads;
-  if (a.nch > 0) {
-    const dim3 grid(a.nch, c.n_kv_heads, (G * M + ATT_QB - 1) / ATT_QB);
-    if (hd == 128) hipLaunchKernelGGL((k_attn_partial<KT, 128>), grid, dim3(ATT_THREADS), 0, e->stream, a);
-    else hipLaunchKernelGGL((k_attn_partial<KT, 64>), grid, dim3(ATT_THREADS), 0, e->stream, a);
-  }
-  const float* self = mode == MODE_DP ? e->selfkv : nullptr;
-  if (hd == 128)
-    hipLaunchKernelGGL(k_attn_combine<128>, dim3(M * c.n_heads), dim3(128), 0, e->stream, e->apart, a.nch,
-                       e->lay.nch_max, c.n_heads, c.n_kv_heads, e->qrot, self, a.scale, e->aout);
+  a.nz = (G * M + ATT_QB - 1) / ATT_QB;
+  const dim3 grid(a.nch, c.n_kv_heads, a.nz);
+  if (hd == 128) hipLaunchKernelGGL((k_attention<KT, WT, 128>), grid, dim3(ATT_THREADS), 0, e->stream, a);
+  else hipLaunchKernelGGL((k_attention<KT, WT, 64>), grid, dim3(ATT_THREADS), 0, e->stream, a);
+}
+
+template <typename WT>
+void attention_w(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
+  if (e->kv16) attention<uint16_t, WT>(e, l, M, mode, pos0, quant);
+  else attention<float, WT>(e, l, M, mode, pos0, quant);
+}
+
+// RMSNorm + int8 codes of M rows of h into the projection input x (quantized drafts)
+void norm_quant(lss_engine* e, const float* h, int M, const float* g, void* x) {
+  const auto& c = e->cfg;
+  if (e->bf16)
+    hipLaunchKernelGGL(k_rmsnorm_quant<uint16_t>, dim3(M), dim3(LSS_NORM_THREADS), 0, e->stream, h, c.d_model, g,
+                       c.d_model, c.rms_eps, x, e->xs);
   else
-    hipLaunchKernelGGL(k_attn_combine<64>, dim3(M * c.n_heads), dim3(64), 0, e->stream, e->apart, a.nch,
-                       e->lay.nch_max, c.n_heads, c.n_kv_heads, e->qrot, self, a.scale, e->aout);
+    hipLaunchKernelGGL(k_rmsnorm_quant<float>, dim3(M), dim3(LSS_NORM_THREADS), 0, e->stream, h, c.d_model, g,
+                       c.d_model, c.rms_eps, x, e->xs);
+}
+
+void quant_rows(lss_engine* e, const float* x, int M, int n, void* xo) {
+  if (e->bf16)
+    hipLaunchKernelGGL(k_quant_rows<uint16_t>, dim3(M), dim3(256), 0, e->stream, x, n, n, xo, e->xs, (int8_t*)nullptr);
+  else
+    hipLaunchKernelGGL(k_quant_rows<float>, dim3(M), dim3(256), 0, e->stream, x, n, n, xo, e->xs, (int8_t*)nullptr);
+}
+
+// projection input + partial sums of squares of M rows of h (row stride d) with gain g
+void prep_rows(lss_engine* e, const float* h, int M, const float* g, void* xo, float* po) {
+  const int d = e->cfg.d_model;
+  if (e->bf16) hipLaunchKernelGGL(k_prep_rows<uint16_t>, dim3(M), dim3(256), 0, e->stream, h, d, d, g, xo, po);
+  else hipLaunchKernelGGL(k_prep_rows<float>, dim3(M), dim3(256), 0, e->stream, h, d, d, g, xo, po);
 }
 
 // One decoder layer on M rows: h_out = layer(h_in).  Rows are consecutive
 // positions pos0.. (causal), the single draft slot at pos0, or all at pos0
-// (layer selection).
-void layer_forward(lss_engine* e, int l, int M, const float* h_in, float* h_out, int mode, int pos0, int quant) {
+// (layer selection).  xa_in / pa_in hold h_in's projection input (attention
+// norm gain) and its partial sums of squares.  g_next != nullptr: also write
+// h_out's projection input with that gain into e->xa / e->pa (rows 0..M-1).
+void layer_forward(lss_engine* e, int l, int M, const float* h_in, const void* xa_in, const float* pa_in,
+                   float* h_out, const float* g_next, int mode, int pos0, int quant) {
   const auto& c = e->cfg;
   const LayerW& w = e->layers[l];
   const int d = c.d_model, F = c.ffn_dim, hd = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
   const int qd = Hq * hd, kvd = Hkv * hd;
-  rmsnorm(e, h_in, M, w.attn_norm, quant);
   {
-    GemmArgs ga = gemm_args(w.wq, qd + 2 * kvd, d, e->xn, e->lay.xld, M, quant ? e->xs : nullptr, e->qkv,
-                            qd + 2 * kvd);
+    GemmArgs ga;
+    if (quant) {
+      norm_quant(e, h_in, M, w.attn_norm, e->xa);
+      ga = gemm_args(w.wq, qd + 2 * kvd, d, e->xa, d, M, e->qkv, qd + 2 * kvd);
+      ga.scale = SCALE_XS; ga.xs = e->xs;
+    } else {
+      ga = gemm_args(w.wq, qd + 2 * kvd, d, xa_in, d, M, e->qkv, qd + 2 * kvd);
+      ga.scale = SCALE_NORM; ga.pin = pa_in; ga.eps = c.rms_eps;
+    }
     ga.w[0] = w.wq; ga.nseg[0] = qd;
     ga.w[1] = w.wk; ga.nseg[1] = kvd;
     ga.w[2] = w.wv; ga.nseg[2] = kvd;
     gemm<EPI_STORE>(e, ga);
   }
-  const int pos_step = mode == MODE_DP ? 0 : 1;
-  float* self = mode == MODE_DP ? e->selfkv : nullptr;
-  if (e->kv16)
-    hipLaunchKernelGGL(k_rope_kv<uint16_t>, dim3(M, Hq + 2 * Hkv), dim3(hd / 2), 0, e->stream, e->qkv,
-                       qd + 2 * kvd, Hq, Hkv, hd, e->rope, pos0, pos_step, e->qrot, (uint16_t*)kc_layer(e, l),
-                       (uint16_t*)vc_layer(e, l), c.max_seq, self);
-  else
-    hipLaunchKernelGGL(k_rope_kv<float>, dim3(M, Hq + 2 * Hkv), dim3(hd / 2), 0, e->stream, e->qkv,
-                       qd + 2 * kvd, Hq, Hkv, hd, e->rope, pos0, pos_step, e->qrot, (float*)kc_layer(e, l),
-                       (float*)vc_layer(e, l), c.max_seq, self);
-  if (e->kv16) attention<uint16_t>(e, l, M, mode, pos0);
-  else attention<float>(e, l, M, mode, pos0);
-  if (quant)
-    hipLaunchKernelGGL(k_quant_rows, dim3(M), dim3(256), 0, e->stream, e->aout, qd, qd, e->xs, (int8_t*)nullptr);
+  if (e->bf16) attention_w<uint16_t>(e, l, M, mode, pos0, quant);
+  else attention_w<float>(e, l, M, mode, pos0, quant);
+  if (quant) quant_rows(e, e->aout, M, qd, e->xb);
   {
-    GemmArgs ga = gemm_args(w.wo, d, qd, e->aout, qd, M, quant ? e->xs : nullptr, e->hmid, d);
+    GemmArgs ga = gemm_args(w.wo, d, qd, e->xb, qd, M, e->hmid, d);
+    if (quant) { ga.scale = SCALE_XS; ga.xs = e->xs; }
     ga.R = h_in; ga.ldr = d;
+    if (!quant) { ga.xo = e->xc; ga.ldo = d; ga.go = w.ffn_norm; ga.po = e->pc; }
     gemm<EPI_RESID>(e, ga);
   }
-  rmsnorm(e, e->hmid, M, w.ffn_norm, quant);
   {
-    GemmArgs ga = gemm_args(w.wg, F, d, e->xn, e->lay.xld, M, quant ? e->xs : nullptr, e->act, F);
+    GemmArgs ga = gemm_args(w.wg, F, d, e->xc, d, M, e->act, F);
+    if (quant) {
+      norm_quant(e, e->hmid, M, w.ffn_norm, e->xc);
+      ga.scale = SCALE_XS; ga.xs = e->xs;
+    } else {
+      ga.scale = SCALE_NORM; ga.pin = e->pc; ga.eps = c.rms_eps;
+      ga.xo = e->xb; ga.ldo = F;
+    }
     ga.w2 = w.wu;
     gemm<EPI_SWIGLU>(e, ga);
   }
-  if (quant)
-    hipLaunchKernelGGL(k_quant_rows, dim3(M), dim3(256), 0, e->stream, e->act, F, F, e->xs, (int8_t*)nullptr);
+  if (quant) quant_rows(e, e->act, M, F, e->xb);
   {
-    GemmArgs ga = gemm_args(w.wd, d, F, e->act, F, M, quant ? e->xs : nullptr, h_out, d);
+    GemmArgs ga = gemm_args(w.wd, d, F, e->xb, F, M, h_out, d);
+    if (quant) { ga.scale = SCALE_XS; ga.xs = e->xs; }
     ga.R = e->hmid; ga.ldr = d;
+    if (g_next) { ga.xo = e->xa; ga.ldo = d; ga.go = g_next; ga.po = e->pa; }
     gemm<EPI_RESID>(e, ga);
   }
 }
 
-// Final norm + LM head on M rows of h (row stride d); per-row argmax and top-1
-// probability land in res->argmax/pmax[row0 + m].
-void head(lss_engine* e, const float* h, int M, int row0) {
+// Final norm + LM head on M rows whose projection input (final-norm gain)
+// and partial sums of squares start at row r0 of e->xa / e->pa; per-row
+// argmax and top-1 probability land in res->argmax/pmax[row0 + m].
+void head(lss_engine* e, int r0, int M, int row0) {
   const auto& c = e->cfg;
-  rmsnorm(e, h, M, e->final_norm, 0);
-  GemmArgs ga = gemm_args(e->lm_head, c.vocab, c.d_model, e->xn, e->lay.xld, M, nullptr, e->logits, c.vocab);
+  GemmArgs ga = gemm_args(e->lm_head, c.vocab, c.d_model, xrow(e->xa, c.d_model, r0), c.d_model, M, e->logits,
+                          c.vocab);
+  ga.scale = SCALE_NORM; ga.pin = e->pa + (size_t)r0 * (c.d_model / 16); ga.eps = c.rms_eps;
   ga.part = e->hpart;
   gemm<EPI_LOGITS>(e, ga);
   hipLaunchKernelGGL(k_head_reduce, dim3(M), dim3(256), 0, e->stream, e->hpart, e->lay.ntile, e->res, row0);
   e->logits_rows = M;
 }
 
-void embed(lss_engine* e, const int32_t* tok_dev, int M, float* h) {
+// embedding rows of tokens tok_dev[0..M) into h, with the projection input
+// for gain g into e->xa / e->pa
+void embed(lss_engine* e, const int32_t* tok_dev, int M, float* h, const float* g) {
   const auto& c = e->cfg;
   if (e->bf16)
     hipLaunchKernelGGL(k_embed<uint16_t>, dim3(M), dim3(256), 0, e->stream, (const uint16_t*)e->embed, tok_dev,
-                       c.d_model, h, c.d_model);
+                       c.d_model, h, g, e->xa, e->pa);
   else
     hipLaunchKernelGGL(k_embed<float>, dim3(M), dim3(256), 0, e->stream, (const float*)e->embed, tok_dev,
-                       c.d_model, h, c.d_model);
+                       c.d_model, h, g, e->xa, e->pa);
+}
+
+// gain of the RMSNorm that consumes the residual after layer l (l = -1: the
+// embedding): the next executed layer's attention norm, else the final norm
+const float* next_gain(const lss_engine* e, const uint8_t* mask, int l) {
+  for (int j = l + 1; j < e->cfg.n_layers; ++j)
+    if (!mask || !mask[j]) return e->layers[j].attn_norm;
+  return e->final_norm;
+}
+
+// a full-model pass of M causal rows at positions pos0.. whose embeddings are
+// tokens tok_dev[0..M): residual stash in hs, projection input of the final
+// residual in e->xa (final-norm gain)
+void forward_rows(lss_engine* e, const int32_t* tok_dev, int M, int pos0) {
+  const int L = e->cfg.n_layers;
+  embed(e, tok_dev, M, hs_row(e, 0, 0), next_gain(e, nullptr, -1));
+  for (int l = 0; l < L; ++l)
+    layer_forward(e, l, M, hs_row(e, l, 0), e->xa, e->pa, hs_row(e, l + 1, 0), next_gain(e, nullptr, l),
+                  MODE_CAUSAL, pos0, 0);
 }
 
 int sync_res(lss_engine* e) {
@@ -396,9 +467,11 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
   char* ws = (char*)workspace;
   e->ws = ws;
   e->kc = ws + lay.kc; e->vc = ws + lay.vc;
-  e->hs = (float*)(ws + lay.hs); e->hmid = (float*)(ws + lay.hmid); e->xn = (float*)(ws + lay.xn);
-  e->xs = (float*)(ws + lay.xs); e->qkv = (float*)(ws + lay.qkv); e->qrot = (float*)(ws + lay.qrot);
-  e->selfkv = (float*)(ws + lay.selfkv); e->apart = (float*)(ws + lay.apart); e->aout = (float*)(ws + lay.aout);
+  e->hs = (float*)(ws + lay.hs); e->hmid = (float*)(ws + lay.hmid);
+  e->xa = ws + lay.xa; e->xb = ws + lay.xb; e->xc = ws + lay.xc;
+  e->pa = (float*)(ws + lay.pa); e->pc = (float*)(ws + lay.pc);
+  e->xs = (float*)(ws + lay.xs); e->qkv = (float*)(ws + lay.qkv);
+  e->apart = (float*)(ws + lay.apart); e->actr = (int*)(ws + lay.actr); e->aout = (float*)(ws + lay.aout);
   e->act = (float*)(ws + lay.act); e->logits = (float*)(ws + lay.logits); e->hpart = (float*)(ws + lay.hpart);
   e->rope = (float2*)(ws + lay.rope); e->target = (float*)(ws + lay.target);
   e->dpg[0] = (float*)(ws + lay.dpg0); e->dpg[1] = (float*)(ws + lay.dpg1); e->dpx = (float*)(ws + lay.dpx);
@@ -463,12 +536,10 @@ int lss_prefill(lss_engine* e, const int32_t* tokens, int32_t n, int32_t* t0_out
   int last_m = 0;
   for (int c0 = 0; c0 < n; c0 += R) {
     const int M = std::min(R, n - c0);
-    embed(e, e->seqtok + c0, M, hs_row(e, 0, 0));
-    for (int l = 0; l < c.n_layers; ++l)
-      layer_forward(e, l, M, hs_row(e, l, 0), hs_row(e, l + 1, 0), MODE_CAUSAL, c0, 0);
+    forward_rows(e, e->seqtok + c0, M, c0);
     last_m = M - 1;
   }
-  head(e, hs_row(e, c.n_layers, last_m), 1, 0);
+  head(e, last_m, 1, 0);
   hipLaunchKernelGGL(k_accept, dim3(1), dim3(1), 0, e->stream, e->res, 0, e->tok);  // tok[0] = argmax
   hipLaunchKernelGGL(k_gather_target, dim3(c.n_layers + 1), dim3(256), 0, e->stream, e->hs, R, c.d_model,
                      (const HeadRes*)nullptr, last_m, e->target);
@@ -502,15 +573,15 @@ int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, floa
   for (int s = 0; s < k; ++s) {
     const int slot = e->win;
     const int pos = e->p + slot;
-    embed(e, e->tok + slot, 1, hs_row(e, 0, 0));
+    embed(e, e->tok + slot, 1, hs_row(e, 0, 0), next_gain(e, mask, -1));
     const float* h = hs_row(e, 0, 0);
     for (int l = 0; l < c.n_layers; ++l) {
       if (mask[l]) continue;
       e->valid[l] |= 1u << slot;
-      layer_forward(e, l, 1, h, hs_row(e, l + 1, 0), MODE_DRAFT, pos, quant);
+      layer_forward(e, l, 1, h, e->xa, e->pa, hs_row(e, l + 1, 0), next_gain(e, mask, l), MODE_DRAFT, pos, quant);
       h = hs_row(e, l + 1, 0);
     }
-    head(e, h, 1, slot);
+    head(e, 0, 1, slot);
     hipLaunchKernelGGL(k_draft_commit, dim3(1), dim3(1), 0, e->stream, e->res, slot, e->tok);
     e->win++;
     done++;
@@ -550,10 +621,8 @@ int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k) {
     HIPCHK(hipMemcpyAsync(e->tok + 1, e->hstage, sizeof(int32_t) * k, hipMemcpyHostToDevice, e->stream));
   }
   const int M = k + 1;
-  embed(e, e->tok, M, hs_row(e, 0, 0));
-  for (int l = 0; l < c.n_layers; ++l)
-    layer_forward(e, l, M, hs_row(e, l, 0), hs_row(e, l + 1, 0), MODE_CAUSAL, e->p, 0);
-  head(e, hs_row(e, c.n_layers, 0), M, 0);
+  forward_rows(e, e->tok, M, e->p);
+  head(e, 0, M, 0);
   hipLaunchKernelGGL(k_accept, dim3(1), dim3(1), 0, e->stream, e->res, k, e->tok);
   hipLaunchKernelGGL(k_gather_target, dim3(c.n_layers + 1), dim3(256), 0, e->stream, e->hs, c.max_rows,
                      c.d_model, (const HeadRes*)e->res, 0, e->target);
@@ -596,16 +665,27 @@ int lss_select_layers_dp(lss_engine* e, int32_t S, int32_t Le, uint8_t* mask_out
   const int tstar = e->target_pos;
   fill_u32(e, e->dpdec, (size_t)(L + 1) * (L + 1) * 3, 0x7fc00000u);
   HIPCHK(hipMemcpyAsync(e->dpg[0], e->target, sizeof(float) * d, hipMemcpyDeviceToDevice, e->stream));
+  if (Le > 0) prep_rows(e, e->dpg[0], 1, e->layers[0].attn_norm, e->xa, e->pa);
+  const int T = d / 16;
   int cur = 0;
   for (int i = 1; i <= Le; ++i) {
     const int lo_p = lo(i - 1), hi_p = hi(i - 1), lo_i = lo(i), hi_i = hi(i);
     const int ex_lo = std::max(lo_i, lo_p), ex_hi = std::min(hi_i, hi_p);
     const int ne = ex_hi - ex_lo + 1;
+    const int off = ex_lo - lo_p;     // first executed row among the stage's input rows
     if (ne > 0)
-      layer_forward(e, i - 1, ne, e->dpg[cur] + (size_t)(ex_lo - lo_p) * d, e->dpx, MODE_DP, tstar, 0);
-    hipLaunchKernelGGL(k_dp_select, dim3(hi_i - lo_i + 1), dim3(256), 0, e->stream, e->dpx, ex_lo, ex_hi,
-                       e->dpg[cur], lo_p, hi_p, e->target + (size_t)i * d, d, lo_i, e->dpg[cur ^ 1],
-                       e->dpdec + (size_t)i * (L + 1) * 3);
+      layer_forward(e, i - 1, ne, e->dpg[cur] + (size_t)off * d, xrow(e->xa, d, off), e->pa + (size_t)off * T,
+                    e->dpx, nullptr, MODE_DP, tstar, 0);
+    const float* g = i < Le ? e->layers[i].attn_norm : nullptr;
+    void* xo = i < Le ? e->xa : nullptr;
+    if (e->bf16)
+      hipLaunchKernelGGL(k_dp_select<uint16_t>, dim3(hi_i - lo_i + 1), dim3(256), 0, e->stream, e->dpx, ex_lo, ex_hi,
+                         e->dpg[cur], lo_p, hi_p, e->target + (size_t)i * d, d, lo_i, e->dpg[cur ^ 1],
+                         e->dpdec + (size_t)i * (L + 1) * 3, g, xo, e->pa);
+    else
+      hipLaunchKernelGGL(k_dp_select<float>, dim3(hi_i - lo_i + 1), dim3(256), 0, e->stream, e->dpx, ex_lo, ex_hi,
+                         e->dpg[cur], lo_p, hi_p, e->target + (size_t)i * d, d, lo_i, e->dpg[cur ^ 1],
+                         e->dpdec + (size_t)i * (L + 1) * 3, g, xo, e->pa);
     cur ^= 1;
   }
   int rc = check_launch(e, "select_layers_dp");
@@ -662,7 +742,7 @@ int lss_op_quantize_rows(const float* x, int32_t rows, int32_t n, int8_t* q, flo
       hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, (hipStream_t)stream, (uint32_t*)scale, (size_t)rows, 0u);
     return hipGetLastError() == hipSuccess ? LSS_OK : LSS_EHIP;
   }
-  hipLaunchKernelGGL(k_quant_rows, dim3(rows), dim3(256), 0, (hipStream_t)stream, const_cast<float*>(x), n, n,
+  hipLaunchKernelGGL(k_quant_rows<float>, dim3(rows), dim3(256), 0, (hipStream_t)stream, x, n, n, (void*)nullptr,
                      scale, q);
   return hipGetLastError() == hipSuccess ? LSS_OK : LSS_EHIP;
 }

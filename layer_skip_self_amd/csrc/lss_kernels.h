@@ -16,7 +16,6 @@ namespace lss {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------- scalars
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -39,6 +38,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// fixed-order sum over the 16 lanes of a lane group
+__device__ __forceinline__ float sum16(float v) {
+  for (int o = 8; o >= 1; o >>= 1) v = __fadd_rn(v, __shfl_xor(v, o, 16));
   return v;
 }
 // Block-wide sum in a fixed order (wave tree, then waves in index order).
@@ -64,6 +68,32 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return t;
 }
 
+// ---------------------------------------------------------------- projection input format
+// The activation operand of every projection is written once, by the kernel
+// that produces it, in the layout the MFMA loop reads:
+//   bf16 weights: blocks of 8 elements {8 x bf16 hi, 8 x bf16 lo} with
+//     hi = bf16(x), lo = bf16(x - hi) (exact: x - hi is representable), so the
+//     activation keeps ~16 significant bits; a row of K elements is 4K bytes;
+//   float32 weights: plain float32.
+// Inputs of RMSNorm'd projections are stored already multiplied by the norm
+// gain, together with per-16-column partial sums of squares of the raw row;
+// the projection applies 1/sqrt(mean + eps) per row in its epilogue.
+template <typename WT> struct AF;
+template <> struct AF<uint16_t> {
+  static __device__ __forceinline__ void store(void* xa, size_t row_off, int n, float x) {
+    uint16_t* b = reinterpret_cast<uint16_t*>(xa) + 2 * row_off + (size_t)(n >> 3) * 16 + (n & 7);
+    const uint16_t hb = f2bf(x);
+    b[0] = hb;
+    b[8] = f2bf(__fsub_rn(x, bf2f(hb)));
+  }
+  // element n of row row_off (for the layer-selection copies)
+};
+template <> struct AF<float> {
+  static __device__ __forceinline__ void store(void* xa, size_t row_off, int n, float x) {
+    reinterpret_cast<float*>(xa)[row_off + n] = x;
+  }
+};
+
 // ---------------------------------------------------------------- small kernels
 __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -71,17 +101,41 @@ __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
   for (; i < n; i += stride) p[i] = v;
 }
 
-// h[m][:] = E[tok[m]][:]  (float32 residual stream)
+// Projection input of rows h[m][0..d): xo = h * g (g == nullptr: h) in the
+// projection format, po[m][t] = sum of h^2 over columns 16t..16t+15.
+// One block of 256 threads per row.
 template <typename WT>
-__global__ void k_embed(const WT* __restrict__ E, const int32_t* __restrict__ tok, int d,
-                        float* __restrict__ h, int ldh) {
-  const int m = blockIdx.x;
-  const size_t row = (size_t)tok[m] * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) h[(size_t)m * ldh + i] = ld_elem<WT>(E, row + i);
+__device__ __forceinline__ void prep_row(const float* h, int d, const float* g, void* xo, float* po, int m) {
+  for (int i0 = 0; i0 < d; i0 += blockDim.x) {
+    const int i = i0 + threadIdx.x;          // d is a multiple of 16: whole tiles per pass
+    const float v = (i < d) ? h[i] : 0.f;
+    if (i < d && xo) AF<WT>::store(xo, (size_t)m * d, i, g ? __fmul_rn(v, g[i]) : v);
+    const float s = sum16(__fmul_rn(v, v));
+    if (po && i < d && (i & 15) == 0) po[(size_t)m * (d >> 4) + (i >> 4)] = s;
+  }
 }
 
-// Symmetric per-token int8 codes of n values held by this thread group.
-// inv = fl32(127 / amax) (correctly rounded), q = clamp(rint(x * inv), +-127).
+template <typename WT>
+__global__ void k_prep_rows(const float* __restrict__ h, int ldh, int d, const float* __restrict__ g, void* xo,
+                            float* __restrict__ po) {
+  const int m = blockIdx.x;
+  prep_row<WT>(h + (size_t)m * ldh, d, g, xo, po, m);
+}
+
+// h[m][:] = E[tok[m]][:] (float32 residual stream) and its projection input.
+template <typename WT>
+__global__ void k_embed(const WT* __restrict__ E, const int32_t* __restrict__ tok, int d, float* __restrict__ h,
+                        const float* __restrict__ g, void* xo, float* __restrict__ po) {
+  const int m = blockIdx.x;
+  const size_t row = (size_t)tok[m] * d;
+  float* hr = h + (size_t)m * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) hr[i] = ld_elem<WT>(E, row + i);
+  __syncthreads();
+  prep_row<WT>(hr, d, g, xo, po, m);
+}
+
+// Symmetric per-token int8 codes: inv = fl32(127 / amax) (correctly rounded),
+// q = clamp(rint(x * inv), +-127).
 __device__ __forceinline__ float quant_code(float x, float inv) {
   float q = rintf(__fmul_rn(x, inv));
   return fminf(fmaxf(q, -127.f), 127.f);
@@ -90,14 +144,13 @@ __device__ __forceinline__ float quant_code(float x, float inv) {
 #define LSS_NORM_THREADS 256
 #define LSS_NORM_PER_THREAD 32   // d_model <= 8192
 
-// RMSNorm of rows of h: x = h / sqrt(mean(h^2) + eps) * g, optionally
-// followed by int8 quantization (x replaced by its integer codes, xs[m] =
-// amax/127).  Without quantization xs[m] = 1.
-template <typename GT>
-__global__ __launch_bounds__(LSS_NORM_THREADS) void k_rmsnorm(const float* __restrict__ h, int ldh,
-                                                              const GT* __restrict__ g, int d, float eps,
-                                                              float* __restrict__ x, int ldx,
-                                                              float* __restrict__ xs, int quant) {
+// RMSNorm + dynamic int8 quantization of rows of h (the quantized draft):
+// x = h / sqrt(mean(h^2) + eps) * g; codes of x in the projection format,
+// xs[m] = amax / 127.
+template <typename WT>
+__global__ __launch_bounds__(LSS_NORM_THREADS) void k_rmsnorm_quant(const float* __restrict__ h, int ldh,
+                                                                    const float* __restrict__ g, int d, float eps,
+                                                                    void* xo, float* __restrict__ xs) {
   __shared__ float red[LSS_NORM_THREADS / 64];
   const int m = blockIdx.x;
   const float* hr = h + (size_t)m * ldh;
@@ -115,37 +168,29 @@ __global__ __launch_bounds__(LSS_NORM_THREADS) void k_rmsnorm(const float* __res
 #pragma unroll
   for (int j = 0; j < LSS_NORM_PER_THREAD; ++j) {
     const int i = threadIdx.x + j * LSS_NORM_THREADS;
-    if (i < d) v[j] = __fmul_rn(__fmul_rn(v[j], rstd), ld_elem<GT>(g, i));
+    if (i < d) v[j] = __fmul_rn(__fmul_rn(v[j], rstd), g[i]);
     amax = fmaxf(amax, fabsf(v[j]));
-  }
-  float* xr = x + (size_t)m * ldx;
-  if (!quant) {
-#pragma unroll
-    for (int j = 0; j < LSS_NORM_PER_THREAD; ++j) {
-      const int i = threadIdx.x + j * LSS_NORM_THREADS;
-      if (i < d) xr[i] = v[j];
-    }
-    if (threadIdx.x == 0) xs[m] = 1.0f;
-    return;
   }
   amax = block_max(amax, red);
   const float inv = amax > 0.f ? __fdiv_rn(127.0f, amax) : 0.f;
 #pragma unroll
   for (int j = 0; j < LSS_NORM_PER_THREAD; ++j) {
     const int i = threadIdx.x + j * LSS_NORM_THREADS;
-    if (i < d) xr[i] = quant_code(v[j], inv);
+    if (i < d) AF<WT>::store(xo, (size_t)m * d, i, quant_code(v[j], inv));
   }
   if (threadIdx.x == 0) xs[m] = __fdiv_rn(amax, 127.0f);
 }
 
-// In-place int8 quantization of rows x[m][0..n) (codes as float, or into q8),
-// scale -> xs[m].  Used for the attention output and the SwiGLU output of a
-// quantized draft layer, and by the stand-alone quantization entry point.
-__global__ __launch_bounds__(256) void k_quant_rows(float* __restrict__ x, int ldx, int n,
+// Dynamic int8 quantization of float32 rows x[m][0..n): codes in the
+// projection format (xo) or as int8 (q8, the stand-alone entry point),
+// scale -> xs[m].  Used for the attention and SwiGLU outputs of a quantized
+// draft layer.
+template <typename WT>
+__global__ __launch_bounds__(256) void k_quant_rows(const float* __restrict__ x, int ldx, int n, void* xo,
                                                    float* __restrict__ xs, int8_t* __restrict__ q8) {
   __shared__ float red[4];
   const int m = blockIdx.x;
-  float* xr = x + (size_t)m * ldx;
+  const float* xr = x + (size_t)m * ldx;
   float amax = 0.f;
   for (int i = threadIdx.x; i < n; i += blockDim.x) amax = fmaxf(amax, fabsf(xr[i]));
   amax = block_max(amax, red);
@@ -153,7 +198,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(float* __restrict__ x, int l
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const float q = quant_code(xr[i], inv);
     if (q8) q8[(size_t)m * n + i] = (int8_t)q;
-    else xr[i] = q;
+    else AF<WT>::store(xo, (size_t)m * n, i, q);
   }
   if (threadIdx.x == 0) xs[m] = __fdiv_rn(amax, 127.0f);
 }
@@ -161,169 +206,260 @@ __global__ __launch_bounds__(256) void k_quant_rows(float* __restrict__ x, int l
 // ---------------------------------------------------------------- small-M MFMA GEMM
 // Y[m][n] = sum_k X[m][k] * W[n][k] for m < M <= 16*MT, weights row-major
 // [N][K] streamed once from HBM.  One workgroup = one 16-column tile of N and
-// GEMM_WAVES waves that split K into fixed contiguous ranges; the waves'
-// partial tiles are summed in LDS in wave order.  The K split, the per-lane
-// k assignment and the MFMA sequence depend only on K, so row m's result is
-// the same for every M (rows are independent MFMA rows; padding rows are 0).
+// GEMM_WAVES waves that split K into fixed contiguous ranges of whole steps;
+// the waves' partial tiles are summed in LDS in wave order.  The K split,
+// the per-lane k assignment and the MFMA sequence depend only on K, so row
+// m's result is the same for every M (rows are independent MFMA rows;
+// padding rows only produce discarded outputs).
 //
 // MFMA operand use (16x16x32 bf16 / 16x16x4 f32): lane l supplies A row
 // (l & 15) = activation row, B column (l & 15) = weight row, over a k group
 // chosen by (l >> 4).  Because a dot product does not depend on which k a
-// lane holds as long as A and B agree, each lane reads 4 consecutive 16-byte
-// vectors of its weight row (64 contiguous bytes; 256 bytes per row per
-// wave step), the activation values at the same k, and feeds them to 4 (bf16)
-// or 16 (f32) MFMAs.  bf16 weights: the float32 activation is split into
-// hi = bf16(x) and lo = bf16(x - hi) and both are multiplied (two MFMAs), so
-// the activation keeps ~16 significant bits; int8 codes are exact in hi.
-#define GEMM_WAVES 8
+// lane holds as long as A and B agree, the k of a wave step are assigned so
+// that each load instruction reads 64 contiguous bytes of each of the 16
+// weight rows (the four lanes of a row take consecutive 16-byte vectors);
+// four such loads cover 256 contiguous bytes per row.  With bf16 weights each
+// 8-element vector meets the activation's hi and lo parts (two MFMAs), with
+// float32 weights each 4-element vector feeds four MFMAs.
+//
+// The loop body has no branches on loaded data and no masking of loaded
+// values: addresses are clamped into the row, steps past K are skipped with
+// a wave-uniform test, so the compiler's wait before each MFMA covers only
+// the oldest step while GEMM_D - 1 later steps stay in flight.
+#ifndef GEMM_WAVES
+#define GEMM_WAVES 4
+#endif
 #define GEMM_U 4
+#ifndef GEMM_D
+#define GEMM_D 2   // weight steps in flight per wave
+#endif
 
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+enum { SCALE_NONE = 0, SCALE_NORM = 1, SCALE_XS = 2 };
 
 struct GemmArgs {
   const void* w[3];      // weight segments stacked along N
   int nseg[3];           // rows per segment (multiples of 16)
   const void* w2;        // SWIGLU: up-projection weights [N][K]
   int N, K;
-  const float* X; int ldx; int M;
-  const float* xs;       // per-row scale of X (int8 codes) or nullptr
-  float* Y; int ldy;
+  const void* A; int lda; int M;   // activations in the projection format
+  int scale;             // SCALE_*: per-row output scale
+  const float* pin;      // SCALE_NORM: partial sums of squares [M][K/16]
+  float eps;
+  const float* xs;       // SCALE_XS: int8 scale per row
+  float* Y; int ldy;     // float32 output (STORE, RESID, LOGITS; SWIGLU when xo == null)
   const float* R; int ldr;  // RESID: residual input
+  void* xo; int ldo;     // projection-format output of the result (RESID: times go)
+  const float* go;       // RESID: gain of the next RMSNorm (nullptr: 1)
+  float* po;             // RESID: partial sums of squares of Y [M][N/16]
   float* part;           // LOGITS: per (row, tile) {max, argmax bits, sum exp}
 };
 
 template <typename WT> struct WTr;
-template <> struct WTr<uint16_t> { static constexpr int EPL = 8; };  // bf16: 8 per 16 bytes
-template <> struct WTr<float> { static constexpr int EPL = 4; };
-
-__device__ __forceinline__ void split_bf16(const float* v, bf16x8_t& hi, bf16x8_t& lo) {
-  u16x8 h, l;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint16_t hb = f2bf(v[e]);
-    h[e] = hb;
-    l[e] = f2bf(__fsub_rn(v[e], bf2f(hb)));
-  }
-  hi = __builtin_bit_cast(bf16x8_t, h);
-  lo = __builtin_bit_cast(bf16x8_t, l);
-}
+template <> struct WTr<uint16_t> { static constexpr int EPL = 8, ANV = 2; };  // bf16: hi + lo vectors
+template <> struct WTr<float> { static constexpr int EPL = 4, ANV = 1; };
 
 template <typename WT, int MT>
-__device__ __forceinline__ void gemm_step(const uint4 (&w)[GEMM_U], const float (&a)[MT][GEMM_U][WTr<WT>::EPL],
-                                          f32x4 (&acc)[MT]) {
-  if constexpr (sizeof(WT) == 2) {
+__device__ __forceinline__ void gemm_step(const uint4 (&w)[GEMM_U], const uint4 (&a)[MT][GEMM_U][WTr<WT>::ANV],
+                                          f32x4 (&acc)[MT], int kstep, int K) {
+  constexpr int EPL = WTr<WT>::EPL;
 #pragma unroll
-    for (int u = 0; u < GEMM_U; ++u) {
+  for (int u = 0; u < GEMM_U; ++u) {
+    if (kstep + u * 4 * EPL >= K) break;       // wave-uniform: past the end of K
+    if constexpr (sizeof(WT) == 2) {
       const bf16x8_t b = __builtin_bit_cast(bf16x8_t, w[u]);
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        bf16x8_t hi, lo;
-        split_bf16(a[t][u], hi, lo);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[t][u][0]), b, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[t][u][1]), b, acc[t], 0, 0, 0);
       }
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < GEMM_U; ++u) {
+    } else {
       const float wf[4] = {__uint_as_float(w[u].x), __uint_as_float(w[u].y), __uint_as_float(w[u].z),
                            __uint_as_float(w[u].w)};
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int t = 0; t < MT; ++t) {
+        const float af[4] = {__uint_as_float(a[t][u][0].x), __uint_as_float(a[t][u][0].y),
+                             __uint_as_float(a[t][u][0].z), __uint_as_float(a[t][u][0].w)};
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t][u][e], wf[e], acc[t], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[e], wf[e], acc[t], 0, 0, 0);
+      }
     }
   }
 }
 
 template <typename WT>
-__device__ __forceinline__ void load_w(uint4 (&w)[GEMM_U], const WT* row, int kb, int K, bool ok) {
+__device__ __forceinline__ void load_w(uint4 (&w)[GEMM_U], const WT* row, int kb, int K) {
+  constexpr int EPL = WTr<WT>::EPL;
+#pragma unroll
+  for (int u = 0; u < GEMM_U; ++u) w[u] = *reinterpret_cast<const uint4*>(row + min(kb + u * 4 * EPL, K - EPL));
+}
+
+// activation vectors of one row (row pointer in format units) for step kb
+template <typename WT>
+__device__ __forceinline__ void load_a(uint4 (&a)[GEMM_U][WTr<WT>::ANV], const void* arow, int kb, int K) {
   constexpr int EPL = WTr<WT>::EPL;
 #pragma unroll
   for (int u = 0; u < GEMM_U; ++u) {
-    const int k = kb + u * EPL;
-    if (ok && k < K) w[u] = *reinterpret_cast<const uint4*>(row + k);
-    else w[u] = make_uint4(0, 0, 0, 0);
-  }
-}
-
-template <typename WT, int MT>
-__device__ __forceinline__ void load_a(float (&a)[MT][GEMM_U][WTr<WT>::EPL], const float* X, int ldx, int M,
-                                       int r, int kb, int K) {
-  constexpr int EPL = WTr<WT>::EPL;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int m = t * 16 + r;
-#pragma unroll
-    for (int u = 0; u < GEMM_U; ++u) {
-      const int k = kb + u * EPL;
-      if (m < M && k < K) {
-        const float4* p = reinterpret_cast<const float4*>(X + (size_t)m * ldx + k);
-#pragma unroll
-        for (int e4 = 0; e4 < EPL / 4; ++e4) {
-          const float4 f = p[e4];
-          a[t][u][e4 * 4 + 0] = f.x; a[t][u][e4 * 4 + 1] = f.y;
-          a[t][u][e4 * 4 + 2] = f.z; a[t][u][e4 * 4 + 3] = f.w;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) a[t][u][e] = 0.f;
-      }
+    const int k = min(kb + u * 4 * EPL, K - EPL);
+    if constexpr (sizeof(WT) == 2) {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(arow) + (size_t)(k >> 3) * 16);
+      a[u][0] = p[0];
+      a[u][1] = p[1];
+    } else {
+      a[u][0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(arow) + k);
     }
   }
 }
 
+// Activation rows staged in LDS (ALDS launches): rows of M x K elements
+// (4 bytes each) copied with direct-to-LDS loads in 1 KB chunks; row stride
+// a_lds_ld(K) elements (chunk-rounded, plus 8 elements so rows start on
+// different banks).
+#define GEMM_A_LDS_MAX 65536
+__host__ __device__ __forceinline__ int a_lds_ld(int K) { return ((K + 255) & ~255) + 8; }
+
+template <typename WT>
+__device__ __forceinline__ const void* a_row(const void* A, int lda, int m) {
+  return sizeof(WT) == 2 ? (const void*)(reinterpret_cast<const uint16_t*>(A) + 2 * (size_t)m * lda)
+                         : (const void*)(reinterpret_cast<const float*>(A) + (size_t)m * lda);
+}
+
 // ONE = the launch has exactly one row (draft steps, greedy steps): the same
 // arithmetic as MT = 1, compiled separately so profiles attribute it apart.
-template <typename WT, int MT, int EPI, bool ONE>
+template <typename WT, int MT, int EPI, bool ONE, bool ALDS>
 __global__ __launch_bounds__(64 * GEMM_WAVES) void k_gemm(GemmArgs ga) {
   constexpr int EPL = WTr<WT>::EPL;
+  constexpr int ANV = WTr<WT>::ANV;
   constexpr int KS = 4 * EPL * GEMM_U;  // k per wave step
   constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
+  constexpr bool APRE = MT == 1 && !ALDS;   // activations prefetched with the weights
+  extern __shared__ uint4 a_s[];             // ALDS: staged activation rows
   __shared__ float red[NACC][MT][GEMM_WAVES][64][4];
+  __shared__ float rstd_s[MT * 16];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16;
+  const int M = ONE ? 1 : ga.M;
+  const int K = ga.K;
   // weight segment of this tile
   int seg = 0, nloc = n0;
   while (seg < 2 && nloc >= ga.nseg[seg]) { nloc -= ga.nseg[seg]; ++seg; }
   const bool row_ok = (n0 + r) < ga.N;
-  const WT* wrow = reinterpret_cast<const WT*>(ga.w[seg]) + (size_t)(row_ok ? nloc + r : 0) * ga.K;
-  const WT* wrow2 = (EPI == EPI_SWIGLU)
-                        ? reinterpret_cast<const WT*>(ga.w2) + (size_t)(row_ok ? n0 + r : 0) * ga.K
-                        : nullptr;
-  const int K = ga.K;
+  const WT* wrow = reinterpret_cast<const WT*>(ga.w[seg]) + (size_t)(row_ok ? nloc + r : 0) * K;
+  const WT* wrow2 = (EPI == EPI_SWIGLU) ? reinterpret_cast<const WT*>(ga.w2) + (size_t)(row_ok ? n0 + r : 0) * K
+                                        : nullptr;
   const int nsteps = (K + KS - 1) / KS;
-  const int s0 = (wave * nsteps) / GEMM_WAVES, s1 = ((wave + 1) * nsteps) / GEMM_WAVES;
+  int S_w = (nsteps + GEMM_WAVES - 1) / GEMM_WAVES;
+  S_w = (S_w + GEMM_D - 1) / GEMM_D * GEMM_D;
+  const int s0 = wave * S_w;
+  const int kg = g * EPL;                    // this lane's offset inside a step
+
+  // RMSNorm scale: partial sums of squares, loads issued first (in order)
+  constexpr int PV = 8;                      // partials per lane per row: K/16/64 <= 8 (K <= 8192)
+  constexpr int RPW = (MT * 16 + GEMM_WAVES - 1) / GEMM_WAVES;   // rows per wave
+  float pr[RPW][PV];
+  const bool norm = ga.scale == SCALE_NORM;
+  const int T = K >> 4;
+  if (norm) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int m = min(wave + i * GEMM_WAVES, M - 1);
+#pragma unroll
+      for (int j = 0; j < PV; ++j) {
+        const int t = lane + j * 64;
+        pr[i][j] = ga.pin[(size_t)m * T + min(t, T - 1)];
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // weights (and activations) of the first GEMM_D steps
+  uint4 wb[GEMM_D][NACC][GEMM_U];
+  uint4 ab[APRE ? GEMM_D : 1][1][GEMM_U][ANV];
+  const void* arow0 = a_row<WT>(ga.A, ga.lda, r < M ? r : 0);
+#pragma unroll
+  for (int d = 0; d < GEMM_D; ++d) {
+    const int kb = (s0 + d) * KS + kg;
+    load_w<WT>(wb[d][0], wrow, kb, K);
+    if constexpr (NACC == 2) load_w<WT>(wb[d][1], wrow2, kb, K);
+    if constexpr (APRE) load_a<WT>(ab[d][0], arow0, kb, K);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int ald = a_lds_ld(K);
+  if constexpr (ALDS) {
+    // copy rows [0, M) of A into LDS, 1 KB chunks, wave w takes chunks w, w + GEMM_WAVES, ...
+    const int cpr = (K + 255) >> 8;          // chunks per row
+    for (int c = wave; c < M * cpr; c += GEMM_WAVES) {
+      const int m = c / cpr, kc = (c - m * cpr) << 8;
+      const int k = min(kc + lane * 4, K - 4);
+      const char* src = reinterpret_cast<const char*>(ga.A) + ((size_t)m * ga.lda + k) * 4;
+      char* dst = reinterpret_cast<char*>(a_s) + ((size_t)m * ald + kc) * 4;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                       (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (norm) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int m = wave + i * GEMM_WAVES;
+      float v = 0.f;
+#pragma unroll
+      for (int j = 0; j < PV; ++j)
+        if (lane + j * 64 < T) v = __fadd_rn(v, pr[i][j]);
+      v = wave_sum(v);
+      if (lane == 0 && m < MT * 16)
+        rstd_s[m] = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(v, (float)K), ga.eps)));
+    }
+  }
 
   f32x4 acc[NACC][MT];
 #pragma unroll
-  for (int q = 0; q < NACC; ++q)
+  for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (s0 < s1) {
-    uint4 wc[NACC][GEMM_U], wn[NACC][GEMM_U];
-    float ac[MT][GEMM_U][EPL];
-    int kb = s0 * KS + g * EPL * GEMM_U;
-    load_w<WT>(wc[0], wrow, kb, K, row_ok);
-    if constexpr (NACC == 2) load_w<WT>(wc[1], wrow2, kb, K, row_ok);
-    for (int s = s0; s < s1; ++s) {
-      load_a<WT, MT>(ac, ga.X, ga.ldx, ONE ? 1 : ga.M, r, kb, K);
-      const int kn = kb + KS;
-      if (s + 1 < s1) {
-        load_w<WT>(wn[0], wrow, kn, K, row_ok);
-        if constexpr (NACC == 2) load_w<WT>(wn[1], wrow2, kn, K, row_ok);
+    for (int q = 0; q < NACC; ++q) acc[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < S_w; i += GEMM_D) {
+#pragma unroll
+    for (int d = 0; d < GEMM_D; ++d) {
+      const int s = s0 + i + d;
+      const int kb = s * KS + kg;
+      const int kstep = s * KS;
+      if constexpr (APRE) {
+        gemm_step<WT, MT>(wb[d][0], ab[d], acc[0], kstep, K);
+        if constexpr (NACC == 2) gemm_step<WT, MT>(wb[d][1], ab[d], acc[1], kstep, K);
+      } else if constexpr (ALDS) {
+        uint4 a[MT][GEMM_U][ANV];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int m = t * 16 + r;
+          const char* rowp = reinterpret_cast<const char*>(a_s) + (size_t)(m < M ? m : 0) * ald * 4;
+#pragma unroll
+          for (int u = 0; u < GEMM_U; ++u) {
+            const int k = min(kb + u * 4 * EPL, K - EPL);
+            const uint4* q = reinterpret_cast<const uint4*>(rowp + (size_t)k * 4);
+            a[t][u][0] = q[0];
+            if constexpr (ANV == 2) a[t][u][1] = q[1];
+          }
+        }
+        gemm_step<WT, MT>(wb[d][0], a, acc[0], kstep, K);
+        if constexpr (NACC == 2) gemm_step<WT, MT>(wb[d][1], a, acc[1], kstep, K);
+      } else {
+        uint4 a[MT][GEMM_U][ANV];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int m = t * 16 + r;
+          load_a<WT>(a[t], a_row<WT>(ga.A, ga.lda, m < M ? m : 0), kb, K);
+        }
+        gemm_step<WT, MT>(wb[d][0], a, acc[0], kstep, K);
+        if constexpr (NACC == 2) gemm_step<WT, MT>(wb[d][1], a, acc[1], kstep, K);
       }
-      gemm_step<WT, MT>(wc[0], ac, acc[0]);
-      if constexpr (NACC == 2) gemm_step<WT, MT>(wc[1], ac, acc[1]);
-#pragma unroll
-      for (int q = 0; q < NACC; ++q)
-#pragma unroll
-        for (int u = 0; u < GEMM_U; ++u) wc[q][u] = wn[q][u];
-      kb = kn;
+      // refill this buffer with step s + GEMM_D (past the wave's range: a clamped dummy)
+      const int kn = (i + d + GEMM_D < S_w) ? kb + GEMM_D * KS : K;
+      load_w<WT>(wb[d][0], wrow, kn, K);
+      if constexpr (NACC == 2) load_w<WT>(wb[d][1], wrow2, kn, K);
+      if constexpr (APRE) load_a<WT>(ab[d][0], arow0, kn, K);
     }
   }
 #pragma unroll
@@ -350,18 +486,32 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void k_gemm(GemmArgs ga) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int m = t * 16 + 4 * g + j;
-    const bool ok = (m < ga.M) && (n < ga.N);
-    float y = v[0][j];
-    if (ga.xs && m < ga.M) y = __fmul_rn(y, ga.xs[m]);
+    const bool ok = (m < M) && (n < ga.N);
+    float sc = 1.0f;
+    bool scaled = false;
+    if (m < M) {
+      if (norm) { sc = rstd_s[m]; scaled = true; }
+      else if (ga.scale == SCALE_XS) { sc = ga.xs[m]; scaled = true; }
+    }
+    float y = scaled ? __fmul_rn(v[0][j], sc) : v[0][j];
     if constexpr (EPI == EPI_STORE) {
       if (ok) ga.Y[(size_t)m * ga.ldy + n] = y;
     } else if constexpr (EPI == EPI_RESID) {
-      if (ok) ga.Y[(size_t)m * ga.ldy + n] = __fadd_rn(ga.R[(size_t)m * ga.ldr + n], y);
+      const float h = ok ? __fadd_rn(ga.R[(size_t)m * ga.ldr + n], y) : 0.f;
+      if (ok) ga.Y[(size_t)m * ga.ldy + n] = h;
+      if (ga.xo && ok) AF<WT>::store(ga.xo, (size_t)m * ga.ldo, n, ga.go ? __fmul_rn(h, ga.go[n]) : h);
+      if (ga.po) {
+        const float s2 = sum16(__fmul_rn(h, h));
+        if (r == 0 && m < M) ga.po[(size_t)m * gridDim.x + blockIdx.x] = s2;
+      }
     } else if constexpr (EPI == EPI_SWIGLU) {
-      float u = v[1][j];
-      if (ga.xs && m < ga.M) u = __fmul_rn(u, ga.xs[m]);
+      const float u = scaled ? __fmul_rn(v[1][j], sc) : v[1][j];
       const float sg = __fdiv_rn(y, __fadd_rn(1.0f, expf(-y)));
-      if (ok) ga.Y[(size_t)m * ga.ldy + n] = __fmul_rn(sg, u);
+      const float o = __fmul_rn(sg, u);
+      if (ok) {
+        if (ga.xo) AF<WT>::store(ga.xo, (size_t)m * ga.ldo, n, o);
+        else ga.Y[(size_t)m * ga.ldy + n] = o;
+      }
     } else {  // EPI_LOGITS: store and reduce the 16 columns of row m held by lanes 16g..16g+15
       if (ok) ga.Y[(size_t)m * ga.ldy + n] = y;
       float mx = (n < ga.N) ? y : -INFINITY;
@@ -372,9 +522,8 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void k_gemm(GemmArgs ga) {
         if (om > mx || (om == mx && oi < idx)) { mx = om; idx = oi; }
       }
       float e = (n < ga.N) ? expf(__fsub_rn(y, mx)) : 0.f;
-      // fixed-order sum over the 16 lanes
-      for (int o = 8; o >= 1; o >>= 1) e = __fadd_rn(e, __shfl_xor(e, o, 16));
-      if (r == 0 && m < ga.M) {
+      e = sum16(e);
+      if (r == 0 && m < M) {
         float* p = ga.part + ((size_t)m * gridDim.x + blockIdx.x) * 3;
         p[0] = mx;
         p[1] = __int_as_float(idx);
@@ -384,118 +533,162 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void k_gemm(GemmArgs ga) {
   }
 }
 
-// ---------------------------------------------------------------- RoPE + KV append
-// qkv[m] = [q (Hq*hd) | k (Hkv*hd) | v (Hkv*hd)] from the fused projection.
-// Rotates q and k by the rotate-half rule at position pos0 + m*pos_step with
-// the host-built cos/sin table, writes q to qrot and k, v either into the
-// layer's KV cache ([Hkv][max_seq][hd]) or, for layer-selection rows, into
-// selfkv[m][2][Hkv][hd] (those rows' own key/value, never cached).
-template <typename KT>
-__global__ void k_rope_kv(const float* __restrict__ qkv, int ldqkv, int Hq, int Hkv, int hd,
-                          const float2* __restrict__ cs, int pos0, int pos_step, float* __restrict__ qrot,
-                          KT* __restrict__ kc, KT* __restrict__ vc, int max_seq, float* __restrict__ selfkv) {
-  const int m = blockIdx.x, h = blockIdx.y;
-  const int half = hd / 2;
-  const int pos = pos0 + m * pos_step;
-  const float* src = qkv + (size_t)m * ldqkv + (size_t)h * hd;
-  for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    const float x1 = src[i], x2 = src[i + half];
-    if (h < Hq + Hkv) {
-      const float2 c = cs[(size_t)pos * half + i];
-      const float y1 = __fsub_rn(__fmul_rn(x1, c.x), __fmul_rn(x2, c.y));
-      const float y2 = __fadd_rn(__fmul_rn(x2, c.x), __fmul_rn(x1, c.y));
-      if (h < Hq) {
-        float* q = qrot + ((size_t)m * Hq + h) * hd;
-        q[i] = y1;
-        q[i + half] = y2;
-      } else {
-        const int kh = h - Hq;
-        if (selfkv) {
-          float* k = selfkv + (((size_t)m * 2 + 0) * Hkv + kh) * hd;
-          k[i] = y1;
-          k[i + half] = y2;
-        } else {
-          const size_t o = ((size_t)kh * max_seq + pos) * hd;
-          st_elem<KT>(kc, o + i, y1);
-          st_elem<KT>(kc, o + i + half, y2);
-        }
-      }
-    } else {
-      const int kh = h - Hq - Hkv;
-      if (selfkv) {
-        float* v = selfkv + (((size_t)m * 2 + 1) * Hkv + kh) * hd;
-        v[i] = x1;
-        v[i + half] = x2;
-      } else {
-        const size_t o = ((size_t)kh * max_seq + pos) * hd;
-        st_elem<KT>(vc, o + i, x1);
-        st_elem<KT>(vc, o + i + half, x2);
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- attention
-// Split-key attention.  Keys are cut into fixed 64-position chunks of the
-// cache (absolute positions), so a row's chunks do not depend on the other
-// rows of the launch.  Row m sees cache position u iff
+// One launch per layer: rotary embedding of the queries and of this launch's
+// new keys, KV-cache append, split-key attention and the merge.
+//
+// Keys are cut into fixed 64-position chunks of absolute cache positions; a
+// workgroup (chunk c, kv head, query block) computes, for each of its
+// queries, the chunk's max score, sum of exponentials and weighted value sum.
+// The last workgroup of a (kv head, query block) to finish -- found with an
+// integer atomic counter -- merges the chunks in chunk order (and, for
+// layer-selection rows, the row's own key/value).  The merge order depends
+// only on positions, never on the rows in the launch or on timing, so a
+// verify row equals the greedy step at the same position bit for bit.
+//
+// Row m (position pos0 + m*pos_step) sees cache position u iff
 //   u < lim_base + m*lim_step            (committed prefix / causal rows)
 //   or u - wbase in [0, 32) with bit (u - wbase) of wmask set
-//                                       (draft window slots this layer wrote)
-// plus, for layer-selection rows, its own key/value (added by the combine).
+//                                       (draft window slots this layer wrote).
+// In causal/draft launches the rows' own keys/values are positions
+// pos0 .. pos0+M-1: every workgroup rotates them from the projection output
+// itself (rounded to the cache type), and query block 0 of the chunk that
+// holds them writes them to the cache.  Layer-selection launches write
+// nothing; each row's own key/value enters the merge directly.
 #define ATT_CH 64
 #define ATT_QB 32
 #define ATT_THREADS 256
 
 struct AttnArgs {
-  const void* kc; const void* vc;  // layer cache [Hkv][max_seq][hd]
-  int max_seq, Hq, Hkv, hd, M;
-  const float* qrot;               // [M][Hq][hd]
+  const float* qkv; int ldqkv;     // [M][(Hq + 2 Hkv) hd] projection output
+  const float2* cs;                // rotary cos/sin [max_seq][hd/2]
+  void* kc; void* vc;              // layer cache [Hkv][max_seq][hd]
+  int max_seq, Hq, Hkv, M;
+  int pos0, pos_step;
   int lim_base, lim_step, wbase;
   uint32_t wmask;
-  int nch;                         // chunks in this launch
-  float* part;                     // [M][Hq][nch_max][hd + 2]
-  int nch_max;
+  int self_kv;                     // 1: layer-selection rows (own key/value, no cache write)
+  int nch, nz;                     // key chunks, query blocks in this launch
+  float* part;                     // [Hkv][nz_max][nch_max][QB][hd + 2]
+  int nz_max, nch_max;
+  int* counters;                   // [Hkv][nz_max], zero between launches
+  float* out;                      // [M][Hq * hd] float32 output (when xo == nullptr)
+  void* xo;                        // [M][Hq * hd] projection-format output
   float scale;                     // 1/sqrt(hd)
 };
 
+template <typename KT> __device__ __forceinline__ float kv_round(float v);
+template <> __device__ __forceinline__ float kv_round<float>(float v) { return v; }
+template <> __device__ __forceinline__ float kv_round<uint16_t>(float v) { return bf2f(f2bf(v)); }
+
+// element i of the rotated (rotate-half) vector x at rotary row cs
+__device__ __forceinline__ float rope_elem(const float* x, const float2* cs, int i, int half) {
+  if (i < half) {
+    const float2 c = cs[i];
+    return __fsub_rn(__fmul_rn(x[i], c.x), __fmul_rn(x[i + half], c.y));
+  }
+  const float2 c = cs[i - half];
+  return __fadd_rn(__fmul_rn(x[i], c.x), __fmul_rn(x[i - half], c.y));
+}
+
+// 4 consecutive cache elements as float
+template <typename KT> __device__ __forceinline__ float4 ld4(const KT* p);
+template <> __device__ __forceinline__ float4 ld4<float>(const float* p) { return *reinterpret_cast<const float4*>(p); }
+template <> __device__ __forceinline__ float4 ld4<uint16_t>(const uint16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                     __uint_as_float(v.y & 0xffff0000u));
+}
+
+// A 64-position tile of the layer cache for one kv head, issued as independent
+// 4-element loads (positions past the capacity read the last row; the
+// visibility mask never selects them).
 template <typename KT, int HD>
-__global__ __launch_bounds__(ATT_THREADS) void k_attn_partial(AttnArgs a) {
+struct AttTile {
+  static constexpr int NV = ATT_CH * HD / 4 / ATT_THREADS;   // float4 per thread
+  float4 v[NV];
+  __device__ __forceinline__ void load(const KT* cache, int u0, int max_seq) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int f = threadIdx.x + j * ATT_THREADS;
+      const int u = f / (HD / 4), d4 = f % (HD / 4);
+      const int pos = min(u0 + u, max_seq - 1);
+      v[j] = ld4<KT>(cache + (size_t)pos * HD + d4 * 4);
+    }
+  }
+  __device__ __forceinline__ void store(float (*t)[HD + 1]) const {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int f = threadIdx.x + j * ATT_THREADS;
+      const int u = f / (HD / 4), d4 = f % (HD / 4);
+      t[u][d4 * 4 + 0] = v[j].x; t[u][d4 * 4 + 1] = v[j].y; t[u][d4 * 4 + 2] = v[j].z; t[u][d4 * 4 + 3] = v[j].w;
+    }
+  }
+};
+
+// Replace the tile rows that are rows of this launch by their own keys
+// (rotated) or values, rounded to the cache type; query block 0 also writes
+// them to the cache.
+template <typename KT, int HD>
+__device__ __forceinline__ void att_new_rows(float (*t)[HD + 1], const AttnArgs& a, int kh, int u0, int z,
+                                             bool is_v) {
+  if (a.self_kv) return;
+  const int r0 = max(u0, a.pos0), r1 = min(u0 + ATT_CH, a.pos0 + a.M);
+  if (r0 >= r1) return;
+  KT* cache = reinterpret_cast<KT*>(is_v ? a.vc : a.kc) + (size_t)kh * a.max_seq * HD;
+  const int off = (is_v ? a.Hq + a.Hkv : a.Hq) + kh;
+  for (int i = threadIdx.x; i < (r1 - r0) * HD; i += ATT_THREADS) {
+    const int pos = r0 + i / HD, dd = i % HD;
+    const float* x = a.qkv + (size_t)(pos - a.pos0) * a.ldqkv + (size_t)off * HD;
+    float v = is_v ? x[dd] : rope_elem(x, a.cs + (size_t)pos * (HD / 2), dd, HD / 2);
+    v = kv_round<KT>(v);
+    if (z == 0) st_elem<KT>(cache, (size_t)pos * HD + dd, v);
+    t[pos - u0][dd] = v;
+  }
+}
+
+template <typename KT, typename WT, int HD>
+__global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
   __shared__ float kv_s[ATT_CH][HD + 1];
   __shared__ float q_s[ATT_QB][HD];
   __shared__ float p_s[ATT_QB][ATT_CH];
   __shared__ float st_s[ATT_QB][2];
-  const int c = blockIdx.x, kh = blockIdx.y, qb = blockIdx.z;
+  __shared__ float self_s[ATT_QB];
+  __shared__ int last_s;
+  const int c = blockIdx.x, kh = blockIdx.y, z = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int nq = G * a.M;
-  const int q0 = qb * ATT_QB;
+  const int q0 = z * ATT_QB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int u0 = c * ATT_CH;
   const KT* kc = reinterpret_cast<const KT*>(a.kc) + (size_t)kh * a.max_seq * HD;
   const KT* vc = reinterpret_cast<const KT*>(a.vc) + (size_t)kh * a.max_seq * HD;
-  const int u0 = c * ATT_CH;
 
-  for (int i = tid; i < ATT_CH * HD; i += ATT_THREADS) {
-    const int u = i / HD, dd = i % HD;
-    const int pos = u0 + u;
-    kv_s[u][dd] = (pos < a.max_seq) ? ld_elem<KT>(kc, (size_t)pos * HD + dd) : 0.f;
-  }
+  AttTile<KT, HD> kt, vt;
+  kt.load(kc, u0, a.max_seq);
+  vt.load(vc, u0, a.max_seq);
+  // rotated queries of this block
   for (int i = tid; i < ATT_QB * HD; i += ATT_THREADS) {
     const int qi = i / HD, dd = i % HD;
     const int gq = q0 + qi;
     float v = 0.f;
     if (gq < nq) {
       const int m = gq / G, h = kh * G + gq % G;
-      v = a.qrot[((size_t)m * a.Hq + h) * HD + dd];
+      const int pos = a.pos0 + m * a.pos_step;
+      v = rope_elem(a.qkv + (size_t)m * a.ldqkv + (size_t)h * HD, a.cs + (size_t)pos * (HD / 2), dd, HD / 2);
     }
     q_s[qi][dd] = v;
   }
+  kt.store(kv_s);
   __syncthreads();
-  // scores: lane = key, wave handles queries wave, wave+4, ...
+  att_new_rows<KT, HD>(kv_s, a, kh, u0, z, false);
+  __syncthreads();
+  // scores: lane = key, each wave takes queries wave, wave + 4, ...
   {
-    const int u = lane;
-    const int pos = u0 + u;
+    const int u = lane, pos = u0 + u;
     for (int qi = wave; qi < ATT_QB; qi += ATT_THREADS / 64) {
       const int gq = q0 + qi;
+      if (q0 + (qi & ~3) >= nq) break;               // wave-uniform: no valid query left
       float s = -INFINITY;
       if (gq < nq) {
         const int m = gq / G;
@@ -517,64 +710,96 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn_partial(AttnArgs a) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < ATT_CH * HD; i += ATT_THREADS) {
-    const int u = i / HD, dd = i % HD;
-    const int pos = u0 + u;
-    kv_s[u][dd] = (pos < a.max_seq) ? ld_elem<KT>(vc, (size_t)pos * HD + dd) : 0.f;
-  }
+  vt.store(kv_s);
   __syncthreads();
+  att_new_rows<KT, HD>(kv_s, a, kh, u0, z, true);
+  __syncthreads();
+  float* part = a.part + (((size_t)kh * a.nz_max + z) * a.nch_max + c) * ATT_QB * (HD + 2);
   for (int i = tid; i < ATT_QB * HD; i += ATT_THREADS) {
     const int qi = i / HD, dd = i % HD;
-    const int gq = q0 + qi;
-    if (gq >= nq) continue;
+    if (q0 + qi >= nq) break;
     float acc = 0.f;
 #pragma unroll 8
     for (int u = 0; u < ATT_CH; ++u) acc = fmaf(p_s[qi][u], kv_s[u][dd], acc);
+    float* o = part + (size_t)qi * (HD + 2);
+    o[dd] = acc;
+    if (dd == 0) { o[HD] = st_s[qi][0]; o[HD + 1] = st_s[qi][1]; }
+  }
+  // the last workgroup of this (kv head, query block) merges the chunks
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    int* ctr = a.counters + kh * a.nz_max + z;
+    const int prev = atomicAdd(ctr, 1);
+    last_s = (prev == a.nch - 1);
+    if (last_s) atomicExch(ctr, 0);
+  }
+  __syncthreads();
+  if (!last_s) return;
+  __threadfence();
+  const int nqb = min(ATT_QB, nq - q0);
+  if (a.self_kv) {       // score of each row's own key
+    for (int qi = wave; qi < nqb; qi += ATT_THREADS / 64) {
+      const int gq = q0 + qi;
+      const int m = gq / G;
+      const int pos = a.pos0 + m * a.pos_step;
+      const float* kx = a.qkv + (size_t)m * a.ldqkv + (size_t)(a.Hq + kh) * HD;
+      const float2* cs = a.cs + (size_t)pos * (HD / 2);
+      float dot = 0.f;
+      for (int dd = lane; dd < HD; dd += 64) dot = fmaf(q_s[qi][dd], rope_elem(kx, cs, dd, HD / 2), dot);
+      dot = wave_sum(dot);
+      if (lane == 0) self_s[qi] = __fmul_rn(dot, a.scale);
+    }
+  }
+  // pass 1 (one thread per query): max over the chunks that saw a key, the
+  // chunk weights exp(m_c - M) and the normalizer, in chunk order
+  float* wgt = &p_s[0][0];                  // reuse: [QB][nch] chunk weights (nch <= 64: max_seq <= 4096)
+  const float* pb = a.part + ((size_t)kh * a.nz_max + z) * a.nch_max * ATT_QB * (HD + 2);
+  __syncthreads();
+  if (tid < nqb) {
+    const int qi = tid;
+    float M = -INFINITY;
+    for (int cc = 0; cc < a.nch; ++cc) {
+      const float* pc = pb + ((size_t)cc * ATT_QB + qi) * (HD + 2);
+      if (pc[HD + 1] != 0.f) M = fmaxf(M, pc[HD]);
+    }
+    if (a.self_kv) M = fmaxf(M, self_s[qi]);
+    float L = 0.f;
+    for (int cc = 0; cc < a.nch; ++cc) {
+      const float* pc = pb + ((size_t)cc * ATT_QB + qi) * (HD + 2);
+      const float lc = pc[HD + 1];
+      const float wc = (lc != 0.f) ? expf(__fsub_rn(pc[HD], M)) : 0.f;
+      wgt[qi * ATT_CH + cc] = wc;
+      if (lc != 0.f) L = __fadd_rn(L, __fmul_rn(lc, wc));
+    }
+    float ws = 0.f;
+    if (a.self_kv) {
+      ws = expf(__fsub_rn(self_s[qi], M));
+      L = __fadd_rn(L, ws);
+    }
+    st_s[qi][0] = L;
+    st_s[qi][1] = ws;
+  }
+  __syncthreads();
+  // pass 2: weighted value sums in chunk order
+  for (int i = tid; i < nqb * HD; i += ATT_THREADS) {
+    const int qi = i / HD, dd = i % HD;
+    float acc = 0.f;
+    for (int cc = 0; cc < a.nch; ++cc) {
+      const float* pc = pb + ((size_t)cc * ATT_QB + qi) * (HD + 2);
+      const float wc = wgt[qi * ATT_CH + cc];
+      if (wc != 0.f) acc = __fadd_rn(acc, __fmul_rn(pc[dd], wc));
+    }
+    const int gq = q0 + qi;
     const int m = gq / G, h = kh * G + gq % G;
-    float* out = a.part + (((size_t)m * a.Hq + h) * a.nch_max + c) * (HD + 2);
-    out[dd] = acc;
-    if (dd == 0) { out[HD] = st_s[qi][0]; out[HD + 1] = st_s[qi][1]; }
+    if (a.self_kv) {
+      const float v = a.qkv[(size_t)m * a.ldqkv + (size_t)(a.Hq + a.Hkv + kh) * HD + dd];
+      acc = __fadd_rn(acc, __fmul_rn(v, st_s[qi][1]));
+    }
+    const float o = __fdiv_rn(acc, st_s[qi][0]);
+    if (a.xo) AF<WT>::store(a.xo, (size_t)m * a.Hq * HD, h * HD + dd, o);
+    else a.out[(size_t)m * a.Hq * HD + (size_t)h * HD + dd] = o;
   }
-}
-
-// Merge the chunk partials of each (row, head) in chunk order, then (for
-// layer-selection rows) the row's own key/value; o[m][h*hd + d].
-template <int HD>
-__global__ __launch_bounds__(HD) void k_attn_combine(const float* __restrict__ part, int nch, int nch_max,
-                                                     int Hq, int Hkv, const float* __restrict__ qrot,
-                                                     const float* __restrict__ selfkv, float scale,
-                                                     float* __restrict__ o) {
-  __shared__ float red[HD / 64 > 0 ? HD / 64 : 1];
-  const int m = blockIdx.x / Hq, h = blockIdx.x % Hq;
-  const int dd = threadIdx.x;
-  const float* p = part + ((size_t)m * Hq + h) * nch_max * (HD + 2);
-  float M = -INFINITY, L = 0.f, acc = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const float* pc = p + (size_t)c * (HD + 2);
-    const float lc = pc[HD + 1];
-    if (lc == 0.f) continue;
-    const float mc = pc[HD];
-    const float Mn = fmaxf(M, mc);
-    const float fa = (M == -INFINITY) ? 0.f : expf(__fsub_rn(M, Mn));
-    const float fb = expf(__fsub_rn(mc, Mn));
-    acc = __fadd_rn(__fmul_rn(acc, fa), __fmul_rn(pc[dd], fb));
-    L = __fadd_rn(__fmul_rn(L, fa), __fmul_rn(lc, fb));
-    M = Mn;
-  }
-  if (selfkv) {
-    const int G = Hq / Hkv, kh = h / G;
-    const float* k = selfkv + (((size_t)m * 2 + 0) * Hkv + kh) * HD;
-    const float* v = selfkv + (((size_t)m * 2 + 1) * Hkv + kh) * HD;
-    const float* q = qrot + ((size_t)m * Hq + h) * HD;
-    const float s = __fmul_rn(block_sum(__fmul_rn(q[dd], k[dd]), red), scale);
-    const float Mn = fmaxf(M, s);
-    const float fa = (M == -INFINITY) ? 0.f : expf(__fsub_rn(M, Mn));
-    const float fb = expf(__fsub_rn(s, Mn));
-    acc = __fadd_rn(__fmul_rn(acc, fa), __fmul_rn(v[dd], fb));
-    L = __fadd_rn(__fmul_rn(L, fa), fb);
-    M = Mn;
-  }
-  o[((size_t)m * Hq + h) * HD + dd] = __fdiv_rn(acc, L);
 }
 
 // ---------------------------------------------------------------- LM head reduce / accept
@@ -650,10 +875,14 @@ __global__ void k_gather_target(const float* __restrict__ hs, int rows_stride, i
 // candidate ex[j - ex_lo] (valid iff j in [ex_lo, ex_hi]) and the skipped
 // candidate gp[j - 1 - lo_p] (valid iff j-1 in [lo_p, hi_p]) by cosine
 // similarity with the target state H; keep the skip only if strictly better.
+// The chosen state goes to gn[j - lo_i] with its projection input for the
+// next layer (gain g) when xo != nullptr.
+template <typename WT>
 __global__ __launch_bounds__(256) void k_dp_select(const float* __restrict__ ex, int ex_lo, int ex_hi,
                                                    const float* __restrict__ gp, int lo_p, int hi_p,
                                                    const float* __restrict__ H, int d, int lo_i,
-                                                   float* __restrict__ gn, float* __restrict__ dec) {
+                                                   float* __restrict__ gn, float* __restrict__ dec,
+                                                   const float* __restrict__ g, void* xo, float* __restrict__ po) {
   __shared__ float red[4];
   __shared__ int take_s;
   const int j = lo_i + blockIdx.x;
@@ -685,8 +914,11 @@ __global__ __launch_bounds__(256) void k_dp_select(const float* __restrict__ ex,
   }
   __syncthreads();
   const float* src = take_s ? s : e;
-  float* dst = gn + (size_t)(j - lo_i) * d;
+  const int row = j - lo_i;
+  float* dst = gn + (size_t)row * d;
   for (int i = threadIdx.x; i < d; i += blockDim.x) dst[i] = src[i];
+  __syncthreads();
+  if (xo) prep_row<WT>(dst, d, g, xo, po, row);
 }
 
 }  // namespace lss
