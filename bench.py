@@ -66,6 +66,27 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
                       f"{len(recs)} rounds in {dt:.1f} s"}
 
 
+def recorded_traffic():
+    """HBM bytes per launch of the draft gate/up kernel measured with rocprofv3
+    counters (profiles/draft_gemv_llama3_8b.md), or None when the kernel
+    source changed since the counters were taken."""
+    import hashlib
+    src = os.path.join(ROOT, "layer_skip_self_amd", "csrc", "lss_kernels.h")
+    rec = os.path.join(ROOT, "profiles", "draft_gemv_llama3_8b.md")
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        fields = {}
+        for line in open(rec):
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+        if fields.get("kernel source sha256") != sha:
+            return None
+        return int(fields["traffic bytes per launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -74,8 +95,11 @@ def main():
     ap.add_argument("--workload", default="llama3_8b", choices=sorted(WORKLOADS))
     ap.add_argument("--ar-steps", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--cpu-prompt", type=int, default=64)
+    ap.add_argument("--gen", type=int, default=None, help="override the generated length (profiling runs)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this engine runs one sequence on one GPU; --gpus must be 1 "
@@ -93,7 +117,7 @@ def main():
     torch.cuda.set_device(dev)
     weights = lss_synth.make_weights(shape, device=dev)
     prompt = lss_synth.make_prompt(shape, wl["prompt"])
-    G = wl["gen"]
+    G = wl["gen"] if args.gen is None else args.gen
     max_seq = wl["prompt"] + G + 33
     eng = Engine(shape, weights, max_seq=max_seq, max_rows=64)
     stream = eng.stream
@@ -122,10 +146,17 @@ def main():
     eng.profile_kernel("gate_up", enable=False)
 
     ar_times, ar_toks = [], None
-    run({"mode": "ar"})
+    if args.ar_steps > 0:
+        run({"mode": "ar"})
     for _ in range(args.ar_steps):
         ar_toks, _, dt = run({"mode": "ar"})
         ar_times.append(dt)
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     pre = []
     for _ in range(3):
         torch.cuda.synchronize()
@@ -137,7 +168,7 @@ def main():
 
     step_s = t_all / args.steps
     value = G / step_s
-    ar_value = G / (sum(ar_times) / len(ar_times))
+    ar_value = G / (sum(ar_times) / len(ar_times)) if ar_times else None
     st = stats[-1]
     rounds = st["rounds"]
     avg_launch_us = 1e3 * k_ms / max(k_n, 1)
@@ -158,9 +189,9 @@ def main():
         "data": "synthetic (seeded random-init weights and uniform-random prompt)",
         "config": {"workload": wl["desc"], "global_batch": 1, "seq_len": wl["prompt"] + G,
                    "parallelism": "none (1 GPU)"},
-        "speedup_vs_ar": round(value / ar_value, 4),
-        "ar_tokens_per_s": round(ar_value, 3),
-        "lossless": spec_toks == ar_toks,
+        "speedup_vs_ar": round(value / ar_value, 4) if ar_value else None,
+        "ar_tokens_per_s": round(ar_value, 3) if ar_value else None,
+        "lossless": (spec_toks == ar_toks) if ar_toks is not None else None,
         "mean_accepted": round(st["accepted"] / max(rounds, 1), 4),
         "tokens_per_round": round((st["emitted"] - 1) / max(rounds, 1), 4),
         "drafted_per_round": round(st["drafted"] / max(rounds, 1), 4),
@@ -176,7 +207,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
-            "traffic": None,
+            "traffic": recorded_traffic(),
             "bytes_per_launch": int(bytes_per_launch),
             "avg_launch_us": round(avg_launch_us, 3),
             "launches": k_n,

@@ -307,8 +307,8 @@ void quant_rows(lss_engine* e, const float* x, int M, int n, void* xo) {
 // projection input + partial sums of squares of M rows of h (row stride d) with gain g
 void prep_rows(lss_engine* e, const float* h, int M, const float* g, void* xo, float* po) {
   const int d = e->cfg.d_model;
-  if (e->bf16) hipLaunchKernelGGL(k_prep_rows<uint16_t>, dim3(M), dim3(256), 0, e->stream, h, d, d, g, xo, po);
-  else hipLaunchKernelGGL(k_prep_rows<float>, dim3(M), dim3(256), 0, e->stream, h, d, d, g, xo, po);
+  if (e->bf16) hipLaunchKernelGGL(k_prep_rows<uint16_t>, dim3(M), dim3(PREP_THREADS), 0, e->stream, h, d, d, g, xo, po);
+  else hipLaunchKernelGGL(k_prep_rows<float>, dim3(M), dim3(PREP_THREADS), 0, e->stream, h, d, d, g, xo, po);
 }
 
 // One decoder layer on M rows: h_out = layer(h_in).  Rows are consecutive
@@ -379,7 +379,8 @@ void head(lss_engine* e, int r0, int M, int row0) {
   ga.scale = SCALE_NORM; ga.pin = e->pa + (size_t)r0 * (c.d_model / 16); ga.eps = c.rms_eps;
   ga.part = e->hpart;
   gemm<EPI_LOGITS>(e, ga);
-  hipLaunchKernelGGL(k_head_reduce, dim3(M), dim3(256), 0, e->stream, e->hpart, e->lay.ntile, e->res, row0);
+  hipLaunchKernelGGL(k_head_reduce, dim3(M), dim3(HEAD_RED_THREADS), 0, e->stream, e->hpart, e->lay.ntile, e->res,
+                     row0);
   e->logits_rows = M;
 }
 
@@ -388,10 +389,10 @@ void head(lss_engine* e, int r0, int M, int row0) {
 void embed(lss_engine* e, const int32_t* tok_dev, int M, float* h, const float* g) {
   const auto& c = e->cfg;
   if (e->bf16)
-    hipLaunchKernelGGL(k_embed<uint16_t>, dim3(M), dim3(256), 0, e->stream, (const uint16_t*)e->embed, tok_dev,
+    hipLaunchKernelGGL(k_embed<uint16_t>, dim3(M), dim3(PREP_THREADS), 0, e->stream, (const uint16_t*)e->embed, tok_dev,
                        c.d_model, h, g, e->xa, e->pa);
   else
-    hipLaunchKernelGGL(k_embed<float>, dim3(M), dim3(256), 0, e->stream, (const float*)e->embed, tok_dev,
+    hipLaunchKernelGGL(k_embed<float>, dim3(M), dim3(PREP_THREADS), 0, e->stream, (const float*)e->embed, tok_dev,
                        c.d_model, h, g, e->xa, e->pa);
 }
 
@@ -679,11 +680,11 @@ int lss_select_layers_dp(lss_engine* e, int32_t S, int32_t Le, uint8_t* mask_out
     const float* g = i < Le ? e->layers[i].attn_norm : nullptr;
     void* xo = i < Le ? e->xa : nullptr;
     if (e->bf16)
-      hipLaunchKernelGGL(k_dp_select<uint16_t>, dim3(hi_i - lo_i + 1), dim3(256), 0, e->stream, e->dpx, ex_lo, ex_hi,
+      hipLaunchKernelGGL(k_dp_select<uint16_t>, dim3(hi_i - lo_i + 1), dim3(PREP_THREADS), 0, e->stream, e->dpx, ex_lo, ex_hi,
                          e->dpg[cur], lo_p, hi_p, e->target + (size_t)i * d, d, lo_i, e->dpg[cur ^ 1],
                          e->dpdec + (size_t)i * (L + 1) * 3, g, xo, e->pa);
     else
-      hipLaunchKernelGGL(k_dp_select<float>, dim3(hi_i - lo_i + 1), dim3(256), 0, e->stream, e->dpx, ex_lo, ex_hi,
+      hipLaunchKernelGGL(k_dp_select<float>, dim3(hi_i - lo_i + 1), dim3(PREP_THREADS), 0, e->stream, e->dpx, ex_lo, ex_hi,
                          e->dpg[cur], lo_p, hi_p, e->target + (size_t)i * d, d, lo_i, e->dpg[cur ^ 1],
                          e->dpdec + (size_t)i * (L + 1) * 3, g, xo, e->pa);
     cur ^= 1;

@@ -101,37 +101,61 @@ __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
   for (; i < n; i += stride) p[i] = v;
 }
 
-// Projection input of rows h[m][0..d): xo = h * g (g == nullptr: h) in the
-// projection format, po[m][t] = sum of h^2 over columns 16t..16t+15.
-// One block of 256 threads per row.
+// Projection input of a row held in registers by a 256-thread block
+// (v[j] = element threadIdx.x + 256 j, d <= 8192): xo = h * g (g == nullptr:
+// h) in the projection format, po[m][t] = sum of h^2 over columns
+// 16t..16t+15 (fixed 16-lane tree).
+#define PREP_THREADS 256
+#define PREP_PER_THREAD 32
 template <typename WT>
-__device__ __forceinline__ void prep_row(const float* h, int d, const float* g, void* xo, float* po, int m) {
-  for (int i0 = 0; i0 < d; i0 += blockDim.x) {
-    const int i = i0 + threadIdx.x;          // d is a multiple of 16: whole tiles per pass
-    const float v = (i < d) ? h[i] : 0.f;
-    if (i < d && xo) AF<WT>::store(xo, (size_t)m * d, i, g ? __fmul_rn(v, g[i]) : v);
-    const float s = sum16(__fmul_rn(v, v));
-    if (po && i < d && (i & 15) == 0) po[(size_t)m * (d >> 4) + (i >> 4)] = s;
+__device__ __forceinline__ void prep_vals(const float (&v)[PREP_PER_THREAD], int d, const float* g, void* xo,
+                                          float* po, int m) {
+#pragma unroll
+  for (int j = 0; j < PREP_PER_THREAD; ++j) {
+    const int i = threadIdx.x + j * PREP_THREADS;   // d is a multiple of 16: whole tiles per pass
+    if (j * PREP_THREADS >= d) break;
+    const float s = sum16(__fmul_rn(v[j], v[j]));
+    if (i < d) {
+      if (xo) AF<WT>::store(xo, (size_t)m * d, i, g ? __fmul_rn(v[j], g[i]) : v[j]);
+      if (po && (i & 15) == 0) po[(size_t)m * (d >> 4) + (i >> 4)] = s;
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void load_vals(float (&v)[PREP_PER_THREAD], const T* src, int d) {
+#pragma unroll
+  for (int j = 0; j < PREP_PER_THREAD; ++j) {
+    const int i = threadIdx.x + j * PREP_THREADS;
+    v[j] = (i < d) ? ld_elem<T>(src, i) : 0.f;
   }
 }
 
 template <typename WT>
-__global__ void k_prep_rows(const float* __restrict__ h, int ldh, int d, const float* __restrict__ g, void* xo,
-                            float* __restrict__ po) {
+__global__ __launch_bounds__(PREP_THREADS) void k_prep_rows(const float* __restrict__ h, int ldh, int d,
+                                                            const float* __restrict__ g, void* xo,
+                                                            float* __restrict__ po) {
   const int m = blockIdx.x;
-  prep_row<WT>(h + (size_t)m * ldh, d, g, xo, po, m);
+  float v[PREP_PER_THREAD];
+  load_vals<float>(v, h + (size_t)m * ldh, d);
+  prep_vals<WT>(v, d, g, xo, po, m);
 }
 
 // h[m][:] = E[tok[m]][:] (float32 residual stream) and its projection input.
 template <typename WT>
-__global__ void k_embed(const WT* __restrict__ E, const int32_t* __restrict__ tok, int d, float* __restrict__ h,
-                        const float* __restrict__ g, void* xo, float* __restrict__ po) {
+__global__ __launch_bounds__(PREP_THREADS) void k_embed(const WT* __restrict__ E, const int32_t* __restrict__ tok,
+                                                        int d, float* __restrict__ h, const float* __restrict__ g,
+                                                        void* xo, float* __restrict__ po) {
   const int m = blockIdx.x;
-  const size_t row = (size_t)tok[m] * d;
+  float v[PREP_PER_THREAD];
+  load_vals<WT>(v, E + (size_t)tok[m] * d, d);
   float* hr = h + (size_t)m * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) hr[i] = ld_elem<WT>(E, row + i);
-  __syncthreads();
-  prep_row<WT>(hr, d, g, xo, po, m);
+#pragma unroll
+  for (int j = 0; j < PREP_PER_THREAD; ++j) {
+    const int i = threadIdx.x + j * PREP_THREADS;
+    if (i < d) hr[i] = v[j];
+  }
+  prep_vals<WT>(v, d, g, xo, po, m);
 }
 
 // Symmetric per-token int8 codes: inv = fl32(127 / amax) (correctly rounded),
@@ -751,24 +775,32 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
       if (lane == 0) self_s[qi] = __fmul_rn(dot, a.scale);
     }
   }
-  // pass 1 (one thread per query): max over the chunks that saw a key, the
-  // chunk weights exp(m_c - M) and the normalizer, in chunk order
-  float* wgt = &p_s[0][0];                  // reuse: [QB][nch] chunk weights (nch <= 64: max_seq <= 4096)
+  // merge: (1) every chunk's {max, sum} per query -> LDS in one parallel pass;
+  // (2) one thread per query: max over the chunks that saw a key, chunk weights
+  // exp(m_c - M) and the normalizer, in chunk order; (3) weighted value sums
+  // in chunk order with unconditional loads (a chunk without visible keys has
+  // weight 0 and an all-zero partial, adding exactly 0).
   const float* pb = a.part + ((size_t)kh * a.nz_max + z) * a.nch_max * ATT_QB * (HD + 2);
+  float (*stat)[ATT_QB][2] = reinterpret_cast<float (*)[ATT_QB][2]>(&kv_s[0][0]);   // [nch <= 64][QB][2]
+  float* wgt = &p_s[0][0];                                                          // [QB][64]
+  __syncthreads();
+  for (int i = tid; i < a.nch * nqb; i += ATT_THREADS) {
+    const int cc = i / nqb, qi = i - cc * nqb;
+    const float* pc = pb + ((size_t)cc * ATT_QB + qi) * (HD + 2);
+    stat[cc][qi][0] = pc[HD];
+    stat[cc][qi][1] = pc[HD + 1];
+  }
   __syncthreads();
   if (tid < nqb) {
     const int qi = tid;
     float M = -INFINITY;
-    for (int cc = 0; cc < a.nch; ++cc) {
-      const float* pc = pb + ((size_t)cc * ATT_QB + qi) * (HD + 2);
-      if (pc[HD + 1] != 0.f) M = fmaxf(M, pc[HD]);
-    }
+    for (int cc = 0; cc < a.nch; ++cc)
+      if (stat[cc][qi][1] != 0.f) M = fmaxf(M, stat[cc][qi][0]);
     if (a.self_kv) M = fmaxf(M, self_s[qi]);
     float L = 0.f;
     for (int cc = 0; cc < a.nch; ++cc) {
-      const float* pc = pb + ((size_t)cc * ATT_QB + qi) * (HD + 2);
-      const float lc = pc[HD + 1];
-      const float wc = (lc != 0.f) ? expf(__fsub_rn(pc[HD], M)) : 0.f;
+      const float lc = stat[cc][qi][1];
+      const float wc = (lc != 0.f) ? expf(__fsub_rn(stat[cc][qi][0], M)) : 0.f;
       wgt[qi * ATT_CH + cc] = wc;
       if (lc != 0.f) L = __fadd_rn(L, __fmul_rn(lc, wc));
     }
@@ -781,15 +813,11 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
     st_s[qi][1] = ws;
   }
   __syncthreads();
-  // pass 2: weighted value sums in chunk order
   for (int i = tid; i < nqb * HD; i += ATT_THREADS) {
     const int qi = i / HD, dd = i % HD;
     float acc = 0.f;
-    for (int cc = 0; cc < a.nch; ++cc) {
-      const float* pc = pb + ((size_t)cc * ATT_QB + qi) * (HD + 2);
-      const float wc = wgt[qi * ATT_CH + cc];
-      if (wc != 0.f) acc = __fadd_rn(acc, __fmul_rn(pc[dd], wc));
-    }
+    for (int cc = 0; cc < a.nch; ++cc)
+      acc = __fadd_rn(acc, __fmul_rn(pb[((size_t)cc * ATT_QB + qi) * (HD + 2) + dd], wgt[qi * ATT_CH + cc]));
     const int gq = q0 + qi;
     const int m = gq / G, h = kh * G + gq % G;
     if (a.self_kv) {
@@ -810,11 +838,12 @@ struct HeadRes {                 // device result block, mirrored to the host
 
 // Per row: argmax over the tile partials (lowest index on ties) and the
 // top-1 softmax probability 1 / sum_j exp(z_j - z_max).
-__global__ __launch_bounds__(256) void k_head_reduce(const float* __restrict__ part, int ntile,
-                                                     HeadRes* __restrict__ res, int row0) {
-  __shared__ float redf[4];
-  __shared__ float bm[4];
-  __shared__ int bi[4];
+#define HEAD_RED_THREADS 1024
+__global__ __launch_bounds__(HEAD_RED_THREADS) void k_head_reduce(const float* __restrict__ part, int ntile,
+                                                                  HeadRes* __restrict__ res, int row0) {
+  __shared__ float redf[HEAD_RED_THREADS / 64];
+  __shared__ float bm[HEAD_RED_THREADS / 64];
+  __shared__ int bi[HEAD_RED_THREADS / 64];
   const int m = blockIdx.x;
   const float* p = part + (size_t)m * ntile * 3;
   float mx = -INFINITY;
@@ -878,7 +907,7 @@ __global__ void k_gather_target(const float* __restrict__ hs, int rows_stride, i
 // The chosen state goes to gn[j - lo_i] with its projection input for the
 // next layer (gain g) when xo != nullptr.
 template <typename WT>
-__global__ __launch_bounds__(256) void k_dp_select(const float* __restrict__ ex, int ex_lo, int ex_hi,
+__global__ __launch_bounds__(PREP_THREADS) void k_dp_select(const float* __restrict__ ex, int ex_lo, int ex_hi,
                                                    const float* __restrict__ gp, int lo_p, int hi_p,
                                                    const float* __restrict__ H, int d, int lo_i,
                                                    float* __restrict__ gn, float* __restrict__ dec,
@@ -916,9 +945,14 @@ __global__ __launch_bounds__(256) void k_dp_select(const float* __restrict__ ex,
   const float* src = take_s ? s : e;
   const int row = j - lo_i;
   float* dst = gn + (size_t)row * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) dst[i] = src[i];
-  __syncthreads();
-  if (xo) prep_row<WT>(dst, d, g, xo, po, row);
+  float v[PREP_PER_THREAD];
+  load_vals<float>(v, src, d);
+#pragma unroll
+  for (int jj = 0; jj < PREP_PER_THREAD; ++jj) {
+    const int i = threadIdx.x + jj * PREP_THREADS;
+    if (i < d) dst[i] = v[jj];
+  }
+  if (xo) prep_vals<WT>(v, d, g, xo, po, row);
 }
 
 }  // namespace lss
