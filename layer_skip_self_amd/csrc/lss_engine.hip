@@ -8,6 +8,7 @@
 // plus its own key/value).  Because every kernel is row-independent with a
 // fixed reduction order, verify rows equal autoregressive steps bit for bit.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <cmath>
@@ -186,24 +187,34 @@ float* hs_row(lss_engine* e, int l, int m) {
 }
 
 // ------------------------------------------------------------------ launches
+// Launch one projection kernel.  With t0/t1 set the launch goes through
+// hipExtLaunchKernelGGL, which stamps the two events from the kernel's own
+// dispatch (start and end of execution), not from separate marker packets.
+template <typename K>
+void launch_k(K kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, hipEvent_t t0, hipEvent_t t1,
+              const GemmArgs& ga) {
+  if (t0) hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, t0, t1, 0u, ga);
+  else hipLaunchKernelGGL(kern, grid, block, lds, s, ga);
+}
+
 template <typename WT, int EPI>
-void gemm_mt(const GemmArgs& ga, hipStream_t s) {
+void gemm_mt(const GemmArgs& ga, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr) {
   const dim3 grid((ga.N + 15) / 16), block(64 * GEMM_WAVES);
   const size_t a_lds = (size_t)ga.M * a_lds_ld(ga.K) * 4;
   const bool alds = ga.M <= 16 && a_lds <= GEMM_A_LDS_MAX;
   if (ga.M == 1) {
-    if (alds) hipLaunchKernelGGL((k_gemm<WT, 1, EPI, true, true>), grid, block, a_lds, s, ga);
-    else hipLaunchKernelGGL((k_gemm<WT, 1, EPI, true, false>), grid, block, 0, s, ga);
+    if (alds) launch_k(k_gemm<WT, 1, EPI, true, true>, grid, block, a_lds, s, t0, t1, ga);
+    else launch_k(k_gemm<WT, 1, EPI, true, false>, grid, block, 0, s, t0, t1, ga);
     return;
   }
   switch ((ga.M + 15) / 16) {
     case 1:
-      if (alds) hipLaunchKernelGGL((k_gemm<WT, 1, EPI, false, true>), grid, block, a_lds, s, ga);
-      else hipLaunchKernelGGL((k_gemm<WT, 1, EPI, false, false>), grid, block, 0, s, ga);
+      if (alds) launch_k(k_gemm<WT, 1, EPI, false, true>, grid, block, a_lds, s, t0, t1, ga);
+      else launch_k(k_gemm<WT, 1, EPI, false, false>, grid, block, 0, s, t0, t1, ga);
       break;
-    case 2: hipLaunchKernelGGL((k_gemm<WT, 2, EPI, false, false>), grid, block, 0, s, ga); break;
-    case 3: hipLaunchKernelGGL((k_gemm<WT, 3, EPI, false, false>), grid, block, 0, s, ga); break;
-    default: hipLaunchKernelGGL((k_gemm<WT, 4, EPI, false, false>), grid, block, 0, s, ga); break;
+    case 2: launch_k(k_gemm<WT, 2, EPI, false, false>, grid, block, 0, s, t0, t1, ga); break;
+    case 3: launch_k(k_gemm<WT, 3, EPI, false, false>, grid, block, 0, s, t0, t1, ga); break;
+    default: launch_k(k_gemm<WT, 4, EPI, false, false>, grid, block, 0, s, t0, t1, ga); break;
   }
 }
 
@@ -224,12 +235,11 @@ void gemm(lss_engine* e, const GemmArgs& ga) {
       (void)hipStreamSynchronize(e->stream);
       prof_resolve(e);
     }
-    (void)hipEventRecord(e->ev_start[e->ev_used], e->stream);
   }
-  if (e->bf16) gemm_mt<uint16_t, EPI>(ga, e->stream);
-  else gemm_mt<float, EPI>(ga, e->stream);
+  hipEvent_t t0 = prof ? e->ev_start[e->ev_used] : nullptr, t1 = prof ? e->ev_stop[e->ev_used] : nullptr;
+  if (e->bf16) gemm_mt<uint16_t, EPI>(ga, e->stream, t0, t1);
+  else gemm_mt<float, EPI>(ga, e->stream, t0, t1);
   if (prof) {
-    (void)hipEventRecord(e->ev_stop[e->ev_used], e->stream);
     e->ev_used++;
     const int64_t elt = e->bf16 ? 2 : 4;
     const int64_t nw = (EPI == EPI_SWIGLU) ? 2 : 1;
