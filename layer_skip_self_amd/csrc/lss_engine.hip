@@ -48,6 +48,10 @@ bool cfg_valid(const lss_config* c, std::string* why) {
   if (c->d_model % kq || c->ffn_dim % kq || c->vocab % 16)
     return fail("d_model, ffn_dim must be multiples of 32 (bf16) / 16 (float32), vocab of 16");
   if (c->d_model > 8192) return fail("d_model > 8192");
+  // projection depth of the decode GEMV: GV_WAVES waves x 8 chunks of 64 lanes x 16 bytes
+  const long kmax = (long)GV_WAVES * 8 * gv_chunk(c->dtype == LSS_BF16 ? 2 : 4);
+  if (c->ffn_dim > kmax || (long)c->n_heads * c->head_dim > kmax)
+    return fail("ffn_dim and n_heads * head_dim must be <= 32768 (bf16) / 16384 (float32)");
   if (c->dtype != LSS_F32 && c->dtype != LSS_BF16) return fail("dtype must be LSS_F32 or LSS_BF16");
   if (c->kv_dtype != LSS_F32 && c->kv_dtype != LSS_BF16) return fail("kv_dtype must be LSS_F32 or LSS_BF16");
   if (c->max_rows < 1 || c->max_rows > LSS_ROWS_MAX) return fail("max_rows out of [1, 64]");
@@ -142,6 +146,10 @@ struct lss_engine {
   int logits_rows = 0;
   bool have_target = false;
   int target_pos = 0;
+  // projections of draft / verify rows go through the vector-ALU GEMV
+  // (one arithmetic for every row count); prefill and layer selection
+  // through the MFMA kernels
+  bool gemv = false;
   // kernel timing (lss_profile_kernel)
   int prof_epi = -1, prof_rows = 0;
   std::vector<hipEvent_t> ev_start, ev_stop;
@@ -218,6 +226,68 @@ void gemm_mt(const GemmArgs& ga, hipStream_t s, hipEvent_t t0 = nullptr, hipEven
   }
 }
 
+// GemmArgs of rows r0 .. r0 + Mg - 1 of a projection
+GemmArgs rows_from(const GemmArgs& ga, int r0, int Mg) {
+  GemmArgs g = ga;
+  g.M = Mg;
+  g.A = (const char*)ga.A + (size_t)r0 * ga.lda * 4;
+  if (ga.pin) g.pin = ga.pin + (size_t)r0 * (ga.K / 16);
+  if (ga.xs) g.xs = ga.xs + r0;
+  if (ga.Y) g.Y = ga.Y + (size_t)r0 * ga.ldy;
+  if (ga.R) g.R = ga.R + (size_t)r0 * ga.ldr;
+  if (ga.xo) g.xo = (char*)ga.xo + (size_t)r0 * ga.ldo * 4;
+  if (ga.po) g.po = ga.po + (size_t)r0 * (ga.N / 16);
+  if (ga.part) g.part = ga.part + (size_t)r0 * (ga.N / 16) * 3;
+  return g;
+}
+
+// chunks per wave a vector-GEMV launch over K needs (a power of two)
+int gemv_ncw(int K, int wbytes) {
+  const int CH = gv_chunk(wbytes);
+  const int per = ((K + CH - 1) / CH + GV_WAVES - 1) / GV_WAVES;
+  int ncw = 1;
+  while (ncw < per) ncw *= 2;
+  return ncw;
+}
+// rows per vector-GEMV launch: the activation chunks of a wave stay in registers
+int gemv_cap(int K, int wbytes) { return std::max(1, std::min(GV_MB_MAX, GV_ACT_MAX / gemv_ncw(K, wbytes))); }
+
+template <typename WT, int EPI, int NCW>
+void gemv_launch(const GemmArgs& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  const dim3 grid((g.N + 15) / 16), block(64 * GV_WAVES);
+  if constexpr (NCW == 1) {
+    if (g.M == 1) launch_k(k_gemv<WT, 1, 1, EPI>, grid, block, 0, s, t0, t1, g);
+    else if (g.M == 2) launch_k(k_gemv<WT, 2, 1, EPI>, grid, block, 0, s, t0, t1, g);
+    else if (g.M <= 4) launch_k(k_gemv<WT, 4, 1, EPI>, grid, block, 0, s, t0, t1, g);
+    else launch_k(k_gemv<WT, 8, 1, EPI>, grid, block, 0, s, t0, t1, g);
+  } else if constexpr (NCW == 2) {
+    if (g.M == 1) launch_k(k_gemv<WT, 1, 2, EPI>, grid, block, 0, s, t0, t1, g);
+    else if (g.M == 2) launch_k(k_gemv<WT, 2, 2, EPI>, grid, block, 0, s, t0, t1, g);
+    else launch_k(k_gemv<WT, 4, 2, EPI>, grid, block, 0, s, t0, t1, g);
+  } else if constexpr (NCW == 4) {
+    if (g.M == 1) launch_k(k_gemv<WT, 1, 4, EPI>, grid, block, 0, s, t0, t1, g);
+    else launch_k(k_gemv<WT, 2, 4, EPI>, grid, block, 0, s, t0, t1, g);
+  } else {
+    launch_k(k_gemv<WT, 1, 8, EPI>, grid, block, 0, s, t0, t1, g);
+  }
+}
+
+// M rows in launches of at most gemv_cap rows (each row's arithmetic is the
+// same in any launch)
+template <typename WT, int EPI>
+void gemv_mt(const GemmArgs& ga, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr) {
+  const int ncw = gemv_ncw(ga.K, sizeof(WT));
+  const int cap = gemv_cap(ga.K, sizeof(WT));
+  for (int r0 = 0; r0 < ga.M; r0 += cap) {
+    const int Mg = std::min(cap, ga.M - r0);
+    const GemmArgs g = (r0 == 0 && Mg == ga.M) ? ga : rows_from(ga, r0, Mg);
+    if (ncw == 1) gemv_launch<WT, EPI, 1>(g, s, t0, t1);
+    else if (ncw == 2) gemv_launch<WT, EPI, 2>(g, s, t0, t1);
+    else if (ncw == 4) gemv_launch<WT, EPI, 4>(g, s, t0, t1);
+    else gemv_launch<WT, EPI, 8>(g, s, t0, t1);
+  }
+}
+
 // Sum the elapsed times of recorded event pairs (the stream must be synced).
 void prof_resolve(lss_engine* e) {
   for (int i = 0; i < e->ev_used; ++i) {
@@ -229,7 +299,9 @@ void prof_resolve(lss_engine* e) {
 
 template <int EPI>
 void gemm(lss_engine* e, const GemmArgs& ga) {
-  const bool prof = e->prof_epi == EPI && (e->prof_rows == 0 || e->prof_rows == ga.M);
+  const bool vec = e->gemv;
+  const bool one_launch = !vec || ga.M <= gemv_cap(ga.K, e->bf16 ? 2 : 4);
+  const bool prof = e->prof_epi == EPI && (e->prof_rows == 0 || e->prof_rows == ga.M) && one_launch;
   if (prof) {
     if (e->ev_used == (int)e->ev_start.size()) {
       (void)hipStreamSynchronize(e->stream);
@@ -237,8 +309,13 @@ void gemm(lss_engine* e, const GemmArgs& ga) {
     }
   }
   hipEvent_t t0 = prof ? e->ev_start[e->ev_used] : nullptr, t1 = prof ? e->ev_stop[e->ev_used] : nullptr;
-  if (e->bf16) gemm_mt<uint16_t, EPI>(ga, e->stream, t0, t1);
-  else gemm_mt<float, EPI>(ga, e->stream, t0, t1);
+  if (vec) {
+    if (e->bf16) gemv_mt<uint16_t, EPI>(ga, e->stream, t0, t1);
+    else gemv_mt<float, EPI>(ga, e->stream, t0, t1);
+  } else {
+    if (e->bf16) gemm_mt<uint16_t, EPI>(ga, e->stream, t0, t1);
+    else gemm_mt<float, EPI>(ga, e->stream, t0, t1);
+  }
   if (prof) {
     e->ev_used++;
     const int64_t elt = e->bf16 ? 2 : 4;
@@ -432,6 +509,13 @@ int sync_res(lss_engine* e) {
   return LSS_OK;
 }
 
+// draft and verify rows: projections through the vector-ALU GEMV
+struct GemvScope {
+  lss_engine* e;
+  explicit GemvScope(lss_engine* en) : e(en) { e->gemv = true; }
+  ~GemvScope() { e->gemv = false; }
+};
+
 void fill_u32(lss_engine* e, void* p, size_t n, uint32_t v) {
   const size_t blocks = std::min<size_t>((n + 255) / 256, 65536);
   if (n) hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, e->stream, (uint32_t*)p, n, v);
@@ -572,6 +656,7 @@ int lss_prefill(lss_engine* e, const int32_t* tokens, int32_t n, int32_t* t0_out
 int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, float exit_tau, int32_t* tokens_out,
               int32_t* k_done) {
   if (!e) return LSS_EINVAL;
+  const GemvScope gv(e);
   const auto& c = e->cfg;
   if (!e->have_seq || e->pending_accept) return fail(e, LSS_ESTATE, "draft: needs a prefilled sequence and no pending accept");
   if (!mask || k < 0 || (quant != 0 && quant != 1)) return fail(e, LSS_EINVAL, "draft: bad arguments");
@@ -617,6 +702,7 @@ int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, floa
 
 int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k) {
   if (!e) return LSS_EINVAL;
+  const GemvScope gv(e);
   const auto& c = e->cfg;
   if (!e->have_seq || e->pending_accept) return fail(e, LSS_ESTATE, "verify: needs a prefilled sequence and no pending accept");
   if (drafts) {

@@ -40,6 +40,25 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
+// Sum over the 64 lanes without LDS traffic: four DPP steps inside each
+// 16-lane row (partners lane ^ 1, lane ^ 2, the mirrored lane of the 8-lane
+// half, the mirrored lane of the row; every lane of a row then holds the
+// same row sum, since a + b == b + a), then the four row sums added as
+// (r0 + r1) + (r2 + r3).  The result is the same in every lane.
+template <int CTRL> __device__ __forceinline__ float dpp_t(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = __fadd_rn(v, dpp_t<0xB1>(v));    // quad_perm [1, 0, 3, 2]
+  v = __fadd_rn(v, dpp_t<0x4E>(v));    // quad_perm [2, 3, 0, 1]
+  v = __fadd_rn(v, dpp_t<0x141>(v));   // row_half_mirror
+  v = __fadd_rn(v, dpp_t<0x140>(v));   // row_mirror
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return __fadd_rn(__fadd_rn(a, b), __fadd_rn(c, d));
+}
 // fixed-order sum over the 16 lanes of a lane group
 __device__ __forceinline__ float sum16(float v) {
   for (int o = 8; o >= 1; o >>= 1) v = __fadd_rn(v, __shfl_xor(v, o, 16));
@@ -348,6 +367,51 @@ __device__ __forceinline__ const void* a_row(const void* A, int lda, int m) {
                          : (const void*)(reinterpret_cast<const float*>(A) + (size_t)m * lda);
 }
 
+// One output element (row m, column n) of a projection.  y (and u, the
+// up-projection of SWIGLU) carry the row scale already.  The 16 lanes of an
+// aligned lane group hold columns 16 b .. 16 b + 15 (b = blockIdx.x) of the
+// same row and call this together: RESID's partial sum of squares and
+// LOGITS' tile max / argmax / sum of exponentials are fixed 16-lane trees.
+template <typename WT, int EPI>
+__device__ __forceinline__ void proj_out(const GemmArgs& ga, int m, int M, int n, int cl, float y, float u) {
+  const bool ok = (m < M) && (n < ga.N);
+  if constexpr (EPI == EPI_STORE) {
+    if (ok) ga.Y[(size_t)m * ga.ldy + n] = y;
+  } else if constexpr (EPI == EPI_RESID) {
+    const float h = ok ? __fadd_rn(ga.R[(size_t)m * ga.ldr + n], y) : 0.f;
+    if (ok) ga.Y[(size_t)m * ga.ldy + n] = h;
+    if (ga.xo && ok) AF<WT>::store(ga.xo, (size_t)m * ga.ldo, n, ga.go ? __fmul_rn(h, ga.go[n]) : h);
+    if (ga.po) {
+      const float s2 = sum16(__fmul_rn(h, h));
+      if (cl == 0 && m < M) ga.po[(size_t)m * gridDim.x + blockIdx.x] = s2;
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    const float sg = __fdiv_rn(y, __fadd_rn(1.0f, expf(-y)));
+    const float o = __fmul_rn(sg, u);
+    if (ok) {
+      if (ga.xo) AF<WT>::store(ga.xo, (size_t)m * ga.ldo, n, o);
+      else ga.Y[(size_t)m * ga.ldy + n] = o;
+    }
+  } else {  // EPI_LOGITS: store, then the tile's max / lowest argmax / sum of exp(z - max)
+    if (ok) ga.Y[(size_t)m * ga.ldy + n] = y;
+    float mx = (n < ga.N) ? y : -INFINITY;
+    int idx = n;
+    for (int o = 8; o >= 1; o >>= 1) {
+      const float om = __shfl_xor(mx, o, 16);
+      const int oi = __shfl_xor(idx, o, 16);
+      if (om > mx || (om == mx && oi < idx)) { mx = om; idx = oi; }
+    }
+    float e = (n < ga.N) ? expf(__fsub_rn(y, mx)) : 0.f;
+    e = sum16(e);
+    if (cl == 0 && m < M) {
+      float* p = ga.part + ((size_t)m * gridDim.x + blockIdx.x) * 3;
+      p[0] = mx;
+      p[1] = __int_as_float(idx);
+      p[2] = e;
+    }
+  }
+}
+
 // ONE = the launch has exactly one row (draft steps, greedy steps): the same
 // arithmetic as MT = 1, compiled separately so profiles attribute it apart.
 template <typename WT, int MT, int EPI, bool ONE, bool ALDS>
@@ -510,51 +574,231 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void k_gemm(GemmArgs ga) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int m = t * 16 + 4 * g + j;
-    const bool ok = (m < M) && (n < ga.N);
     float sc = 1.0f;
     bool scaled = false;
     if (m < M) {
       if (norm) { sc = rstd_s[m]; scaled = true; }
       else if (ga.scale == SCALE_XS) { sc = ga.xs[m]; scaled = true; }
     }
-    float y = scaled ? __fmul_rn(v[0][j], sc) : v[0][j];
-    if constexpr (EPI == EPI_STORE) {
-      if (ok) ga.Y[(size_t)m * ga.ldy + n] = y;
-    } else if constexpr (EPI == EPI_RESID) {
-      const float h = ok ? __fadd_rn(ga.R[(size_t)m * ga.ldr + n], y) : 0.f;
-      if (ok) ga.Y[(size_t)m * ga.ldy + n] = h;
-      if (ga.xo && ok) AF<WT>::store(ga.xo, (size_t)m * ga.ldo, n, ga.go ? __fmul_rn(h, ga.go[n]) : h);
-      if (ga.po) {
-        const float s2 = sum16(__fmul_rn(h, h));
-        if (r == 0 && m < M) ga.po[(size_t)m * gridDim.x + blockIdx.x] = s2;
-      }
-    } else if constexpr (EPI == EPI_SWIGLU) {
-      const float u = scaled ? __fmul_rn(v[1][j], sc) : v[1][j];
-      const float sg = __fdiv_rn(y, __fadd_rn(1.0f, expf(-y)));
-      const float o = __fmul_rn(sg, u);
-      if (ok) {
-        if (ga.xo) AF<WT>::store(ga.xo, (size_t)m * ga.ldo, n, o);
-        else ga.Y[(size_t)m * ga.ldy + n] = o;
-      }
-    } else {  // EPI_LOGITS: store and reduce the 16 columns of row m held by lanes 16g..16g+15
-      if (ok) ga.Y[(size_t)m * ga.ldy + n] = y;
-      float mx = (n < ga.N) ? y : -INFINITY;
-      int idx = n;
-      for (int o = 8; o >= 1; o >>= 1) {
-        const float om = __shfl_xor(mx, o, 16);
-        const int oi = __shfl_xor(idx, o, 16);
-        if (om > mx || (om == mx && oi < idx)) { mx = om; idx = oi; }
-      }
-      float e = (n < ga.N) ? expf(__fsub_rn(y, mx)) : 0.f;
-      e = sum16(e);
-      if (r == 0 && m < M) {
-        float* p = ga.part + ((size_t)m * gridDim.x + blockIdx.x) * 3;
-        p[0] = mx;
-        p[1] = __int_as_float(idx);
-        p[2] = e;
-      }
+    const float y = scaled ? __fmul_rn(v[0][j], sc) : v[0][j];
+    const float u = (NACC == 2) ? (scaled ? __fmul_rn(v[NACC - 1][j], sc) : v[NACC - 1][j]) : 0.f;
+    proj_out<WT, EPI>(ga, m, M, n, r, y, u);
+  }
+}
+
+// ---------------------------------------------------------------- decode GEMV (vector ALU)
+// Y[m][n] = sum_k X[m][k] * W[n][k] for the few rows of a draft, greedy or
+// verify step.  Such a launch is bound by the weight stream, so the load
+// pattern is chosen for HBM: each load instruction of a wave reads one 1 KB
+// contiguous piece ("chunk") of one weight row (lane l: the 16 bytes at
+// offset 16 l), with nontemporal hints since the weights are read once.
+// A workgroup owns a 16-row tile of N; its GV_WAVES waves split the chunks
+// of K into contiguous ranges (wave w: chunks [w nc / W, (w + 1) nc / W)),
+// and each wave walks the tile's rows in groups of RG rows, the chunks of
+// its range inside each group, RG x NACC 1 KB loads per step with two steps
+// in flight.  A lane keeps the activation elements of its k in registers
+// (float32, converted once from the projection format) and multiplies them
+// with its 8 (bf16) / 4 (float32) weights in fused multiply-adds.
+//
+// Per (weight row n, activation row m) the arithmetic is fixed by K alone:
+// lane l runs one FMA chain over k = c CH + l EPL + e for the chunks c of
+// its wave's range (ascending) and e ascending, the 64 lane values are
+// summed by the fixed tree of wave_sum_dpp, and the GV_WAVES wave sums are
+// added in wave order.  Nothing depends on M, on the tile or on the row group, so
+// a verify row gets the same bits as a one-row greedy step.
+#define GV_WAVES 8
+#define GV_MB_MAX 8              // activation rows per launch
+#define GV_ACT_MAX 8             // MB x NCW: activation vectors (one chunk of one row) per lane
+
+template <typename WT> struct GVt;
+template <> struct GVt<uint16_t> { static constexpr int EPL = 8, AV = 2; };   // AV: uint4 per lane of split-bf16 x
+template <> struct GVt<float> { static constexpr int EPL = 4, AV = 1; };
+__host__ __device__ __forceinline__ int gv_chunk(int wbytes) { return wbytes == 2 ? 512 : 256; }
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 16 bytes of weights as floats
+template <typename WT> __device__ __forceinline__ void unpack_w(const uint4& w, float (&f)[GVt<WT>::EPL]);
+template <> __device__ __forceinline__ void unpack_w<uint16_t>(const uint4& w, float (&f)[8]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(u[i] << 16);
+    f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+template <> __device__ __forceinline__ void unpack_w<float>(const uint4& w, float (&f)[4]) {
+  f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y); f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
+}
+// activation elements of one lane from the projection format (hi + lo is exact)
+template <typename WT>
+__device__ __forceinline__ void unpack_x(const uint4 (&a)[GVt<WT>::AV], float (&x)[GVt<WT>::EPL]) {
+  if constexpr (sizeof(WT) == 2) {
+    const uint32_t h[4] = {a[0].x, a[0].y, a[0].z, a[0].w}, l[4] = {a[1].x, a[1].y, a[1].z, a[1].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __fadd_rn(__uint_as_float(h[i] << 16), __uint_as_float(l[i] << 16));
+      x[2 * i + 1] = __fadd_rn(__uint_as_float(h[i] & 0xffff0000u), __uint_as_float(l[i] & 0xffff0000u));
+    }
+  } else {
+    x[0] = __uint_as_float(a[0].x); x[1] = __uint_as_float(a[0].y);
+    x[2] = __uint_as_float(a[0].z); x[3] = __uint_as_float(a[0].w);
+  }
+}
+
+// MB: activation rows (M <= MB); NCW: chunks per wave the launch may need
+// (>= ceil(nc / GV_WAVES)), MB * NCW <= GV_ACT_MAX.
+template <typename WT, int MB, int NCW, int EPI>
+__global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
+  constexpr int EPL = GVt<WT>::EPL, AV = GVt<WT>::AV, CH = 64 * EPL;
+  constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
+  constexpr int RG = 8 / NACC;                  // weight rows per step: 8 loads of 1 KB
+  constexpr int NG = 16 / RG;                   // row groups per tile
+  constexpr int NU = NG * NCW;                  // steps per wave (chunks past the range are skipped)
+  static_assert(MB * NCW <= GV_ACT_MAX, "activation registers");
+  __shared__ float part_s[GV_WAVES][NACC][MB][16];
+  __shared__ float red_s[GV_WAVES][MB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int M = ga.M, K = ga.K;
+  const int nc = (K + CH - 1) / CH;
+  const int c0 = wave * nc / GV_WAVES;
+  const int ncw = (wave + 1) * nc / GV_WAVES - c0;       // chunks of this wave (<= NCW)
+  const int tile0 = blockIdx.x * 16;
+  int seg = 0, nloc = tile0;
+  while (seg < 2 && nloc >= ga.nseg[seg]) { nloc -= ga.nseg[seg]; ++seg; }
+  const WT* wbase[NACC];
+  wbase[0] = reinterpret_cast<const WT*>(ga.w[seg]) + (size_t)nloc * K;
+  if constexpr (NACC == 2) wbase[NACC - 1] = reinterpret_cast<const WT*>(ga.w2) + (size_t)tile0 * K;
+  const int kl = lane * EPL;
+  const int nrow = min(16, ga.N - tile0);                 // rows of the tile inside N
+
+  // (1) this wave's activation chunks (raw projection format)
+  uint4 xr[NCW][MB][AV];
+#pragma unroll
+  for (int i = 0; i < NCW; ++i) {
+    const int k = min((c0 + min(i, max(ncw - 1, 0))) * CH + kl, K - EPL);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const uint4* pa = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(ga.A) +
+                                                       ((size_t)min(m, M - 1) * ga.lda + k) * 4);
+#pragma unroll
+      for (int v = 0; v < AV; ++v) xr[i][m][v] = pa[v];
     }
   }
+  // (2) RMSNorm partial sums of squares (one per thread and row), summed at the end
+  const bool norm = ga.scale == SCALE_NORM;
+  const int T = K >> 4;                                   // <= 64 * GV_WAVES
+  const float* pp = norm ? ga.pin : reinterpret_cast<const float*>(ga.A);
+  float pr[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) pr[m] = pp[norm ? (size_t)min(m, M - 1) * T + min((int)threadIdx.x, T - 1) : 0];
+  // (3) weight steps: unit u = (row group u / NCW, chunk c0 + u % NCW)
+  auto unit_load = [&](uint4 (&w)[RG][NACC], int u) {
+    const int g = u / NCW, i = u % NCW;
+    const int k = min((c0 + i) * CH + kl, K - EPL);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const size_t ro = (size_t)min(g * RG + r, nrow - 1) * K + k;
+#pragma unroll
+      for (int q = 0; q < NACC; ++q) w[r][q] = ld_nt16(wbase[q] + ro);
+    }
+  };
+  uint4 wb[2][RG][NACC];
+  if (0 < ncw) unit_load(wb[0], 0);
+  if (1 % NCW < ncw) unit_load(wb[1], 1);
+  __builtin_amdgcn_sched_barrier(0);
+  // activations as float32; lanes past K hold zeros
+  float x[NCW][MB][EPL];
+#pragma unroll
+  for (int i = 0; i < NCW; ++i) {
+    const bool kv = (c0 + i) * CH + kl < K;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      unpack_x<WT>(xr[i][m], x[i][m]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[i][m][e] = kv ? x[i][m][e] : 0.f;
+    }
+  }
+
+  float acc[RG][NACC][MB];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int g = u / NCW, i = u % NCW;
+    if (i == 0) {
+#pragma unroll
+      for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int q = 0; q < NACC; ++q)
+#pragma unroll
+          for (int m = 0; m < MB; ++m) acc[r][q][m] = 0.f;
+    }
+    if (i < ncw) {                                         // wave-uniform
+#pragma unroll
+      for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int q = 0; q < NACC; ++q) {
+          float wf[EPL];
+          unpack_w<WT>(wb[u & 1][r][q], wf);
+#pragma unroll
+          for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[r][q][m] = fmaf(wf[e], x[i][m][e], acc[r][q][m]);
+        }
+    }
+    if (u + 2 < NU && (u + 2) % NCW < ncw) unit_load(wb[u & 1], u + 2);
+    if (i == NCW - 1) {                                    // group g done: lane sums -> LDS
+#pragma unroll
+      for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int q = 0; q < NACC; ++q)
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            const float t = wave_sum_dpp(acc[r][q][m]);
+            if (lane == 0) part_s[wave][q][m][g * RG + r] = t;
+          }
+    }
+  }
+  if (norm) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      float v = ((int)threadIdx.x < T) ? pr[m] : 0.f;
+      v = wave_sum_dpp(v);
+      if (lane == 0) red_s[wave][m] = v;
+    }
+  }
+  __syncthreads();
+  // epilogue: thread (m, i) = (tid / 16, tid % 16) -> row m, column tile0 + i
+  if (threadIdx.x >= 16 * MB) return;
+  const int m = threadIdx.x >> 4, i = threadIdx.x & 15;
+  float sc = 1.0f;
+  bool scaled = false;
+  if (m < M) {
+    if (norm) {
+      float v = red_s[0][m];
+#pragma unroll
+      for (int w = 1; w < GV_WAVES; ++w) v = __fadd_rn(v, red_s[w][m]);
+      sc = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(v, (float)K), ga.eps)));
+      scaled = true;
+    } else if (ga.scale == SCALE_XS) {
+      sc = ga.xs[m];
+      scaled = true;
+    }
+  }
+  float y[NACC];
+#pragma unroll
+  for (int q = 0; q < NACC; ++q) {
+    float v = part_s[0][q][m][i];
+#pragma unroll
+    for (int w = 1; w < GV_WAVES; ++w) v = __fadd_rn(v, part_s[w][q][m][i]);
+    y[q] = scaled ? __fmul_rn(v, sc) : v;
+  }
+  proj_out<WT, EPI>(ga, m, M, tile0 + i, i, y[0], NACC == 2 ? y[NACC - 1] : 0.f);
 }
 
 // ---------------------------------------------------------------- attention
@@ -816,8 +1060,16 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
   for (int i = tid; i < nqb * HD; i += ATT_THREADS) {
     const int qi = i / HD, dd = i % HD;
     float acc = 0.f;
-    for (int cc = 0; cc < a.nch; ++cc)
-      acc = __fadd_rn(acc, __fmul_rn(pb[((size_t)cc * ATT_QB + qi) * (HD + 2) + dd], wgt[qi * ATT_CH + cc]));
+    // chunk partials in batches of 16 independent loads (indexes clamped into
+    // the launch's chunks), then added in chunk order
+    for (int c0 = 0; c0 < a.nch; c0 += 16) {
+      float pv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pv[j] = pb[((size_t)min(c0 + j, a.nch - 1) * ATT_QB + qi) * (HD + 2) + dd];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (c0 + j < a.nch) acc = __fadd_rn(acc, __fmul_rn(pv[j], wgt[qi * ATT_CH + c0 + j]));
+    }
     const int gq = q0 + qi;
     const int m = gq / G, h = kh * G + gq % G;
     if (a.self_kv) {
