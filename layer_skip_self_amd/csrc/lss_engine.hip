@@ -30,7 +30,7 @@ constexpr int kWinMax = LSS_WINDOW_MAX;
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t kc, vc, hs, hmid, xa, xb, xc, pa, pc, xs, qkv, apart, actr, aout, act, logits, hpart, rope, target,
+  size_t kc, vc, hs, hmid, xa, xb, xc, pa, pc, xs, qkv, apart, aout, act, logits, hpart, rope, target,
       dpg0, dpg1, dpx, dpdec, tok, seqtok, res, total;
   int xld, nch_max, nz_max, ntile;
 };
@@ -84,7 +84,6 @@ Layout make_layout(const lss_config* c) {
   L.xs = take(R * 4);
   L.qkv = take(R * (Hq + 2 * Hkv) * hd * 4);
   L.apart = take(Hkv * (size_t)L.nz_max * L.nch_max * ATT_QB * (hd + 2) * 4);
-  L.actr = take(Hkv * (size_t)L.nz_max * 4);
   L.aout = take(R * Hq * hd * 4);
   L.act = take(R * F * 4);
   L.logits = take(R * V * 4);
@@ -129,7 +128,6 @@ struct lss_engine {
   float *hs, *hmid, *xs, *qkv, *apart, *aout, *act, *logits, *hpart, *target, *dpg[2], *dpx, *dpdec;
   void *xa, *xb, *xc;   // projection inputs: layer input (attention-norm gain), attention / FFN output, mid-layer
   float *pa, *pc;       // partial sums of squares of the residual rows behind xa and xc
-  int* actr;
   float2* rope;
   int32_t *tok, *seqtok;
   HeadRes* res;
@@ -351,7 +349,6 @@ void attention(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
   a.max_seq = c.max_seq; a.Hq = c.n_heads; a.Hkv = c.n_kv_heads; a.M = M;
   a.pos0 = pos0; a.pos_step = mode == MODE_DP ? 0 : 1;
   a.part = e->apart; a.nz_max = e->lay.nz_max; a.nch_max = e->lay.nch_max;
-  a.counters = e->actr;
   a.out = e->aout;
   a.xo = quant ? nullptr : e->xb;
   a.scale = (float)(1.0 / std::sqrt((double)hd));
@@ -363,8 +360,13 @@ void attention(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
   const int G = c.n_heads / c.n_kv_heads;
   a.nz = (G * M + ATT_QB - 1) / ATT_QB;
   const dim3 grid(a.nch, c.n_kv_heads, a.nz);
-  if (hd == 128) hipLaunchKernelGGL((k_attention<KT, WT, 128>), grid, dim3(ATT_THREADS), 0, e->stream, a);
-  else hipLaunchKernelGGL((k_attention<KT, WT, 64>), grid, dim3(ATT_THREADS), 0, e->stream, a);
+  if (hd == 128) {
+    hipLaunchKernelGGL((k_attention<KT, WT, 128>), grid, dim3(ATT_THREADS), 0, e->stream, a);
+    hipLaunchKernelGGL((k_attn_merge<WT, 128>), dim3(ATT_QB, c.n_kv_heads, a.nz), dim3(128), 0, e->stream, a);
+  } else {
+    hipLaunchKernelGGL((k_attention<KT, WT, 64>), grid, dim3(ATT_THREADS), 0, e->stream, a);
+    hipLaunchKernelGGL((k_attn_merge<WT, 64>), dim3(ATT_QB, c.n_kv_heads, a.nz), dim3(64), 0, e->stream, a);
+  }
 }
 
 template <typename WT>
@@ -566,7 +568,7 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
   e->xa = ws + lay.xa; e->xb = ws + lay.xb; e->xc = ws + lay.xc;
   e->pa = (float*)(ws + lay.pa); e->pc = (float*)(ws + lay.pc);
   e->xs = (float*)(ws + lay.xs); e->qkv = (float*)(ws + lay.qkv);
-  e->apart = (float*)(ws + lay.apart); e->actr = (int*)(ws + lay.actr); e->aout = (float*)(ws + lay.aout);
+  e->apart = (float*)(ws + lay.apart); e->aout = (float*)(ws + lay.aout);
   e->act = (float*)(ws + lay.act); e->logits = (float*)(ws + lay.logits); e->hpart = (float*)(ws + lay.hpart);
   e->rope = (float2*)(ws + lay.rope); e->target = (float*)(ws + lay.target);
   e->dpg[0] = (float*)(ws + lay.dpg0); e->dpg[1] = (float*)(ws + lay.dpg1); e->dpx = (float*)(ws + lay.dpx);

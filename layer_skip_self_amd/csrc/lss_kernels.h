@@ -59,6 +59,17 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
   return __fadd_rn(__fadd_rn(a, b), __fadd_rn(c, d));
 }
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_t<0xB1>(v));
+  v = fmaxf(v, dpp_t<0x4E>(v));
+  v = fmaxf(v, dpp_t<0x141>(v));
+  v = fmaxf(v, dpp_t<0x140>(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
 // fixed-order sum over the 16 lanes of a lane group
 __device__ __forceinline__ float sum16(float v) {
   for (int o = 8; o >= 1; o >>= 1) v = __fadd_rn(v, __shfl_xor(v, o, 16));
@@ -802,17 +813,20 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
 }
 
 // ---------------------------------------------------------------- attention
-// One launch per layer: rotary embedding of the queries and of this launch's
-// new keys, KV-cache append, split-key attention and the merge.
+// Two launches per layer: k_attention (rotary embedding of the queries and
+// of this launch's new keys, KV-cache append, split-key partials) and
+// k_attn_merge.
 //
 // Keys are cut into fixed 64-position chunks of absolute cache positions; a
 // workgroup (chunk c, kv head, query block) computes, for each of its
 // queries, the chunk's max score, sum of exponentials and weighted value sum.
-// The last workgroup of a (kv head, query block) to finish -- found with an
-// integer atomic counter -- merges the chunks in chunk order (and, for
-// layer-selection rows, the row's own key/value).  The merge order depends
-// only on positions, never on the rows in the launch or on timing, so a
-// verify row equals the greedy step at the same position bit for bit.
+// k_attn_merge then combines the chunks of each query in chunk order (and,
+// for layer-selection rows, the row's own key/value).  The merge order
+// depends only on positions, never on the rows in the launch or on timing,
+// so a verify row equals the greedy step at the same position bit for bit.
+// The launch boundary makes the partials visible to the merge; a merge
+// inside the first kernel would need a device-scope fence per workgroup,
+// and on this chip each such fence writes back the L2.
 //
 // Row m (position pos0 + m*pos_step) sees cache position u iff
 //   u < lim_base + m*lim_step            (committed prefix / causal rows)
@@ -839,7 +853,6 @@ struct AttnArgs {
   int nch, nz;                     // key chunks, query blocks in this launch
   float* part;                     // [Hkv][nz_max][nch_max][QB][hd + 2]
   int nz_max, nch_max;
-  int* counters;                   // [Hkv][nz_max], zero between launches
   float* out;                      // [M][Hq * hd] float32 output (when xo == nullptr)
   void* xo;                        // [M][Hq * hd] projection-format output
   float scale;                     // 1/sqrt(hd)
@@ -921,8 +934,6 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
   __shared__ float q_s[ATT_QB][HD];
   __shared__ float p_s[ATT_QB][ATT_CH];
   __shared__ float st_s[ATT_QB][2];
-  __shared__ float self_s[ATT_QB];
-  __shared__ int last_s;
   const int c = blockIdx.x, kh = blockIdx.y, z = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int nq = G * a.M;
@@ -970,9 +981,9 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
           s = __fmul_rn(dot, a.scale);
         }
       }
-      const float mx = wave_max(s);
+      const float mx = wave_max_dpp(s);
       const float e = (s == -INFINITY) ? 0.f : expf(__fsub_rn(s, mx));
-      const float l = wave_sum(e);
+      const float l = wave_sum_dpp(e);
       p_s[qi][u] = e;
       if (lane == 0) { st_s[qi][0] = mx; st_s[qi][1] = l; }
     }
@@ -993,93 +1004,72 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
     o[dd] = acc;
     if (dd == 0) { o[HD] = st_s[qi][0]; o[HD + 1] = st_s[qi][1]; }
   }
-  // the last workgroup of this (kv head, query block) merges the chunks
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    int* ctr = a.counters + kh * a.nz_max + z;
-    const int prev = atomicAdd(ctr, 1);
-    last_s = (prev == a.nch - 1);
-    if (last_s) atomicExch(ctr, 0);
-  }
-  __syncthreads();
-  if (!last_s) return;
-  __threadfence();
-  const int nqb = min(ATT_QB, nq - q0);
-  if (a.self_kv) {       // score of each row's own key
-    for (int qi = wave; qi < nqb; qi += ATT_THREADS / 64) {
-      const int gq = q0 + qi;
-      const int m = gq / G;
+}
+
+// Merge of the chunk partials: one workgroup of HD threads per query
+// (blockIdx = (query in block, kv head, query block)).  Wave 0 reduces the
+// chunk statistics with lane = chunk (nch <= 64): M = max of the chunk
+// maxima over chunks that saw a key (and, for layer-selection rows, the
+// row's own score), weights w_c = exp(m_c - M), normalizer
+// L = sum_c l_c w_c by the fixed lane tree of wave_sum_dpp (+ the own
+// key's weight).  Thread dd then adds w_c * partial_c[dd] over the chunks in
+// chunk order and divides by L.  Every step depends on positions only.
+#define ATT_MERGE_MAXCH 64
+template <typename WT, int HD>
+__global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
+  __shared__ float wgt[ATT_MERGE_MAXCH];
+  __shared__ float st_s[2];
+  const int qi = blockIdx.x, kh = blockIdx.y, z = blockIdx.z;
+  const int G = a.Hq / a.Hkv;
+  const int gq = z * ATT_QB + qi;
+  if (gq >= G * a.M) return;                          // whole workgroup
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int m = gq / G, h = kh * G + gq % G;
+  const float* pb = a.part + ((size_t)kh * a.nz_max + z) * a.nch_max * ATT_QB * (HD + 2) + (size_t)qi * (HD + 2);
+  const size_t cstride = (size_t)ATT_QB * (HD + 2);
+  // this thread's value partials, all chunks issued at once
+  float pv[ATT_MERGE_MAXCH];
+#pragma unroll
+  for (int c = 0; c < ATT_MERGE_MAXCH; ++c)
+    if (c < a.nch) pv[c] = pb[(size_t)c * cstride + tid];
+  if (tid < 64) {
+    const int c = min(lane, a.nch - 1);
+    const float mc = pb[(size_t)c * cstride + HD], lc = pb[(size_t)c * cstride + HD + 1];
+    const bool seen = lane < a.nch && lc != 0.f;
+    float self = -INFINITY;
+    if (a.self_kv) {                                   // the row's own key (rotated), scaled score
       const int pos = a.pos0 + m * a.pos_step;
+      const float* qx = a.qkv + (size_t)m * a.ldqkv + (size_t)h * HD;
       const float* kx = a.qkv + (size_t)m * a.ldqkv + (size_t)(a.Hq + kh) * HD;
       const float2* cs = a.cs + (size_t)pos * (HD / 2);
       float dot = 0.f;
-      for (int dd = lane; dd < HD; dd += 64) dot = fmaf(q_s[qi][dd], rope_elem(kx, cs, dd, HD / 2), dot);
-      dot = wave_sum(dot);
-      if (lane == 0) self_s[qi] = __fmul_rn(dot, a.scale);
+      for (int dd = lane; dd < HD; dd += 64)
+        dot = fmaf(rope_elem(qx, cs, dd, HD / 2), rope_elem(kx, cs, dd, HD / 2), dot);
+      self = __fmul_rn(wave_sum_dpp(dot), a.scale);
     }
-  }
-  // merge: (1) every chunk's {max, sum} per query -> LDS in one parallel pass;
-  // (2) one thread per query: max over the chunks that saw a key, chunk weights
-  // exp(m_c - M) and the normalizer, in chunk order; (3) weighted value sums
-  // in chunk order with unconditional loads (a chunk without visible keys has
-  // weight 0 and an all-zero partial, adding exactly 0).
-  const float* pb = a.part + ((size_t)kh * a.nz_max + z) * a.nch_max * ATT_QB * (HD + 2);
-  float (*stat)[ATT_QB][2] = reinterpret_cast<float (*)[ATT_QB][2]>(&kv_s[0][0]);   // [nch <= 64][QB][2]
-  float* wgt = &p_s[0][0];                                                          // [QB][64]
-  __syncthreads();
-  for (int i = tid; i < a.nch * nqb; i += ATT_THREADS) {
-    const int cc = i / nqb, qi = i - cc * nqb;
-    const float* pc = pb + ((size_t)cc * ATT_QB + qi) * (HD + 2);
-    stat[cc][qi][0] = pc[HD];
-    stat[cc][qi][1] = pc[HD + 1];
-  }
-  __syncthreads();
-  if (tid < nqb) {
-    const int qi = tid;
-    float M = -INFINITY;
-    for (int cc = 0; cc < a.nch; ++cc)
-      if (stat[cc][qi][1] != 0.f) M = fmaxf(M, stat[cc][qi][0]);
-    if (a.self_kv) M = fmaxf(M, self_s[qi]);
-    float L = 0.f;
-    for (int cc = 0; cc < a.nch; ++cc) {
-      const float lc = stat[cc][qi][1];
-      const float wc = (lc != 0.f) ? expf(__fsub_rn(stat[cc][qi][0], M)) : 0.f;
-      wgt[qi * ATT_CH + cc] = wc;
-      if (lc != 0.f) L = __fadd_rn(L, __fmul_rn(lc, wc));
-    }
+    const float M = fmaxf(wave_max_dpp(seen ? mc : -INFINITY), self);
+    const float wc = seen ? expf(__fsub_rn(mc, M)) : 0.f;
+    float L = wave_sum_dpp(seen ? __fmul_rn(lc, wc) : 0.f);
     float ws = 0.f;
     if (a.self_kv) {
-      ws = expf(__fsub_rn(self_s[qi], M));
+      ws = expf(__fsub_rn(self, M));
       L = __fadd_rn(L, ws);
     }
-    st_s[qi][0] = L;
-    st_s[qi][1] = ws;
+    if (lane < ATT_MERGE_MAXCH) wgt[lane] = wc;
+    if (lane == 0) { st_s[0] = L; st_s[1] = ws; }
   }
   __syncthreads();
-  for (int i = tid; i < nqb * HD; i += ATT_THREADS) {
-    const int qi = i / HD, dd = i % HD;
-    float acc = 0.f;
-    // chunk partials in batches of 16 independent loads (indexes clamped into
-    // the launch's chunks), then added in chunk order
-    for (int c0 = 0; c0 < a.nch; c0 += 16) {
-      float pv[16];
+  float acc = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) pv[j] = pb[((size_t)min(c0 + j, a.nch - 1) * ATT_QB + qi) * (HD + 2) + dd];
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (c0 + j < a.nch) acc = __fadd_rn(acc, __fmul_rn(pv[j], wgt[qi * ATT_CH + c0 + j]));
-    }
-    const int gq = q0 + qi;
-    const int m = gq / G, h = kh * G + gq % G;
-    if (a.self_kv) {
-      const float v = a.qkv[(size_t)m * a.ldqkv + (size_t)(a.Hq + a.Hkv + kh) * HD + dd];
-      acc = __fadd_rn(acc, __fmul_rn(v, st_s[qi][1]));
-    }
-    const float o = __fdiv_rn(acc, st_s[qi][0]);
-    if (a.xo) AF<WT>::store(a.xo, (size_t)m * a.Hq * HD, h * HD + dd, o);
-    else a.out[(size_t)m * a.Hq * HD + (size_t)h * HD + dd] = o;
+  for (int c = 0; c < ATT_MERGE_MAXCH; ++c)
+    if (c < a.nch) acc = __fadd_rn(acc, __fmul_rn(pv[c], wgt[c]));
+  if (a.self_kv) {
+    const float v = a.qkv[(size_t)m * a.ldqkv + (size_t)(a.Hq + a.Hkv + kh) * HD + tid];
+    acc = __fadd_rn(acc, __fmul_rn(v, st_s[1]));
   }
+  const float o = __fdiv_rn(acc, st_s[0]);
+  if (a.xo) AF<WT>::store(a.xo, (size_t)m * a.Hq * HD, h * HD + tid, o);
+  else a.out[(size_t)m * a.Hq * HD + (size_t)h * HD + tid] = o;
 }
 
 // ---------------------------------------------------------------- LM head reduce / accept
