@@ -202,7 +202,7 @@ def main():
         "draft_gemv_gbps": round(achieved, 1) if achieved else None,
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_gemv<bf16,1,SWIGLU,lds>: draft gate/up projection + SwiGLU, 1 row",
+            "kernel": "k_gemv<bf16,1,1,SWIGLU>: draft gate/up projection + SwiGLU, 1 row",
             "achieved": round(achieved, 1) if achieved else None,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
