@@ -35,6 +35,18 @@ WORKLOADS = {
                       desc="Llama-2-7B shape, prompt 512, 256 generated, static skip of layers 1,3,..,31, K 6"),
     "tiny": dict(shape="tiny", prompt=32, gen=64, policy={"mode": "static", "k_max": 4, "skip": (1, 2)},
                  desc="4-layer float32 model, prompt 32, 64 generated, skip {1,2}, K 4"),
+    # CAS-Spec three-level cascade on the Llama-3-8B shape.  Levels as (layers
+    # skipped in total, of which the last `exit` by early exit, int8
+    # activations), fast -> precise: L1 skips 70% of 32 layers (4 by early
+    # exit, 18 chosen by the DP), L2 skips 30% (DP) with int8 activations, L3
+    # runs all layers with int8 activations.  DyTC routing with at most 8
+    # drafts per round and a latency model fitted on this engine.
+    "cascade_8b": dict(shape="llama3_8b", prompt=(128, 512, 2048), gen=256,
+                       policy={"mode": "cascade", "k_max": 8, "interval": 32,
+                               "levels": [(22, 4, False), (10, 0, True), (0, 0, True)]},
+                       desc="Llama-3-8B shape, CAS-Spec cascade L1 (22 skipped: 4 early exit + 18 DP) / "
+                            "L2 (10 skipped by DP, int8) / L3 (int8), DyTC routing, K <= 8, prompts 128, 512, "
+                            "2048 with 256 generated each"),
 }
 
 
@@ -55,7 +67,10 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
     model._get("lm_head"); model._get("final_norm")
     pol = oracle.Policy(K=policy.get("k_max", 4), skip=tuple(policy.get("skip", ())),
                         dp_skip=policy.get("n_skip") if policy["mode"] == "dp" else None,
-                        interval=policy.get("interval", 32), tau=policy.get("exit_tau", 0.0))
+                        interval=policy.get("interval", 32), tau=policy.get("exit_tau", 0.0),
+                        quant=bool(policy.get("quant", False)),
+                        cascade=list(policy["levels"]) if policy["mode"] == "cascade" else None,
+                        latency_beta=tuple(policy.get("beta", (1.0, 0.0, 1.0))))
     sample = np.asarray(prompt[:n_prompt])
     t0 = time.perf_counter()
     toks, recs = oracle.speculative_generate(model, sample, n_tokens, pol)
@@ -66,10 +81,11 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
                       f"{len(recs)} rounds in {dt:.1f} s"}
 
 
-def recorded_traffic():
+def recorded_traffic(bytes_per_launch):
     """HBM bytes per launch of the draft gate/up kernel measured with rocprofv3
     counters (profiles/draft_gemv_llama3_8b.md), or None when the kernel
-    source changed since the counters were taken."""
+    source changed since the counters were taken or the launch is not the
+    recorded one (another model shape)."""
     import hashlib
     src = os.path.join(ROOT, "layer_skip_self_amd", "csrc", "lss_kernels.h")
     rec = os.path.join(ROOT, "profiles", "draft_gemv_llama3_8b.md")
@@ -81,6 +97,8 @@ def recorded_traffic():
                 k, v = line[2:].split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
         if fields.get("kernel source sha256") != sha:
+            return None
+        if int(fields["algorithmic bytes per launch"].split()[0]) != int(bytes_per_launch):
             return None
         return int(fields["traffic bytes per launch"])
     except (OSError, KeyError, ValueError):
@@ -116,64 +134,100 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     weights = lss_synth.make_weights(shape, device=dev)
-    prompt = lss_synth.make_prompt(shape, wl["prompt"])
+    lens = wl["prompt"] if isinstance(wl["prompt"], tuple) else (wl["prompt"],)
+    # one seeded prompt per length (the first uses the shape's prompt seed)
+    prompts = [lss_synth.make_prompt(shape, n, seed=shape.prompt_seed + i) for i, n in enumerate(lens)]
     G = wl["gen"] if args.gen is None else args.gen
-    max_seq = wl["prompt"] + G + 33
+    max_seq = max(lens) + G + 33
     eng = Engine(shape, weights, max_seq=max_seq, max_rows=64)
-    stream = eng.stream
+    policy = dict(wl["policy"])
+    latency = None
+    if policy["mode"] == "cascade":
+        # DyTC latency model of this engine: timed one-token drafts at the
+        # levels' depths and at full depth (the verify), seq_len 128 .. 2048
+        L = shape.n_layers
+        depths = sorted({L - lv[0] for lv in policy["levels"]} | {L})
+        cal_lens = tuple(n for n in (128, 512, 1024, 2048) if n + 40 <= max_seq)
+        cal_prompt = lss_synth.make_prompt(shape, max(cal_lens), seed=shape.prompt_seed + 99)
+        beta, samples, err = eng.calibrate_latency(cal_prompt, cal_lens, depths)
+        policy["beta"] = beta
+        latency = {"beta": [float(b) for b in beta], "seq_lens": list(cal_lens), "depths": depths,
+                   "samples": len(samples), "max_rel_err": round(err, 4)}
 
-    def run(policy):
+    def run(pol, prompt):
         torch.cuda.synchronize()
         t = time.perf_counter()
-        toks, st = eng.generate(prompt, G, policy)
+        toks, st = eng.generate(prompt, G, pol)
         torch.cuda.synchronize()
         return toks, st, time.perf_counter() - t
 
     for _ in range(args.warmup):
-        run(wl["policy"])
+        for pr in prompts:
+            run(policy, pr)
     eng.profile_kernel("gate_up", rows=1)
-    times, stats, spec_toks = [], [], None
+    spec_t = [0.0] * len(prompts)
+    stats, spec_toks = [None] * len(prompts), [None] * len(prompts)
     torch.cuda.synchronize()
     t_all = time.perf_counter()
     for _ in range(args.steps):
-        toks, st, dt = run(wl["policy"])
-        times.append(dt)
-        stats.append(st)
-        spec_toks = toks
+        for i, pr in enumerate(prompts):
+            toks, st, dt = run(policy, pr)
+            spec_t[i] += dt
+            stats[i] = st
+            spec_toks[i] = toks
     torch.cuda.synchronize()
     t_all = time.perf_counter() - t_all
     k_ms, k_n, k_bytes = eng.profile_read()
     eng.profile_kernel("gate_up", enable=False)
 
-    ar_times, ar_toks = [], None
+    ar_t, ar_toks = [0.0] * len(prompts), [None] * len(prompts)
     if args.ar_steps > 0:
-        run({"mode": "ar"})
+        for pr in prompts:
+            run({"mode": "ar"}, pr)
     for _ in range(args.ar_steps):
-        ar_toks, _, dt = run({"mode": "ar"})
-        ar_times.append(dt)
+        for i, pr in enumerate(prompts):
+            ar_toks[i], _, dt = run({"mode": "ar"}, pr)
+            ar_t[i] += dt
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    pre = []
-    for _ in range(3):
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        eng.prefill(prompt)
-        torch.cuda.synchronize()
-        pre.append(time.perf_counter() - t)
-    prefill_s = min(pre)
+    prefill_s = []
+    for pr in prompts:
+        pre = []
+        for _ in range(3):
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            eng.prefill(pr)
+            torch.cuda.synchronize()
+            pre.append(time.perf_counter() - t)
+        prefill_s.append(min(pre))
 
+    n_p = len(prompts)
     step_s = t_all / args.steps
-    value = G / step_s
-    ar_value = G / (sum(ar_times) / len(ar_times)) if ar_times else None
-    st = stats[-1]
-    rounds = st["rounds"]
+    value = n_p * G / step_s
+    ar_value = n_p * G / (sum(ar_t) / args.ar_steps) if args.ar_steps > 0 else None
+    rounds = sum(st["rounds"] for st in stats)
+    accepted = sum(st["accepted"] for st in stats)
+    drafted = sum(st["drafted"] for st in stats)
+    emitted = sum(st["emitted"] for st in stats)
+    dp_runs = sum(st["dp_runs"] for st in stats)
     avg_launch_us = 1e3 * k_ms / max(k_n, 1)
     bytes_per_launch = k_bytes / max(k_n, 1)
     achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9 if k_n else None
+    per_prompt = []
+    for i, n in enumerate(lens):
+        st = stats[i]
+        sp = G * args.steps / spec_t[i]
+        ar = G * args.ar_steps / ar_t[i] if args.ar_steps > 0 else None
+        per_prompt.append({"prompt": n, "tokens_per_s": round(sp, 3),
+                           "ar_tokens_per_s": round(ar, 3) if ar else None,
+                           "speedup_vs_ar": round(sp / ar, 4) if ar else None,
+                           "mean_accepted": round(st["accepted"] / max(st["rounds"], 1), 4),
+                           "drafted_per_round": round(st["drafted"] / max(st["rounds"], 1), 4),
+                           "prefill_ms": round(1e3 * prefill_s[i], 3)})
     out = {
         "metric": "gen tokens/s @bs1 (Llama-3-8B shape), speedup vs AR, draft GEMV HBM GB/s",
         "value": round(value, 3),
@@ -187,35 +241,39 @@ def main():
         "vs_baseline": None,
         "dtype": shape.dtype,
         "data": "synthetic (seeded random-init weights and uniform-random prompt)",
-        "config": {"workload": wl["desc"], "global_batch": 1, "seq_len": wl["prompt"] + G,
+        "config": {"workload": wl["desc"], "global_batch": 1, "seq_len": max(lens) + G,
                    "parallelism": "none (1 GPU)"},
         "speedup_vs_ar": round(value / ar_value, 4) if ar_value else None,
         "ar_tokens_per_s": round(ar_value, 3) if ar_value else None,
-        "lossless": (spec_toks == ar_toks) if ar_toks is not None else None,
-        "mean_accepted": round(st["accepted"] / max(rounds, 1), 4),
-        "tokens_per_round": round((st["emitted"] - 1) / max(rounds, 1), 4),
-        "drafted_per_round": round(st["drafted"] / max(rounds, 1), 4),
+        "lossless": (spec_toks == ar_toks) if args.ar_steps > 0 else None,
+        "mean_accepted": round(accepted / max(rounds, 1), 4),
+        "tokens_per_round": round((emitted - n_p) / max(rounds, 1), 4),
+        "drafted_per_round": round(drafted / max(rounds, 1), 4),
         "rounds": rounds,
-        "dp_runs": st["dp_runs"],
-        "prefill_ms": round(1e3 * prefill_s, 3),
-        "decode_tokens_per_s": round((G - 1) / (step_s - prefill_s), 3),
+        "dp_runs": dp_runs,
+        "prefill_ms": round(1e3 * sum(prefill_s), 3),
+        "decode_tokens_per_s": round(n_p * (G - 1) / (step_s - sum(prefill_s)), 3),
         "draft_gemv_gbps": round(achieved, 1) if achieved else None,
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_gemv<bf16,1,1,SWIGLU>: draft gate/up projection + SwiGLU, 1 row",
+            "kernel": f"k_gemv<{shape.dtype},1,SWIGLU>: draft gate/up projection + SwiGLU, 1 row",
             "achieved": round(achieved, 1) if achieved else None,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
-            "traffic": recorded_traffic(),
+            "traffic": recorded_traffic(bytes_per_launch),
             "bytes_per_launch": int(bytes_per_launch),
             "avg_launch_us": round(avg_launch_us, 3),
             "launches": k_n,
         },
     }
+    if n_p > 1:
+        out["per_prompt"] = per_prompt
+    if latency is not None:
+        out["latency_model"] = latency
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, weights, prompt, wl["policy"], args.cpu_tokens,
-                                           min(args.cpu_prompt, wl["prompt"]))
+        out["cpu_baseline"] = cpu_baseline(shape, weights, prompts[0], policy, args.cpu_tokens,
+                                           min(args.cpu_prompt, lens[0]))
     eng.close()
     print(json.dumps(out), flush=True)
 

@@ -124,6 +124,35 @@ class Engine:
                     "lss_select_layers_dp")
         return mask.tolist(), float(score.value)
 
+    def calibrate_latency(self, prompt, seq_lens, depths, reps=3):
+        """Fit the DyTC latency model t = b0 + b1 * seq_len + b2 * depth
+        (CAS-Spec blog, latency prediction section) to timed one-token draft
+        steps: for every seq_len, prefill ``prompt[:seq_len]``, then for every
+        depth draft one token with the first ``depth`` layers executed (wall
+        time of ``lss_draft``, which returns after its stream work), verify it
+        and accept.  The first repetition per (seq_len, depth) is not timed.
+        Returns (beta, samples [(seq_len, depth, seconds)], max relative error
+        of the fit over the samples)."""
+        import time
+        L = self.shape.n_layers
+        samples = []
+        for s in seq_lens:
+            self.prefill(list(prompt[:s]))
+            for depth in depths:
+                mask = [0] * int(depth) + [1] * (L - int(depth))
+                for r in range(reps + 1):
+                    p = self.seq_len
+                    t = time.perf_counter()
+                    self.draft(mask, k=1)
+                    dt = time.perf_counter() - t
+                    self.verify(k=1)
+                    self.accept()
+                    if r:
+                        samples.append((p, int(depth), dt))
+        beta = latency_fit(samples)
+        err = max(abs(beta[0] + beta[1] * s + beta[2] * d - t) / t for s, d, t in samples)
+        return beta, samples, err
+
     def generate(self, prompt, n_gen, policy):
         a, p = _i32(prompt)
         pol = make_policy(policy, self.shape.n_layers)

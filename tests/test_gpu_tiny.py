@@ -259,3 +259,19 @@ def test_quantize_op_bitwise(setup):
         qo, so = oracle.quantize_row(x[i])
         assert np.array_equal(q[i], qo), i
         assert s[i] == so, i
+
+
+def test_latency_calibration_fits_the_router_model(setup):
+    """DyTC latency model (CAS-Spec blog, latency prediction): timed one-token
+    drafts at two depths and two context lengths fit t = b0 + b1 seq_len +
+    b2 depth; deeper drafts cost more, and the engine is left usable."""
+    eng, prompt = setup["eng"], setup["prompt"]
+    long_prompt = lss_synth.make_prompt(setup["shape"], 96, seed=7)
+    beta, samples, err = eng.calibrate_latency(long_prompt, (32, 96), (1, 4), reps=3)
+    assert len(samples) == 2 * 2 * 3
+    assert all(np.isfinite(beta))
+    assert beta[2] > 0.0                      # an executed layer costs time
+    assert err < 0.5, (beta, err)
+    # state is consistent afterwards: a fresh greedy run still matches the oracle
+    toks, _ = eng.generate(prompt, 16, {"mode": "ar"})
+    assert toks == setup["ref"][:16]
