@@ -35,6 +35,12 @@ WORKLOADS = {
                       desc="Llama-2-7B shape, prompt 512, 256 generated, static skip of layers 1,3,..,31, K 6"),
     "tiny": dict(shape="tiny", prompt=32, gen=64, policy={"mode": "static", "k_max": 4, "skip": (1, 2)},
                  desc="4-layer float32 model, prompt 32, 64 generated, skip {1,2}, K 4"),
+    # Llama-3-70B shape on one GPU (~141 GB of bf16 weights), the CLaSp DP
+    # skipping 44 of 80 layers, re-run every 8, 32 or 128 verify rounds.
+    "llama3_70b": dict(shape="llama3_70b", prompt=512, gen=256,
+                       policy=[{"mode": "dp", "k_max": 8, "n_skip": 44, "interval": iv} for iv in (8, 32, 128)],
+                       desc="Llama-3-70B shape, prompt 512, 256 generated, CLaSp DP skip 44 of 80, interval "
+                            "8 / 32 / 128, K 8"),
     # CAS-Spec three-level cascade on the Llama-3-8B shape.  Levels as (layers
     # skipped in total, of which the last `exit` by early exit, int8
     # activations), fast -> precise: L1 skips 70% of 32 layers (4 by early
@@ -140,9 +146,11 @@ def main():
     G = wl["gen"] if args.gen is None else args.gen
     max_seq = max(lens) + G + 33
     eng = Engine(shape, weights, max_seq=max_seq, max_rows=64)
-    policy = dict(wl["policy"])
+    policies = [dict(p) for p in (wl["policy"] if isinstance(wl["policy"], list) else [wl["policy"]])]
     latency = None
-    if policy["mode"] == "cascade":
+    for policy in policies:
+        if policy["mode"] != "cascade":
+            continue
         # DyTC latency model of this engine: timed one-token drafts at the
         # levels' depths and at full depth (the verify), seq_len 128 .. 2048
         L = shape.n_layers
@@ -153,6 +161,7 @@ def main():
         policy["beta"] = beta
         latency = {"beta": [float(b) for b in beta], "seq_lens": list(cal_lens), "depths": depths,
                    "samples": len(samples), "max_rel_err": round(err, 4)}
+    runs = [(pol, i) for pol in policies for i in range(len(prompts))]   # (policy, prompt index)
 
     def run(pol, prompt):
         torch.cuda.synchronize()
@@ -162,19 +171,19 @@ def main():
         return toks, st, time.perf_counter() - t
 
     for _ in range(args.warmup):
-        for pr in prompts:
-            run(policy, pr)
+        for pol, i in runs:
+            run(pol, prompts[i])
     eng.profile_kernel("gate_up", rows=1)
-    spec_t = [0.0] * len(prompts)
-    stats, spec_toks = [None] * len(prompts), [None] * len(prompts)
+    spec_t = [0.0] * len(runs)
+    stats, spec_toks = [None] * len(runs), [None] * len(runs)
     torch.cuda.synchronize()
     t_all = time.perf_counter()
     for _ in range(args.steps):
-        for i, pr in enumerate(prompts):
-            toks, st, dt = run(policy, pr)
-            spec_t[i] += dt
-            stats[i] = st
-            spec_toks[i] = toks
+        for j, (pol, i) in enumerate(runs):
+            toks, st, dt = run(pol, prompts[i])
+            spec_t[j] += dt
+            stats[j] = st
+            spec_toks[j] = toks
     torch.cuda.synchronize()
     t_all = time.perf_counter() - t_all
     k_ms, k_n, k_bytes = eng.profile_read()
@@ -205,10 +214,11 @@ def main():
             pre.append(time.perf_counter() - t)
         prefill_s.append(min(pre))
 
-    n_p = len(prompts)
+    n_r = len(runs)
     step_s = t_all / args.steps
-    value = n_p * G / step_s
-    ar_value = n_p * G / (sum(ar_t) / args.ar_steps) if args.ar_steps > 0 else None
+    value = n_r * G / step_s
+    ar_step = sum(ar_t[i] for _, i in runs) / args.ar_steps if args.ar_steps > 0 else None
+    ar_value = n_r * G / ar_step if ar_step else None
     rounds = sum(st["rounds"] for st in stats)
     accepted = sum(st["accepted"] for st in stats)
     drafted = sum(st["drafted"] for st in stats)
@@ -217,17 +227,22 @@ def main():
     avg_launch_us = 1e3 * k_ms / max(k_n, 1)
     bytes_per_launch = k_bytes / max(k_n, 1)
     achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9 if k_n else None
-    per_prompt = []
-    for i, n in enumerate(lens):
-        st = stats[i]
-        sp = G * args.steps / spec_t[i]
+    per_run = []
+    for j, (pol, i) in enumerate(runs):
+        st = stats[j]
+        sp = G * args.steps / spec_t[j]
         ar = G * args.ar_steps / ar_t[i] if args.ar_steps > 0 else None
-        per_prompt.append({"prompt": n, "tokens_per_s": round(sp, 3),
-                           "ar_tokens_per_s": round(ar, 3) if ar else None,
-                           "speedup_vs_ar": round(sp / ar, 4) if ar else None,
-                           "mean_accepted": round(st["accepted"] / max(st["rounds"], 1), 4),
-                           "drafted_per_round": round(st["drafted"] / max(st["rounds"], 1), 4),
-                           "prefill_ms": round(1e3 * prefill_s[i], 3)})
+        item = {"prompt": lens[i], "tokens_per_s": round(sp, 3),
+                "ar_tokens_per_s": round(ar, 3) if ar else None,
+                "speedup_vs_ar": round(sp / ar, 4) if ar else None,
+                "lossless": spec_toks[j] == ar_toks[i] if args.ar_steps > 0 else None,
+                "mean_accepted": round(st["accepted"] / max(st["rounds"], 1), 4),
+                "drafted_per_round": round(st["drafted"] / max(st["rounds"], 1), 4),
+                "dp_runs": st["dp_runs"], "prefill_ms": round(1e3 * prefill_s[i], 3)}
+        if len(policies) > 1:
+            item["interval"] = pol.get("interval")
+        per_run.append(item)
+    prefill_total = sum(prefill_s[i] for _, i in runs)
     out = {
         "metric": "gen tokens/s @bs1 (Llama-3-8B shape), speedup vs AR, draft GEMV HBM GB/s",
         "value": round(value, 3),
@@ -245,14 +260,14 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "speedup_vs_ar": round(value / ar_value, 4) if ar_value else None,
         "ar_tokens_per_s": round(ar_value, 3) if ar_value else None,
-        "lossless": (spec_toks == ar_toks) if args.ar_steps > 0 else None,
+        "lossless": all(r["lossless"] for r in per_run) if args.ar_steps > 0 else None,
         "mean_accepted": round(accepted / max(rounds, 1), 4),
-        "tokens_per_round": round((emitted - n_p) / max(rounds, 1), 4),
+        "tokens_per_round": round((emitted - n_r) / max(rounds, 1), 4),
         "drafted_per_round": round(drafted / max(rounds, 1), 4),
         "rounds": rounds,
         "dp_runs": dp_runs,
-        "prefill_ms": round(1e3 * sum(prefill_s), 3),
-        "decode_tokens_per_s": round(n_p * (G - 1) / (step_s - sum(prefill_s)), 3),
+        "prefill_ms": round(1e3 * prefill_total, 3),
+        "decode_tokens_per_s": round(n_r * (G - 1) / (step_s - prefill_total), 3),
         "draft_gemv_gbps": round(achieved, 1) if achieved else None,
         "roofline": {
             "bound": "hbm",
@@ -267,13 +282,19 @@ def main():
             "launches": k_n,
         },
     }
-    if n_p > 1:
-        out["per_prompt"] = per_prompt
+    if n_r > 1:
+        out["runs"] = per_run
     if latency is not None:
         out["latency_model"] = latency
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, weights, prompts[0], policy, args.cpu_tokens,
-                                           min(args.cpu_prompt, lens[0]))
+        if shape.total_params() * 4 > 64e9:
+            # the float32 oracle of this shape does not fit a bounded host sample
+            out["cpu_baseline"] = {"value": None, "unit": "tokens/s", "cores": None, "kind": "oracle",
+                                   "sample": "not run: the float32 oracle needs "
+                                             f"{shape.total_params() * 4 / 1e9:.0f} GB of host memory"}
+        else:
+            out["cpu_baseline"] = cpu_baseline(shape, weights, prompts[0], policies[0], args.cpu_tokens,
+                                               min(args.cpu_prompt, lens[0]))
     eng.close()
     print(json.dumps(out), flush=True)
 

@@ -247,8 +247,13 @@ int gemv_ncw(int K, int wbytes) {
   while (ncw < per) ncw *= 2;
   return ncw;
 }
-// rows per vector-GEMV launch: the activation chunks of a wave stay in registers
-int gemv_cap(int K, int wbytes) { return std::max(1, std::min(GV_MB_MAX, GV_ACT_MAX / gemv_ncw(K, wbytes))); }
+// rows per vector-GEMV launch: the activation chunks of a wave stay in
+// registers (MB x NCW <= GV_ACT_MAX; 8 rows only with one chunk per wave,
+// where the accumulators still fit without spilling)
+int gemv_cap(int K, int wbytes) {
+  const int ncw = gemv_ncw(K, wbytes);
+  return ncw == 1 ? GV_MB_MAX : std::max(1, std::min(4, GV_ACT_MAX / ncw));
+}
 
 template <typename WT, int EPI, int NCW>
 void gemv_launch(const GemmArgs& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
@@ -258,15 +263,13 @@ void gemv_launch(const GemmArgs& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1)
     else if (g.M == 2) launch_k(k_gemv<WT, 2, 1, EPI>, grid, block, 0, s, t0, t1, g);
     else if (g.M <= 4) launch_k(k_gemv<WT, 4, 1, EPI>, grid, block, 0, s, t0, t1, g);
     else launch_k(k_gemv<WT, 8, 1, EPI>, grid, block, 0, s, t0, t1, g);
-  } else if constexpr (NCW == 2) {
-    if (g.M == 1) launch_k(k_gemv<WT, 1, 2, EPI>, grid, block, 0, s, t0, t1, g);
-    else if (g.M == 2) launch_k(k_gemv<WT, 2, 2, EPI>, grid, block, 0, s, t0, t1, g);
-    else launch_k(k_gemv<WT, 4, 2, EPI>, grid, block, 0, s, t0, t1, g);
-  } else if constexpr (NCW == 4) {
-    if (g.M == 1) launch_k(k_gemv<WT, 1, 4, EPI>, grid, block, 0, s, t0, t1, g);
-    else launch_k(k_gemv<WT, 2, 4, EPI>, grid, block, 0, s, t0, t1, g);
+  } else if constexpr (NCW == 2 || NCW == 4) {
+    if (g.M == 1) launch_k(k_gemv<WT, 1, NCW, EPI>, grid, block, 0, s, t0, t1, g);
+    else if (g.M == 2) launch_k(k_gemv<WT, 2, NCW, EPI>, grid, block, 0, s, t0, t1, g);
+    else launch_k(k_gemv<WT, 4, NCW, EPI>, grid, block, 0, s, t0, t1, g);
   } else {
-    launch_k(k_gemv<WT, 1, 8, EPI>, grid, block, 0, s, t0, t1, g);
+    if (g.M == 1) launch_k(k_gemv<WT, 1, 8, EPI>, grid, block, 0, s, t0, t1, g);
+    else launch_k(k_gemv<WT, 2, 8, EPI>, grid, block, 0, s, t0, t1, g);
   }
 }
 

@@ -619,7 +619,7 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void k_gemm(GemmArgs ga) {
 // a verify row gets the same bits as a one-row greedy step.
 #define GV_WAVES 8
 #define GV_MB_MAX 8              // activation rows per launch
-#define GV_ACT_MAX 8             // MB x NCW: activation vectors (one chunk of one row) per lane
+#define GV_ACT_MAX 16            // MB x NCW: activation vectors (one chunk of one row) per lane
 
 template <typename WT> struct GVt;
 template <> struct GVt<uint16_t> { static constexpr int EPL = 8, AV = 2; };   // AV: uint4 per lane of split-bf16 x

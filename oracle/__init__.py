@@ -28,7 +28,7 @@ float32, the precision the GPU kernels take them in.
 Parity status per function is listed in each module header.
 """
 from .model import OracleModel, rms_norm, rope, silu, attend, quantize_row, argmax_first
-from .decode import (DecodeState, prefill, forward_row, ar_generate, draft, verify,
+from .decode import (DecodeState, layer_block, prefill, forward_row, ar_generate, draft, verify,
                      accept, speculative_generate, Policy)
 from .clasp import clasp_dp, brute_force_skip, forward_with_mask_at_target
 from .dytc import (ALPHA, A_INIT, ema_update, fit_latency, predict_latency,
@@ -36,7 +36,7 @@ from .dytc import (ALPHA, A_INIT, ema_update, fit_latency, predict_latency,
 
 __all__ = [
     "OracleModel", "rms_norm", "rope", "silu", "attend", "quantize_row", "argmax_first",
-    "DecodeState", "prefill", "forward_row", "ar_generate", "draft", "verify", "accept",
+    "DecodeState", "layer_block", "prefill", "forward_row", "ar_generate", "draft", "verify", "accept",
     "speculative_generate", "Policy", "clasp_dp", "brute_force_skip",
     "forward_with_mask_at_target", "ALPHA", "A_INIT", "ema_update", "fit_latency",
     "predict_latency", "plan_cascade", "update_cascade",

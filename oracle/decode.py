@@ -128,6 +128,42 @@ def forward_row(model, st, tok, pos, mode, skip=None, quant=False):
     return model.head(h), states
 
 
+def layer_block(model, l, H, st=None):
+    """Decoder layer l over a block of causal rows at positions 0..P-1
+    (residual rows H [P][d], every row seeing itself and the rows before it):
+    RMSNorm, q/k/v, rotary embedding, softmax attention, output projection
+    and residual, RMSNorm, SwiGLU FFN and residual (CLaSp article, LLaMA
+    family; shapes from the model).  Writes the block's keys and values into
+    ``st`` when given.  Returns the layer's output rows."""
+    m = model
+    P = H.shape[0]
+    pos = np.arange(P)
+    group = m.Hq // m.Hkv
+    causal = pos[None, :] <= pos[:, None]
+    lw = m.layer(l)
+    X = np.stack([rms_norm(h, lw["attn_norm"], m.eps) for h in H])
+    Q = (X @ lw["wq"].T).reshape(P, m.Hq, m.hd)
+    K = (X @ lw["wk"].T).reshape(P, m.Hkv, m.hd)
+    Vv = (X @ lw["wv"].T).reshape(P, m.Hkv, m.hd)
+    Q = np.stack([rope(Q[t], t, m.theta) for t in range(P)])
+    K = np.stack([rope(K[t], t, m.theta) for t in range(P)])
+    if st is not None:
+        st.k[l, :P], st.v[l, :P] = K, Vv
+    O = np.empty((P, m.Hq, m.hd), m.dt)
+    for hh in range(m.Hq):
+        kh = hh // group
+        S = (Q[:, hh] @ K[:, kh].T) / m.dt.type(np.sqrt(m.hd))
+        S = np.where(causal, S, -np.inf)
+        S = S - S.max(axis=1, keepdims=True)
+        Pm = np.exp(S)
+        Pm = Pm / Pm.sum(axis=1, keepdims=True)
+        O[:, hh] = Pm @ Vv[:, kh]
+    H = H + O.reshape(P, -1) @ lw["wo"].T
+    X = np.stack([rms_norm(h, lw["ffn_norm"], m.eps) for h in H])
+    A = silu(X @ lw["w_gate"].T) * (X @ lw["w_up"].T)
+    return H + A @ lw["w_down"].T
+
+
 def prefill(model, tokens, max_seq, progress=None):
     """Causal full-model pass over the prompt, as one block of rows.
 
@@ -142,31 +178,8 @@ def prefill(model, tokens, max_seq, progress=None):
     st = DecodeState(m, max_seq)
     H = np.stack([m.embed_row(t) for t in tokens])
     last_states = [H[-1].copy()]
-    pos = np.arange(P)
-    group = m.Hq // m.Hkv
-    causal = pos[None, :] <= pos[:, None]
     for l in range(m.L):
-        lw = m.layer(l)
-        X = np.stack([rms_norm(h, lw["attn_norm"], m.eps) for h in H])
-        Q = (X @ lw["wq"].T).reshape(P, m.Hq, m.hd)
-        K = (X @ lw["wk"].T).reshape(P, m.Hkv, m.hd)
-        Vv = (X @ lw["wv"].T).reshape(P, m.Hkv, m.hd)
-        Q = np.stack([rope(Q[t], t, m.theta) for t in range(P)])
-        K = np.stack([rope(K[t], t, m.theta) for t in range(P)])
-        st.k[l, :P], st.v[l, :P] = K, Vv
-        O = np.empty((P, m.Hq, m.hd), m.dt)
-        for hh in range(m.Hq):
-            kh = hh // group
-            S = (Q[:, hh] @ K[:, kh].T) / m.dt.type(np.sqrt(m.hd))
-            S = np.where(causal, S, -np.inf)
-            S = S - S.max(axis=1, keepdims=True)
-            Pm = np.exp(S)
-            Pm = Pm / Pm.sum(axis=1, keepdims=True)
-            O[:, hh] = Pm @ Vv[:, kh]
-        H = H + O.reshape(P, -1) @ lw["wo"].T
-        X = np.stack([rms_norm(h, lw["ffn_norm"], m.eps) for h in H])
-        A = silu(X @ lw["w_gate"].T) * (X @ lw["w_up"].T)
-        H = H + A @ lw["w_down"].T
+        H = layer_block(m, l, H, st)
         last_states.append(H[-1].copy())
         if progress is not None:
             progress(l)

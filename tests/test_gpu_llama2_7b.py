@@ -1,0 +1,125 @@
+"""GPU parity at the Llama-2-7B shape (32 layers, d 4096, 32 heads MHA, FFN
+11008, vocab 32000, bf16; rotary theta 1e4) with its 512-token prompt and
+the static draft that skips layers 1, 3, .., 31 (K = 6).  This shape has no
+grouped queries and an FFN width that is not a whole number of 1 KB weight
+chunks (11008 = 21.5 x 512), so the down projection's last chunk is ragged.
+
+Against the oracle (float32, on the host): prefill logits and last-row
+residual states, draft logits with the static skip set, teacher-forced verify
+logits (bf16 tolerance 2e-2).  Property: speculative output equals greedy
+output bit for bit."""
+import numpy as np
+import pytest
+
+import lss_synth
+import oracle
+from conftest import oracle_gap
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = lss_synth.SHAPES["llama2_7b"]
+P = 512
+MAX_SEQ = 512 + 256 + 33
+TOL = 2e-2
+SKIP = tuple(range(1, 32, 2))
+POLICY = {"mode": "static", "k_max": 6, "skip": SKIP}
+
+
+@pytest.fixture(scope="module")
+def gpu7b():
+    from layer_skip_self_amd import Engine
+    w = lss_synth.make_weights(SHAPE, device="cuda")
+    eng = Engine(SHAPE, w, max_seq=MAX_SEQ, max_rows=64)
+    prompt = lss_synth.make_prompt(SHAPE, P)
+    yield dict(w=w, eng=eng, prompt=prompt)
+    eng.close()
+
+
+@pytest.fixture(scope="module")
+def oracle7b(gpu7b):
+    import time
+    t = time.time()
+    w_host = [(n, t.to("cpu")) for n, t in gpu7b["w"]]
+    model = oracle.OracleModel(SHAPE, lss_synth.LazyF32(w_host), dtype=np.float32, cache_layers=True)
+    for l in range(SHAPE.n_layers):
+        model.layer(l)
+    model.embed_row(0)
+    model.head(np.ones(SHAPE.d_model, np.float32))
+    st, z, states = oracle.prefill(model, gpu7b["prompt"], MAX_SEQ)
+    print(f"\noracle prefill done in {time.time() - t:.1f} s", flush=True)
+    return dict(model=model, st=st, z=z, states=states)
+
+
+def test_speculative_equals_greedy_bitwise_7b(gpu7b):
+    eng, prompt = gpu7b["eng"], gpu7b["prompt"]
+    G = 64
+    ar, _ = eng.generate(prompt, G, {"mode": "ar"})
+    toks, st = eng.generate(prompt, G, POLICY)
+    assert toks == ar
+    assert 0 <= st["accepted"] <= st["drafted"] <= 6 * st["rounds"]
+
+
+def test_prefill_logits_and_states_vs_oracle_7b(gpu7b, oracle7b):
+    eng = gpu7b["eng"]
+    t0 = eng.prefill(gpu7b["prompt"])
+    z = eng.read_logits(1)[0]
+    err = float(np.max(np.abs(z - oracle7b["z"])))
+    print(f"prefill logits max-abs {err:.3e}")
+    assert err <= TOL
+    if oracle_gap(oracle7b["z"]) >= 1e-2:
+        assert t0 == int(np.argmax(oracle7b["z"]))
+    hs = eng.read_states((P - 1) % 64)
+    serr = float(np.max(np.abs(hs - np.stack(oracle7b["states"]))))
+    print(f"prefill last-row residual states max-abs {serr:.3e}")
+    assert serr <= TOL
+
+
+def test_static_draft_logits_vs_oracle_7b(gpu7b, oracle7b):
+    """Two draft steps with the static skip set (layers 1, 3, .., 31)."""
+    import copy
+    eng, model = gpu7b["eng"], oracle7b["model"]
+    st = copy.deepcopy(oracle7b["st"])
+    t0 = eng.prefill(gpu7b["prompt"])
+    if t0 != st.t0:
+        pytest.skip("first token is a near-tie between the two paths")
+    mask = [1 if l in SKIP else 0 for l in range(SHAPE.n_layers)]
+    steps = 0
+    for s in range(2):
+        g = eng.draft(mask, False, 1)
+        zg = eng.read_logits(1)[0]
+        tok_o = st.t0 if not st.window else st.window[-1]
+        zo, _ = oracle.forward_row(model, st, tok_o, st.p + len(st.window), "draft", mask, False)
+        d = int(np.argmax(zo))
+        st.window.append(d)
+        steps += 1
+        err = float(np.max(np.abs(zg - zo)))
+        print(f"draft step {s}: max-abs {err:.3e}")
+        assert err <= TOL
+        if oracle_gap(zo) < 1e-2:
+            break
+        assert g[0] == d
+    eng.verify(None, steps)
+    eng.accept()
+
+
+def test_teacher_forced_verify_logits_vs_oracle_7b(gpu7b, oracle7b):
+    import copy
+    eng, model = gpu7b["eng"], oracle7b["model"]
+    so = copy.deepcopy(oracle7b["st"])
+    t0 = eng.prefill(gpu7b["prompt"])
+    if t0 != so.t0:
+        pytest.skip("first token is a near-tie between the two paths")
+    toks, zs = [so.t0], []
+    for _ in range(4):
+        zz, _ = oracle.forward_row(model, so, so.t0, so.p, "full")
+        zs.append(zz)
+        so.p += 1
+        so.t0 = int(np.argmax(zz))
+        toks.append(so.t0)
+    eng.verify(toks[1:4])
+    zg = eng.read_logits(4)
+    eng.accept()
+    for i in range(4):
+        err = float(np.max(np.abs(zg[i] - zs[i])))
+        print(f"verify row {i}: max-abs {err:.3e}")
+        assert err <= TOL
