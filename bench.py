@@ -41,6 +41,16 @@ WORKLOADS = {
                        policy=[{"mode": "dp", "k_max": 8, "n_skip": 44, "interval": iv} for iv in (8, 32, 128)],
                        desc="Llama-3-70B shape, prompt 512, 256 generated, CLaSp DP skip 44 of 80, interval "
                             "8 / 32 / 128, K 8"),
+    # Supplementary, not the headline configuration: the Llama-3-8B shape with
+    # 16 planted identity layers (wo = w_down = 0, seeded set) and the LM head
+    # scaled x10, so the layers the DP can skip are truly redundant and the
+    # draft's top-1 probability can pass the exit threshold.  It shows the
+    # engine's speculative ceiling when drafts are right.
+    "llama3_8b_planted": dict(shape="llama3_8b", prompt=1024, gen=512, planted=16, head_scale=10.0,
+                              policy={"mode": "dp", "k_max": 8, "n_skip": 16, "interval": 32, "exit_tau": 0.7},
+                              desc="supplementary: Llama-3-8B shape with 16 planted identity layers and a x10 "
+                                   "LM head, prompt 1024, 512 generated, CLaSp DP skip 16 every 32 rounds, exit "
+                                   "threshold 0.7, K <= 8"),
     # CAS-Spec three-level cascade on the Llama-3-8B shape.  Levels as (layers
     # skipped in total, of which the last `exit` by early exit, int8
     # activations), fast -> precise: L1 skips 70% of 32 layers (4 by early
@@ -139,7 +149,12 @@ def main():
     shape = lss_synth.SHAPES[wl["shape"]]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    weights = lss_synth.make_weights(shape, device=dev)
+    planted = ()
+    if wl.get("planted"):
+        rng = np.random.default_rng(shape.weight_seed)
+        planted = tuple(sorted(rng.choice(shape.n_layers, wl["planted"], replace=False).tolist()))
+    weights = lss_synth.make_weights(shape, device=dev, planted_identity=planted,
+                                     head_scale=wl.get("head_scale", 1.0))
     lens = wl["prompt"] if isinstance(wl["prompt"], tuple) else (wl["prompt"],)
     # one seeded prompt per length (the first uses the shape's prompt seed)
     prompts = [lss_synth.make_prompt(shape, n, seed=shape.prompt_seed + i) for i, n in enumerate(lens)]
@@ -255,7 +270,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": shape.dtype,
-        "data": "synthetic (seeded random-init weights and uniform-random prompt)",
+        "data": "synthetic (seeded random-init weights and uniform-random prompt)"
+                + (f"; planted identity layers {list(planted)}" if planted else ""),
         "config": {"workload": wl["desc"], "global_batch": 1, "seq_len": max(lens) + G,
                    "parallelism": "none (1 GPU)"},
         "speedup_vs_ar": round(value / ar_value, 4) if ar_value else None,
