@@ -29,8 +29,21 @@ constexpr int kWinMax = LSS_WINDOW_MAX;
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// K splits of a prefill / layer-selection GEMM (measured at the 8B shapes):
+// wide N keeps ~512 workgroups with few splits (each split adds a pass of
+// the epilogue), narrow N splits up to 8 ways to reach ~1024 workgroups; at
+// least 4 steps of K per split
+int pg_splits(int N, int K, int wbytes) {
+  const int KS = wbytes == 2 ? 128 : 64;
+  const int nsteps = (K + KS - 1) / KS;
+  const int tiles = (N + PG_TN - 1) / PG_TN;
+  int S = tiles >= 128 ? 512 / tiles : (1024 + tiles - 1) / tiles;
+  S = std::min(S, std::max(1, nsteps / 4));
+  return std::max(1, std::min(S, PG_MAX_SPLIT));
+}
+
 struct Layout {
-  size_t kc, vc, hs, hmid, xa, xb, xc, pa, pc, xs, qkv, apart, aout, act, logits, hpart, rope, target,
+  size_t kc, vc, hs, hmid, xa, xb, xc, pa, pc, xs, qkv, apart, aout, pgpart, rstd, act, logits, hpart, rope, target,
       dpg0, dpg1, dpx, dpdec, tok, seqtok, res, total;
   int xld, nch_max, nz_max, ntile;
 };
@@ -85,6 +98,14 @@ Layout make_layout(const lss_config* c) {
   L.qkv = take(R * (Hq + 2 * Hkv) * hd * 4);
   L.apart = take(Hkv * (size_t)L.nz_max * L.nch_max * ATT_QB * (hd + 2) * 4);
   L.aout = take(R * Hq * hd * 4);
+  {  // split partials of the prefill / layer-selection GEMM: max over the projections of S x NACC x N
+    const int wb = c->dtype == LSS_BF16 ? 2 : 4;
+    const size_t qn = (Hq + 2 * Hkv) * hd;
+    const size_t a = pg_splits((int)qn, (int)d, wb) * qn, b = pg_splits((int)d, (int)(Hq * hd), wb) * d,
+                 g = 2 * pg_splits((int)F, (int)d, wb) * F, dn = pg_splits((int)d, (int)F, wb) * d;
+    L.pgpart = take(std::max({a, b, g, dn}) * R * 4);
+  }
+  L.rstd = take(R * 4);
   L.act = take(R * F * 4);
   L.logits = take(R * V * 4);
   L.hpart = take(R * (size_t)L.ntile * 3 * 4);
@@ -126,6 +147,7 @@ struct lss_engine {
   // device buffers
   void *kc = nullptr, *vc = nullptr;
   float *hs, *hmid, *xs, *qkv, *apart, *aout, *act, *logits, *hpart, *target, *dpg[2], *dpx, *dpdec;
+  float *pgpart, *rstd;
   void *xa, *xb, *xc;   // projection inputs: layer input (attention-norm gain), attention / FFN output, mid-layer
   float *pa, *pc;       // partial sums of squares of the residual rows behind xa and xc
   float2* rope;
@@ -203,26 +225,6 @@ void launch_k(K kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, hipEvent
   else hipLaunchKernelGGL(kern, grid, block, lds, s, ga);
 }
 
-template <typename WT, int EPI>
-void gemm_mt(const GemmArgs& ga, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr) {
-  const dim3 grid((ga.N + 15) / 16), block(64 * GEMM_WAVES);
-  const size_t a_lds = (size_t)ga.M * a_lds_ld(ga.K) * 4;
-  const bool alds = ga.M <= 16 && a_lds <= GEMM_A_LDS_MAX;
-  if (ga.M == 1) {
-    if (alds) launch_k(k_gemm<WT, 1, EPI, true, true>, grid, block, a_lds, s, t0, t1, ga);
-    else launch_k(k_gemm<WT, 1, EPI, true, false>, grid, block, 0, s, t0, t1, ga);
-    return;
-  }
-  switch ((ga.M + 15) / 16) {
-    case 1:
-      if (alds) launch_k(k_gemm<WT, 1, EPI, false, true>, grid, block, a_lds, s, t0, t1, ga);
-      else launch_k(k_gemm<WT, 1, EPI, false, false>, grid, block, 0, s, t0, t1, ga);
-      break;
-    case 2: launch_k(k_gemm<WT, 2, EPI, false, false>, grid, block, 0, s, t0, t1, ga); break;
-    case 3: launch_k(k_gemm<WT, 3, EPI, false, false>, grid, block, 0, s, t0, t1, ga); break;
-    default: launch_k(k_gemm<WT, 4, EPI, false, false>, grid, block, 0, s, t0, t1, ga); break;
-  }
-}
 
 // GemmArgs of rows r0 .. r0 + Mg - 1 of a projection
 GemmArgs rows_from(const GemmArgs& ga, int r0, int Mg) {
@@ -289,6 +291,34 @@ void gemv_mt(const GemmArgs& ga, hipStream_t s, hipEvent_t t0 = nullptr, hipEven
   }
 }
 
+// Prefill / layer-selection projection: 1/rms rows, split MFMA GEMM, split
+// sum + epilogue.  The timing events (if any) bracket the GEMM launch.
+template <typename WT, int EPI>
+void pgemm(lss_engine* e, const GemmArgs& ga, hipEvent_t t0, hipEvent_t t1) {
+  constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
+  PgArgs pa{};
+  for (int i = 0; i < 3; ++i) { pa.w[i] = ga.w[i]; pa.nseg[i] = ga.nseg[i]; }
+  pa.w2 = ga.w2; pa.N = ga.N; pa.K = ga.K; pa.A = ga.A; pa.lda = ga.lda; pa.M = ga.M;
+  pa.S = pg_splits(ga.N, ga.K, sizeof(WT));
+  pa.part = e->pgpart;
+  hipStream_t s = e->stream;
+  if (ga.scale == SCALE_NORM)
+    hipLaunchKernelGGL(k_rstd, dim3(ga.M), dim3(256), 0, s, ga.pin, ga.K / 16, ga.K, ga.eps, e->rstd);
+  const dim3 grid((ga.N + PG_TN - 1) / PG_TN, pa.S), block(256);
+  auto go = [&](auto kern) {
+    if (t0) hipExtLaunchKernelGGL(kern, grid, block, 0u, s, t0, t1, 0u, pa);
+    else hipLaunchKernelGGL(kern, grid, block, 0, s, pa);
+  };
+  switch ((ga.M + 15) / 16) {
+    case 1: go(k_pgemm<WT, 1, NACC>); break;
+    case 2: go(k_pgemm<WT, 2, NACC>); break;
+    case 3: go(k_pgemm<WT, 3, NACC>); break;
+    default: go(k_pgemm<WT, 4, NACC>); break;
+  }
+  hipLaunchKernelGGL((k_pepi<WT, EPI>), dim3((ga.N + 15) / 16), dim3(256), 0, s, ga, (const float*)e->pgpart, pa.S,
+                     (const float*)e->rstd);
+}
+
 // Sum the elapsed times of recorded event pairs (the stream must be synced).
 void prof_resolve(lss_engine* e) {
   for (int i = 0; i < e->ev_used; ++i) {
@@ -300,7 +330,8 @@ void prof_resolve(lss_engine* e) {
 
 template <int EPI>
 void gemm(lss_engine* e, const GemmArgs& ga) {
-  const bool vec = e->gemv;
+  // draft / verify rows, and any launch of at most 8 rows, take the vector GEMV
+  const bool vec = e->gemv || ga.M <= 8;
   const bool one_launch = !vec || ga.M <= gemv_cap(ga.K, e->bf16 ? 2 : 4);
   const bool prof = e->prof_epi == EPI && (e->prof_rows == 0 || e->prof_rows == ga.M) && one_launch;
   if (prof) {
@@ -314,8 +345,8 @@ void gemm(lss_engine* e, const GemmArgs& ga) {
     if (e->bf16) gemv_mt<uint16_t, EPI>(ga, e->stream, t0, t1);
     else gemv_mt<float, EPI>(ga, e->stream, t0, t1);
   } else {
-    if (e->bf16) gemm_mt<uint16_t, EPI>(ga, e->stream, t0, t1);
-    else gemm_mt<float, EPI>(ga, e->stream, t0, t1);
+    if (e->bf16) pgemm<uint16_t, EPI>(e, ga, t0, t1);
+    else pgemm<float, EPI>(e, ga, t0, t1);
   }
   if (prof) {
     e->ev_used++;
@@ -571,6 +602,7 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
   e->xa = ws + lay.xa; e->xb = ws + lay.xb; e->xc = ws + lay.xc;
   e->pa = (float*)(ws + lay.pa); e->pc = (float*)(ws + lay.pc);
   e->xs = (float*)(ws + lay.xs); e->qkv = (float*)(ws + lay.qkv);
+  e->pgpart = (float*)(ws + lay.pgpart); e->rstd = (float*)(ws + lay.rstd);
   e->apart = (float*)(ws + lay.apart); e->aout = (float*)(ws + lay.aout);
   e->act = (float*)(ws + lay.act); e->logits = (float*)(ws + lay.logits); e->hpart = (float*)(ws + lay.hpart);
   e->rope = (float2*)(ws + lay.rope); e->target = (float*)(ws + lay.target);

@@ -16,6 +16,7 @@ namespace lss {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- scalars
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -257,36 +258,19 @@ __global__ __launch_bounds__(256) void k_quant_rows(const float* __restrict__ x,
   if (threadIdx.x == 0) xs[m] = __fdiv_rn(amax, 127.0f);
 }
 
-// ---------------------------------------------------------------- small-M MFMA GEMM
-// Y[m][n] = sum_k X[m][k] * W[n][k] for m < M <= 16*MT, weights row-major
-// [N][K] streamed once from HBM.  One workgroup = one 16-column tile of N and
-// GEMM_WAVES waves that split K into fixed contiguous ranges of whole steps;
-// the waves' partial tiles are summed in LDS in wave order.  The K split,
-// the per-lane k assignment and the MFMA sequence depend only on K, so row
-// m's result is the same for every M (rows are independent MFMA rows;
-// padding rows only produce discarded outputs).
+// ---------------------------------------------------------------- projections: shared definitions
+// Projection arguments, the MFMA operand layout of the weights, and the
+// output epilogue shared by the prefill GEMM and the decode GEMV.
 //
 // MFMA operand use (16x16x32 bf16 / 16x16x4 f32): lane l supplies A row
 // (l & 15) = activation row, B column (l & 15) = weight row, over a k group
-// chosen by (l >> 4).  Because a dot product does not depend on which k a
-// lane holds as long as A and B agree, the k of a wave step are assigned so
-// that each load instruction reads 64 contiguous bytes of each of the 16
-// weight rows (the four lanes of a row take consecutive 16-byte vectors);
-// four such loads cover 256 contiguous bytes per row.  With bf16 weights each
-// 8-element vector meets the activation's hi and lo parts (two MFMAs), with
-// float32 weights each 4-element vector feeds four MFMAs.
-//
-// The loop body has no branches on loaded data and no masking of loaded
-// values: addresses are clamped into the row, steps past K are skipped with
-// a wave-uniform test, so the compiler's wait before each MFMA covers only
-// the oldest step while GEMM_D - 1 later steps stay in flight.
-#ifndef GEMM_WAVES
-#define GEMM_WAVES 4
-#endif
+// chosen by (l >> 4).  A dot product does not depend on which k a lane holds
+// as long as A and B agree, so the k of a step (GEMM_U vectors per lane) are
+// assigned such that each load instruction reads 64 contiguous bytes of each
+// of 16 weight rows, four loads covering 256 contiguous bytes per row.  With
+// bf16 weights each 8-element vector meets the activation's hi and lo parts
+// (two MFMAs); with float32 weights each 4-element vector feeds four MFMAs.
 #define GEMM_U 4
-#ifndef GEMM_D
-#define GEMM_D 2   // weight steps in flight per wave
-#endif
 
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 enum { SCALE_NONE = 0, SCALE_NORM = 1, SCALE_XS = 2 };
@@ -313,34 +297,8 @@ template <typename WT> struct WTr;
 template <> struct WTr<uint16_t> { static constexpr int EPL = 8, ANV = 2; };  // bf16: hi + lo vectors
 template <> struct WTr<float> { static constexpr int EPL = 4, ANV = 1; };
 
-template <typename WT, int MT>
-__device__ __forceinline__ void gemm_step(const uint4 (&w)[GEMM_U], const uint4 (&a)[MT][GEMM_U][WTr<WT>::ANV],
-                                          f32x4 (&acc)[MT], int kstep, int K) {
-  constexpr int EPL = WTr<WT>::EPL;
-#pragma unroll
-  for (int u = 0; u < GEMM_U; ++u) {
-    if (kstep + u * 4 * EPL >= K) break;       // wave-uniform: past the end of K
-    if constexpr (sizeof(WT) == 2) {
-      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, w[u]);
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[t][u][0]), b, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[t][u][1]), b, acc[t], 0, 0, 0);
-      }
-    } else {
-      const float wf[4] = {__uint_as_float(w[u].x), __uint_as_float(w[u].y), __uint_as_float(w[u].z),
-                           __uint_as_float(w[u].w)};
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const float af[4] = {__uint_as_float(a[t][u][0].x), __uint_as_float(a[t][u][0].y),
-                             __uint_as_float(a[t][u][0].z), __uint_as_float(a[t][u][0].w)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[e], wf[e], acc[t], 0, 0, 0);
-      }
-    }
-  }
-}
-
+// the GEMM_U weight vectors of one lane for the step at kb (the lane's k
+// offset included), addresses clamped into the row
 template <typename WT>
 __device__ __forceinline__ void load_w(uint4 (&w)[GEMM_U], const WT* row, int kb, int K) {
   constexpr int EPL = WTr<WT>::EPL;
@@ -348,35 +306,6 @@ __device__ __forceinline__ void load_w(uint4 (&w)[GEMM_U], const WT* row, int kb
   for (int u = 0; u < GEMM_U; ++u) w[u] = *reinterpret_cast<const uint4*>(row + min(kb + u * 4 * EPL, K - EPL));
 }
 
-// activation vectors of one row (row pointer in format units) for step kb
-template <typename WT>
-__device__ __forceinline__ void load_a(uint4 (&a)[GEMM_U][WTr<WT>::ANV], const void* arow, int kb, int K) {
-  constexpr int EPL = WTr<WT>::EPL;
-#pragma unroll
-  for (int u = 0; u < GEMM_U; ++u) {
-    const int k = min(kb + u * 4 * EPL, K - EPL);
-    if constexpr (sizeof(WT) == 2) {
-      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(arow) + (size_t)(k >> 3) * 16);
-      a[u][0] = p[0];
-      a[u][1] = p[1];
-    } else {
-      a[u][0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(arow) + k);
-    }
-  }
-}
-
-// Activation rows staged in LDS (ALDS launches): rows of M x K elements
-// (4 bytes each) copied with direct-to-LDS loads in 1 KB chunks; row stride
-// a_lds_ld(K) elements (chunk-rounded, plus 8 elements so rows start on
-// different banks).
-#define GEMM_A_LDS_MAX 65536
-__host__ __device__ __forceinline__ int a_lds_ld(int K) { return ((K + 255) & ~255) + 8; }
-
-template <typename WT>
-__device__ __forceinline__ const void* a_row(const void* A, int lda, int m) {
-  return sizeof(WT) == 2 ? (const void*)(reinterpret_cast<const uint16_t*>(A) + 2 * (size_t)m * lda)
-                         : (const void*)(reinterpret_cast<const float*>(A) + (size_t)m * lda);
-}
 
 // One output element (row m, column n) of a projection.  y (and u, the
 // up-projection of SWIGLU) carry the row scale already.  The 16 lanes of an
@@ -423,177 +352,194 @@ __device__ __forceinline__ void proj_out(const GemmArgs& ga, int m, int M, int n
   }
 }
 
-// ONE = the launch has exactly one row (draft steps, greedy steps): the same
-// arithmetic as MT = 1, compiled separately so profiles attribute it apart.
-template <typename WT, int MT, int EPI, bool ONE, bool ALDS>
-__global__ __launch_bounds__(64 * GEMM_WAVES) void k_gemm(GemmArgs ga) {
+
+// ---------------------------------------------------------------- prefill / layer-selection GEMM (MFMA)
+// P[s][q][m][n] = sum over K split s of X[m][k] W_q[n][k] for M <= 16 MT rows
+// (q = 0, or 0/1 for the gate and up projections).  A workgroup is one
+// 64-row weight tile (4 waves x 16 rows, each wave's rows in the MFMA B
+// layout above) and one contiguous range of the K steps; the
+// activation block of a step (all rows x 128 k, projection format) is
+// staged once in LDS and shared by the 4 waves, so activations cost two
+// bytes of L2 traffic per weight byte instead of eight.  Small N is split
+// over K to fill the chip; k_pepi adds the splits in split order and runs
+// the projection epilogue.  Used where rows need not match the decode GEMV
+// bit for bit (prefill blocks, layer-selection rows).
+#define PG_TN 64
+#define PG_MAX_SPLIT 8
+
+struct PgArgs {
+  const void* w[3]; int nseg[3];   // weight segments stacked along N
+  const void* w2;                  // up projection (NACC = 2)
+  int N, K;
+  const void* A; int lda; int M;   // activations in the projection format
+  int S;                           // K splits (gridDim.y)
+  float* part;                     // [S][NACC][M][N]
+};
+
+template <typename WT, int MT, int NACC>
+__global__ __launch_bounds__(256) void k_pgemm(PgArgs pa) {
   constexpr int EPL = WTr<WT>::EPL;
-  constexpr int ANV = WTr<WT>::ANV;
-  constexpr int KS = 4 * EPL * GEMM_U;  // k per wave step
-  constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
-  constexpr bool APRE = MT == 1 && !ALDS;   // activations prefetched with the weights
-  extern __shared__ uint4 a_s[];             // ALDS: staged activation rows
-  __shared__ float red[NACC][MT][GEMM_WAVES][64][4];
-  __shared__ float rstd_s[MT * 16];
+  constexpr int KS = 4 * EPL * GEMM_U;                 // k per step
+  constexpr int RB = KS * 4 / 16;                      // uint4 per staged row (4 bytes per element)
+  constexpr int LDR = RB + 1;                          // padded LDS row (uint4)
+  constexpr int ROWS = MT * 16;
+  constexpr int SV = ROWS * RB / 256;                  // staged uint4 per thread
+  static_assert(ROWS * RB % 256 == 0, "staging split");
+  __shared__ uint4 a_s[2][ROWS * LDR];                 // double-buffered activation block
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int M = ONE ? 1 : ga.M;
-  const int K = ga.K;
-  // weight segment of this tile
+  const int M = pa.M, K = pa.K;
+  const int n0 = blockIdx.x * PG_TN + wave * 16;        // this wave's 16 weight rows
   int seg = 0, nloc = n0;
-  while (seg < 2 && nloc >= ga.nseg[seg]) { nloc -= ga.nseg[seg]; ++seg; }
-  const bool row_ok = (n0 + r) < ga.N;
-  const WT* wrow = reinterpret_cast<const WT*>(ga.w[seg]) + (size_t)(row_ok ? nloc + r : 0) * K;
-  const WT* wrow2 = (EPI == EPI_SWIGLU) ? reinterpret_cast<const WT*>(ga.w2) + (size_t)(row_ok ? n0 + r : 0) * K
-                                        : nullptr;
+  while (seg < 2 && nloc >= pa.nseg[seg]) { nloc -= pa.nseg[seg]; ++seg; }
+  const bool row_ok = n0 + r < pa.N;
+  const WT* wrow = reinterpret_cast<const WT*>(pa.w[seg]) + (size_t)(row_ok ? nloc + r : 0) * K;
+  const WT* wrow2 = (NACC == 2) ? reinterpret_cast<const WT*>(pa.w2) + (size_t)(row_ok ? n0 + r : 0) * K : nullptr;
   const int nsteps = (K + KS - 1) / KS;
-  int S_w = (nsteps + GEMM_WAVES - 1) / GEMM_WAVES;
-  S_w = (S_w + GEMM_D - 1) / GEMM_D * GEMM_D;
-  const int s0 = wave * S_w;
-  const int kg = g * EPL;                    // this lane's offset inside a step
+  const int st0 = blockIdx.y * nsteps / pa.S, st1 = (blockIdx.y + 1) * nsteps / pa.S;
+  const int kg = g * EPL;
 
-  // RMSNorm scale: partial sums of squares, loads issued first (in order)
-  constexpr int PV = 8;                      // partials per lane per row: K/16/64 <= 8 (K <= 8192)
-  constexpr int RPW = (MT * 16 + GEMM_WAVES - 1) / GEMM_WAVES;   // rows per wave
-  float pr[RPW][PV];
-  const bool norm = ga.scale == SCALE_NORM;
-  const int T = K >> 4;
-  if (norm) {
+  // activation block of a step: thread t moves uint4 t + 256 j of the
+  // (rows x KS) block (4 elements each), k clamped into the row
+  const char* abase = reinterpret_cast<const char*>(pa.A);
+  const int lda4 = pa.lda * 4;
+#define PG_SRC(j, st)                                                                                    \
+  (reinterpret_cast<const u32x4_t*>(abase + (size_t)min((int)(threadIdx.x + (j) * 256) / RB, M - 1) * lda4 + \
+                                  (size_t)min((st) * KS + ((int)(threadIdx.x + (j) * 256) % RB) * 4, K - 4) * 4))
+#define PG_DST(j) (((int)(threadIdx.x + (j) * 256) / RB) * LDR + ((int)(threadIdx.x + (j) * 256) % RB))
+  uint4 wb[2][NACC][GEMM_U];
+  {
+    u32x4_t av[SV];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int m = min(wave + i * GEMM_WAVES, M - 1);
+    for (int j = 0; j < SV; ++j) av[j] = *PG_SRC(j, st0);
 #pragma unroll
-      for (int j = 0; j < PV; ++j) {
-        const int t = lane + j * 64;
-        pr[i][j] = ga.pin[(size_t)m * T + min(t, T - 1)];
-      }
+    for (int d = 0; d < 2; ++d) {
+      const int kb = min(st0 + d, st1 - 1) * KS + kg;
+      load_w<WT>(wb[d][0], wrow, kb, K);
+      if constexpr (NACC == 2) load_w<WT>(wb[d][NACC - 1], wrow2, kb, K);
     }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // weights (and activations) of the first GEMM_D steps
-  uint4 wb[GEMM_D][NACC][GEMM_U];
-  uint4 ab[APRE ? GEMM_D : 1][1][GEMM_U][ANV];
-  const void* arow0 = a_row<WT>(ga.A, ga.lda, r < M ? r : 0);
 #pragma unroll
-  for (int d = 0; d < GEMM_D; ++d) {
-    const int kb = (s0 + d) * KS + kg;
-    load_w<WT>(wb[d][0], wrow, kb, K);
-    if constexpr (NACC == 2) load_w<WT>(wb[d][1], wrow2, kb, K);
-    if constexpr (APRE) load_a<WT>(ab[d][0], arow0, kb, K);
+    for (int j = 0; j < SV; ++j) reinterpret_cast<u32x4_t*>(a_s[0])[PG_DST(j)] = av[j];
   }
-  __builtin_amdgcn_sched_barrier(0);
-  const int ald = a_lds_ld(K);
-  if constexpr (ALDS) {
-    // copy rows [0, M) of A into LDS, 1 KB chunks, wave w takes chunks w, w + GEMM_WAVES, ...
-    const int cpr = (K + 255) >> 8;          // chunks per row
-    for (int c = wave; c < M * cpr; c += GEMM_WAVES) {
-      const int m = c / cpr, kc = (c - m * cpr) << 8;
-      const int k = min(kc + lane * 4, K - 4);
-      const char* src = reinterpret_cast<const char*>(ga.A) + ((size_t)m * ga.lda + k) * 4;
-      char* dst = reinterpret_cast<char*>(a_s) + ((size_t)m * ald + kc) * 4;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                       (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  if (norm) {
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int m = wave + i * GEMM_WAVES;
-      float v = 0.f;
-#pragma unroll
-      for (int j = 0; j < PV; ++j)
-        if (lane + j * 64 < T) v = __fadd_rn(v, pr[i][j]);
-      v = wave_sum(v);
-      if (lane == 0 && m < MT * 16)
-        rstd_s[m] = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(v, (float)K), ga.eps)));
-    }
-  }
-
+  __syncthreads();
   f32x4 acc[NACC][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
+  for (int q = 0; q < NACC; ++q)
 #pragma unroll
-    for (int q = 0; q < NACC; ++q) acc[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < S_w; i += GEMM_D) {
+    for (int t = 0; t < MT; ++t) acc[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s2 = st0; s2 < st1; s2 += 2) {
 #pragma unroll
-    for (int d = 0; d < GEMM_D; ++d) {
-      const int s = s0 + i + d;
-      const int kb = s * KS + kg;
-      const int kstep = s * KS;
-      if constexpr (APRE) {
-        gemm_step<WT, MT>(wb[d][0], ab[d], acc[0], kstep, K);
-        if constexpr (NACC == 2) gemm_step<WT, MT>(wb[d][1], ab[d], acc[1], kstep, K);
-      } else if constexpr (ALDS) {
-        uint4 a[MT][GEMM_U][ANV];
+    for (int d = 0; d < 2; ++d) {                      // d: compile-time buffer index
+      const int st = s2 + d;
+      if (st < st1) {                                  // workgroup-uniform
+        const bool more = st + 1 < st1;
+        u32x4_t av[SV];
+        if (more) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const int m = t * 16 + r;
-          const char* rowp = reinterpret_cast<const char*>(a_s) + (size_t)(m < M ? m : 0) * ald * 4;
+          for (int j = 0; j < SV; ++j) av[j] = *PG_SRC(j, st + 1);
+        }
+        const int kstep = st * KS;
+        const uint4* blk = a_s[d];
 #pragma unroll
-          for (int u = 0; u < GEMM_U; ++u) {
-            const int k = min(kb + u * 4 * EPL, K - EPL);
-            const uint4* q = reinterpret_cast<const uint4*>(rowp + (size_t)k * 4);
-            a[t][u][0] = q[0];
-            if constexpr (ANV == 2) a[t][u][1] = q[1];
+        for (int u = 0; u < GEMM_U; ++u) {
+          if (kstep + u * 4 * EPL >= K) break;         // wave-uniform: past the end of K
+          const int c16 = (kg + u * 4 * EPL) * 4 / 16; // uint4 column of this lane's k in the block
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const uint4* ap = &blk[(t * 16 + r) * LDR + c16];
+            if constexpr (sizeof(WT) == 2) {
+              const bf16x8_t hi = __builtin_bit_cast(bf16x8_t, ap[0]), lo = __builtin_bit_cast(bf16x8_t, ap[1]);
+#pragma unroll
+              for (int q = 0; q < NACC; ++q) {
+                const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, wb[d][q][u]);
+                acc[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bw, acc[q][t], 0, 0, 0);
+                acc[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bw, acc[q][t], 0, 0, 0);
+              }
+            } else {
+              const uint4 a4 = ap[0];
+              const float af[4] = {__uint_as_float(a4.x), __uint_as_float(a4.y), __uint_as_float(a4.z),
+                                   __uint_as_float(a4.w)};
+#pragma unroll
+              for (int q = 0; q < NACC; ++q) {
+                const float wf[4] = {__uint_as_float(wb[d][q][u].x), __uint_as_float(wb[d][q][u].y),
+                                     __uint_as_float(wb[d][q][u].z), __uint_as_float(wb[d][q][u].w)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  acc[q][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[e], wf[e], acc[q][t], 0, 0, 0);
+              }
+            }
           }
         }
-        gemm_step<WT, MT>(wb[d][0], a, acc[0], kstep, K);
-        if constexpr (NACC == 2) gemm_step<WT, MT>(wb[d][1], a, acc[1], kstep, K);
-      } else {
-        uint4 a[MT][GEMM_U][ANV];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const int m = t * 16 + r;
-          load_a<WT>(a[t], a_row<WT>(ga.A, ga.lda, m < M ? m : 0), kb, K);
+        if (st + 2 < st1) {                            // refill this weight buffer with step st + 2
+          const int kb = (st + 2) * KS + kg;
+          load_w<WT>(wb[d][0], wrow, kb, K);
+          if constexpr (NACC == 2) load_w<WT>(wb[d][NACC - 1], wrow2, kb, K);
         }
-        gemm_step<WT, MT>(wb[d][0], a, acc[0], kstep, K);
-        if constexpr (NACC == 2) gemm_step<WT, MT>(wb[d][1], a, acc[1], kstep, K);
+        if (more) {
+#pragma unroll
+          for (int j = 0; j < SV; ++j) reinterpret_cast<u32x4_t*>(a_s[d ^ 1])[PG_DST(j)] = av[j];
+        }
+        __syncthreads();                               // next block staged; this one no longer read
       }
-      // refill this buffer with step s + GEMM_D (past the wave's range: a clamped dummy)
-      const int kn = (i + d + GEMM_D < S_w) ? kb + GEMM_D * KS : K;
-      load_w<WT>(wb[d][0], wrow, kn, K);
-      if constexpr (NACC == 2) load_w<WT>(wb[d][1], wrow2, kn, K);
-      if constexpr (APRE) load_a<WT>(ab[d][0], arow0, kn, K);
     }
   }
+  // lane (r, g) holds D[row 16t + 4g + j][column n0 + r]
+  const int n = n0 + r;
+  if (n >= pa.N) return;
 #pragma unroll
   for (int q = 0; q < NACC; ++q)
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) red[q][t][wave][lane][j] = acc[q][t][j];
-  __syncthreads();
-  if (wave >= MT) return;
-  const int t = wave;
-  float v[NACC][4];
+      for (int j = 0; j < 4; ++j) {
+        const int m = t * 16 + 4 * g + j;
+        if (m < M) pa.part[(((size_t)blockIdx.y * NACC + q) * M + m) * pa.N + n] = acc[q][t][j];
+      }
+#undef PG_SRC
+#undef PG_DST
+}
+
+// 1 / rms of M rows from their per-16-column partial sums of squares
+// (fixed order: thread strides, wave tree, waves in order).
+__global__ __launch_bounds__(256) void k_rstd(const float* __restrict__ pin, int T, int K, float eps,
+                                             float* __restrict__ rstd) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  float v = 0.f;
+  for (int t = threadIdx.x; t < T; t += 256) v = __fadd_rn(v, pin[(size_t)m * T + t]);
+  v = block_sum(v, red);
+  if (threadIdx.x == 0) rstd[m] = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(v, (float)K), eps)));
+}
+
+// Split sum + epilogue of k_pgemm: one workgroup per 16-column tile, thread
+// (tid / 16, tid % 16) = (row in a 16-row pass, column in the tile).
+template <typename WT, int EPI>
+__global__ __launch_bounds__(256) void k_pepi(GemmArgs ga, const float* __restrict__ part, int S,
+                                              const float* __restrict__ rstd) {
+  constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
+  const int i = threadIdx.x & 15;
+  const int n = blockIdx.x * 16 + i;
+  const int M = ga.M;
+  for (int m0 = 0; m0 < M; m0 += 16) {                 // uniform over the workgroup
+    const int m = m0 + (threadIdx.x >> 4);
+    const int mm = min(m, M - 1), nn = min(n, ga.N - 1);
+    float y[NACC];
 #pragma unroll
-  for (int q = 0; q < NACC; ++q)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float s = red[q][t][0][lane][j];
-#pragma unroll
-      for (int w = 1; w < GEMM_WAVES; ++w) s = __fadd_rn(s, red[q][t][w][lane][j]);
-      v[q][j] = s;
+    for (int q = 0; q < NACC; ++q) {
+      float v = part[((size_t)q * M + mm) * ga.N + nn];
+      for (int s = 1; s < S; ++s) v = __fadd_rn(v, part[(((size_t)s * NACC + q) * M + mm) * ga.N + nn]);
+      y[q] = v;
     }
-  // lane (r, g) holds D[row 16t + 4g + j][column n0 + r]
-  const int n = n0 + r;
+    if (ga.scale == SCALE_NORM) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = t * 16 + 4 * g + j;
-    float sc = 1.0f;
-    bool scaled = false;
-    if (m < M) {
-      if (norm) { sc = rstd_s[m]; scaled = true; }
-      else if (ga.scale == SCALE_XS) { sc = ga.xs[m]; scaled = true; }
+      for (int q = 0; q < NACC; ++q) y[q] = __fmul_rn(y[q], rstd[mm]);
+    } else if (ga.scale == SCALE_XS) {
+#pragma unroll
+      for (int q = 0; q < NACC; ++q) y[q] = __fmul_rn(y[q], ga.xs[mm]);
     }
-    const float y = scaled ? __fmul_rn(v[0][j], sc) : v[0][j];
-    const float u = (NACC == 2) ? (scaled ? __fmul_rn(v[NACC - 1][j], sc) : v[NACC - 1][j]) : 0.f;
-    proj_out<WT, EPI>(ga, m, M, n, r, y, u);
+    proj_out<WT, EPI>(ga, m, M, n, i, y[0], NACC == 2 ? y[NACC - 1] : 0.f);
   }
 }
 
@@ -626,7 +572,6 @@ template <> struct GVt<uint16_t> { static constexpr int EPL = 8, AV = 2; };   //
 template <> struct GVt<float> { static constexpr int EPL = 4, AV = 1; };
 __host__ __device__ __forceinline__ int gv_chunk(int wbytes) { return wbytes == 2 ? 512 : 256; }
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_nt16(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
