@@ -97,22 +97,41 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
                       f"{len(recs)} rounds in {dt:.1f} s"}
 
 
-def recorded_traffic(bytes_per_launch):
-    """HBM bytes per launch of the draft gate/up kernel measured with rocprofv3
-    counters (profiles/draft_gemv_llama3_8b.md), or None when the kernel
-    source changed since the counters were taken or the launch is not the
-    recorded one (another model shape)."""
+GEMV_SECTIONS = ("scalars", "projection input format", "projections: shared definitions",
+                 "decode GEMV (vector ALU)")
+
+
+def gemv_source_hash():
+    """sha256 of the kernel-source sections the decode GEMV is built from
+    (the sections of lss_kernels.h named in GEMV_SECTIONS, in file order)."""
     import hashlib
     src = os.path.join(ROOT, "layer_skip_self_amd", "csrc", "lss_kernels.h")
+    mark = "// " + "-" * 64 + " "
+    sections, name = {}, None
+    for line in open(src):
+        if line.startswith(mark):
+            name = line[len(mark):].strip()
+        if name is not None:
+            sections[name] = sections.get(name, "") + line
+    h = hashlib.sha256()
+    for n in GEMV_SECTIONS:
+        h.update(sections[n].encode())
+    return h.hexdigest()
+
+
+def recorded_traffic(bytes_per_launch):
+    """HBM bytes per launch of the draft gate/up kernel measured with rocprofv3
+    counters (profiles/draft_gemv_llama3_8b.md), or None when the kernel's
+    source sections changed since the counters were taken or the launch is
+    not the recorded one (another model shape)."""
     rec = os.path.join(ROOT, "profiles", "draft_gemv_llama3_8b.md")
     try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
         fields = {}
         for line in open(rec):
             if ":" in line and line.startswith("- "):
                 k, v = line[2:].split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
-        if fields.get("kernel source sha256") != sha:
+        if fields.get("kernel source sha256") != gemv_source_hash():
             return None
         if int(fields["algorithmic bytes per launch"].split()[0]) != int(bytes_per_launch):
             return None
