@@ -891,46 +891,49 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
   AttTile<KT, HD> kt, vt;
   kt.load(kc, u0, a.max_seq);
   vt.load(vc, u0, a.max_seq);
-  // rotated queries of this block
-  for (int i = tid; i < ATT_QB * HD; i += ATT_THREADS) {
+  // rotated queries of this block (only rows of real queries are read later)
+  const int nqb = min(ATT_QB, nq - q0);
+  for (int i = tid; i < nqb * HD; i += ATT_THREADS) {
     const int qi = i / HD, dd = i % HD;
     const int gq = q0 + qi;
-    float v = 0.f;
-    if (gq < nq) {
-      const int m = gq / G, h = kh * G + gq % G;
-      const int pos = a.pos0 + m * a.pos_step;
-      v = rope_elem(a.qkv + (size_t)m * a.ldqkv + (size_t)h * HD, a.cs + (size_t)pos * (HD / 2), dd, HD / 2);
-    }
-    q_s[qi][dd] = v;
+    const int m = gq / G, h = kh * G + gq % G;
+    const int pos = a.pos0 + m * a.pos_step;
+    q_s[qi][dd] = rope_elem(a.qkv + (size_t)m * a.ldqkv + (size_t)h * HD, a.cs + (size_t)pos * (HD / 2), dd, HD / 2);
   }
   kt.store(kv_s);
   __syncthreads();
   att_new_rows<KT, HD>(kv_s, a, kh, u0, z, false);
   __syncthreads();
-  // scores: lane = key, each wave takes queries wave, wave + 4, ...
+  // scores: lane = key; each wave takes query pairs (qi, qi + 4) for
+  // qi = wave, wave + 8, ..., two independent dot-product chains per lane
   {
     const int u = lane, pos = u0 + u;
-    for (int qi = wave; qi < ATT_QB; qi += ATT_THREADS / 64) {
-      const int gq = q0 + qi;
-      if (q0 + (qi & ~3) >= nq) break;               // wave-uniform: no valid query left
-      float s = -INFINITY;
-      if (gq < nq) {
-        const int m = gq / G;
+    for (int qb = wave; qb < nqb; qb += 2 * (ATT_THREADS / 64)) {   // wave-uniform
+      const int qc = qb + ATT_THREADS / 64;
+      const bool has_c = qc < nqb;
+      const int qcc = has_c ? qc : qb;
+      float da = 0.f, dc = 0.f;
+#pragma unroll 8
+      for (int dd = 0; dd < HD; ++dd) {
+        const float kv = kv_s[u][dd];
+        da = fmaf(q_s[qb][dd], kv, da);
+        dc = fmaf(q_s[qcc][dd], kv, dc);
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        if (h2 == 1 && !has_c) break;                  // wave-uniform
+        const int qi = h2 ? qc : qb;
+        const int m = (q0 + qi) / G;
         const int lim = a.lim_base + m * a.lim_step;
         const int wo = pos - a.wbase;
         const bool vis = pos < lim || (wo >= 0 && wo < 32 && ((a.wmask >> wo) & 1u));
-        if (vis && pos < a.max_seq) {
-          float dot = 0.f;
-#pragma unroll 8
-          for (int dd = 0; dd < HD; ++dd) dot = fmaf(q_s[qi][dd], kv_s[u][dd], dot);
-          s = __fmul_rn(dot, a.scale);
-        }
+        const float s = (vis && pos < a.max_seq) ? __fmul_rn(h2 ? dc : da, a.scale) : -INFINITY;
+        const float mx = wave_max_dpp(s);
+        const float e = (s == -INFINITY) ? 0.f : expf(__fsub_rn(s, mx));
+        const float l = wave_sum_dpp(e);
+        p_s[qi][u] = e;
+        if (lane == 0) { st_s[qi][0] = mx; st_s[qi][1] = l; }
       }
-      const float mx = wave_max_dpp(s);
-      const float e = (s == -INFINITY) ? 0.f : expf(__fsub_rn(s, mx));
-      const float l = wave_sum_dpp(e);
-      p_s[qi][u] = e;
-      if (lane == 0) { st_s[qi][0] = mx; st_s[qi][1] = l; }
     }
   }
   __syncthreads();
@@ -938,16 +941,29 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
   __syncthreads();
   att_new_rows<KT, HD>(kv_s, a, kh, u0, z, true);
   __syncthreads();
+  // value sums: outputs i and i + 256 of the (query, dim) grid per thread,
+  // two independent chains over the 64 keys
   float* part = a.part + (((size_t)kh * a.nz_max + z) * a.nch_max + c) * ATT_QB * (HD + 2);
-  for (int i = tid; i < ATT_QB * HD; i += ATT_THREADS) {
-    const int qi = i / HD, dd = i % HD;
-    if (q0 + qi >= nq) break;
-    float acc = 0.f;
+  const int nout = nqb * HD;
+  for (int i0 = tid; i0 < nout; i0 += 2 * ATT_THREADS) {
+    const int i1 = i0 + ATT_THREADS;
+    const bool has1 = i1 < nout;
+    const int qa = i0 / HD, da = i0 % HD;
+    const int qc = has1 ? i1 / HD : qa, dc = has1 ? i1 % HD : da;
+    float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll 8
-    for (int u = 0; u < ATT_CH; ++u) acc = fmaf(p_s[qi][u], kv_s[u][dd], acc);
-    float* o = part + (size_t)qi * (HD + 2);
-    o[dd] = acc;
-    if (dd == 0) { o[HD] = st_s[qi][0]; o[HD + 1] = st_s[qi][1]; }
+    for (int u = 0; u < ATT_CH; ++u) {
+      acc0 = fmaf(p_s[qa][u], kv_s[u][da], acc0);
+      acc1 = fmaf(p_s[qc][u], kv_s[u][dc], acc1);
+    }
+    float* o0 = part + (size_t)qa * (HD + 2);
+    o0[da] = acc0;
+    if (da == 0) { o0[HD] = st_s[qa][0]; o0[HD + 1] = st_s[qa][1]; }
+    if (has1) {
+      float* o1 = part + (size_t)qc * (HD + 2);
+      o1[dc] = acc1;
+      if (dc == 0) { o1[HD] = st_s[qc][0]; o1[HD + 1] = st_s[qc][1]; }
+    }
   }
 }
 
