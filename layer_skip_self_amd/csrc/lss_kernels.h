@@ -33,48 +33,68 @@ template <typename T> __device__ __forceinline__ void st_elem(T* p, size_t i, fl
 template <> __device__ __forceinline__ void st_elem<float>(float* p, size_t i, float v) { p[i] = v; }
 template <> __device__ __forceinline__ void st_elem<uint16_t>(uint16_t* p, size_t i, float v) { p[i] = f2bf(v); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-// Sum over the 64 lanes without LDS traffic: four DPP steps inside each
-// 16-lane row (partners lane ^ 1, lane ^ 2, the mirrored lane of the 8-lane
-// half, the mirrored lane of the row; every lane of a row then holds the
-// same row sum, since a + b == b + a), then the four row sums added as
-// (r0 + r1) + (r2 + r3).  The result is the same in every lane.
+// Cross-lane reductions without LDS traffic.  Inside each 16-lane row four
+// DPP steps pair lane i with i ^ 1, i ^ 2, the mirrored lane of its 8-lane
+// half and the mirrored lane of the row; after them every lane of a row
+// holds the same row result (a + b == b + a).  Wave results then combine
+// the four row results (lanes 0, 16, 32, 48) as (r0 . r1) . (r2 . r3).
+// Callers run them with the whole row / wave active.
 template <int CTRL> __device__ __forceinline__ float dpp_t(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v = __fadd_rn(v, dpp_t<0xB1>(v));    // quad_perm [1, 0, 3, 2]
-  v = __fadd_rn(v, dpp_t<0x4E>(v));    // quad_perm [2, 3, 0, 1]
-  v = __fadd_rn(v, dpp_t<0x141>(v));   // row_half_mirror
-  v = __fadd_rn(v, dpp_t<0x140>(v));   // row_mirror
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return __fadd_rn(__fadd_rn(a, b), __fadd_rn(c, d));
+template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = fmaxf(v, dpp_t<0xB1>(v));
-  v = fmaxf(v, dpp_t<0x4E>(v));
-  v = fmaxf(v, dpp_t<0x141>(v));
-  v = fmaxf(v, dpp_t<0x140>(v));
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+#define LSS_DPP_XOR1 0xB1     // quad_perm [1, 0, 3, 2]
+#define LSS_DPP_XOR2 0x4E     // quad_perm [2, 3, 0, 1]
+#define LSS_DPP_HMIRROR 0x141 // row_half_mirror
+#define LSS_DPP_MIRROR 0x140  // row_mirror
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
-// fixed-order sum over the 16 lanes of a lane group
+// fixed-order sum over the 16 lanes of a row
 __device__ __forceinline__ float sum16(float v) {
-  for (int o = 8; o >= 1; o >>= 1) v = __fadd_rn(v, __shfl_xor(v, o, 16));
+  v = __fadd_rn(v, dpp_t<LSS_DPP_XOR1>(v));
+  v = __fadd_rn(v, dpp_t<LSS_DPP_XOR2>(v));
+  v = __fadd_rn(v, dpp_t<LSS_DPP_HMIRROR>(v));
+  v = __fadd_rn(v, dpp_t<LSS_DPP_MIRROR>(v));
   return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum16(v);
+  return __fadd_rn(__fadd_rn(readlane_f(v, 0), readlane_f(v, 16)), __fadd_rn(readlane_f(v, 32), readlane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_t<LSS_DPP_XOR1>(v));
+  v = fmaxf(v, dpp_t<LSS_DPP_XOR2>(v));
+  v = fmaxf(v, dpp_t<LSS_DPP_HMIRROR>(v));
+  v = fmaxf(v, dpp_t<LSS_DPP_MIRROR>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+// (value, index) maximum with the lowest index on ties: a total order, so the
+// result does not depend on the reduction tree
+__device__ __forceinline__ void argmax_merge(float& mx, int& idx, float om, int oi) {
+  if (om > mx || (om == mx && oi < idx)) { mx = om; idx = oi; }
+}
+template <int CTRL> __device__ __forceinline__ void argmax_dpp_step(float& mx, int& idx) {
+  const float om = dpp_t<CTRL>(mx);
+  const int oi = dpp_i<CTRL>(idx);
+  argmax_merge(mx, idx, om, oi);
+}
+__device__ __forceinline__ void argmax16(float& mx, int& idx) {
+  argmax_dpp_step<LSS_DPP_XOR1>(mx, idx);
+  argmax_dpp_step<LSS_DPP_XOR2>(mx, idx);
+  argmax_dpp_step<LSS_DPP_HMIRROR>(mx, idx);
+  argmax_dpp_step<LSS_DPP_MIRROR>(mx, idx);
+}
+__device__ __forceinline__ void argmax_wave(float& mx, int& idx) {
+  argmax16(mx, idx);
+  float m0 = readlane_f(mx, 0);
+  int i0 = __builtin_amdgcn_readlane(idx, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) argmax_merge(m0, i0, readlane_f(mx, 16 * r), __builtin_amdgcn_readlane(idx, 16 * r));
+  mx = m0;
+  idx = i0;
 }
 // Block-wide sum in a fixed order (wave tree, then waves in index order).
 // `red` holds >= blockDim/64 floats; returns the total to every thread.
@@ -336,11 +356,7 @@ __device__ __forceinline__ void proj_out(const GemmArgs& ga, int m, int M, int n
     if (ok) ga.Y[(size_t)m * ga.ldy + n] = y;
     float mx = (n < ga.N) ? y : -INFINITY;
     int idx = n;
-    for (int o = 8; o >= 1; o >>= 1) {
-      const float om = __shfl_xor(mx, o, 16);
-      const int oi = __shfl_xor(idx, o, 16);
-      if (om > mx || (om == mx && oi < idx)) { mx = om; idx = oi; }
-    }
+    argmax16(mx, idx);
     float e = (n < ga.N) ? expf(__fsub_rn(y, mx)) : 0.f;
     e = sum16(e);
     if (cl == 0 && m < M) {
@@ -560,7 +576,7 @@ __global__ __launch_bounds__(256) void k_pepi(GemmArgs ga, const float* __restri
 // Per (weight row n, activation row m) the arithmetic is fixed by K alone:
 // lane l runs one FMA chain over k = c CH + l EPL + e for the chunks c of
 // its wave's range (ascending) and e ascending, the 64 lane values are
-// summed by the fixed tree of wave_sum_dpp, and the GV_WAVES wave sums are
+// summed by the fixed tree of wave_sum, and the GV_WAVES wave sums are
 // added in wave order.  Nothing depends on M, on the tile or on the row group, so
 // a verify row gets the same bits as a one-row greedy step.
 #define GV_WAVES 8
@@ -715,7 +731,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
         for (int q = 0; q < NACC; ++q)
 #pragma unroll
           for (int m = 0; m < MB; ++m) {
-            const float t = wave_sum_dpp(acc[r][q][m]);
+            const float t = wave_sum(acc[r][q][m]);
             if (lane == 0) part_s[wave][q][m][g * RG + r] = t;
           }
     }
@@ -724,7 +740,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       float v = ((int)threadIdx.x < T) ? pr[m] : 0.f;
-      v = wave_sum_dpp(v);
+      v = wave_sum(v);
       if (lane == 0) red_s[wave][m] = v;
     }
   }
@@ -928,9 +944,9 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
         const int wo = pos - a.wbase;
         const bool vis = pos < lim || (wo >= 0 && wo < 32 && ((a.wmask >> wo) & 1u));
         const float s = (vis && pos < a.max_seq) ? __fmul_rn(h2 ? dc : da, a.scale) : -INFINITY;
-        const float mx = wave_max_dpp(s);
+        const float mx = wave_max(s);
         const float e = (s == -INFINITY) ? 0.f : expf(__fsub_rn(s, mx));
-        const float l = wave_sum_dpp(e);
+        const float l = wave_sum(e);
         p_s[qi][u] = e;
         if (lane == 0) { st_s[qi][0] = mx; st_s[qi][1] = l; }
       }
@@ -972,7 +988,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
 // chunk statistics with lane = chunk (nch <= 64): M = max of the chunk
 // maxima over chunks that saw a key (and, for layer-selection rows, the
 // row's own score), weights w_c = exp(m_c - M), normalizer
-// L = sum_c l_c w_c by the fixed lane tree of wave_sum_dpp (+ the own
+// L = sum_c l_c w_c by the fixed lane tree of wave_sum (+ the own
 // key's weight).  Thread dd then adds w_c * partial_c[dd] over the chunks in
 // chunk order and divides by L.  Every step depends on positions only.
 #define ATT_MERGE_MAXCH 64
@@ -1006,11 +1022,11 @@ __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
       float dot = 0.f;
       for (int dd = lane; dd < HD; dd += 64)
         dot = fmaf(rope_elem(qx, cs, dd, HD / 2), rope_elem(kx, cs, dd, HD / 2), dot);
-      self = __fmul_rn(wave_sum_dpp(dot), a.scale);
+      self = __fmul_rn(wave_sum(dot), a.scale);
     }
-    const float M = fmaxf(wave_max_dpp(seen ? mc : -INFINITY), self);
+    const float M = fmaxf(wave_max(seen ? mc : -INFINITY), self);
     const float wc = seen ? expf(__fsub_rn(mc, M)) : 0.f;
-    float L = wave_sum_dpp(seen ? __fmul_rn(lc, wc) : 0.f);
+    float L = wave_sum(seen ? __fmul_rn(lc, wc) : 0.f);
     float ws = 0.f;
     if (a.self_kv) {
       ws = expf(__fsub_rn(self, M));
@@ -1054,19 +1070,15 @@ __global__ __launch_bounds__(HEAD_RED_THREADS) void k_head_reduce(const float* _
   for (int w = threadIdx.x; w < ntile; w += blockDim.x) {
     const float v = p[w * 3];
     const int i = __float_as_int(p[w * 3 + 1]);
-    if (v > mx || (v == mx && i < idx)) { mx = v; idx = i; }
+    argmax_merge(mx, idx, v, i);
   }
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float om = __shfl_xor(mx, o, 64);
-    const int oi = __shfl_xor(idx, o, 64);
-    if (om > mx || (om == mx && oi < idx)) { mx = om; idx = oi; }
-  }
+  argmax_wave(mx, idx);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   if (lane == 0) { bm[wv] = mx; bi[wv] = idx; }
   __syncthreads();
   mx = bm[0]; idx = bi[0];
   for (int i = 1; i < (int)(blockDim.x >> 6); ++i)
-    if (bm[i] > mx || (bm[i] == mx && bi[i] < idx)) { mx = bm[i]; idx = bi[i]; }
+    argmax_merge(mx, idx, bm[i], bi[i]);
   float s = 0.f;
   for (int w = threadIdx.x; w < ntile; w += blockDim.x)
     s = __fadd_rn(s, __fmul_rn(p[w * 3 + 2], expf(__fsub_rn(p[w * 3], mx))));
