@@ -306,7 +306,7 @@ def main():
         "draft_gemv_gbps": round(achieved, 1) if achieved else None,
         "roofline": {
             "bound": "hbm",
-            "kernel": f"k_gemv<{shape.dtype},1,SWIGLU>: draft gate/up projection + SwiGLU, 1 row",
+            "kernel": f"k_gemv<{shape.dtype},1,1,SWIGLU,8>: draft gate/up projection + SwiGLU, 1 row",
             "achieved": round(achieved, 1) if achieved else None,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -257,21 +257,26 @@ int gemv_cap(int K, int wbytes) {
   return ncw == 1 ? GV_MB_MAX : std::max(1, std::min(4, GV_ACT_MAX / ncw));
 }
 
+// 8-row tiles where the epilogue has no per-16-column partials (more
+// workgroups, so their tails overlap other workgroups' loads)
+template <int EPI> constexpr int gemv_tile() { return (EPI == EPI_STORE || EPI == EPI_SWIGLU) ? 8 : 16; }
+
 template <typename WT, int EPI, int NCW>
 void gemv_launch(const GemmArgs& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  const dim3 grid((g.N + 15) / 16), block(64 * GV_WAVES);
+  constexpr int TR = gemv_tile<EPI>();
+  const dim3 grid((g.N + TR - 1) / TR), block(64 * GV_WAVES);
   if constexpr (NCW == 1) {
-    if (g.M == 1) launch_k(k_gemv<WT, 1, 1, EPI>, grid, block, 0, s, t0, t1, g);
-    else if (g.M == 2) launch_k(k_gemv<WT, 2, 1, EPI>, grid, block, 0, s, t0, t1, g);
-    else if (g.M <= 4) launch_k(k_gemv<WT, 4, 1, EPI>, grid, block, 0, s, t0, t1, g);
-    else launch_k(k_gemv<WT, 8, 1, EPI>, grid, block, 0, s, t0, t1, g);
+    if (g.M == 1) launch_k(k_gemv<WT, 1, 1, EPI, TR>, grid, block, 0, s, t0, t1, g);
+    else if (g.M == 2) launch_k(k_gemv<WT, 2, 1, EPI, TR>, grid, block, 0, s, t0, t1, g);
+    else if (g.M <= 4) launch_k(k_gemv<WT, 4, 1, EPI, TR>, grid, block, 0, s, t0, t1, g);
+    else launch_k(k_gemv<WT, 8, 1, EPI, TR>, grid, block, 0, s, t0, t1, g);
   } else if constexpr (NCW == 2 || NCW == 4) {
-    if (g.M == 1) launch_k(k_gemv<WT, 1, NCW, EPI>, grid, block, 0, s, t0, t1, g);
-    else if (g.M == 2) launch_k(k_gemv<WT, 2, NCW, EPI>, grid, block, 0, s, t0, t1, g);
-    else launch_k(k_gemv<WT, 4, NCW, EPI>, grid, block, 0, s, t0, t1, g);
+    if (g.M == 1) launch_k(k_gemv<WT, 1, NCW, EPI, TR>, grid, block, 0, s, t0, t1, g);
+    else if (g.M == 2) launch_k(k_gemv<WT, 2, NCW, EPI, TR>, grid, block, 0, s, t0, t1, g);
+    else launch_k(k_gemv<WT, 4, NCW, EPI, TR>, grid, block, 0, s, t0, t1, g);
   } else {
-    if (g.M == 1) launch_k(k_gemv<WT, 1, 8, EPI>, grid, block, 0, s, t0, t1, g);
-    else launch_k(k_gemv<WT, 2, 8, EPI>, grid, block, 0, s, t0, t1, g);
+    if (g.M == 1) launch_k(k_gemv<WT, 1, 8, EPI, TR>, grid, block, 0, s, t0, t1, g);
+    else launch_k(k_gemv<WT, 2, 8, EPI, TR>, grid, block, 0, s, t0, t1, g);
   }
 }
 

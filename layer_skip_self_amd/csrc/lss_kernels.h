@@ -565,11 +565,12 @@ __global__ __launch_bounds__(256) void k_pepi(GemmArgs ga, const float* __restri
 // pattern is chosen for HBM: each load instruction of a wave reads one 1 KB
 // contiguous piece ("chunk") of one weight row (lane l: the 16 bytes at
 // offset 16 l), with nontemporal hints since the weights are read once.
-// A workgroup owns a 16-row tile of N; its GV_WAVES waves split the chunks
+// A workgroup owns a tile of 16 rows of N (8 where the epilogue has no
+// per-16-column partials: store, SwiGLU); its GV_WAVES waves split the chunks
 // of K into contiguous ranges (wave w: chunks [w nc / W, (w + 1) nc / W)),
 // and each wave walks the tile's rows in groups of RG rows, the chunks of
-// its range inside each group, RG x NACC 1 KB loads per step with two steps
-// in flight.  A lane keeps the activation elements of its k in registers
+// its range inside each group, RG x NACC 1 KB loads per step with GV_ST
+// steps in flight.  A lane keeps the activation elements of its k in registers
 // (float32, converted once from the projection format) and multiplies them
 // with its 8 (bf16) / 4 (float32) weights in fused multiply-adds.
 //
@@ -580,6 +581,9 @@ __global__ __launch_bounds__(256) void k_pepi(GemmArgs ga, const float* __restri
 // added in wave order.  Nothing depends on M, on the tile or on the row group, so
 // a verify row gets the same bits as a one-row greedy step.
 #define GV_WAVES 8
+#ifndef GV_ST
+#define GV_ST 2                  // weight steps in flight per wave
+#endif
 #define GV_MB_MAX 8              // activation rows per launch
 #define GV_ACT_MAX 16            // MB x NCW: activation vectors (one chunk of one row) per lane
 
@@ -624,15 +628,17 @@ __device__ __forceinline__ void unpack_x(const uint4 (&a)[GVt<WT>::AV], float (&
 
 // MB: activation rows (M <= MB); NCW: chunks per wave the launch may need
 // (>= ceil(nc / GV_WAVES)), MB * NCW <= GV_ACT_MAX.
-template <typename WT, int MB, int NCW, int EPI>
+template <typename WT, int MB, int NCW, int EPI, int TR = 16>
 __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
   constexpr int EPL = GVt<WT>::EPL, AV = GVt<WT>::AV, CH = 64 * EPL;
   constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int RG = 8 / NACC;                  // weight rows per step: 8 loads of 1 KB
-  constexpr int NG = 16 / RG;                   // row groups per tile
+  constexpr int NG = TR / RG;                   // row groups per tile
+  static_assert(TR == 16 || (TR == 8 && (EPI == EPI_STORE || EPI == EPI_SWIGLU)),
+                "8-row tiles only without per-16-column epilogue partials");
   constexpr int NU = NG * NCW;                  // steps per wave (chunks past the range are skipped)
   static_assert(MB * NCW <= GV_ACT_MAX, "activation registers");
-  __shared__ float part_s[GV_WAVES][NACC][MB][16];
+  __shared__ float part_s[GV_WAVES][NACC][MB][TR];
   __shared__ float red_s[GV_WAVES][MB];
 
   const int lane = threadIdx.x & 63;
@@ -641,14 +647,14 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
   const int nc = (K + CH - 1) / CH;
   const int c0 = wave * nc / GV_WAVES;
   const int ncw = (wave + 1) * nc / GV_WAVES - c0;       // chunks of this wave (<= NCW)
-  const int tile0 = blockIdx.x * 16;
+  const int tile0 = blockIdx.x * TR;
   int seg = 0, nloc = tile0;
   while (seg < 2 && nloc >= ga.nseg[seg]) { nloc -= ga.nseg[seg]; ++seg; }
   const WT* wbase[NACC];
   wbase[0] = reinterpret_cast<const WT*>(ga.w[seg]) + (size_t)nloc * K;
   if constexpr (NACC == 2) wbase[NACC - 1] = reinterpret_cast<const WT*>(ga.w2) + (size_t)tile0 * K;
   const int kl = lane * EPL;
-  const int nrow = min(16, ga.N - tile0);                 // rows of the tile inside N
+  const int nrow = min(TR, ga.N - tile0);                 // rows of the tile inside N
 
   // (1) this wave's activation chunks (raw projection format)
   uint4 xr[NCW][MB][AV];
@@ -681,9 +687,10 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
       for (int q = 0; q < NACC; ++q) w[r][q] = ld_nt16(wbase[q] + ro);
     }
   };
-  uint4 wb[2][RG][NACC];
-  if (0 < ncw) unit_load(wb[0], 0);
-  if (1 % NCW < ncw) unit_load(wb[1], 1);
+  uint4 wb[GV_ST][RG][NACC];
+#pragma unroll
+  for (int u = 0; u < GV_ST; ++u)
+    if (u < NU && u % NCW < ncw) unit_load(wb[u], u);
   __builtin_amdgcn_sched_barrier(0);
   // activations as float32; lanes past K hold zeros
   float x[NCW][MB][EPL];
@@ -716,14 +723,14 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
 #pragma unroll
         for (int q = 0; q < NACC; ++q) {
           float wf[EPL];
-          unpack_w<WT>(wb[u & 1][r][q], wf);
+          unpack_w<WT>(wb[u % GV_ST][r][q], wf);
 #pragma unroll
           for (int m = 0; m < MB; ++m)
 #pragma unroll
             for (int e = 0; e < EPL; ++e) acc[r][q][m] = fmaf(wf[e], x[i][m][e], acc[r][q][m]);
         }
     }
-    if (u + 2 < NU && (u + 2) % NCW < ncw) unit_load(wb[u & 1], u + 2);
+    if (u + GV_ST < NU && (u + GV_ST) % NCW < ncw) unit_load(wb[u % GV_ST], u + GV_ST);
     if (i == NCW - 1) {                                    // group g done: lane sums -> LDS
 #pragma unroll
       for (int r = 0; r < RG; ++r)
@@ -748,6 +755,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
   // epilogue: thread (m, i) = (tid / 16, tid % 16) -> row m, column tile0 + i
   if (threadIdx.x >= 16 * MB) return;
   const int m = threadIdx.x >> 4, i = threadIdx.x & 15;
+  if (TR < 16 && i >= TR) return;                      // no 16-lane reductions in these epilogues
   float sc = 1.0f;
   bool scaled = false;
   if (m < M) {
