@@ -19,6 +19,9 @@ Sources (the pages this implements; no equations beyond two are printed there):
     三 (draft -> verify -> layer-optimization workflow, the DP over
     (i layers, j skipped) with cosine similarity, sequence-parallel batching
     of the j-states with a special mask), section 四 (interval, exit threshold).
+  * Sampling (``oracle.sampling``): the pages' claim that the method keeps the
+    full model's output distribution, read as the standard speculative-
+    sampling acceptance rule with a counter-based generator.
 
 Floating point: the oracle computes in float64 by default (``dtype``
 argument); the pages fix no precision.  Decisions that turn floating point
@@ -33,11 +36,12 @@ from .decode import (DecodeState, layer_block, prefill, forward_row, ar_generate
 from .clasp import clasp_dp, brute_force_skip, forward_with_mask_at_target
 from .dytc import (ALPHA, A_INIT, ema_update, fit_latency, predict_latency,
                    plan_cascade, update_cascade)
+from . import sampling
 
 __all__ = [
     "OracleModel", "rms_norm", "rope", "silu", "attend", "quantize_row", "argmax_first",
     "DecodeState", "layer_block", "prefill", "forward_row", "ar_generate", "draft", "verify", "accept",
     "speculative_generate", "Policy", "clasp_dp", "brute_force_skip",
     "forward_with_mask_at_target", "ALPHA", "A_INIT", "ema_update", "fit_latency",
-    "predict_latency", "plan_cascade", "update_cascade",
+    "predict_latency", "plan_cascade", "update_cascade", "sampling",
 ]

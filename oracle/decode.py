@@ -40,6 +40,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from .model import rms_norm, rope, silu, attend, fake_quant, argmax_first
+from . import sampling as smp
 
 WINDOW_MAX = 32
 
@@ -58,6 +59,8 @@ class DecodeState:
         self.valid = [0] * L       # per layer: bit j set = KV at p+j written by a draft
         self.target_states = None  # full states H*[0..L] of the last accepted token
         self.target_pos = None     # its position t*
+        self.window_logits = []    # sampling: draft logits that produced each window token
+        self.margins = []          # sampling: slack of every random decision taken
 
 
 def _project(W, x):
@@ -164,11 +167,23 @@ def layer_block(model, l, H, st=None):
     return H + A @ lw["w_down"].T
 
 
-def prefill(model, tokens, max_seq, progress=None):
+def _pick(st, z, sampling, purpose, pos):
+    """Greedy argmax (sampling None) or a draw from softmax(z / T) with the
+    (seed, purpose, pos) stream of ``oracle.sampling``."""
+    if sampling is None:
+        return argmax_first(z)
+    T, seed = sampling
+    t, m = smp.sample(z, T, seed, purpose, pos)
+    st.margins.append(m)
+    return t
+
+
+def prefill(model, tokens, max_seq, progress=None, sampling=None):
     """Causal full-model pass over the prompt, as one block of rows.
 
     Returns (state, logits of the last row, states of the last row).  The
-    pending token t0 is the argmax of the last row; the last prompt row is the
+    pending token t0 is the argmax of the last row (with ``sampling`` =
+    (T, seed): its TARGET draw at position P-1); the last prompt row is the
     first layer-selection target (its own KV stays committed at P-1).
     """
     m = model
@@ -185,19 +200,22 @@ def prefill(model, tokens, max_seq, progress=None):
             progress(l)
     z = m.head(H[-1])
     st.p = P
-    st.t0 = argmax_first(z)
+    st.t0 = _pick(st, z, sampling, smp.TARGET, P - 1)
     st.target_states = last_states
     st.target_pos = P - 1
     return st, z, last_states
 
 
-def draft(model, st, skip, quant, k, tau=0.0):
+def draft(model, st, skip, quant, k, tau=0.0, sampling=None):
     """Draft up to ``k`` tokens into the window with a skip mask.
 
     Returns (tokens drafted by this call, top-1 probabilities).  Appends to
     any tokens already in the window (several draft levels may share one
     window).  With ``tau > 0`` drafting stops after the first token whose
-    top-1 softmax probability is below ``tau``.
+    top-1 softmax probability is below ``tau``.  With ``sampling`` =
+    (T, seed) each token is the DRAFT draw of its row's position, the top-1
+    probability is taken at temperature T, and the logits are kept for the
+    acceptance test.
     """
     out, pmax = [], []
     for _ in range(k):
@@ -206,11 +224,15 @@ def draft(model, st, skip, quant, k, tau=0.0):
         tok = st.t0 if not st.window else st.window[-1]
         pos = st.p + len(st.window)
         z, _ = forward_row(model, st, tok, pos, "draft", skip, quant)
-        d = argmax_first(z)
+        d = _pick(st, z, sampling, smp.DRAFT, pos)
         st.window.append(d)
+        st.window_logits.append(z)
         out.append(d)
-        zs = z - np.max(z)
-        pm = 1.0 / float(np.sum(np.exp(zs)))
+        if sampling is None:
+            zs = z - np.max(z)
+            pm = 1.0 / float(np.sum(np.exp(zs)))
+        else:
+            pm = smp.top1_prob(z, sampling[0])
         pmax.append(pm)
         if tau > 0 and pm < tau:
             break
@@ -233,41 +255,52 @@ def verify(model, st, drafts=None):
     return np.stack(logits), states, d
 
 
-def accept(st, logits, states, drafts):
+def accept(st, logits, states, drafts, sampling=None):
     """Greedy acceptance and rollback.
 
     a_i = argmax of verify row i; n = length of the longest prefix of the
-    drafts that equals a_0..a_{n-1}; bonus = a_n.  The committed length moves
-    to p + n + 1 (rows past it are stale and never read); the window is
-    cleared; row n becomes the next layer-selection target.
+    drafts that equals a_0..a_{n-1}; bonus = a_n.  With ``sampling`` =
+    (T, seed) the speculative-sampling rule of ``oracle.sampling`` decides n
+    and the bonus (the replacement draw at a rejection).  The committed
+    length moves to p + n + 1 (rows past it are stale and never read); the
+    window is cleared; row n becomes the next layer-selection target.
     Returns (n, bonus, emitted tokens d_1..d_n + [bonus]).
     """
     k = len(drafts)
-    a = [argmax_first(z) for z in logits]
-    n = 0
-    while n < k and a[n] == drafts[n]:
-        n += 1
-    bonus = a[n]
+    if sampling is None:
+        a = [argmax_first(z) for z in logits]
+        n = 0
+        while n < k and a[n] == drafts[n]:
+            n += 1
+        bonus = a[n]
+    else:
+        if k and len(st.window_logits) != k:
+            raise ValueError("sampling acceptance needs the draft logits of every window token")
+        T, seed = sampling
+        n, bonus, mg = smp.accept_sampling(logits, st.window_logits, drafts, T, seed, st.p)
+        st.margins.extend(mg)
     emitted = list(drafts[:n]) + [bonus]
     st.target_states = states[n]
     st.target_pos = st.p + n
     st.p = st.p + n + 1
     st.t0 = bonus
     st.window = []
+    st.window_logits = []
     st.valid = [0] * len(st.valid)
     return n, bonus, emitted
 
 
-def ar_generate(model, prompt, G, max_seq=None):
-    """Greedy autoregressive decoding: G tokens (t0 included)."""
+def ar_generate(model, prompt, G, max_seq=None, sampling=None):
+    """Autoregressive decoding of G tokens (t0 included): greedy, or with
+    ``sampling`` = (T, seed) the TARGET draw of every row's position."""
     max_seq = max_seq or len(prompt) + G + 1
-    st, z, _ = prefill(model, prompt, max_seq)
+    st, z, _ = prefill(model, prompt, max_seq, sampling=sampling)
     out = [st.t0]
     while len(out) < G:
         zz, s = forward_row(model, st, st.t0, st.p, "full")
         st.target_states, st.target_pos = s, st.p
+        st.t0 = _pick(st, zz, sampling, smp.TARGET, st.p)
         st.p += 1
-        st.t0 = argmax_first(zz)
         out.append(st.t0)
     return out
 
@@ -280,7 +313,9 @@ class Policy:
     CLaSp DP chooses (overrides ``skip``), re-run every ``interval`` verify
     rounds; tau: draft exit threshold (0 = off); cascade: a list of levels
     ``[(n_skip_by_dp, exit_layers, quant)]`` ordered fast -> precise, routed
-    by the DyTC heuristics with at most ``K`` drafts per round.
+    by the DyTC heuristics with at most ``K`` drafts per round;
+    temperature > 0: speculative sampling with that temperature and seed
+    (``oracle.sampling``), 0: greedy.
     """
     K: int = 4
     skip: tuple = ()
@@ -291,6 +326,13 @@ class Policy:
     cascade: list = None
     latency_beta: tuple = (1.0, 0.0, 1.0)
     forced_drafts: dict = field(default_factory=dict)
+    temperature: float = 0.0
+    seed: int = 0
+
+    @property
+    def sampling(self):
+        """(T, seed) for speculative sampling, None for greedy decoding."""
+        return (self.temperature, self.seed) if self.temperature > 0 else None
 
 
 def _mask_from_set(L, s):
@@ -300,8 +342,9 @@ def _mask_from_set(L, s):
     return m
 
 
-def speculative_generate(model, prompt, G, policy, max_seq=None, log=None):
-    """Self-speculative greedy decoding of G tokens (t0 included).
+def speculative_generate(model, prompt, G, policy, max_seq=None, log=None, state_out=None):
+    """Self-speculative decoding of G tokens (t0 included): greedy, or
+    speculative sampling when ``policy.temperature`` > 0.
 
     Returns (tokens, per-round records).  The DP (if any) runs once after the
     prefill and again after every ``interval``-th verify round.
@@ -310,7 +353,10 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None):
     from .dytc import A_INIT, plan_cascade, update_cascade, predict_latency
     L = model.L
     max_seq = max_seq or len(prompt) + G + WINDOW_MAX + 1
-    st, _, _ = prefill(model, prompt, max_seq)
+    sam = policy.sampling
+    st, _, _ = prefill(model, prompt, max_seq, sampling=sam)
+    if state_out is not None:
+        state_out.append(st)
     out = [st.t0]
     records = []
 
@@ -342,7 +388,7 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None):
                 steps.append((lev, masks[lev], kk))
             drafted_levels = []
             for lev, mk, kk in steps:
-                toks, _ = draft(model, st, mk, policy.cascade[lev][2], kk, 0.0)
+                toks, _ = draft(model, st, mk, policy.cascade[lev][2], kk, 0.0, sam)
                 drafted_levels += [lev] * len(toks)
         else:
             kk = min(policy.K, budget)
@@ -350,10 +396,10 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None):
                 d = list(policy.forced_drafts[rounds])[:kk]
                 st.window = d
             else:
-                draft(model, st, masks[0], policy.quant, kk, policy.tau)
+                draft(model, st, masks[0], policy.quant, kk, policy.tau, sam)
             drafted_levels = None
         logits, states, d = verify(model, st)
-        n, bonus, emitted = accept(st, logits, states, d)
+        n, bonus, emitted = accept(st, logits, states, d, sam)
         out += emitted
         rounds += 1
         rec = {"k": len(d), "n": n, "bonus": bonus}
