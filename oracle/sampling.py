@@ -23,7 +23,8 @@ What it follows:
     engine draws the same numbers:
         key     = (seed, purpose)
         counter = (j, position, 0, 0)     block j gives entries 4j .. 4j+3
-        u       = ((x >> 40) + 1/2) / 2**24      24-bit uniform in (0, 1)
+        u       = ((x >> 41) + 1/2) / 2**23      23-bit uniform in (0, 1), exact
+                                                 in float32 as well
     Purposes: DRAFT (the draft's sample at a draft row), TARGET (the full
     model's sample: prefill token, sampled AR step, bonus token), ACCEPT
     (the uniform of the acceptance test of the draft a row checks), RESIDUAL
@@ -111,12 +112,12 @@ def uniforms(seed, purpose, pos, n):
     nb = (n + 3) // 4
     if nb <= 4:                      # short streams: plain integers
         words = [w for j in range(nb) for w in philox4x64_int((j, pos, 0, 0), (seed, purpose))][:n]
-        return (np.array([w >> 40 for w in words], np.float64) + 0.5) / float(1 << 24)
+        return (np.array([w >> 41 for w in words], np.float64) + 0.5) / float(1 << 23)
     ctr = np.zeros((nb, 4), np.uint64)
     ctr[:, 0] = np.arange(nb, dtype=np.uint64)
     ctr[:, 1] = np.uint64(pos)
     x = philox4x64(ctr, (np.uint64(seed), np.uint64(purpose))).reshape(-1)[:n]
-    return ((x >> np.uint64(40)).astype(np.float64) + 0.5) / float(1 << 24)
+    return ((x >> np.uint64(41)).astype(np.float64) + 0.5) / float(1 << 23)
 
 
 def gumbel(seed, purpose, pos, n):

@@ -38,9 +38,10 @@ def test_philox_matches_numpy_bit_generator(key, ctr):
     assert smp.philox4x64_int(nxt, key) == [int(x) for x in ref]
 
 
-def test_uniforms_are_24_bit_and_open():
+def test_uniforms_are_23_bit_and_open():
     u = smp.uniforms(11, smp.TARGET, 5, 4000)
-    codes = u * 2**24 - 0.5
+    codes = u * 2**23 - 0.5
+    assert np.all(u.astype(np.float32).astype(np.float64) == u)   # exact in float32
     assert np.all(codes == np.round(codes))
     assert np.all((u > 0) & (u < 1))
     # streams differ by purpose and by position
