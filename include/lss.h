@@ -90,9 +90,33 @@ void lss_destroy(lss_engine* e);
 const char* lss_last_error(const lss_engine* e);
 
 /* Full-model causal pass over the prompt (row blocks of max_rows).  Resets
- * the sequence.  *t0_out = greedy next token, which becomes the pending
- * token; the last prompt row becomes the layer-selection target. */
+ * the sequence.  *t0_out = greedy next token (with sampling on: the full
+ * model's draw at the last prompt row), which becomes the pending token; the
+ * last prompt row becomes the layer-selection target. */
 int lss_prefill(lss_engine* e, const int32_t* tokens, int32_t n, int32_t* t0_out);
+
+/* Speculative sampling (the pages call the scheme lossless: it keeps the
+ * full model's output distribution -- CAS-Spec abstract; CLaSp section 3,
+ * verification predicts a distribution per draft token; CLaSp section 4).
+ * temperature > 0 turns it on for the following calls, 0 returns to greedy
+ * decoding.  Every random draw is a pure function of (seed, purpose,
+ * position, index): Philox-4x64-10 with key (seed, purpose) and counter
+ * (index / 4, position, 0, 0), word index % 4, uniform
+ * ((x >> 41) + 1/2) / 2^23, Gumbel noise -log(-log u); purposes 1 draft
+ * draw, 2 full-model draw, 3 acceptance uniform, 4 replacement draw; the
+ * position is that of the row whose distribution is drawn from or tested.
+ *   - draws: argmax of z / T + Gumbel noise (a draw from softmax(z / T));
+ *   - draft i is accepted iff r q(d) < p(d) (p, q at temperature T; r the
+ *     acceptance uniform of verify row i's position);
+ *   - the first rejection draws the replacement from max(0, p - q)
+ *     (Gumbel-max over log of it; from p if rounding leaves it empty);
+ *     with every draft accepted the bonus is the draw of verify row k;
+ *   - the draft exit threshold compares the top-1 probability at T.
+ * LSS_EINVAL for a negative or non-finite temperature; LSS_ESTATE while a
+ * draft window or verify is pending.  Host-forced drafts (lss_verify with
+ * drafts != NULL and k > 0) are rejected with LSS_EINVAL in this mode: they
+ * carry no draft distribution. */
+int lss_set_sampling(lss_engine* e, float temperature, uint64_t seed);
 
 /* Draft up to k tokens with the layers where skip_mask[l] != 0 skipped
  * (CLaSp section 3, draft stage; an early exit is a mask whose tail is
@@ -115,7 +139,8 @@ int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k);
 
 /* Greedy acceptance and O(1) rollback: n = longest prefix of the drafts that
  * equals the full model's argmax tokens, bonus = the full model's token
- * after it.  The committed length becomes p + n + 1 (later KV rows are stale
+ * after it (with sampling on: n and the bonus come from the speculative-
+ * sampling rule of lss_set_sampling, decided on the device in verify).  The committed length becomes p + n + 1 (later KV rows are stale
  * and never read), the window is cleared, the bonus token is pending, and
  * verify row n becomes the layer-selection target.  accepted_out (may be
  * NULL) receives the n + 1 emitted tokens d1..dn, bonus. */

@@ -44,7 +44,7 @@ int pg_splits(int N, int K, int wbytes) {
 
 struct Layout {
   size_t kc, vc, hs, hmid, xa, xb, xc, pa, pc, xs, qkv, apart, aout, pgpart, rstd, act, logits, hpart, rope, target,
-      dpg0, dpg1, dpx, dpdec, tok, seqtok, res, total;
+      dpg0, dpg1, dpx, dpdec, tok, seqtok, res, dlogits, srec, total;
   int xld, nch_max, nz_max, ntile;
 };
 
@@ -108,7 +108,7 @@ Layout make_layout(const lss_config* c) {
   L.rstd = take(R * 4);
   L.act = take(R * F * 4);
   L.logits = take(R * V * 4);
-  L.hpart = take(R * (size_t)L.ntile * 3 * 4);
+  L.hpart = take(R * (size_t)L.ntile * HEAD_PART * 4);
   L.rope = take((size_t)c->max_seq * (hd / 2) * 8);
   L.target = take((NL + 1) * d * 4);
   L.dpg0 = take(R * d * 4);
@@ -118,6 +118,8 @@ Layout make_layout(const lss_config* c) {
   L.tok = take(64 * 4);
   L.seqtok = take((size_t)c->max_seq * 4);
   L.res = take(sizeof(HeadRes));
+  L.dlogits = take((size_t)std::min<size_t>(kWinMax, R) * V * 4);       // sampling: draft logits per window slot
+  L.srec = take((size_t)((V + SPEC_RES_PER_WG - 1) / SPEC_RES_PER_WG) * 4 * 4);
   L.total = off;
   return L;
 }
@@ -148,6 +150,7 @@ struct lss_engine {
   void *kc = nullptr, *vc = nullptr;
   float *hs, *hmid, *xs, *qkv, *apart, *aout, *act, *logits, *hpart, *target, *dpg[2], *dpx, *dpdec;
   float *pgpart, *rstd;
+  float *dlogits = nullptr, *srec = nullptr;  // sampling: draft logits of the window slots, replacement-draw records
   void *xa, *xb, *xc;   // projection inputs: layer input (attention-norm gain), attention / FFN output, mid-layer
   float *pa, *pc;       // partial sums of squares of the residual rows behind xa and xc
   float2* rope;
@@ -166,6 +169,9 @@ struct lss_engine {
   int logits_rows = 0;
   bool have_target = false;
   int target_pos = 0;
+  // speculative sampling (lss_set_sampling): 1 / temperature (0: greedy) and seed
+  float inv_t = 0.f;
+  uint64_t seed = 0;
   // projections of draft / verify rows go through the vector-ALU GEMV
   // (one arithmetic for every row count); prefill and layer selection
   // through the MFMA kernels
@@ -237,7 +243,8 @@ GemmArgs rows_from(const GemmArgs& ga, int r0, int Mg) {
   if (ga.R) g.R = ga.R + (size_t)r0 * ga.ldr;
   if (ga.xo) g.xo = (char*)ga.xo + (size_t)r0 * ga.ldo * 4;
   if (ga.po) g.po = ga.po + (size_t)r0 * (ga.N / 16);
-  if (ga.part) g.part = ga.part + (size_t)r0 * (ga.N / 16) * 3;
+  if (ga.part) g.part = ga.part + (size_t)r0 * (ga.N / 16) * HEAD_PART;
+  g.pos0 = ga.pos0 + r0 * ga.pos_step;
   return g;
 }
 
@@ -498,18 +505,25 @@ void layer_forward(lss_engine* e, int l, int M, const float* h_in, const void* x
 }
 
 // Final norm + LM head on M rows whose projection input (final-norm gain)
-// and partial sums of squares start at row r0 of e->xa / e->pa; per-row
-// argmax and top-1 probability land in res->argmax/pmax[row0 + m].
-void head(lss_engine* e, int r0, int M, int row0) {
+// and partial sums of squares start at row r0 of e->xa / e->pa; row m sits
+// at position pos0 + m.  Per-row argmax and top-1 probability land in
+// res->argmax/pmax[row0 + m].  With sampling on, every row also draws a
+// token (the draft stream for a draft row, the full model's otherwise) into
+// res->sample[row0 + m] with its log-sum-exp; a draft row keeps its logits
+// in the window slot row0 of e->dlogits.
+void head(lss_engine* e, int r0, int M, int row0, int pos0, bool draft) {
   const auto& c = e->cfg;
-  GemmArgs ga = gemm_args(e->lm_head, c.vocab, c.d_model, xrow(e->xa, c.d_model, r0), c.d_model, M, e->logits,
-                          c.vocab);
+  const bool samp = e->inv_t > 0.f;
+  float* Y = (samp && draft) ? e->dlogits + (size_t)row0 * c.vocab : e->logits;
+  GemmArgs ga = gemm_args(e->lm_head, c.vocab, c.d_model, xrow(e->xa, c.d_model, r0), c.d_model, M, Y, c.vocab);
   ga.scale = SCALE_NORM; ga.pin = e->pa + (size_t)r0 * (c.d_model / 16); ga.eps = c.rms_eps;
   ga.part = e->hpart;
+  ga.inv_t = e->inv_t; ga.seed = e->seed; ga.purpose = draft ? RNG_DRAFT : RNG_TARGET;
+  ga.pos0 = pos0; ga.pos_step = 1;
   gemm<EPI_LOGITS>(e, ga);
   hipLaunchKernelGGL(k_head_reduce, dim3(M), dim3(HEAD_RED_THREADS), 0, e->stream, e->hpart, e->lay.ntile, e->res,
-                     row0);
-  e->logits_rows = M;
+                     row0, samp ? 1 : 0, draft ? 1 : 0);
+  if (!(samp && draft)) e->logits_rows = M;
 }
 
 // embedding rows of tokens tok_dev[0..M) into h, with the projection input
@@ -614,7 +628,19 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
   e->dpg[0] = (float*)(ws + lay.dpg0); e->dpg[1] = (float*)(ws + lay.dpg1); e->dpx = (float*)(ws + lay.dpx);
   e->dpdec = (float*)(ws + lay.dpdec); e->tok = (int32_t*)(ws + lay.tok); e->seqtok = (int32_t*)(ws + lay.seqtok);
   e->res = (HeadRes*)(ws + lay.res);
+  e->dlogits = (float*)(ws + lay.dlogits); e->srec = (float*)(ws + lay.srec);
   e->valid.assign(cfg->n_layers, 0u);
+  {  // every workspace pointer must be set (a null one would be written by a kernel)
+    const void* ptrs[] = {e->kc, e->vc, e->hs, e->hmid, e->xa, e->xb, e->xc, e->pa, e->pc, e->xs, e->qkv,
+                          e->pgpart, e->rstd, e->apart, e->aout, e->act, e->logits, e->hpart, e->rope,
+                          e->target, e->dpg[0], e->dpg[1], e->dpx, e->dpdec, e->tok, e->seqtok, e->res,
+                          e->dlogits, e->srec};
+    for (const void* q : ptrs)
+      if (!q) {
+        lss_destroy(e);
+        return LSS_EINVAL;
+      }
+  }
 
   hipError_t s = hipHostMalloc((void**)&e->hres, sizeof(HeadRes), hipHostMallocDefault);
   if (s == hipSuccess)
@@ -660,6 +686,18 @@ const char* lss_last_error(const lss_engine* e) { return e ? e->err.c_str() : "n
 
 int32_t lss_seq_len(const lss_engine* e) { return e ? e->p : -1; }
 
+int lss_set_sampling(lss_engine* e, float temperature, uint64_t seed) {
+  if (!e) return LSS_EINVAL;
+  if (!(temperature >= 0.f) || !std::isfinite(temperature))
+    return fail(e, LSS_EINVAL, "set_sampling: temperature must be finite and >= 0");
+  if (e->win > 0 || e->pending_accept) return fail(e, LSS_ESTATE, "set_sampling: a draft window or verify is pending");
+  const float inv = temperature > 0.f ? 1.0f / temperature : 0.f;
+  if (temperature > 0.f && !std::isfinite(inv)) return fail(e, LSS_EINVAL, "set_sampling: temperature too small");
+  e->inv_t = inv;
+  e->seed = seed;
+  return LSS_OK;
+}
+
 int lss_prefill(lss_engine* e, const int32_t* tokens, int32_t n, int32_t* t0_out) {
   if (!e) return LSS_EINVAL;
   const auto& c = e->cfg;
@@ -676,8 +714,9 @@ int lss_prefill(lss_engine* e, const int32_t* tokens, int32_t n, int32_t* t0_out
     forward_rows(e, e->seqtok + c0, M, c0);
     last_m = M - 1;
   }
-  head(e, last_m, 1, 0);
-  hipLaunchKernelGGL(k_accept, dim3(1), dim3(1), 0, e->stream, e->res, 0, e->tok);  // tok[0] = argmax
+  head(e, last_m, 1, 0, n - 1, false);
+  hipLaunchKernelGGL(k_accept, dim3(1), dim3(1), 0, e->stream, e->res, 0, e->tok,
+                     e->inv_t > 0.f ? 1 : 0);  // tok[0] = argmax, or the draw
   hipLaunchKernelGGL(k_gather_target, dim3(c.n_layers + 1), dim3(256), 0, e->stream, e->hs, R, c.d_model,
                      (const HeadRes*)nullptr, last_m, e->target);
   int rc = check_launch(e, "prefill");
@@ -691,7 +730,7 @@ int lss_prefill(lss_engine* e, const int32_t* tokens, int32_t n, int32_t* t0_out
   e->pending_accept = false;
   e->have_target = true;
   e->target_pos = n - 1;
-  if (t0_out) *t0_out = e->hres->argmax[0];
+  if (t0_out) *t0_out = e->hres->bonus;
   return LSS_OK;
 }
 
@@ -719,8 +758,8 @@ int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, floa
       layer_forward(e, l, 1, h, e->xa, e->pa, hs_row(e, l + 1, 0), next_gain(e, mask, l), MODE_DRAFT, pos, quant);
       h = hs_row(e, l + 1, 0);
     }
-    head(e, 0, 1, slot);
-    hipLaunchKernelGGL(k_draft_commit, dim3(1), dim3(1), 0, e->stream, e->res, slot, e->tok);
+    head(e, 0, 1, slot, pos, true);
+    hipLaunchKernelGGL(k_draft_commit, dim3(1), dim3(1), 0, e->stream, e->res, slot, e->tok, e->inv_t > 0.f ? 1 : 0);
     e->win++;
     done++;
     if (exit_tau > 0.f) {
@@ -736,7 +775,8 @@ int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, floa
   if (done > 0) {
     rc = sync_res(e);
     if (rc) return rc;
-    for (int i = 0; i < done; ++i) tokens_out[i] = e->hres->argmax[start + i];
+    const int32_t* drawn = e->inv_t > 0.f ? e->hres->sample : e->hres->argmax;
+    for (int i = 0; i < done; ++i) tokens_out[i] = drawn[start + i];
   }
   if (k_done) *k_done = done;
   return LSS_OK;
@@ -747,7 +787,9 @@ int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k) {
   const GemvScope gv(e);
   const auto& c = e->cfg;
   if (!e->have_seq || e->pending_accept) return fail(e, LSS_ESTATE, "verify: needs a prefilled sequence and no pending accept");
+  const bool samp = e->inv_t > 0.f;
   if (drafts) {
+    if (samp && k > 0) return fail(e, LSS_EINVAL, "verify: host-forced drafts need greedy mode (no draft distribution)");
     if (k < 0 || k > std::min(kWinMax, c.max_rows - 1)) return fail(e, LSS_ECAPACITY, "verify: k exceeds the window capacity");
     for (int i = 0; i < k; ++i)
       if (drafts[i] < 0 || drafts[i] >= c.vocab) return fail(e, LSS_EINVAL, "verify: token id out of range");
@@ -761,8 +803,18 @@ int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k) {
   }
   const int M = k + 1;
   forward_rows(e, e->tok, M, e->p);
-  head(e, 0, M, 0);
-  hipLaunchKernelGGL(k_accept, dim3(1), dim3(1), 0, e->stream, e->res, k, e->tok);
+  head(e, 0, M, 0, e->p, false);
+  if (samp && k > 0) {
+    const int nrec = (c.vocab + SPEC_RES_PER_WG - 1) / SPEC_RES_PER_WG;
+    hipLaunchKernelGGL(k_spec_residual, dim3(nrec), dim3(SPEC_RES_THREADS), 0, e->stream, (const float*)e->logits,
+                       (const float*)e->dlogits, c.vocab, (const HeadRes*)e->res, (const int32_t*)e->tok, k, e->inv_t,
+                       e->seed, e->p, e->srec);
+    hipLaunchKernelGGL(k_spec_final, dim3(1), dim3(SPEC_FIN_THREADS), 0, e->stream, (const float*)e->logits,
+                       (const float*)e->dlogits, c.vocab, e->res, e->tok, k, e->inv_t, e->seed, e->p,
+                       (const float*)e->srec, nrec);
+  } else {
+    hipLaunchKernelGGL(k_accept, dim3(1), dim3(1), 0, e->stream, e->res, k, e->tok, samp ? 1 : 0);
+  }
   hipLaunchKernelGGL(k_gather_target, dim3(c.n_layers + 1), dim3(256), 0, e->stream, e->hs, c.max_rows,
                      c.d_model, (const HeadRes*)e->res, 0, e->target);
   const int rc = check_launch(e, "verify");
@@ -782,7 +834,7 @@ int lss_accept_and_rollback(lss_engine* e, int32_t* n_accepted, int32_t* bonus, 
   if (n_accepted) *n_accepted = n;
   if (bonus) *bonus = e->hres->bonus;
   if (accepted_out)
-    for (int i = 0; i <= n; ++i) accepted_out[i] = e->hres->argmax[i];
+    for (int i = 0; i <= n; ++i) accepted_out[i] = e->hres->emit[i];
   e->target_pos = e->p + n;
   e->have_target = true;
   e->p += n + 1;

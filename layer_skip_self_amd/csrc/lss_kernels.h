@@ -278,6 +278,46 @@ __global__ __launch_bounds__(256) void k_quant_rows(const float* __restrict__ x,
   if (threadIdx.x == 0) xs[m] = __fdiv_rn(amax, 127.0f);
 }
 
+// ---------------------------------------------------------------- sampling noise
+// Counter-based random numbers of speculative sampling: Philox-4x64 with 10
+// rounds (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
+// 1, 2, 3", SC 2011).  Entry v of the stream (seed, purpose, position) is
+// word v % 4 of Philox(counter (v / 4, position, 0, 0), key (seed, purpose)).
+// Its uniform is ((x >> 41) + 1/2) / 2^23 (exact in float32) and its Gumbel
+// noise -log(-log u).  Purposes: the draft's draw at a draft row, the full
+// model's draw at a row (prefill token, sampled step, bonus token), the
+// acceptance uniform of the draft a verify row checks, and the replacement
+// draw after a rejection.
+enum { RNG_DRAFT = 1, RNG_TARGET = 2, RNG_ACCEPT = 3, RNG_RESIDUAL = 4 };
+
+struct U64x4 { uint64_t v[4]; };
+
+__device__ __forceinline__ U64x4 philox4x64(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
+                                            uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) { k0 += W0; k1 += W1; }
+    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+  }
+  return {{c0, c1, c2, c3}};
+}
+
+__device__ __forceinline__ float rng_uniform(uint64_t x) {
+  return __fmul_rn(__fadd_rn((float)(uint32_t)(x >> 41), 0.5f), 0x1p-23f);
+}
+__device__ __forceinline__ float rng_gumbel(uint64_t x) { return -logf(-logf(rng_uniform(x))); }
+// the generator word of entry v of a stream
+__device__ __forceinline__ uint64_t rng_word(uint64_t seed, int purpose, int pos, int v) {
+  const U64x4 r = philox4x64((uint64_t)(v >> 2), (uint64_t)pos, 0ull, 0ull, seed, (uint64_t)purpose);
+  const int w = v & 3;
+  return w == 0 ? r.v[0] : w == 1 ? r.v[1] : w == 2 ? r.v[2] : r.v[3];
+}
+
 // ---------------------------------------------------------------- projections: shared definitions
 // Projection arguments, the MFMA operand layout of the weights, and the
 // output epilogue shared by the prefill GEMM and the decode GEMV.
@@ -310,8 +350,14 @@ struct GemmArgs {
   void* xo; int ldo;     // projection-format output of the result (RESID: times go)
   const float* go;       // RESID: gain of the next RMSNorm (nullptr: 1)
   float* po;             // RESID: partial sums of squares of Y [M][N/16]
-  float* part;           // LOGITS: per (row, tile) {max, argmax bits, sum exp}
+  float* part;           // LOGITS: per (row, tile) HEAD_PART floats (below)
+  float inv_t;           // LOGITS: 1 / temperature; 0: greedy (no draws)
+  uint64_t seed; int purpose; int pos0, pos_step;   // LOGITS draws: stream of row m is position pos0 + m pos_step
 };
+
+// LOGITS tile record: max of z / T, its lowest index, sum of exp(z / T - max),
+// and (sampling) the max of z / T + Gumbel noise with its lowest index
+#define HEAD_PART 5
 
 template <typename WT> struct WTr;
 template <> struct WTr<uint16_t> { static constexpr int EPL = 8, ANV = 2; };  // bf16: hi + lo vectors
@@ -352,18 +398,28 @@ __device__ __forceinline__ void proj_out(const GemmArgs& ga, int m, int M, int n
       if (ga.xo) AF<WT>::store(ga.xo, (size_t)m * ga.ldo, n, o);
       else ga.Y[(size_t)m * ga.ldy + n] = o;
     }
-  } else {  // EPI_LOGITS: store, then the tile's max / lowest argmax / sum of exp(z - max)
+  } else {  // EPI_LOGITS: store, then the tile record (HEAD_PART) of z / T
     if (ok) ga.Y[(size_t)m * ga.ldy + n] = y;
-    float mx = (n < ga.N) ? y : -INFINITY;
+    const bool samp = ga.inv_t > 0.f;                  // uniform
+    const float zt = samp ? __fmul_rn(y, ga.inv_t) : y;
+    float mx = (n < ga.N) ? zt : -INFINITY;
     int idx = n;
     argmax16(mx, idx);
-    float e = (n < ga.N) ? expf(__fsub_rn(y, mx)) : 0.f;
+    float e = (n < ga.N) ? expf(__fsub_rn(zt, mx)) : 0.f;
     e = sum16(e);
+    float gk = -INFINITY;
+    int gi = n;
+    if (samp) {
+      if (n < ga.N) gk = __fadd_rn(zt, rng_gumbel(rng_word(ga.seed, ga.purpose, ga.pos0 + m * ga.pos_step, n)));
+      argmax16(gk, gi);
+    }
     if (cl == 0 && m < M) {
-      float* p = ga.part + ((size_t)m * gridDim.x + blockIdx.x) * 3;
+      float* p = ga.part + ((size_t)m * gridDim.x + blockIdx.x) * HEAD_PART;
       p[0] = mx;
       p[1] = __int_as_float(idx);
       p[2] = e;
+      p[3] = gk;
+      p[4] = __int_as_float(gi);
     }
   }
 }
@@ -1061,55 +1117,199 @@ __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
 struct HeadRes {                 // device result block, mirrored to the host
   int32_t n, bonus, argmax[64];
   float pmax[64];
+  int32_t sample[64];            // sampling: draw of each row (draft slot or verify row)
+  float lse[64];                 // sampling: log-sum-exp of z / T of each verify row
+  float dlse[64];                // sampling: the same for each draft slot
+  int32_t emit[64];              // tokens a verify round emits: accepted drafts, then the bonus
 };
 
-// Per row: argmax over the tile partials (lowest index on ties) and the
-// top-1 softmax probability 1 / sum_j exp(z_j - z_max).
+// Per row: argmax over the tile records (lowest index on ties) and the
+// top-1 softmax probability 1 / sum_j exp(z_j / T - max).  With draws
+// (samp): the row's Gumbel-max draw and its log-sum-exp, the latter in
+// dlse (draft slots) or lse (verify rows).
 #define HEAD_RED_THREADS 1024
 __global__ __launch_bounds__(HEAD_RED_THREADS) void k_head_reduce(const float* __restrict__ part, int ntile,
-                                                                  HeadRes* __restrict__ res, int row0) {
+                                                                  HeadRes* __restrict__ res, int row0, int samp,
+                                                                  int draft) {
   __shared__ float redf[HEAD_RED_THREADS / 64];
-  __shared__ float bm[HEAD_RED_THREADS / 64];
-  __shared__ int bi[HEAD_RED_THREADS / 64];
+  __shared__ float bm[HEAD_RED_THREADS / 64], gm[HEAD_RED_THREADS / 64];
+  __shared__ int bi[HEAD_RED_THREADS / 64], gx[HEAD_RED_THREADS / 64];
   const int m = blockIdx.x;
-  const float* p = part + (size_t)m * ntile * 3;
-  float mx = -INFINITY;
-  int idx = 0x7fffffff;
+  const float* p = part + (size_t)m * ntile * HEAD_PART;
+  float mx = -INFINITY, gmx = -INFINITY;
+  int idx = 0x7fffffff, gidx = 0x7fffffff;
   for (int w = threadIdx.x; w < ntile; w += blockDim.x) {
-    const float v = p[w * 3];
-    const int i = __float_as_int(p[w * 3 + 1]);
-    argmax_merge(mx, idx, v, i);
+    argmax_merge(mx, idx, p[w * HEAD_PART], __float_as_int(p[w * HEAD_PART + 1]));
+    if (samp) argmax_merge(gmx, gidx, p[w * HEAD_PART + 3], __float_as_int(p[w * HEAD_PART + 4]));
   }
   argmax_wave(mx, idx);
+  if (samp) argmax_wave(gmx, gidx);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  if (lane == 0) { bm[wv] = mx; bi[wv] = idx; }
+  if (lane == 0) { bm[wv] = mx; bi[wv] = idx; gm[wv] = gmx; gx[wv] = gidx; }
   __syncthreads();
-  mx = bm[0]; idx = bi[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i)
+  mx = bm[0]; idx = bi[0]; gmx = gm[0]; gidx = gx[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) {
     argmax_merge(mx, idx, bm[i], bi[i]);
+    argmax_merge(gmx, gidx, gm[i], gx[i]);
+  }
   float s = 0.f;
   for (int w = threadIdx.x; w < ntile; w += blockDim.x)
-    s = __fadd_rn(s, __fmul_rn(p[w * 3 + 2], expf(__fsub_rn(p[w * 3], mx))));
+    s = __fadd_rn(s, __fmul_rn(p[w * HEAD_PART + 2], expf(__fsub_rn(p[w * HEAD_PART], mx))));
   s = block_sum(s, redf);
   if (threadIdx.x == 0) {
+    // NaN logits win no comparison: keep the indices inside the vocabulary
+    const int V = ntile * 16;
+    if (idx < 0 || idx >= V) idx = 0;
+    if (gidx < 0 || gidx >= V) gidx = 0;
     res->argmax[row0 + m] = idx;
     res->pmax[row0 + m] = __fdiv_rn(1.0f, s);
+    if (samp) {
+      res->sample[row0 + m] = gidx;
+      (draft ? res->dlse : res->lse)[row0 + m] = __fadd_rn(mx, logf(s));
+    }
   }
 }
 
-// Draft step bookkeeping: the drafted token becomes the next window input.
-__global__ void k_draft_commit(HeadRes* res, int slot, int32_t* tok) {
-  tok[slot + 1] = res->argmax[slot];
+// Draft step bookkeeping: the drafted token (argmax, or the draw) becomes
+// the next window input.
+__global__ void k_draft_commit(HeadRes* res, int slot, int32_t* tok, int samp) {
+  tok[slot + 1] = samp ? res->sample[slot] : res->argmax[slot];
 }
 
 // Greedy acceptance: n = first i with argmax_i != draft_{i+1}; bonus =
-// argmax_n; the bonus becomes the pending token tok[0].
-__global__ void k_accept(HeadRes* res, int k, int32_t* tok) {
+// argmax_n (with k = 0 and draws: the draw of row 0); the bonus becomes the
+// pending token tok[0].
+__global__ void k_accept(HeadRes* res, int k, int32_t* tok, int samp) {
   int n = 0;
   while (n < k && res->argmax[n] == tok[n + 1]) ++n;
+  const int b = samp ? res->sample[n] : res->argmax[n];
   res->n = n;
-  res->bonus = res->argmax[n];
-  tok[0] = res->argmax[n];
+  res->bonus = b;
+  for (int i = 0; i < n; ++i) res->emit[i] = tok[i + 1];
+  res->emit[n] = b;
+  tok[0] = b;
+}
+
+// Speculative-sampling acceptance (the rule that keeps the full model's
+// distribution): draft i (token tok[i+1], drawn from draft logits row i at
+// position pos0 + i) is accepted iff r_i q_i(d) < p_i(d), with p_i the
+// softmax of verify row i at temperature T, q_i that of the draft row and
+// r_i the acceptance uniform of position pos0 + i.  Lane i of every wave
+// takes test i; the first rejection is the lowest rejecting lane (k if none).
+__device__ __forceinline__ int spec_first_reject(const float* __restrict__ zp, const float* __restrict__ zq, int V,
+                                                 const HeadRes* res, const int32_t* tok, int k, float inv_t,
+                                                 uint64_t seed, int pos0) {
+  const int i = threadIdx.x & 63;
+  bool rej = false;
+  if (i < k) {
+    const int d = min(max(tok[i + 1], 0), V - 1);
+    const float p = expf(__fsub_rn(__fmul_rn(zp[(size_t)i * V + d], inv_t), res->lse[i]));
+    const float q = expf(__fsub_rn(__fmul_rn(zq[(size_t)i * V + d], inv_t), res->dlse[i]));
+    const float r = rng_uniform(rng_word(seed, RNG_ACCEPT, pos0 + i, 0));
+    rej = !(__fmul_rn(r, q) < p);
+  }
+  const unsigned long long mask = __ballot(rej);
+  return mask ? __ffsll((long long)mask) - 1 : k;
+}
+
+// Replacement draw after the first rejection i: Gumbel-max over
+// log max(0, p_i - q_i) with the replacement stream of position pos0 + i,
+// and the same noise on z_i / T (used only if rounding leaves no positive
+// entry).  Workgroup b covers entries [b SPEC_RES_PER_WG, ...), four
+// consecutive entries (one generator block) per thread, and writes
+// {max, index, fallback max, fallback index}.  Nothing runs when every
+// draft is accepted.
+#define SPEC_RES_THREADS 256
+#define SPEC_RES_PER_WG (4 * SPEC_RES_THREADS)
+__global__ __launch_bounds__(SPEC_RES_THREADS) void k_spec_residual(const float* __restrict__ zp,
+                                                                    const float* __restrict__ zq, int V,
+                                                                    const HeadRes* __restrict__ res,
+                                                                    const int32_t* __restrict__ tok, int k,
+                                                                    float inv_t, uint64_t seed, int pos0,
+                                                                    float* __restrict__ out) {
+  __shared__ float sm[SPEC_RES_THREADS / 64][2];
+  __shared__ int si[SPEC_RES_THREADS / 64][2];
+  const int i = spec_first_reject(zp, zq, V, res, tok, k, inv_t, seed, pos0);
+  if (i >= k) return;                                  // uniform over the workgroup
+  const float* rp = zp + (size_t)i * V;
+  const float* rq = zq + (size_t)i * V;
+  const float lsp = res->lse[i], lsq = res->dlse[i];
+  float km = -INFINITY, fm = -INFINITY;
+  int ki = 0x7fffffff, fi = 0x7fffffff;
+  const int v0 = blockIdx.x * SPEC_RES_PER_WG + threadIdx.x * 4;
+  if (v0 < V) {
+    const U64x4 r = philox4x64((uint64_t)(v0 >> 2), (uint64_t)(pos0 + i), 0ull, 0ull, seed, RNG_RESIDUAL);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int v = v0 + w;
+      if (v < V) {
+        const float zpt = __fmul_rn(rp[v], inv_t);
+        const float g = rng_gumbel(r.v[w]);
+        const float pw = expf(__fsub_rn(zpt, lsp));
+        const float qw = expf(__fsub_rn(__fmul_rn(rq[v], inv_t), lsq));
+        const float wv = __fsub_rn(pw, qw);
+        argmax_merge(km, ki, wv > 0.f ? __fadd_rn(logf(wv), g) : -INFINITY, v);
+        argmax_merge(fm, fi, __fadd_rn(zpt, g), v);
+      }
+    }
+  }
+  argmax_wave(km, ki);
+  argmax_wave(fm, fi);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) { sm[wv][0] = km; si[wv][0] = ki; sm[wv][1] = fm; si[wv][1] = fi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < SPEC_RES_THREADS / 64; ++w) {
+      argmax_merge(km, ki, sm[w][0], si[w][0]);
+      argmax_merge(fm, fi, sm[w][1], si[w][1]);
+    }
+    float* o = out + (size_t)blockIdx.x * 4;
+    o[0] = km; o[1] = __int_as_float(ki); o[2] = fm; o[3] = __int_as_float(fi);
+  }
+}
+
+// Round result of speculative sampling: n = first rejection; the bonus is
+// the replacement draw (merged over the workgroup records in workgroup
+// order) or, with every draft accepted, the draw of verify row k.
+#define SPEC_FIN_THREADS 256
+__global__ __launch_bounds__(SPEC_FIN_THREADS) void k_spec_final(const float* __restrict__ zp,
+                                                                 const float* __restrict__ zq, int V,
+                                                                 HeadRes* __restrict__ res, int32_t* tok, int k,
+                                                                 float inv_t, uint64_t seed, int pos0,
+                                                                 const float* __restrict__ rec, int nrec) {
+  __shared__ float sm[SPEC_FIN_THREADS / 64][2];
+  __shared__ int si[SPEC_FIN_THREADS / 64][2];
+  const int i = spec_first_reject(zp, zq, V, res, tok, k, inv_t, seed, pos0);
+  int b;
+  if (i >= k) {
+    b = res->sample[k];
+  } else {
+    float km = -INFINITY, fm = -INFINITY;
+    int ki = 0x7fffffff, fi = 0x7fffffff;
+    for (int w = threadIdx.x; w < nrec; w += blockDim.x) {
+      argmax_merge(km, ki, rec[w * 4], __float_as_int(rec[w * 4 + 1]));
+      argmax_merge(fm, fi, rec[w * 4 + 2], __float_as_int(rec[w * 4 + 3]));
+    }
+    argmax_wave(km, ki);
+    argmax_wave(fm, fi);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (lane == 0) { sm[wv][0] = km; si[wv][0] = ki; sm[wv][1] = fm; si[wv][1] = fi; }
+    __syncthreads();
+    km = sm[0][0]; ki = si[0][0]; fm = sm[0][1]; fi = si[0][1];
+    for (int w = 1; w < SPEC_FIN_THREADS / 64; ++w) {
+      argmax_merge(km, ki, sm[w][0], si[w][0]);
+      argmax_merge(fm, fi, sm[w][1], si[w][1]);
+    }
+    b = km > -INFINITY ? ki : fi;
+    if (b < 0 || b >= V) b = 0;                        // NaN logits win no comparison
+  }
+  if (threadIdx.x == 0) {
+    res->n = i;
+    res->bonus = b;
+    for (int j = 0; j < i; ++j) res->emit[j] = tok[j + 1];
+    res->emit[i] = b;
+    tok[0] = b;
+  }
 }
 
 // Copy the residual states of verify row res->n (or `row` if res == nullptr)

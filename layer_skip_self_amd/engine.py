@@ -86,6 +86,10 @@ class Engine:
         return int(self.lib.lss_seq_len(self.h))
 
     # -------------------------------------------------------------- hot path
+    def set_sampling(self, temperature, seed=0):
+        """Speculative sampling at ``temperature`` with ``seed`` (0: greedy)."""
+        self._check(self.lib.lss_set_sampling(self.h, float(temperature), int(seed) % 2**64), "lss_set_sampling")
+
     def prefill(self, tokens):
         a, p = _i32(tokens)
         t0 = C.c_int32()
@@ -154,6 +158,9 @@ class Engine:
         return beta, samples, err
 
     def generate(self, prompt, n_gen, policy):
+        """Prefill + decoding of n_gen tokens under ``policy`` (``make_policy``;
+        its ``temperature`` / ``seed`` select greedy decoding or sampling)."""
+        self.set_sampling(policy.get("temperature", 0.0), policy.get("seed", 0))
         a, p = _i32(prompt)
         pol = make_policy(policy, self.shape.n_layers)
         out = np.zeros(n_gen, np.int32)
@@ -197,7 +204,8 @@ class Engine:
 
 def make_policy(policy, n_layers):
     """``policy``: dict with ``mode`` in {"ar", "static", "dp", "cascade"} and
-    the matching fields of ``lss_policy``."""
+    the matching fields of ``lss_policy`` (``temperature`` and ``seed`` are
+    applied by ``Engine.generate`` through ``lss_set_sampling``)."""
     pol = N.lss_policy()
     mode = policy.get("mode", "ar")
     pol.mode = {"ar": N.LSS_MODE_AR, "static": N.LSS_MODE_STATIC, "dp": N.LSS_MODE_DP,

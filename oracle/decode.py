@@ -290,11 +290,14 @@ def accept(st, logits, states, drafts, sampling=None):
     return n, bonus, emitted
 
 
-def ar_generate(model, prompt, G, max_seq=None, sampling=None):
+def ar_generate(model, prompt, G, max_seq=None, sampling=None, state_out=None):
     """Autoregressive decoding of G tokens (t0 included): greedy, or with
-    ``sampling`` = (T, seed) the TARGET draw of every row's position."""
+    ``sampling`` = (T, seed) the TARGET draw of every row's position.
+    ``state_out`` (a list) receives the decode state (its ``margins``)."""
     max_seq = max_seq or len(prompt) + G + 1
     st, z, _ = prefill(model, prompt, max_seq, sampling=sampling)
+    if state_out is not None:
+        state_out.append(st)
     out = [st.t0]
     while len(out) < G:
         zz, s = forward_row(model, st, st.t0, st.p, "full")

@@ -144,3 +144,59 @@ def test_dp_finds_planted_identity_layers_8b():
     n, _, _ = eng.accept()
     assert n == len(d) == 8
     eng.close()
+
+
+def test_sampling_round_vs_oracle_8b(gpu8b, oracle8b):
+    """Speculative sampling at T = 1 through the step API: the prefill draw,
+    the drafts of a 16-layer-skip draft, the acceptance count and the
+    replacement / bonus token equal the oracle's.  Decisions are compared in
+    order up to the first one whose oracle margin (gap of the Gumbel-max
+    draw, or relative slack of the acceptance test) is below 0.1: the bf16
+    logits may differ by 2e-2, which moves a z / T gap by up to 4e-2 and a
+    probability ratio by up to about 8%."""
+    import copy
+    from oracle import sampling as smp
+    eng, model, prompt = gpu8b["eng"], oracle8b["model"], gpu8b["prompt"]
+    T, seed, thr = 1.0, 77, 0.1
+    mask = [l % 2 for l in range(SHAPE.n_layers)]
+    eng.set_sampling(T, seed)
+    try:
+        t0 = eng.prefill(prompt)
+        d = eng.draft(mask, False, 3)
+        eng.verify(k=len(d))
+        n, b, emitted = eng.accept()
+    finally:
+        eng.set_sampling(0.0)
+    st = copy.deepcopy(oracle8b["st"])
+    ot0, m0 = smp.sample(oracle8b["z"], T, seed, smp.TARGET, P - 1)
+    print(f"gpu t0 {t0} drafts {d} n {n} bonus {b}; oracle t0 {ot0} (margin {m0:.3g})")
+    if m0 < thr:
+        pytest.skip("prefill draw within the bf16 tolerance of a tie")
+    assert t0 == ot0
+    st.t0, st.margins = ot0, []
+    od, _ = oracle.draft(model, st, mask, False, 3, 0.0, (T, seed))
+    print(f"oracle drafts {od}, margins {[f'{x:.3g}' for x in st.margins]}")
+    for i in range(3):
+        if st.margins[i] < thr:
+            return                              # later drafts follow a legitimately different prefix
+        assert d[i] == od[i], i
+    logits, states, dd = oracle.verify(model, st)
+    on, ob, oe = oracle.accept(st, logits, states, dd, (T, seed))
+    acc_m = st.margins[3:]
+    print(f"oracle n {on} bonus {ob}; acceptance / draw margins {[f'{x:.3g}' for x in acc_m]}")
+    if min(acc_m) >= thr:
+        assert (n, b, emitted) == (on, ob, oe)
+
+
+def test_sampling_empty_mask_accepted_in_full_8b(gpu8b):
+    """q = p bit for bit (batch-invariant rows), so r q < p for every r < 1."""
+    eng = gpu8b["eng"]
+    eng.set_sampling(1.0, 9)
+    try:
+        eng.prefill(gpu8b["prompt"])
+        d = eng.draft([0] * SHAPE.n_layers, False, 8)
+        eng.verify(None, len(d))
+        n, _, _ = eng.accept()
+    finally:
+        eng.set_sampling(0.0)
+    assert n == len(d) == 8
