@@ -57,6 +57,14 @@ WORKLOADS = {
     # exit, 18 chosen by the DP), L2 skips 30% (DP) with int8 activations, L3
     # runs all layers with int8 activations.  DyTC routing with at most 8
     # drafts per round and a latency model fitted on this engine.
+    # Speculative sampling at temperature 1 (the acceptance rule that keeps
+    # the full model's distribution) with the headline draft policy; the AR
+    # leg samples at the same temperature and seed.
+    "llama3_8b_sampling": dict(shape="llama3_8b", prompt=1024, gen=512,
+                               policy={"mode": "dp", "k_max": 8, "n_skip": 16, "interval": 32, "exit_tau": 0.7,
+                                       "temperature": 1.0, "seed": 2025},
+                               desc="Llama-3-8B shape, prompt 1024, 512 generated, speculative sampling at "
+                                    "temperature 1, CLaSp DP skip 16 every 32 rounds, exit threshold 0.7, K <= 8"),
     "cascade_8b": dict(shape="llama3_8b", prompt=(128, 512, 2048), gen=256,
                        policy={"mode": "cascade", "k_max": 8, "interval": 32,
                                "levels": [(22, 4, False), (10, 0, True), (0, 0, True)]},
@@ -86,7 +94,8 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
                         interval=policy.get("interval", 32), tau=policy.get("exit_tau", 0.0),
                         quant=bool(policy.get("quant", False)),
                         cascade=list(policy["levels"]) if policy["mode"] == "cascade" else None,
-                        latency_beta=tuple(policy.get("beta", (1.0, 0.0, 1.0))))
+                        latency_beta=tuple(policy.get("beta", (1.0, 0.0, 1.0))),
+                        temperature=float(policy.get("temperature", 0.0)), seed=int(policy.get("seed", 0)))
     sample = np.asarray(prompt[:n_prompt])
     t0 = time.perf_counter()
     toks, recs = oracle.speculative_generate(model, sample, n_tokens, pol)
@@ -223,13 +232,17 @@ def main():
     k_ms, k_n, k_bytes = eng.profile_read()
     eng.profile_kernel("gate_up", enable=False)
 
+    # the AR leg decodes the same way (greedy, or sampling at the same
+    # temperature and seed)
+    ar_pol = {"mode": "ar", "temperature": policies[0].get("temperature", 0.0), "seed": policies[0].get("seed", 0)}
+    sampling = ar_pol["temperature"] > 0
     ar_t, ar_toks = [0.0] * len(prompts), [None] * len(prompts)
     if args.ar_steps > 0:
         for pr in prompts:
-            run({"mode": "ar"}, pr)
+            run(ar_pol, pr)
     for _ in range(args.ar_steps):
         for i, pr in enumerate(prompts):
-            ar_toks[i], _, dt = run({"mode": "ar"}, pr)
+            ar_toks[i], _, dt = run(ar_pol, pr)
             ar_t[i] += dt
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -269,7 +282,7 @@ def main():
         item = {"prompt": lens[i], "tokens_per_s": round(sp, 3),
                 "ar_tokens_per_s": round(ar, 3) if ar else None,
                 "speedup_vs_ar": round(sp / ar, 4) if ar else None,
-                "lossless": spec_toks[j] == ar_toks[i] if args.ar_steps > 0 else None,
+                "lossless": spec_toks[j] == ar_toks[i] if args.ar_steps > 0 and not sampling else None,
                 "mean_accepted": round(st["accepted"] / max(st["rounds"], 1), 4),
                 "drafted_per_round": round(st["drafted"] / max(st["rounds"], 1), 4),
                 "dp_runs": st["dp_runs"], "prefill_ms": round(1e3 * prefill_s[i], 3)}
@@ -295,7 +308,9 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "speedup_vs_ar": round(value / ar_value, 4) if ar_value else None,
         "ar_tokens_per_s": round(ar_value, 3) if ar_value else None,
-        "lossless": all(r["lossless"] for r in per_run) if args.ar_steps > 0 else None,
+        "lossless": all(r["lossless"] for r in per_run) if args.ar_steps > 0 and not sampling else None,
+        "decoding": (f"speculative sampling, temperature {ar_pol['temperature']}, seed {ar_pol['seed']}"
+                     if sampling else "greedy"),
         "mean_accepted": round(accepted / max(rounds, 1), 4),
         "tokens_per_round": round((emitted - n_r) / max(rounds, 1), 4),
         "drafted_per_round": round(drafted / max(rounds, 1), 4),
