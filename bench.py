@@ -92,7 +92,7 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
     pol = oracle.Policy(K=policy.get("k_max", 4), skip=tuple(policy.get("skip", ())),
                         dp_skip=policy.get("n_skip") if policy["mode"] == "dp" else None,
                         interval=policy.get("interval", 32), tau=policy.get("exit_tau", 0.0),
-                        quant=bool(policy.get("quant", False)),
+                        quant=int(policy.get("quant", 0)),
                         cascade=list(policy["levels"]) if policy["mode"] == "cascade" else None,
                         latency_beta=tuple(policy.get("beta", (1.0, 0.0, 1.0))),
                         temperature=float(policy.get("temperature", 0.0)), seed=int(policy.get("seed", 0)))

@@ -30,7 +30,8 @@ float32, the precision the GPU kernels take them in.
 
 Parity status per function is listed in each module header.
 """
-from .model import OracleModel, rms_norm, rope, silu, attend, quantize_row, argmax_first
+from .model import (OracleModel, rms_norm, rope, silu, attend, quantize_row, argmax_first, quantize_weight_rows,
+                    w8a8_accumulate, w8a8_project)
 from .decode import (DecodeState, layer_block, prefill, forward_row, ar_generate, draft, verify,
                      accept, speculative_generate, Policy)
 from .clasp import clasp_dp, brute_force_skip, forward_with_mask_at_target
@@ -40,6 +41,7 @@ from . import sampling
 
 __all__ = [
     "OracleModel", "rms_norm", "rope", "silu", "attend", "quantize_row", "argmax_first",
+    "quantize_weight_rows", "w8a8_accumulate", "w8a8_project",
     "DecodeState", "layer_block", "prefill", "forward_row", "ar_generate", "draft", "verify", "accept",
     "speculative_generate", "Policy", "clasp_dp", "brute_force_skip",
     "forward_with_mask_at_target", "ALPHA", "A_INIT", "ema_update", "fit_latency",

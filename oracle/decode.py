@@ -39,7 +39,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .model import rms_norm, rope, silu, attend, fake_quant, argmax_first
+from .model import rms_norm, rope, silu, attend, fake_quant, argmax_first, w8a8_project
 from . import sampling as smp
 
 WINDOW_MAX = 32
@@ -74,16 +74,30 @@ def layer_row(model, l, h, pos, st, mode, quant=False):
     mode "draft": writes its k, v at ``pos`` (a window slot) and sets the
                   layer's valid bit; attends to [0, p) plus valid window slots.
     mode "dp":    writes nothing; attends to [0, pos) plus its own k, v.
+
+    quant: 0 full precision; 1 (or True) int8 activations (codes times
+    scale) into the full-precision weights; 2 int8 activations and the
+    layer's int8 weight copy (``w8a8_project``).  The same four points are
+    quantized either way: the attention input (shared by q/k/v), the
+    attention output, the FFN input (shared by gate/up) and the SwiGLU output.
     """
     m = model
     lw = m.layer(l)
     dt = m.dt
-    x = rms_norm(h, lw["attn_norm"], m.eps)
-    if quant:
-        x = fake_quant(x, dt)
-    q = _project(lw["wq"], x).reshape(m.Hq, m.hd)
-    k = _project(lw["wk"], x).reshape(m.Hkv, m.hd)
-    v = _project(lw["wv"], x).reshape(m.Hkv, m.hd)
+    w8 = m.layer_w8(l) if quant == 2 else None
+
+    def proj(name, x):
+        if w8 is not None:
+            return w8a8_project(*w8[name], x).astype(dt)
+        return _project(lw[name], x)
+
+    def qz(x):
+        return fake_quant(x, dt) if quant == 1 else x
+
+    x = qz(rms_norm(h, lw["attn_norm"], m.eps))
+    q = proj("wq", x).reshape(m.Hq, m.hd)
+    k = proj("wk", x).reshape(m.Hkv, m.hd)
+    v = proj("wv", x).reshape(m.Hkv, m.hd)
     q = rope(q, pos, m.theta)
     k = rope(k, pos, m.theta)
     if mode == "full":
@@ -104,16 +118,10 @@ def layer_row(model, l, h, pos, st, mode, quant=False):
     group = m.Hq // m.Hkv
     o = np.concatenate([attend(q[hh], keys[:, hh // group], vals[:, hh // group])
                         for hh in range(m.Hq)])
-    if quant:
-        o = fake_quant(o, dt)
-    h = h + _project(lw["wo"], o)
-    x = rms_norm(h, lw["ffn_norm"], m.eps)
-    if quant:
-        x = fake_quant(x, dt)
-    a = silu(_project(lw["w_gate"], x)) * _project(lw["w_up"], x)
-    if quant:
-        a = fake_quant(a, dt)
-    return h + _project(lw["w_down"], a)
+    h = h + proj("wo", qz(o))
+    x = qz(rms_norm(h, lw["ffn_norm"], m.eps))
+    a = silu(proj("w_gate", x)) * proj("w_up", x)
+    return h + proj("w_down", qz(a))
 
 
 def forward_row(model, st, tok, pos, mode, skip=None, quant=False):
@@ -314,7 +322,9 @@ class Policy:
 
     skip: static skip set (layer indices); dp_skip: number of layers the
     CLaSp DP chooses (overrides ``skip``), re-run every ``interval`` verify
-    rounds; tau: draft exit threshold (0 = off); cascade: a list of levels
+    rounds; tau: draft exit threshold (0 = off); quant: 0 full precision, 1
+    int8 activations, 2 int8 activations and int8 weights (``layer_row``);
+    cascade: a list of levels
     ``[(n_skip_by_dp, exit_layers, quant)]`` ordered fast -> precise, routed
     by the DyTC heuristics with at most ``K`` drafts per round;
     temperature > 0: speculative sampling with that temperature and seed
@@ -325,7 +335,7 @@ class Policy:
     dp_skip: int = None
     interval: int = 32
     tau: float = 0.0
-    quant: bool = False
+    quant: int = 0
     cascade: list = None
     latency_beta: tuple = (1.0, 0.0, 1.0)
     forced_drafts: dict = field(default_factory=dict)

@@ -45,6 +45,7 @@ class OracleModel:
         if cache_layers is None:
             cache_layers = shape.total_params() * self.dt.itemsize < 2e9
         self._cache = {} if cache_layers else None
+        self._w8 = {} if cache_layers else None
 
     def _get(self, name):
         if self._cache is not None and name in self._cache:
@@ -57,6 +58,18 @@ class OracleModel:
     def layer(self, l):
         names = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
         return {n: self._get(f"layers.{l}.{n}") for n in names}
+
+    def layer_w8(self, l):
+        """int8 weight copies (codes, row scales) of layer l's projections,
+        from the exact float32 weights; cached."""
+        key = ("w8", l)
+        if self._w8 is not None and key in self._w8:
+            return self._w8[key]
+        names = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+        r = {n: quantize_weight_rows(np.asarray(self.w[f"layers.{l}.{n}"], np.float32)) for n in names}
+        if self._w8 is not None:
+            self._w8[key] = r
+        return r
 
     def embed_row(self, tok):
         if self._cache is not None:
@@ -122,6 +135,39 @@ def quantize_row(x):
     inv = np.float32(127.0) / amax
     q = np.clip(np.rint(x32 * inv), -127, 127).astype(np.int8)
     return q, np.float32(amax / np.float32(127.0))
+
+
+def quantize_weight_rows(W):
+    """Per-output-row int8 codes of a weight matrix [N][K] (the W8A8 draft's
+    weight copy): every row is quantized like an activation row
+    (``quantize_row``: float32 decisions, amax / 127 scale, half-even codes),
+    written for all rows at once.  Returns (int8 codes [N][K], float32
+    scales [N])."""
+    W32 = np.asarray(W, dtype=np.float32)
+    amax = np.max(np.abs(W32), axis=1).astype(np.float32) if W32.shape[1] else np.zeros(W32.shape[0], np.float32)
+    zero = amax == 0
+    inv = np.where(zero, np.float32(0), np.float32(127.0) / np.where(zero, np.float32(1), amax)).astype(np.float32)
+    Q = np.clip(np.rint(W32 * inv[:, None]), -127, 127).astype(np.int8)
+    S = np.where(zero, np.float32(0), amax / np.float32(127.0)).astype(np.float32)
+    return Q, S
+
+
+def w8a8_accumulate(Q, q):
+    """Exact integer dot products sum_k q[k] Q[n][k] (int64).  The products
+    and every partial sum are integers below 2**53, so a float64 matrix
+    product computes them exactly."""
+    return np.rint(np.asarray(Q, np.float64) @ np.asarray(q, np.float64)).astype(np.int64)
+
+
+def w8a8_project(Q, S, x):
+    """W8A8 projection of one activation row (the int8-weight draft; a
+    widening of [CAS blog] 2.1's 8-bit activations to 8-bit weights):
+    (q, s_x) = quantize_row(x); y[n] = fl32(fl32(acc_n) * fl32(S[n] * s_x))
+    with acc_n the exact integer dot product.  Returns float32 [N]."""
+    q, sx = quantize_row(x)
+    acc = w8a8_accumulate(Q, q)
+    c = (np.asarray(S, np.float32) * np.float32(sx)).astype(np.float32)
+    return (acc.astype(np.float32) * c).astype(np.float32)
 
 
 def fake_quant(x, dt):
