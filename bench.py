@@ -65,6 +65,14 @@ WORKLOADS = {
                                        "temperature": 1.0, "seed": 2025},
                                desc="Llama-3-8B shape, prompt 1024, 512 generated, speculative sampling at "
                                     "temperature 1, CLaSp DP skip 16 every 32 rounds, exit threshold 0.7, K <= 8"),
+    # The headline policy with a W8A8 draft: the executed layers' projections
+    # read an int8 copy of the weights (per-row scales) with int8
+    # activations, halving the bytes a draft token streams.
+    "llama3_8b_w8a8": dict(shape="llama3_8b", prompt=1024, gen=512,
+                           policy={"mode": "dp", "k_max": 8, "n_skip": 16, "interval": 32, "exit_tau": 0.7,
+                                   "quant": 2},
+                           desc="Llama-3-8B shape, prompt 1024, 512 generated, CLaSp DP skip 16 every 32 rounds, "
+                                "exit threshold 0.7, K <= 8, W8A8 draft (int8 weight copy + int8 activations)"),
     "cascade_8b": dict(shape="llama3_8b", prompt=(128, 512, 2048), gen=256,
                        policy={"mode": "cascade", "k_max": 8, "interval": 32,
                                "levels": [(22, 4, False), (10, 0, True), (0, 0, True)]},
@@ -190,6 +198,9 @@ def main():
     max_seq = max(lens) + G + 33
     eng = Engine(shape, weights, max_seq=max_seq, max_rows=64)
     policies = [dict(p) for p in (wl["policy"] if isinstance(wl["policy"], list) else [wl["policy"]])]
+    w8 = any(p.get("quant") == 2 or any(lv[2] == 2 for lv in p.get("levels", [])) for p in policies)
+    if w8:
+        eng.attach_w8()
     latency = None
     for policy in policies:
         if policy["mode"] != "cascade":
@@ -321,7 +332,9 @@ def main():
         "draft_gemv_gbps": round(achieved, 1) if achieved else None,
         "roofline": {
             "bound": "hbm",
-            "kernel": f"k_gemv<{shape.dtype},1,1,SWIGLU,8>: draft gate/up projection + SwiGLU, 1 row",
+            "kernel": (f"k_gemv8<{shape.dtype},SWIGLU>: draft gate/up projection on the int8 weight copy + "
+                       "SwiGLU, 1 row" if w8 else
+                       f"k_gemv<{shape.dtype},1,1,SWIGLU,8>: draft gate/up projection + SwiGLU, 1 row"),
             "achieved": round(achieved, 1) if achieved else None,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

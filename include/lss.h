@@ -120,8 +120,11 @@ int lss_set_sampling(lss_engine* e, float temperature, uint64_t seed);
 
 /* Draft up to k tokens with the layers where skip_mask[l] != 0 skipped
  * (CLaSp section 3, draft stage; an early exit is a mask whose tail is
- * skipped).  quant != 0 quantizes every projection input of an executed
- * layer to int8 per token (CAS-Spec blog section 2.1).  exit_tau > 0 stops
+ * skipped).  quant = 1 quantizes every projection input of an executed
+ * layer to int8 per token (CAS-Spec blog section 2.1); quant = 2 also
+ * replaces that layer's weights by their int8 copy (lss_attach_w8: the
+ * 8-bit strategy carried over to the weights, the bytes a batch-1 draft
+ * streams halved; LSS_ESTATE if no copy is attached).  exit_tau > 0 stops
  * after the first token whose top-1 softmax probability is below exit_tau
  * (CLaSp section 4, draft exit threshold).  Appends to the pending window
  * (several levels may draft into one window).  tokens_out[k] receives the
@@ -227,6 +230,37 @@ int lss_profile_read(lss_engine* e, double* total_ms, int64_t* launches, int64_t
  * Enqueued on hip_stream; no synchronization. */
 int lss_op_quantize_rows(const float* x_dev, int32_t rows, int32_t n, int8_t* q_dev,
                          float* scale_dev, void* hip_stream);
+
+/* int8 weight copy for the W8A8 draft (lss_draft quant = 2): the 8-bit
+ * dynamic quantization of CAS-Spec blog section 2.1 applied per output row
+ * to the weights of every layer's seven projections.  Each row gets the
+ * activation rule: codes clamp(rint(w * fl(127/amax)), -127, 127), scale
+ * amax/127 (float32 decisions).  lss_w8_bytes: bytes the copy needs (0 for
+ * an invalid config).  lss_attach_w8 quantizes the engine's weights into
+ * the caller-owned device buffer (256-byte aligned, at least lss_w8_bytes;
+ * it must outlive the engine), synchronously on the engine stream.
+ * LSS_EINVAL for a null or unaligned buffer, LSS_ECAPACITY if too small. */
+size_t lss_w8_bytes(const lss_config* cfg);
+int lss_attach_w8(lss_engine* e, void* buf_dev, size_t bytes);
+
+/* Stand-alone forms of the two W8A8 kernels, enqueued on hip_stream:
+ * lss_op_w8_quantize: codes q_dev[rows][k] and scale_dev[rows] of a weight
+ *   matrix w_dev[rows][k] of dtype LSS_F32 or LSS_BF16 (rule above);
+ * lss_op_w8a8_gemv: one activation row of codes xq_dev[k] with scale
+ *   xscale_dev[0] against wq_dev[n][k] with row scales wscale_dev[n]:
+ *   y_dev[n] = fl32(fl32(acc) * fl32(wscale[n] * xscale)), acc the exact
+ *   integer dot product;
+ * lss_op_w8a8_gemv_f32: the same with a float32 row x_dev[k], quantized in
+ *   the kernel by the per-token rule of lss_op_quantize_rows (the form the
+ *   W8A8 draft runs: every workgroup forms the codes itself).
+ * n and k multiples of 16, k <= 32768, wq_dev and xq_dev 16-byte aligned;
+ * LSS_EINVAL otherwise. */
+int lss_op_w8_quantize(const void* w_dev, int32_t dtype, int32_t rows, int32_t k, int8_t* q_dev,
+                       float* scale_dev, void* hip_stream);
+int lss_op_w8a8_gemv(const int8_t* wq_dev, const float* wscale_dev, int32_t n, int32_t k, const int8_t* xq_dev,
+                     const float* xscale_dev, float* y_dev, void* hip_stream);
+int lss_op_w8a8_gemv_f32(const int8_t* wq_dev, const float* wscale_dev, int32_t n, int32_t k, const float* x_dev,
+                         float* y_dev, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -69,6 +69,14 @@ SIGNATURES = {
                                    C.POINTER(C.c_int64)]),
     "lss_op_quantize_rows": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                        C.c_void_p]),
+    "lss_w8_bytes": (C.c_size_t, [C.POINTER(lss_config)]),
+    "lss_attach_w8": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t]),
+    "lss_op_w8_quantize": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                     C.c_void_p]),
+    "lss_op_w8a8_gemv": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_void_p]),
+    "lss_op_w8a8_gemv_f32": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                       C.c_void_p]),
 }
 
 _lib = None

@@ -11,6 +11,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -44,7 +45,7 @@ int pg_splits(int N, int K, int wbytes) {
 
 struct Layout {
   size_t kc, vc, hs, hmid, xa, xb, xc, pa, pc, xs, qkv, apart, aout, pgpart, rstd, act, logits, hpart, rope, target,
-      dpg0, dpg1, dpx, dpdec, tok, seqtok, res, dlogits, srec, total;
+      dpg0, dpg1, dpx, dpdec, tok, seqtok, res, dlogits, srec, q8, total;
   int xld, nch_max, nz_max, ntile;
 };
 
@@ -120,6 +121,7 @@ Layout make_layout(const lss_config* c) {
   L.res = take(sizeof(HeadRes));
   L.dlogits = take((size_t)std::min<size_t>(kWinMax, R) * V * 4);       // sampling: draft logits per window slot
   L.srec = take((size_t)((V + SPEC_RES_PER_WG - 1) / SPEC_RES_PER_WG) * 4 * 4);
+  L.q8 = take(R * (size_t)L.xld);                  // int8-weight draft: activation codes
   L.total = off;
   return L;
 }
@@ -130,6 +132,35 @@ struct LayerW {
   const float* ffn_norm;
   const void *wg, *wu, *wd;
 };
+
+// int8 copy of one layer's projections (codes [N][K], row scales [N]) in
+// the order q, k, v, o, gate, up, down
+struct LayerW8 {
+  const int8_t* q[7];
+  const float* s[7];
+};
+
+// (rows, columns) of the seven projections of a layer
+void w8_shapes(const lss_config* c, int (&n)[7], int (&k)[7]) {
+  const int d = c->d_model, F = c->ffn_dim, qd = c->n_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
+  const int nn[7] = {qd, kvd, kvd, d, F, F, d}, kk[7] = {d, d, d, qd, d, d, F};
+  for (int i = 0; i < 7; ++i) { n[i] = nn[i]; k[i] = kk[i]; }
+}
+// bytes of the int8 copy of every layer; offsets[l][i] of codes and scales
+size_t w8_layout(const lss_config* c, std::vector<std::array<size_t, 14>>* offs) {
+  int n[7], k[7];
+  w8_shapes(c, n, k);
+  size_t off = 0;
+  if (offs) offs->resize(c->n_layers);
+  for (int l = 0; l < c->n_layers; ++l)
+    for (int i = 0; i < 7; ++i) {
+      if (offs) (*offs)[l][i] = off;
+      off += align_up((size_t)n[i] * k[i]);
+      if (offs) (*offs)[l][7 + i] = off;
+      off += align_up((size_t)n[i] * 4);
+    }
+  return off;
+}
 
 enum RowMode { MODE_CAUSAL = 0, MODE_DRAFT = 1, MODE_DP = 2 };
 
@@ -151,6 +182,8 @@ struct lss_engine {
   float *hs, *hmid, *xs, *qkv, *apart, *aout, *act, *logits, *hpart, *target, *dpg[2], *dpx, *dpdec;
   float *pgpart, *rstd;
   float *dlogits = nullptr, *srec = nullptr;  // sampling: draft logits of the window slots, replacement-draw records
+  int8_t* q8 = nullptr;                       // int8-weight draft: activation codes of the row
+  std::vector<LayerW8> w8;                    // int8 weight copies (lss_attach_w8), empty until attached
   void *xa, *xb, *xc;   // projection inputs: layer input (attention-norm gain), attention / FFN output, mid-layer
   float *pa, *pc;       // partial sums of squares of the residual rows behind xa and xc
   float2* rope;
@@ -422,21 +455,56 @@ void attention_w(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
 }
 
 // RMSNorm + int8 codes of M rows of h into the projection input x (quantized drafts)
-void norm_quant(lss_engine* e, const float* h, int M, const float* g, void* x) {
+// int8 codes of the normalized rows: in the projection format (x), or raw
+// into q8 when q8 != nullptr (the int8-weight draft)
+void norm_quant(lss_engine* e, const float* h, int M, const float* g, void* x, int8_t* q8 = nullptr) {
   const auto& c = e->cfg;
   if (e->bf16)
     hipLaunchKernelGGL(k_rmsnorm_quant<uint16_t>, dim3(M), dim3(LSS_NORM_THREADS), 0, e->stream, h, c.d_model, g,
-                       c.d_model, c.rms_eps, x, e->xs);
+                       c.d_model, c.rms_eps, x, e->xs, q8);
   else
     hipLaunchKernelGGL(k_rmsnorm_quant<float>, dim3(M), dim3(LSS_NORM_THREADS), 0, e->stream, h, c.d_model, g,
-                       c.d_model, c.rms_eps, x, e->xs);
+                       c.d_model, c.rms_eps, x, e->xs, q8);
 }
 
-void quant_rows(lss_engine* e, const float* x, int M, int n, void* xo) {
+void quant_rows(lss_engine* e, const float* x, int M, int n, void* xo, int8_t* q8 = nullptr) {
   if (e->bf16)
-    hipLaunchKernelGGL(k_quant_rows<uint16_t>, dim3(M), dim3(256), 0, e->stream, x, n, n, xo, e->xs, (int8_t*)nullptr);
+    hipLaunchKernelGGL(k_quant_rows<uint16_t>, dim3(M), dim3(256), 0, e->stream, x, n, n, xo, e->xs, q8);
   else
-    hipLaunchKernelGGL(k_quant_rows<float>, dim3(M), dim3(256), 0, e->stream, x, n, n, xo, e->xs, (int8_t*)nullptr);
+    hipLaunchKernelGGL(k_quant_rows<float>, dim3(M), dim3(256), 0, e->stream, x, n, n, xo, e->xs, q8);
+}
+
+// int8 GEMV of the row e->q8 (scale e->xs[0]) against int8 weights; the
+// timing events of lss_profile_kernel bracket it like the bf16 launches
+template <int EPI>
+void gemm8(lss_engine* e, const GemmArgs& ga) {
+  const bool prof = e->prof_epi == EPI && (e->prof_rows == 0 || e->prof_rows == ga.M);
+  if (prof && e->ev_used == (int)e->ev_start.size()) {
+    (void)hipStreamSynchronize(e->stream);
+    prof_resolve(e);
+  }
+  hipEvent_t t0 = prof ? e->ev_start[e->ev_used] : nullptr, t1 = prof ? e->ev_stop[e->ev_used] : nullptr;
+  const dim3 grid((ga.N + G8_TR - 1) / G8_TR), block(G8_THREADS);
+  auto go = [&](auto wt) {
+    using WT = decltype(wt);
+    const int per = (ga.K + G8_THREADS - 1) / G8_THREADS;
+    if (ga.xq || per <= 8) launch_k(k_gemv8<WT, EPI, 8>, grid, block, 0, e->stream, t0, t1, ga);
+    else if (per <= 16) launch_k(k_gemv8<WT, EPI, 16>, grid, block, 0, e->stream, t0, t1, ga);
+    else if (per <= 32) launch_k(k_gemv8<WT, EPI, 32>, grid, block, 0, e->stream, t0, t1, ga);
+    else launch_k(k_gemv8<WT, EPI, 64>, grid, block, 0, e->stream, t0, t1, ga);
+  };
+  if (e->bf16) go(uint16_t{});
+  else go(float{});
+  if (prof) {
+    e->ev_used++;
+    e->prof_launches++;
+    const int64_t nw = (EPI == EPI_SWIGLU) ? 2 : 1;
+    const int64_t outw = (ga.Y && !(EPI == EPI_SWIGLU && ga.xo) ? 4 : 0) + (ga.xo ? 4 : 0);
+    // int8 weights + row scales + activation row (codes, or float32 quantized in place) + rows written
+    e->prof_bytes += nw * ((int64_t)ga.N * ga.K + (int64_t)ga.N * 4) + (int64_t)ga.K * (ga.xq ? 1 : 4) +
+                     (int64_t)ga.N * outw +
+                     (EPI == EPI_RESID ? (int64_t)ga.N * 4 : 0);
+  }
 }
 
 // projection input + partial sums of squares of M rows of h (row stride d) with gain g
@@ -457,6 +525,45 @@ void layer_forward(lss_engine* e, int l, int M, const float* h_in, const void* x
   const LayerW& w = e->layers[l];
   const int d = c.d_model, F = c.ffn_dim, hd = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
   const int qd = Hq * hd, kvd = Hkv * hd;
+  if (quant == 2) {   // int8 weights and int8 activations (one draft row)
+    // each int8 GEMV forms its activation codes itself: from the residual row
+    // and its partial sums of squares (RMSNorm inputs) or from the float32 row
+    const LayerW8& w8 = e->w8[l];
+    auto args8 = [&](int i, int N, int K, const float* A, float* Y) {
+      GemmArgs ga = gemm_args(w8.q[i], N, K, A, K, M, Y, N);
+      ga.wsc[0] = ga.wsc[1] = ga.wsc[2] = w8.s[i];
+      return ga;
+    };
+    {
+      GemmArgs ga = args8(0, qd + 2 * kvd, d, h_in, e->qkv);
+      ga.scale = SCALE_NORM; ga.pin = pa_in; ga.eps = c.rms_eps; ga.gin = w.attn_norm;
+      ga.w[0] = w8.q[0]; ga.nseg[0] = qd; ga.wsc[0] = w8.s[0];
+      ga.w[1] = w8.q[1]; ga.nseg[1] = kvd; ga.wsc[1] = w8.s[1];
+      ga.w[2] = w8.q[2]; ga.nseg[2] = kvd; ga.wsc[2] = w8.s[2];
+      gemm8<EPI_STORE>(e, ga);
+    }
+    if (e->bf16) attention_w<uint16_t>(e, l, M, mode, pos0, quant);
+    else attention_w<float>(e, l, M, mode, pos0, quant);
+    {
+      GemmArgs ga = args8(3, d, qd, e->aout, e->hmid);
+      ga.R = h_in; ga.ldr = d;
+      ga.po = e->pc;                                   // partial sums of squares for the FFN norm
+      gemm8<EPI_RESID>(e, ga);
+    }
+    {
+      GemmArgs ga = args8(4, F, d, e->hmid, e->act);
+      ga.scale = SCALE_NORM; ga.pin = e->pc; ga.eps = c.rms_eps; ga.gin = w.ffn_norm;
+      ga.w2 = w8.q[5]; ga.wsc2 = w8.s[5];
+      gemm8<EPI_SWIGLU>(e, ga);
+    }
+    {
+      GemmArgs ga = args8(6, d, F, e->act, h_out);
+      ga.R = e->hmid; ga.ldr = d;
+      if (g_next) { ga.xo = e->xa; ga.ldo = d; ga.go = g_next; ga.po = e->pa; }
+      gemm8<EPI_RESID>(e, ga);
+    }
+    return;
+  }
   {
     GemmArgs ga;
     if (quant) {
@@ -629,12 +736,13 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
   e->dpdec = (float*)(ws + lay.dpdec); e->tok = (int32_t*)(ws + lay.tok); e->seqtok = (int32_t*)(ws + lay.seqtok);
   e->res = (HeadRes*)(ws + lay.res);
   e->dlogits = (float*)(ws + lay.dlogits); e->srec = (float*)(ws + lay.srec);
+  e->q8 = (int8_t*)(ws + lay.q8);
   e->valid.assign(cfg->n_layers, 0u);
   {  // every workspace pointer must be set (a null one would be written by a kernel)
     const void* ptrs[] = {e->kc, e->vc, e->hs, e->hmid, e->xa, e->xb, e->xc, e->pa, e->pc, e->xs, e->qkv,
                           e->pgpart, e->rstd, e->apart, e->aout, e->act, e->logits, e->hpart, e->rope,
                           e->target, e->dpg[0], e->dpg[1], e->dpx, e->dpdec, e->tok, e->seqtok, e->res,
-                          e->dlogits, e->srec};
+                          e->dlogits, e->srec, e->q8};
     for (const void* q : ptrs)
       if (!q) {
         lss_destroy(e);
@@ -685,6 +793,86 @@ void lss_destroy(lss_engine* e) {
 const char* lss_last_error(const lss_engine* e) { return e ? e->err.c_str() : "null engine"; }
 
 int32_t lss_seq_len(const lss_engine* e) { return e ? e->p : -1; }
+
+size_t lss_w8_bytes(const lss_config* cfg) {
+  if (!cfg_valid(cfg, nullptr)) return 0;
+  return w8_layout(cfg, nullptr);
+}
+
+int lss_attach_w8(lss_engine* e, void* buf, size_t bytes) {
+  if (!e) return LSS_EINVAL;
+  const lss_config* c = &e->cfg;
+  std::vector<std::array<size_t, 14>> offs;
+  const size_t need = w8_layout(c, &offs);
+  if (!buf || ((uintptr_t)buf & 255)) return fail(e, LSS_EINVAL, "attach_w8: null or unaligned buffer");
+  if (bytes < need) return fail(e, LSS_ECAPACITY, "attach_w8: buffer smaller than lss_w8_bytes");
+  int n[7], k[7];
+  w8_shapes(c, n, k);
+  std::vector<LayerW8> w8(c->n_layers);
+  char* b = (char*)buf;
+  for (int l = 0; l < c->n_layers; ++l) {
+    const LayerW& w = e->layers[l];
+    const void* src[7] = {w.wq, w.wk, w.wv, w.wo, w.wg, w.wu, w.wd};
+    for (int i = 0; i < 7; ++i) {
+      int8_t* q = (int8_t*)(b + offs[l][i]);
+      float* sc = (float*)(b + offs[l][7 + i]);
+      if (e->bf16)
+        hipLaunchKernelGGL(k_quant_w8<uint16_t>, dim3(n[i]), dim3(256), 0, e->stream, (const uint16_t*)src[i], k[i], q, sc);
+      else
+        hipLaunchKernelGGL(k_quant_w8<float>, dim3(n[i]), dim3(256), 0, e->stream, (const float*)src[i], k[i], q, sc);
+      w8[l].q[i] = q;
+      w8[l].s[i] = sc;
+    }
+  }
+  int rc = check_launch(e, "attach_w8");
+  if (rc) return rc;
+  HIPCHK(hipStreamSynchronize(e->stream));
+  e->w8 = std::move(w8);
+  return LSS_OK;
+}
+
+int lss_op_w8_quantize(const void* w, int32_t dtype, int32_t rows, int32_t k, int8_t* q, float* scale, void* stream) {
+  if (!w || !q || !scale || rows < 0 || k < 0 || (dtype != LSS_F32 && dtype != LSS_BF16)) return LSS_EINVAL;
+  if (rows == 0) return LSS_OK;
+  if (dtype == LSS_BF16)
+    hipLaunchKernelGGL(k_quant_w8<uint16_t>, dim3(rows), dim3(256), 0, (hipStream_t)stream, (const uint16_t*)w, k, q, scale);
+  else
+    hipLaunchKernelGGL(k_quant_w8<float>, dim3(rows), dim3(256), 0, (hipStream_t)stream, (const float*)w, k, q, scale);
+  return hipGetLastError() == hipSuccess ? LSS_OK : LSS_EHIP;
+}
+
+int lss_op_w8a8_gemv(const int8_t* wq, const float* wscale, int32_t n, int32_t k, const int8_t* xq,
+                     const float* xscale, float* y, void* stream) {
+  if (!wq || !wscale || !xq || !xscale || !y || n < 1 || k < 16 || n % 16 || k % 16 || k > G8_KMAX)
+    return LSS_EINVAL;
+  if (((uintptr_t)wq & 15) || ((uintptr_t)xq & 15)) return LSS_EINVAL;
+  GemmArgs ga{};
+  ga.w[0] = ga.w[1] = ga.w[2] = wq;
+  ga.nseg[0] = n;
+  ga.wsc[0] = ga.wsc[1] = ga.wsc[2] = wscale;
+  ga.N = n; ga.K = k; ga.M = 1; ga.xq = xq; ga.xs = xscale; ga.Y = y; ga.ldy = n;
+  hipLaunchKernelGGL((k_gemv8<float, EPI_STORE, 8>), dim3(n / G8_TR), dim3(G8_THREADS), 0, (hipStream_t)stream, ga);
+  return hipGetLastError() == hipSuccess ? LSS_OK : LSS_EHIP;
+}
+
+int lss_op_w8a8_gemv_f32(const int8_t* wq, const float* wscale, int32_t n, int32_t k, const float* x, float* y,
+                         void* stream) {
+  if (!wq || !wscale || !x || !y || n < 1 || k < 16 || n % 16 || k % 16 || k > G8_KMAX) return LSS_EINVAL;
+  if ((uintptr_t)wq & 15) return LSS_EINVAL;
+  GemmArgs ga{};
+  ga.w[0] = ga.w[1] = ga.w[2] = wq;
+  ga.nseg[0] = n;
+  ga.wsc[0] = ga.wsc[1] = ga.wsc[2] = wscale;
+  ga.N = n; ga.K = k; ga.M = 1; ga.A = x; ga.lda = k; ga.scale = SCALE_NONE; ga.Y = y; ga.ldy = n;
+  const dim3 grid(n / G8_TR), block(G8_THREADS);
+  const hipStream_t s = (hipStream_t)stream;
+  const int per = (k + G8_THREADS - 1) / G8_THREADS;
+  if (per <= 8) hipLaunchKernelGGL((k_gemv8<float, EPI_STORE, 8>), grid, block, 0, s, ga);
+  else if (per <= 16) hipLaunchKernelGGL((k_gemv8<float, EPI_STORE, 16>), grid, block, 0, s, ga);
+  else if (per <= 32) hipLaunchKernelGGL((k_gemv8<float, EPI_STORE, 32>), grid, block, 0, s, ga);
+  else hipLaunchKernelGGL((k_gemv8<float, EPI_STORE, 64>), grid, block, 0, s, ga);
+  return hipGetLastError() == hipSuccess ? LSS_OK : LSS_EHIP;
+}
 
 int lss_set_sampling(lss_engine* e, float temperature, uint64_t seed) {
   if (!e) return LSS_EINVAL;
@@ -740,7 +928,8 @@ int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, floa
   const GemvScope gv(e);
   const auto& c = e->cfg;
   if (!e->have_seq || e->pending_accept) return fail(e, LSS_ESTATE, "draft: needs a prefilled sequence and no pending accept");
-  if (!mask || k < 0 || (quant != 0 && quant != 1)) return fail(e, LSS_EINVAL, "draft: bad arguments");
+  if (!mask || k < 0 || quant < 0 || quant > 2) return fail(e, LSS_EINVAL, "draft: bad arguments");
+  if (quant == 2 && e->w8.empty()) return fail(e, LSS_ESTATE, "draft: int8 weights not attached (lss_attach_w8)");
   if (k > 0 && !tokens_out) return fail(e, LSS_EINVAL, "draft: null tokens_out");
   const int win_cap = std::min(kWinMax, c.max_rows - 1);
   if (e->win + k > win_cap) return fail(e, LSS_ECAPACITY, "draft: window would exceed its capacity");

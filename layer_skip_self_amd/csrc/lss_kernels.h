@@ -220,12 +220,13 @@ __device__ __forceinline__ float quant_code(float x, float inv) {
 #define LSS_NORM_PER_THREAD 32   // d_model <= 8192
 
 // RMSNorm + dynamic int8 quantization of rows of h (the quantized draft):
-// x = h / sqrt(mean(h^2) + eps) * g; codes of x in the projection format,
-// xs[m] = amax / 127.
+// x = h / sqrt(mean(h^2) + eps) * g; codes of x in the projection format
+// (xo), or as int8 (q8, the int8-weight draft), xs[m] = amax / 127.
 template <typename WT>
 __global__ __launch_bounds__(LSS_NORM_THREADS) void k_rmsnorm_quant(const float* __restrict__ h, int ldh,
                                                                     const float* __restrict__ g, int d, float eps,
-                                                                    void* xo, float* __restrict__ xs) {
+                                                                    void* xo, float* __restrict__ xs,
+                                                                    int8_t* __restrict__ q8) {
   __shared__ float red[LSS_NORM_THREADS / 64];
   const int m = blockIdx.x;
   const float* hr = h + (size_t)m * ldh;
@@ -251,9 +252,30 @@ __global__ __launch_bounds__(LSS_NORM_THREADS) void k_rmsnorm_quant(const float*
 #pragma unroll
   for (int j = 0; j < LSS_NORM_PER_THREAD; ++j) {
     const int i = threadIdx.x + j * LSS_NORM_THREADS;
-    if (i < d) AF<WT>::store(xo, (size_t)m * d, i, quant_code(v[j], inv));
+    if (i < d) {
+      const float q = quant_code(v[j], inv);
+      if (q8) q8[(size_t)m * d + i] = (int8_t)q;
+      else AF<WT>::store(xo, (size_t)m * d, i, q);
+    }
   }
   if (threadIdx.x == 0) xs[m] = __fdiv_rn(amax, 127.0f);
+}
+
+// Per-row int8 copy of a weight matrix [rows][k] for the int8-weight draft:
+// each row is quantized with the activation rule (codes rint(w fl32(127 /
+// amax)) clamped to +-127, scale amax / 127, amax = 0 gives codes 0).
+template <typename WT>
+__global__ __launch_bounds__(256) void k_quant_w8(const WT* __restrict__ w, int k, int8_t* __restrict__ q,
+                                                 float* __restrict__ scale) {
+  __shared__ float red[4];
+  const size_t r = blockIdx.x;
+  const WT* wr = w + r * k;
+  float amax = 0.f;
+  for (int i = threadIdx.x; i < k; i += blockDim.x) amax = fmaxf(amax, fabsf(ld_elem<WT>(wr, i)));
+  amax = block_max(amax, red);
+  const float inv = amax > 0.f ? __fdiv_rn(127.0f, amax) : 0.f;
+  for (int i = threadIdx.x; i < k; i += blockDim.x) q[r * k + i] = (int8_t)quant_code(ld_elem<WT>(wr, i), inv);
+  if (threadIdx.x == 0) scale[r] = __fdiv_rn(amax, 127.0f);
 }
 
 // Dynamic int8 quantization of float32 rows x[m][0..n): codes in the
@@ -351,6 +373,10 @@ struct GemmArgs {
   const float* go;       // RESID: gain of the next RMSNorm (nullptr: 1)
   float* po;             // RESID: partial sums of squares of Y [M][N/16]
   float* part;           // LOGITS: per (row, tile) HEAD_PART floats (below)
+  const int8_t* xq;      // int8 GEMV: activation codes of the row (scale xs[0]); nullptr: quantize A
+  const float* gin;      // int8 GEMV quantizing A with SCALE_NORM: gain of that RMSNorm
+  const float* wsc[3];   // int8 GEMV: per-row weight scales of each segment
+  const float* wsc2;     // int8 GEMV, SWIGLU: scales of the up projection
   float inv_t;           // LOGITS: 1 / temperature; 0: greedy (no draws)
   uint64_t seed; int purpose; int pos0, pos_step;   // LOGITS draws: stream of row m is position pos0 + m pos_step
 };
@@ -835,6 +861,168 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
     y[q] = scaled ? __fmul_rn(v, sc) : v;
   }
   proj_out<WT, EPI>(ga, m, M, tile0 + i, i, y[0], NACC == 2 ? y[NACC - 1] : 0.f);
+}
+
+// ---------------------------------------------------------------- int8 decode GEMV (W8A8 draft)
+// One activation row against int8 weight rows with one float32 scale per row:
+//   y[n] = fl32(fl32(acc_n) * fl32(s_n * s_x)),   acc_n = sum_k q[k] w[n][k],
+// the integer sum exact (|acc| <= 127^2 K < 2^31).  The activation codes q
+// (scale s_x) are given (xq, xs[0]), or formed by every workgroup from the
+// float32 row A: x = A (SCALE_NONE) or x = A / sqrt(mean(A^2) + eps) * gin
+// (SCALE_NORM, the mean from the per-16-column partial sums pin), then the
+// per-token rule q = clamp(rint(x * fl32(127 / amax)), +-127), s_x =
+// amax / 127.  Every workgroup computes the same codes (same inputs, fixed
+// reduction order), so a separate quantization launch is not needed; the
+// first weight loads are issued before that work.  Loads as in the bf16
+// GEMV: one wave instruction reads one 1 KB chunk of one weight row (16
+// codes per lane, nontemporal).  A workgroup owns G8_TR weight rows, two per
+// wave; a wave walks all of K for its rows in batches of G8_U chunks and
+// multiplies four code pairs per v_dot4.  Integer sums are exact, so
+// neither the split nor the order of the lane and wave sums changes a bit.
+#define G8_WAVES 8
+#define G8_THREADS (64 * G8_WAVES)
+#define G8_TR 16
+#define G8_RW (G8_TR / G8_WAVES)     // weight rows per wave
+#define G8_U 4
+#define G8_KMAX 32768                // codes staged in LDS
+
+__device__ __forceinline__ int dot16_i8(const uint4& a, const uint4& w, int acc) {
+  acc = __builtin_amdgcn_sdot4((int)a.x, (int)w.x, acc, false);
+  acc = __builtin_amdgcn_sdot4((int)a.y, (int)w.y, acc, false);
+  acc = __builtin_amdgcn_sdot4((int)a.z, (int)w.z, acc, false);
+  acc = __builtin_amdgcn_sdot4((int)a.w, (int)w.w, acc, false);
+  return acc;
+}
+// integer sum over a wave (exact, any order)
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<LSS_DPP_XOR1>(v);
+  v += dpp_i<LSS_DPP_XOR2>(v);
+  v += dpp_i<LSS_DPP_HMIRROR>(v);
+  v += dpp_i<LSS_DPP_MIRROR>(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+         __builtin_amdgcn_readlane(v, 48);
+}
+
+// WT: the model's weight type (format of the projection input the epilogue
+// writes for the next full-precision consumer).  XPT: activation elements
+// per thread held in registers while the codes are formed (K <= XPT *
+// G8_THREADS); K is a multiple of 16 and at most G8_KMAX.
+template <typename WT, int EPI, int XPT>
+__global__ __launch_bounds__(G8_THREADS) void k_gemv8(GemmArgs ga) {
+  constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
+  __shared__ uint4 xq_s[G8_KMAX / 16];
+  __shared__ int acc_s[NACC][G8_TR];
+  __shared__ float red_s[2][G8_WAVES];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K = ga.K;
+  const int nv = K >> 4;                                 // 16-code vectors of the row
+  const int tile0 = blockIdx.x * G8_TR;
+  int seg = 0, nloc = tile0;
+  while (seg < 2 && nloc >= ga.nseg[seg]) { nloc -= ga.nseg[seg]; ++seg; }
+  const int8_t* wb[NACC];
+  wb[0] = reinterpret_cast<const int8_t*>(ga.w[seg]) + (size_t)nloc * K;
+  if constexpr (NACC == 2) wb[NACC - 1] = reinterpret_cast<const int8_t*>(ga.w2) + (size_t)tile0 * K;
+  const int nrow = min(G8_TR, ga.N - tile0);
+  const int nch = (K + 1023) >> 10;
+  const int kl = lane * 16;
+  size_t ro[G8_RW];
+#pragma unroll
+  for (int r = 0; r < G8_RW; ++r) ro[r] = (size_t)min(wave + r * G8_WAVES, nrow - 1) * K;
+  uint4 w[G8_U][G8_RW][NACC];
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < G8_U; ++u) {
+      const int k = (c0 + u) * 1024 + kl;
+      const int kk = k < K ? k : 0;
+#pragma unroll
+      for (int r = 0; r < G8_RW; ++r)
+#pragma unroll
+        for (int q = 0; q < NACC; ++q) w[u][r][q] = ld_nt16(wb[q] + ro[r] + kk);
+    }
+  };
+  load_batch(0);
+  // activation codes into LDS (and the scale): one round of global loads
+  // (row elements k = tid + G8_THREADS j, gains, partial sums), then 1/rms
+  // and amax by block reductions, codes from registers
+  float sx;
+  if (ga.xq) {
+    for (int v = threadIdx.x; v < nv; v += G8_THREADS) xq_s[v] = reinterpret_cast<const uint4*>(ga.xq)[v];
+    sx = ga.xs[0];
+  } else {
+    const float* xf = reinterpret_cast<const float*>(ga.A);
+    const bool norm = ga.scale == SCALE_NORM;
+    float x[XPT], g[XPT];
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int k = threadIdx.x + j * G8_THREADS;
+      x[j] = k < K ? xf[k] : 0.f;
+      g[j] = (norm && k < K) ? ga.gin[k] : 0.f;
+    }
+    float ps = (norm && (int)threadIdx.x < nv) ? ga.pin[threadIdx.x] : 0.f;
+    if (norm) {                                          // 1/rms from the partial sums, in wave order
+      ps = wave_sum(ps);
+      if (lane == 0) red_s[0][wave] = ps;
+      __syncthreads();
+      float v = red_s[0][0];
+#pragma unroll
+      for (int i = 1; i < G8_WAVES; ++i) v = __fadd_rn(v, red_s[0][i]);
+      const float rstd = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(v, (float)K), ga.eps)));
+#pragma unroll
+      for (int j = 0; j < XPT; ++j) x[j] = __fmul_rn(__fmul_rn(x[j], rstd), g[j]);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    amax = wave_max(amax);
+    if (lane == 0) red_s[1][wave] = amax;
+    __syncthreads();
+    amax = red_s[1][0];
+#pragma unroll
+    for (int i = 1; i < G8_WAVES; ++i) amax = fmaxf(amax, red_s[1][i]);
+    const float inv = amax > 0.f ? __fdiv_rn(127.0f, amax) : 0.f;
+    sx = __fdiv_rn(amax, 127.0f);
+    int8_t* qs = reinterpret_cast<int8_t*>(xq_s);
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int k = threadIdx.x + j * G8_THREADS;
+      if (k < K) qs[k] = (int8_t)(int)quant_code(x[j], inv);
+    }
+  }
+  __syncthreads();
+  int acc[G8_RW][NACC];
+#pragma unroll
+  for (int r = 0; r < G8_RW; ++r)
+#pragma unroll
+    for (int q = 0; q < NACC; ++q) acc[r][q] = 0;
+  for (int c0 = 0; c0 < nch; c0 += G8_U) {
+    if (c0 > 0) load_batch(c0);
+#pragma unroll
+    for (int u = 0; u < G8_U; ++u) {
+      const int v = (c0 + u) * 64 + lane;
+      const uint4 a = v < nv ? xq_s[v] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int r = 0; r < G8_RW; ++r)
+#pragma unroll
+        for (int q = 0; q < NACC; ++q) acc[r][q] = dot16_i8(a, w[u][r][q], acc[r][q]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < G8_RW; ++r)
+#pragma unroll
+    for (int q = 0; q < NACC; ++q) {
+      const int t = wave_sum_i(acc[r][q]);
+      if (lane == 0) acc_s[q][wave + r * G8_WAVES] = t;
+    }
+  __syncthreads();
+  // epilogue: lanes 0..15 of wave 0 -> columns tile0 .. tile0 + 15
+  if (threadIdx.x >= 16) return;
+  const int i = threadIdx.x;
+  const int n = tile0 + i, il = min(i, nrow - 1);
+  const float y = __fmul_rn((float)acc_s[0][il], __fmul_rn(ga.wsc[seg][nloc + il], sx));
+  float u = 0.f;
+  if constexpr (NACC == 2) u = __fmul_rn((float)acc_s[1][il], __fmul_rn(ga.wsc2[tile0 + il], sx));
+  proj_out<WT, EPI>(ga, 0, 1, n, i, y, u);
 }
 
 // ---------------------------------------------------------------- attention

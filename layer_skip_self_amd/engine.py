@@ -86,6 +86,14 @@ class Engine:
         return int(self.lib.lss_seq_len(self.h))
 
     # -------------------------------------------------------------- hot path
+    def attach_w8(self):
+        """int8 copy of every layer's weights for the W8A8 draft (quant = 2),
+        in a device buffer this object owns."""
+        import torch
+        nbytes = int(self.lib.lss_w8_bytes(C.byref(self.cfg)))
+        self._w8 = torch.empty(nbytes, dtype=torch.uint8, device=self._ws.device)
+        self._check(self.lib.lss_attach_w8(self.h, C.c_void_p(self._w8.data_ptr()), nbytes), "lss_attach_w8")
+
     def set_sampling(self, temperature, seed=0):
         """Speculative sampling at ``temperature`` with ``seed`` (0: greedy)."""
         self._check(self.lib.lss_set_sampling(self.h, float(temperature), int(seed) % 2**64), "lss_set_sampling")
@@ -96,11 +104,13 @@ class Engine:
         self._check(self.lib.lss_prefill(self.h, p, len(a), C.byref(t0)), "lss_prefill")
         return int(t0.value)
 
-    def draft(self, skip_mask, quant=False, k=1, exit_tau=0.0):
+    def draft(self, skip_mask, quant=0, k=1, exit_tau=0.0):
+        """quant: 0 / False full precision, 1 / True int8 activations, 2 int8
+        activations and int8 weights (``attach_w8`` first)."""
         m, mp = _u8(skip_mask)
         out = np.zeros(max(k, 1), np.int32)
         done = C.c_int32()
-        self._check(self.lib.lss_draft(self.h, mp, int(bool(quant)), int(k), float(exit_tau),
+        self._check(self.lib.lss_draft(self.h, mp, int(quant), int(k), float(exit_tau),
                                        out.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(done)), "lss_draft")
         return out[:done.value].tolist()
 
@@ -212,7 +222,7 @@ def make_policy(policy, n_layers):
                 "cascade": N.LSS_MODE_CASCADE}[mode]
     pol.k_max = int(policy.get("k_max", 0))
     pol.exit_tau = float(policy.get("exit_tau", 0.0))
-    pol.quant = int(bool(policy.get("quant", False)))
+    pol.quant = int(policy.get("quant", 0))
     if mode == "static":
         mask = np.zeros(n_layers, np.uint8)
         for l in policy["skip"]:
@@ -226,7 +236,7 @@ def make_policy(policy, n_layers):
     for i, (skip, exit_, quant) in enumerate(levels):
         pol.level_skip[i] = int(skip)
         pol.level_exit[i] = int(exit_)
-        pol.level_quant[i] = int(bool(quant))
+        pol.level_quant[i] = int(quant)
     beta = policy.get("beta", (0.0, 0.0, 0.0))
     for i in range(3):
         pol.beta[i] = float(beta[i])
@@ -266,6 +276,54 @@ def latency_fit(samples):
     if rc != 0:
         raise LssError("lss_latency_fit", rc)
     return tuple(beta)
+
+
+def w8_quantize(w):
+    """int8 codes and row scales of a CUDA weight matrix (float32 or bf16)."""
+    import torch
+    lib = N.load()
+    w = w.contiguous()
+    rows, k = w.shape
+    dt = {torch.float32: N.LSS_F32, torch.bfloat16: N.LSS_BF16}[w.dtype]
+    q = torch.empty((rows, k), dtype=torch.int8, device=w.device)
+    s = torch.empty((rows,), dtype=torch.float32, device=w.device)
+    rc = lib.lss_op_w8_quantize(C.c_void_p(w.data_ptr()), dt, rows, k, C.c_void_p(q.data_ptr()),
+                                C.c_void_p(s.data_ptr()), C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise LssError("lss_op_w8_quantize", rc)
+    return q, s
+
+
+def w8a8_gemv(wq, wscale, xq, xscale):
+    """y = fl32(fl32(wq @ xq) * fl32(wscale * xscale)) for CUDA int8 tensors
+    wq [n][k], xq [k] and float32 wscale [n], xscale [1]."""
+    import torch
+    lib = N.load()
+    wq, wscale, xq, xscale = (t.contiguous() for t in (wq, wscale, xq, xscale))
+    n, k = wq.shape
+    y = torch.empty((n,), dtype=torch.float32, device=wq.device)
+    rc = lib.lss_op_w8a8_gemv(C.c_void_p(wq.data_ptr()), C.c_void_p(wscale.data_ptr()), n, k,
+                              C.c_void_p(xq.data_ptr()), C.c_void_p(xscale.data_ptr()), C.c_void_p(y.data_ptr()),
+                              C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise LssError("lss_op_w8a8_gemv", rc)
+    return y
+
+
+def w8a8_gemv_f32(wq, wscale, x):
+    """The W8A8 projection of a float32 CUDA row x [k] (quantized in the
+    kernel) against int8 wq [n][k] with row scales wscale [n]."""
+    import torch
+    lib = N.load()
+    wq, wscale, x = (t.contiguous() for t in (wq, wscale, x))
+    n, k = wq.shape
+    y = torch.empty((n,), dtype=torch.float32, device=wq.device)
+    rc = lib.lss_op_w8a8_gemv_f32(C.c_void_p(wq.data_ptr()), C.c_void_p(wscale.data_ptr()), n, k,
+                                  C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()),
+                                  C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise LssError("lss_op_w8a8_gemv_f32", rc)
+    return y
 
 
 def quantize_rows(x):

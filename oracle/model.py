@@ -66,7 +66,10 @@ class OracleModel:
         if self._w8 is not None and key in self._w8:
             return self._w8[key]
         names = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
-        r = {n: quantize_weight_rows(np.asarray(self.w[f"layers.{l}.{n}"], np.float32)) for n in names}
+        r = {}
+        for n in names:
+            Q, S = quantize_weight_rows(np.asarray(self.w[f"layers.{l}.{n}"], np.float32))
+            r[n] = (Q.astype(np.float32), S)      # codes kept as exact float32 values
         if self._w8 is not None:
             self._w8[key] = r
         return r
@@ -152,11 +155,22 @@ def quantize_weight_rows(W):
     return Q, S
 
 
+W8_BLOCK = 1024
+
+
 def w8a8_accumulate(Q, q):
-    """Exact integer dot products sum_k q[k] Q[n][k] (int64).  The products
-    and every partial sum are integers below 2**53, so a float64 matrix
-    product computes them exactly."""
-    return np.rint(np.asarray(Q, np.float64) @ np.asarray(q, np.float64)).astype(np.int64)
+    """Exact integer dot products sum_k q[k] Q[n][k] (int64).  Q may hold the
+    codes as int8 or as their exact float32 values.  Columns are taken in
+    blocks of 1024: within a block every product and partial sum is an
+    integer of magnitude <= 127^2 * 1024 < 2^24, so a float32 matrix product
+    computes the block sum exactly in any order; the block sums are added
+    as int64."""
+    q32 = np.asarray(q, np.float32)
+    acc = np.zeros(Q.shape[0], np.int64)
+    for c in range(0, Q.shape[1], W8_BLOCK):
+        blk = np.asarray(Q[:, c:c + W8_BLOCK], np.float32) @ q32[c:c + W8_BLOCK]
+        acc += np.rint(blk).astype(np.int64)
+    return acc
 
 
 def w8a8_project(Q, S, x):

@@ -45,6 +45,13 @@ def test_accumulator_is_exact():
     q = rng.integers(-127, 128, 53).astype(np.int8)
     ref = [sum(int(Q[n, k]) * int(q[k]) for k in range(53)) for n in range(7)]
     assert w8a8_accumulate(Q, q).tolist() == ref
+    assert w8a8_accumulate(Q.astype(np.float32), q).tolist() == ref
+    # several 1024-column blocks with every partial sum at the largest magnitude
+    K3 = 3000
+    Q3 = np.where(np.arange(K3) % 3 == 0, 127, -127).astype(np.int8)[None].repeat(2, 0)
+    Q3[1] = 127
+    q3 = np.where(np.arange(K3) % 3 == 0, 127, -127).astype(np.int8)
+    assert w8a8_accumulate(Q3, q3).tolist() == [127 * 127 * K3, sum(127 * int(v) for v in q3)]
     K = 28672                                    # largest K of the shapes (70B down projection)
     big = np.full((2, K), 127, np.int8)
     big[1] = -127
