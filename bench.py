@@ -116,45 +116,53 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
 
 GEMV_SECTIONS = ("scalars", "projection input format", "projections: shared definitions",
                  "decode GEMV (vector ALU)")
+# the int8 GEMV also takes the activation rule (small kernels) and the load
+# helper of the bf16 GEMV
+GEMV8_SECTIONS = ("scalars", "projection input format", "small kernels", "projections: shared definitions",
+                  "decode GEMV (vector ALU)", "int8 decode GEMV (W8A8 draft)")
+TRAFFIC_RECORDS = (("draft_gemv_llama3_8b.md", GEMV_SECTIONS),
+                   ("draft_gemv8_llama3_8b_w8a8.md", GEMV8_SECTIONS))
 
 
-def gemv_source_hash():
-    """sha256 of the kernel-source sections the decode GEMV is built from
-    (the sections of lss_kernels.h named in GEMV_SECTIONS, in file order)."""
+def gemv_source_hash(sections=GEMV_SECTIONS):
+    """sha256 of kernel-source sections of lss_kernels.h (the named sections,
+    in the given order) a recorded kernel is built from."""
     import hashlib
     src = os.path.join(ROOT, "layer_skip_self_amd", "csrc", "lss_kernels.h")
     mark = "// " + "-" * 64 + " "
-    sections, name = {}, None
+    found, name = {}, None
     for line in open(src):
         if line.startswith(mark):
             name = line[len(mark):].strip()
         if name is not None:
-            sections[name] = sections.get(name, "") + line
+            found[name] = found.get(name, "") + line
     h = hashlib.sha256()
-    for n in GEMV_SECTIONS:
-        h.update(sections[n].encode())
+    for n in sections:
+        h.update(found[n].encode())
     return h.hexdigest()
 
 
 def recorded_traffic(bytes_per_launch):
-    """HBM bytes per launch of the draft gate/up kernel measured with rocprofv3
-    counters (profiles/draft_gemv_llama3_8b.md), or None when the kernel's
-    source sections changed since the counters were taken or the launch is
-    not the recorded one (another model shape)."""
-    rec = os.path.join(ROOT, "profiles", "draft_gemv_llama3_8b.md")
-    try:
-        fields = {}
-        for line in open(rec):
-            if ":" in line and line.startswith("- "):
-                k, v = line[2:].split(":", 1)
-                fields[k.strip()] = v.strip().strip("`")
-        if fields.get("kernel source sha256") != gemv_source_hash():
-            return None
-        if int(fields["algorithmic bytes per launch"].split()[0]) != int(bytes_per_launch):
-            return None
-        return int(fields["traffic bytes per launch"])
-    except (OSError, KeyError, ValueError):
-        return None
+    """HBM bytes per launch of the timed draft gate/up kernel measured with
+    rocprofv3 counters (the records in profiles/), or None when no record
+    matches: its kernel's source sections changed since the counters were
+    taken, or the launch is not the recorded one (another shape or kernel)."""
+    for name, sections in TRAFFIC_RECORDS:
+        rec = os.path.join(ROOT, "profiles", name)
+        try:
+            fields = {}
+            for line in open(rec):
+                if ":" in line and line.startswith("- "):
+                    k, v = line[2:].split(":", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+            if fields.get("kernel source sha256") != gemv_source_hash(sections):
+                continue
+            if int(fields["algorithmic bytes per launch"].split()[0]) != int(bytes_per_launch):
+                continue
+            return int(fields["traffic bytes per launch"])
+        except (OSError, KeyError, ValueError):
+            continue
+    return None
 
 
 def main():
@@ -227,7 +235,8 @@ def main():
     for _ in range(args.warmup):
         for pol, i in runs:
             run(pol, prompts[i])
-    eng.profile_kernel("gate_up", rows=1)
+    prof_kernel = "gate_up_int8" if w8 else "gate_up"      # the draft's gate/up kernel
+    eng.profile_kernel(prof_kernel, rows=1)
     spec_t = [0.0] * len(runs)
     stats, spec_toks = [None] * len(runs), [None] * len(runs)
     torch.cuda.synchronize()
@@ -241,7 +250,7 @@ def main():
     torch.cuda.synchronize()
     t_all = time.perf_counter() - t_all
     k_ms, k_n, k_bytes = eng.profile_read()
-    eng.profile_kernel("gate_up", enable=False)
+    eng.profile_kernel(prof_kernel, enable=False)
 
     # the AR leg decodes the same way (greedy, or sampling at the same
     # temperature and seed)

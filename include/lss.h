@@ -215,8 +215,9 @@ int lss_latency_fit(const double* samples, int32_t n, double* beta_out);
 /* Measurement: time every launch of one GEMM family with HIP events on the
  * engine stream.  epilogue: 0 = fused q/k/v projection, 1 = projection +
  * residual add (attention output, FFN down), 2 = gate/up projection + SwiGLU,
- * 3 = LM head + argmax partials; rows: match only launches with this many
- * rows (0 = any).  enable = 0 stops recording.  lss_profile_read syncs the
+ * 3 = LM head + argmax partials; 16 + the same code selects the int8 GEMV
+ * of the W8A8 draft (16 q/k/v, 17 residual, 18 gate/up); rows: match only
+ * launches with this many rows (0 = any).  enable = 0 stops recording.  lss_profile_read syncs the
  * stream and returns the summed launch time, the launch count and the summed
  * algorithmic bytes (weights + activation rows read + output rows written)
  * since profiling was enabled. */

@@ -478,7 +478,7 @@ void quant_rows(lss_engine* e, const float* x, int M, int n, void* xo, int8_t* q
 // timing events of lss_profile_kernel bracket it like the bf16 launches
 template <int EPI>
 void gemm8(lss_engine* e, const GemmArgs& ga) {
-  const bool prof = e->prof_epi == EPI && (e->prof_rows == 0 || e->prof_rows == ga.M);
+  const bool prof = e->prof_epi == EPI + 16 && (e->prof_rows == 0 || e->prof_rows == ga.M);
   if (prof && e->ev_used == (int)e->ev_start.size()) {
     (void)hipStreamSynchronize(e->stream);
     prof_resolve(e);
@@ -500,8 +500,10 @@ void gemm8(lss_engine* e, const GemmArgs& ga) {
     e->prof_launches++;
     const int64_t nw = (EPI == EPI_SWIGLU) ? 2 : 1;
     const int64_t outw = (ga.Y && !(EPI == EPI_SWIGLU && ga.xo) ? 4 : 0) + (ga.xo ? 4 : 0);
-    // int8 weights + row scales + activation row (codes, or float32 quantized in place) + rows written
+    // int8 weights + row scales + activation row (codes, or float32 quantized in place, with the RMSNorm
+    // gains and partial sums) + rows written
     e->prof_bytes += nw * ((int64_t)ga.N * ga.K + (int64_t)ga.N * 4) + (int64_t)ga.K * (ga.xq ? 1 : 4) +
+                     (ga.scale == SCALE_NORM ? (int64_t)ga.K * 4 + (int64_t)(ga.K / 16) * 4 : 0) +
                      (int64_t)ga.N * outw +
                      (EPI == EPI_RESID ? (int64_t)ga.N * 4 : 0);
   }
@@ -1235,7 +1237,8 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
 
 int lss_profile_kernel(lss_engine* e, int32_t epi, int32_t rows, int32_t enable) {
   if (!e) return LSS_EINVAL;
-  if (enable && (epi < 0 || epi > 3 || rows < 0)) return fail(e, LSS_EINVAL, "profile_kernel: bad epilogue / rows");
+  if (enable && (epi < 0 || (epi > 3 && (epi < 16 || epi > 18)) || rows < 0))
+    return fail(e, LSS_EINVAL, "profile_kernel: bad epilogue / rows");
   HIPCHK(hipStreamSynchronize(e->stream));
   prof_resolve(e);
   if (!enable) {

@@ -180,7 +180,8 @@ class Engine:
         return out.tolist(), {f: getattr(st, f) for f, _ in N.lss_stats._fields_}
 
     # -------------------------------------------------------------- measurement
-    EPILOGUES = {"qkv": 0, "resid": 1, "gate_up": 2, "lm_head": 3}
+    EPILOGUES = {"qkv": 0, "resid": 1, "gate_up": 2, "lm_head": 3,
+                 "qkv_int8": 16, "resid_int8": 17, "gate_up_int8": 18}
 
     def profile_kernel(self, epilogue, rows=0, enable=True):
         self._check(self.lib.lss_profile_kernel(self.h, self.EPILOGUES[epilogue], int(rows), int(enable)),
