@@ -118,6 +118,18 @@ def test_error_paths(tiny):
     eng.set_sampling(0.0)
 
 
+def test_sampling_with_w8a8_draft_matches_oracle(tiny):
+    """Speculative sampling with a W8A8 draft (q from the int8 draft)."""
+    T, seed = 1.0, 1006
+    ref, _, margins = _oracle_run(tiny, oracle.Policy(K=4, skip=(1,), quant=2), T, seed)
+    print(f"W8A8 + sampling: smallest oracle margin {min(margins):.3g}")
+    assert min(margins) > MARGIN, "seed leaves a decision too close to call; pick another"
+    tiny["eng"].attach_w8()
+    toks, _ = tiny["eng"].generate(tiny["prompt"], G, {"mode": "static", "k_max": 4, "skip": (1,), "quant": 2,
+                                                       "temperature": T, "seed": seed})
+    assert toks == ref
+
+
 def test_empty_mask_accepts_every_draft(tiny):
     toks, st = tiny["eng"].generate(tiny["prompt"], G, {"mode": "static", "k_max": 6, "skip": (),
                                                         "temperature": 0.8, "seed": 5})
