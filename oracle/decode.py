@@ -60,6 +60,7 @@ class DecodeState:
         self.target_states = None  # full states H*[0..L] of the last accepted token
         self.target_pos = None     # its position t*
         self.window_logits = []    # sampling: draft logits that produced each window token
+        self.tree = False          # the window holds sibling candidates (draft_tree)
         self.margins = []          # sampling: slack of every random decision taken
 
 
@@ -298,6 +299,70 @@ def accept(st, logits, states, drafts, sampling=None):
     return n, bonus, emitted
 
 
+def top_b(z, B):
+    """Indices of the B largest logits, largest first; equal logits keep the
+    lowest index first (so top_b(z, 1) == [argmax_first(z)])."""
+    z = np.asarray(z, np.float64)
+    order = np.lexsort((np.arange(len(z)), -z))
+    return [int(i) for i in order[:B]]
+
+
+def draft_tree(model, st, skip, quant, B):
+    """Tree draft of width B and depth 1: the draft model runs the pending
+    token's row (position p) with the skip mask and proposes its B most
+    likely tokens as sibling candidates for position p + 1.  Returns the
+    candidates (the window) and the draft's top-1 probability."""
+    z, _ = forward_row(model, st, st.t0, st.p, "draft", skip, quant)
+    st.window = top_b(z, B)
+    st.tree = True
+    zs = z - np.max(z)
+    return list(st.window), 1.0 / float(np.sum(np.exp(zs)))
+
+
+def verify_tree(model, st):
+    """Tree verify in one pass: row 0 is the pending token at position p; row
+    i >= 1 is candidate i at position p + 1 and sees the committed prefix,
+    the pending token and its own key and value only (a tree mask: siblings
+    are invisible to each other).  Each candidate row is therefore the full
+    model's step at p + 1 after that candidate.  Returns (logits [B+1][V],
+    states, candidates, per-candidate KV [B][L] of position p + 1)."""
+    cands = list(st.window)
+    z0, s0 = forward_row(model, st, st.t0, st.p, "full")
+    logits, states, kv = [z0], [s0], []
+    for c in cands:
+        z, s = forward_row(model, st, c, st.p + 1, "full")     # writes its KV at p + 1
+        logits.append(z)
+        states.append(s)
+        kv.append((st.k[:, st.p + 1].copy(), st.v[:, st.p + 1].copy()))
+    return np.stack(logits), states, cands, kv
+
+
+def accept_tree(st, logits, states, cands, kv):
+    """Greedy acceptance of a width-B tree: a_0 = argmax of row 0; if a
+    candidate equals a_0 (at most one can), it is accepted together with the
+    bonus a_i = argmax of its row (n = 1), and its KV becomes position
+    p + 1's; otherwise the bonus is a_0 (n = 0).  Returns (n, bonus,
+    emitted tokens)."""
+    a0 = argmax_first(logits[0])
+    hit = [i for i, c in enumerate(cands) if c == a0]
+    if hit:
+        i = hit[0]
+        bonus = argmax_first(logits[i + 1])
+        st.k[:, st.p + 1], st.v[:, st.p + 1] = kv[i]
+        n, row, emitted = 1, i + 1, [a0, bonus]
+    else:
+        n, row, emitted, bonus = 0, 0, [a0], a0
+    st.target_states = states[row]
+    st.target_pos = st.p + n
+    st.p = st.p + n + 1
+    st.t0 = bonus
+    st.window = []
+    st.window_logits = []
+    st.tree = False
+    st.valid = [0] * len(st.valid)
+    return n, bonus, emitted
+
+
 def ar_generate(model, prompt, G, max_seq=None, sampling=None, state_out=None):
     """Autoregressive decoding of G tokens (t0 included): greedy, or with
     ``sampling`` = (T, seed) the TARGET draw of every row's position.
@@ -328,7 +393,9 @@ class Policy:
     ``[(n_skip_by_dp, exit_layers, quant)]`` ordered fast -> precise, routed
     by the DyTC heuristics with at most ``K`` drafts per round;
     temperature > 0: speculative sampling with that temperature and seed
-    (``oracle.sampling``), 0: greedy.
+    (``oracle.sampling``), 0: greedy; tree_width B > 0 (greedy, static or
+    DP mask): every round drafts a width-B, depth-1 token tree
+    (``draft_tree``) instead of a chain.
     """
     K: int = 4
     skip: tuple = ()
@@ -341,6 +408,7 @@ class Policy:
     forced_drafts: dict = field(default_factory=dict)
     temperature: float = 0.0
     seed: int = 0
+    tree_width: int = 0
 
     @property
     def sampling(self):
@@ -403,6 +471,19 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None, state
             for lev, mk, kk in steps:
                 toks, _ = draft(model, st, mk, policy.cascade[lev][2], kk, 0.0, sam)
                 drafted_levels += [lev] * len(toks)
+        elif policy.tree_width and budget > 0:
+            draft_tree(model, st, masks[0], policy.quant, policy.tree_width)
+            logits, states, cands, kv = verify_tree(model, st)
+            n, bonus, emitted = accept_tree(st, logits, states, cands, kv)
+            out += emitted
+            rounds += 1
+            rec = {"k": len(cands), "n": n, "bonus": bonus, "tree": True}
+            records.append(rec)
+            if policy.dp_skip is not None and rounds % policy.interval == 0:
+                masks = select_masks()
+            if log is not None:
+                log.append(rec)
+            continue
         else:
             kk = min(policy.K, budget)
             if rounds in policy.forced_drafts:
