@@ -133,6 +133,22 @@ int lss_set_sampling(lss_engine* e, float temperature, uint64_t seed);
 int lss_draft(lss_engine* e, const uint8_t* skip_mask, int32_t quant, int32_t k, float exit_tau,
               int32_t* tokens_out, int32_t* k_done);
 
+/* Token-tree draft of width B (1 <= B <= 8) and depth 1, the pages' "dynamic
+ * tree cascade" read as a token tree (CAS-Spec abstract; CAS-Spec blog
+ * section 3): the draft (skip mask, quant as in lss_draft) runs the pending
+ * token's row at position p and proposes its B most likely tokens (largest
+ * logit first, ties to the lower id) as sibling candidates for position
+ * p + 1; tokens_out[B] receives them.  lss_verify(e, NULL, B) then verifies
+ * them in one pass with a tree mask (each candidate sees the committed
+ * prefix, the pending token and itself, so its row equals the full model's
+ * step after it bit for bit) and accepts greedily: the candidate equal to
+ * the full model's token after the pending one, with its own successor as
+ * the bonus (n = 1), else that token alone (n = 0); the accepted
+ * candidate's keys and values become position p + 1's.  Greedy only
+ * (LSS_EINVAL with sampling on); LSS_ESTATE unless the window is empty;
+ * LSS_ECAPACITY if B + 1 > max_rows or the KV capacity is exceeded. */
+int lss_draft_tree(lss_engine* e, const uint8_t* skip_mask, int32_t quant, int32_t B, int32_t* tokens_out);
+
 /* Verify the window in one full-model pass over rows [t0, d1..dk] at
  * positions p..p+k (CLaSp section 3, verification).  drafts == NULL
  * verifies the pending window; otherwise the k host tokens replace it (a
@@ -187,6 +203,7 @@ typedef struct lss_policy {
   int32_t level_exit[LSS_LEVELS_MAX];  /* early-exit tail length per level */
   int32_t level_quant[LSS_LEVELS_MAX]; /* int8 activations per level */
   double beta[3];            /* CASCADE latency model b0 + b1*seq_len + b2*executed_layers */
+  int32_t tree_width;        /* STATIC / DP: > 0 drafts a width-B token tree per round (lss_draft_tree) */
 } lss_policy;
 
 typedef struct lss_stats {

@@ -29,7 +29,8 @@ class lss_policy(C.Structure):
                 ("quant", C.c_int32), ("static_mask", C.POINTER(C.c_uint8)),
                 ("n_skip", C.c_int32), ("interval", C.c_int32), ("n_levels", C.c_int32),
                 ("level_skip", C.c_int32 * LSS_LEVELS_MAX), ("level_exit", C.c_int32 * LSS_LEVELS_MAX),
-                ("level_quant", C.c_int32 * LSS_LEVELS_MAX), ("beta", C.c_double * 3)]
+                ("level_quant", C.c_int32 * LSS_LEVELS_MAX), ("beta", C.c_double * 3),
+                ("tree_width", C.c_int32)]
 
 
 class lss_stats(C.Structure):
@@ -47,6 +48,7 @@ SIGNATURES = {
     "lss_prefill": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.POINTER(C.c_int32)]),
     "lss_draft": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint8), C.c_int32, C.c_int32, C.c_float,
                             C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
+    "lss_draft_tree": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint8), C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
     "lss_verify": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32]),
     "lss_accept_and_rollback": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                                           C.POINTER(C.c_int32)]),

@@ -162,7 +162,7 @@ size_t w8_layout(const lss_config* c, std::vector<std::array<size_t, 14>>* offs)
   return off;
 }
 
-enum RowMode { MODE_CAUSAL = 0, MODE_DRAFT = 1, MODE_DP = 2 };
+enum RowMode { MODE_CAUSAL = 0, MODE_DRAFT = 1, MODE_DP = 2, MODE_TREE = 3 };
 
 }  // namespace
 
@@ -183,6 +183,7 @@ struct lss_engine {
   float *pgpart, *rstd;
   float *dlogits = nullptr, *srec = nullptr;  // sampling: draft logits of the window slots, replacement-draw records
   int8_t* q8 = nullptr;                       // int8-weight draft: activation codes of the row
+  int tree = 0;                               // width of the pending tree window (0: a chain)
   std::vector<LayerW8> w8;                    // int8 weight copies (lss_attach_w8), empty until attached
   void *xa, *xb, *xc;   // projection inputs: layer input (attention-norm gain), attention / FFN output, mid-layer
   float *pa, *pc;       // partial sums of squares of the residual rows behind xa and xc
@@ -427,23 +428,28 @@ void attention(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
   a.kc = kc_layer(e, l); a.vc = vc_layer(e, l);
   a.max_seq = c.max_seq; a.Hq = c.n_heads; a.Hkv = c.n_kv_heads; a.M = M;
   a.pos0 = pos0; a.pos_step = mode == MODE_DP ? 0 : 1;
+  a.tree = mode == MODE_TREE ? 1 : 0;
   a.part = e->apart; a.nz_max = e->lay.nz_max; a.nch_max = e->lay.nch_max;
   a.out = e->aout;
   a.xo = quant ? nullptr : e->xb;
   a.scale = (float)(1.0 / std::sqrt((double)hd));
   int kmax;
   if (mode == MODE_CAUSAL) { a.lim_base = pos0 + 1; a.lim_step = 1; a.wbase = 0; a.wmask = 0; kmax = pos0 + M; }
+  else if (mode == MODE_TREE) { a.lim_base = pos0 + 1; a.lim_step = 0; a.wbase = 0; a.wmask = 0; kmax = pos0 + M; }
   else if (mode == MODE_DRAFT) { a.lim_base = e->p; a.lim_step = 0; a.wbase = e->p; a.wmask = e->valid[l]; kmax = pos0 + 1; }
   else { a.lim_base = pos0; a.lim_step = 0; a.wbase = 0; a.wmask = 0; a.self_kv = 1; kmax = pos0; }
   a.nch = std::max(1, (kmax + ATT_CH - 1) / ATT_CH);
   const int G = c.n_heads / c.n_kv_heads;
   a.nz = (G * M + ATT_QB - 1) / ATT_QB;
   const dim3 grid(a.nch, c.n_kv_heads, a.nz);
+  const bool tree = mode == MODE_TREE;
   if (hd == 128) {
-    hipLaunchKernelGGL((k_attention<KT, WT, 128>), grid, dim3(ATT_THREADS), 0, e->stream, a);
+    if (tree) hipLaunchKernelGGL((k_attention<KT, WT, 128, true>), grid, dim3(ATT_THREADS), 0, e->stream, a);
+    else hipLaunchKernelGGL((k_attention<KT, WT, 128>), grid, dim3(ATT_THREADS), 0, e->stream, a);
     hipLaunchKernelGGL((k_attn_merge<WT, 128>), dim3(ATT_QB, c.n_kv_heads, a.nz), dim3(128), 0, e->stream, a);
   } else {
-    hipLaunchKernelGGL((k_attention<KT, WT, 64>), grid, dim3(ATT_THREADS), 0, e->stream, a);
+    if (tree) hipLaunchKernelGGL((k_attention<KT, WT, 64, true>), grid, dim3(ATT_THREADS), 0, e->stream, a);
+    else hipLaunchKernelGGL((k_attention<KT, WT, 64>), grid, dim3(ATT_THREADS), 0, e->stream, a);
     hipLaunchKernelGGL((k_attn_merge<WT, 64>), dim3(ATT_QB, c.n_kv_heads, a.nz), dim3(64), 0, e->stream, a);
   }
 }
@@ -658,12 +664,12 @@ const float* next_gain(const lss_engine* e, const uint8_t* mask, int l) {
 // a full-model pass of M causal rows at positions pos0.. whose embeddings are
 // tokens tok_dev[0..M): residual stash in hs, projection input of the final
 // residual in e->xa (final-norm gain)
-void forward_rows(lss_engine* e, const int32_t* tok_dev, int M, int pos0) {
+void forward_rows(lss_engine* e, const int32_t* tok_dev, int M, int pos0, int mode = MODE_CAUSAL) {
   const int L = e->cfg.n_layers;
   embed(e, tok_dev, M, hs_row(e, 0, 0), next_gain(e, nullptr, -1));
   for (int l = 0; l < L; ++l)
     layer_forward(e, l, M, hs_row(e, l, 0), e->xa, e->pa, hs_row(e, l + 1, 0), next_gain(e, nullptr, l),
-                  MODE_CAUSAL, pos0, 0);
+                  mode, pos0, 0);
 }
 
 int sync_res(lss_engine* e) {
@@ -932,6 +938,7 @@ int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, floa
   if (!e->have_seq || e->pending_accept) return fail(e, LSS_ESTATE, "draft: needs a prefilled sequence and no pending accept");
   if (!mask || k < 0 || quant < 0 || quant > 2) return fail(e, LSS_EINVAL, "draft: bad arguments");
   if (quant == 2 && e->w8.empty()) return fail(e, LSS_ESTATE, "draft: int8 weights not attached (lss_attach_w8)");
+  if (e->tree > 0) return fail(e, LSS_ESTATE, "draft: a tree window is pending");
   if (k > 0 && !tokens_out) return fail(e, LSS_EINVAL, "draft: null tokens_out");
   const int win_cap = std::min(kWinMax, c.max_rows - 1);
   if (e->win + k > win_cap) return fail(e, LSS_ECAPACITY, "draft: window would exceed its capacity");
@@ -973,6 +980,39 @@ int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, floa
   return LSS_OK;
 }
 
+int lss_draft_tree(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t B, int32_t* tokens_out) {
+  if (!e) return LSS_EINVAL;
+  const GemvScope gv(e);
+  const auto& c = e->cfg;
+  if (!e->have_seq || e->pending_accept || e->win != 0)
+    return fail(e, LSS_ESTATE, "draft_tree: needs a prefilled sequence, no pending accept and an empty window");
+  if (!mask || !tokens_out || B < 1 || B > TOPB_MAX || B > c.vocab || quant < 0 || quant > 2)
+    return fail(e, LSS_EINVAL, "draft_tree: bad arguments (1 <= B <= 8)");
+  if (e->inv_t > 0.f) return fail(e, LSS_EINVAL, "draft_tree: tree acceptance is greedy; sampling is on");
+  if (quant == 2 && e->w8.empty()) return fail(e, LSS_ESTATE, "draft_tree: int8 weights not attached");
+  if (B + 1 > c.max_rows || B > std::min(kWinMax, c.max_rows - 1)) return fail(e, LSS_ECAPACITY, "draft_tree: B + 1 > max_rows");
+  if (e->p + B + 1 > c.max_seq) return fail(e, LSS_ECAPACITY, "draft_tree: KV capacity exceeded");
+  // the draft row of the pending token (slot 0, position p), then its top B
+  embed(e, e->tok, 1, hs_row(e, 0, 0), next_gain(e, mask, -1));
+  const float* h = hs_row(e, 0, 0);
+  for (int l = 0; l < c.n_layers; ++l) {
+    if (mask[l]) continue;
+    e->valid[l] |= 1u;
+    layer_forward(e, l, 1, h, e->xa, e->pa, hs_row(e, l + 1, 0), next_gain(e, mask, l), MODE_DRAFT, e->p, quant);
+    h = hs_row(e, l + 1, 0);
+  }
+  head(e, 0, 1, 0, e->p, true);
+  hipLaunchKernelGGL(k_topb, dim3(1), dim3(TOPB_THREADS), 0, e->stream, (const float*)e->logits, c.vocab, B, e->tok);
+  int rc = check_launch(e, "draft_tree");
+  if (rc) return rc;
+  HIPCHK(hipMemcpyAsync(e->hstage, e->tok + 1, sizeof(int32_t) * B, hipMemcpyDeviceToHost, e->stream));
+  HIPCHK(hipStreamSynchronize(e->stream));
+  std::memcpy(tokens_out, e->hstage, sizeof(int32_t) * B);
+  e->win = B;
+  e->tree = B;
+  return LSS_OK;
+}
+
 int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k) {
   if (!e) return LSS_EINVAL;
   const GemvScope gv(e);
@@ -993,6 +1033,27 @@ int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k) {
     HIPCHK(hipMemcpyAsync(e->tok + 1, e->hstage, sizeof(int32_t) * k, hipMemcpyHostToDevice, e->stream));
   }
   const int M = k + 1;
+  if (e->tree > 0) {                                   // width-B tree: one pass, tree mask
+    if (drafts) return fail(e, LSS_EINVAL, "verify: a tree window is pending; verify it with drafts == NULL");
+    forward_rows(e, e->tok, M, e->p, MODE_TREE);
+    head(e, 0, M, 0, e->p, false);
+    hipLaunchKernelGGL(k_accept_tree, dim3(1), dim3(1), 0, e->stream, e->res, k, e->tok);
+    const dim3 fg(c.n_layers, c.n_kv_heads);
+    if (e->kv16)
+      hipLaunchKernelGGL(k_tree_kv_fix<uint16_t>, fg, dim3(128), 0, e->stream, (const HeadRes*)e->res,
+                         (uint16_t*)e->kc, (uint16_t*)e->vc, c.n_kv_heads, c.max_seq, c.head_dim, e->p);
+    else
+      hipLaunchKernelGGL(k_tree_kv_fix<float>, fg, dim3(128), 0, e->stream, (const HeadRes*)e->res, (float*)e->kc,
+                         (float*)e->vc, c.n_kv_heads, c.max_seq, c.head_dim, e->p);
+    hipLaunchKernelGGL(k_gather_target, dim3(c.n_layers + 1), dim3(256), 0, e->stream, e->hs, c.max_rows,
+                       c.d_model, (const HeadRes*)e->res, 0, e->target);
+    const int rc = check_launch(e, "verify");
+    if (rc) return rc;
+    e->win = k;
+    e->verify_rows = M;
+    e->pending_accept = true;
+    return LSS_OK;
+  }
   forward_rows(e, e->tok, M, e->p);
   head(e, 0, M, 0, e->p, false);
   if (samp && k > 0) {
@@ -1030,6 +1091,7 @@ int lss_accept_and_rollback(lss_engine* e, int32_t* n_accepted, int32_t* bonus, 
   e->have_target = true;
   e->p += n + 1;
   e->win = 0;
+  e->tree = 0;
   std::fill(e->valid.begin(), e->valid.end(), 0u);
   e->pending_accept = false;
   return LSS_OK;
@@ -1140,6 +1202,9 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
   if (pol->mode != LSS_MODE_AR && (pol->k_max < 0 || pol->k_max > std::min(kWinMax, c.max_rows - 1)))
     return fail(e, LSS_EINVAL, "generate: k_max out of range");
   if (pol->mode == LSS_MODE_STATIC && !pol->static_mask) return fail(e, LSS_EINVAL, "generate: static mask missing");
+  if (pol->tree_width < 0 || pol->tree_width > TOPB_MAX ||
+      (pol->tree_width > 0 && pol->mode != LSS_MODE_STATIC && pol->mode != LSS_MODE_DP))
+    return fail(e, LSS_EINVAL, "generate: tree_width must be 0..8 and needs the static or DP mode");
   if ((pol->mode == LSS_MODE_DP || pol->mode == LSS_MODE_CASCADE) && pol->interval < 1)
     return fail(e, LSS_EINVAL, "generate: interval < 1");
   if (pol->mode == LSS_MODE_CASCADE) {
@@ -1185,7 +1250,12 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
   while (emitted < n_gen) {
     const int budget = n_gen - emitted - 1;
     slot_levels.clear();
-    if (pol->mode == LSS_MODE_STATIC || pol->mode == LSS_MODE_DP) {
+    if ((pol->mode == LSS_MODE_STATIC || pol->mode == LSS_MODE_DP) && pol->tree_width > 0) {
+      if (budget > 0) {
+        rc = lss_draft_tree(e, masks[0].data(), pol->quant, pol->tree_width, toks.data());
+        if (rc) return rc;
+      }
+    } else if (pol->mode == LSS_MODE_STATIC || pol->mode == LSS_MODE_DP) {
       const int k = std::min(pol->k_max, budget);
       if (k > 0) {
         int kd = 0;

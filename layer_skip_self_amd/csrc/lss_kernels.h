@@ -1050,6 +1050,13 @@ __global__ __launch_bounds__(G8_THREADS) void k_gemv8(GemmArgs ga) {
 // itself (rounded to the cache type), and query block 0 of the chunk that
 // holds them writes them to the cache.  Layer-selection launches write
 // nothing; each row's own key/value enters the merge directly.
+//
+// Tree launches (a width-B token tree): row 0 is the pending token at pos0;
+// rows 1..B are sibling candidates of position pos0 + 1, rotated there and
+// written to cache slots pos0 + m.  Row m >= 1 sees u < pos0 + 2 with slot
+// pos0 + 1 holding its own key and value (a per-row substitute inside that
+// slot's chunk), so its scores, chunk partials and merge are those of the
+// plain step at pos0 + 1 after that candidate, bit for bit.
 #define ATT_CH 64
 #define ATT_QB 32
 #define ATT_THREADS 256
@@ -1063,6 +1070,7 @@ struct AttnArgs {
   int lim_base, lim_step, wbase;
   uint32_t wmask;
   int self_kv;                     // 1: layer-selection rows (own key/value, no cache write)
+  int tree;                        // 1: tree launch (row 0 pending token, rows >= 1 candidates)
   int nch, nz;                     // key chunks, query blocks in this launch
   float* part;                     // [Hkv][nz_max][nch_max][QB][hd + 2]
   int nz_max, nch_max;
@@ -1083,6 +1091,11 @@ __device__ __forceinline__ float rope_elem(const float* x, const float2* cs, int
   }
   const float2 c = cs[i - half];
   return __fadd_rn(__fmul_rn(x[i], c.x), __fmul_rn(x[i - half], c.y));
+}
+
+// rotary position of launch row m (tree launches: all candidates at pos0 + 1)
+__device__ __forceinline__ int att_row_pos(const AttnArgs& a, int m) {
+  return a.tree ? a.pos0 + (m > 0 ? 1 : 0) : a.pos0 + m * a.pos_step;
 }
 
 // 4 consecutive cache elements as float
@@ -1134,19 +1147,23 @@ __device__ __forceinline__ void att_new_rows(float (*t)[HD + 1], const AttnArgs&
   for (int i = threadIdx.x; i < (r1 - r0) * HD; i += ATT_THREADS) {
     const int pos = r0 + i / HD, dd = i % HD;
     const float* x = a.qkv + (size_t)(pos - a.pos0) * a.ldqkv + (size_t)off * HD;
-    float v = is_v ? x[dd] : rope_elem(x, a.cs + (size_t)pos * (HD / 2), dd, HD / 2);
+    const int rp = att_row_pos(a, pos - a.pos0);
+    float v = is_v ? x[dd] : rope_elem(x, a.cs + (size_t)rp * (HD / 2), dd, HD / 2);
     v = kv_round<KT>(v);
     if (z == 0) st_elem<KT>(cache, (size_t)pos * HD + dd, v);
     t[pos - u0][dd] = v;
   }
 }
 
-template <typename KT, typename WT, int HD>
+#define ATT_TREE_MAX 8
+template <typename KT, typename WT, int HD, bool TREE = false>
 __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
   __shared__ float kv_s[ATT_CH][HD + 1];
   __shared__ float q_s[ATT_QB][HD];
   __shared__ float p_s[ATT_QB][ATT_CH];
   __shared__ float st_s[ATT_QB][2];
+  __shared__ float own_s[TREE ? ATT_TREE_MAX + 1 : 1][TREE ? HD : 1];   // tree: candidates' own keys
+  __shared__ float own_v[TREE ? ATT_TREE_MAX + 1 : 1][TREE ? HD : 1];   // and values
   const int c = blockIdx.x, kh = blockIdx.y, z = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int nq = G * a.M;
@@ -1165,10 +1182,26 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
     const int qi = i / HD, dd = i % HD;
     const int gq = q0 + qi;
     const int m = gq / G, h = kh * G + gq % G;
-    const int pos = a.pos0 + m * a.pos_step;
+    const int pos = att_row_pos(a, m);
     q_s[qi][dd] = rope_elem(a.qkv + (size_t)m * a.ldqkv + (size_t)h * HD, a.cs + (size_t)pos * (HD / 2), dd, HD / 2);
   }
   kt.store(kv_s);
+  // tree: the candidates' own keys and values (rotated at pos0 + 1, rounded
+  // to the cache type) for the chunk that holds slot pos0 + 1
+  const int uown = a.pos0 + 1 - u0;
+  const bool has_own = TREE && uown >= 0 && uown < ATT_CH;
+  if constexpr (TREE) {
+    if (has_own) {
+      const int nown = min(a.M - 1, ATT_TREE_MAX);
+      for (int i = tid; i < nown * HD; i += ATT_THREADS) {
+        const int m = 1 + i / HD, dd = i % HD;
+        const float* xk = a.qkv + (size_t)m * a.ldqkv + (size_t)(a.Hq + kh) * HD;
+        const float* xv = a.qkv + (size_t)m * a.ldqkv + (size_t)(a.Hq + a.Hkv + kh) * HD;
+        own_s[m][dd] = kv_round<KT>(rope_elem(xk, a.cs + (size_t)(a.pos0 + 1) * (HD / 2), dd, HD / 2));
+        own_v[m][dd] = kv_round<KT>(xv[dd]);
+      }
+    }
+  }
   __syncthreads();
   att_new_rows<KT, HD>(kv_s, a, kh, u0, z, false);
   __syncthreads();
@@ -1181,18 +1214,30 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
       const bool has_c = qc < nqb;
       const int qcc = has_c ? qc : qb;
       float da = 0.f, dc = 0.f;
+      if constexpr (TREE) {
+        // a candidate row's own slot reads its own key (same FMA order)
+        const int ma = (q0 + qb) / G, mc = (q0 + qcc) / G;
+        const float* ka = (has_own && u == uown && ma >= 1) ? own_s[ma] : kv_s[u];
+        const float* kc = (has_own && u == uown && mc >= 1) ? own_s[mc] : kv_s[u];
 #pragma unroll 8
-      for (int dd = 0; dd < HD; ++dd) {
-        const float kv = kv_s[u][dd];
-        da = fmaf(q_s[qb][dd], kv, da);
-        dc = fmaf(q_s[qcc][dd], kv, dc);
+        for (int dd = 0; dd < HD; ++dd) {
+          da = fmaf(q_s[qb][dd], ka[dd], da);
+          dc = fmaf(q_s[qcc][dd], kc[dd], dc);
+        }
+      } else {
+#pragma unroll 8
+        for (int dd = 0; dd < HD; ++dd) {
+          const float kv = kv_s[u][dd];
+          da = fmaf(q_s[qb][dd], kv, da);
+          dc = fmaf(q_s[qcc][dd], kv, dc);
+        }
       }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         if (h2 == 1 && !has_c) break;                  // wave-uniform
         const int qi = h2 ? qc : qb;
         const int m = (q0 + qi) / G;
-        const int lim = a.lim_base + m * a.lim_step;
+        const int lim = TREE ? a.lim_base + (m > 0 ? 1 : 0) : a.lim_base + m * a.lim_step;
         const int wo = pos - a.wbase;
         const bool vis = pos < lim || (wo >= 0 && wo < 32 && ((a.wmask >> wo) & 1u));
         const float s = (vis && pos < a.max_seq) ? __fmul_rn(h2 ? dc : da, a.scale) : -INFINITY;
@@ -1219,10 +1264,20 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
     const int qa = i0 / HD, da = i0 % HD;
     const int qc = has1 ? i1 / HD : qa, dc = has1 ? i1 % HD : da;
     float acc0 = 0.f, acc1 = 0.f;
+    if constexpr (TREE) {
+      const int ma = (q0 + qa) / G, mc = (q0 + qc) / G;
+      const int ua = (has_own && ma >= 1) ? uown : -1, uc = (has_own && mc >= 1) ? uown : -1;
 #pragma unroll 8
-    for (int u = 0; u < ATT_CH; ++u) {
-      acc0 = fmaf(p_s[qa][u], kv_s[u][da], acc0);
-      acc1 = fmaf(p_s[qc][u], kv_s[u][dc], acc1);
+      for (int u = 0; u < ATT_CH; ++u) {
+        acc0 = fmaf(p_s[qa][u], u == ua ? own_v[ma][da] : kv_s[u][da], acc0);
+        acc1 = fmaf(p_s[qc][u], u == uc ? own_v[mc][dc] : kv_s[u][dc], acc1);
+      }
+    } else {
+#pragma unroll 8
+      for (int u = 0; u < ATT_CH; ++u) {
+        acc0 = fmaf(p_s[qa][u], kv_s[u][da], acc0);
+        acc1 = fmaf(p_s[qc][u], kv_s[u][dc], acc1);
+      }
     }
     float* o0 = part + (size_t)qa * (HD + 2);
     o0[da] = acc0;
@@ -1309,6 +1364,7 @@ struct HeadRes {                 // device result block, mirrored to the host
   float lse[64];                 // sampling: log-sum-exp of z / T of each verify row
   float dlse[64];                // sampling: the same for each draft slot
   int32_t emit[64];              // tokens a verify round emits: accepted drafts, then the bonus
+  int32_t trow;                  // verify row whose states become the layer-selection target
 };
 
 // Per row: argmax over the tile records (lowest index on ties) and the
@@ -1373,9 +1429,94 @@ __global__ void k_accept(HeadRes* res, int k, int32_t* tok, int samp) {
   const int b = samp ? res->sample[n] : res->argmax[n];
   res->n = n;
   res->bonus = b;
+  res->trow = n;
   for (int i = 0; i < n; ++i) res->emit[i] = tok[i + 1];
   res->emit[n] = b;
   tok[0] = b;
+}
+
+// Top-B tokens of one logits row (B <= TOPB_MAX), largest first, equal
+// logits in index order: the tree draft's candidates, written to
+// tok[1..B].  Each thread keeps the best B of its entries (a sorted list,
+// compile-time indices), then B rounds of a block-wide maximum pick the
+// winners; the winning thread drops its head.
+#define TOPB_MAX 8
+#define TOPB_THREADS 1024
+__device__ __forceinline__ bool topb_before(float a, int ia, float b, int ib) {
+  return a > b || (a == b && ia < ib);
+}
+__global__ __launch_bounds__(TOPB_THREADS) void k_topb(const float* __restrict__ z, int V, int B,
+                                                      int32_t* __restrict__ tok) {
+  __shared__ float bm[TOPB_THREADS / 64];
+  __shared__ int bi[TOPB_THREADS / 64];
+  float lv[TOPB_MAX];
+  int li[TOPB_MAX];
+#pragma unroll
+  for (int j = 0; j < TOPB_MAX; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
+  for (int v = threadIdx.x; v < V; v += blockDim.x) {
+    float cv = z[v];
+    int ci = v;
+    if (cv != cv) cv = -INFINITY;                      // NaN ranks last
+#pragma unroll
+    for (int j = 0; j < TOPB_MAX; ++j)                 // insert: carry the smaller one down
+      if (topb_before(cv, ci, lv[j], li[j])) {
+        const float tv = lv[j];
+        const int ti = li[j];
+        lv[j] = cv; li[j] = ci;
+        cv = tv; ci = ti;
+      }
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int r = 0; r < B; ++r) {
+    float mx = lv[0];
+    int idx = li[0];
+    argmax_wave(mx, idx);
+    if (lane == 0) { bm[wv] = mx; bi[wv] = idx; }
+    __syncthreads();
+    mx = bm[0]; idx = bi[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) argmax_merge(mx, idx, bm[i], bi[i]);
+    __syncthreads();
+    if (threadIdx.x == 0) tok[1 + r] = (idx >= 0 && idx < V) ? idx : 0;
+    if (li[0] == idx) {                                // the owner drops its head
+#pragma unroll
+      for (int j = 0; j + 1 < TOPB_MAX; ++j) { lv[j] = lv[j + 1]; li[j] = li[j + 1]; }
+      lv[TOPB_MAX - 1] = -INFINITY;
+      li[TOPB_MAX - 1] = 0x7fffffff;
+    }
+  }
+}
+
+// Greedy acceptance of a width-B tree (rows: pending token, candidates
+// tok[1..B] of one position): a_0 = argmax of row 0; the candidate equal to
+// a_0 (the lowest such row) is accepted with its row's argmax as the bonus
+// (n = 1); otherwise n = 0 and the bonus is a_0.  trow = the accepted row.
+__global__ void k_accept_tree(HeadRes* res, int B, int32_t* tok) {
+  const int a0 = res->argmax[0];
+  int row = 0;
+  for (int i = 1; i <= B && !row; ++i)
+    if (tok[i] == a0) row = i;
+  const int b = row ? res->argmax[row] : a0;
+  res->n = row ? 1 : 0;
+  res->bonus = b;
+  res->trow = row;
+  res->emit[0] = a0;
+  res->emit[1] = b;
+  tok[0] = b;
+}
+
+// After a tree round: the accepted candidate's keys and values (cache slot
+// p + trow, rotated at p + 1) become slot p + 1's, for every layer.  Nothing
+// to do when no candidate or the first one was accepted.
+template <typename KT>
+__global__ void k_tree_kv_fix(const HeadRes* __restrict__ res, KT* kc, KT* vc, int Hkv, int max_seq, int hd,
+                              int p) {
+  const int row = res->trow;
+  if (row < 2) return;
+  const size_t base = (size_t)blockIdx.x * Hkv * max_seq * hd + (size_t)blockIdx.y * max_seq * hd;
+  for (int d = threadIdx.x; d < hd; d += blockDim.x) {
+    kc[base + (size_t)(p + 1) * hd + d] = kc[base + (size_t)(p + row) * hd + d];
+    vc[base + (size_t)(p + 1) * hd + d] = vc[base + (size_t)(p + row) * hd + d];
+  }
 }
 
 // Speculative-sampling acceptance (the rule that keeps the full model's
@@ -1494,18 +1635,19 @@ __global__ __launch_bounds__(SPEC_FIN_THREADS) void k_spec_final(const float* __
   if (threadIdx.x == 0) {
     res->n = i;
     res->bonus = b;
+    res->trow = i;
     for (int j = 0; j < i; ++j) res->emit[j] = tok[j + 1];
     res->emit[i] = b;
     tok[0] = b;
   }
 }
 
-// Copy the residual states of verify row res->n (or `row` if res == nullptr)
-// into the layer-selection target [L+1][d].
+// Copy the residual states of verify row res->trow (or `row` if res ==
+// nullptr) into the layer-selection target [L+1][d].
 __global__ void k_gather_target(const float* __restrict__ hs, int rows_stride, int d, const HeadRes* res,
                                 int row, float* __restrict__ target) {
   const int l = blockIdx.x;
-  const int rr = res ? res->n : row;
+  const int rr = res ? res->trow : row;
   const float* src = hs + ((size_t)l * rows_stride + rr) * d;
   for (int i = threadIdx.x; i < d; i += blockDim.x) target[(size_t)l * d + i] = src[i];
 }

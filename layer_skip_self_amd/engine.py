@@ -114,6 +114,14 @@ class Engine:
                                        out.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(done)), "lss_draft")
         return out[:done.value].tolist()
 
+    def draft_tree(self, skip_mask, quant=0, B=2):
+        """Width-B, depth-1 token tree: the draft's B most likely next tokens."""
+        m, mp = _u8(skip_mask)
+        out = np.zeros(B, np.int32)
+        self._check(self.lib.lss_draft_tree(self.h, mp, int(quant), int(B),
+                                            out.ctypes.data_as(C.POINTER(C.c_int32))), "lss_draft_tree")
+        return out.tolist()
+
     def verify(self, drafts=None, k=None):
         if drafts is None:
             self._check(self.lib.lss_verify(self.h, None, int(k)), "lss_verify")
@@ -241,6 +249,7 @@ def make_policy(policy, n_layers):
     beta = policy.get("beta", (0.0, 0.0, 0.0))
     for i in range(3):
         pol.beta[i] = float(beta[i])
+    pol.tree_width = int(policy.get("tree_width", 0))
     return pol
 
 

@@ -477,7 +477,8 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None, state
             n, bonus, emitted = accept_tree(st, logits, states, cands, kv)
             out += emitted
             rounds += 1
-            rec = {"k": len(cands), "n": n, "bonus": bonus, "tree": True}
+            rec = {"k": len(cands), "n": n, "bonus": bonus, "tree": True,
+                   "row": cands.index(emitted[0]) + 1 if n else 0}
             records.append(rec)
             if policy.dp_skip is not None and rounds % policy.interval == 0:
                 masks = select_masks()

@@ -243,3 +243,15 @@ def test_quantized_draft_layers_vs_oracle_and_lossless_8b(gpu8b, oracle8b, quant
     toks, st8 = eng.generate(prompt, G, dict(BENCH_POLICY, quant=quant))
     assert toks == ar
     assert 0 <= st8["accepted"] <= st8["drafted"]
+
+
+def test_tree_drafting_lossless_8b(gpu8b):
+    """Width-4 token trees with the headline DP draft: speculative output
+    equal to greedy output bit for bit (each candidate row is the greedy step
+    after it, own key included)."""
+    eng, prompt = gpu8b["eng"], gpu8b["prompt"]
+    G = 48
+    ar, _ = eng.generate(prompt, G, {"mode": "ar"})
+    toks, st = eng.generate(prompt, G, {"mode": "dp", "k_max": 1, "n_skip": 16, "interval": 32, "tree_width": 4})
+    print(f"tree width 4: {st['rounds']} rounds, {st['accepted']} accepted")
+    assert toks == ar
