@@ -73,6 +73,12 @@ WORKLOADS = {
                                    "quant": 2},
                            desc="Llama-3-8B shape, prompt 1024, 512 generated, CLaSp DP skip 16 every 32 rounds, "
                                 "exit threshold 0.7, K <= 8, W8A8 draft (int8 weight copy + int8 activations)"),
+    # Token trees of width 4 (depth 1) with the headline DP draft: the draft's
+    # 4 most likely next tokens verified in one pass with a tree mask.
+    "llama3_8b_tree": dict(shape="llama3_8b", prompt=1024, gen=512,
+                           policy={"mode": "dp", "k_max": 1, "n_skip": 16, "interval": 32, "tree_width": 4},
+                           desc="Llama-3-8B shape, prompt 1024, 512 generated, CLaSp DP skip 16 every 32 rounds, "
+                                "token tree of width 4 and depth 1 per round"),
     "cascade_8b": dict(shape="llama3_8b", prompt=(128, 512, 2048), gen=256,
                        policy={"mode": "cascade", "k_max": 8, "interval": 32,
                                "levels": [(22, 4, False), (10, 0, True), (0, 0, True)]},
@@ -103,7 +109,8 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
                         quant=int(policy.get("quant", 0)),
                         cascade=list(policy["levels"]) if policy["mode"] == "cascade" else None,
                         latency_beta=tuple(policy.get("beta", (1.0, 0.0, 1.0))),
-                        temperature=float(policy.get("temperature", 0.0)), seed=int(policy.get("seed", 0)))
+                        temperature=float(policy.get("temperature", 0.0)), seed=int(policy.get("seed", 0)),
+                        tree_width=int(policy.get("tree_width", 0)))
     sample = np.asarray(prompt[:n_prompt])
     t0 = time.perf_counter()
     toks, recs = oracle.speculative_generate(model, sample, n_tokens, pol)
