@@ -241,6 +241,17 @@ int lss_latency_fit(const double* samples, int32_t n, double* beta_out);
 int lss_profile_kernel(lss_engine* e, int32_t epilogue, int32_t rows, int32_t enable);
 int lss_profile_read(lss_engine* e, double* total_ms, int64_t* launches, int64_t* bytes);
 
+/* Grid of the decode GEMV (the vector-ALU projection of draft, greedy and
+ * verify rows): wgs_per_cu = 0 launches one workgroup per weight tile;
+ * wgs_per_cu > 0 launches at most that many workgroups per compute unit
+ * (capped by the kernel's occupancy), each walking a contiguous range of
+ * tiles with its weight loads kept in flight across tile boundaries.  The
+ * arithmetic of every output is the same under either grid, so results are
+ * identical bit for bit; only the time changes.  The default is the tile
+ * walk with 1 workgroup per compute unit.  LSS_EINVAL for a negative value
+ * or a value above 8. */
+int lss_set_gemv_grid(lss_engine* e, int32_t wgs_per_cu);
+
 /* Stand-alone dynamic per-token int8 quantization (CAS-Spec blog section
  * 2.1): for each of `rows` rows of x_dev[rows][n] (float32), codes q_dev
  * [rows][n] = clamp(rint(x * fl(127/amax)), -127, 127) and scale_dev[rows]

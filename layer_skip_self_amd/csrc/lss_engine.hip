@@ -166,6 +166,12 @@ enum RowMode { MODE_CAUSAL = 0, MODE_DRAFT = 1, MODE_DP = 2, MODE_TREE = 3 };
 
 }  // namespace
 
+// decode-GEMV grid policy of an engine (lss_set_gemv_grid)
+#define LSS_GEMV_WGS_PER_CU 1
+struct GemvLaunch {
+  int ncu = 0, gmax_cu = 0;   // compute units; workgroups per unit (0: one per tile)
+};
+
 struct lss_engine {
   lss_config cfg{};
   Layout lay{};
@@ -210,6 +216,7 @@ struct lss_engine {
   // (one arithmetic for every row count); prefill and layer selection
   // through the MFMA kernels
   bool gemv = false;
+  GemvLaunch gvl;
   // kernel timing (lss_profile_kernel)
   int prof_epi = -1, prof_rows = 0;
   std::vector<hipEvent_t> ev_start, ev_stop;
@@ -298,42 +305,69 @@ int gemv_cap(int K, int wbytes) {
   return ncw == 1 ? GV_MB_MAX : std::max(1, std::min(4, GV_ACT_MAX / ncw));
 }
 
-// 8-row tiles where the epilogue has no per-16-column partials (more
-// workgroups, so their tails overlap other workgroups' loads)
-template <int EPI> constexpr int gemv_tile() { return (EPI == EPI_STORE || EPI == EPI_SWIGLU) ? 8 : 16; }
+// 16 weight rows per tile (8 for gate/up, whose steps read two matrices)
+template <int EPI> constexpr int gemv_tile() { return EPI == EPI_SWIGLU ? 8 : 16; }
+
+// Workgroups of one decode-GEMV launch.  gmax_cu = 0: one per tile.
+// Otherwise, with at most gmax = gmax_cu workgroups per compute unit (capped
+// by the kernel's occupancy): launches of at most 2 gmax tiles keep one
+// workgroup per tile (a walk of two tiles would leave compute units idle);
+// larger ones take ceil(tiles / ceil(tiles / gmax)) workgroups, each walking
+// the same number of tiles give or take one.
+int gemv_grid(int ntile, int ncu, int gmax_cu, int occ) {
+  if (gmax_cu <= 0 || ncu <= 0) return ntile;
+  const int gmax = ncu * std::max(1, std::min(gmax_cu, occ));
+  if (ntile <= 2 * gmax) return ntile;
+  const int per = (ntile + gmax - 1) / gmax;
+  return (ntile + per - 1) / per;
+}
+
+template <typename WT, int MB, int NCW, int EPI, int TR>
+void gemv_go(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  static const int occ = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_gemv<WT, MB, NCW, EPI, TR>, 64 * GV_WAVES, 0) !=
+            hipSuccess || nb < 1)
+      nb = 1;
+    return nb;
+  }();
+  const int ntile = (g.N + TR - 1) / TR;
+  const dim3 grid(gemv_grid(ntile, gl.ncu, gl.gmax_cu, occ)), block(64 * GV_WAVES);
+  launch_k(k_gemv<WT, MB, NCW, EPI, TR>, grid, block, 0, s, t0, t1, g);
+}
 
 template <typename WT, int EPI, int NCW>
-void gemv_launch(const GemmArgs& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+void gemv_launch(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   constexpr int TR = gemv_tile<EPI>();
-  const dim3 grid((g.N + TR - 1) / TR), block(64 * GV_WAVES);
   if constexpr (NCW == 1) {
-    if (g.M == 1) launch_k(k_gemv<WT, 1, 1, EPI, TR>, grid, block, 0, s, t0, t1, g);
-    else if (g.M == 2) launch_k(k_gemv<WT, 2, 1, EPI, TR>, grid, block, 0, s, t0, t1, g);
-    else if (g.M <= 4) launch_k(k_gemv<WT, 4, 1, EPI, TR>, grid, block, 0, s, t0, t1, g);
-    else launch_k(k_gemv<WT, 8, 1, EPI, TR>, grid, block, 0, s, t0, t1, g);
+    if (g.M == 1) gemv_go<WT, 1, 1, EPI, TR>(g, gl, s, t0, t1);
+    else if (g.M == 2) gemv_go<WT, 2, 1, EPI, TR>(g, gl, s, t0, t1);
+    else if (g.M <= 4) gemv_go<WT, 4, 1, EPI, TR>(g, gl, s, t0, t1);
+    else gemv_go<WT, 8, 1, EPI, TR>(g, gl, s, t0, t1);
   } else if constexpr (NCW == 2 || NCW == 4) {
-    if (g.M == 1) launch_k(k_gemv<WT, 1, NCW, EPI, TR>, grid, block, 0, s, t0, t1, g);
-    else if (g.M == 2) launch_k(k_gemv<WT, 2, NCW, EPI, TR>, grid, block, 0, s, t0, t1, g);
-    else launch_k(k_gemv<WT, 4, NCW, EPI, TR>, grid, block, 0, s, t0, t1, g);
+    if (g.M == 1) gemv_go<WT, 1, NCW, EPI, TR>(g, gl, s, t0, t1);
+    else if (g.M == 2) gemv_go<WT, 2, NCW, EPI, TR>(g, gl, s, t0, t1);
+    else gemv_go<WT, 4, NCW, EPI, TR>(g, gl, s, t0, t1);
   } else {
-    if (g.M == 1) launch_k(k_gemv<WT, 1, 8, EPI, TR>, grid, block, 0, s, t0, t1, g);
-    else launch_k(k_gemv<WT, 2, 8, EPI, TR>, grid, block, 0, s, t0, t1, g);
+    if (g.M == 1) gemv_go<WT, 1, 8, EPI, TR>(g, gl, s, t0, t1);
+    else gemv_go<WT, 2, 8, EPI, TR>(g, gl, s, t0, t1);
   }
 }
 
 // M rows in launches of at most gemv_cap rows (each row's arithmetic is the
 // same in any launch)
 template <typename WT, int EPI>
-void gemv_mt(const GemmArgs& ga, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr) {
+void gemv_mt(const GemmArgs& ga, const GemvLaunch& gl, hipStream_t s, hipEvent_t t0 = nullptr,
+             hipEvent_t t1 = nullptr) {
   const int ncw = gemv_ncw(ga.K, sizeof(WT));
   const int cap = gemv_cap(ga.K, sizeof(WT));
   for (int r0 = 0; r0 < ga.M; r0 += cap) {
     const int Mg = std::min(cap, ga.M - r0);
     const GemmArgs g = (r0 == 0 && Mg == ga.M) ? ga : rows_from(ga, r0, Mg);
-    if (ncw == 1) gemv_launch<WT, EPI, 1>(g, s, t0, t1);
-    else if (ncw == 2) gemv_launch<WT, EPI, 2>(g, s, t0, t1);
-    else if (ncw == 4) gemv_launch<WT, EPI, 4>(g, s, t0, t1);
-    else gemv_launch<WT, EPI, 8>(g, s, t0, t1);
+    if (ncw == 1) gemv_launch<WT, EPI, 1>(g, gl, s, t0, t1);
+    else if (ncw == 2) gemv_launch<WT, EPI, 2>(g, gl, s, t0, t1);
+    else if (ncw == 4) gemv_launch<WT, EPI, 4>(g, gl, s, t0, t1);
+    else gemv_launch<WT, EPI, 8>(g, gl, s, t0, t1);
   }
 }
 
@@ -388,8 +422,8 @@ void gemm(lss_engine* e, const GemmArgs& ga) {
   }
   hipEvent_t t0 = prof ? e->ev_start[e->ev_used] : nullptr, t1 = prof ? e->ev_stop[e->ev_used] : nullptr;
   if (vec) {
-    if (e->bf16) gemv_mt<uint16_t, EPI>(ga, e->stream, t0, t1);
-    else gemv_mt<float, EPI>(ga, e->stream, t0, t1);
+    if (e->bf16) gemv_mt<uint16_t, EPI>(ga, e->gvl, e->stream, t0, t1);
+    else gemv_mt<float, EPI>(ga, e->gvl, e->stream, t0, t1);
   } else {
     if (e->bf16) pgemm<uint16_t, EPI>(e, ga, t0, t1);
     else pgemm<float, EPI>(e, ga, t0, t1);
@@ -721,6 +755,13 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
   e->stream = (hipStream_t)hip_stream;
   e->bf16 = cfg->dtype == LSS_BF16;
   e->kv16 = cfg->kv_dtype == LSS_BF16;
+  {  // decode-GEMV grid: the compute units of the current device
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      e->gvl.ncu = ncu;
+    e->gvl.gmax_cu = LSS_GEMV_WGS_PER_CU;
+  }
   e->embed = tensors[0];
   e->final_norm = (const float*)tensors[1];
   e->lm_head = tensors[2];
@@ -891,6 +932,13 @@ int lss_set_sampling(lss_engine* e, float temperature, uint64_t seed) {
   if (temperature > 0.f && !std::isfinite(inv)) return fail(e, LSS_EINVAL, "set_sampling: temperature too small");
   e->inv_t = inv;
   e->seed = seed;
+  return LSS_OK;
+}
+
+int lss_set_gemv_grid(lss_engine* e, int32_t wgs_per_cu) {
+  if (!e) return LSS_EINVAL;
+  if (wgs_per_cu < 0 || wgs_per_cu > 8) return fail(e, LSS_EINVAL, "set_gemv_grid: wgs_per_cu must be in [0, 8]");
+  e->gvl.gmax_cu = wgs_per_cu;
   return LSS_OK;
 }
 

@@ -49,6 +49,7 @@ template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
 #define LSS_DPP_XOR2 0x4E     // quad_perm [2, 3, 0, 1]
 #define LSS_DPP_HMIRROR 0x141 // row_half_mirror
 #define LSS_DPP_MIRROR 0x140  // row_mirror
+#define LSS_DPP_ROR8 0x128    // row_ror:8 (lane i and i ^ 8 of a row)
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
@@ -70,6 +71,73 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_t<LSS_DPP_HMIRROR>(v));
   v = fmaxf(v, dpp_t<LSS_DPP_MIRROR>(v));
   return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+// Transposed wave sums: the totals over the 64 lanes of V values per lane
+// (V a power of two, 8 <= V <= 64) with the pairing tree of wave_sum, level s
+// adding lanes that differ in bit s of the lane id: quad_perm xor 1 and
+// xor 2, row_half_mirror (flips bits 0-2), row_ror:8, permlane16_swap,
+// permlane32_swap.  While a lane still holds more than one value, a level
+// halves the list: the lane keeps one half and adds its partner's copy of
+// that half (one add per kept value instead of a full tree per value).  The
+// half a lane keeps at level s is k_s = bit s of its id, except
+// k_0 = b0 ^ b2 and k_1 = b1 ^ b2, so that the lanes row_half_mirror pairs
+// hold the same values.  Every add has the operands of the matching add in
+// wave_sum, so each total is the same bit for bit.  Afterwards v[0] of
+// lane l is the total of value wst_index<V>(l); lanes 0 .. V - 1 hold every
+// value once.
+template <int V> __device__ __forceinline__ int wst_index(int l) {
+  const int b2 = (l >> 2) & 1;
+  const int k[6] = {(l & 1) ^ b2, ((l >> 1) & 1) ^ b2, b2, (l >> 3) & 1, (l >> 4) & 1, (l >> 5) & 1};
+  int j = 0, h = V;
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    if (h > 1) {
+      h >>= 1;
+      j += k[s] * h;
+    }
+  }
+  return j;
+}
+template <int CTRL, int N, int V> __device__ __forceinline__ void wst_dpp(float (&v)[V], bool k) {
+  if constexpr (N == 1) {
+    v[0] = __fadd_rn(v[0], dpp_t<CTRL>(v[0]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float a = v[i], b = v[i + N / 2];
+      v[i] = __fadd_rn(k ? b : a, dpp_t<CTRL>(k ? a : b));
+    }
+  }
+}
+template <bool P32> __device__ __forceinline__ float swap_add(float a, float b) {
+  if constexpr (P32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __fadd_rn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __fadd_rn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+}
+// levels 4 / 5: swap(a, b) leaves a's rows (halves) with an even bit 4 (5)
+// and b's rows with an odd one; a + b is then the kept half's partial sum
+template <int N, int V, bool P32> __device__ __forceinline__ void wst_swap(float (&v)[V]) {
+  if constexpr (N == 1) {
+    v[0] = swap_add<P32>(v[0], v[0]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) v[i] = swap_add<P32>(v[i], v[i + N / 2]);
+  }
+}
+template <int V> __device__ __forceinline__ void wave_sum_t(float (&v)[V]) {
+  static_assert(V >= 8 && V <= 64 && (V & (V - 1)) == 0, "8 .. 64 values, a power of two");
+  const int l = threadIdx.x & 63;
+  const int b2 = (l >> 2) & 1;
+  wst_dpp<LSS_DPP_XOR1, V, V>(v, ((l & 1) ^ b2) != 0);
+  wst_dpp<LSS_DPP_XOR2, V / 2, V>(v, (((l >> 1) & 1) ^ b2) != 0);
+  wst_dpp<LSS_DPP_HMIRROR, V / 4, V>(v, b2 != 0);
+  wst_dpp<LSS_DPP_ROR8, V / 8, V>(v, ((l >> 3) & 1) != 0);
+  wst_swap<(V >= 32 ? V / 16 : 1), V, false>(v);
+  wst_swap<(V >= 64 ? V / 32 : 1), V, true>(v);
 }
 // (value, index) maximum with the lowest index on ties: a total order, so the
 // result does not depend on the reduction tree
@@ -401,11 +469,13 @@ __device__ __forceinline__ void load_w(uint4 (&w)[GEMM_U], const WT* row, int kb
 
 // One output element (row m, column n) of a projection.  y (and u, the
 // up-projection of SWIGLU) carry the row scale already.  The 16 lanes of an
-// aligned lane group hold columns 16 b .. 16 b + 15 (b = blockIdx.x) of the
-// same row and call this together: RESID's partial sum of squares and
-// LOGITS' tile max / argmax / sum of exponentials are fixed 16-lane trees.
+// aligned lane group hold columns 16 b .. 16 b + 15 of the same row (b = t16,
+// one of n16 such column tiles) and call this together: RESID's partial sum
+// of squares and LOGITS' tile max / argmax / sum of exponentials are fixed
+// 16-lane trees.
 template <typename WT, int EPI>
-__device__ __forceinline__ void proj_out(const GemmArgs& ga, int m, int M, int n, int cl, float y, float u) {
+__device__ __forceinline__ void proj_out(const GemmArgs& ga, int m, int M, int n, int cl, int t16, int n16, float y,
+                                         float u) {
   const bool ok = (m < M) && (n < ga.N);
   if constexpr (EPI == EPI_STORE) {
     if (ok) ga.Y[(size_t)m * ga.ldy + n] = y;
@@ -415,7 +485,7 @@ __device__ __forceinline__ void proj_out(const GemmArgs& ga, int m, int M, int n
     if (ga.xo && ok) AF<WT>::store(ga.xo, (size_t)m * ga.ldo, n, ga.go ? __fmul_rn(h, ga.go[n]) : h);
     if (ga.po) {
       const float s2 = sum16(__fmul_rn(h, h));
-      if (cl == 0 && m < M) ga.po[(size_t)m * gridDim.x + blockIdx.x] = s2;
+      if (cl == 0 && m < M) ga.po[(size_t)m * n16 + t16] = s2;
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     const float sg = __fdiv_rn(y, __fadd_rn(1.0f, expf(-y)));
@@ -440,7 +510,7 @@ __device__ __forceinline__ void proj_out(const GemmArgs& ga, int m, int M, int n
       argmax16(gk, gi);
     }
     if (cl == 0 && m < M) {
-      float* p = ga.part + ((size_t)m * gridDim.x + blockIdx.x) * HEAD_PART;
+      float* p = ga.part + ((size_t)m * n16 + t16) * HEAD_PART;
       p[0] = mx;
       p[1] = __int_as_float(idx);
       p[2] = e;
@@ -637,7 +707,7 @@ __global__ __launch_bounds__(256) void k_pepi(GemmArgs ga, const float* __restri
 #pragma unroll
       for (int q = 0; q < NACC; ++q) y[q] = __fmul_rn(y[q], ga.xs[mm]);
     }
-    proj_out<WT, EPI>(ga, m, M, n, i, y[0], NACC == 2 ? y[NACC - 1] : 0.f);
+    proj_out<WT, EPI>(ga, m, M, n, i, blockIdx.x, gridDim.x, y[0], NACC == 2 ? y[NACC - 1] : 0.f);
   }
 }
 
@@ -647,12 +717,18 @@ __global__ __launch_bounds__(256) void k_pepi(GemmArgs ga, const float* __restri
 // pattern is chosen for HBM: each load instruction of a wave reads one 1 KB
 // contiguous piece ("chunk") of one weight row (lane l: the 16 bytes at
 // offset 16 l), with nontemporal hints since the weights are read once.
-// A workgroup owns a tile of 16 rows of N (8 where the epilogue has no
-// per-16-column partials: store, SwiGLU); its GV_WAVES waves split the chunks
-// of K into contiguous ranges (wave w: chunks [w nc / W, (w + 1) nc / W)),
-// and each wave walks the tile's rows in groups of RG rows, the chunks of
-// its range inside each group, RG x NACC 1 KB loads per step with GV_ST
-// steps in flight.  A lane keeps the activation elements of its k in registers
+// The weight rows are cut into tiles of 16 rows (8 for gate/up, whose steps
+// read two matrices: two 4-row groups per tile, like the 8-row groups of a
+// 16-row tile), and a workgroup walks a contiguous
+// range of tiles (one tile when the grid has a workgroup per tile).  Its
+// GV_WAVES waves split the chunks of K into contiguous ranges (wave w: chunks
+// [w nc / W, (w + 1) nc / W)), and each wave walks every tile's rows in groups
+// of RG rows, the chunks of its range inside each group, RG x NACC 1 KB loads
+// per step with GV_ST steps in flight.  The steps run on across tile
+// boundaries: the first loads of the next tile are in flight while the wave
+// sums of the current tile go through LDS and its epilogue runs, so a
+// workgroup keeps the weight stream going from its first load to its last.
+// The activation rows are read once per workgroup.  A lane keeps the activation elements of its k in registers
 // (float32, converted once from the projection format) and multiplies them
 // with its 8 (bf16) / 4 (float32) weights in fused multiply-adds.
 //
@@ -661,7 +737,9 @@ __global__ __launch_bounds__(256) void k_pepi(GemmArgs ga, const float* __restri
 // its wave's range (ascending) and e ascending, the 64 lane values are
 // summed by the fixed tree of wave_sum, and the GV_WAVES wave sums are
 // added in wave order.  Nothing depends on M, on the tile or on the row group, so
-// a verify row gets the same bits as a one-row greedy step.
+// a verify row gets the same bits as a one-row greedy step.  The lane sums of
+// a row group (RG x NACC x MB values) are formed together by the transposed
+// reduction wave_sum_t, whose totals are those of wave_sum.
 #define GV_WAVES 8
 #ifndef GV_ST
 #define GV_ST 2                  // weight steps in flight per wave
@@ -716,11 +794,11 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
   constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int RG = 8 / NACC;                  // weight rows per step: 8 loads of 1 KB
   constexpr int NG = TR / RG;                   // row groups per tile
-  static_assert(TR == 16 || (TR == 8 && (EPI == EPI_STORE || EPI == EPI_SWIGLU)),
-                "8-row tiles only without per-16-column epilogue partials");
-  constexpr int NU = NG * NCW;                  // steps per wave (chunks past the range are skipped)
+  static_assert(TR == 16 || (TR == 8 && EPI == EPI_SWIGLU), "8-row tiles only for gate/up (4-row groups)");
+  constexpr int NU = NG * NCW;                  // steps per wave and tile (chunks past the range are skipped)
+  static_assert(NU % GV_ST == 0, "a tile's steps start at the same buffer of the load ring");
   static_assert(MB * NCW <= GV_ACT_MAX, "activation registers");
-  __shared__ float part_s[GV_WAVES][NACC][MB][TR];
+  __shared__ float part_s[2][GV_WAVES][NACC][MB][TR];   // by tile parity
   __shared__ float red_s[GV_WAVES][MB];
 
   const int lane = threadIdx.x & 63;
@@ -729,14 +807,32 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
   const int nc = (K + CH - 1) / CH;
   const int c0 = wave * nc / GV_WAVES;
   const int ncw = (wave + 1) * nc / GV_WAVES - c0;       // chunks of this wave (<= NCW)
-  const int tile0 = blockIdx.x * TR;
-  int seg = 0, nloc = tile0;
-  while (seg < 2 && nloc >= ga.nseg[seg]) { nloc -= ga.nseg[seg]; ++seg; }
-  const WT* wbase[NACC];
-  wbase[0] = reinterpret_cast<const WT*>(ga.w[seg]) + (size_t)nloc * K;
-  if constexpr (NACC == 2) wbase[NACC - 1] = reinterpret_cast<const WT*>(ga.w2) + (size_t)tile0 * K;
+  const int ntile = (ga.N + TR - 1) / TR;
+  const int tb = (int)((long)blockIdx.x * ntile / gridDim.x);           // this workgroup's tiles [tb, te)
+  const int te = (int)((long)(blockIdx.x + 1) * ntile / gridDim.x);
+  if (tb >= te) return;                                   // whole workgroup (grid <= tiles on the host)
   const int kl = lane * EPL;
-  const int nrow = min(TR, ga.N - tile0);                 // rows of the tile inside N
+
+  // weight rows of tile t: segment lookup (segments hold multiples of 16 rows)
+  auto tile_rows = [&](int t, const WT* (&wr)[NACC], int& nrow) {
+    const int tile0 = t * TR;
+    int seg = 0, nloc = tile0;
+    while (seg < 2 && nloc >= ga.nseg[seg]) { nloc -= ga.nseg[seg]; ++seg; }
+    wr[0] = reinterpret_cast<const WT*>(ga.w[seg]) + (size_t)nloc * K;
+    if constexpr (NACC == 2) wr[NACC - 1] = reinterpret_cast<const WT*>(ga.w2) + (size_t)tile0 * K;
+    nrow = min(TR, ga.N - tile0);                          // rows of the tile inside N
+  };
+  // weight step u of a tile = (row group u / NCW, chunk c0 + u % NCW)
+  auto unit_load = [&](uint4 (&w)[RG][NACC], const WT* const (&wr)[NACC], int nrow, int u) {
+    const int g = u / NCW, i = u % NCW;
+    const int k = min((c0 + i) * CH + kl, K - EPL);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const size_t ro = (size_t)min(g * RG + r, nrow - 1) * K + k;
+#pragma unroll
+      for (int q = 0; q < NACC; ++q) w[r][q] = ld_nt16(wr[q] + ro);
+    }
+  };
 
   // (1) this wave's activation chunks (raw projection format)
   uint4 xr[NCW][MB][AV];
@@ -751,28 +847,21 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
       for (int v = 0; v < AV; ++v) xr[i][m][v] = pa[v];
     }
   }
-  // (2) RMSNorm partial sums of squares (one per thread and row), summed at the end
+  // (2) RMSNorm partial sums of squares (one per thread and row), summed below
   const bool norm = ga.scale == SCALE_NORM;
   const int T = K >> 4;                                   // <= 64 * GV_WAVES
   const float* pp = norm ? ga.pin : reinterpret_cast<const float*>(ga.A);
   float pr[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) pr[m] = pp[norm ? (size_t)min(m, M - 1) * T + min((int)threadIdx.x, T - 1) : 0];
-  // (3) weight steps: unit u = (row group u / NCW, chunk c0 + u % NCW)
-  auto unit_load = [&](uint4 (&w)[RG][NACC], int u) {
-    const int g = u / NCW, i = u % NCW;
-    const int k = min((c0 + i) * CH + kl, K - EPL);
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const size_t ro = (size_t)min(g * RG + r, nrow - 1) * K + k;
-#pragma unroll
-      for (int q = 0; q < NACC; ++q) w[r][q] = ld_nt16(wbase[q] + ro);
-    }
-  };
+  // (3) the first weight steps
+  const WT* cw[NACC];
+  int cn;
+  tile_rows(tb, cw, cn);
   uint4 wb[GV_ST][RG][NACC];
 #pragma unroll
   for (int u = 0; u < GV_ST; ++u)
-    if (u < NU && u % NCW < ncw) unit_load(wb[u], u);
+    if (u % NCW < ncw) unit_load(wb[u], cw, cn, u);
   __builtin_amdgcn_sched_barrier(0);
   // activations as float32; lanes past K hold zeros
   float x[NCW][MB][EPL];
@@ -786,45 +875,6 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
       for (int e = 0; e < EPL; ++e) x[i][m][e] = kv ? x[i][m][e] : 0.f;
     }
   }
-
-  float acc[RG][NACC][MB];
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int g = u / NCW, i = u % NCW;
-    if (i == 0) {
-#pragma unroll
-      for (int r = 0; r < RG; ++r)
-#pragma unroll
-        for (int q = 0; q < NACC; ++q)
-#pragma unroll
-          for (int m = 0; m < MB; ++m) acc[r][q][m] = 0.f;
-    }
-    if (i < ncw) {                                         // wave-uniform
-#pragma unroll
-      for (int r = 0; r < RG; ++r)
-#pragma unroll
-        for (int q = 0; q < NACC; ++q) {
-          float wf[EPL];
-          unpack_w<WT>(wb[u % GV_ST][r][q], wf);
-#pragma unroll
-          for (int m = 0; m < MB; ++m)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[r][q][m] = fmaf(wf[e], x[i][m][e], acc[r][q][m]);
-        }
-    }
-    if (u + GV_ST < NU && (u + GV_ST) % NCW < ncw) unit_load(wb[u % GV_ST], u + GV_ST);
-    if (i == NCW - 1) {                                    // group g done: lane sums -> LDS
-#pragma unroll
-      for (int r = 0; r < RG; ++r)
-#pragma unroll
-        for (int q = 0; q < NACC; ++q)
-#pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            const float t = wave_sum(acc[r][q][m]);
-            if (lane == 0) part_s[wave][q][m][g * RG + r] = t;
-          }
-    }
-  }
   if (norm) {
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
@@ -833,34 +883,102 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
       if (lane == 0) red_s[wave][m] = v;
     }
   }
-  __syncthreads();
-  // epilogue: thread (m, i) = (tid / 16, tid % 16) -> row m, column tile0 + i
-  if (threadIdx.x >= 16 * MB) return;
-  const int m = threadIdx.x >> 4, i = threadIdx.x & 15;
-  if (TR < 16 && i >= TR) return;                      // no 16-lane reductions in these epilogues
-  float sc = 1.0f;
-  bool scaled = false;
-  if (m < M) {
-    if (norm) {
-      float v = red_s[0][m];
+
+  // epilogue thread (m, i) = (tid / 16, tid % 16) -> row m, column tile0 + i
+  const int em = threadIdx.x >> 4, ei = threadIdx.x & 15;
+  const bool epi_thread = (int)threadIdx.x < 16 * MB && (TR == 16 || ei < TR);
+  const int n16 = (ga.N + 15) / 16;
+  const int wj = wst_index<RG * NACC * MB>(lane);          // the group value this lane's reduction ends with
+  for (int t = tb; t < te; ++t) {
+    const int par = (t - tb) & 1;
+    const bool has_next = t + 1 < te;                      // uniform
+    const WT* nw[NACC];
+    int nn = cn;
 #pragma unroll
-      for (int w = 1; w < GV_WAVES; ++w) v = __fadd_rn(v, red_s[w][m]);
-      sc = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(v, (float)K), ga.eps)));
-      scaled = true;
-    } else if (ga.scale == SCALE_XS) {
-      sc = ga.xs[m];
-      scaled = true;
+    for (int q = 0; q < NACC; ++q) nw[q] = cw[q];
+    if (has_next) tile_rows(t + 1, nw, nn);
+    float acc[RG][NACC][MB];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int g = u / NCW, i = u % NCW;
+      if (i == 0) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+          for (int q = 0; q < NACC; ++q)
+#pragma unroll
+            for (int m = 0; m < MB; ++m) acc[r][q][m] = 0.f;
+      }
+      if (i < ncw) {                                       // wave-uniform
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+          for (int q = 0; q < NACC; ++q) {
+            float wf[EPL];
+            unpack_w<WT>(wb[u % GV_ST][r][q], wf);
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) acc[r][q][m] = fmaf(wf[e], x[i][m][e], acc[r][q][m]);
+          }
+      }
+      // refill the ring: the step GV_ST ahead, in this tile or the next
+      const int un = u + GV_ST;
+      if (un < NU) {
+        if (un % NCW < ncw) unit_load(wb[u % GV_ST], cw, cn, un);
+      } else if (has_next && (un - NU) % NCW < ncw) {
+        unit_load(wb[u % GV_ST], nw, nn, un - NU);
+      }
+      if (i == NCW - 1) {                                  // group g done: lane sums -> LDS
+        float red[RG * NACC * MB];
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+          for (int q = 0; q < NACC; ++q)
+#pragma unroll
+            for (int m = 0; m < MB; ++m) red[(r * NACC + q) * MB + m] = acc[r][q][m];
+        wave_sum_t<RG * NACC * MB>(red);
+        if (lane < RG * NACC * MB) {
+          const int m = wj % MB, q = (wj / MB) % NACC, r = wj / (MB * NACC);
+          part_s[par][wave][q][m][g * RG + r] = red[0];
+        }
+      }
     }
-  }
-  float y[NACC];
+    // one barrier per tile: the next writes to part_s[par] come after the
+    // next tile's barrier, which every epilogue thread reaches only after
+    // finishing this tile
+    __syncthreads();
+    if (epi_thread) {
+      const int m = em, i = ei;
+      float sc = 1.0f;
+      bool scaled = false;
+      if (m < M) {
+        if (norm) {
+          float v = red_s[0][m];
 #pragma unroll
-  for (int q = 0; q < NACC; ++q) {
-    float v = part_s[0][q][m][i];
+          for (int w = 1; w < GV_WAVES; ++w) v = __fadd_rn(v, red_s[w][m]);
+          sc = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(v, (float)K), ga.eps)));
+          scaled = true;
+        } else if (ga.scale == SCALE_XS) {
+          sc = ga.xs[m];
+          scaled = true;
+        }
+      }
+      float y[NACC];
 #pragma unroll
-    for (int w = 1; w < GV_WAVES; ++w) v = __fadd_rn(v, part_s[w][q][m][i]);
-    y[q] = scaled ? __fmul_rn(v, sc) : v;
+      for (int q = 0; q < NACC; ++q) {
+        float v = part_s[par][0][q][m][i];
+#pragma unroll
+        for (int w = 1; w < GV_WAVES; ++w) v = __fadd_rn(v, part_s[par][w][q][m][i]);
+        y[q] = scaled ? __fmul_rn(v, sc) : v;
+      }
+      const int tile0 = t * TR;
+      proj_out<WT, EPI>(ga, m, M, tile0 + i, i, tile0 / 16, n16, y[0], NACC == 2 ? y[NACC - 1] : 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < NACC; ++q) cw[q] = nw[q];
+    cn = nn;
   }
-  proj_out<WT, EPI>(ga, m, M, tile0 + i, i, y[0], NACC == 2 ? y[NACC - 1] : 0.f);
 }
 
 // ---------------------------------------------------------------- int8 decode GEMV (W8A8 draft)
@@ -1022,7 +1140,7 @@ __global__ __launch_bounds__(G8_THREADS) void k_gemv8(GemmArgs ga) {
   const float y = __fmul_rn((float)acc_s[0][il], __fmul_rn(ga.wsc[seg][nloc + il], sx));
   float u = 0.f;
   if constexpr (NACC == 2) u = __fmul_rn((float)acc_s[1][il], __fmul_rn(ga.wsc2[tile0 + il], sx));
-  proj_out<WT, EPI>(ga, 0, 1, n, i, y, u);
+  proj_out<WT, EPI>(ga, 0, 1, n, i, blockIdx.x, gridDim.x, y, u);
 }
 
 // ---------------------------------------------------------------- attention

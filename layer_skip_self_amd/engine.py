@@ -98,6 +98,11 @@ class Engine:
         """Speculative sampling at ``temperature`` with ``seed`` (0: greedy)."""
         self._check(self.lib.lss_set_sampling(self.h, float(temperature), int(seed) % 2**64), "lss_set_sampling")
 
+    def set_gemv_grid(self, wgs_per_cu):
+        """Decode-GEMV grid: 0 = one workgroup per weight tile, n > 0 = at
+        most n workgroups per compute unit walking tile ranges (same bits)."""
+        self._check(self.lib.lss_set_gemv_grid(self.h, int(wgs_per_cu)), "lss_set_gemv_grid")
+
     def prefill(self, tokens):
         a, p = _i32(tokens)
         t0 = C.c_int32()

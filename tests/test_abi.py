@@ -32,6 +32,12 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(N.SIGNATURES), set(names) ^ set(N.SIGNATURES)
 
 
+def test_null_engine_calls_are_rejected():
+    lib = N.load()
+    assert lib.lss_set_gemv_grid(None, 1) == N.LSS_EINVAL
+    assert lib.lss_set_sampling(None, 1.0, 0) == N.LSS_EINVAL
+
+
 def test_workspace_size_and_invalid_configs():
     sh = lss_synth.SHAPES["llama3_8b"]
     nb = lss.workspace_bytes(sh, max_seq=1600, max_rows=16)

@@ -64,6 +64,32 @@ def test_speculative_equals_greedy_bitwise_8b(gpu8b):
         assert 0 <= st["accepted"] <= st["drafted"]
 
 
+@pytest.mark.parametrize("grid", [0, 2])
+def test_gemv_grid_policies_bitwise_equal_8b(gpu8b, grid):
+    """The decode GEMV's grid (one workgroup per tile, or workgroups walking
+    tile ranges) changes no bit: verify logits and residual states of 1, 2,
+    5 and 9 rows (the 9-row verify takes two launches at K = 14336) equal
+    those of the default grid."""
+    eng, prompt = gpu8b["eng"], gpu8b["prompt"]
+    out = {}
+    try:
+        for g in (1, grid):
+            eng.set_gemv_grid(g)
+            for rows in (1, 2, 5, 9):
+                eng.prefill(prompt)
+                eng.verify(drafts=list(range(11, 11 + rows - 1)))
+                z = eng.read_logits(rows)
+                hs = eng.read_states(rows - 1)
+                eng.accept()
+                if g == 1:
+                    out[rows] = (z, hs)
+                else:
+                    assert np.array_equal(z.view(np.uint32), out[rows][0].view(np.uint32)), rows
+                    assert np.array_equal(hs.view(np.uint32), out[rows][1].view(np.uint32)), rows
+    finally:
+        eng.set_gemv_grid(1)
+
+
 def test_empty_mask_draft_accepted_in_full_8b(gpu8b):
     eng = gpu8b["eng"]
     eng.prefill(gpu8b["prompt"])

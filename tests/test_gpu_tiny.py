@@ -114,6 +114,31 @@ def test_verify_logits_equal_ar_logits_bitwise(setup):
         pos += n + 1
 
 
+def test_gemv_grid_policies_bitwise_equal(setup):
+    """Tiny model (float32, one 1 KB chunk of K per wave at most): greedy
+    tokens and verify logits do not depend on the decode GEMV's grid."""
+    eng, prompt = setup["eng"], setup["prompt"]
+    out = {}
+    try:
+        for g in (1, 0, 2, 8):
+            eng.set_gemv_grid(g)
+            eng.prefill(prompt)
+            eng.verify(drafts=[3, 5, 7, 9])
+            z = eng.read_logits(5)
+            eng.accept()
+            toks, _ = eng.generate(prompt, 24, {"mode": "static", "k_max": 4, "skip": (1, 2)})
+            if not out:
+                out = dict(z=z, toks=toks)
+            else:
+                assert np.array_equal(z.view(np.uint32), out["z"].view(np.uint32)), g
+                assert toks == out["toks"], g
+        from layer_skip_self_amd import LssError
+        with pytest.raises(LssError):
+            eng.set_gemv_grid(-1)
+    finally:
+        eng.set_gemv_grid(1)
+
+
 def test_draft_logits_and_quant_draft(setup):
     """Draft steps (skip mask, with and without int8 activations) against the
     oracle's draft on the same committed state."""
