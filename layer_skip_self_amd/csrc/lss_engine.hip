@@ -305,19 +305,20 @@ int gemv_cap(int K, int wbytes) {
   return ncw == 1 ? GV_MB_MAX : std::max(1, std::min(4, GV_ACT_MAX / ncw));
 }
 
-// 16 weight rows per tile (8 for gate/up, whose steps read two matrices)
-template <int EPI> constexpr int gemv_tile() { return EPI == EPI_SWIGLU ? 8 : 16; }
+// 8-row tiles where the epilogue has no per-16-column partials
+template <int EPI> constexpr int gemv_tile() { return (EPI == EPI_STORE || EPI == EPI_SWIGLU) ? 8 : 16; }
 
 // Workgroups of one decode-GEMV launch.  gmax_cu = 0: one per tile.
 // Otherwise, with at most gmax = gmax_cu workgroups per compute unit (capped
-// by the kernel's occupancy): launches of at most 2 gmax tiles keep one
-// workgroup per tile (a walk of two tiles would leave compute units idle);
-// larger ones take ceil(tiles / ceil(tiles / gmax)) workgroups, each walking
-// the same number of tiles give or take one.
+// by the kernel's occupancy): launches of at most 4 gmax tiles keep one
+// workgroup per tile (several resident workgroups per compute unit fill it
+// faster than a short walk); larger ones take
+// ceil(tiles / ceil(tiles / gmax)) workgroups, each walking the same number
+// of tiles give or take one.
 int gemv_grid(int ntile, int ncu, int gmax_cu, int occ) {
   if (gmax_cu <= 0 || ncu <= 0) return ntile;
   const int gmax = ncu * std::max(1, std::min(gmax_cu, occ));
-  if (ntile <= 2 * gmax) return ntile;
+  if (ntile <= 4 * gmax) return ntile;
   const int per = (ntile + gmax - 1) / gmax;
   return (ntile + per - 1) / per;
 }

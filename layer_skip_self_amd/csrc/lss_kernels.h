@@ -73,7 +73,7 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 // Transposed wave sums: the totals over the 64 lanes of V values per lane
-// (V a power of two, 8 <= V <= 64) with the pairing tree of wave_sum, level s
+// (V a power of two, 1 <= V <= 64) with the pairing tree of wave_sum, level s
 // adding lanes that differ in bit s of the lane id: quad_perm xor 1 and
 // xor 2, row_half_mirror (flips bits 0-2), row_ror:8, permlane16_swap,
 // permlane32_swap.  While a lane still holds more than one value, a level
@@ -129,15 +129,15 @@ template <int N, int V, bool P32> __device__ __forceinline__ void wst_swap(float
   }
 }
 template <int V> __device__ __forceinline__ void wave_sum_t(float (&v)[V]) {
-  static_assert(V >= 8 && V <= 64 && (V & (V - 1)) == 0, "8 .. 64 values, a power of two");
+  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "1 .. 64 values, a power of two");
   const int l = threadIdx.x & 63;
   const int b2 = (l >> 2) & 1;
   wst_dpp<LSS_DPP_XOR1, V, V>(v, ((l & 1) ^ b2) != 0);
-  wst_dpp<LSS_DPP_XOR2, V / 2, V>(v, (((l >> 1) & 1) ^ b2) != 0);
-  wst_dpp<LSS_DPP_HMIRROR, V / 4, V>(v, b2 != 0);
-  wst_dpp<LSS_DPP_ROR8, V / 8, V>(v, ((l >> 3) & 1) != 0);
-  wst_swap<(V >= 32 ? V / 16 : 1), V, false>(v);
-  wst_swap<(V >= 64 ? V / 32 : 1), V, true>(v);
+  wst_dpp<LSS_DPP_XOR2, (V >= 2 ? V / 2 : 1), V>(v, (((l >> 1) & 1) ^ b2) != 0);
+  wst_dpp<LSS_DPP_HMIRROR, (V >= 4 ? V / 4 : 1), V>(v, b2 != 0);
+  wst_dpp<LSS_DPP_ROR8, (V >= 8 ? V / 8 : 1), V>(v, ((l >> 3) & 1) != 0);
+  wst_swap<(V >= 16 ? V / 16 : 1), V, false>(v);
+  wst_swap<(V >= 32 ? V / 32 : 1), V, true>(v);
 }
 // (value, index) maximum with the lowest index on ties: a total order, so the
 // result does not depend on the reduction tree
@@ -472,17 +472,18 @@ __device__ __forceinline__ void load_w(uint4 (&w)[GEMM_U], const WT* row, int kb
 // aligned lane group hold columns 16 b .. 16 b + 15 of the same row (b = t16,
 // one of n16 such column tiles) and call this together: RESID's partial sum
 // of squares and LOGITS' tile max / argmax / sum of exponentials are fixed
-// 16-lane trees.
+// 16-lane trees.  RESID with pre = true takes the residual input and the
+// next gain from rv / gv (loaded early by the caller) instead of reading them.
 template <typename WT, int EPI>
 __device__ __forceinline__ void proj_out(const GemmArgs& ga, int m, int M, int n, int cl, int t16, int n16, float y,
-                                         float u) {
+                                         float u, bool pre = false, float rv = 0.f, float gv = 1.f) {
   const bool ok = (m < M) && (n < ga.N);
   if constexpr (EPI == EPI_STORE) {
     if (ok) ga.Y[(size_t)m * ga.ldy + n] = y;
   } else if constexpr (EPI == EPI_RESID) {
-    const float h = ok ? __fadd_rn(ga.R[(size_t)m * ga.ldr + n], y) : 0.f;
+    const float h = ok ? __fadd_rn(pre ? rv : ga.R[(size_t)m * ga.ldr + n], y) : 0.f;
     if (ok) ga.Y[(size_t)m * ga.ldy + n] = h;
-    if (ga.xo && ok) AF<WT>::store(ga.xo, (size_t)m * ga.ldo, n, ga.go ? __fmul_rn(h, ga.go[n]) : h);
+    if (ga.xo && ok) AF<WT>::store(ga.xo, (size_t)m * ga.ldo, n, ga.go ? __fmul_rn(h, pre ? gv : ga.go[n]) : h);
     if (ga.po) {
       const float s2 = sum16(__fmul_rn(h, h));
       if (cl == 0 && m < M) ga.po[(size_t)m * n16 + t16] = s2;
@@ -717,14 +718,14 @@ __global__ __launch_bounds__(256) void k_pepi(GemmArgs ga, const float* __restri
 // pattern is chosen for HBM: each load instruction of a wave reads one 1 KB
 // contiguous piece ("chunk") of one weight row (lane l: the 16 bytes at
 // offset 16 l), with nontemporal hints since the weights are read once.
-// The weight rows are cut into tiles of 16 rows (8 for gate/up, whose steps
-// read two matrices: two 4-row groups per tile, like the 8-row groups of a
-// 16-row tile), and a workgroup walks a contiguous
+// The weight rows are cut into tiles of 16 rows (8 where the epilogue has
+// no per-16-column partials: store, SwiGLU; more workgroups for the small
+// q/k/v launch), and a workgroup walks a contiguous
 // range of tiles (one tile when the grid has a workgroup per tile).  Its
 // GV_WAVES waves split the chunks of K into contiguous ranges (wave w: chunks
 // [w nc / W, (w + 1) nc / W)), and each wave walks every tile's rows in groups
 // of RG rows, the chunks of its range inside each group, RG x NACC 1 KB loads
-// per step with GV_ST steps in flight.  The steps run on across tile
+// per step with ST steps in flight.  The steps run on across tile
 // boundaries: the first loads of the next tile are in flight while the wave
 // sums of the current tile go through LDS and its epilogue runs, so a
 // workgroup keeps the weight stream going from its first load to its last.
@@ -794,9 +795,14 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
   constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int RG = 8 / NACC;                  // weight rows per step: 8 loads of 1 KB
   constexpr int NG = TR / RG;                   // row groups per tile
-  static_assert(TR == 16 || (TR == 8 && EPI == EPI_SWIGLU), "8-row tiles only for gate/up (4-row groups)");
+  // steps in flight per wave: one for the q/k/v and residual projections
+  // (fewer registers, more resident workgroups), GV_ST for gate/up and the
+  // LM head
+  constexpr int ST = (EPI == EPI_STORE || EPI == EPI_RESID) ? 1 : GV_ST;
+  static_assert(TR == 16 || (TR == 8 && (EPI == EPI_STORE || EPI == EPI_SWIGLU)),
+                "8-row tiles only without per-16-column epilogue partials");
   constexpr int NU = NG * NCW;                  // steps per wave and tile (chunks past the range are skipped)
-  static_assert(NU % GV_ST == 0, "a tile's steps start at the same buffer of the load ring");
+  static_assert(NU % ST == 0, "a tile's steps start at the same buffer of the load ring");
   static_assert(MB * NCW <= GV_ACT_MAX, "activation registers");
   __shared__ float part_s[2][GV_WAVES][NACC][MB][TR];   // by tile parity
   __shared__ float red_s[GV_WAVES][MB];
@@ -858,9 +864,9 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
   const WT* cw[NACC];
   int cn;
   tile_rows(tb, cw, cn);
-  uint4 wb[GV_ST][RG][NACC];
+  uint4 wb[ST][RG][NACC];
 #pragma unroll
-  for (int u = 0; u < GV_ST; ++u)
+  for (int u = 0; u < ST; ++u)
     if (u % NCW < ncw) unit_load(wb[u], cw, cn, u);
   __builtin_amdgcn_sched_barrier(0);
   // activations as float32; lanes past K hold zeros
@@ -897,6 +903,15 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
 #pragma unroll
     for (int q = 0; q < NACC; ++q) nw[q] = cw[q];
     if (has_next) tile_rows(t + 1, nw, nn);
+    // RESID: the epilogue's residual input and next gain, loaded under the weight stream
+    float rpre = 0.f, gpre = 1.f;
+    if constexpr (EPI == EPI_RESID) {
+      const int n = t * TR + ei;
+      if (epi_thread && em < M && n < ga.N) {
+        rpre = ga.R[(size_t)em * ga.ldr + n];
+        if (ga.go) gpre = ga.go[n];
+      }
+    }
     float acc[RG][NACC][MB];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -915,19 +930,19 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
 #pragma unroll
           for (int q = 0; q < NACC; ++q) {
             float wf[EPL];
-            unpack_w<WT>(wb[u % GV_ST][r][q], wf);
+            unpack_w<WT>(wb[u % ST][r][q], wf);
 #pragma unroll
             for (int m = 0; m < MB; ++m)
 #pragma unroll
               for (int e = 0; e < EPL; ++e) acc[r][q][m] = fmaf(wf[e], x[i][m][e], acc[r][q][m]);
           }
       }
-      // refill the ring: the step GV_ST ahead, in this tile or the next
-      const int un = u + GV_ST;
+      // refill the ring: the step ST ahead, in this tile or the next
+      const int un = u + ST;
       if (un < NU) {
-        if (un % NCW < ncw) unit_load(wb[u % GV_ST], cw, cn, un);
+        if (un % NCW < ncw) unit_load(wb[u % ST], cw, cn, un);
       } else if (has_next && (un - NU) % NCW < ncw) {
-        unit_load(wb[u % GV_ST], nw, nn, un - NU);
+        unit_load(wb[u % ST], nw, nn, un - NU);
       }
       if (i == NCW - 1) {                                  // group g done: lane sums -> LDS
         float red[RG * NACC * MB];
@@ -973,7 +988,8 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
         y[q] = scaled ? __fmul_rn(v, sc) : v;
       }
       const int tile0 = t * TR;
-      proj_out<WT, EPI>(ga, m, M, tile0 + i, i, tile0 / 16, n16, y[0], NACC == 2 ? y[NACC - 1] : 0.f);
+      proj_out<WT, EPI>(ga, m, M, tile0 + i, i, tile0 / 16, n16, y[0], NACC == 2 ? y[NACC - 1] : 0.f,
+                        EPI == EPI_RESID, rpre, gpre);
     }
 #pragma unroll
     for (int q = 0; q < NACC; ++q) cw[q] = nw[q];
@@ -1178,6 +1194,10 @@ __global__ __launch_bounds__(G8_THREADS) void k_gemv8(GemmArgs ga) {
 #define ATT_CH 64
 #define ATT_QB 32
 #define ATT_THREADS 256
+// row stride (floats) of the LDS key / value tile: 16-byte rows for vector
+// stores and score reads, rows 4 banks apart (a key per lane reads without
+// bank conflicts)
+#define ATT_LD (HD + 4)
 
 struct AttnArgs {
   const float* qkv; int ldqkv;     // [M][(Hq + 2 Hkv) hd] projection output
@@ -1201,14 +1221,15 @@ template <typename KT> __device__ __forceinline__ float kv_round(float v);
 template <> __device__ __forceinline__ float kv_round<float>(float v) { return v; }
 template <> __device__ __forceinline__ float kv_round<uint16_t>(float v) { return bf2f(f2bf(v)); }
 
-// element i of the rotated (rotate-half) vector x at rotary row cs
+// element i of the rotated (rotate-half) vector x at rotary row cs, from
+// xi = x[i], its partner xp = x[i +- half] and the pair's (cos, sin)
+__device__ __forceinline__ float rope_val(float xi, float xp, float2 c, bool low) {
+  return low ? __fsub_rn(__fmul_rn(xi, c.x), __fmul_rn(xp, c.y)) : __fadd_rn(__fmul_rn(xi, c.x), __fmul_rn(xp, c.y));
+}
 __device__ __forceinline__ float rope_elem(const float* x, const float2* cs, int i, int half) {
-  if (i < half) {
-    const float2 c = cs[i];
-    return __fsub_rn(__fmul_rn(x[i], c.x), __fmul_rn(x[i + half], c.y));
-  }
-  const float2 c = cs[i - half];
-  return __fadd_rn(__fmul_rn(x[i], c.x), __fmul_rn(x[i - half], c.y));
+  const bool low = i < half;
+  const int j = low ? i + half : i - half;
+  return rope_val(x[i], x[j], cs[low ? i : j], low);
 }
 
 // rotary position of launch row m (tree launches: all candidates at pos0 + 1)
@@ -1241,43 +1262,80 @@ struct AttTile {
       v[j] = ld4<KT>(cache + (size_t)pos * HD + d4 * 4);
     }
   }
-  __device__ __forceinline__ void store(float (*t)[HD + 1]) const {
+  __device__ __forceinline__ void store(float (*t)[ATT_LD]) const {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int f = threadIdx.x + j * ATT_THREADS;
       const int u = f / (HD / 4), d4 = f % (HD / 4);
-      t[u][d4 * 4 + 0] = v[j].x; t[u][d4 * 4 + 1] = v[j].y; t[u][d4 * 4 + 2] = v[j].z; t[u][d4 * 4 + 3] = v[j].w;
+      *reinterpret_cast<float4*>(&t[u][d4 * 4]) = v[j];
     }
   }
 };
 
 // Replace the tile rows that are rows of this launch by their own keys
 // (rotated) or values, rounded to the cache type; query block 0 also writes
-// them to the cache.
+// them to the cache.  The first ATT_NR_J elements per thread come from
+// registers filled at kernel start (AttNew::load, so their reads overlap the
+// tile loads); any further ones (prefill blocks) are read here.
+#define ATT_NR_J 4
 template <typename KT, int HD>
-__device__ __forceinline__ void att_new_rows(float (*t)[HD + 1], const AttnArgs& a, int kh, int u0, int z,
-                                             bool is_v) {
-  if (a.self_kv) return;
-  const int r0 = max(u0, a.pos0), r1 = min(u0 + ATT_CH, a.pos0 + a.M);
-  if (r0 >= r1) return;
-  KT* cache = reinterpret_cast<KT*>(is_v ? a.vc : a.kc) + (size_t)kh * a.max_seq * HD;
-  const int off = (is_v ? a.Hq + a.Hkv : a.Hq) + kh;
-  for (int i = threadIdx.x; i < (r1 - r0) * HD; i += ATT_THREADS) {
-    const int pos = r0 + i / HD, dd = i % HD;
-    const float* x = a.qkv + (size_t)(pos - a.pos0) * a.ldqkv + (size_t)off * HD;
-    const int rp = att_row_pos(a, pos - a.pos0);
-    float v = is_v ? x[dd] : rope_elem(x, a.cs + (size_t)rp * (HD / 2), dd, HD / 2);
-    v = kv_round<KT>(v);
-    if (z == 0) st_elem<KT>(cache, (size_t)pos * HD + dd, v);
-    t[pos - u0][dd] = v;
+struct AttNew {
+  float xi[ATT_NR_J], xp[ATT_NR_J];   // key element and its rotation partner, or the value element
+  float2 c[ATT_NR_J];
+  int r0, n;                          // first new row of the chunk, elements (rows x HD)
+  __device__ __forceinline__ void load(const AttnArgs& a, int kh, int u0, bool is_v) {
+    r0 = max(u0, a.pos0);
+    n = a.self_kv ? 0 : max(0, min(u0 + ATT_CH, a.pos0 + a.M) - r0) * HD;
+    const int off = (is_v ? a.Hq + a.Hkv : a.Hq) + kh;
+#pragma unroll
+    for (int j = 0; j < ATT_NR_J; ++j) {
+      const int i = threadIdx.x + j * ATT_THREADS;
+      if (i < n) {
+        const int pos = r0 + i / HD, dd = i % HD;
+        const float* x = a.qkv + (size_t)(pos - a.pos0) * a.ldqkv + (size_t)off * HD;
+        xi[j] = x[dd];
+        if (!is_v) {
+          const bool low = dd < HD / 2;
+          const int pj = low ? dd + HD / 2 : dd - HD / 2;
+          xp[j] = x[pj];
+          c[j] = a.cs[(size_t)att_row_pos(a, pos - a.pos0) * (HD / 2) + (low ? dd : pj)];
+        }
+      }
+    }
   }
-}
+  __device__ __forceinline__ void apply(float (*t)[ATT_LD], const AttnArgs& a, int kh, int u0, int z,
+                                        bool is_v) const {
+    if (n == 0) return;
+    KT* cache = reinterpret_cast<KT*>(is_v ? a.vc : a.kc) + (size_t)kh * a.max_seq * HD;
+#pragma unroll
+    for (int j = 0; j < ATT_NR_J; ++j) {
+      const int i = threadIdx.x + j * ATT_THREADS;
+      if (i < n) {
+        const int pos = r0 + i / HD, dd = i % HD;
+        float v = is_v ? xi[j] : rope_val(xi[j], xp[j], c[j], dd < HD / 2);
+        v = kv_round<KT>(v);
+        if (z == 0) st_elem<KT>(cache, (size_t)pos * HD + dd, v);
+        t[pos - u0][dd] = v;
+      }
+    }
+    const int off = (is_v ? a.Hq + a.Hkv : a.Hq) + kh;
+    for (int i = threadIdx.x + ATT_NR_J * ATT_THREADS; i < n; i += ATT_THREADS) {
+      const int pos = r0 + i / HD, dd = i % HD;
+      const float* x = a.qkv + (size_t)(pos - a.pos0) * a.ldqkv + (size_t)off * HD;
+      const int rp = att_row_pos(a, pos - a.pos0);
+      float v = is_v ? x[dd] : rope_elem(x, a.cs + (size_t)rp * (HD / 2), dd, HD / 2);
+      v = kv_round<KT>(v);
+      if (z == 0) st_elem<KT>(cache, (size_t)pos * HD + dd, v);
+      t[pos - u0][dd] = v;
+    }
+  }
+};
 
 #define ATT_TREE_MAX 8
 template <typename KT, typename WT, int HD, bool TREE = false>
 __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
-  __shared__ float kv_s[ATT_CH][HD + 1];
-  __shared__ float q_s[ATT_QB][HD];
+  __shared__ __align__(16) float kv_s[ATT_CH][ATT_LD];
+  __shared__ __align__(16) float q_s[ATT_QB][HD];
   __shared__ float p_s[ATT_QB][ATT_CH];
   __shared__ float st_s[ATT_QB][2];
   __shared__ float own_s[TREE ? ATT_TREE_MAX + 1 : 1][TREE ? HD : 1];   // tree: candidates' own keys
@@ -1294,6 +1352,9 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
   AttTile<KT, HD> kt, vt;
   kt.load(kc, u0, a.max_seq);
   vt.load(vc, u0, a.max_seq);
+  AttNew<KT, HD> nk, nv;                              // this launch's rows that fall in the chunk
+  nk.load(a, kh, u0, false);
+  nv.load(a, kh, u0, true);
   // rotated queries of this block (only rows of real queries are read later)
   const int nqb = min(ATT_QB, nq - q0);
   for (int i = tid; i < nqb * HD; i += ATT_THREADS) {
@@ -1321,7 +1382,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
     }
   }
   __syncthreads();
-  att_new_rows<KT, HD>(kv_s, a, kh, u0, z, false);
+  nk.apply(kv_s, a, kh, u0, z, false);
   __syncthreads();
   // scores: lane = key; each wave takes query pairs (qi, qi + 4) for
   // qi = wave, wave + 8, ..., two independent dot-product chains per lane
@@ -1343,11 +1404,15 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
           dc = fmaf(q_s[qcc][dd], kc[dd], dc);
         }
       } else {
-#pragma unroll 8
-        for (int dd = 0; dd < HD; ++dd) {
-          const float kv = kv_s[u][dd];
-          da = fmaf(q_s[qb][dd], kv, da);
-          dc = fmaf(q_s[qcc][dd], kv, dc);
+#pragma unroll 4
+        for (int d4 = 0; d4 < HD / 4; ++d4) {
+          const float4 kv = *reinterpret_cast<const float4*>(&kv_s[u][d4 * 4]);
+          const float4 qa = *reinterpret_cast<const float4*>(&q_s[qb][d4 * 4]);
+          const float4 qc = *reinterpret_cast<const float4*>(&q_s[qcc][d4 * 4]);
+          da = fmaf(qa.x, kv.x, da); dc = fmaf(qc.x, kv.x, dc);
+          da = fmaf(qa.y, kv.y, da); dc = fmaf(qc.y, kv.y, dc);
+          da = fmaf(qa.z, kv.z, da); dc = fmaf(qc.z, kv.z, dc);
+          da = fmaf(qa.w, kv.w, da); dc = fmaf(qc.w, kv.w, dc);
         }
       }
 #pragma unroll
@@ -1370,7 +1435,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
   __syncthreads();
   vt.store(kv_s);
   __syncthreads();
-  att_new_rows<KT, HD>(kv_s, a, kh, u0, z, true);
+  nv.apply(kv_s, a, kh, u0, z, true);
   __syncthreads();
   // value sums: outputs i and i + 256 of the (query, dim) grid per thread,
   // two independent chains over the 64 keys
@@ -1490,6 +1555,7 @@ struct HeadRes {                 // device result block, mirrored to the host
 // (samp): the row's Gumbel-max draw and its log-sum-exp, the latter in
 // dlse (draft slots) or lse (verify rows).
 #define HEAD_RED_THREADS 1024
+#define HEAD_RED_REG 8
 __global__ __launch_bounds__(HEAD_RED_THREADS) void k_head_reduce(const float* __restrict__ part, int ntile,
                                                                   HeadRes* __restrict__ res, int row0, int samp,
                                                                   int draft) {
@@ -1500,10 +1566,24 @@ __global__ __launch_bounds__(HEAD_RED_THREADS) void k_head_reduce(const float* _
   const float* p = part + (size_t)m * ntile * HEAD_PART;
   float mx = -INFINITY, gmx = -INFINITY;
   int idx = 0x7fffffff, gidx = 0x7fffffff;
-  for (int w = threadIdx.x; w < ntile; w += blockDim.x) {
-    argmax_merge(mx, idx, p[w * HEAD_PART], __float_as_int(p[w * HEAD_PART + 1]));
-    if (samp) argmax_merge(gmx, gidx, p[w * HEAD_PART + 3], __float_as_int(p[w * HEAD_PART + 4]));
+  // this thread's first HEAD_RED_REG records, all loaded before any is used
+  // (tiles w = tid + j blockDim; vocabularies up to 16 x 1024 x 16 columns)
+  float rm[HEAD_RED_REG], rl[HEAD_RED_REG];
+  int ri[HEAD_RED_REG];
+#pragma unroll
+  for (int j = 0; j < HEAD_RED_REG; ++j) {
+    const int w = threadIdx.x + j * HEAD_RED_THREADS;
+    rm[j] = w < ntile ? p[w * HEAD_PART] : -INFINITY;
+    ri[j] = w < ntile ? __float_as_int(p[w * HEAD_PART + 1]) : 0x7fffffff;
+    rl[j] = w < ntile ? p[w * HEAD_PART + 2] : 0.f;
   }
+#pragma unroll
+  for (int j = 0; j < HEAD_RED_REG; ++j) argmax_merge(mx, idx, rm[j], ri[j]);
+  for (int w = threadIdx.x + HEAD_RED_REG * HEAD_RED_THREADS; w < ntile; w += blockDim.x)
+    argmax_merge(mx, idx, p[w * HEAD_PART], __float_as_int(p[w * HEAD_PART + 1]));
+  if (samp)
+    for (int w = threadIdx.x; w < ntile; w += blockDim.x)
+      argmax_merge(gmx, gidx, p[w * HEAD_PART + 3], __float_as_int(p[w * HEAD_PART + 4]));
   argmax_wave(mx, idx);
   if (samp) argmax_wave(gmx, gidx);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -1514,8 +1594,11 @@ __global__ __launch_bounds__(HEAD_RED_THREADS) void k_head_reduce(const float* _
     argmax_merge(mx, idx, bm[i], bi[i]);
     argmax_merge(gmx, gidx, gm[i], gx[i]);
   }
-  float s = 0.f;
-  for (int w = threadIdx.x; w < ntile; w += blockDim.x)
+  float s = 0.f;                                       // tiles in the same order as before
+#pragma unroll
+  for (int j = 0; j < HEAD_RED_REG; ++j)
+    if (threadIdx.x + j * HEAD_RED_THREADS < ntile) s = __fadd_rn(s, __fmul_rn(rl[j], expf(__fsub_rn(rm[j], mx))));
+  for (int w = threadIdx.x + HEAD_RED_REG * HEAD_RED_THREADS; w < ntile; w += blockDim.x)
     s = __fadd_rn(s, __fmul_rn(p[w * HEAD_PART + 2], expf(__fsub_rn(p[w * HEAD_PART], mx))));
   s = block_sum(s, redf);
   if (threadIdx.x == 0) {
