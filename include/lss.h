@@ -252,17 +252,6 @@ int lss_profile_read(lss_engine* e, double* total_ms, int64_t* launches, int64_t
  * or a value above 8. */
 int lss_set_gemv_grid(lss_engine* e, int32_t wgs_per_cu);
 
-/* Cache warming on a second stream: mode 1 reads each layer's O-projection
- * weights, mode 2 also the first gate/up tile of every workgroup of the
- * walking gate/up launch, while that layer's attention runs (decode rows
- * only), so that those projections find them in the last-level cache.  The
- * warming kernels read weights and write nothing; the engine stream waits
- * for them before the LM head and before any synchronization, so all work
- * stays ordered on the engine stream.  Outputs are unchanged.  mode 0 (the
- * default) turns it off.  The first nonzero mode creates the stream and two
- * events (LSS_EHIP if that fails).  LSS_EINVAL for a mode outside 0..2. */
-int lss_set_prefetch(lss_engine* e, int32_t mode);
-
 /* Stand-alone dynamic per-token int8 quantization (CAS-Spec blog section
  * 2.1): for each of `rows` rows of x_dev[rows][n] (float32), codes q_dev
  * [rows][n] = clamp(rint(x * fl(127/amax)), -127, 127) and scale_dev[rows]

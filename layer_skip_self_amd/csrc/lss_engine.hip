@@ -217,12 +217,6 @@ struct lss_engine {
   // through the MFMA kernels
   bool gemv = false;
   GemvLaunch gvl;
-  // cache warming on a side stream (lss_set_prefetch): 0 off, 1 the O
-  // weights, 2 also the first gate/up tile of every walking workgroup
-  int prefetch = 0;
-  hipStream_t side = nullptr;
-  hipEvent_t ev_q = nullptr, ev_w = nullptr;
-  bool side_pending = false;
   // kernel timing (lss_profile_kernel)
   int prof_epi = -1, prof_rows = 0;
   std::vector<hipEvent_t> ev_start, ev_stop;
@@ -245,14 +239,6 @@ int fail(lss_engine* e, int code, const std::string& msg) {
     if (_s != hipSuccess)                                                               \
       return fail(e, LSS_EHIP, std::string(#expr) + ": " + hipGetErrorString(_s));     \
   } while (0)
-
-// the main stream waits for the side stream's warming launches
-void side_join(lss_engine* e) {
-  if (e->side_pending) {
-    (void)hipStreamWaitEvent(e->stream, e->ev_w, 0);
-    e->side_pending = false;
-  }
-}
 
 int check_launch(lss_engine* e, const char* what) {
   hipError_t s = hipGetLastError();
@@ -576,32 +562,6 @@ void prep_rows(lss_engine* e, const float* h, int M, const float* g, void* xo, f
 // (layer selection).  xa_in / pa_in hold h_in's projection input (attention
 // norm gain) and its partial sums of squares.  g_next != nullptr: also write
 // h_out's projection input with that gain into e->xa / e->pa (rows 0..M-1).
-// Warm the last-level cache with the weights this layer reads after its
-// attention: the O projection, and (prefetch 2) the first 8-row tile of
-// gate and up of every workgroup of the walking gate/up launch.  On the side
-// stream, after the q/k/v launch, concurrent with attention and merge.
-void warm_layer(lss_engine* e, const LayerW& w, int M) {
-  const auto& c = e->cfg;
-  const size_t elt = e->bf16 ? 2 : 4;
-  (void)hipEventRecord(e->ev_q, e->stream);
-  (void)hipStreamWaitEvent(e->side, e->ev_q, 0);
-  const size_t o16 = (size_t)c.d_model * c.n_heads * c.head_dim * elt / 16;
-  hipLaunchKernelGGL(k_warm, dim3(256), dim3(WARM_THREADS), 0, e->side, (const uint4*)w.wo, o16, o16, 1);
-  if (e->prefetch >= 2) {
-    const int ntile = c.ffn_dim / 8;
-    const int G = gemv_grid(ntile, e->gvl.ncu, e->gvl.gmax_cu, 1);
-    if (G < ntile && ntile % G == 0) {           // equal walks: first tiles ntile / G apart
-      const size_t row16 = (size_t)c.d_model * elt / 16;
-      for (const void* m : {w.wg, w.wu})
-        hipLaunchKernelGGL(k_warm, dim3(256), dim3(WARM_THREADS), 0, e->side, (const uint4*)m, 8 * row16,
-                           (size_t)(ntile / G) * 8 * row16, G);
-    }
-  }
-  (void)hipEventRecord(e->ev_w, e->side);
-  e->side_pending = true;
-  (void)M;
-}
-
 void layer_forward(lss_engine* e, int l, int M, const float* h_in, const void* xa_in, const float* pa_in,
                    float* h_out, const float* g_next, int mode, int pos0, int quant) {
   const auto& c = e->cfg;
@@ -662,7 +622,6 @@ void layer_forward(lss_engine* e, int l, int M, const float* h_in, const void* x
     ga.w[2] = w.wv; ga.nseg[2] = kvd;
     gemm<EPI_STORE>(e, ga);
   }
-  if (e->prefetch && e->side && e->gemv && M <= GV_MB_MAX) warm_layer(e, w, M);
   if (e->bf16) attention_w<uint16_t>(e, l, M, mode, pos0, quant);
   else attention_w<float>(e, l, M, mode, pos0, quant);
   if (quant) quant_rows(e, e->aout, M, qd, e->xb);
@@ -703,7 +662,6 @@ void layer_forward(lss_engine* e, int l, int M, const float* h_in, const void* x
 // res->sample[row0 + m] with its log-sum-exp; a draft row keeps its logits
 // in the window slot row0 of e->dlogits.
 void head(lss_engine* e, int r0, int M, int row0, int pos0, bool draft) {
-  side_join(e);
   const auto& c = e->cfg;
   const bool samp = e->inv_t > 0.f;
   float* Y = (samp && draft) ? e->dlogits + (size_t)row0 * c.vocab : e->logits;
@@ -750,7 +708,6 @@ void forward_rows(lss_engine* e, const int32_t* tok_dev, int M, int pos0, int mo
 }
 
 int sync_res(lss_engine* e) {
-  side_join(e);
   HIPCHK(hipMemcpyAsync(e->hres, e->res, sizeof(HeadRes), hipMemcpyDeviceToHost, e->stream));
   HIPCHK(hipStreamSynchronize(e->stream));
   if (e->ev_used) prof_resolve(e);
@@ -875,14 +832,7 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
 
 void lss_destroy(lss_engine* e) {
   if (!e) return;
-  side_join(e);
   (void)hipStreamSynchronize(e->stream);
-  if (e->side) {
-    (void)hipStreamSynchronize(e->side);
-    (void)hipEventDestroy(e->ev_q);
-    (void)hipEventDestroy(e->ev_w);
-    (void)hipStreamDestroy(e->side);
-  }
   for (auto ev : e->ev_start) (void)hipEventDestroy(ev);
   for (auto ev : e->ev_stop) (void)hipEventDestroy(ev);
   if (e->hres) (void)hipHostFree(e->hres);
@@ -983,26 +933,6 @@ int lss_set_sampling(lss_engine* e, float temperature, uint64_t seed) {
   if (temperature > 0.f && !std::isfinite(inv)) return fail(e, LSS_EINVAL, "set_sampling: temperature too small");
   e->inv_t = inv;
   e->seed = seed;
-  return LSS_OK;
-}
-
-int lss_set_prefetch(lss_engine* e, int32_t mode) {
-  if (!e) return LSS_EINVAL;
-  if (mode < 0 || mode > 2) return fail(e, LSS_EINVAL, "set_prefetch: mode must be 0, 1 or 2");
-  if (mode > 0 && !e->side) {
-    if (hipStreamCreateWithFlags(&e->side, hipStreamNonBlocking) != hipSuccess) {
-      e->side = nullptr;
-      return fail(e, LSS_EHIP, "set_prefetch: stream creation failed");
-    }
-    if (hipEventCreateWithFlags(&e->ev_q, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&e->ev_w, hipEventDisableTiming) != hipSuccess) {
-      (void)hipStreamDestroy(e->side);
-      e->side = nullptr;
-      return fail(e, LSS_EHIP, "set_prefetch: event creation failed");
-    }
-  }
-  side_join(e);
-  e->prefetch = mode;
   return LSS_OK;
 }
 

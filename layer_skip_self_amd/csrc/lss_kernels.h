@@ -1539,32 +1539,6 @@ __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
   else a.out[(size_t)m * a.Hq * HD + (size_t)h * HD + tid] = o;
 }
 
-// ---------------------------------------------------------------- cache warming
-// Reads nseg segments of seg16 16-byte words, segment s at p + s * stride16,
-// with plain loads (which allocate in the last-level cache) and discards
-// them.  Launched on a second stream while a layer's attention leaves HBM
-// mostly idle, it brings the weights of the next projections into the
-// cache; it writes nothing.
-#define WARM_THREADS 256
-#define WARM_U 8
-__global__ __launch_bounds__(WARM_THREADS) void k_warm(const uint4* __restrict__ p, size_t seg16, size_t stride16,
-                                                       int nseg) {
-  const size_t total = seg16 * (size_t)nseg;
-  const size_t step = (size_t)gridDim.x * WARM_THREADS * WARM_U;
-  uint32_t acc = 0;
-  for (size_t i0 = (size_t)blockIdx.x * WARM_THREADS * WARM_U + threadIdx.x; i0 < total; i0 += step) {
-    uint4 v[WARM_U];
-#pragma unroll
-    for (int u = 0; u < WARM_U; ++u) {
-      const size_t i = min(i0 + (size_t)u * WARM_THREADS, total - 1);
-      v[u] = p[(i / seg16) * stride16 + i % seg16];
-    }
-#pragma unroll
-    for (int u = 0; u < WARM_U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
-  asm volatile("" ::"v"(acc));   // keeps the loads; nothing is stored
-}
-
 // ---------------------------------------------------------------- LM head reduce / accept
 struct HeadRes {                 // device result block, mirrored to the host
   int32_t n, bonus, argmax[64];

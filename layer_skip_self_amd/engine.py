@@ -103,11 +103,6 @@ class Engine:
         most n workgroups per compute unit walking tile ranges (same bits)."""
         self._check(self.lib.lss_set_gemv_grid(self.h, int(wgs_per_cu)), "lss_set_gemv_grid")
 
-    def set_prefetch(self, mode):
-        """Cache warming of the O (1) and first gate/up (2) weights during
-        attention, on a second stream; 0 turns it off.  Outputs unchanged."""
-        self._check(self.lib.lss_set_prefetch(self.h, int(mode)), "lss_set_prefetch")
-
     def prefill(self, tokens):
         a, p = _i32(tokens)
         t0 = C.c_int32()

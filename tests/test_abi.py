@@ -35,7 +35,6 @@ def test_library_exports_every_declared_symbol():
 def test_null_engine_calls_are_rejected():
     lib = N.load()
     assert lib.lss_set_gemv_grid(None, 1) == N.LSS_EINVAL
-    assert lib.lss_set_prefetch(None, 1) == N.LSS_EINVAL
     assert lib.lss_set_sampling(None, 1.0, 0) == N.LSS_EINVAL
 
 

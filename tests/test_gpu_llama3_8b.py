@@ -90,32 +90,6 @@ def test_gemv_grid_policies_bitwise_equal_8b(gpu8b, grid):
         eng.set_gemv_grid(1)
 
 
-@pytest.mark.parametrize("mode", [1, 2])
-def test_cache_warming_changes_no_output_8b(gpu8b, mode):
-    """Warming the O and gate/up weights on a second stream during attention
-    reads weights only: verify logits (1 and 5 rows) and the speculative and
-    greedy tokens equal those without it, bit for bit."""
-    eng, prompt = gpu8b["eng"], gpu8b["prompt"]
-    out = {}
-    try:
-        for m in (0, mode):
-            eng.set_prefetch(m)
-            zs = []
-            for rows in (1, 5):
-                eng.prefill(prompt)
-                eng.verify(drafts=list(range(21, 21 + rows - 1)))
-                zs.append(eng.read_logits(rows))
-                eng.accept()
-            ar, _ = eng.generate(prompt, 24, {"mode": "ar"})
-            sp, _ = eng.generate(prompt, 24, BENCH_POLICY)
-            out[m] = (zs, ar, sp)
-        for a, b in zip(out[0][0], out[mode][0]):
-            assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
-        assert out[0][1] == out[mode][1] == out[0][2] == out[mode][2]
-    finally:
-        eng.set_prefetch(0)
-
-
 def test_empty_mask_draft_accepted_in_full_8b(gpu8b):
     eng = gpu8b["eng"]
     eng.prefill(gpu8b["prompt"])
