@@ -1876,63 +1876,44 @@ __global__ __launch_bounds__(PREP_THREADS) void k_dp_select(const float* __restr
                                                    const float* __restrict__ H, int d, int lo_i,
                                                    float* __restrict__ gn, float* __restrict__ dec,
                                                    const float* __restrict__ g, void* xo, float* __restrict__ po) {
-  constexpr int NW = PREP_THREADS / 64;
-  __shared__ float red[5][NW];
+  __shared__ float red[4];
+  __shared__ int take_s;
   const int j = lo_i + blockIdx.x;
   const bool eok = j >= ex_lo && j <= ex_hi;
   const bool sok = (j - 1) >= lo_p && (j - 1) <= hi_p;
   const float* e = eok ? ex + (size_t)(j - ex_lo) * d : nullptr;
   const float* s = sok ? gp + (size_t)(j - 1 - lo_p) * d : nullptr;
-  // the three rows' elements i = tid + PREP_THREADS jj, loaded before use
-  float hv[PREP_PER_THREAD], ev[PREP_PER_THREAD], sv[PREP_PER_THREAD];
-#pragma unroll
-  for (int jj = 0; jj < PREP_PER_THREAD; ++jj) {
-    const int i = threadIdx.x + jj * PREP_THREADS;
-    hv[jj] = i < d ? H[i] : 0.f;
-    ev[jj] = (eok && i < d) ? e[i] : 0.f;
-    sv[jj] = (sok && i < d) ? s[i] : 0.f;
-  }
   float hh = 0.f, eh = 0.f, ee = 0.f, sh = 0.f, ss = 0.f;
-#pragma unroll
-  for (int jj = 0; jj < PREP_PER_THREAD; ++jj) {
-    if (threadIdx.x + jj * PREP_THREADS < d) {
-      hh = fmaf(hv[jj], hv[jj], hh);
-      if (eok) { eh = fmaf(ev[jj], hv[jj], eh); ee = fmaf(ev[jj], ev[jj], ee); }
-      if (sok) { sh = fmaf(sv[jj], hv[jj], sh); ss = fmaf(sv[jj], sv[jj], ss); }
-    }
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    const float hv = H[i];
+    hh = fmaf(hv, hv, hh);
+    if (eok) { const float v = e[i]; eh = fmaf(v, hv, eh); ee = fmaf(v, v, ee); }
+    if (sok) { const float v = s[i]; sh = fmaf(v, hv, sh); ss = fmaf(v, v, ss); }
   }
-  // five block sums in one exchange: wave sums, then waves in index order
-  // from 0 (the order of block_sum)
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const float ws[5] = {wave_sum(hh), wave_sum(eh), wave_sum(ee), wave_sum(sh), wave_sum(ss)};
-  if (lane == 0) {
-#pragma unroll
-    for (int q = 0; q < 5; ++q) red[q][wv] = ws[q];
-  }
-  __syncthreads();
-  float t[5];
-#pragma unroll
-  for (int q = 0; q < 5; ++q) {
-    t[q] = 0.f;
-    for (int w = 0; w < NW; ++w) t[q] += red[q][w];
-  }
-  hh = t[0]; eh = t[1]; ee = t[2]; sh = t[3]; ss = t[4];
+  hh = block_sum(hh, red);
+  eh = block_sum(eh, red);
+  ee = block_sum(ee, red);
+  sh = block_sum(sh, red);
+  ss = block_sum(ss, red);
   const float nh = __fsqrt_rn(hh);
   const float ce = eok ? __fdiv_rn(eh, __fmul_rn(__fsqrt_rn(ee), nh)) : NAN;
   const float cs = sok ? __fdiv_rn(sh, __fmul_rn(__fsqrt_rn(ss), nh)) : NAN;
-  const bool take = sok && (!eok || cs > ce);            // the same decision in every thread
   if (threadIdx.x == 0) {
+    const int take = sok && (!eok || cs > ce);
+    take_s = take;
     dec[(size_t)j * 3 + 0] = (float)take;
     dec[(size_t)j * 3 + 1] = cs;
     dec[(size_t)j * 3 + 2] = ce;
   }
+  __syncthreads();
+  const float* src = take_s ? s : e;
   const int row = j - lo_i;
   float* dst = gn + (size_t)row * d;
   float v[PREP_PER_THREAD];
+  load_vals<float>(v, src, d);
 #pragma unroll
   for (int jj = 0; jj < PREP_PER_THREAD; ++jj) {
     const int i = threadIdx.x + jj * PREP_THREADS;
-    v[jj] = take ? sv[jj] : ev[jj];
     if (i < d) dst[i] = v[jj];
   }
   if (xo) prep_vals<WT>(v, d, g, xo, po, row);
