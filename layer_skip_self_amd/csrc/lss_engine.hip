@@ -476,16 +476,17 @@ void attention(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
   a.nch = std::max(1, (kmax + ATT_CH - 1) / ATT_CH);
   const int G = c.n_heads / c.n_kv_heads;
   a.nz = (G * M + ATT_QB - 1) / ATT_QB;
+  const int mq = std::min(ATT_QB, G * M);             // merge workgroups per query block and kv head
   const dim3 grid(a.nch, c.n_kv_heads, a.nz);
   const bool tree = mode == MODE_TREE;
   if (hd == 128) {
     if (tree) hipLaunchKernelGGL((k_attention<KT, WT, 128, true>), grid, dim3(ATT_THREADS), 0, e->stream, a);
     else hipLaunchKernelGGL((k_attention<KT, WT, 128>), grid, dim3(ATT_THREADS), 0, e->stream, a);
-    hipLaunchKernelGGL((k_attn_merge<WT, 128>), dim3(ATT_QB, c.n_kv_heads, a.nz), dim3(128), 0, e->stream, a);
+    hipLaunchKernelGGL((k_attn_merge<WT, 128>), dim3(mq, c.n_kv_heads, a.nz), dim3(128), 0, e->stream, a);
   } else {
     if (tree) hipLaunchKernelGGL((k_attention<KT, WT, 64, true>), grid, dim3(ATT_THREADS), 0, e->stream, a);
     else hipLaunchKernelGGL((k_attention<KT, WT, 64>), grid, dim3(ATT_THREADS), 0, e->stream, a);
-    hipLaunchKernelGGL((k_attn_merge<WT, 64>), dim3(ATT_QB, c.n_kv_heads, a.nz), dim3(64), 0, e->stream, a);
+    hipLaunchKernelGGL((k_attn_merge<WT, 64>), dim3(mq, c.n_kv_heads, a.nz), dim3(64), 0, e->stream, a);
   }
 }
 
