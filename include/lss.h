@@ -242,14 +242,15 @@ int lss_profile_kernel(lss_engine* e, int32_t epilogue, int32_t rows, int32_t en
 int lss_profile_read(lss_engine* e, double* total_ms, int64_t* launches, int64_t* bytes);
 
 /* Grid of the decode GEMV (the vector-ALU projection of draft, greedy and
- * verify rows): wgs_per_cu = 0 launches one workgroup per weight tile;
- * wgs_per_cu > 0 launches at most that many workgroups per compute unit
- * (capped by the kernel's occupancy), each walking a contiguous range of
- * tiles with its weight loads kept in flight across tile boundaries.  The
- * arithmetic of every output is the same under either grid, so results are
- * identical bit for bit; only the time changes.  The default is the tile
- * walk with 1 workgroup per compute unit.  LSS_EINVAL for a negative value
- * or a value above 8. */
+ * verify rows): wgs_per_cu = 0 launches one workgroup per weight tile.
+ * wgs_per_cu > 0 allows at most that many workgroups per compute unit
+ * (capped by the kernel's occupancy): launches with more than 4 times that
+ * many tiles then run that many workgroups, each walking a contiguous range
+ * of tiles with its weight loads kept in flight across tile boundaries;
+ * smaller launches keep one workgroup per tile.  The arithmetic of every
+ * output is the same under any grid, so results are identical bit for bit;
+ * only the time changes.  The default is 1.  LSS_EINVAL for a negative
+ * value or a value above 8. */
 int lss_set_gemv_grid(lss_engine* e, int32_t wgs_per_cu);
 
 /* Stand-alone dynamic per-token int8 quantization (CAS-Spec blog section
