@@ -1203,7 +1203,7 @@ __global__ __launch_bounds__(G8_THREADS) void k_gemv8(GemmArgs ga) {
 // plain step at pos0 + 1 after that candidate, bit for bit.
 #define ATT_CH 64
 #define ATT_QB 32
-#define ATT_THREADS 256
+#define ATT_THREADS 512
 // row stride (floats) of the LDS key / value tile: 16-byte rows for vector
 // stores and score reads, rows 4 banks apart (a key per lane reads without
 // bank conflicts)
