@@ -305,8 +305,12 @@ int gemv_cap(int K, int wbytes) {
   return ncw == 1 ? GV_MB_MAX : std::max(1, std::min(4, GV_ACT_MAX / ncw));
 }
 
-// 8-row tiles where the epilogue has no per-16-column partials
-template <int EPI> constexpr int gemv_tile() { return (EPI == EPI_STORE || EPI == EPI_SWIGLU) ? 8 : 16; }
+// 8-row tiles for gate/up and for one-row q/k/v launches (more workgroups);
+// 16-row tiles otherwise (multi-row q/k/v measured faster with them).  The
+// tile size does not change any output bit.
+template <int EPI, int MB> constexpr int gemv_tile() {
+  return (EPI == EPI_SWIGLU || (EPI == EPI_STORE && MB == 1)) ? 8 : 16;
+}
 
 // Workgroups of one decode-GEMV launch.  gmax_cu = 0: one per tile.
 // Otherwise, with at most gmax = gmax_cu workgroups per compute unit (capped
@@ -323,8 +327,9 @@ int gemv_grid(int ntile, int ncu, int gmax_cu, int occ) {
   return (ntile + per - 1) / per;
 }
 
-template <typename WT, int MB, int NCW, int EPI, int TR>
+template <typename WT, int MB, int NCW, int EPI>
 void gemv_go(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  constexpr int TR = gemv_tile<EPI, MB>();
   static const int occ = [] {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_gemv<WT, MB, NCW, EPI, TR>, 64 * GV_WAVES, 0) !=
@@ -339,19 +344,18 @@ void gemv_go(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t 
 
 template <typename WT, int EPI, int NCW>
 void gemv_launch(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  constexpr int TR = gemv_tile<EPI>();
   if constexpr (NCW == 1) {
-    if (g.M == 1) gemv_go<WT, 1, 1, EPI, TR>(g, gl, s, t0, t1);
-    else if (g.M == 2) gemv_go<WT, 2, 1, EPI, TR>(g, gl, s, t0, t1);
-    else if (g.M <= 4) gemv_go<WT, 4, 1, EPI, TR>(g, gl, s, t0, t1);
-    else gemv_go<WT, 8, 1, EPI, TR>(g, gl, s, t0, t1);
+    if (g.M == 1) gemv_go<WT, 1, 1, EPI>(g, gl, s, t0, t1);
+    else if (g.M == 2) gemv_go<WT, 2, 1, EPI>(g, gl, s, t0, t1);
+    else if (g.M <= 4) gemv_go<WT, 4, 1, EPI>(g, gl, s, t0, t1);
+    else gemv_go<WT, 8, 1, EPI>(g, gl, s, t0, t1);
   } else if constexpr (NCW == 2 || NCW == 4) {
-    if (g.M == 1) gemv_go<WT, 1, NCW, EPI, TR>(g, gl, s, t0, t1);
-    else if (g.M == 2) gemv_go<WT, 2, NCW, EPI, TR>(g, gl, s, t0, t1);
-    else gemv_go<WT, 4, NCW, EPI, TR>(g, gl, s, t0, t1);
+    if (g.M == 1) gemv_go<WT, 1, NCW, EPI>(g, gl, s, t0, t1);
+    else if (g.M == 2) gemv_go<WT, 2, NCW, EPI>(g, gl, s, t0, t1);
+    else gemv_go<WT, 4, NCW, EPI>(g, gl, s, t0, t1);
   } else {
-    if (g.M == 1) gemv_go<WT, 1, 8, EPI, TR>(g, gl, s, t0, t1);
-    else gemv_go<WT, 2, 8, EPI, TR>(g, gl, s, t0, t1);
+    if (g.M == 1) gemv_go<WT, 1, 8, EPI>(g, gl, s, t0, t1);
+    else gemv_go<WT, 2, 8, EPI>(g, gl, s, t0, t1);
   }
 }
 
