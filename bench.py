@@ -93,11 +93,22 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
     import numpy as np
     import lss_synth
     import oracle
+    # BLAS threads: every CPU this process may run on, capped by the CPU
+    # share the environment grants one GPU job (OMP_NUM_THREADS, 16 on the
+    # GPU hosts); the host's total is reported beside it
+    host_cpus = os.cpu_count()
     try:
-        from threadpoolctl import threadpool_info
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = host_cpus
+    share = int(os.environ.get("OMP_NUM_THREADS") or allowed)
+    threads = max(1, min(allowed, share))
+    try:
+        from threadpoolctl import threadpool_limits, threadpool_info
+        limiter = threadpool_limits(limits=threads)
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count()
+        limiter, cores = None, threads
     w_host = [(n, t.to("cpu")) for n, t in w_gpu]
     model = oracle.OracleModel(shape, lss_synth.LazyF32(w_host), dtype=np.float32, cache_layers=True)
     for l in range(shape.n_layers):           # widen every weight once (setup, not timed)
@@ -115,10 +126,14 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
     t0 = time.perf_counter()
     toks, recs = oracle.speculative_generate(model, sample, n_tokens, pol)
     dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {"value": len(toks) / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "host_cpus": host_cpus, "affinity_cpus": allowed, "blas_threads": int(cores),
             "sample": f"oracle float32 speculative decoding (same policy) of {len(toks)} tokens after a "
                       f"{n_prompt}-token prompt of the same workload; prefill + layer selection + "
-                      f"{len(recs)} rounds in {dt:.1f} s"}
+                      f"{len(recs)} rounds in {dt:.1f} s; BLAS threads {cores} = the CPUs this job may "
+                      f"use (affinity {allowed}, job share {share}) of the host's {host_cpus}"}
 
 
 GEMV_SECTIONS = ("scalars", "projection input format", "projections: shared definitions",

@@ -70,23 +70,43 @@ typedef struct lss_config {
 
 typedef struct lss_engine lss_engine;
 
-/* Bytes of device workspace lss_create needs for `cfg` (KV cache, residual
+/* Bytes of device workspace an engine needs for `cfg` (KV cache, residual
  * stash, activations, partial results).  0 if cfg is invalid. */
 size_t lss_workspace_bytes(const lss_config* cfg);
 
-/* load_weights: create an engine over caller-owned device tensors.
- * tensors_dev: n_tensors = 3 + 9*n_layers device pointers in the order
- *   embed [V][d], final_norm [d], lm_head [V][d], then per layer
- *   attn_norm [d], wq [Hq*hd][d], wk [Hkv*hd][d], wv [Hkv*hd][d],
- *   wo [d][Hq*hd], ffn_norm [d], w_gate [F][d], w_up [F][d], w_down [d][F];
- *   matrices row-major [out][in] in cfg->dtype, norm gains float32.
- * workspace_dev: >= lss_workspace_bytes(cfg) bytes of device memory.
- * Both are borrowed (never freed) and must outlive the engine.  The engine
- * allocates only a small pinned host buffer of its own.
- * hip_stream: a hipStream_t (NULL = the null stream). */
+/* One weight tensor handed to lss_load_weights (borrowed, never copied). */
+typedef struct lss_tensor {
+  const char* name;     /* canonical name, see lss_load_weights */
+  const void* dev_ptr;  /* device pointer, 16-byte aligned */
+  int64_t numel;        /* element count, checked against the config */
+} lss_tensor;
+
+/* load_weights: create an engine over an existing model's weights (the
+ * method is plug-and-play over a trained model, no training step: CLaSp
+ * article, introduction and section 3; CAS-Spec abstract).
+ * tensors: n_tensors = 3 + 9*n_layers entries in the canonical order
+ *   "embed" [V][d], "final_norm" [d], "lm_head" [V][d], then for each layer
+ *   l: "layers.<l>.attn_norm" [d], ".wq" [Hq*hd][d], ".wk" [Hkv*hd][d],
+ *   ".wv" [Hkv*hd][d], ".wo" [d][Hq*hd], ".ffn_norm" [d], ".w_gate" [F][d],
+ *   ".w_up" [F][d], ".w_down" [d][F]; matrices row-major [out][in] in
+ *   cfg->dtype, norm gains float32.  A wrong name, element count, null or
+ *   misaligned pointer is LSS_EINVAL.
+ * workspace_dev: >= lss_workspace_bytes(cfg) bytes of device memory, 256-byte
+ *   aligned (LSS_ECAPACITY if smaller).
+ * Weights and workspace are borrowed (never freed) and must outlive the
+ * engine; the engine allocates only two small pinned host buffers of its
+ * own.  hip_stream: a hipStream_t (NULL = the null stream); every later
+ * call of the engine enqueues its device work there.  On failure *out is
+ * NULL and lss_last_error(NULL) describes the failure (per thread). */
+int lss_load_weights(const lss_config* cfg, const lss_tensor* tensors, int32_t n_tensors,
+                     void* workspace_dev, size_t workspace_bytes, void* hip_stream, lss_engine** out);
+/* The same with bare pointers in the canonical order (no name or size
+ * check). */
 int lss_create(const lss_config* cfg, const void* const* tensors_dev, int32_t n_tensors,
                void* workspace_dev, size_t workspace_bytes, void* hip_stream, lss_engine** out);
 void lss_destroy(lss_engine* e);
+/* Message of the engine's last failure; with e == NULL, of this thread's
+ * last failed lss_load_weights / lss_create. */
 const char* lss_last_error(const lss_engine* e);
 
 /* Full-model causal pass over the prompt (row blocks of max_rows).  Resets

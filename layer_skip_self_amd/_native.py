@@ -24,6 +24,10 @@ class lss_config(C.Structure):
                 ("kv_dtype", C.c_int32)]
 
 
+class lss_tensor(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("dev_ptr", C.c_void_p), ("numel", C.c_int64)]
+
+
 class lss_policy(C.Structure):
     _fields_ = [("mode", C.c_int32), ("k_max", C.c_int32), ("exit_tau", C.c_float),
                 ("quant", C.c_int32), ("static_mask", C.POINTER(C.c_uint8)),
@@ -41,6 +45,8 @@ class lss_stats(C.Structure):
 # name -> (restype, argtypes); every symbol include/lss.h declares
 SIGNATURES = {
     "lss_workspace_bytes": (C.c_size_t, [C.POINTER(lss_config)]),
+    "lss_load_weights": (C.c_int, [C.POINTER(lss_config), C.POINTER(lss_tensor), C.c_int32, C.c_void_p,
+                                   C.c_size_t, C.c_void_p, C.POINTER(C.c_void_p)]),
     "lss_create": (C.c_int, [C.POINTER(lss_config), C.POINTER(C.c_void_p), C.c_int32, C.c_void_p,
                              C.c_size_t, C.c_void_p, C.POINTER(C.c_void_p)]),
     "lss_destroy": (None, [C.c_void_p]),

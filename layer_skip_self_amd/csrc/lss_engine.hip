@@ -731,6 +731,14 @@ void fill_u32(lss_engine* e, void* p, size_t n, uint32_t v) {
   if (n) hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, e->stream, (uint32_t*)p, n, v);
 }
 
+// message of the last failed engine creation on this thread (lss_last_error(NULL))
+thread_local std::string g_create_err = "no failure";
+
+int create_fail(int code, const std::string& msg) {
+  g_create_err = msg;
+  return code;
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -745,15 +753,18 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
                size_t workspace_bytes, void* hip_stream, lss_engine** out) {
   lss_engine* e = nullptr;
   std::string why;
-  if (!out) return LSS_EINVAL;
+  if (!out) return create_fail(LSS_EINVAL, "create: null out");
   *out = nullptr;
-  if (!cfg_valid(cfg, &why)) return LSS_EINVAL;
-  if (!tensors || n_tensors != 3 + 9 * cfg->n_layers || !workspace) return LSS_EINVAL;
+  if (!cfg_valid(cfg, &why)) return create_fail(LSS_EINVAL, "create: " + why);
+  if (!tensors || n_tensors != 3 + 9 * cfg->n_layers)
+    return create_fail(LSS_EINVAL, "create: expected 3 + 9 * n_layers tensors");
+  if (!workspace) return create_fail(LSS_EINVAL, "create: null workspace");
   for (int i = 0; i < n_tensors; ++i)
-    if (!tensors[i] || ((uintptr_t)tensors[i] & 15)) return LSS_EINVAL;
-  if (((uintptr_t)workspace & 255)) return LSS_EINVAL;
+    if (!tensors[i] || ((uintptr_t)tensors[i] & 15))
+      return create_fail(LSS_EINVAL, "create: tensor " + std::to_string(i) + " is null or not 16-byte aligned");
+  if (((uintptr_t)workspace & 255)) return create_fail(LSS_EINVAL, "create: workspace not 256-byte aligned");
   const Layout lay = make_layout(cfg);
-  if (workspace_bytes < lay.total) return LSS_ECAPACITY;
+  if (workspace_bytes < lay.total) return create_fail(LSS_ECAPACITY, "create: workspace smaller than lss_workspace_bytes");
 
   e = new lss_engine();
   e->cfg = *cfg;
@@ -801,7 +812,7 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
     for (const void* q : ptrs)
       if (!q) {
         lss_destroy(e);
-        return LSS_EINVAL;
+        return create_fail(LSS_EINVAL, "create: workspace layout has a null buffer");
       }
   }
 
@@ -810,7 +821,7 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
     s = hipHostMalloc((void**)&e->hstage, ((size_t)cfg->max_seq + 64) * sizeof(int32_t), hipHostMallocDefault);
   if (s != hipSuccess) {
     lss_destroy(e);
-    return LSS_EHIP;
+    return create_fail(LSS_EHIP, std::string("create: hipHostMalloc: ") + hipGetErrorString(s));
   }
   // zero the workspace (stale KV rows past the committed length must be finite)
   fill_u32(e, ws, lay.total / 4, 0u);
@@ -828,11 +839,48 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
     if (s == hipSuccess) s = hipGetLastError();
     if (s != hipSuccess) {
       lss_destroy(e);
-      return LSS_EHIP;
+      return create_fail(LSS_EHIP, std::string("create: workspace setup: ") + hipGetErrorString(s));
     }
   }
   *out = e;
   return LSS_OK;
+}
+
+int lss_load_weights(const lss_config* cfg, const lss_tensor* tensors, int32_t n_tensors, void* workspace,
+                     size_t workspace_bytes, void* hip_stream, lss_engine** out) {
+  std::string why;
+  if (!out) return create_fail(LSS_EINVAL, "load_weights: null out");
+  *out = nullptr;
+  if (!cfg_valid(cfg, &why)) return create_fail(LSS_EINVAL, "load_weights: " + why);
+  if (!tensors || n_tensors != 3 + 9 * cfg->n_layers)
+    return create_fail(LSS_EINVAL, "load_weights: expected 3 + 9 * n_layers tensors");
+  const int64_t d = cfg->d_model, F = cfg->ffn_dim, V = cfg->vocab;
+  const int64_t qd = (int64_t)cfg->n_heads * cfg->head_dim, kvd = (int64_t)cfg->n_kv_heads * cfg->head_dim;
+  static const char* const kLayer[9] = {"attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down"};
+  const int64_t layer_numel[9] = {d, qd * d, kvd * d, kvd * d, d * qd, d, F * d, F * d, d * F};
+  std::vector<const void*> ptrs(n_tensors);
+  for (int i = 0; i < n_tensors; ++i) {
+    std::string name;
+    int64_t numel;
+    if (i < 3) {
+      static const char* const kGlobal[3] = {"embed", "final_norm", "lm_head"};
+      name = kGlobal[i];
+      numel = i == 1 ? d : V * d;
+    } else {
+      const int l = (i - 3) / 9, j = (i - 3) % 9;
+      name = "layers." + std::to_string(l) + "." + kLayer[j];
+      numel = layer_numel[j];
+    }
+    const lss_tensor& t = tensors[i];
+    if (!t.name || name != t.name)
+      return create_fail(LSS_EINVAL, "load_weights: tensor " + std::to_string(i) + " must be '" + name + "', got '" +
+                                         (t.name ? t.name : "(null)") + "'");
+    if (t.numel != numel)
+      return create_fail(LSS_EINVAL, "load_weights: '" + name + "' has " + std::to_string(t.numel) +
+                                         " elements, the config implies " + std::to_string(numel));
+    ptrs[i] = t.dev_ptr;
+  }
+  return lss_create(cfg, ptrs.data(), n_tensors, workspace, workspace_bytes, hip_stream, out);
 }
 
 void lss_destroy(lss_engine* e) {
@@ -845,7 +893,7 @@ void lss_destroy(lss_engine* e) {
   delete e;
 }
 
-const char* lss_last_error(const lss_engine* e) { return e ? e->err.c_str() : "null engine"; }
+const char* lss_last_error(const lss_engine* e) { return e ? e->err.c_str() : g_create_err.c_str(); }
 
 int32_t lss_seq_len(const lss_engine* e) { return e ? e->p : -1; }
 
@@ -1082,13 +1130,15 @@ int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k) {
     if (k != e->win) return fail(e, LSS_EINVAL, "verify: k must equal the pending window length");
   }
   if (e->p + k + 1 > c.max_seq) return fail(e, LSS_ECAPACITY, "verify: KV capacity exceeded");
+  if (e->tree > 0 && drafts)
+    return fail(e, LSS_EINVAL, "verify: a tree window is pending; verify it with drafts == NULL");
+  // every check is done: only now may host-forced drafts replace the window
   if (drafts && k > 0) {
     std::memcpy(e->hstage, drafts, sizeof(int32_t) * k);
     HIPCHK(hipMemcpyAsync(e->tok + 1, e->hstage, sizeof(int32_t) * k, hipMemcpyHostToDevice, e->stream));
   }
   const int M = k + 1;
   if (e->tree > 0) {                                   // width-B tree: one pass, tree mask
-    if (drafts) return fail(e, LSS_EINVAL, "verify: a tree window is pending; verify it with drafts == NULL");
     forward_rows(e, e->tok, M, e->p, MODE_TREE);
     head(e, 0, M, 0, e->p, false);
     hipLaunchKernelGGL(k_accept_tree, dim3(1), dim3(1), 0, e->stream, e->res, k, e->tok);

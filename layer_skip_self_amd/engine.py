@@ -56,12 +56,15 @@ class Engine:
             raise LssError("lss_workspace_bytes", N.LSS_EINVAL, "invalid config")
         self._ws = torch.empty(int(nbytes), dtype=torch.uint8, device=device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self._ws.device)
-        ptrs = (C.c_void_p * n)(*[t.data_ptr() for t in self._tensors])
+        self._names = [name.encode() for name, _ in weights]
+        tens = (N.lss_tensor * n)(*[N.lss_tensor(nm, t.data_ptr(), t.numel())
+                                    for nm, t in zip(self._names, self._tensors)])
         h = C.c_void_p()
-        rc = self.lib.lss_create(C.byref(self.cfg), ptrs, n, C.c_void_p(self._ws.data_ptr()), nbytes,
-                                 C.c_void_p(self.stream.cuda_stream), C.byref(h))
+        rc = self.lib.lss_load_weights(C.byref(self.cfg), tens, n, C.c_void_p(self._ws.data_ptr()), nbytes,
+                                       C.c_void_p(self.stream.cuda_stream), C.byref(h))
         if rc != 0:
-            raise LssError("lss_create", rc)
+            msg = self.lib.lss_last_error(None)
+            raise LssError("lss_load_weights", rc, msg.decode() if msg else "")
         self.h = h
 
     # -------------------------------------------------------------- helpers
@@ -151,31 +154,38 @@ class Engine:
                     "lss_select_layers_dp")
         return mask.tolist(), float(score.value)
 
-    def calibrate_latency(self, prompt, seq_lens, depths, reps=3):
+    def calibrate_latency(self, prompt, seq_lens, depths, reps=5):
         """Fit the DyTC latency model t = b0 + b1 * seq_len + b2 * depth
         (CAS-Spec blog, latency prediction section) to timed one-token draft
         steps: for every seq_len, prefill ``prompt[:seq_len]``, then for every
-        depth draft one token with the first ``depth`` layers executed (wall
-        time of ``lss_draft``, which returns after its stream work), verify it
-        and accept.  The first repetition per (seq_len, depth) is not timed.
-        Returns (beta, samples [(seq_len, depth, seconds)], max relative error
-        of the fit over the samples)."""
-        import time
+        depth draft one token with the first ``depth`` layers executed, verify
+        it and accept.  Each draft is timed with HIP events recorded on the
+        engine stream around ``lss_draft``; the first repetition per
+        (seq_len, depth) is not timed and the median of the other ``reps``
+        is one sample.  Returns (beta, samples [(seq_len, depth, seconds)],
+        max relative error of the fit over the samples)."""
+        import torch
         L = self.shape.n_layers
         samples = []
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for s in seq_lens:
             self.prefill(list(prompt[:s]))
             for depth in depths:
                 mask = [0] * int(depth) + [1] * (L - int(depth))
+                times, ps = [], []
                 for r in range(reps + 1):
                     p = self.seq_len
-                    t = time.perf_counter()
+                    ev0.record(self.stream)
                     self.draft(mask, k=1)
-                    dt = time.perf_counter() - t
+                    ev1.record(self.stream)
+                    ev1.synchronize()
+                    dt = ev0.elapsed_time(ev1) * 1e-3
                     self.verify(k=1)
                     self.accept()
                     if r:
-                        samples.append((p, int(depth), dt))
+                        times.append(dt)
+                        ps.append(p)
+                samples.append((int(np.median(ps)), int(depth), float(np.median(times))))
         beta = latency_fit(samples)
         err = max(abs(beta[0] + beta[1] * s + beta[2] * d - t) / t for s, d, t in samples)
         return beta, samples, err

@@ -106,3 +106,37 @@ def test_router_rejects_bad_arguments():
         lss.router_plan([0.5] * 5, [1.0] * 5, 1.0, 8)
     with pytest.raises(lss.LssError):
         lss.router_update([0.5, 0.5], [0, 3], 1)
+
+
+def test_load_weights_checks_names_and_sizes_without_gpu():
+    """lss_load_weights validates every tensor's canonical name and element
+    count before touching a device, and reports why through
+    lss_last_error(NULL)."""
+    sh = lss_synth.SHAPES["tiny"]
+    lib = N.load()
+    cfg = lss.make_config(sh, 64, 8)
+    names = lss_synth.shapes.tensor_names(sh)
+    numel = [int(np.prod(lss_synth.shapes.tensor_shape(sh, nm))) for nm in names]
+    keep = [nm.encode() for nm in names]
+
+    def tensors(nms, sizes):
+        return (N.lss_tensor * len(nms))(*[N.lss_tensor(nm, 0x1000, sz) for nm, sz in zip(nms, sizes)])
+
+    h = C.c_void_p()
+    n = len(names)
+    # correct names and sizes, fake aligned pointers: only the workspace size fails
+    rc = lib.lss_load_weights(C.byref(cfg), tensors(keep, numel), n, C.c_void_p(0x100000), 16, None, C.byref(h))
+    assert rc == N.LSS_ECAPACITY and not h.value
+    bad = list(keep)
+    bad[7] = b"layers.0.wx"
+    rc = lib.lss_load_weights(C.byref(cfg), tensors(bad, numel), n, C.c_void_p(0x100000), 1 << 30, None, C.byref(h))
+    assert rc == N.LSS_EINVAL
+    assert b"layers.0.wo" in lib.lss_last_error(None)
+    sizes = list(numel)
+    sizes[2] -= 1                             # lm_head one element short
+    rc = lib.lss_load_weights(C.byref(cfg), tensors(keep, sizes), n, C.c_void_p(0x100000), 1 << 30, None, C.byref(h))
+    assert rc == N.LSS_EINVAL
+    assert b"lm_head" in lib.lss_last_error(None)
+    rc = lib.lss_load_weights(C.byref(cfg), tensors(keep, numel), n - 1, C.c_void_p(0x100000), 1 << 30, None,
+                              C.byref(h))
+    assert rc == N.LSS_EINVAL

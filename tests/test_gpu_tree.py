@@ -88,13 +88,20 @@ def test_tree_error_paths(tiny):
     with pytest.raises(LssError):
         eng.draft_tree([0, 1, 1, 0], 0, 2)              # greedy only
     eng.set_sampling(0.0)
-    eng.draft_tree([0, 1, 1, 0], 0, 2)
+    cands = eng.draft_tree([0, 1, 1, 0], 0, 2)
     with pytest.raises(LssError):
         eng.draft([0, 1, 1, 0], 0, 1)                   # a tree window is pending
     with pytest.raises(LssError):
         eng.verify(drafts=[1, 2])
+    # the rejected call left the candidates in place: the tree round still
+    # verifies what draft_tree returned, as the oracle's round does
     eng.verify(k=2)
-    eng.accept()
+    got = eng.accept()
+    st, _, _ = oracle.prefill(tiny["model"], prompt, 256)
+    assert oracle.draft_tree(tiny["model"], st, [0, 1, 1, 0], False, 2)[0] == cands
+    logits, states, oc, kv = oracle.verify_tree(tiny["model"], st)
+    n, b, emitted = oracle.accept_tree(st, logits, states, oc, kv)
+    assert got == (n, b, emitted)
     with pytest.raises(LssError):
         eng.generate(prompt, 8, {"mode": "cascade", "k_max": 4, "tree_width": 2, "interval": 4,
                                  "levels": [(2, 0, False)]})
