@@ -30,15 +30,21 @@ WORKLOADS = {
                       policy={"mode": "dp", "k_max": 8, "n_skip": 16, "interval": 32, "exit_tau": 0.7},
                       desc="Llama-3-8B shape, prompt 1024, 512 generated, CLaSp DP skip 16 every 32 "
                            "rounds, exit threshold 0.7, K <= 8"),
+    # Workloads whose verifies carry many rows (K = 6 or 8, token trees) run
+    # the full-model rows on the MFMA decode GEMM (one weight pass for all
+    # rows, measured faster there); the 8B headline verifies about 2 rows per
+    # round, where the vector-ALU GEMV is faster.
     "llama2_7b": dict(shape="llama2_7b", prompt=512, gen=256,
-                      policy={"mode": "static", "k_max": 6, "skip": tuple(range(1, 32, 2))},
+                      policy={"mode": "static", "k_max": 6, "skip": tuple(range(1, 32, 2)),
+                              "decode_kernel": "mfma_verify"},
                       desc="Llama-2-7B shape, prompt 512, 256 generated, static skip of layers 1,3,..,31, K 6"),
     "tiny": dict(shape="tiny", prompt=32, gen=64, policy={"mode": "static", "k_max": 4, "skip": (1, 2)},
                  desc="4-layer float32 model, prompt 32, 64 generated, skip {1,2}, K 4"),
     # Llama-3-70B shape on one GPU (~141 GB of bf16 weights), the CLaSp DP
     # skipping 44 of 80 layers, re-run every 8, 32 or 128 verify rounds.
     "llama3_70b": dict(shape="llama3_70b", prompt=512, gen=256,
-                       policy=[{"mode": "dp", "k_max": 8, "n_skip": 44, "interval": iv} for iv in (8, 32, 128)],
+                       policy=[{"mode": "dp", "k_max": 8, "n_skip": 44, "interval": iv, "decode_kernel": "mfma_verify"}
+                               for iv in (8, 32, 128)],
                        desc="Llama-3-70B shape, prompt 512, 256 generated, CLaSp DP skip 44 of 80, interval "
                             "8 / 32 / 128, K 8"),
     # Supplementary, not the headline configuration: the Llama-3-8B shape with
@@ -76,7 +82,8 @@ WORKLOADS = {
     # Token trees of width 4 (depth 1) with the headline DP draft: the draft's
     # 4 most likely next tokens verified in one pass with a tree mask.
     "llama3_8b_tree": dict(shape="llama3_8b", prompt=1024, gen=512,
-                           policy={"mode": "dp", "k_max": 1, "n_skip": 16, "interval": 32, "tree_width": 4},
+                           policy={"mode": "dp", "k_max": 1, "n_skip": 16, "interval": 32, "tree_width": 4,
+                                   "decode_kernel": "mfma_verify"},
                            desc="Llama-3-8B shape, prompt 1024, 512 generated, CLaSp DP skip 16 every 32 rounds, "
                                 "token tree of width 4 and depth 1 per round"),
     "cascade_8b": dict(shape="llama3_8b", prompt=(128, 512, 2048), gen=256,
@@ -200,6 +207,8 @@ def main():
     ap.add_argument("--gen", type=int, default=None, help="override the generated length (profiling runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--decode-kernel", choices=("vector", "mfma", "mfma_verify"), default=None,
+                    help="override the workload's decode-row kernel (A/B runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this engine runs one sequence on one GPU; --gpus must be 1 "
@@ -228,6 +237,10 @@ def main():
     max_seq = max(lens) + G + 33
     eng = Engine(shape, weights, max_seq=max_seq, max_rows=64)
     policies = [dict(p) for p in (wl["policy"] if isinstance(wl["policy"], list) else [wl["policy"]])]
+    for p in policies:
+        if args.decode_kernel:
+            p["decode_kernel"] = args.decode_kernel
+        p.setdefault("decode_kernel", "vector")
     w8 = any(p.get("quant") == 2 or any(lv[2] == 2 for lv in p.get("levels", [])) for p in policies)
     if w8:
         eng.attach_w8()
@@ -276,7 +289,8 @@ def main():
 
     # the AR leg decodes the same way (greedy, or sampling at the same
     # temperature and seed)
-    ar_pol = {"mode": "ar", "temperature": policies[0].get("temperature", 0.0), "seed": policies[0].get("seed", 0)}
+    ar_pol = {"mode": "ar", "temperature": policies[0].get("temperature", 0.0), "seed": policies[0].get("seed", 0),
+              "decode_kernel": policies[0]["decode_kernel"]}
     sampling = ar_pol["temperature"] > 0
     ar_t, ar_toks = [0.0] * len(prompts), [None] * len(prompts)
     if args.ar_steps > 0:
@@ -353,6 +367,7 @@ def main():
         "lossless": all(r["lossless"] for r in per_run) if args.ar_steps > 0 and not sampling else None,
         "decoding": (f"speculative sampling, temperature {ar_pol['temperature']}, seed {ar_pol['seed']}"
                      if sampling else "greedy"),
+        "decode_kernel": policies[0]["decode_kernel"],
         "mean_accepted": round(accepted / max(rounds, 1), 4),
         "tokens_per_round": round((emitted - n_r) / max(rounds, 1), 4),
         "drafted_per_round": round(drafted / max(rounds, 1), 4),
@@ -365,12 +380,14 @@ def main():
             "bound": "hbm",
             "kernel": (f"k_gemv8<{shape.dtype},SWIGLU>: draft gate/up projection on the int8 weight copy + "
                        "SwiGLU, 1 row" if w8 else
+                       "k_vgemm<SWIGLU,16>: draft gate/up projection (MFMA) + SwiGLU, 1 row"
+                       if policies[0]["decode_kernel"] == "mfma" else
                        f"k_gemv<{shape.dtype},1,1,SWIGLU,8>: draft gate/up projection + SwiGLU, 1 row"),
             "achieved": round(achieved, 1) if achieved else None,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
-            "traffic": recorded_traffic(bytes_per_launch),
+            "traffic": recorded_traffic(bytes_per_launch) if policies[0]["decode_kernel"] != "mfma" or w8 else None,
             "bytes_per_launch": int(bytes_per_launch),
             "avg_launch_us": round(avg_launch_us, 3),
             "launches": k_n,

@@ -273,6 +273,23 @@ int lss_profile_read(lss_engine* e, double* total_ms, int64_t* launches, int64_t
  * value or a value above 8. */
 int lss_set_gemv_grid(lss_engine* e, int32_t wgs_per_cu);
 
+/* Kernel of the decode rows with bf16 weights (projections of draft steps,
+ * verify passes and greedy steps):
+ *   kind 0 (the default): the vector-ALU GEMV for every decode row -- the
+ *     fastest at 1 or 2 rows; rows beyond its register budget (8 at
+ *     K = 4096, 4 at K = 14336, 2 at K = 28672) go to further launches;
+ *   kind 1: the MFMA GEMM for every decode row -- one launch that streams
+ *     each weight byte once for up to 16 rows;
+ *   kind 2: the MFMA GEMM for the full-model rows (verify, greedy steps),
+ *     the vector-ALU GEMV for the draft rows.
+ * Under every kind a verify row gets the bits of the greedy step at the
+ * same position (both are full-model rows); with kinds 0 and 1 a draft that
+ * skips nothing also equals the full model bit for bit.  The kinds differ
+ * in rounding only.  Float32 weights always take the vector-ALU GEMV.
+ * LSS_EINVAL for another kind, LSS_ESTATE while a draft window or verify is
+ * pending. */
+int lss_set_decode_kernel(lss_engine* e, int32_t kind);
+
 /* Stand-alone dynamic per-token int8 quantization (CAS-Spec blog section
  * 2.1): for each of `rows` rows of x_dev[rows][n] (float32), codes q_dev
  * [rows][n] = clamp(rint(x * fl(127/amax)), -127, 127) and scale_dev[rows]

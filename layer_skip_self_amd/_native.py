@@ -63,6 +63,7 @@ SIGNATURES = {
     "lss_seq_len": (C.c_int32, [C.c_void_p]),
     "lss_set_sampling": (C.c_int, [C.c_void_p, C.c_float, C.c_uint64]),
     "lss_set_gemv_grid": (C.c_int, [C.c_void_p, C.c_int32]),
+    "lss_set_decode_kernel": (C.c_int, [C.c_void_p, C.c_int32]),
     "lss_read_logits": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_float)]),
     "lss_read_states": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_float)]),
     "lss_read_dp_decisions": (C.c_int, [C.c_void_p, C.POINTER(C.c_float)]),

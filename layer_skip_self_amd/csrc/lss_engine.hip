@@ -217,6 +217,11 @@ struct lss_engine {
   // through the MFMA kernels
   bool gemv = false;
   GemvLaunch gvl;
+  // decode rows of bf16 weights (lss_set_decode_kernel): MFMA GEMM (one
+  // launch for up to 16 rows) or the vector-ALU GEMV, separately for the
+  // full-model rows (verify, greedy steps) and the draft rows
+  bool decode_mfma = false, draft_mfma = false;
+  bool in_draft = false;       // a draft step is running
   // kernel timing (lss_profile_kernel)
   int prof_epi = -1, prof_rows = 0;
   std::vector<hipEvent_t> ev_start, ev_stop;
@@ -376,6 +381,45 @@ void gemv_mt(const GemmArgs& ga, const GemvLaunch& gl, hipStream_t s, hipEvent_t
   }
 }
 
+// MFMA decode GEMM: one launch for all M <= 16 rows.  Tiles of 32 weight
+// rows where the launch walks tiles anyway (half the activation reads per
+// weight byte), 16 rows otherwise (more workgroups for the short
+// projections) and for gate/up (two weight matrices per tile).  The tile
+// width changes no output bit.
+#ifndef VG_ST
+#define VG_ST 2
+#endif
+template <int EPI, int TN>
+void vgemm_go(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  static const int occ = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_vgemm<EPI, TN, VG_ST>, 64 * (VG_WAVES + 1), 0) !=
+            hipSuccess || nb < 1)
+      nb = 1;
+    return nb;
+  }();
+  // policy > 0: no more workgroups than are resident at once, each walking
+  // an equal share of the tiles (give or take one)
+  const int ntile = (g.N + TN - 1) / TN;
+  int nwg = ntile;
+  if (gl.gmax_cu > 0 && gl.ncu > 0 && ntile > gl.ncu * occ) {
+    const int per = (ntile + gl.ncu * occ - 1) / (gl.ncu * occ);
+    nwg = (ntile + per - 1) / per;
+  }
+  const dim3 grid(nwg), block(64 * (VG_WAVES + 1));
+  launch_k(k_vgemm<EPI, TN, VG_ST>, grid, block, 0, s, t0, t1, g);
+}
+template <int EPI>
+void vgemm(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if constexpr (EPI != EPI_SWIGLU) {
+    if (gl.ncu > 0 && g.N / 32 >= 4 * gl.ncu) {
+      vgemm_go<EPI, 32>(g, gl, s, t0, t1);
+      return;
+    }
+  }
+  vgemm_go<EPI, 16>(g, gl, s, t0, t1);
+}
+
 // Prefill / layer-selection projection: 1/rms rows, split MFMA GEMM, split
 // sum + epilogue.  The timing events (if any) bracket the GEMM launch.
 template <typename WT, int EPI>
@@ -415,9 +459,11 @@ void prof_resolve(lss_engine* e) {
 
 template <int EPI>
 void gemm(lss_engine* e, const GemmArgs& ga) {
-  // draft / verify rows, and any launch of at most 8 rows, take the vector GEMV
-  const bool vec = e->gemv || ga.M <= 8;
-  const bool one_launch = !vec || ga.M <= gemv_cap(ga.K, e->bf16 ? 2 : 4);
+  // draft / verify rows, and any launch of at most 16 (MFMA decode GEMM) or
+  // 8 (vector GEMV) rows, take the decode kernel
+  const bool mf = e->bf16 && (e->in_draft ? e->draft_mfma : e->decode_mfma);
+  const bool vec = e->gemv || ga.M <= (mf ? VG_MMAX : 8);
+  const bool one_launch = !vec || (mf && ga.M <= VG_MMAX) || ga.M <= gemv_cap(ga.K, e->bf16 ? 2 : 4);
   const bool prof = e->prof_epi == EPI && (e->prof_rows == 0 || e->prof_rows == ga.M) && one_launch;
   if (prof) {
     if (e->ev_used == (int)e->ev_start.size()) {
@@ -427,7 +473,8 @@ void gemm(lss_engine* e, const GemmArgs& ga) {
   }
   hipEvent_t t0 = prof ? e->ev_start[e->ev_used] : nullptr, t1 = prof ? e->ev_stop[e->ev_used] : nullptr;
   if (vec) {
-    if (e->bf16) gemv_mt<uint16_t, EPI>(ga, e->gvl, e->stream, t0, t1);
+    if (mf && ga.M <= VG_MMAX) vgemm<EPI>(ga, e->gvl, e->stream, t0, t1);
+    else if (e->bf16) gemv_mt<uint16_t, EPI>(ga, e->gvl, e->stream, t0, t1);
     else gemv_mt<float, EPI>(ga, e->gvl, e->stream, t0, t1);
   } else {
     if (e->bf16) pgemm<uint16_t, EPI>(e, ga, t0, t1);
@@ -719,11 +766,17 @@ int sync_res(lss_engine* e) {
   return LSS_OK;
 }
 
-// draft and verify rows: projections through the vector-ALU GEMV
+// draft and verify rows: projections through the decode kernels
 struct GemvScope {
   lss_engine* e;
-  explicit GemvScope(lss_engine* en) : e(en) { e->gemv = true; }
-  ~GemvScope() { e->gemv = false; }
+  explicit GemvScope(lss_engine* en, bool draft = false) : e(en) {
+    e->gemv = true;
+    e->in_draft = draft;
+  }
+  ~GemvScope() {
+    e->gemv = false;
+    e->in_draft = false;
+  }
 };
 
 void fill_u32(lss_engine* e, void* p, size_t n, uint32_t v) {
@@ -996,6 +1049,16 @@ int lss_set_gemv_grid(lss_engine* e, int32_t wgs_per_cu) {
   return LSS_OK;
 }
 
+int lss_set_decode_kernel(lss_engine* e, int32_t kind) {
+  if (!e) return LSS_EINVAL;
+  if (kind < 0 || kind > 2) return fail(e, LSS_EINVAL, "set_decode_kernel: kind must be 0, 1 or 2");
+  if (e->win > 0 || e->pending_accept)
+    return fail(e, LSS_ESTATE, "set_decode_kernel: a draft window or verify is pending");
+  e->decode_mfma = kind >= 1;
+  e->draft_mfma = kind == 1;
+  return LSS_OK;
+}
+
 int lss_prefill(lss_engine* e, const int32_t* tokens, int32_t n, int32_t* t0_out) {
   if (!e) return LSS_EINVAL;
   const auto& c = e->cfg;
@@ -1035,7 +1098,7 @@ int lss_prefill(lss_engine* e, const int32_t* tokens, int32_t n, int32_t* t0_out
 int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, float exit_tau, int32_t* tokens_out,
               int32_t* k_done) {
   if (!e) return LSS_EINVAL;
-  const GemvScope gv(e);
+  const GemvScope gv(e, true);
   const auto& c = e->cfg;
   if (!e->have_seq || e->pending_accept) return fail(e, LSS_ESTATE, "draft: needs a prefilled sequence and no pending accept");
   if (!mask || k < 0 || quant < 0 || quant > 2) return fail(e, LSS_EINVAL, "draft: bad arguments");
@@ -1084,7 +1147,7 @@ int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, floa
 
 int lss_draft_tree(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t B, int32_t* tokens_out) {
   if (!e) return LSS_EINVAL;
-  const GemvScope gv(e);
+  const GemvScope gv(e, true);
   const auto& c = e->cfg;
   if (!e->have_seq || e->pending_accept || e->win != 0)
     return fail(e, LSS_ESTATE, "draft_tree: needs a prefilled sequence, no pending accept and an empty window");

@@ -1007,6 +1007,301 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
   }
 }
 
+// ---------------------------------------------------------------- decode GEMM (MFMA, up to 16 rows)
+// Y[m][n] = sum_k X[m][k] W[n][k] for the 1 .. 16 rows of a greedy step, a
+// verify pass or a draft step with bf16 weights, in one pass over the
+// weights for any row count (a verify is one forward pass: CLaSp article,
+// section 3).  The activations (projection format, bf16 hi + lo) are the
+// MFMA A operand, the weight rows the B operand of v_mfma_f32_16x16x32_bf16:
+// lane (r, g) supplies activation row r and weight row r at k group g, and
+// receives D[4 g + j][r].  Rows past M are zeros and never stored.
+//
+// Weights are streamed in wide contiguous pieces: one load instruction reads
+// 256 contiguous bytes of each of 4 weight rows (lane l: row l / 16, bytes
+// 16 (l % 16)), which the memory system serves as fast as whole 1 KB rows,
+// unlike the 16-row x 64-byte MFMA operand shape.  A wave writes the
+// pieces of its unit (TN rows x 256 B per matrix) into a wave-private LDS
+// buffer (row stride 272 B: the 16-row operand reads hit 16 distinct bank
+// groups) and reads them back in the operand layout.  The activation
+// operands of a unit come straight from L2 (rows < M only).
+//
+// Work split as in the vector GEMV: tiles of TN weight rows, a workgroup
+// walks a contiguous range of tiles, its VG_WAVES waves split K into fixed
+// contiguous ranges of 128-element pieces, and every wave walks the same
+// number of units per tile (units past its range are empty) with ST units
+// in flight across tile boundaries.  Per (n, m) the arithmetic is fixed by
+// K alone: each wave runs one MFMA chain over its pieces in increasing k,
+// 32 k per step, the hi then the lo part of the activation; the wave sums
+// are added in wave order.  The MFMA's sum for one output does not depend
+// on the row's place in the operand or on the other rows, so a verify row
+// gets the bits of the greedy step at the same position.
+#ifndef VG_WAVES
+#define VG_WAVES 4                     // MFMA waves per workgroup (plus one epilogue wave)
+#endif
+#define VG_PB 256                      // bytes of one weight row per unit (128 bf16)
+#define VG_RS (VG_PB + 16)             // LDS row stride of the transposition buffer
+#define VG_MMAX 16
+
+// one unit of a wave's ring: NI weight loads and the SUB activation
+// operand pairs (hi, lo) of one 128-element piece of K
+template <int NI, int SUB> struct VgUnit {
+  uint4 w[NI];
+  uint4 ah[SUB], al[SUB];
+};
+
+// weight rows of one tile: first row of each 16-row block, per matrix
+// (segments hold multiples of 16 rows; blocks past N read the last block,
+// whose outputs are never stored)
+template <int NACC, int NB, int TN>
+__device__ __forceinline__ void vg_tile_rows(const GemmArgs& ga, int t, const uint16_t* (&wr)[NACC][NB]) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int n0 = min(t * TN + b * 16, ga.N - 16);
+    int seg = 0, nloc = n0;
+    while (seg < 2 && nloc >= ga.nseg[seg]) { nloc -= ga.nseg[seg]; ++seg; }
+    wr[0][b] = reinterpret_cast<const uint16_t*>(ga.w[seg]) + (size_t)nloc * ga.K;
+    if constexpr (NACC == 2) wr[NACC - 1][b] = reinterpret_cast<const uint16_t*>(ga.w2) + (size_t)n0 * ga.K;
+  }
+}
+
+// issue the loads of the unit for piece pc.  Every address is valid and no
+// load is conditional (a conditional load merged with another value makes
+// the compiler wait for it at the merge): lanes of rows >= M read row M - 1
+// (the caller points arow_ptr there) and the steps of a ragged last piece
+// past K read the row's last block; neither result is ever used.
+template <int NACC, int NB, int TN, int NI, int SUB>
+__device__ __forceinline__ void vg_load(VgUnit<NI, SUB>& U, const uint16_t* const (&wr)[NACC][NB], int pc, int K,
+                                        int la, int lc, const char* arow_ptr, int g) {
+  const int k0 = pc * 128;
+  const int kw = min(k0 + lc * 8, K - 8);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int q = i / (TN / 4), row = (i % (TN / 4)) * 4 + la;
+    U.w[i] = ld_nt16(wr[q][row >> 4] + (size_t)(row & 15) * K + kw);
+  }
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) {
+    const int blk = min((k0 + 32 * s) / 8 + g, K / 8 - 1);
+    const uint4* pa = reinterpret_cast<const uint4*>(arow_ptr + (size_t)blk * 32);
+    U.ah[s] = pa[0];
+    U.al[s] = pa[1];
+  }
+}
+
+template <int EPI, int TN, int ST>
+__global__ __launch_bounds__(64 * (VG_WAVES + 1)) void k_vgemm(GemmArgs ga) {
+  constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
+  constexpr int NB = TN / 16;                      // 16-column operand blocks per tile
+  constexpr int NI = NACC * TN / 4;                // load instructions per unit
+  constexpr int SUB = VG_PB / 64;                  // 32-k MFMA steps per unit
+  constexpr int RPP = 64 / TN;                     // epilogue rows per pass of the epilogue wave
+  static_assert(TN == 16 || TN == 32, "tile of 16 or 32 weight rows");
+  __shared__ __align__(16) char wl_s[VG_WAVES][NACC * TN * VG_RS];
+  __shared__ float part_s[2][VG_WAVES][NACC][VG_MMAX][TN];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int M = ga.M, K = ga.K;
+  const int ntile = (ga.N + TN - 1) / TN;
+  const int tb = (int)((long)blockIdx.x * ntile / gridDim.x);
+  const int te = (int)((long)(blockIdx.x + 1) * ntile / gridDim.x);
+  if (tb >= te) return;                            // whole workgroup (grid <= tiles on the host)
+
+  if (wave == VG_WAVES) {
+    // ---- epilogue wave: the only wave that stores.  Loads and stores share
+    // one counter on this chip, so a store among the MFMA waves' loads would
+    // make every later wait for a load a wait for everything.
+    const int n16 = (ga.N + 15) / 16;
+    const int ei = lane % TN;
+    const int npass = (M + RPP - 1) / RPP;
+    // per-row output scale of this lane's rows (pass p: row p RPP + lane / TN)
+    float sc[VG_MMAX / RPP];
+#pragma unroll
+    for (int p = 0; p < VG_MMAX / RPP; ++p)
+      sc[p] = (ga.scale == SCALE_XS) ? ga.xs[min(p * RPP + lane / TN, M - 1)] : 1.0f;
+    const bool norm = ga.scale == SCALE_NORM;
+    const bool scaled = norm || ga.scale == SCALE_XS;
+    if (norm) {
+      // 1 / rms of each row from its per-16-column partial sums of squares
+      // (K <= 8192: at most 8 per lane): lane l adds entries l + 64 j in
+      // order, then the wave's fixed tree.  Four rows' loads are in flight
+      // together; all of it overlaps the MFMA waves' first tile.
+      const int T = K >> 4;
+      for (int m0 = 0; m0 < M; m0 += 4) {
+        float pv[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            pv[i][j] = ga.pin[(size_t)min(m0 + i, M - 1) * T + min(lane + 64 * j, T - 1)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (lane + 64 * j < T) v = __fadd_rn(v, pv[i][j]);
+          v = wave_sum(v);
+          const float rs = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(v, (float)K), ga.eps)));
+#pragma unroll
+          for (int p = 0; p < VG_MMAX / RPP; ++p)
+            if (m0 + i == p * RPP + lane / TN) sc[p] = rs;
+        }
+      }
+    }
+    // residual inputs and next-norm gains of a tile, loaded one tile ahead
+    float rv[VG_MMAX / RPP], gv = 1.f;
+    auto load_resid = [&](int t) {
+      if constexpr (EPI == EPI_RESID) {
+        const int n = min(t * TN + ei, ga.N - 1);
+        gv = ga.go ? ga.go[n] : 1.f;
+#pragma unroll
+        for (int p = 0; p < VG_MMAX / RPP; ++p)
+          rv[p] = ga.R[(size_t)min(p * RPP + lane / TN, M - 1) * ga.ldr + n];
+      }
+    };
+    load_resid(tb);
+    for (int t = tb; t < te; ++t) {
+      const int par = (t - tb) & 1;
+      __syncthreads();                             // the MFMA waves' partials of tile t are in part_s[par]
+      const int tile0 = t * TN;
+      float rcur[VG_MMAX / RPP], gcur = gv;
+#pragma unroll
+      for (int p = 0; p < VG_MMAX / RPP; ++p) rcur[p] = (EPI == EPI_RESID) ? rv[p] : 0.f;
+      if (t + 1 < te) load_resid(t + 1);
+#pragma unroll
+      for (int p = 0; p < VG_MMAX / RPP; ++p) {
+        if (p < npass) {                           // wave-uniform
+          const int m = p * RPP + lane / TN;
+          // whole 16-column groups inside N, rows inside M (uniform per 16 lanes)
+          if (m < M && tile0 + (ei & ~15) < ga.N) {
+            float y[NACC];
+#pragma unroll
+            for (int q = 0; q < NACC; ++q) {
+              float v = part_s[par][0][q][m][ei];
+#pragma unroll
+              for (int w = 1; w < VG_WAVES; ++w) v = __fadd_rn(v, part_s[par][w][q][m][ei]);
+              y[q] = scaled ? __fmul_rn(v, sc[p]) : v;
+            }
+            proj_out<uint16_t, EPI>(ga, m, M, tile0 + ei, ei & 15, (tile0 + (ei & ~15)) / 16, n16, y[0],
+                                    NACC == 2 ? y[NACC - 1] : 0.f, EPI == EPI_RESID, rcur[p], gcur);
+          }
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- MFMA waves: loads, LDS transposition, MFMA; no global stores
+  const int npc = (K + 127) >> 7;                  // 128-element pieces of a row
+  const int p0 = wave * npc / VG_WAVES;
+  const int np = (wave + 1) * npc / VG_WAVES - p0; // pieces of this wave
+  const int nmax = (npc + VG_WAVES - 1) / VG_WAVES;
+  const int NUP = (nmax + ST - 1) / ST * ST;       // units per tile (every wave), a multiple of ST
+  const int la = lane >> 4, lc = lane & 15;        // load role: row la of 4, 16-byte piece lc
+  const int r = lane & 15, g = lane >> 4;          // operand role: row / column r, k group g
+  char* wl = wl_s[wave];
+  const char* arow_ptr = reinterpret_cast<const char*>(ga.A) + (size_t)min(r, M - 1) * ga.lda * 4;
+
+  const uint16_t* cw[NACC][NB];
+  vg_tile_rows<NACC, NB, TN>(ga, tb, cw);
+  VgUnit<NI, SUB> ring[ST];
+  // the piece a ring slot loads for unit u: units past the wave's range
+  // re-read its last piece (an L2 hit, never used), so that every refill is
+  // issued and the count of loads in flight is the same on every path
+  const int plast = p0 + max(np, 1) - 1;
+  // slot by slot, in order (the scheduler may not interleave the slots'
+  // loads: the first unit's wait would then cover the whole ring)
+#pragma unroll
+  for (int d = 0; d < ST; ++d) {
+    vg_load<NACC, NB, TN>(ring[d], cw, min(p0 + d, plast), K, la, lc, arow_ptr, g);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  for (int t = tb; t < te; ++t) {
+    const int par = (t - tb) & 1;
+    const bool has_next = t + 1 < te;
+    const uint16_t* nw[NACC][NB];
+#pragma unroll
+    for (int q = 0; q < NACC; ++q)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) nw[q][b] = cw[q][b];
+    if (has_next) vg_tile_rows<NACC, NB, TN>(ga, t + 1, nw);
+    f32x4 acc[NACC][NB];
+#pragma unroll
+    for (int q = 0; q < NACC; ++q)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[q][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u0 = 0; u0 < NUP; u0 += ST) {
+#pragma unroll
+      for (int d = 0; d < ST; ++d) {
+        const int u = u0 + d;
+        if (u < np) {                              // wave-uniform
+          // weights of the unit -> LDS (rows x 256 B), then the operand layout.
+          // The buffer is private to the wave and LDS operations of a wave
+          // complete in order, so no barrier is needed; the wavefront-scope
+          // fences only keep the compiler from moving the previous unit's
+          // reads past these writes or these writes past the reads below.
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            const int q = i / (TN / 4), row = (i % (TN / 4)) * 4 + la;
+            *reinterpret_cast<uint4*>(wl + (q * TN + row) * VG_RS + lc * 16) = ring[d].w[i];
+          }
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          const int k0 = (p0 + u) * 128;
+#pragma unroll
+          for (int s = 0; s < SUB; ++s) {
+            if (k0 + 32 * s < K) {                 // wave-uniform
+              const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, ring[d].ah[s]);
+              const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, ring[d].al[s]);
+#pragma unroll
+              for (int q = 0; q < NACC; ++q)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                  const uint4 wf =
+                      *reinterpret_cast<const uint4*>(wl + (q * TN + b * 16 + r) * VG_RS + s * 64 + g * 16);
+                  const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, wf);
+                  acc[q][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bw, acc[q][b], 0, 0, 0);
+                  acc[q][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bw, acc[q][b], 0, 0, 0);
+                }
+            }
+          }
+        }
+        // refill this ring slot, unconditionally: the unit ST ahead, in this
+        // tile or the next (after the last tile: this tile's rows again)
+        const int un = u + ST;
+        const bool nxt = un >= NUP && has_next;
+        const int uu = un >= NUP ? un - NUP : un;
+        {
+          const uint16_t* lw[NACC][NB];
+#pragma unroll
+          for (int q = 0; q < NACC; ++q)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) lw[q][b] = nxt ? nw[q][b] : cw[q][b];
+          vg_load<NACC, NB, TN>(ring[d], lw, min(p0 + uu, plast), K, la, lc, arow_ptr, g);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    // wave partials -> LDS: lane (r, g) holds D[4 g + j][column r] of each block
+#pragma unroll
+    for (int q = 0; q < NACC; ++q)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * g + j < M) part_s[par][wave][q][4 * g + j][b * 16 + r] = acc[q][b][j];
+    // one barrier per tile: part_s[par] is rewritten two tiles later, after
+    // the next tile's barrier, which the epilogue wave reaches only after
+    // finishing this tile's epilogue
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NACC; ++q)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) cw[q][b] = nw[q][b];
+  }
+}
+
 // ---------------------------------------------------------------- int8 decode GEMV (W8A8 draft)
 // One activation row against int8 weight rows with one float32 scale per row:
 //   y[n] = fl32(fl32(acc_n) * fl32(s_n * s_x)),   acc_n = sum_k q[k] w[n][k],

@@ -106,6 +106,14 @@ class Engine:
         most n workgroups per compute unit walking tile ranges (same bits)."""
         self._check(self.lib.lss_set_gemv_grid(self.h, int(wgs_per_cu)), "lss_set_gemv_grid")
 
+    DECODE_KERNELS = {"vector": 0, "mfma": 1, "mfma_verify": 2}
+
+    def set_decode_kernel(self, kind):
+        """Decode rows with bf16 weights: "vector" (the vector-ALU GEMV, the
+        default), "mfma" (one MFMA GEMM launch for up to 16 rows) or
+        "mfma_verify" (MFMA for verify and greedy rows, vector for drafts)."""
+        self._check(self.lib.lss_set_decode_kernel(self.h, self.DECODE_KERNELS[kind]), "lss_set_decode_kernel")
+
     def prefill(self, tokens):
         a, p = _i32(tokens)
         t0 = C.c_int32()
@@ -194,6 +202,8 @@ class Engine:
         """Prefill + decoding of n_gen tokens under ``policy`` (``make_policy``;
         its ``temperature`` / ``seed`` select greedy decoding or sampling)."""
         self.set_sampling(policy.get("temperature", 0.0), policy.get("seed", 0))
+        if "decode_kernel" in policy:
+            self.set_decode_kernel(policy["decode_kernel"])
         a, p = _i32(prompt)
         pol = make_policy(policy, self.shape.n_layers)
         out = np.zeros(n_gen, np.int32)

@@ -43,6 +43,12 @@ SHAPES = {
     # 4 layers, d 256, 4 MHA heads of 64, SwiGLU 688, vocab 1024, fp32.
     "tiny": ModelShape("tiny", 4, 256, 4, 4, 64, 688, 1024, 1e4, "f32",
                        weight_seed=1, prompt_seed=101),
+    # Small bf16 model for fast edge cases of the bf16 decode kernels: 3 L,
+    # d 320, 5 q heads / 1 kv head of 64 (GQA 5), SwiGLU 864, vocab 1008.  Its
+    # projection depths (320, 864) are not whole numbers of 128-element
+    # pieces, and some waves of a decode launch get no piece of K at all.
+    "small_bf16": ModelShape("small_bf16", 3, 320, 5, 1, 64, 864, 1008, 1e4, "bf16",
+                             weight_seed=11, prompt_seed=111),
     # Llama-2-7B shape: 32 L, d 4096, 32 MHA heads, FFN 11008, vocab 32000.
     "llama2_7b": ModelShape("llama2_7b", 32, 4096, 32, 32, 128, 11008, 32000, 1e4, "bf16",
                             weight_seed=2, prompt_seed=102),

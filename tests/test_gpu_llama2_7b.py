@@ -103,6 +103,8 @@ def test_static_draft_logits_vs_oracle_7b(gpu7b, oracle7b):
 
 
 def test_teacher_forced_verify_logits_vs_oracle_7b(gpu7b, oracle7b):
+    """A 7-row verify (this workload's K = 6) of the oracle's greedy tokens
+    against the oracle's full-model rows."""
     import copy
     eng, model = gpu7b["eng"], oracle7b["model"]
     so = copy.deepcopy(oracle7b["st"])
@@ -110,16 +112,26 @@ def test_teacher_forced_verify_logits_vs_oracle_7b(gpu7b, oracle7b):
     if t0 != so.t0:
         pytest.skip("first token is a near-tie between the two paths")
     toks, zs = [so.t0], []
-    for _ in range(4):
+    for _ in range(7):
         zz, _ = oracle.forward_row(model, so, so.t0, so.p, "full")
         zs.append(zz)
         so.p += 1
         so.t0 = int(np.argmax(zz))
         toks.append(so.t0)
-    eng.verify(toks[1:4])
-    zg = eng.read_logits(4)
+    eng.verify(toks[1:7])
+    zg = eng.read_logits(7)
     eng.accept()
-    for i in range(4):
+    for i in range(7):
         err = float(np.max(np.abs(zg[i] - zs[i])))
         print(f"verify row {i}: max-abs {err:.3e}")
         assert err <= TOL
+
+
+def test_greedy_token_ids_vs_oracle_7b(gpu7b, oracle7b):
+    """The token rule of the parity protocol over 41 greedy positions,
+    teacher-forced along the GPU's own sequence."""
+    from conftest import greedy_ids_vs_oracle
+    n, total, worst = greedy_ids_vs_oracle(gpu7b["eng"], oracle7b["model"], gpu7b["prompt"], oracle7b["st"],
+                                           oracle7b["z"], 40, TOL)
+    print(f"{n} of {total} token ids compared (the rest within 1e-2 of a tie); logits max-abs {worst:.3e}")
+    assert n >= 32

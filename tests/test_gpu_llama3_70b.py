@@ -73,3 +73,41 @@ def test_speculative_equals_greedy_bitwise_70b(gpu70b):
     toks, st = eng.generate(prompt, G, {"mode": "dp", "k_max": 8, "n_skip": 44, "interval": 8})
     assert toks == ar
     assert st["dp_runs"] >= 1
+    # with the MFMA GEMM for the full-model rows (one launch per 9-row verify)
+    eng.set_decode_kernel("mfma_verify")
+    try:
+        ar2, _ = eng.generate(prompt, G, {"mode": "ar"})
+        toks2, _ = eng.generate(prompt, G, {"mode": "dp", "k_max": 8, "n_skip": 44, "interval": 8})
+        assert toks2 == ar2
+    finally:
+        eng.set_decode_kernel("vector")
+
+
+def test_decode_rows_vs_oracle_70b(gpu70b, slice_model):
+    """The decode path at the 70B shape (the vector-ALU projections of
+    verify rows, K = 8192 and 28672): after the 64-token prefill, a 3-row
+    verify; for each sampled layer the oracle first rebuilds that layer's
+    keys and values of the prompt from the GPU's own input rows, then runs
+    the verify rows through ``oracle.decode.layer_row`` one by one on the
+    GPU's inputs; outputs and the rows' logits within 2e-2."""
+    eng = gpu70b["eng"]
+    eng.prefill(gpu70b["prompt"])
+    pre = np.stack([eng.read_states(r) for r in range(P)])          # [P][L+1][d]
+    eng.verify(drafts=[17, 4242])
+    z = eng.read_logits(3)
+    rows = np.stack([eng.read_states(r) for r in range(3)])         # [3][L+1][d]
+    eng.accept()
+    st = oracle.DecodeState(slice_model, P + 8)
+    for l in SLICES:
+        oracle.layer_block(slice_model, l, pre[:, l, :].astype(np.float32), st)
+        worst = 0.0
+        for i in range(3):
+            ho = oracle.decode.layer_row(slice_model, l, rows[i, l, :].astype(np.float32), P + i, st, "full")
+            worst = max(worst, float(np.max(np.abs(rows[i, l + 1, :] - ho))))
+        print(f"layer {l}: verify rows max-abs {worst:.3e}", flush=True)
+        assert worst <= TOL
+    for i in range(3):
+        zo = slice_model.head(rows[i, SHAPE.n_layers, :].astype(np.float32))
+        err = float(np.max(np.abs(z[i] - zo)))
+        print(f"verify row {i} logits max-abs {err:.3e}", flush=True)
+        assert err <= TOL

@@ -117,7 +117,9 @@ def test_prefill_logits_and_states_vs_oracle_8b(gpu8b, oracle8b):
 
 
 def test_teacher_forced_verify_logits_vs_oracle_8b(gpu8b, oracle8b):
-    """Verify rows [t0, o1, o2, o3] (oracle greedy tokens as host-forced drafts)."""
+    """A 9-row verify (K = 8: rows [t0, o1..o8], the oracle's greedy tokens
+    as host-forced drafts), in the launch configuration of the timed
+    workload, against the oracle's full-model rows one by one."""
     eng, model = gpu8b["eng"], oracle8b["model"]
     st = oracle8b["st"]
     t0 = eng.prefill(gpu8b["prompt"])
@@ -127,33 +129,56 @@ def test_teacher_forced_verify_logits_vs_oracle_8b(gpu8b, oracle8b):
     import copy
     so = copy.deepcopy(st)
     toks, zs = [so.t0], []
-    for _ in range(4):
+    for _ in range(9):
         zz, _ = oracle.forward_row(model, so, so.t0, so.p, "full")
         zs.append(zz)
         so.p += 1
         so.t0 = int(np.argmax(zz))
         toks.append(so.t0)
-    eng.verify(toks[1:4])
-    zg = eng.read_logits(4)
-    eng.accept()
-    for i in range(4):
+    eng.verify(toks[1:9])
+    zg = eng.read_logits(9)
+    n, bonus, _ = eng.accept()
+    for i in range(9):
         err = float(np.max(np.abs(zg[i] - zs[i])))
         print(f"verify row {i}: max-abs {err:.3e}")
         assert err <= TOL
+    gaps = [oracle_gap(z) for z in zs]
+    first_tie = next((i for i, g in enumerate(gaps) if g < 1e-2), 9)
+    assert n >= min(first_tie, 8)
+    if first_tie == 9:
+        assert (n, bonus) == (8, toks[9])
+
+
+def test_greedy_token_ids_vs_oracle_8b(gpu8b, oracle8b):
+    """The benchmark spec's token rule over 41 greedy positions, teacher-forced
+    along the GPU's own sequence (``conftest.greedy_ids_vs_oracle``)."""
+    from conftest import greedy_ids_vs_oracle
+    n, total, worst = greedy_ids_vs_oracle(gpu8b["eng"], oracle8b["model"], gpu8b["prompt"], oracle8b["st"],
+                                           oracle8b["z"], 40, TOL)
+    print(f"{n} of {total} token ids compared (the rest within 1e-2 of a tie); logits max-abs {worst:.3e}")
+    assert n >= 32
 
 
 def test_dp_skip_set_vs_oracle_8b(gpu8b, oracle8b):
+    """Every (i, j) cosine of the batched DP against the oracle's, and every
+    skip/execute decision whose oracle margin clears 1e-3 (states downstream
+    of a closer call are not compared).  A cosine bound of 4e-4 makes two
+    paths that both meet it take the same decision at any margin >= 1e-3."""
+    from conftest import compare_dp
     eng = gpu8b["eng"]
     eng.prefill(gpu8b["prompt"])
     mg, sg = eng.select_layers_dp(16)
+    gd = eng.read_dp_decisions()
     mo, so, dec = oracle.clasp_dp(oracle8b["model"], oracle8b["st"], 16)
+    n_dec, total, n_cos, worst, tainted = compare_dp(gd, dec, 4e-4, 1e-3)
     margins = sorted(abs(cs - ce) for _, cs, ce in dec.values() if cs is not None and ce is not None)
-    diff = [l for l in range(SHAPE.n_layers) if mg[l] != mo[l]]
-    print(f"DP score gpu {sg:.6f} oracle {so:.6f}; smallest oracle margins {margins[:3]}; "
+    print(f"DP score gpu {sg:.6f} oracle {so:.6f}; {n_dec} of {total} decisions and {n_cos} cosines compared, "
+          f"worst cosine error {worst:.2e}; smallest oracle margins {margins[:3]}; "
           f"gpu skip {[l for l in range(32) if mg[l]]}, oracle skip {[l for l in range(32) if mo[l]]}")
     assert abs(sg - so) <= 1e-3
-    if margins[0] >= 1e-3:
-        assert not diff
+    assert n_dec >= total // 2
+    if not tainted[(SHAPE.n_layers, 16)]:
+        assert mg == mo
 
 
 def test_dp_finds_planted_identity_layers_8b():
@@ -281,3 +306,54 @@ def test_tree_drafting_lossless_8b(gpu8b):
     toks, st = eng.generate(prompt, G, {"mode": "dp", "k_max": 1, "n_skip": 16, "interval": 32, "tree_width": 4})
     print(f"tree width 4: {st['rounds']} rounds, {st['accepted']} accepted")
     assert toks == ar
+
+
+@pytest.mark.parametrize("kind", ["mfma", "mfma_verify"])
+def test_mfma_decode_rows_8b(gpu8b, oracle8b, kind):
+    """The MFMA decode GEMM at the full shape (one launch per projection for
+    up to 16 rows): a 9-row verify of the oracle's greedy tokens against the
+    oracle's rows; every verify row equal to the one-row greedy step at its
+    position bit for bit (rows 1, 2, 9, 16); speculative output equal to
+    greedy output with the headline policy."""
+    import copy
+    eng, model, prompt = gpu8b["eng"], oracle8b["model"], gpu8b["prompt"]
+    eng.set_decode_kernel(kind)
+    try:
+        st = oracle8b["st"]
+        t0 = eng.prefill(prompt)
+        so = copy.deepcopy(st)
+        toks, zs = [so.t0], []
+        for _ in range(9):
+            zz, _ = oracle.forward_row(model, so, so.t0, so.p, "full")
+            zs.append(zz)
+            so.p += 1
+            so.t0 = int(np.argmax(zz))
+            toks.append(so.t0)
+        if t0 == st.t0:
+            eng.verify(toks[1:9])
+            zg = eng.read_logits(9)
+            eng.accept()
+            err = max(float(np.max(np.abs(zg[i] - zs[i]))) for i in range(9))
+            print(f"{kind}: 9-row verify vs oracle max-abs {err:.3e}")
+            assert err <= TOL
+        eng.prefill(prompt)
+        ar_z, g = [], []
+        for _ in range(16):
+            eng.verify(None, 0)
+            ar_z.append(eng.read_logits(1)[0].copy())
+            _, b, _ = eng.accept()
+            g.append(b)
+        for rows in (16, 9, 2):
+            eng.prefill(prompt)
+            eng.verify(drafts=g[:rows - 1])
+            z = eng.read_logits(rows)
+            for i in range(rows):
+                assert np.array_equal(z[i].view(np.uint32), ar_z[i].view(np.uint32)), (rows, i)
+            n, _, _ = eng.accept()
+            assert n == rows - 1
+        G = 48
+        ar, _ = eng.generate(prompt, G, {"mode": "ar"})
+        sp, _ = eng.generate(prompt, G, BENCH_POLICY)
+        assert sp == ar
+    finally:
+        eng.set_decode_kernel("vector")

@@ -68,6 +68,34 @@ def test_greedy_tokens_match_oracle(setup):
     assert n >= 8
 
 
+def test_decode_steps_vs_oracle_every_position(setup):
+    """The autoregressive path itself (one-row verify steps, the decode
+    projections), teacher-forced along the GPU's own tokens: logits within
+    1e-4 of the oracle's at all 64 positions, ids equal wherever the oracle's
+    top-1/top-2 gap is at least 1e-2."""
+    from conftest import greedy_ids_vs_oracle
+    st0, z0, _ = oracle.prefill(setup["model"], setup["prompt"], 256)
+    n, total, worst = greedy_ids_vs_oracle(setup["eng"], setup["model"], setup["prompt"], st0, z0, G - 1, TOL)
+    print(f"{n} of {total} ids compared, logits max-abs {worst:.3e}")
+    assert n >= total - 4
+
+
+@pytest.mark.parametrize("rows", [2, 5, 9, 16])
+def test_teacher_forced_verify_rows_vs_oracle(setup, rows):
+    """One verify of ``rows`` rows (the oracle's greedy tokens as host-forced
+    drafts; 16 = the engine's row limit) against the oracle's rows."""
+    eng, ref, ref_z = setup["eng"], setup["ref"], setup["ref_z"]
+    eng.prefill(setup["prompt"])
+    eng.verify(drafts=ref[1:rows])
+    z = eng.read_logits(rows)
+    n, _, _ = eng.accept()
+    # verify row i is the token ref[i] at position p + i, which the oracle's
+    # greedy run scored as ref_z[i + 1] (ref_z[0] is the prompt's last row)
+    err = float(np.max(np.abs(z - np.stack(ref_z[1:rows + 1]))))
+    print(f"{rows} rows: max-abs {err:.3e}, {n} accepted")
+    assert err <= TOL
+
+
 POLICIES = {
     "static_12_K4": {"mode": "static", "k_max": 4, "skip": (1, 2)},
     "empty_mask_K6": {"mode": "static", "k_max": 6, "skip": ()},
