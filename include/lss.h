@@ -106,7 +106,7 @@ int lss_create(const lss_config* cfg, const void* const* tensors_dev, int32_t n_
                void* workspace_dev, size_t workspace_bytes, void* hip_stream, lss_engine** out);
 void lss_destroy(lss_engine* e);
 /* Message of the engine's last failure; with e == NULL, of this thread's
- * last failed lss_load_weights / lss_create. */
+ * last failed lss_load_weights / lss_create or stand-alone acceptance op. */
 const char* lss_last_error(const lss_engine* e);
 
 /* Full-model causal pass over the prompt (row blocks of max_rows).  Resets
@@ -297,6 +297,29 @@ int lss_set_decode_kernel(lss_engine* e, int32_t kind);
  * Enqueued on hip_stream; no synchronization. */
 int lss_op_quantize_rows(const float* x_dev, int32_t rows, int32_t n, int8_t* q_dev,
                          float* scale_dev, void* hip_stream);
+
+/* Stand-alone greedy acceptance, the fused argmax-compare step of
+ * verification (CLaSp article, section 3: the full model scores every draft
+ * in one pass; the first draft that differs from the full model's token is
+ * replaced by it and the rest are dropped) on logits the caller holds.
+ *   logits_dev: [rows][vocab] float32, the verify rows [t0, d1..dk] (rows =
+ *     k + 1, 1 <= rows <= LSS_ACCEPT_ROWS_MAX);
+ *   drafts_dev: [rows - 1] int32 draft tokens d1..dk (may be NULL if rows
+ *     is 1);
+ *   result_dev: [2 + rows] int32, written on the device: result[0] = n, the
+ *     length of the longest prefix of the drafts equal to the rows' argmax
+ *     tokens (lowest index on ties; NaN never wins; a row of NaNs gives 0),
+ *     result[1] = the bonus token (argmax of row n), result[2 + r] = argmax
+ *     of row r.
+ * lss_op_accept_greedy_workspace_bytes: scratch bytes the op needs (0 for
+ * invalid sizes).  lss_op_accept_greedy takes that scratch as workspace_dev
+ * (caller-owned device memory, 8-byte aligned; LSS_ECAPACITY if smaller).
+ * Enqueued on hip_stream, no synchronization; LSS_EINVAL for bad sizes or
+ * null pointers.  On failure lss_last_error(NULL) describes it. */
+#define LSS_ACCEPT_ROWS_MAX 64
+size_t lss_op_accept_greedy_workspace_bytes(int32_t rows, int32_t vocab);
+int lss_op_accept_greedy(const float* logits_dev, int32_t rows, int32_t vocab, const int32_t* drafts_dev,
+                         int32_t* result_dev, void* workspace_dev, size_t workspace_bytes, void* hip_stream);
 
 /* int8 weight copy for the W8A8 draft (lss_draft quant = 2): the 8-bit
  * dynamic quantization of CAS-Spec blog section 2.1 applied per output row

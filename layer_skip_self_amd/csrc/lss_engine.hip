@@ -784,7 +784,8 @@ void fill_u32(lss_engine* e, void* p, size_t n, uint32_t v) {
   if (n) hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, e->stream, (uint32_t*)p, n, v);
 }
 
-// message of the last failed engine creation on this thread (lss_last_error(NULL))
+// message of the last failed engine creation or stand-alone op on this
+// thread (lss_last_error(NULL))
 thread_local std::string g_create_err = "no failure";
 
 int create_fail(int code, const std::string& msg) {
@@ -1356,6 +1357,50 @@ int lss_op_quantize_rows(const float* x, int32_t rows, int32_t n, int8_t* q, flo
   hipLaunchKernelGGL(k_quant_rows<float>, dim3(rows), dim3(256), 0, (hipStream_t)stream, x, n, n, (void*)nullptr,
                      scale, q);
   return hipGetLastError() == hipSuccess ? LSS_OK : LSS_EHIP;
+}
+
+// ---------------------------------------------------------------- stand-alone greedy acceptance
+}  // extern "C" (the helpers below have C++ linkage)
+namespace {
+
+size_t accept_records(int32_t rows, int32_t vocab) {
+  return (size_t)rows * ((vocab + ACC_CH - 1) / ACC_CH) * sizeof(AccRec);
+}
+
+int accept_launch(const float* logits, int32_t rows, int32_t vocab, const int32_t* drafts, int32_t* result,
+                  AccRec* rec, hipStream_t s) {
+  const int nchunk = (vocab + ACC_CH - 1) / ACC_CH;
+  hipLaunchKernelGGL(k_argmax_chunks, dim3(nchunk, rows), dim3(ACC_THREADS), 0, s, logits, vocab, rec, nchunk);
+  hipLaunchKernelGGL(k_accept_records, dim3(1), dim3(ACC_THREADS), 0, s, (const AccRec*)rec, nchunk, rows, vocab,
+                     drafts, result);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return create_fail(LSS_EHIP, std::string("accept_greedy: launch: ") + hipGetErrorString(e));
+  return LSS_OK;
+}
+
+int accept_args(const float* logits, int32_t rows, int32_t vocab, const int32_t* drafts, int32_t* result) {
+  if (!logits || !result || (rows > 1 && !drafts)) return create_fail(LSS_EINVAL, "accept_greedy: null pointer");
+  if (rows < 1 || rows > LSS_ACCEPT_ROWS_MAX || vocab < 1)
+    return create_fail(LSS_EINVAL, "accept_greedy: rows must be in [1, 64], vocab >= 1");
+  return LSS_OK;
+}
+
+}  // namespace
+extern "C" {
+
+size_t lss_op_accept_greedy_workspace_bytes(int32_t rows, int32_t vocab) {
+  if (rows < 1 || rows > LSS_ACCEPT_ROWS_MAX || vocab < 1) return 0;
+  return accept_records(rows, vocab);
+}
+
+int lss_op_accept_greedy(const float* logits, int32_t rows, int32_t vocab, const int32_t* drafts, int32_t* result,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = accept_args(logits, rows, vocab, drafts, result);
+  if (rc) return rc;
+  if (!workspace) return create_fail(LSS_EINVAL, "accept_greedy: null workspace");
+  if (workspace_bytes < accept_records(rows, vocab))
+    return create_fail(LSS_ECAPACITY, "accept_greedy: workspace smaller than lss_op_accept_greedy_workspace_bytes");
+  return accept_launch(logits, rows, vocab, drafts, result, (AccRec*)workspace, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- generation loop

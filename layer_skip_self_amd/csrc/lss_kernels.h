@@ -2148,6 +2148,73 @@ __global__ __launch_bounds__(SPEC_FIN_THREADS) void k_spec_final(const float* __
   }
 }
 
+// ---------------------------------------------------------------- stand-alone greedy acceptance
+// The fused argmax-compare acceptance on logits the caller already holds:
+// rows [k+1][V] of a verify pass and the k drafts.  k_argmax_chunks writes
+// one {max, lowest index} record per (row, chunk of ACC_CH columns);
+// k_accept_records reduces each row's records (the same total order, so the
+// split changes nothing), then takes the greedy rule: n = length of the
+// longest prefix of the drafts equal to the rows' argmaxes, bonus = argmax
+// of row n.  NaN never wins a comparison; a row of NaNs yields index 0.
+#define ACC_CH 4096
+#define ACC_THREADS 256
+struct AccRec { float mx; int idx; };
+
+__global__ __launch_bounds__(ACC_THREADS) void k_argmax_chunks(const float* __restrict__ z, int V,
+                                                              AccRec* __restrict__ rec, int nchunk) {
+  __shared__ float bm[ACC_THREADS / 64];
+  __shared__ int bi[ACC_THREADS / 64];
+  const int c = blockIdx.x, row = blockIdx.y;
+  const float* zr = z + (size_t)row * V;
+  float mx = -INFINITY;
+  int idx = 0x7fffffff;
+  const int v0 = c * ACC_CH;
+  const int v1 = min(v0 + ACC_CH, V);
+  float vals[ACC_CH / ACC_THREADS];                  // all loads in flight before the compares
+#pragma unroll
+  for (int j = 0; j < ACC_CH / ACC_THREADS; ++j) {
+    const int v = v0 + (int)threadIdx.x + j * ACC_THREADS;
+    vals[j] = v < v1 ? zr[v] : -INFINITY;
+  }
+#pragma unroll
+  for (int j = 0; j < ACC_CH / ACC_THREADS; ++j) {
+    const int v = v0 + (int)threadIdx.x + j * ACC_THREADS;
+    if (v < v1) argmax_merge(mx, idx, vals[j], v);
+  }
+  argmax_wave(mx, idx);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) { bm[w] = mx; bi[w] = idx; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < ACC_THREADS / 64; ++i) argmax_merge(mx, idx, bm[i], bi[i]);
+    rec[(size_t)row * nchunk + c] = AccRec{mx, idx};
+  }
+}
+
+// result[0] = n, result[1] = bonus, result[2 + r] = argmax of row r
+__global__ __launch_bounds__(ACC_THREADS) void k_accept_records(const AccRec* __restrict__ rec, int nchunk, int rows,
+                                                               int V, const int32_t* __restrict__ drafts,
+                                                               int32_t* __restrict__ result) {
+  __shared__ int am_s[64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int r = w; r < rows; r += ACC_THREADS / 64) {   // one wave per row, lane = chunk
+    float mx = -INFINITY;
+    int idx = 0x7fffffff;
+    for (int c = lane; c < nchunk; c += 64) argmax_merge(mx, idx, rec[(size_t)r * nchunk + c].mx,
+                                                         rec[(size_t)r * nchunk + c].idx);
+    argmax_wave(mx, idx);
+    if (lane == 0) am_s[r] = (idx >= 0 && idx < V) ? idx : 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = 0;
+    while (n < rows - 1 && am_s[n] == drafts[n]) ++n;
+    result[0] = n;
+    result[1] = am_s[n];
+  }
+  for (int r = threadIdx.x; r < rows; r += ACC_THREADS) result[2 + r] = am_s[r];
+}
+
 // Copy the residual states of verify row res->trow (or `row` if res ==
 // nullptr) into the layer-selection target [L+1][d].
 __global__ void k_gather_target(const float* __restrict__ hs, int rows_stride, int d, const HeadRes* res,
