@@ -317,9 +317,20 @@ int lss_op_quantize_rows(const float* x_dev, int32_t rows, int32_t n, int8_t* q_
  * Enqueued on hip_stream, no synchronization; LSS_EINVAL for bad sizes or
  * null pointers.  On failure lss_last_error(NULL) describes it. */
 #define LSS_ACCEPT_ROWS_MAX 64
+#define LSS_ACCEPT_VOCAB_MAX 262144
 size_t lss_op_accept_greedy_workspace_bytes(int32_t rows, int32_t vocab);
 int lss_op_accept_greedy(const float* logits_dev, int32_t rows, int32_t vocab, const int32_t* drafts_dev,
                          int32_t* result_dev, void* workspace_dev, size_t workspace_bytes, void* hip_stream);
+
+/* The same with no workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): its scratch is a fixed 32 KB array inside the library,
+ * one per GPU, held until the process ends; vocab <= LSS_ACCEPT_VOCAB_MAX
+ * (LSS_ECAPACITY above it).  It calls no allocating routine.  All calls on
+ * one GPU share that array: calls that overlap on one GPU (several streams,
+ * several host threads) race and must be ordered by the caller. */
+int lss_op_accept_greedy_noalloc(const float* logits_dev, int32_t rows, int32_t vocab, const int32_t* drafts_dev,
+                                 int32_t* result_dev, void* hip_stream);
 
 /* int8 weight copy for the W8A8 draft (lss_draft quant = 2): the 8-bit
  * dynamic quantization of CAS-Spec blog section 2.1 applied per output row

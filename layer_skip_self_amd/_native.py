@@ -12,6 +12,7 @@ LSS_WINDOW_MAX = 31
 LSS_ROWS_MAX = 64
 LSS_LEVELS_MAX = 4
 LSS_ACCEPT_ROWS_MAX = 64
+LSS_ACCEPT_VOCAB_MAX = 262144
 
 STATUS_NAMES = {0: "LSS_OK", -1: "LSS_EINVAL", -2: "LSS_ESTATE", -3: "LSS_ECAPACITY",
                 -4: "LSS_EHIP", -5: "LSS_ENOTIMPL"}
@@ -81,6 +82,8 @@ SIGNATURES = {
     "lss_op_accept_greedy_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
     "lss_op_accept_greedy": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                        C.c_size_t, C.c_void_p]),
+    "lss_op_accept_greedy_noalloc": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                               C.c_void_p]),
     "lss_op_quantize_rows": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                        C.c_void_p]),
     "lss_w8_bytes": (C.c_size_t, [C.POINTER(lss_config)]),

@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <array>
+#include <mutex>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -27,6 +28,7 @@ using namespace lss;
 namespace {
 
 constexpr int kWinMax = LSS_WINDOW_MAX;
+#define LSS_MAX_DEVICES 64
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -1360,8 +1362,35 @@ int lss_op_quantize_rows(const float* x, int32_t rows, int32_t n, int8_t* q, flo
 }
 
 // ---------------------------------------------------------------- stand-alone greedy acceptance
+// Scratch of the allocation-free form: per-chunk records of up to
+// LSS_ACCEPT_ROWS_MAX rows of LSS_ACCEPT_VOCAB_MAX logits (32 KB).  Every
+// GPU the library runs on holds its own copy until the process ends; host
+// code must use the address hipGetSymbolAddress gives for the current
+// device, never the array's name (a host-side stand-in).
+static __device__ __align__(256) AccRec scratch[LSS_ACCEPT_ROWS_MAX * (LSS_ACCEPT_VOCAB_MAX / ACC_CH)];
+
 }  // extern "C" (the helpers below have C++ linkage)
 namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[LSS_MAX_DEVICES] = {};
+
+// this device's address of `scratch`, looked up once per device
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= LSS_MAX_DEVICES)
+    return create_fail(LSS_EHIP, "accept_greedy_noalloc: no current device (or device id >= 64)");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t s = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (s != hipSuccess || !p)
+      return create_fail(LSS_EHIP, std::string("accept_greedy_noalloc: hipGetSymbolAddress: ") + hipGetErrorString(s));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LSS_OK;
+}
 
 size_t accept_records(int32_t rows, int32_t vocab) {
   return (size_t)rows * ((vocab + ACC_CH - 1) / ACC_CH) * sizeof(AccRec);
@@ -1401,6 +1430,19 @@ int lss_op_accept_greedy(const float* logits, int32_t rows, int32_t vocab, const
   if (workspace_bytes < accept_records(rows, vocab))
     return create_fail(LSS_ECAPACITY, "accept_greedy: workspace smaller than lss_op_accept_greedy_workspace_bytes");
   return accept_launch(logits, rows, vocab, drafts, result, (AccRec*)workspace, (hipStream_t)stream);
+}
+
+int lss_op_accept_greedy_noalloc(const float* logits, int32_t rows, int32_t vocab, const int32_t* drafts,
+                                 int32_t* result, void* stream) {
+  int rc = accept_args(logits, rows, vocab, drafts, result);
+  if (rc) return rc;
+  if (vocab > LSS_ACCEPT_VOCAB_MAX)
+    return create_fail(LSS_ECAPACITY, "accept_greedy_noalloc: vocab above LSS_ACCEPT_VOCAB_MAX (262144); use "
+                                      "lss_op_accept_greedy with a workspace");
+  void* p = nullptr;
+  rc = scratch_ptr(&p);
+  if (rc) return rc;
+  return accept_launch(logits, rows, vocab, drafts, result, (AccRec*)p, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- generation loop

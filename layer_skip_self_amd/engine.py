@@ -381,10 +381,11 @@ def _op_error(what, rc):
     return LssError(what, rc, msg.decode() if msg else "")
 
 
-def accept_greedy(logits, drafts):
+def accept_greedy(logits, drafts, noalloc=False):
     """Greedy acceptance on CUDA logits [rows][vocab] (float32) and drafts
     [rows - 1] (int32): returns the device result [2 + rows] = {n, bonus,
-    argmax of every row}; the op's workspace is allocated here."""
+    argmax of every row}.  ``noalloc`` runs the allocation-free entry point
+    (library-owned scratch); otherwise a workspace tensor is allocated here."""
     import torch
     lib = N.load()
     logits = logits.contiguous()
@@ -393,12 +394,18 @@ def accept_greedy(logits, drafts):
     res = torch.empty((2 + rows,), dtype=torch.int32, device=logits.device)
     stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
     dp = C.c_void_p(drafts.data_ptr()) if drafts is not None else None
-    nb = int(lib.lss_op_accept_greedy_workspace_bytes(rows, vocab))
-    if nb == 0:
-        raise LssError("lss_op_accept_greedy_workspace_bytes", N.LSS_EINVAL, "bad sizes")
-    ws = torch.empty((nb,), dtype=torch.uint8, device=logits.device)
-    rc = lib.lss_op_accept_greedy(C.c_void_p(logits.data_ptr()), rows, vocab, dp, C.c_void_p(res.data_ptr()),
-                                  C.c_void_p(ws.data_ptr()), nb, stream)
-    if rc != 0:
-        raise _op_error("lss_op_accept_greedy", rc)
+    if noalloc:
+        rc = lib.lss_op_accept_greedy_noalloc(C.c_void_p(logits.data_ptr()), rows, vocab, dp,
+                                              C.c_void_p(res.data_ptr()), stream)
+        if rc != 0:
+            raise _op_error("lss_op_accept_greedy_noalloc", rc)
+    else:
+        nb = int(lib.lss_op_accept_greedy_workspace_bytes(rows, vocab))
+        if nb == 0:
+            raise LssError("lss_op_accept_greedy_workspace_bytes", N.LSS_EINVAL, "bad sizes")
+        ws = torch.empty((nb,), dtype=torch.uint8, device=logits.device)
+        rc = lib.lss_op_accept_greedy(C.c_void_p(logits.data_ptr()), rows, vocab, dp, C.c_void_p(res.data_ptr()),
+                                      C.c_void_p(ws.data_ptr()), nb, stream)
+        if rc != 0:
+            raise _op_error("lss_op_accept_greedy", rc)
     return res
