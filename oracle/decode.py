@@ -60,7 +60,7 @@ class DecodeState:
         self.target_states = None  # full states H*[0..L] of the last accepted token
         self.target_pos = None     # its position t*
         self.window_logits = []    # sampling: draft logits that produced each window token
-        self.tree = False          # the window holds sibling candidates (draft_tree)
+        self.tree = False          # (B, D) while the window holds a token tree (draft_tree)
         self.margins = []          # sampling: slack of every random decision taken
 
 
@@ -307,51 +307,80 @@ def top_b(z, B):
     return [int(i) for i in order[:B]]
 
 
-def draft_tree(model, st, skip, quant, B):
-    """Tree draft of width B and depth 1: the draft model runs the pending
-    token's row (position p) with the skip mask and proposes its B most
-    likely tokens as sibling candidates for position p + 1.  Returns the
-    candidates (the window) and the draft's top-1 probability."""
+def draft_tree(model, st, skip, quant, B, D=1):
+    """Token tree of width B and depth D, drafted by the skipped-layer model.
+
+    The draft runs the pending token's row (position p) and proposes its B
+    most likely tokens for position p + 1 (the first nodes of B branches);
+    the draft then extends every branch greedily by D - 1 more tokens, the
+    row of node j of a branch (position p + j) seeing the committed prefix,
+    the pending token and that branch's earlier nodes only.  Returns (the
+    branches [B][D], the draft's top-1 probability at the pending row); the
+    window holds the branches one after the other."""
     z, _ = forward_row(model, st, st.t0, st.p, "draft", skip, quant)
-    st.window = top_b(z, B)
-    st.tree = True
+    firsts = top_b(z, B)
+    root_valid = list(st.valid)                      # window slot 0: the pending token
+    branches = []
+    for c in firsts:
+        st.valid = list(root_valid)                  # another branch's nodes are invisible
+        br = [c]
+        for j in range(1, D):
+            zz, _ = forward_row(model, st, br[-1], st.p + j, "draft", skip, quant)
+            br.append(argmax_first(zz))
+        branches.append(br)
+    st.valid = list(root_valid)
+    st.window = [t for br in branches for t in br]
+    st.tree = (B, D)
     zs = z - np.max(z)
-    return list(st.window), 1.0 / float(np.sum(np.exp(zs)))
+    return branches, 1.0 / float(np.sum(np.exp(zs)))
 
 
 def verify_tree(model, st):
-    """Tree verify in one pass: row 0 is the pending token at position p; row
-    i >= 1 is candidate i at position p + 1 and sees the committed prefix,
-    the pending token and its own key and value only (a tree mask: siblings
-    are invisible to each other).  Each candidate row is therefore the full
-    model's step at p + 1 after that candidate.  Returns (logits [B+1][V],
-    states, candidates, per-candidate KV [B][L] of position p + 1)."""
-    cands = list(st.window)
+    """Tree verify in one pass over rows [pending token, branch 1 nodes 1..D,
+    branch 2 nodes, ...]: row 0 is the pending token at position p; the row
+    of node j of branch b is at position p + j and sees the committed
+    prefix, the pending token and nodes 1..j of its own branch (a tree
+    mask), so it is the full model's step at p + j after that branch's
+    first j tokens.  Returns (logits [1 + B D][V], states, branches, the
+    keys/values each branch's nodes give positions p + 1 .. p + D)."""
+    B, D = st.tree
+    branches = [list(st.window[b * D:(b + 1) * D]) for b in range(B)]
     z0, s0 = forward_row(model, st, st.t0, st.p, "full")
     logits, states, kv = [z0], [s0], []
-    for c in cands:
-        z, s = forward_row(model, st, c, st.p + 1, "full")     # writes its KV at p + 1
-        logits.append(z)
-        states.append(s)
-        kv.append((st.k[:, st.p + 1].copy(), st.v[:, st.p + 1].copy()))
-    return np.stack(logits), states, cands, kv
+    for br in branches:
+        bkv = []
+        for j, c in enumerate(br, start=1):
+            z, s = forward_row(model, st, c, st.p + j, "full")    # writes and sees its branch's positions
+            logits.append(z)
+            states.append(s)
+            bkv.append((st.k[:, st.p + j].copy(), st.v[:, st.p + j].copy()))
+        kv.append(bkv)
+    return np.stack(logits), states, branches, kv
 
 
-def accept_tree(st, logits, states, cands, kv):
-    """Greedy acceptance of a width-B tree: a_0 = argmax of row 0; if a
-    candidate equals a_0 (at most one can), it is accepted together with the
-    bonus a_i = argmax of its row (n = 1), and its KV becomes position
-    p + 1's; otherwise the bonus is a_0 (n = 0).  Returns (n, bonus,
+def accept_tree(st, logits, states, branches, kv):
+    """Greedy acceptance of a tree: a_0 = argmax of row 0; the branch whose
+    first node equals a_0 (at most one: the first nodes are distinct) is
+    followed while its next node equals the full model's token after the
+    last accepted one; n = accepted nodes, bonus = the full model's token
+    after them, and their keys/values become positions p + 1 .. p + n.
+    With no such branch n = 0 and the bonus is a_0.  Returns (n, bonus,
     emitted tokens)."""
+    B, D = st.tree
     a0 = argmax_first(logits[0])
-    hit = [i for i, c in enumerate(cands) if c == a0]
+    hit = [b for b, br in enumerate(branches) if br[0] == a0]
     if hit:
-        i = hit[0]
-        bonus = argmax_first(logits[i + 1])
-        st.k[:, st.p + 1], st.v[:, st.p + 1] = kv[i]
-        n, row, emitted = 1, i + 1, [a0, bonus]
+        b = hit[0]
+        n, row = 1, 1 + b * D
+        while n < D and branches[b][n] == argmax_first(logits[row]):
+            n += 1
+            row += 1
+        bonus = argmax_first(logits[row])
+        for j in range(n):
+            st.k[:, st.p + 1 + j], st.v[:, st.p + 1 + j] = kv[b][j]
+        emitted = list(branches[b][:n]) + [bonus]
     else:
-        n, row, emitted, bonus = 0, 0, [a0], a0
+        n, row, bonus, emitted = 0, 0, a0, [a0]
     st.target_states = states[row]
     st.target_pos = st.p + n
     st.p = st.p + n + 1
@@ -394,8 +423,9 @@ class Policy:
     by the DyTC heuristics with at most ``K`` drafts per round;
     temperature > 0: speculative sampling with that temperature and seed
     (``oracle.sampling``), 0: greedy; tree_width B > 0 (greedy, static or
-    DP mask): every round drafts a width-B, depth-1 token tree
-    (``draft_tree``) instead of a chain.
+    DP mask): every round drafts a token tree of width B and depth
+    min(tree_depth, tokens still to emit) (``draft_tree``) instead of a
+    chain.
     """
     K: int = 4
     skip: tuple = ()
@@ -409,6 +439,7 @@ class Policy:
     temperature: float = 0.0
     seed: int = 0
     tree_width: int = 0
+    tree_depth: int = 1
 
     @property
     def sampling(self):
@@ -472,13 +503,15 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None, state
                 toks, _ = draft(model, st, mk, policy.cascade[lev][2], kk, 0.0, sam)
                 drafted_levels += [lev] * len(toks)
         elif policy.tree_width and budget > 0:
-            draft_tree(model, st, masks[0], policy.quant, policy.tree_width)
-            logits, states, cands, kv = verify_tree(model, st)
-            n, bonus, emitted = accept_tree(st, logits, states, cands, kv)
+            depth = min(policy.tree_depth, budget)
+            draft_tree(model, st, masks[0], policy.quant, policy.tree_width, depth)
+            logits, states, branches, kv = verify_tree(model, st)
+            n, bonus, emitted = accept_tree(st, logits, states, branches, kv)
             out += emitted
             rounds += 1
-            rec = {"k": len(cands), "n": n, "bonus": bonus, "tree": True,
-                   "row": cands.index(emitted[0]) + 1 if n else 0}
+            firsts = [br[0] for br in branches]
+            rec = {"k": len(branches) * depth, "n": n, "bonus": bonus, "tree": True,
+                   "branch": firsts.index(emitted[0]) if n else -1}
             records.append(rec)
             if policy.dp_skip is not None and rounds % policy.interval == 0:
                 masks = select_masks()

@@ -1,18 +1,23 @@
 """Pins of the oracle's tree drafting (CPU only).
 
 Reading of the pages' "dynamic tree cascade" (CAS abs abstract and method
-list; CAS blog section 3): a token tree, here of width B and depth 1 -- the
-draft model's B most likely tokens for the next position, verified in one
-pass with a tree mask (each candidate sees the committed prefix, the pending
-token and itself).  What fixes the expected values:
+list; CAS blog section 3): a token tree of width B and depth D -- the draft
+model's B most likely tokens for the next position, each extended greedily
+by the draft to a branch of D tokens, all verified in one pass with a tree
+mask (the row of a node sees the committed prefix, the pending token and
+its own branch's earlier nodes).  What fixes the expected values:
   * losslessness: the output equals the full model's greedy output for every
-    width and policy (the tree only changes how many tokens a round emits);
-  * B = 1 is the chain with one draft token, round for round;
-  * a candidate row of the tree verify equals the full model's last row over
-    the whole sequence recomputed as one causal block (a sibling leaking into
-    the mask, or a wrong position, fails it);
-  * from one state, acceptance is monotone in B (accepted iff the greedy
-    token is among the draft's top B);
+    width, depth and policy (the tree only changes how many tokens a round
+    emits);
+  * depth 1 and width 1 reduce to the one-token chain; width 1 and depth D
+    is the chain of D drafts, round for round;
+  * every node row of the tree verify equals the full model's last row over
+    the whole sequence (prompt, pending token, the branch up to the node)
+    recomputed as one causal block: a sibling or another branch leaking into
+    the mask, or a wrong position, fails it;
+  * acceptance: n is the longest prefix of the branch that starts with the
+    full model's token along which every node is the full model's token
+    after the previous one; at depth 1, acceptance is monotone in B;
   * top-B ordering with ties to the lowest index.
 """
 import copy
@@ -38,44 +43,90 @@ def ar(tiny_model, tiny_prompt):
     return oracle.ar_generate(tiny_model, tiny_prompt, G)
 
 
-@pytest.mark.parametrize("B", [1, 2, 4, 8])
+@pytest.mark.parametrize("B,D", [(1, 1), (2, 1), (4, 1), (8, 1), (1, 3), (2, 2), (4, 3), (3, 4)])
 @pytest.mark.parametrize("kind", ["static", "dp"])
-def test_tree_decoding_is_lossless(tiny_model, tiny_prompt, ar, B, kind):
-    pol = (oracle.Policy(tree_width=B, skip=(1, 2)) if kind == "static"
-           else oracle.Policy(tree_width=B, dp_skip=2, interval=3))
+def test_tree_decoding_is_lossless(tiny_model, tiny_prompt, ar, B, D, kind):
+    pol = (oracle.Policy(tree_width=B, tree_depth=D, skip=(1, 2)) if kind == "static"
+           else oracle.Policy(tree_width=B, tree_depth=D, dp_skip=2, interval=3))
     toks, recs = oracle.speculative_generate(tiny_model, tiny_prompt, G, pol)
     assert toks == ar
-    assert all(r["n"] in (0, 1) for r in recs)
+    assert all(0 <= r["n"] <= D for r in recs)
 
 
-def test_width_one_is_the_one_token_chain(tiny_model, tiny_prompt):
-    t1, r1 = oracle.speculative_generate(tiny_model, tiny_prompt, G, oracle.Policy(tree_width=1, skip=(1, 2)))
-    tc, rc = oracle.speculative_generate(tiny_model, tiny_prompt, G, oracle.Policy(K=1, skip=(1, 2)))
-    assert t1 == tc
-    assert [r["n"] for r in r1] == [r["n"] for r in rc]
+def test_width_one_is_the_chain(tiny_model, tiny_prompt):
+    for D in (1, 3):
+        t1, r1 = oracle.speculative_generate(tiny_model, tiny_prompt, G,
+                                             oracle.Policy(tree_width=1, tree_depth=D, skip=(1, 2)))
+        tc, rc = oracle.speculative_generate(tiny_model, tiny_prompt, G, oracle.Policy(K=D, skip=(1, 2)))
+        assert t1 == tc
+        assert [r["n"] for r in r1] == [r["n"] for r in rc]
 
 
-def test_candidate_rows_equal_a_full_causal_recompute(tiny_model, tiny_prompt):
+def _causal_last_row(m, seq):
+    H = np.stack([m.embed_row(t) for t in seq])
+    for l in range(m.L):
+        H = layer_block(m, l, H)
+    return m.head(H[-1])
+
+
+@pytest.mark.parametrize("B,D", [(4, 1), (3, 3)])
+def test_node_rows_equal_a_full_causal_recompute(tiny_model, tiny_prompt, B, D):
     m = tiny_model
     st, _, _ = oracle.prefill(m, tiny_prompt, 64)
     t0 = st.t0
-    cands, _ = draft_tree(m, st, [0, 1, 1, 0], False, 4)
+    branches, _ = draft_tree(m, st, [0, 1, 1, 0], False, B, D)
+    assert len(branches) == B and all(len(br) == D for br in branches)
     logits, _, _, _ = verify_tree(m, st)
-    for i, c in enumerate(cands):
-        seq = list(tiny_prompt) + [t0, c]
-        H = np.stack([m.embed_row(t) for t in seq])
-        for l in range(m.L):
-            H = layer_block(m, l, H)
-        z = m.head(H[-1])
-        assert np.max(np.abs(z - logits[i + 1])) < 1e-9
-    H = np.stack([m.embed_row(t) for t in list(tiny_prompt) + [t0]])
-    for l in range(m.L):
-        H = layer_block(m, l, H)
-    assert np.max(np.abs(m.head(H[-1]) - logits[0])) < 1e-9
+    assert np.max(np.abs(_causal_last_row(m, list(tiny_prompt) + [t0]) - logits[0])) < 1e-9
+    for b, br in enumerate(branches):
+        for j in range(1, D + 1):
+            z = _causal_last_row(m, list(tiny_prompt) + [t0] + br[:j])
+            assert np.max(np.abs(z - logits[1 + b * D + j - 1])) < 1e-9
+
+
+def test_draft_branches_follow_the_draft_model(tiny_model, tiny_prompt):
+    """Each branch after its first node is the draft's own greedy chain: node
+    j + 1 is the argmax of the draft run over prompt + pending token + the
+    branch's first j nodes (a plain chain draft from that state)."""
+    m = tiny_model
+    mask = [0, 1, 1, 0]
+    st, _, _ = oracle.prefill(m, tiny_prompt, 64)
+    base = copy.deepcopy(st)
+    branches, _ = draft_tree(m, st, mask, False, 3, 3)
+    for br in branches:
+        sc = copy.deepcopy(base)
+        sc.window = []
+        z, _ = oracle.forward_row(m, sc, sc.t0, sc.p, "draft", mask, False)
+        for j in range(1, 3):
+            z, _ = oracle.forward_row(m, sc, br[j - 1], sc.p + j, "draft", mask, False)
+            assert br[j] == oracle.argmax_first(z)
+
+
+def test_acceptance_follows_the_greedy_path(tiny_model, tiny_prompt, ar):
+    """From states along the greedy path, with the all-skipped draft and with
+    an empty mask (the draft is the full model): n equals the number of
+    leading nodes of the branch starting with the greedy token that continue
+    the greedy output; an empty-mask tree accepts its full depth."""
+    m = tiny_model
+    for mask, full in (([1, 1, 1, 1], False), ([0, 0, 0, 0], True)):
+        for j in range(6):
+            st, _, _ = oracle.prefill(m, list(tiny_prompt) + ar[:j], 64)
+            branches, _ = draft_tree(m, st, mask, False, 3, 3)
+            logits, states, brs, kv = verify_tree(m, st)
+            n, bonus, emitted = accept_tree(st, logits, states, brs, kv)
+            assert emitted == ar[j + 1:j + 2 + n]
+            hit = [br for br in branches if br[0] == ar[j + 1]]
+            expect = 0
+            if hit:
+                while expect < 3 and hit[0][expect] == ar[j + 1 + expect]:
+                    expect += 1
+            assert n == expect
+            if full:
+                assert n == 3
 
 
 def test_acceptance_is_monotone_in_width(tiny_model, tiny_prompt, ar):
-    """Along the greedy path, with the all-skipped draft: accepted iff the
+    """Depth 1 along the greedy path, all-skipped draft: accepted iff the
     greedy token is among the draft's top B, hence monotone in B; some state
     must reject at B = 1 and accept at a larger width (else the test proves
     nothing)."""
@@ -87,12 +138,36 @@ def test_acceptance_is_monotone_in_width(tiny_model, tiny_prompt, ar):
         for B in range(1, 9):
             st = copy.deepcopy(base)
             draft_tree(m, st, [1, 1, 1, 1], False, B)
-            logits, states, cands, kv = verify_tree(m, st)
-            n, bonus, emitted = accept_tree(st, logits, states, cands, kv)
+            logits, states, branches, kv = verify_tree(m, st)
+            n, bonus, emitted = accept_tree(st, logits, states, branches, kv)
             a0 = oracle.argmax_first(logits[0])
-            assert n == (1 if a0 in cands else 0)
+            assert n == (1 if a0 in [br[0] for br in branches] else 0)
             assert emitted[0] == ar[j + 1]
             ns.append(n)
         assert ns == sorted(ns)
         flips += ns[0] == 0 and ns[-1] == 1
     assert flips > 0
+
+
+def test_accepted_keys_values_are_the_branch_positions(tiny_model, tiny_prompt, ar):
+    """After a depth-3 round the cache at p + 1 .. p + n holds the accepted
+    nodes' keys and values, so the next greedy step equals a recompute."""
+    m = tiny_model
+    st, _, _ = oracle.prefill(m, tiny_prompt, 64)
+    draft_tree(m, st, [0, 0, 0, 0], False, 2, 3)
+    logits, states, branches, kv = verify_tree(m, st)
+    n, bonus, emitted = accept_tree(st, logits, states, branches, kv)
+    assert n == 3
+    z, _ = oracle.forward_row(m, st, st.t0, st.p, "full")
+    ref = _causal_last_row(m, list(tiny_prompt) + ar[:1] + emitted)
+    assert np.max(np.abs(z - ref)) < 1e-9
+
+
+def test_some_run_accepts_deep_in_a_later_branch(tiny_model, tiny_prompt, ar):
+    """The skip-{1} draft with width 3 and depth 3 has rounds where a branch
+    other than the first is accepted two or more nodes deep, so the move of
+    the accepted nodes' keys and values is exercised by the lossless runs."""
+    toks, recs = oracle.speculative_generate(tiny_model, tiny_prompt, 48,
+                                             oracle.Policy(tree_width=3, tree_depth=3, skip=(1,)))
+    assert toks == oracle.ar_generate(tiny_model, tiny_prompt, 48)
+    assert any(r.get("branch", -1) >= 1 and r["n"] >= 2 for r in recs)
