@@ -86,6 +86,13 @@ WORKLOADS = {
                                    "decode_kernel": "mfma_verify"},
                            desc="Llama-3-8B shape, prompt 1024, 512 generated, CLaSp DP skip 16 every 32 rounds, "
                                 "token tree of width 4 and depth 1 per round"),
+    # Deeper trees: 3 branches of 4 tokens each (12 nodes + the pending
+    # token: 13 verify rows, one MFMA weight pass).
+    "llama3_8b_tree_deep": dict(shape="llama3_8b", prompt=1024, gen=512,
+                                policy={"mode": "dp", "k_max": 1, "n_skip": 16, "interval": 32, "tree_width": 3,
+                                        "tree_depth": 4, "decode_kernel": "mfma_verify"},
+                                desc="Llama-3-8B shape, prompt 1024, 512 generated, CLaSp DP skip 16 every 32 "
+                                     "rounds, token tree of width 3 and depth 4 per round"),
     "cascade_8b": dict(shape="llama3_8b", prompt=(128, 512, 2048), gen=256,
                        policy={"mode": "cascade", "k_max": 8, "interval": 32,
                                "levels": [(22, 4, False), (10, 0, True), (0, 0, True)]},
@@ -128,7 +135,7 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
                         cascade=list(policy["levels"]) if policy["mode"] == "cascade" else None,
                         latency_beta=tuple(policy.get("beta", (1.0, 0.0, 1.0))),
                         temperature=float(policy.get("temperature", 0.0)), seed=int(policy.get("seed", 0)),
-                        tree_width=int(policy.get("tree_width", 0)))
+                        tree_width=int(policy.get("tree_width", 0)), tree_depth=int(policy.get("tree_depth", 1)))
     sample = np.asarray(prompt[:n_prompt])
     t0 = time.perf_counter()
     toks, recs = oracle.speculative_generate(model, sample, n_tokens, pol)

@@ -153,21 +153,29 @@ int lss_set_sampling(lss_engine* e, float temperature, uint64_t seed);
 int lss_draft(lss_engine* e, const uint8_t* skip_mask, int32_t quant, int32_t k, float exit_tau,
               int32_t* tokens_out, int32_t* k_done);
 
-/* Token-tree draft of width B (1 <= B <= 8) and depth 1, the pages' "dynamic
- * tree cascade" read as a token tree (CAS-Spec abstract; CAS-Spec blog
- * section 3): the draft (skip mask, quant as in lss_draft) runs the pending
- * token's row at position p and proposes its B most likely tokens (largest
- * logit first, ties to the lower id) as sibling candidates for position
- * p + 1; tokens_out[B] receives them.  lss_verify(e, NULL, B) then verifies
- * them in one pass with a tree mask (each candidate sees the committed
- * prefix, the pending token and itself, so its row equals the full model's
- * step after it bit for bit) and accepts greedily: the candidate equal to
- * the full model's token after the pending one, with its own successor as
- * the bonus (n = 1), else that token alone (n = 0); the accepted
- * candidate's keys and values become position p + 1's.  Greedy only
- * (LSS_EINVAL with sampling on); LSS_ESTATE unless the window is empty;
- * LSS_ECAPACITY if B + 1 > max_rows or the KV capacity is exceeded. */
-int lss_draft_tree(lss_engine* e, const uint8_t* skip_mask, int32_t quant, int32_t B, int32_t* tokens_out);
+/* Token-tree draft of width B (1 <= B <= 8) and depth D >= 1, the pages'
+ * "dynamic tree cascade" read as a token tree (CAS-Spec abstract; CAS-Spec
+ * blog section 3): the draft (skip mask, quant as in lss_draft) runs the
+ * pending token's row at position p and takes its B most likely tokens
+ * (largest logit first, ties to the lower id) as the first nodes of B
+ * branches for position p + 1, then extends every branch greedily by D - 1
+ * tokens, all branches' rows of one depth in one draft pass (node j of a
+ * branch, at position p + j, sees the committed prefix, the pending token
+ * and its branch's nodes 1..j only).  tokens_out[B * D] receives the
+ * branches one after the other (branch b's node j at index b D + j - 1).
+ * lss_verify(e, NULL, B * D) then verifies every node in one pass with a
+ * tree mask (each node's row equals the full model's step after its
+ * branch's earlier nodes, bit for bit) and accepts greedily: the branch
+ * whose first node equals the full model's token after the pending one is
+ * followed while each next node equals the full model's token after the
+ * previous one; n = accepted nodes, the bonus the full model's token after
+ * the last of them (n = 0 and that first token when no branch matches);
+ * the accepted nodes' keys and values become positions p + 1 .. p + n.
+ * Greedy only (LSS_EINVAL with sampling on); LSS_ESTATE unless the window
+ * is empty; LSS_ECAPACITY if B D > LSS_TREE_NODES_MAX, B D + 1 > max_rows
+ * or the KV capacity is exceeded. */
+#define LSS_TREE_NODES_MAX 15
+int lss_draft_tree(lss_engine* e, const uint8_t* skip_mask, int32_t quant, int32_t B, int32_t D, int32_t* tokens_out);
 
 /* Verify the window in one full-model pass over rows [t0, d1..dk] at
  * positions p..p+k (CLaSp section 3, verification).  drafts == NULL
@@ -224,6 +232,7 @@ typedef struct lss_policy {
   int32_t level_quant[LSS_LEVELS_MAX]; /* int8 activations per level */
   double beta[3];            /* CASCADE latency model b0 + b1*seq_len + b2*executed_layers */
   int32_t tree_width;        /* STATIC / DP: > 0 drafts a width-B token tree per round (lss_draft_tree) */
+  int32_t tree_depth;        /* tree depth (0 or 1: depth 1), cut to the tokens still to emit per round */
 } lss_policy;
 
 typedef struct lss_stats {

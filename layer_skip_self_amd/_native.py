@@ -9,6 +9,7 @@ LSS_OK, LSS_EINVAL, LSS_ESTATE, LSS_ECAPACITY, LSS_EHIP, LSS_ENOTIMPL = 0, -1, -
 LSS_F32, LSS_BF16 = 0, 1
 LSS_MODE_AR, LSS_MODE_STATIC, LSS_MODE_DP, LSS_MODE_CASCADE = 0, 1, 2, 3
 LSS_WINDOW_MAX = 31
+LSS_TREE_NODES_MAX = 15
 LSS_ROWS_MAX = 64
 LSS_LEVELS_MAX = 4
 LSS_ACCEPT_ROWS_MAX = 64
@@ -36,7 +37,7 @@ class lss_policy(C.Structure):
                 ("n_skip", C.c_int32), ("interval", C.c_int32), ("n_levels", C.c_int32),
                 ("level_skip", C.c_int32 * LSS_LEVELS_MAX), ("level_exit", C.c_int32 * LSS_LEVELS_MAX),
                 ("level_quant", C.c_int32 * LSS_LEVELS_MAX), ("beta", C.c_double * 3),
-                ("tree_width", C.c_int32)]
+                ("tree_width", C.c_int32), ("tree_depth", C.c_int32)]
 
 
 class lss_stats(C.Structure):
@@ -56,7 +57,8 @@ SIGNATURES = {
     "lss_prefill": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.POINTER(C.c_int32)]),
     "lss_draft": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint8), C.c_int32, C.c_int32, C.c_float,
                             C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
-    "lss_draft_tree": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint8), C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
+    "lss_draft_tree": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint8), C.c_int32, C.c_int32, C.c_int32,
+                                 C.POINTER(C.c_int32)]),
     "lss_verify": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32]),
     "lss_accept_and_rollback": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                                           C.POINTER(C.c_int32)]),

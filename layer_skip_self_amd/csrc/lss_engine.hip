@@ -164,7 +164,9 @@ size_t w8_layout(const lss_config* c, std::vector<std::array<size_t, 14>>* offs)
   return off;
 }
 
-enum RowMode { MODE_CAUSAL = 0, MODE_DRAFT = 1, MODE_DP = 2, MODE_TREE = 3 };
+// MODE_TREE: a tree verify pass; MODE_TREE_DRAFT: a tree draft step (rows =
+// the nodes of one depth of consecutive branches)
+enum RowMode { MODE_CAUSAL = 0, MODE_DRAFT = 1, MODE_DP = 2, MODE_TREE = 3, MODE_TREE_DRAFT = 4 };
 
 }  // namespace
 
@@ -192,6 +194,8 @@ struct lss_engine {
   float *dlogits = nullptr, *srec = nullptr;  // sampling: draft logits of the window slots, replacement-draw records
   int8_t* q8 = nullptr;                       // int8-weight draft: activation codes of the row
   int tree = 0;                               // width of the pending tree window (0: a chain)
+  int tree_D = 1;                             // its depth
+  int tree_step = 0, tree_b0 = 0;             // MODE_TREE_DRAFT rows: depth, branch of the first row
   std::vector<LayerW8> w8;                    // int8 weight copies (lss_attach_w8), empty until attached
   void *xa, *xb, *xc;   // projection inputs: layer input (attention-norm gain), attention / FFN output, mid-layer
   float *pa, *pc;       // partial sums of squares of the residual rows behind xa and xc
@@ -516,7 +520,11 @@ void attention(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
   a.kc = kc_layer(e, l); a.vc = vc_layer(e, l);
   a.max_seq = c.max_seq; a.Hq = c.n_heads; a.Hkv = c.n_kv_heads; a.M = M;
   a.pos0 = pos0; a.pos_step = mode == MODE_DP ? 0 : 1;
-  a.tree = mode == MODE_TREE ? 1 : 0;
+  const bool tree = mode == MODE_TREE || mode == MODE_TREE_DRAFT;
+  a.tree = tree ? 1 : 0;
+  a.tree_D = e->tree_D;
+  a.tree_step = mode == MODE_TREE_DRAFT ? e->tree_step : 0;
+  a.tree_b0 = mode == MODE_TREE_DRAFT ? e->tree_b0 : 0;
   a.part = e->apart; a.nz_max = e->lay.nz_max; a.nch_max = e->lay.nch_max;
   a.out = e->aout;
   a.xo = quant ? nullptr : e->xb;
@@ -524,6 +532,10 @@ void attention(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
   int kmax;
   if (mode == MODE_CAUSAL) { a.lim_base = pos0 + 1; a.lim_step = 1; a.wbase = 0; a.wmask = 0; kmax = pos0 + M; }
   else if (mode == MODE_TREE) { a.lim_base = pos0 + 1; a.lim_step = 0; a.wbase = 0; a.wmask = 0; kmax = pos0 + M; }
+  else if (mode == MODE_TREE_DRAFT) {             // last row's slot: pos0 + j + (b0 + M - 1) D
+    a.lim_base = pos0 + 1; a.lim_step = 0; a.wbase = 0; a.wmask = 0;
+    kmax = pos0 + e->tree_step + (e->tree_b0 + M - 1) * e->tree_D + 1;
+  }
   else if (mode == MODE_DRAFT) { a.lim_base = e->p; a.lim_step = 0; a.wbase = e->p; a.wmask = e->valid[l]; kmax = pos0 + 1; }
   else { a.lim_base = pos0; a.lim_step = 0; a.wbase = 0; a.wmask = 0; a.self_kv = 1; kmax = pos0; }
   a.nch = std::max(1, (kmax + ATT_CH - 1) / ATT_CH);
@@ -531,7 +543,6 @@ void attention(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
   a.nz = (G * M + ATT_QB - 1) / ATT_QB;
   const int mq = std::min(ATT_QB, G * M);             // merge workgroups per query block and kv head
   const dim3 grid(a.nch, c.n_kv_heads, a.nz);
-  const bool tree = mode == MODE_TREE;
   if (hd == 128) {
     if (tree) hipLaunchKernelGGL((k_attention<KT, WT, 128, true>), grid, dim3(ATT_THREADS), 0, e->stream, a);
     else hipLaunchKernelGGL((k_attention<KT, WT, 128>), grid, dim3(ATT_THREADS), 0, e->stream, a);
@@ -730,16 +741,16 @@ void head(lss_engine* e, int r0, int M, int row0, int pos0, bool draft) {
   if (!(samp && draft)) e->logits_rows = M;
 }
 
-// embedding rows of tokens tok_dev[0..M) into h, with the projection input
+// embedding rows of tokens tok_dev[0], tok_dev[ts], .. (M rows) into h, with the projection input
 // for gain g into e->xa / e->pa
-void embed(lss_engine* e, const int32_t* tok_dev, int M, float* h, const float* g) {
+void embed(lss_engine* e, const int32_t* tok_dev, int M, float* h, const float* g, int ts = 1) {
   const auto& c = e->cfg;
   if (e->bf16)
     hipLaunchKernelGGL(k_embed<uint16_t>, dim3(M), dim3(PREP_THREADS), 0, e->stream, (const uint16_t*)e->embed, tok_dev,
-                       c.d_model, h, g, e->xa, e->pa);
+                       ts, c.d_model, h, g, e->xa, e->pa);
   else
     hipLaunchKernelGGL(k_embed<float>, dim3(M), dim3(PREP_THREADS), 0, e->stream, (const float*)e->embed, tok_dev,
-                       c.d_model, h, g, e->xa, e->pa);
+                       ts, c.d_model, h, g, e->xa, e->pa);
 }
 
 // gain of the RMSNorm that consumes the residual after layer l (l = -1: the
@@ -1148,19 +1159,23 @@ int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, floa
   return LSS_OK;
 }
 
-int lss_draft_tree(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t B, int32_t* tokens_out) {
+int lss_draft_tree(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t B, int32_t D, int32_t* tokens_out) {
   if (!e) return LSS_EINVAL;
   const GemvScope gv(e, true);
   const auto& c = e->cfg;
   if (!e->have_seq || e->pending_accept || e->win != 0)
     return fail(e, LSS_ESTATE, "draft_tree: needs a prefilled sequence, no pending accept and an empty window");
-  if (!mask || !tokens_out || B < 1 || B > TOPB_MAX || B > c.vocab || quant < 0 || quant > 2)
-    return fail(e, LSS_EINVAL, "draft_tree: bad arguments (1 <= B <= 8)");
+  if (!mask || !tokens_out || B < 1 || B > TOPB_MAX || B > c.vocab || D < 1 || quant < 0 || quant > 2)
+    return fail(e, LSS_EINVAL, "draft_tree: bad arguments (1 <= B <= 8, D >= 1)");
   if (e->inv_t > 0.f) return fail(e, LSS_EINVAL, "draft_tree: tree acceptance is greedy; sampling is on");
   if (quant == 2 && e->w8.empty()) return fail(e, LSS_ESTATE, "draft_tree: int8 weights not attached");
-  if (B + 1 > c.max_rows || B > std::min(kWinMax, c.max_rows - 1)) return fail(e, LSS_ECAPACITY, "draft_tree: B + 1 > max_rows");
-  if (e->p + B + 1 > c.max_seq) return fail(e, LSS_ECAPACITY, "draft_tree: KV capacity exceeded");
+  const long nodes = (long)B * D;
+  if (nodes > LSS_TREE_NODES_MAX || nodes + 1 > c.max_rows || nodes > kWinMax)
+    return fail(e, LSS_ECAPACITY, "draft_tree: B * D above LSS_TREE_NODES_MAX or max_rows - 1");
+  if (e->p + nodes + 1 > c.max_seq) return fail(e, LSS_ECAPACITY, "draft_tree: KV capacity exceeded");
+  static_assert(LSS_TREE_NODES_MAX < ATT_TREE_NODES, "tree nodes must fit the attention kernel's node arrays");
   // the draft row of the pending token (slot 0, position p), then its top B
+  // as the branches' first nodes (window slots 1 + b D)
   embed(e, e->tok, 1, hs_row(e, 0, 0), next_gain(e, mask, -1));
   const float* h = hs_row(e, 0, 0);
   for (int l = 0; l < c.n_layers; ++l) {
@@ -1170,13 +1185,39 @@ int lss_draft_tree(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t B,
     h = hs_row(e, l + 1, 0);
   }
   head(e, 0, 1, 0, e->p, true);
-  hipLaunchKernelGGL(k_topb, dim3(1), dim3(TOPB_THREADS), 0, e->stream, (const float*)e->logits, c.vocab, B, e->tok);
+  hipLaunchKernelGGL(k_topb, dim3(1), dim3(TOPB_THREADS), 0, e->stream, (const float*)e->logits, c.vocab, B, D, e->tok);
+  // depth j = 1 .. D - 1: node j of branches b0 .. b0 + M - 1 (window slots
+  // 1 + b D + j - 1) through the draft, their argmax nodes j + 1.  Int8
+  // weights draft one row at a time, so one branch per pass there.
+  e->tree_D = D;
+  auto step = [&](int j, int b0, int M) {
+    e->tree_step = j;
+    e->tree_b0 = b0;
+    embed(e, e->tok + 1 + b0 * D + j - 1, M, hs_row(e, 0, 0), next_gain(e, mask, -1), D);
+    const float* hh = hs_row(e, 0, 0);
+    for (int l = 0; l < c.n_layers; ++l) {
+      if (mask[l]) continue;
+      layer_forward(e, l, M, hh, e->xa, e->pa, hs_row(e, l + 1, 0), next_gain(e, mask, l), MODE_TREE_DRAFT, e->p,
+                    quant);
+      hh = hs_row(e, l + 1, 0);
+    }
+    head(e, 0, M, b0, e->p + j, true);
+  };
+  for (int j = 1; j < D; ++j) {
+    if (quant == 2)
+      for (int b = 0; b < B; ++b) step(j, b, 1);
+    else
+      step(j, 0, B);
+    hipLaunchKernelGGL(k_tree_draft_commit, dim3(1), dim3(64), 0, e->stream, (const HeadRes*)e->res, B, D, j, e->tok);
+  }
+  e->tree_step = 0;
+  e->tree_b0 = 0;
   int rc = check_launch(e, "draft_tree");
   if (rc) return rc;
-  HIPCHK(hipMemcpyAsync(e->hstage, e->tok + 1, sizeof(int32_t) * B, hipMemcpyDeviceToHost, e->stream));
+  HIPCHK(hipMemcpyAsync(e->hstage, e->tok + 1, sizeof(int32_t) * nodes, hipMemcpyDeviceToHost, e->stream));
   HIPCHK(hipStreamSynchronize(e->stream));
-  std::memcpy(tokens_out, e->hstage, sizeof(int32_t) * B);
-  e->win = B;
+  std::memcpy(tokens_out, e->hstage, sizeof(int32_t) * nodes);
+  e->win = (int)nodes;
   e->tree = B;
   return LSS_OK;
 }
@@ -1207,14 +1248,14 @@ int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k) {
   if (e->tree > 0) {                                   // width-B tree: one pass, tree mask
     forward_rows(e, e->tok, M, e->p, MODE_TREE);
     head(e, 0, M, 0, e->p, false);
-    hipLaunchKernelGGL(k_accept_tree, dim3(1), dim3(1), 0, e->stream, e->res, k, e->tok);
+    hipLaunchKernelGGL(k_accept_tree, dim3(1), dim3(1), 0, e->stream, e->res, e->tree, e->tree_D, e->tok);
     const dim3 fg(c.n_layers, c.n_kv_heads);
     if (e->kv16)
-      hipLaunchKernelGGL(k_tree_kv_fix<uint16_t>, fg, dim3(128), 0, e->stream, (const HeadRes*)e->res,
+      hipLaunchKernelGGL(k_tree_kv_fix<uint16_t>, fg, dim3(256), 0, e->stream, (const HeadRes*)e->res, e->tree_D,
                          (uint16_t*)e->kc, (uint16_t*)e->vc, c.n_kv_heads, c.max_seq, c.head_dim, e->p);
     else
-      hipLaunchKernelGGL(k_tree_kv_fix<float>, fg, dim3(128), 0, e->stream, (const HeadRes*)e->res, (float*)e->kc,
-                         (float*)e->vc, c.n_kv_heads, c.max_seq, c.head_dim, e->p);
+      hipLaunchKernelGGL(k_tree_kv_fix<float>, fg, dim3(256), 0, e->stream, (const HeadRes*)e->res, e->tree_D,
+                         (float*)e->kc, (float*)e->vc, c.n_kv_heads, c.max_seq, c.head_dim, e->p);
     hipLaunchKernelGGL(k_gather_target, dim3(c.n_layers + 1), dim3(256), 0, e->stream, e->hs, c.max_rows,
                        c.d_model, (const HeadRes*)e->res, 0, e->target);
     const int rc = check_launch(e, "verify");
@@ -1262,6 +1303,7 @@ int lss_accept_and_rollback(lss_engine* e, int32_t* n_accepted, int32_t* bonus, 
   e->p += n + 1;
   e->win = 0;
   e->tree = 0;
+  e->tree_D = 1;
   std::fill(e->valid.begin(), e->valid.end(), 0u);
   e->pending_accept = false;
   return LSS_OK;
@@ -1459,6 +1501,9 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
   if (pol->tree_width < 0 || pol->tree_width > TOPB_MAX ||
       (pol->tree_width > 0 && pol->mode != LSS_MODE_STATIC && pol->mode != LSS_MODE_DP))
     return fail(e, LSS_EINVAL, "generate: tree_width must be 0..8 and needs the static or DP mode");
+  const int tree_depth = std::max(1, pol->tree_depth);   // 0: depth 1
+  if (pol->tree_width > 0 && (pol->tree_depth < 0 || (long)pol->tree_width * tree_depth > LSS_TREE_NODES_MAX))
+    return fail(e, LSS_EINVAL, "generate: tree_depth must be >= 0 with tree_width * tree_depth <= 15");
   if ((pol->mode == LSS_MODE_DP || pol->mode == LSS_MODE_CASCADE) && pol->interval < 1)
     return fail(e, LSS_EINVAL, "generate: interval < 1");
   if (pol->mode == LSS_MODE_CASCADE) {
@@ -1506,7 +1551,8 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
     slot_levels.clear();
     if ((pol->mode == LSS_MODE_STATIC || pol->mode == LSS_MODE_DP) && pol->tree_width > 0) {
       if (budget > 0) {
-        rc = lss_draft_tree(e, masks[0].data(), pol->quant, pol->tree_width, toks.data());
+        rc = lss_draft_tree(e, masks[0].data(), pol->quant, pol->tree_width, std::min(tree_depth, budget),
+                            toks.data());
         if (rc) return rc;
       }
     } else if (pol->mode == LSS_MODE_STATIC || pol->mode == LSS_MODE_DP) {

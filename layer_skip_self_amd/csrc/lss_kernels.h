@@ -263,11 +263,12 @@ __global__ __launch_bounds__(PREP_THREADS) void k_prep_rows(const float* __restr
 // h[m][:] = E[tok[m]][:] (float32 residual stream) and its projection input.
 template <typename WT>
 __global__ __launch_bounds__(PREP_THREADS) void k_embed(const WT* __restrict__ E, const int32_t* __restrict__ tok,
-                                                        int d, float* __restrict__ h, const float* __restrict__ g,
-                                                        void* xo, float* __restrict__ po) {
+                                                        int ts, int d, float* __restrict__ h,
+                                                        const float* __restrict__ g, void* xo,
+                                                        float* __restrict__ po) {
   const int m = blockIdx.x;
   float v[PREP_PER_THREAD];
-  load_vals<WT>(v, E + (size_t)tok[m] * d, d);
+  load_vals<WT>(v, E + (size_t)tok[(size_t)m * ts] * d, d);
   float* hr = h + (size_t)m * d;
 #pragma unroll
   for (int j = 0; j < PREP_PER_THREAD; ++j) {
@@ -1490,12 +1491,15 @@ __global__ __launch_bounds__(G8_THREADS) void k_gemv8(GemmArgs ga) {
 // holds them writes them to the cache.  Layer-selection launches write
 // nothing; each row's own key/value enters the merge directly.
 //
-// Tree launches (a width-B token tree): row 0 is the pending token at pos0;
-// rows 1..B are sibling candidates of position pos0 + 1, rotated there and
-// written to cache slots pos0 + m.  Row m >= 1 sees u < pos0 + 2 with slot
-// pos0 + 1 holding its own key and value (a per-row substitute inside that
-// slot's chunk), so its scores, chunk partials and merge are those of the
-// plain step at pos0 + 1 after that candidate, bit for bit.
+// Tree launches (a token tree of width B and depth D; node (b, j) is the
+// j-th token of branch b, at position pos0 + j): a row of depth j sees
+// positions u <= pos0 + j, and inside the chunks that hold positions
+// pos0 + 1 .. pos0 + j its own branch's nodes 1..j stand in for the keys and
+// values there (per-row substitutes), so its scores, chunk partials and
+// merge are those of the plain step at pos0 + j after that branch's first j
+// tokens, bit for bit.  Nodes that are rows of the launch are rotated from
+// its projection output; a draft step's earlier nodes come from their cache
+// slots.
 #define ATT_CH 64
 #define ATT_QB 32
 #define ATT_THREADS 512
@@ -1513,7 +1517,9 @@ struct AttnArgs {
   int lim_base, lim_step, wbase;
   uint32_t wmask;
   int self_kv;                     // 1: layer-selection rows (own key/value, no cache write)
-  int tree;                        // 1: tree launch (row 0 pending token, rows >= 1 candidates)
+  int tree;                        // 1: token-tree launch (rows below)
+  int tree_D, tree_step;           // tree depth; 0: verify rows, j >= 1: draft rows of depth j
+  int tree_b0;                     // draft rows: branch of row 0
   int nch, nz;                     // key chunks, query blocks in this launch
   float* part;                     // [Hkv][nz_max][nch_max][QB][hd + 2]
   int nz_max, nch_max;
@@ -1537,9 +1543,33 @@ __device__ __forceinline__ float rope_elem(const float* x, const float2* cs, int
   return rope_val(x[i], x[j], cs[low ? i : j], low);
 }
 
-// rotary position of launch row m (tree launches: all candidates at pos0 + 1)
+// Token trees (width B, depth D; node j of branch b is the token at
+// position pos0 + j): a verify launch has rows [pending token, branch 0
+// nodes 1..D, branch 1 nodes, ...]; a draft launch of depth j has row b =
+// node j of branch b.  Node (b, j) keeps its keys and values in cache slot
+// pos0 + 1 + b D + (j - 1) (its verify row index), and a row of depth j sees
+// positions [0, pos0 + j] with its own branch's nodes standing in for
+// positions pos0 + 1 .. pos0 + j.
+__device__ __forceinline__ int att_tree_depth(const AttnArgs& a, int m) {
+  return a.tree_step > 0 ? a.tree_step : (m == 0 ? 0 : (m - 1) % a.tree_D + 1);
+}
+__device__ __forceinline__ int att_tree_branch(const AttnArgs& a, int m) {
+  return a.tree_step > 0 ? a.tree_b0 + m : (m == 0 ? 0 : (m - 1) / a.tree_D);
+}
+// rotary position of launch row m
 __device__ __forceinline__ int att_row_pos(const AttnArgs& a, int m) {
-  return a.tree ? a.pos0 + (m > 0 ? 1 : 0) : a.pos0 + m * a.pos_step;
+  return a.tree ? a.pos0 + att_tree_depth(a, m) : a.pos0 + m * a.pos_step;
+}
+// cache slot of launch row m: pos0 + m, or for a tree draft step of depth j
+// pos0 + j + b D (increasing with the row either way)
+__device__ __forceinline__ bool att_tree_draft(const AttnArgs& a) { return a.tree && a.tree_step > 0; }
+__device__ __forceinline__ int att_row_slot(const AttnArgs& a, int m) {
+  return att_tree_draft(a) ? a.pos0 + a.tree_step + (a.tree_b0 + m) * a.tree_D : a.pos0 + m;
+}
+// first launch row whose cache slot is >= s (M if none)
+__device__ __forceinline__ int att_first_row(const AttnArgs& a, int s) {
+  const int base = att_row_slot(a, 0), st = att_tree_draft(a) ? a.tree_D : 1;
+  return s <= base ? 0 : min(a.M, (s - base + st - 1) / st);
 }
 
 // 4 consecutive cache elements as float
@@ -1587,23 +1617,26 @@ template <typename KT, int HD>
 struct AttNew {
   float xi[ATT_NR_J], xp[ATT_NR_J];   // key element and its rotation partner, or the value element
   float2 c[ATT_NR_J];
-  int r0, n;                          // first new row of the chunk, elements (rows x HD)
+  int m0, n;                          // first launch row whose slot is in the chunk, elements (rows x HD)
   __device__ __forceinline__ void load(const AttnArgs& a, int kh, int u0, bool is_v) {
-    r0 = max(u0, a.pos0);
-    n = a.self_kv ? 0 : max(0, min(u0 + ATT_CH, a.pos0 + a.M) - r0) * HD;
+    // launch rows with a slot in [u0, u0 + ATT_CH): a contiguous range of rows
+    const int lo = a.self_kv ? 0 : att_first_row(a, u0);
+    const int hi = a.self_kv ? 0 : att_first_row(a, u0 + ATT_CH);
+    m0 = lo;
+    n = (hi - lo) * HD;
     const int off = (is_v ? a.Hq + a.Hkv : a.Hq) + kh;
 #pragma unroll
     for (int j = 0; j < ATT_NR_J; ++j) {
       const int i = threadIdx.x + j * ATT_THREADS;
       if (i < n) {
-        const int pos = r0 + i / HD, dd = i % HD;
-        const float* x = a.qkv + (size_t)(pos - a.pos0) * a.ldqkv + (size_t)off * HD;
+        const int m = m0 + i / HD, dd = i % HD;
+        const float* x = a.qkv + (size_t)m * a.ldqkv + (size_t)off * HD;
         xi[j] = x[dd];
         if (!is_v) {
           const bool low = dd < HD / 2;
           const int pj = low ? dd + HD / 2 : dd - HD / 2;
           xp[j] = x[pj];
-          c[j] = a.cs[(size_t)att_row_pos(a, pos - a.pos0) * (HD / 2) + (low ? dd : pj)];
+          c[j] = a.cs[(size_t)att_row_pos(a, m) * (HD / 2) + (low ? dd : pj)];
         }
       }
     }
@@ -1616,35 +1649,38 @@ struct AttNew {
     for (int j = 0; j < ATT_NR_J; ++j) {
       const int i = threadIdx.x + j * ATT_THREADS;
       if (i < n) {
-        const int pos = r0 + i / HD, dd = i % HD;
+        const int m = m0 + i / HD, dd = i % HD;
+        const int slot = att_row_slot(a, m);
         float v = is_v ? xi[j] : rope_val(xi[j], xp[j], c[j], dd < HD / 2);
         v = kv_round<KT>(v);
-        if (z == 0) st_elem<KT>(cache, (size_t)pos * HD + dd, v);
-        t[pos - u0][dd] = v;
+        if (z == 0) st_elem<KT>(cache, (size_t)slot * HD + dd, v);
+        t[slot - u0][dd] = v;
       }
     }
     const int off = (is_v ? a.Hq + a.Hkv : a.Hq) + kh;
     for (int i = threadIdx.x + ATT_NR_J * ATT_THREADS; i < n; i += ATT_THREADS) {
-      const int pos = r0 + i / HD, dd = i % HD;
-      const float* x = a.qkv + (size_t)(pos - a.pos0) * a.ldqkv + (size_t)off * HD;
-      const int rp = att_row_pos(a, pos - a.pos0);
+      const int m = m0 + i / HD, dd = i % HD;
+      const int slot = att_row_slot(a, m);
+      const float* x = a.qkv + (size_t)m * a.ldqkv + (size_t)off * HD;
+      const int rp = att_row_pos(a, m);
       float v = is_v ? x[dd] : rope_elem(x, a.cs + (size_t)rp * (HD / 2), dd, HD / 2);
       v = kv_round<KT>(v);
-      if (z == 0) st_elem<KT>(cache, (size_t)pos * HD + dd, v);
-      t[pos - u0][dd] = v;
+      if (z == 0) st_elem<KT>(cache, (size_t)slot * HD + dd, v);
+      t[slot - u0][dd] = v;
     }
   }
 };
 
-#define ATT_TREE_MAX 8
+// tree nodes (B D) a launch may hold
+#define ATT_TREE_NODES 16
 template <typename KT, typename WT, int HD, bool TREE = false>
 __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
   __shared__ __align__(16) float kv_s[ATT_CH][ATT_LD];
   __shared__ __align__(16) float q_s[ATT_QB][HD];
   __shared__ float p_s[ATT_QB][ATT_CH];
   __shared__ float st_s[ATT_QB][2];
-  __shared__ float own_s[TREE ? ATT_TREE_MAX + 1 : 1][TREE ? HD : 1];   // tree: candidates' own keys
-  __shared__ float own_v[TREE ? ATT_TREE_MAX + 1 : 1][TREE ? HD : 1];   // and values
+  __shared__ float own_s[TREE ? ATT_TREE_NODES : 1][TREE ? HD : 1];   // tree: node b D + j - 1's key
+  __shared__ float own_v[TREE ? ATT_TREE_NODES : 1][TREE ? HD : 1];   // and value
   const int c = blockIdx.x, kh = blockIdx.y, z = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int nq = G * a.M;
@@ -1670,19 +1706,34 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
     q_s[qi][dd] = rope_elem(a.qkv + (size_t)m * a.ldqkv + (size_t)h * HD, a.cs + (size_t)pos * (HD / 2), dd, HD / 2);
   }
   kt.store(kv_s);
-  // tree: the candidates' own keys and values (rotated at pos0 + 1, rounded
-  // to the cache type) for the chunk that holds slot pos0 + 1
-  const int uown = a.pos0 + 1 - u0;
-  const bool has_own = TREE && uown >= 0 && uown < ATT_CH;
+  // tree: the keys and values of the nodes whose positions lie in this
+  // chunk (rotated at their positions, rounded to the cache type)
   if constexpr (TREE) {
-    if (has_own) {
-      const int nown = min(a.M - 1, ATT_TREE_MAX);
-      for (int i = tid; i < nown * HD; i += ATT_THREADS) {
-        const int m = 1 + i / HD, dd = i % HD;
-        const float* xk = a.qkv + (size_t)m * a.ldqkv + (size_t)(a.Hq + kh) * HD;
-        const float* xv = a.qkv + (size_t)m * a.ldqkv + (size_t)(a.Hq + a.Hkv + kh) * HD;
-        own_s[m][dd] = kv_round<KT>(rope_elem(xk, a.cs + (size_t)(a.pos0 + 1) * (HD / 2), dd, HD / 2));
-        own_v[m][dd] = kv_round<KT>(xv[dd]);
+    const int imax = a.tree_step > 0 ? a.tree_step : a.tree_D;
+    const int ilo = max(1, u0 - a.pos0), ihi = min(imax, u0 + ATT_CH - 1 - a.pos0);
+    if (ilo <= ihi) {
+      const int bfirst = a.tree_step > 0 ? a.tree_b0 : 0;
+      const int nb = a.tree_step > 0 ? a.M : (a.M - 1) / a.tree_D;
+      const int ni = ihi - ilo + 1;
+      for (int t = tid; t < nb * ni * HD; t += ATT_THREADS) {
+        const int dd = t % HD, r = t / HD;
+        const int b = bfirst + r / ni, i = ilo + r % ni;
+        const int k = b * a.tree_D + i - 1;
+        if (k >= ATT_TREE_NODES) continue;
+        float kv, vv;
+        if (a.tree_step > 0 && i < a.tree_step) {      // an earlier draft step's node: its cache slot
+          const size_t slot = (size_t)(a.pos0 + 1 + k);
+          kv = ld_elem<KT>(kc, slot * HD + dd);
+          vv = ld_elem<KT>(vc, slot * HD + dd);
+        } else {
+          const int m = a.tree_step > 0 ? b - a.tree_b0 : 1 + k;
+          const float* x = a.qkv + (size_t)m * a.ldqkv;
+          kv = kv_round<KT>(rope_elem(x + (size_t)(a.Hq + kh) * HD, a.cs + (size_t)(a.pos0 + i) * (HD / 2), dd,
+                                      HD / 2));
+          vv = kv_round<KT>(x[(size_t)(a.Hq + a.Hkv + kh) * HD + dd]);
+        }
+        own_s[k][dd] = kv;
+        own_v[k][dd] = vv;
       }
     }
   }
@@ -1699,10 +1750,13 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
       const int qcc = has_c ? qc : qb;
       float da = 0.f, dc = 0.f;
       if constexpr (TREE) {
-        // a candidate row's own slot reads its own key (same FMA order)
+        // positions pos0 + 1 .. pos0 + j of a depth-j row read its branch's
+        // nodes (same FMA order)
         const int ma = (q0 + qb) / G, mc = (q0 + qcc) / G;
-        const float* ka = (has_own && u == uown && ma >= 1) ? own_s[ma] : kv_s[u];
-        const float* kc = (has_own && u == uown && mc >= 1) ? own_s[mc] : kv_s[u];
+        const int i = pos - a.pos0;
+        const bool sa = i >= 1 && i <= att_tree_depth(a, ma), sc = i >= 1 && i <= att_tree_depth(a, mc);
+        const float* ka = sa ? own_s[att_tree_branch(a, ma) * a.tree_D + i - 1] : kv_s[u];
+        const float* kc = sc ? own_s[att_tree_branch(a, mc) * a.tree_D + i - 1] : kv_s[u];
 #pragma unroll 8
         for (int dd = 0; dd < HD; ++dd) {
           da = fmaf(q_s[qb][dd], ka[dd], da);
@@ -1725,7 +1779,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
         if (h2 == 1 && !has_c) break;                  // wave-uniform
         const int qi = h2 ? qc : qb;
         const int m = (q0 + qi) / G;
-        const int lim = TREE ? a.lim_base + (m > 0 ? 1 : 0) : a.lim_base + m * a.lim_step;
+        const int lim = TREE ? a.lim_base + att_tree_depth(a, m) : a.lim_base + m * a.lim_step;
         const int wo = pos - a.wbase;
         const bool vis = pos < lim || (wo >= 0 && wo < 32 && ((a.wmask >> wo) & 1u));
         const float s = (vis && pos < a.max_seq) ? __fmul_rn(h2 ? dc : da, a.scale) : -INFINITY;
@@ -1753,12 +1807,17 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
     const int qc = has1 ? i1 / HD : qa, dc = has1 ? i1 % HD : da;
     float acc0 = 0.f, acc1 = 0.f;
     if constexpr (TREE) {
+      // keys u in [ulo, ulo + j - 1] of a depth-j row are its branch's nodes
+      // b D + (u - ulo)
       const int ma = (q0 + qa) / G, mc = (q0 + qc) / G;
-      const int ua = (has_own && ma >= 1) ? uown : -1, uc = (has_own && mc >= 1) ? uown : -1;
+      const int ulo = a.pos0 + 1 - u0;
+      const int uha = ulo + att_tree_depth(a, ma) - 1, uhc = ulo + att_tree_depth(a, mc) - 1;
+      const int kba = att_tree_branch(a, ma) * a.tree_D - ulo, kbc = att_tree_branch(a, mc) * a.tree_D - ulo;
 #pragma unroll 8
       for (int u = 0; u < ATT_CH; ++u) {
-        acc0 = fmaf(p_s[qa][u], u == ua ? own_v[ma][da] : kv_s[u][da], acc0);
-        acc1 = fmaf(p_s[qc][u], u == uc ? own_v[mc][dc] : kv_s[u][dc], acc1);
+        const bool sa = u >= ulo && u <= uha, sc = u >= ulo && u <= uhc;
+        acc0 = fmaf(p_s[qa][u], sa ? own_v[sa ? kba + u : 0][da] : kv_s[u][da], acc0);
+        acc1 = fmaf(p_s[qc][u], sc ? own_v[sc ? kbc + u : 0][dc] : kv_s[u][dc], acc1);
       }
     } else {
 #pragma unroll 8
@@ -1951,7 +2010,7 @@ __global__ void k_accept(HeadRes* res, int k, int32_t* tok, int samp) {
 __device__ __forceinline__ bool topb_before(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
 }
-__global__ __launch_bounds__(TOPB_THREADS) void k_topb(const float* __restrict__ z, int V, int B,
+__global__ __launch_bounds__(TOPB_THREADS) void k_topb(const float* __restrict__ z, int V, int B, int ts,
                                                       int32_t* __restrict__ tok) {
   __shared__ float bm[TOPB_THREADS / 64];
   __shared__ int bi[TOPB_THREADS / 64];
@@ -1982,7 +2041,7 @@ __global__ __launch_bounds__(TOPB_THREADS) void k_topb(const float* __restrict__
     mx = bm[0]; idx = bi[0];
     for (int i = 1; i < (int)(blockDim.x >> 6); ++i) argmax_merge(mx, idx, bm[i], bi[i]);
     __syncthreads();
-    if (threadIdx.x == 0) tok[1 + r] = (idx >= 0 && idx < V) ? idx : 0;
+    if (threadIdx.x == 0) tok[1 + r * ts] = (idx >= 0 && idx < V) ? idx : 0;
     if (li[0] == idx) {                                // the owner drops its head
 #pragma unroll
       for (int j = 0; j + 1 < TOPB_MAX; ++j) { lv[j] = lv[j + 1]; li[j] = li[j + 1]; }
@@ -1992,36 +2051,57 @@ __global__ __launch_bounds__(TOPB_THREADS) void k_topb(const float* __restrict__
   }
 }
 
-// Greedy acceptance of a width-B tree (rows: pending token, candidates
-// tok[1..B] of one position): a_0 = argmax of row 0; the candidate equal to
-// a_0 (the lowest such row) is accepted with its row's argmax as the bonus
-// (n = 1); otherwise n = 0 and the bonus is a_0.  trow = the accepted row.
-__global__ void k_accept_tree(HeadRes* res, int B, int32_t* tok) {
-  const int a0 = res->argmax[0];
-  int row = 0;
-  for (int i = 1; i <= B && !row; ++i)
-    if (tok[i] == a0) row = i;
-  const int b = row ? res->argmax[row] : a0;
-  res->n = row ? 1 : 0;
-  res->bonus = b;
-  res->trow = row;
-  res->emit[0] = a0;
-  res->emit[1] = b;
-  tok[0] = b;
+// A tree draft step of depth j: row b's argmax is node j + 1 of branch b,
+// window slot 1 + b D + j.
+__global__ void k_tree_draft_commit(const HeadRes* __restrict__ res, int B, int D, int j, int32_t* tok) {
+  const int b = threadIdx.x;
+  if (b < B) tok[1 + b * D + j] = res->argmax[b];
 }
 
-// After a tree round: the accepted candidate's keys and values (cache slot
-// p + trow, rotated at p + 1) become slot p + 1's, for every layer.  Nothing
-// to do when no candidate or the first one was accepted.
+// Greedy acceptance of a tree of width B and depth D (rows: pending token,
+// then branch b's nodes 1..D in window slots 1 + b D ..): a_0 = argmax of
+// row 0; the lowest branch whose first node is a_0 is followed while its
+// next node equals the argmax of the row of the last accepted one.  n =
+// accepted nodes, bonus = the argmax of the last accepted node's row (a_0
+// when no branch starts with a_0); trow = that row.
+__global__ void k_accept_tree(HeadRes* res, int B, int D, int32_t* tok) {
+  const int a0 = res->argmax[0];
+  int b = -1;
+  for (int i = 0; i < B && b < 0; ++i)
+    if (tok[1 + i * D] == a0) b = i;
+  int n = 0, row = 0;
+  if (b >= 0) {
+    n = 1;
+    row = 1 + b * D;
+    while (n < D && tok[1 + b * D + n] == res->argmax[row]) { ++n; ++row; }
+  }
+  const int bonus = res->argmax[row];
+  for (int i = 0; i < n; ++i) res->emit[i] = tok[1 + b * D + i];
+  res->emit[n] = bonus;
+  res->n = n;
+  res->bonus = bonus;
+  res->trow = row;
+  tok[0] = bonus;
+}
+
+// After a tree round: the accepted nodes' keys and values (branch b's
+// slots p + 1 + b D + i - 1, rotated at p + i) become positions p + i,
+// i = 1..n, in every layer (blockIdx = (layer, kv head)).  Branch 0's
+// nodes are in place already; a later branch's slots all lie beyond
+// p + D >= p + n, so sources and destinations never overlap.
 template <typename KT>
-__global__ void k_tree_kv_fix(const HeadRes* __restrict__ res, KT* kc, KT* vc, int Hkv, int max_seq, int hd,
+__global__ void k_tree_kv_fix(const HeadRes* __restrict__ res, int D, KT* kc, KT* vc, int Hkv, int max_seq, int hd,
                               int p) {
   const int row = res->trow;
-  if (row < 2) return;
+  if (row < 1) return;
+  const int b = (row - 1) / D, n = (row - 1) % D + 1;
+  if (b == 0) return;
   const size_t base = (size_t)blockIdx.x * Hkv * max_seq * hd + (size_t)blockIdx.y * max_seq * hd;
-  for (int d = threadIdx.x; d < hd; d += blockDim.x) {
-    kc[base + (size_t)(p + 1) * hd + d] = kc[base + (size_t)(p + row) * hd + d];
-    vc[base + (size_t)(p + 1) * hd + d] = vc[base + (size_t)(p + row) * hd + d];
+  for (int t = threadIdx.x; t < n * hd; t += blockDim.x) {
+    const int i = 1 + t / hd, d = t % hd;
+    const size_t dst = base + (size_t)(p + i) * hd + d, src = base + (size_t)(p + b * D + i) * hd + d;
+    kc[dst] = kc[src];
+    vc[dst] = vc[src];
   }
 }
 

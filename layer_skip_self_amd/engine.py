@@ -130,13 +130,15 @@ class Engine:
                                        out.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(done)), "lss_draft")
         return out[:done.value].tolist()
 
-    def draft_tree(self, skip_mask, quant=0, B=2):
-        """Width-B, depth-1 token tree: the draft's B most likely next tokens."""
+    def draft_tree(self, skip_mask, quant=0, B=2, D=1):
+        """Token tree of width B and depth D: the draft's B most likely next
+        tokens, each extended greedily by D - 1 more.  Returns the branches
+        ([B][D] token lists)."""
         m, mp = _u8(skip_mask)
-        out = np.zeros(B, np.int32)
-        self._check(self.lib.lss_draft_tree(self.h, mp, int(quant), int(B),
+        out = np.zeros(max(B * D, 1), np.int32)
+        self._check(self.lib.lss_draft_tree(self.h, mp, int(quant), int(B), int(D),
                                             out.ctypes.data_as(C.POINTER(C.c_int32))), "lss_draft_tree")
-        return out.tolist()
+        return [out[b * D:(b + 1) * D].tolist() for b in range(B)]
 
     def verify(self, drafts=None, k=None):
         if drafts is None:
@@ -275,6 +277,7 @@ def make_policy(policy, n_layers):
     for i in range(3):
         pol.beta[i] = float(beta[i])
     pol.tree_width = int(policy.get("tree_width", 0))
+    pol.tree_depth = int(policy.get("tree_depth", 1))
     return pol
 
 

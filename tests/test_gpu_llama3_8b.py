@@ -297,14 +297,19 @@ def test_quantized_draft_layers_vs_oracle_and_lossless_8b(gpu8b, oracle8b, quant
 
 
 def test_tree_drafting_lossless_8b(gpu8b):
-    """Width-4 token trees with the headline DP draft: speculative output
-    equal to greedy output bit for bit (each candidate row is the greedy step
-    after it, own key included)."""
+    """Token trees (width 4 depth 1, width 3 depth 4) with the headline DP
+    draft: speculative output equal to greedy output bit for bit (each node's
+    row is the greedy step after its branch's earlier nodes, own keys
+    included)."""
     eng, prompt = gpu8b["eng"], gpu8b["prompt"]
     G = 48
     ar, _ = eng.generate(prompt, G, {"mode": "ar"})
     toks, st = eng.generate(prompt, G, {"mode": "dp", "k_max": 1, "n_skip": 16, "interval": 32, "tree_width": 4})
     print(f"tree width 4: {st['rounds']} rounds, {st['accepted']} accepted")
+    assert toks == ar
+    toks, st = eng.generate(prompt, G, {"mode": "dp", "k_max": 1, "n_skip": 16, "interval": 32, "tree_width": 3,
+                                        "tree_depth": 4})
+    print(f"tree width 3 depth 4: {st['rounds']} rounds, {st['accepted']} accepted")
     assert toks == ar
 
 

@@ -101,6 +101,8 @@ POLICIES = {
     "quant_K6": {"mode": "static", "k_max": 6, "skip": (2,), "quant": 1},
     "dp_S1_I3": {"mode": "dp", "k_max": 5, "n_skip": 1, "interval": 3},
     "tree_B4": {"mode": "dp", "k_max": 1, "n_skip": 1, "interval": 4, "tree_width": 4},
+    "tree_B3_D4": {"mode": "dp", "k_max": 1, "n_skip": 1, "interval": 4, "tree_width": 3, "tree_depth": 4},
+    "tree_empty_mask_B2_D5": {"mode": "static", "k_max": 1, "skip": (), "tree_width": 2, "tree_depth": 5},
 }
 
 
@@ -112,6 +114,10 @@ def test_speculative_equals_greedy(small, kernel, name):
     assert toks == ar
     if name == "empty_mask_K8" and kernel != "mfma_verify":
         assert st["accepted"] == st["drafted"]     # the draft is the full model bit for bit
+    if name == "tree_empty_mask_B2_D5" and kernel != "mfma_verify":
+        # the full-model draft's first branch is the greedy continuation: every
+        # round accepts its whole depth (drafted counts both branches' nodes)
+        assert 2 * st["accepted"] == st["drafted"]
 
 
 def test_grid_policies_bitwise_equal(small, kernel):
