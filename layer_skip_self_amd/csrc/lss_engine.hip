@@ -415,10 +415,18 @@ void vgemm_go(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t
   const dim3 grid(nwg), block(64 * (VG_WAVES + 1));
   launch_k(k_vgemm<EPI, TN, VG_ST>, grid, block, 0, s, t0, t1, g);
 }
+// tiles of 32 weight rows (half the activation loads per weight byte of
+// 16-row tiles) once there are at least this many such tiles per hundred
+// compute units: at the 8B shape the q/k/v projection (192 tiles, 0.75 per
+// unit) runs 18 % faster at one row and 27 % at 9 rows with 32-row tiles,
+// the 4096-row projections (128 tiles) 22 % slower
+#ifndef VG_TN32_MIN_TILES_PCT
+#define VG_TN32_MIN_TILES_PCT 75
+#endif
 template <int EPI>
 void vgemm(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   if constexpr (EPI != EPI_SWIGLU) {
-    if (gl.ncu > 0 && g.N / 32 >= 4 * gl.ncu) {
+    if (gl.ncu > 0 && (long)(g.N / 32) * 100 >= (long)VG_TN32_MIN_TILES_PCT * gl.ncu) {
       vgemm_go<EPI, 32>(g, gl, s, t0, t1);
       return;
     }

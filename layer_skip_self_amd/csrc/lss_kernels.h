@@ -1269,17 +1269,22 @@ __global__ __launch_bounds__(64 * (VG_WAVES + 1)) void k_vgemm(GemmArgs ga) {
           }
         }
         // refill this ring slot, unconditionally: the unit ST ahead, in this
-        // tile or the next (after the last tile: this tile's rows again)
+        // tile or the next.  After the last tile the refill only keeps the
+        // count of loads in flight: every lane reads the same 16 bytes of
+        // this tile's last piece (one line per instruction; re-reading whole
+        // pieces would fetch them from memory again, as streamed lines leave
+        // L2 first)
         const int un = u + ST;
         const bool nxt = un >= NUP && has_next;
-        const int uu = un >= NUP ? un - NUP : un;
+        const bool dummy = un >= NUP && !has_next;
+        const int uu = un >= NUP ? (has_next ? un - NUP : max(np, 1) - 1) : un;
         {
           const uint16_t* lw[NACC][NB];
 #pragma unroll
           for (int q = 0; q < NACC; ++q)
 #pragma unroll
             for (int b = 0; b < NB; ++b) lw[q][b] = nxt ? nw[q][b] : cw[q][b];
-          vg_load<NACC, NB, TN>(ring[d], lw, min(p0 + uu, plast), K, la, lc, arow_ptr, g);
+          vg_load<NACC, NB, TN>(ring[d], lw, min(p0 + uu, plast), K, dummy ? 0 : la, dummy ? 0 : lc, arow_ptr, g);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
