@@ -66,7 +66,14 @@ typedef struct lss_config {
   int32_t max_seq;  /* KV capacity in positions (prompt + generated + window), <= 4096 */
   int32_t max_rows; /* row-block limit, 1..LSS_ROWS_MAX */
   int32_t kv_dtype; /* lss_dtype of the KV cache (float32 keeps keys/values unrounded) */
+  int32_t max_seqs; /* independent sequences the engine holds, 0 or 1 (one) .. LSS_SEQS_MAX; each has
+                       its own KV cache of max_seq positions (see lss_seq_select) */
 } lss_config;
+
+/* Largest number of sequences an engine holds, and of sequences one batched
+ * pass takes (more go to further passes). */
+#define LSS_SEQS_MAX 64
+#define LSS_BATCH_PASS_SEQS 16
 
 typedef struct lss_engine lss_engine;
 
@@ -205,6 +212,50 @@ int lss_select_layers_dp(lss_engine* e, int32_t n_skip, int32_t n_layers_eff, ui
 /* Committed sequence length p. */
 int32_t lss_seq_len(const lss_engine* e);
 
+/* ---- Several sequences (batch > 1).  Neither page batches requests; a
+ * batch here is a set of independent sequences, each decoded exactly as on
+ * its own (the same drafts, acceptances and tokens; CLaSp article, section
+ * 3, per sequence), whose rows share passes over the weights.
+ *
+ * lss_seq_select: sequence `seq` (0 .. max_seqs - 1) becomes the current
+ * one; every single-sequence call (prefill, draft, draft_tree, verify,
+ * accept_and_rollback, select_layers_dp, generate, seq_len) acts on it and
+ * on its own KV cache, window, layer-selection target and results.
+ * LSS_EINVAL for a bad index; LSS_ESTATE when sampling is on and the
+ * current sequence has an unverified window (its draft distributions share
+ * one buffer).  The logits and residual-state readers return the engine's
+ * last pass, whichever sequence(s) it served. */
+int lss_seq_select(lss_engine* e, int32_t seq);
+
+/* Batched draft of n distinct sequences seqs[n] (each prefilled, no verify
+ * pending, no tree window): sequence seqs[i] appends up to k[i] tokens to
+ * its window with its own skip mask masks[i * n_layers ..] (1 = skip),
+ * stopping early when its draft's top-1 probability falls below exit_tau
+ * (> 0), exactly as lss_draft would.  Sequences with identical masks share
+ * each draft step's pass (one row each, at their own positions).  quant: 0
+ * or 1 (int8 activations); the W8A8 draft (2) is single-row only
+ * (LSS_EINVAL).  tokens_out[i * LSS_WINDOW_MAX + j] receives sequence i's
+ * j-th new token, k_done[i] their count.  Greedy only (LSS_EINVAL with
+ * sampling on).  LSS_ECAPACITY as lss_draft, per sequence; nothing is
+ * drafted then. */
+int lss_batch_draft(lss_engine* e, int32_t n, const int32_t* seqs, const uint8_t* masks, int32_t quant,
+                    const int32_t* k, float exit_tau, int32_t* tokens_out, int32_t* k_done);
+
+/* Batched verify of the pending windows of n distinct sequences (a window
+ * may be empty: a greedy step).  Each sequence's rows [pending token,
+ * drafts] at its own positions see only its own cache, causally; every row
+ * equals the single-sequence verify row bit for bit.  Sequences are packed
+ * into passes of at most max_rows rows and LSS_BATCH_PASS_SEQS sequences.
+ * Acceptance runs on the device per sequence; lss_batch_accept reads it. */
+int lss_batch_verify(lss_engine* e, int32_t n, const int32_t* seqs);
+
+/* Accept and roll back each listed sequence after lss_batch_verify, as
+ * lss_accept_and_rollback: n_accepted[i], bonus[i], and
+ * accepted_out[i * (LSS_WINDOW_MAX + 1) ..] the n_accepted[i] + 1 emitted
+ * tokens (any output may be NULL). */
+int lss_batch_accept(lss_engine* e, int32_t n, const int32_t* seqs, int32_t* n_accepted, int32_t* bonus,
+                     int32_t* accepted_out);
+
 /* Parity helpers: logits [rows][vocab] of the last verify / draft step /
  * prefill row; residual states [n_layers + 1][d] of verify row `row` (valid
  * until the next draft, verify or prefill); the last DP's decisions
@@ -244,6 +295,17 @@ typedef struct lss_stats {
  * greedy autoregressive baseline (verify of the pending token alone). */
 int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t n_gen,
                  const lss_policy* policy, int32_t* out_tokens, lss_stats* stats);
+
+/* Decode n_seqs prompts together (sequences 0 .. n_seqs - 1; prompt i is
+ * prompt_lens[i] tokens at prompts + sum of the earlier lengths) until each
+ * has n_gen tokens in out_tokens[i * n_gen ..]: every sequence runs the
+ * policy's rounds as lss_generate would on its own (LSS_MODE_AR, STATIC, or
+ * DP with its own layer selection), the rounds of all sequences batched.
+ * stats[n_seqs] per sequence (may be NULL).  The cascade mode, trees,
+ * sampling and the W8A8 draft are single-sequence only (LSS_EINVAL). */
+int lss_generate_batch(lss_engine* e, int32_t n_seqs, const int32_t* prompts, const int32_t* prompt_lens,
+                       int32_t n_gen, const lss_policy* policy, int32_t* out_tokens,
+                       lss_stats* stats);
 
 /* DyTC router on the host (CAS-Spec blog sections 3.1-3.2, CAS-Spec
  * abstract).  plan: draft length per level (index 0 = fastest) maximizing

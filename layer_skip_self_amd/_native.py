@@ -11,6 +11,8 @@ LSS_MODE_AR, LSS_MODE_STATIC, LSS_MODE_DP, LSS_MODE_CASCADE = 0, 1, 2, 3
 LSS_WINDOW_MAX = 31
 LSS_TREE_NODES_MAX = 15
 LSS_ROWS_MAX = 64
+LSS_SEQS_MAX = 64
+LSS_BATCH_PASS_SEQS = 16
 LSS_LEVELS_MAX = 4
 LSS_ACCEPT_ROWS_MAX = 64
 LSS_ACCEPT_VOCAB_MAX = 262144
@@ -24,7 +26,7 @@ class lss_config(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_dim", C.c_int32),
                 ("vocab", C.c_int32), ("rope_theta", C.c_float), ("rms_eps", C.c_float),
                 ("dtype", C.c_int32), ("max_seq", C.c_int32), ("max_rows", C.c_int32),
-                ("kv_dtype", C.c_int32)]
+                ("kv_dtype", C.c_int32), ("max_seqs", C.c_int32)]
 
 
 class lss_tensor(C.Structure):
@@ -55,6 +57,14 @@ SIGNATURES = {
     "lss_destroy": (None, [C.c_void_p]),
     "lss_last_error": (C.c_char_p, [C.c_void_p]),
     "lss_prefill": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.POINTER(C.c_int32)]),
+    "lss_seq_select": (C.c_int, [C.c_void_p, C.c_int32]),
+    "lss_batch_draft": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_uint8), C.c_int32,
+                                  C.POINTER(C.c_int32), C.c_float, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
+    "lss_batch_verify": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32)]),
+    "lss_batch_accept": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                   C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
+    "lss_generate_batch": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.c_int32,
+                                     C.POINTER(lss_policy), C.POINTER(C.c_int32), C.POINTER(lss_stats)]),
     "lss_draft": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint8), C.c_int32, C.c_int32, C.c_float,
                             C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "lss_draft_tree": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint8), C.c_int32, C.c_int32, C.c_int32,

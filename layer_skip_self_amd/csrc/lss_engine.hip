@@ -45,7 +45,12 @@ int pg_splits(int N, int K, int wbytes) {
   return std::max(1, std::min(S, PG_MAX_SPLIT));
 }
 
+// token slots per sequence (pending token + window)
+constexpr int kTokSlots = 64;
+
 struct Layout {
+  size_t seq_kv;   // bytes of one sequence's K (or V) cache
+  int nseq;
   size_t kc, vc, hs, hmid, xa, xb, xc, pa, pc, xs, qkv, apart, aout, pgpart, rstd, act, logits, hpart, rope, target,
       dpg0, dpg1, dpx, dpdec, tok, seqtok, res, dlogits, srec, q8, total;
   int xld, nch_max, nz_max, ntile;
@@ -72,6 +77,7 @@ bool cfg_valid(const lss_config* c, std::string* why) {
   if (c->kv_dtype != LSS_F32 && c->kv_dtype != LSS_BF16) return fail("kv_dtype must be LSS_F32 or LSS_BF16");
   if (c->max_rows < 1 || c->max_rows > LSS_ROWS_MAX) return fail("max_rows out of [1, 64]");
   if (c->max_seq < 2 || c->max_seq > 4096) return fail("max_seq out of [2, 4096]");
+  if (c->max_seqs < 0 || c->max_seqs > LSS_SEQS_MAX) return fail("max_seqs out of [0, 64]");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail("bad rms_eps / rope_theta");
   return true;
 }
@@ -81,14 +87,18 @@ Layout make_layout(const lss_config* c) {
   const size_t elt = c->kv_dtype == LSS_BF16 ? 2 : 4;
   const size_t R = c->max_rows, d = c->d_model, F = c->ffn_dim, hd = c->head_dim;
   const size_t Hq = c->n_heads, Hkv = c->n_kv_heads, V = c->vocab, NL = c->n_layers;
+  const size_t S = (size_t)std::max(1, c->max_seqs);
+  L.nseq = (int)S;
   L.xld = (int)std::max({d, F, Hq * hd});
   L.nch_max = (c->max_seq + ATT_CH - 1) / ATT_CH;
-  L.nz_max = (int)(((Hq / Hkv) * R + ATT_QB - 1) / ATT_QB);
+  // query blocks of a pass: a batched pass rounds up per sequence
+  L.nz_max = (int)(((Hq / Hkv) * R + ATT_QB - 1) / ATT_QB) + (S > 1 ? (int)std::min<size_t>(S, ATT_SEQ_MAX) : 0);
   L.ntile = (int)((V + 15) / 16);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
-  L.kc = take(NL * Hkv * (size_t)c->max_seq * hd * elt);
-  L.vc = take(NL * Hkv * (size_t)c->max_seq * hd * elt);
+  L.seq_kv = NL * Hkv * (size_t)c->max_seq * hd * elt;
+  L.kc = take(S * L.seq_kv);
+  L.vc = take(S * L.seq_kv);
   L.hs = take((NL + 1) * R * d * 4);
   L.hmid = take(R * d * 4);
   // projection inputs (4 bytes per element in both formats) and partial sums of squares
@@ -113,14 +123,14 @@ Layout make_layout(const lss_config* c) {
   L.logits = take(R * V * 4);
   L.hpart = take(R * (size_t)L.ntile * HEAD_PART * 4);
   L.rope = take((size_t)c->max_seq * (hd / 2) * 8);
-  L.target = take((NL + 1) * d * 4);
+  L.target = take(S * (NL + 1) * d * 4);
   L.dpg0 = take(R * d * 4);
   L.dpg1 = take(R * d * 4);
   L.dpx = take(R * d * 4);
   L.dpdec = take((NL + 1) * (NL + 1) * 3 * 4);
-  L.tok = take(64 * 4);
+  L.tok = take(S * kTokSlots * 4);
   L.seqtok = take((size_t)c->max_seq * 4);
-  L.res = take(sizeof(HeadRes));
+  L.res = take((S + 1) * sizeof(HeadRes));        // one per sequence, then the batched passes' rows
   L.dlogits = take((size_t)std::min<size_t>(kWinMax, R) * V * 4);       // sampling: draft logits per window slot
   L.srec = take((size_t)((V + SPEC_RES_PER_WG - 1) / SPEC_RES_PER_WG) * 4 * 4);
   L.q8 = take(R * (size_t)L.xld);                  // int8-weight draft: activation codes
@@ -166,9 +176,28 @@ size_t w8_layout(const lss_config* c, std::vector<std::array<size_t, 14>>* offs)
 
 // MODE_TREE: a tree verify pass; MODE_TREE_DRAFT: a tree draft step (rows =
 // the nodes of one depth of consecutive branches)
-enum RowMode { MODE_CAUSAL = 0, MODE_DRAFT = 1, MODE_DP = 2, MODE_TREE = 3, MODE_TREE_DRAFT = 4 };
+// MODE_BATCH / MODE_BATCH_DRAFT: the rows of a batched pass (verify rows,
+// draft rows) of the sequences in lss_engine::pass
+enum RowMode { MODE_CAUSAL = 0, MODE_DRAFT = 1, MODE_DP = 2, MODE_TREE = 3, MODE_TREE_DRAFT = 4, MODE_BATCH = 5,
+               MODE_BATCH_DRAFT = 6 };
 
 }  // namespace
+
+// state of one sequence while it is not the current one (lss_seq_select);
+// the current sequence's state lives in the engine's own fields
+struct SeqState {
+  int p = 0, win = 0, tree = 0, tree_D = 1;
+  std::vector<uint32_t> valid;
+  bool have_seq = false, pending_accept = false;
+  int verify_rows = 0;
+  bool have_target = false;
+  int target_pos = 0;
+};
+
+// sequence i of a batched pass: its rows and position (lss_batch_*)
+struct PassSeq {
+  int seq, row0, M, pos0;
+};
 
 // decode-GEMV grid policy of an engine (lss_set_gemv_grid)
 #define LSS_GEMV_WGS_PER_CU 1
@@ -205,6 +234,16 @@ struct lss_engine {
   // pinned host mirrors
   HeadRes* hres = nullptr;
   int32_t* hstage = nullptr;
+  // sequences: the current one (its state in the fields below), the saved
+  // state of every sequence, and the per-sequence blocks of the workspace
+  int nseq = 1, cur = 0;
+  std::vector<SeqState> seqs;
+  char *kc_all = nullptr, *vc_all = nullptr;
+  int32_t* tok_all = nullptr;
+  float* target_all = nullptr;
+  HeadRes *res_all = nullptr, *hres_all = nullptr;   // device / pinned host, nseq + 1 (the last: batched rows)
+  std::vector<PassSeq> pass;                         // sequences of the running batched pass
+  bool pass_draft = false;
   // sequence state
   int p = 0;                  // committed length
   int win = 0;                // drafted tokens in the window
@@ -270,6 +309,31 @@ void* vc_layer(lss_engine* e, int l) {
 }
 float* hs_row(lss_engine* e, int l, int m) {
   return e->hs + ((size_t)l * e->cfg.max_rows + m) * e->cfg.d_model;
+}
+
+// the current sequence's fields to its saved state, and back
+void seq_save(lss_engine* e) {
+  SeqState& q = e->seqs[e->cur];
+  q.p = e->p; q.win = e->win; q.tree = e->tree; q.tree_D = e->tree_D;
+  q.valid = e->valid;
+  q.have_seq = e->have_seq; q.pending_accept = e->pending_accept;
+  q.verify_rows = e->verify_rows;
+  q.have_target = e->have_target; q.target_pos = e->target_pos;
+}
+void seq_load(lss_engine* e, int i) {
+  const SeqState& q = e->seqs[i];
+  e->cur = i;
+  e->p = q.p; e->win = q.win; e->tree = q.tree; e->tree_D = q.tree_D;
+  e->valid = q.valid;
+  e->have_seq = q.have_seq; e->pending_accept = q.pending_accept;
+  e->verify_rows = q.verify_rows;
+  e->have_target = q.have_target; e->target_pos = q.target_pos;
+  e->kc = e->kc_all + (size_t)i * e->lay.seq_kv;
+  e->vc = e->vc_all + (size_t)i * e->lay.seq_kv;
+  e->tok = e->tok_all + (size_t)i * kTokSlots;
+  e->target = e->target_all + (size_t)i * (e->cfg.n_layers + 1) * e->cfg.d_model;
+  e->res = e->res_all + i;
+  e->hres = e->hres_all + i;
 }
 
 // ------------------------------------------------------------------ launches
@@ -474,7 +538,9 @@ void prof_resolve(lss_engine* e) {
 template <int EPI>
 void gemm(lss_engine* e, const GemmArgs& ga) {
   // draft / verify rows, and any launch of at most 16 (MFMA decode GEMM) or
-  // 8 (vector GEMV) rows, take the decode kernel
+  // 8 (vector GEMV) rows, take the decode kernel; with the MFMA kernel more
+  // than 16 rows go in 16-row launches (never to another kernel, whose
+  // arithmetic would differ from the greedy rows')
   const bool mf = e->bf16 && (e->in_draft ? e->draft_mfma : e->decode_mfma);
   const bool vec = e->gemv || ga.M <= (mf ? VG_MMAX : 8);
   const bool one_launch = !vec || (mf && ga.M <= VG_MMAX) || ga.M <= gemv_cap(ga.K, e->bf16 ? 2 : 4);
@@ -487,8 +553,10 @@ void gemm(lss_engine* e, const GemmArgs& ga) {
   }
   hipEvent_t t0 = prof ? e->ev_start[e->ev_used] : nullptr, t1 = prof ? e->ev_stop[e->ev_used] : nullptr;
   if (vec) {
-    if (mf && ga.M <= VG_MMAX) vgemm<EPI>(ga, e->gvl, e->stream, t0, t1);
-    else if (e->bf16) gemv_mt<uint16_t, EPI>(ga, e->gvl, e->stream, t0, t1);
+    if (mf) {                                      // blocks of 16 rows, each row's arithmetic unchanged
+      for (int r0 = 0; r0 < ga.M; r0 += VG_MMAX)
+        vgemm<EPI>(ga.M <= VG_MMAX ? ga : rows_from(ga, r0, std::min(VG_MMAX, ga.M - r0)), e->gvl, e->stream, t0, t1);
+    } else if (e->bf16) gemv_mt<uint16_t, EPI>(ga, e->gvl, e->stream, t0, t1);
     else gemv_mt<float, EPI>(ga, e->gvl, e->stream, t0, t1);
   } else {
     if (e->bf16) pgemm<uint16_t, EPI>(e, ga, t0, t1);
@@ -562,8 +630,73 @@ void attention(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
   }
 }
 
+// attention of a batched pass: every sequence of e->pass with its own rows,
+// cache block, position and visibility (verify rows causal from its
+// committed length; a draft row sees its prefix and its window slots that
+// this layer wrote), in one launch pair
+template <typename KT, typename WT>
+void attention_batch(lss_engine* e, int l, int mode, int quant) {
+  const auto& c = e->cfg;
+  const int hd = c.head_dim;
+  const bool draft = mode == MODE_BATCH_DRAFT;
+  AttnArgs a{};
+  a.qkv = e->qkv; a.ldqkv = (c.n_heads + 2 * c.n_kv_heads) * hd;
+  a.cs = e->rope;
+  const size_t elt = e->kv16 ? 2 : 4;
+  a.kc = e->kc_all + (size_t)l * kv_layer_elems(e) * elt;
+  a.vc = e->vc_all + (size_t)l * kv_layer_elems(e) * elt;
+  a.seq_stride = (int64_t)e->lay.seq_kv;
+  a.max_seq = c.max_seq; a.Hq = c.n_heads; a.Hkv = c.n_kv_heads;
+  a.pos_step = 1;
+  a.lim_step = draft ? 0 : 1;
+  a.part = e->apart; a.nz_max = e->lay.nz_max; a.nch_max = e->lay.nch_max;
+  a.out = e->aout;
+  a.xo = quant ? nullptr : e->xb;
+  a.scale = (float)(1.0 / std::sqrt((double)hd));
+  const int G = c.n_heads / c.n_kv_heads;
+  AttnSeqs q{};
+  q.n = (int)e->pass.size();
+  int nch = 1, mmax = 1, rows = 0;
+  q.zs[0] = 0;
+  for (int i = 0; i < q.n; ++i) {
+    const PassSeq& ps = e->pass[i];
+    const SeqState& st = e->seqs[ps.seq];
+    q.row0[i] = ps.row0; q.M[i] = ps.M; q.pos0[i] = ps.pos0; q.slot[i] = ps.seq;
+    int kmax;
+    if (draft) {
+      q.lim_base[i] = st.p; q.wbase[i] = st.p; q.wmask[i] = st.valid[l];
+      kmax = ps.pos0 + 1;
+    } else {
+      q.lim_base[i] = ps.pos0 + 1; q.wbase[i] = 0; q.wmask[i] = 0;
+      kmax = ps.pos0 + ps.M;
+    }
+    q.nch[i] = std::max(1, (kmax + ATT_CH - 1) / ATT_CH);
+    q.zs[i + 1] = q.zs[i] + (G * ps.M + ATT_QB - 1) / ATT_QB;
+    nch = std::max(nch, q.nch[i]);
+    mmax = std::max(mmax, ps.M);
+    rows += ps.M;
+  }
+  a.M = rows;
+  a.nch = nch;
+  a.nz = q.zs[q.n];
+  const int mq = std::min(ATT_QB, G * mmax);
+  const dim3 grid(nch, c.n_kv_heads, a.nz);
+  if (hd == 128) {
+    hipLaunchKernelGGL((k_attention_b<KT, WT, 128>), grid, dim3(ATT_THREADS), 0, e->stream, a, q);
+    hipLaunchKernelGGL((k_attn_merge_b<WT, 128>), dim3(mq, c.n_kv_heads, a.nz), dim3(128), 0, e->stream, a, q);
+  } else {
+    hipLaunchKernelGGL((k_attention_b<KT, WT, 64>), grid, dim3(ATT_THREADS), 0, e->stream, a, q);
+    hipLaunchKernelGGL((k_attn_merge_b<WT, 64>), dim3(mq, c.n_kv_heads, a.nz), dim3(64), 0, e->stream, a, q);
+  }
+}
+
 template <typename WT>
 void attention_w(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
+  if (mode == MODE_BATCH || mode == MODE_BATCH_DRAFT) {
+    if (e->kv16) attention_batch<uint16_t, WT>(e, l, mode, quant);
+    else attention_batch<float, WT>(e, l, mode, quant);
+    return;
+  }
   if (e->kv16) attention<uint16_t, WT>(e, l, M, mode, pos0, quant);
   else attention<float, WT>(e, l, M, mode, pos0, quant);
 }
@@ -734,7 +867,7 @@ void layer_forward(lss_engine* e, int l, int M, const float* h_in, const void* x
 // token (the draft stream for a draft row, the full model's otherwise) into
 // res->sample[row0 + m] with its log-sum-exp; a draft row keeps its logits
 // in the window slot row0 of e->dlogits.
-void head(lss_engine* e, int r0, int M, int row0, int pos0, bool draft) {
+void head(lss_engine* e, int r0, int M, int row0, int pos0, bool draft, HeadRes* res = nullptr) {
   const auto& c = e->cfg;
   const bool samp = e->inv_t > 0.f;
   float* Y = (samp && draft) ? e->dlogits + (size_t)row0 * c.vocab : e->logits;
@@ -744,8 +877,8 @@ void head(lss_engine* e, int r0, int M, int row0, int pos0, bool draft) {
   ga.inv_t = e->inv_t; ga.seed = e->seed; ga.purpose = draft ? RNG_DRAFT : RNG_TARGET;
   ga.pos0 = pos0; ga.pos_step = 1;
   gemm<EPI_LOGITS>(e, ga);
-  hipLaunchKernelGGL(k_head_reduce, dim3(M), dim3(HEAD_RED_THREADS), 0, e->stream, e->hpart, e->lay.ntile, e->res,
-                     row0, samp ? 1 : 0, draft ? 1 : 0);
+  hipLaunchKernelGGL(k_head_reduce, dim3(M), dim3(HEAD_RED_THREADS), 0, e->stream, e->hpart, e->lay.ntile,
+                     res ? res : e->res, row0, samp ? 1 : 0, draft ? 1 : 0);
   if (!(samp && draft)) e->logits_rows = M;
 }
 
@@ -759,6 +892,17 @@ void embed(lss_engine* e, const int32_t* tok_dev, int M, float* h, const float* 
   else
     hipLaunchKernelGGL(k_embed<float>, dim3(M), dim3(PREP_THREADS), 0, e->stream, (const float*)e->embed, tok_dev,
                        ts, c.d_model, h, g, e->xa, e->pa);
+}
+
+// embedding rows of a batched pass: row m's token is e->tok_all[off[m]]
+void embed_rows(lss_engine* e, const RowTok& rt, int M, float* h, const float* g) {
+  const auto& c = e->cfg;
+  if (e->bf16)
+    hipLaunchKernelGGL(k_embed_rows<uint16_t>, dim3(M), dim3(PREP_THREADS), 0, e->stream, (const uint16_t*)e->embed,
+                       e->tok_all, rt, c.d_model, h, g, e->xa, e->pa);
+  else
+    hipLaunchKernelGGL(k_embed_rows<float>, dim3(M), dim3(PREP_THREADS), 0, e->stream, (const float*)e->embed,
+                       e->tok_all, rt, c.d_model, h, g, e->xa, e->pa);
 }
 
 // gain of the RMSNorm that consumes the residual after layer l (l = -1: the
@@ -864,7 +1008,8 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
   }
   char* ws = (char*)workspace;
   e->ws = ws;
-  e->kc = ws + lay.kc; e->vc = ws + lay.vc;
+  e->kc_all = ws + lay.kc; e->vc_all = ws + lay.vc;
+  e->kc = e->kc_all; e->vc = e->vc_all;
   e->hs = (float*)(ws + lay.hs); e->hmid = (float*)(ws + lay.hmid);
   e->xa = ws + lay.xa; e->xb = ws + lay.xb; e->xc = ws + lay.xc;
   e->pa = (float*)(ws + lay.pa); e->pc = (float*)(ws + lay.pc);
@@ -872,13 +1017,17 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
   e->pgpart = (float*)(ws + lay.pgpart); e->rstd = (float*)(ws + lay.rstd);
   e->apart = (float*)(ws + lay.apart); e->aout = (float*)(ws + lay.aout);
   e->act = (float*)(ws + lay.act); e->logits = (float*)(ws + lay.logits); e->hpart = (float*)(ws + lay.hpart);
-  e->rope = (float2*)(ws + lay.rope); e->target = (float*)(ws + lay.target);
+  e->rope = (float2*)(ws + lay.rope); e->target_all = (float*)(ws + lay.target); e->target = e->target_all;
   e->dpg[0] = (float*)(ws + lay.dpg0); e->dpg[1] = (float*)(ws + lay.dpg1); e->dpx = (float*)(ws + lay.dpx);
-  e->dpdec = (float*)(ws + lay.dpdec); e->tok = (int32_t*)(ws + lay.tok); e->seqtok = (int32_t*)(ws + lay.seqtok);
-  e->res = (HeadRes*)(ws + lay.res);
+  e->dpdec = (float*)(ws + lay.dpdec); e->tok_all = (int32_t*)(ws + lay.tok); e->tok = e->tok_all;
+  e->seqtok = (int32_t*)(ws + lay.seqtok);
+  e->res_all = (HeadRes*)(ws + lay.res); e->res = e->res_all;
   e->dlogits = (float*)(ws + lay.dlogits); e->srec = (float*)(ws + lay.srec);
   e->q8 = (int8_t*)(ws + lay.q8);
   e->valid.assign(cfg->n_layers, 0u);
+  e->nseq = lay.nseq;
+  e->seqs.resize(e->nseq);
+  for (auto& q : e->seqs) q.valid.assign(cfg->n_layers, 0u);
   {  // every workspace pointer must be set (a null one would be written by a kernel)
     const void* ptrs[] = {e->kc, e->vc, e->hs, e->hmid, e->xa, e->xb, e->xc, e->pa, e->pc, e->xs, e->qkv,
                           e->pgpart, e->rstd, e->apart, e->aout, e->act, e->logits, e->hpart, e->rope,
@@ -891,7 +1040,8 @@ int lss_create(const lss_config* cfg, const void* const* tensors, int32_t n_tens
       }
   }
 
-  hipError_t s = hipHostMalloc((void**)&e->hres, sizeof(HeadRes), hipHostMallocDefault);
+  hipError_t s = hipHostMalloc((void**)&e->hres_all, sizeof(HeadRes) * (e->nseq + 1), hipHostMallocDefault);
+  e->hres = e->hres_all;
   if (s == hipSuccess)
     s = hipHostMalloc((void**)&e->hstage, ((size_t)cfg->max_seq + 64) * sizeof(int32_t), hipHostMallocDefault);
   if (s != hipSuccess) {
@@ -963,7 +1113,7 @@ void lss_destroy(lss_engine* e) {
   (void)hipStreamSynchronize(e->stream);
   for (auto ev : e->ev_start) (void)hipEventDestroy(ev);
   for (auto ev : e->ev_stop) (void)hipEventDestroy(ev);
-  if (e->hres) (void)hipHostFree(e->hres);
+  if (e->hres_all) (void)hipHostFree(e->hres_all);
   if (e->hstage) (void)hipHostFree(e->hstage);
   delete e;
 }
@@ -1056,7 +1206,10 @@ int lss_set_sampling(lss_engine* e, float temperature, uint64_t seed) {
   if (!e) return LSS_EINVAL;
   if (!(temperature >= 0.f) || !std::isfinite(temperature))
     return fail(e, LSS_EINVAL, "set_sampling: temperature must be finite and >= 0");
-  if (e->win > 0 || e->pending_accept) return fail(e, LSS_ESTATE, "set_sampling: a draft window or verify is pending");
+  seq_save(e);
+  for (const SeqState& q : e->seqs)
+    if (q.win > 0 || q.pending_accept)
+      return fail(e, LSS_ESTATE, "set_sampling: a draft window or verify is pending (on some sequence)");
   const float inv = temperature > 0.f ? 1.0f / temperature : 0.f;
   if (temperature > 0.f && !std::isfinite(inv)) return fail(e, LSS_EINVAL, "set_sampling: temperature too small");
   e->inv_t = inv;
@@ -1495,6 +1648,248 @@ int lss_op_accept_greedy_noalloc(const float* logits, int32_t rows, int32_t voca
   return accept_launch(logits, rows, vocab, drafts, result, (AccRec*)p, (hipStream_t)stream);
 }
 
+// ---------------------------------------------------------------- several sequences
+int lss_seq_select(lss_engine* e, int32_t seq) {
+  if (!e) return LSS_EINVAL;
+  if (seq < 0 || seq >= e->nseq) return fail(e, LSS_EINVAL, "seq_select: index out of [0, max_seqs)");
+  if (seq == e->cur) return LSS_OK;
+  if (e->inv_t > 0.f && e->win > 0 && !e->pending_accept)
+    return fail(e, LSS_ESTATE, "seq_select: sampling keeps one draft-distribution buffer; verify this window first");
+  seq_save(e);
+  seq_load(e, seq);
+  return LSS_OK;
+}
+
+namespace {
+
+// distinct sequence indices in range
+bool seqs_valid(const lss_engine* e, int n, const int32_t* seqs) {
+  if (n < 1 || n > e->nseq || !seqs) return false;
+  std::vector<char> seen(e->nseq, 0);
+  for (int i = 0; i < n; ++i) {
+    if (seqs[i] < 0 || seqs[i] >= e->nseq || seen[seqs[i]]) return false;
+    seen[seqs[i]] = 1;
+  }
+  return true;
+}
+
+// one batched draft step: one row per listed sequence (window slot win, at
+// position p + win) through the layers mask keeps; the argmax becomes the
+// slot's drafted token
+void batch_draft_step(lss_engine* e, const std::vector<int>& sq, const uint8_t* mask, int quant) {
+  const auto& c = e->cfg;
+  const int M = (int)sq.size();
+  RowTok rt{};
+  BatchRows br{};
+  br.n = M;
+  e->pass.clear();
+  for (int m = 0; m < M; ++m) {
+    const SeqState& st = e->seqs[sq[m]];
+    rt.off[m] = sq[m] * kTokSlots + st.win;
+    br.seq[m] = sq[m];
+    br.slot[m] = st.win;
+    e->pass.push_back(PassSeq{sq[m], m, 1, st.p + st.win});
+  }
+  embed_rows(e, rt, M, hs_row(e, 0, 0), next_gain(e, mask, -1));
+  const float* h = hs_row(e, 0, 0);
+  for (int l = 0; l < c.n_layers; ++l) {
+    if (mask[l]) continue;
+    for (int m = 0; m < M; ++m) e->seqs[sq[m]].valid[l] |= 1u << e->seqs[sq[m]].win;
+    layer_forward(e, l, M, h, e->xa, e->pa, hs_row(e, l + 1, 0), next_gain(e, mask, l), MODE_BATCH_DRAFT, 0, quant);
+    h = hs_row(e, l + 1, 0);
+  }
+  HeadRes* bres = e->res_all + e->nseq;
+  head(e, 0, M, 0, 0, true, bres);
+  hipLaunchKernelGGL(k_draft_commit_b, dim3(1), dim3(BATCH_ROWS_MAX), 0, e->stream, (const HeadRes*)bres, br,
+                     e->res_all, e->tok_all, kTokSlots);
+  for (int m = 0; m < M; ++m) e->seqs[sq[m]].win++;
+}
+
+// one batched verify pass over the listed sequences' windows
+void batch_verify_pass(lss_engine* e, const std::vector<int>& sq) {
+  const auto& c = e->cfg;
+  RowTok rt{};
+  BatchSeqs bs{};
+  bs.n = (int)sq.size();
+  e->pass.clear();
+  int M = 0;
+  for (int i = 0; i < bs.n; ++i) {
+    const SeqState& st = e->seqs[sq[i]];
+    bs.seq[i] = sq[i];
+    bs.row0[i] = M;
+    bs.k[i] = st.win;
+    e->pass.push_back(PassSeq{sq[i], M, st.win + 1, st.p});
+    for (int j = 0; j <= st.win; ++j) rt.off[M + j] = sq[i] * kTokSlots + j;
+    M += st.win + 1;
+  }
+  embed_rows(e, rt, M, hs_row(e, 0, 0), next_gain(e, nullptr, -1));
+  for (int l = 0; l < c.n_layers; ++l)
+    layer_forward(e, l, M, hs_row(e, l, 0), e->xa, e->pa, hs_row(e, l + 1, 0), next_gain(e, nullptr, l), MODE_BATCH,
+                  0, 0);
+  HeadRes* bres = e->res_all + e->nseq;
+  head(e, 0, M, 0, 0, false, bres);
+  hipLaunchKernelGGL(k_accept_b, dim3(1), dim3(ATT_SEQ_MAX), 0, e->stream, (const HeadRes*)bres, bs, e->res_all,
+                     e->tok_all, kTokSlots);
+  hipLaunchKernelGGL(k_gather_target_b, dim3(c.n_layers + 1, bs.n), dim3(256), 0, e->stream, e->hs, c.max_rows,
+                     c.d_model, (const HeadRes*)e->res_all, bs, e->target_all,
+                     (size_t)(c.n_layers + 1) * c.d_model);
+}
+
+int sync_res_all(lss_engine* e) {
+  HIPCHK(hipMemcpyAsync(e->hres_all, e->res_all, sizeof(HeadRes) * (e->nseq + 1), hipMemcpyDeviceToHost, e->stream));
+  HIPCHK(hipStreamSynchronize(e->stream));
+  if (e->ev_used) prof_resolve(e);
+  return LSS_OK;
+}
+
+}  // namespace
+
+int lss_batch_draft(lss_engine* e, int32_t n, const int32_t* seqs, const uint8_t* masks, int32_t quant,
+                    const int32_t* k, float exit_tau, int32_t* tokens_out, int32_t* k_done) {
+  if (!e) return LSS_EINVAL;
+  const auto& c = e->cfg;
+  const int L = c.n_layers;
+  if (!seqs_valid(e, n, seqs)) return fail(e, LSS_EINVAL, "batch_draft: sequences must be distinct and in range");
+  if (!masks || !k || quant < 0 || quant > 1)
+    return fail(e, LSS_EINVAL, "batch_draft: bad arguments (quant 0 or 1; the W8A8 draft is single-row)");
+  if (e->inv_t > 0.f) return fail(e, LSS_EINVAL, "batch_draft: batches are greedy; sampling is on");
+  seq_save(e);
+  const int win_cap = std::min(kWinMax, c.max_rows - 1);
+  int any = 0;
+  for (int i = 0; i < n; ++i) {
+    const SeqState& st = e->seqs[seqs[i]];
+    if (!st.have_seq || st.pending_accept || st.tree > 0)
+      return fail(e, LSS_ESTATE, "batch_draft: every sequence needs a prefill, no pending accept, no tree window");
+    if (k[i] < 0) return fail(e, LSS_EINVAL, "batch_draft: negative k");
+    if (st.win + k[i] > win_cap) return fail(e, LSS_ECAPACITY, "batch_draft: window would exceed its capacity");
+    if (st.p + st.win + k[i] + 1 > c.max_seq) return fail(e, LSS_ECAPACITY, "batch_draft: KV capacity exceeded");
+    any += k[i];
+  }
+  if (any > 0 && !tokens_out) return fail(e, LSS_EINVAL, "batch_draft: null tokens_out");
+  const GemvScope gv(e, true);
+  std::vector<int> start(n), done(n, 0);
+  std::vector<char> live(n);
+  for (int i = 0; i < n; ++i) {
+    start[i] = e->seqs[seqs[i]].win;
+    live[i] = k[i] > 0;
+  }
+  // groups of identical masks, in order of first appearance
+  std::vector<int> grp(n, -1);
+  int ng = 0;
+  for (int i = 0; i < n; ++i) {
+    for (int j = 0; j < i && grp[i] < 0; ++j)
+      if (!std::memcmp(masks + (size_t)i * L, masks + (size_t)j * L, L)) grp[i] = grp[j];
+    if (grp[i] < 0) grp[i] = ng++;
+  }
+  const int per_pass = std::min(c.max_rows, ATT_SEQ_MAX);
+  for (int g = 0; g < ng; ++g) {
+    int gi = 0;
+    while (grp[gi] != g) ++gi;
+    const uint8_t* mask = masks + (size_t)gi * L;
+    for (;;) {
+      std::vector<int> rows;                            // indices into seqs[] still drafting
+      for (int i = 0; i < n; ++i)
+        if (grp[i] == g && live[i] && done[i] < k[i]) rows.push_back(i);
+      if (rows.empty()) break;
+      for (size_t r0 = 0; r0 < rows.size(); r0 += per_pass) {
+        std::vector<int> sq;
+        for (size_t r = r0; r < std::min(rows.size(), r0 + per_pass); ++r) sq.push_back(seqs[rows[r]]);
+        batch_draft_step(e, sq, mask, quant);
+        if (exit_tau > 0.f) {
+          int rc = check_launch(e, "batch_draft");
+          if (rc) { seq_load(e, e->cur); return rc; }
+          rc = sync_res_all(e);
+          if (rc) { seq_load(e, e->cur); return rc; }
+          const HeadRes& b = e->hres_all[e->nseq];
+          for (size_t m = 0; m < sq.size(); ++m)
+            if (b.pmax[m] < exit_tau) live[rows[r0 + m]] = 0;
+        }
+      }
+      for (int i : rows) done[i]++;
+    }
+  }
+  int rc = check_launch(e, "batch_draft");
+  if (rc == LSS_OK && any > 0) rc = sync_res_all(e);
+  if (rc == LSS_OK && any > 0)
+    for (int i = 0; i < n; ++i)
+      for (int j = 0; j < done[i]; ++j)
+        tokens_out[(size_t)i * LSS_WINDOW_MAX + j] = e->hres_all[seqs[i]].argmax[start[i] + j];
+  if (k_done)
+    for (int i = 0; i < n; ++i) k_done[i] = done[i];
+  seq_load(e, e->cur);
+  return rc;
+}
+
+int lss_batch_verify(lss_engine* e, int32_t n, const int32_t* seqs) {
+  if (!e) return LSS_EINVAL;
+  const auto& c = e->cfg;
+  if (!seqs_valid(e, n, seqs)) return fail(e, LSS_EINVAL, "batch_verify: sequences must be distinct and in range");
+  if (e->inv_t > 0.f) return fail(e, LSS_EINVAL, "batch_verify: batches are greedy; sampling is on");
+  seq_save(e);
+  for (int i = 0; i < n; ++i) {
+    const SeqState& st = e->seqs[seqs[i]];
+    if (!st.have_seq || st.pending_accept || st.tree > 0)
+      return fail(e, LSS_ESTATE, "batch_verify: every sequence needs a prefill, no pending accept, no tree window");
+    if (st.p + st.win + 1 > c.max_seq) return fail(e, LSS_ECAPACITY, "batch_verify: KV capacity exceeded");
+  }
+  const GemvScope gv(e);
+  // passes: sequences in order while their rows fit max_rows and the pass
+  // holds at most LSS_BATCH_PASS_SEQS sequences
+  std::vector<int> sq;
+  int rows = 0;
+  for (int i = 0; i <= n; ++i) {
+    const int r = i < n ? e->seqs[seqs[i]].win + 1 : 0;
+    if (i == n || rows + r > c.max_rows || (int)sq.size() == LSS_BATCH_PASS_SEQS) {
+      batch_verify_pass(e, sq);
+      sq.clear();
+      rows = 0;
+    }
+    if (i < n) {
+      sq.push_back(seqs[i]);
+      rows += r;
+    }
+  }
+  const int rc = check_launch(e, "batch_verify");
+  if (rc == LSS_OK)
+    for (int i = 0; i < n; ++i) {
+      SeqState& st = e->seqs[seqs[i]];
+      st.verify_rows = st.win + 1;
+      st.pending_accept = true;
+    }
+  seq_load(e, e->cur);
+  return rc;
+}
+
+int lss_batch_accept(lss_engine* e, int32_t n, const int32_t* seqs, int32_t* n_accepted, int32_t* bonus,
+                     int32_t* accepted_out) {
+  if (!e) return LSS_EINVAL;
+  if (!seqs_valid(e, n, seqs)) return fail(e, LSS_EINVAL, "batch_accept: sequences must be distinct and in range");
+  seq_save(e);
+  for (int i = 0; i < n; ++i)
+    if (!e->seqs[seqs[i]].pending_accept) return fail(e, LSS_ESTATE, "batch_accept: a sequence has no verify pending");
+  int rc = sync_res_all(e);
+  if (rc) return rc;
+  for (int i = 0; i < n; ++i) {
+    SeqState& st = e->seqs[seqs[i]];
+    const HeadRes& h = e->hres_all[seqs[i]];
+    const int na = h.n;
+    if (n_accepted) n_accepted[i] = na;
+    if (bonus) bonus[i] = h.bonus;
+    if (accepted_out)
+      for (int j = 0; j <= na; ++j) accepted_out[(size_t)i * (LSS_WINDOW_MAX + 1) + j] = h.emit[j];
+    st.target_pos = st.p + na;
+    st.have_target = true;
+    st.p += na + 1;
+    st.win = 0;
+    st.tree = 0;
+    st.tree_D = 1;
+    std::fill(st.valid.begin(), st.valid.end(), 0u);
+    st.pending_accept = false;
+  }
+  seq_load(e, e->cur);
+  return LSS_OK;
+}
+
 // ---------------------------------------------------------------- generation loop
 int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t n_gen, const lss_policy* pol,
                  int32_t* out, lss_stats* stats) {
@@ -1611,6 +2006,98 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
   st.emitted = emitted;
   if (stats) *stats = st;
   return LSS_OK;
+}
+
+int lss_generate_batch(lss_engine* e, int32_t n, const int32_t* prompts, const int32_t* lens, int32_t n_gen,
+                       const lss_policy* pol, int32_t* out, lss_stats* stats) {
+  if (!e) return LSS_EINVAL;
+  const auto& c = e->cfg;
+  const int L = c.n_layers;
+  if (!pol || !out || !prompts || !lens || n_gen < 1 || n < 1 || n > e->nseq)
+    return fail(e, LSS_EINVAL, "generate_batch: bad arguments (1 <= n_seqs <= max_seqs)");
+  if (pol->mode != LSS_MODE_AR && pol->mode != LSS_MODE_STATIC && pol->mode != LSS_MODE_DP)
+    return fail(e, LSS_EINVAL, "generate_batch: modes AR, STATIC and DP only");
+  if (pol->tree_width > 0 || pol->quant < 0 || pol->quant > 1 || e->inv_t > 0.f)
+    return fail(e, LSS_EINVAL, "generate_batch: no trees, no W8A8 draft, greedy only");
+  if (pol->mode != LSS_MODE_AR && (pol->k_max < 0 || pol->k_max > std::min(kWinMax, c.max_rows - 1)))
+    return fail(e, LSS_EINVAL, "generate_batch: k_max out of range");
+  if (pol->mode == LSS_MODE_STATIC && !pol->static_mask) return fail(e, LSS_EINVAL, "generate_batch: static mask missing");
+  if (pol->mode == LSS_MODE_DP && pol->interval < 1) return fail(e, LSS_EINVAL, "generate_batch: interval < 1");
+  for (int i = 0; i < n; ++i)
+    if (lens[i] < 1 || (long)lens[i] + n_gen + std::min(kWinMax, c.max_rows - 1) + 1 > c.max_seq)
+      return fail(e, LSS_ECAPACITY, "generate_batch: a prompt is empty or prompt + generation + window exceeds max_seq");
+  const int cur0 = e->cur;
+  std::vector<int32_t> seqs(n);
+  std::vector<uint8_t> masks((size_t)n * L, 0);
+  std::vector<int> emitted(n, 0);
+  std::vector<lss_stats> st(n);
+  int rc = LSS_OK;
+  auto fin = [&](int r) {
+    if (e->cur != cur0) {
+      seq_save(e);
+      seq_load(e, cur0);
+    }
+    return r;
+  };
+  auto dp = [&](int i) -> int {
+    int r = lss_seq_select(e, i);
+    if (r) return r;
+    r = lss_select_layers_dp(e, pol->n_skip, L, masks.data() + (size_t)i * L, nullptr);
+    if (r == LSS_OK) st[i].dp_runs++;
+    return r;
+  };
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    seqs[i] = i;
+    rc = lss_seq_select(e, i);
+    int32_t t0 = 0;
+    if (rc == LSS_OK) rc = lss_prefill(e, prompts + off, lens[i], &t0);
+    if (rc) return fin(rc);
+    off += lens[i];
+    out[(size_t)i * n_gen] = t0;
+    emitted[i] = 1;
+    if (pol->mode == LSS_MODE_STATIC) std::copy(pol->static_mask, pol->static_mask + L, masks.begin() + (size_t)i * L);
+    if (pol->mode == LSS_MODE_DP && (rc = dp(i))) return fin(rc);
+  }
+  std::vector<int32_t> act, dk, done(n), toks((size_t)n * LSS_WINDOW_MAX), na(n), acc((size_t)n * (LSS_WINDOW_MAX + 1));
+  std::vector<uint8_t> dmask;
+  for (;;) {
+    act.clear();
+    for (int i = 0; i < n; ++i)
+      if (emitted[i] < n_gen) act.push_back(i);
+    if (act.empty()) break;
+    const int na_ = (int)act.size();
+    std::fill(done.begin(), done.end(), 0);
+    if (pol->mode != LSS_MODE_AR) {
+      dk.assign(na_, 0);
+      dmask.assign((size_t)na_ * L, 0);
+      for (int a = 0; a < na_; ++a) {
+        dk[a] = std::min(pol->k_max, n_gen - emitted[act[a]] - 1);
+        std::copy(masks.begin() + (size_t)act[a] * L, masks.begin() + (size_t)(act[a] + 1) * L,
+                  dmask.begin() + (size_t)a * L);
+      }
+      rc = lss_batch_draft(e, na_, act.data(), dmask.data(), pol->quant, dk.data(), pol->exit_tau, toks.data(),
+                           done.data());
+      if (rc) return fin(rc);
+    }
+    rc = lss_batch_verify(e, na_, act.data());
+    if (rc == LSS_OK) rc = lss_batch_accept(e, na_, act.data(), na.data(), nullptr, acc.data());
+    if (rc) return fin(rc);
+    for (int a = 0; a < na_; ++a) {
+      const int i = act[a];
+      for (int j = 0; j <= na[a] && emitted[i] < n_gen; ++j)
+        out[(size_t)i * n_gen + emitted[i]++] = acc[(size_t)a * (LSS_WINDOW_MAX + 1) + j];
+      st[i].rounds++;
+      st[i].drafted += done[a];
+      st[i].accepted += na[a];
+      if (pol->mode == LSS_MODE_DP && st[i].rounds % pol->interval == 0 && (rc = dp(i))) return fin(rc);
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    st[i].emitted = emitted[i];
+    if (stats) stats[i] = st[i];
+  }
+  return fin(LSS_OK);
 }
 
 int lss_profile_kernel(lss_engine* e, int32_t epi, int32_t rows, int32_t enable) {

@@ -262,13 +262,10 @@ __global__ __launch_bounds__(PREP_THREADS) void k_prep_rows(const float* __restr
 
 // h[m][:] = E[tok[m]][:] (float32 residual stream) and its projection input.
 template <typename WT>
-__global__ __launch_bounds__(PREP_THREADS) void k_embed(const WT* __restrict__ E, const int32_t* __restrict__ tok,
-                                                        int ts, int d, float* __restrict__ h,
-                                                        const float* __restrict__ g, void* xo,
-                                                        float* __restrict__ po) {
-  const int m = blockIdx.x;
+__device__ __forceinline__ void embed_body(const WT* __restrict__ E, int id, int d, float* __restrict__ h,
+                                           const float* __restrict__ g, void* xo, float* __restrict__ po, int m) {
   float v[PREP_PER_THREAD];
-  load_vals<WT>(v, E + (size_t)tok[(size_t)m * ts] * d, d);
+  load_vals<WT>(v, E + (size_t)id * d, d);
   float* hr = h + (size_t)m * d;
 #pragma unroll
   for (int j = 0; j < PREP_PER_THREAD; ++j) {
@@ -276,6 +273,27 @@ __global__ __launch_bounds__(PREP_THREADS) void k_embed(const WT* __restrict__ E
     if (i < d) hr[i] = v[j];
   }
   prep_vals<WT>(v, d, g, xo, po, m);
+}
+template <typename WT>
+__global__ __launch_bounds__(PREP_THREADS) void k_embed(const WT* __restrict__ E, const int32_t* __restrict__ tok,
+                                                        int ts, int d, float* __restrict__ h,
+                                                        const float* __restrict__ g, void* xo,
+                                                        float* __restrict__ po) {
+  const int m = blockIdx.x;
+  embed_body<WT>(E, tok[(size_t)m * ts], d, h, g, xo, po, m);
+}
+// rows of a batch: row m's token is tok[off[m]]
+#define BATCH_ROWS_MAX 64
+struct RowTok {
+  int32_t off[BATCH_ROWS_MAX];
+};
+template <typename WT>
+__global__ __launch_bounds__(PREP_THREADS) void k_embed_rows(const WT* __restrict__ E, const int32_t* __restrict__ tok,
+                                                             RowTok rt, int d, float* __restrict__ h,
+                                                             const float* __restrict__ g, void* xo,
+                                                             float* __restrict__ po) {
+  const int m = blockIdx.x;
+  embed_body<WT>(E, tok[rt.off[m]], d, h, g, xo, po, m);
 }
 
 // Symmetric per-token int8 codes: inv = fl32(127 / amax) (correctly rounded),
@@ -1531,6 +1549,21 @@ struct AttnArgs {
   float* out;                      // [M][Hq * hd] float32 output (when xo == nullptr)
   void* xo;                        // [M][Hq * hd] projection-format output
   float scale;                     // 1/sqrt(hd)
+  int64_t seq_stride;              // batched launches: bytes between two sequences' caches
+};
+
+// Batched launches (several independent sequences, each with its own cache
+// block, rows, position and visibility): the launch's query blocks are the
+// sequences' blocks one after the other; sequence i owns blocks
+// [zs[i], zs[i + 1]) and rows [row0[i], row0[i] + M[i]) of the projection
+// output, and its cache block is slot[i] (seq_stride bytes apart).
+#define ATT_SEQ_MAX 16
+struct AttnSeqs {
+  int n;
+  int zs[ATT_SEQ_MAX + 1];
+  int row0[ATT_SEQ_MAX], M[ATT_SEQ_MAX], pos0[ATT_SEQ_MAX], lim_base[ATT_SEQ_MAX], wbase[ATT_SEQ_MAX];
+  int nch[ATT_SEQ_MAX], slot[ATT_SEQ_MAX];
+  uint32_t wmask[ATT_SEQ_MAX];
 };
 
 template <typename KT> __device__ __forceinline__ float kv_round(float v);
@@ -1678,15 +1711,16 @@ struct AttNew {
 
 // tree nodes (B D) a launch may hold
 #define ATT_TREE_NODES 16
-template <typename KT, typename WT, int HD, bool TREE = false>
-__global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
+template <typename KT, typename WT, int HD, bool TREE>
+__device__ __forceinline__ void attention_body(const AttnArgs& a, int z, int zp) {
   __shared__ __align__(16) float kv_s[ATT_CH][ATT_LD];
   __shared__ __align__(16) float q_s[ATT_QB][HD];
   __shared__ float p_s[ATT_QB][ATT_CH];
   __shared__ float st_s[ATT_QB][2];
   __shared__ float own_s[TREE ? ATT_TREE_NODES : 1][TREE ? HD : 1];   // tree: node b D + j - 1's key
   __shared__ float own_v[TREE ? ATT_TREE_NODES : 1][TREE ? HD : 1];   // and value
-  const int c = blockIdx.x, kh = blockIdx.y, z = blockIdx.z;
+  // z: query block of the sequence, zp: its partials' slot in the launch
+  const int c = blockIdx.x, kh = blockIdx.y;
   const int G = a.Hq / a.Hkv;
   const int nq = G * a.M;
   const int q0 = z * ATT_QB;
@@ -1803,7 +1837,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
   __syncthreads();
   // value sums: outputs i and i + 256 of the (query, dim) grid per thread,
   // two independent chains over the 64 keys
-  float* part = a.part + (((size_t)kh * a.nz_max + z) * a.nch_max + c) * ATT_QB * (HD + 2);
+  float* part = a.part + (((size_t)kh * a.nz_max + zp) * a.nch_max + c) * ATT_QB * (HD + 2);
   const int nout = nqb * HD;
   for (int i0 = tid; i0 < nout; i0 += 2 * ATT_THREADS) {
     const int i1 = i0 + ATT_THREADS;
@@ -1842,6 +1876,44 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
   }
 }
 
+// the arguments of sequence i of a batched launch
+template <int HD>
+__device__ __forceinline__ AttnArgs att_for_seq(const AttnArgs& a0, const AttnSeqs& q, int i) {
+  AttnArgs a = a0;
+  const int r0 = q.row0[i];
+  a.qkv = a0.qkv + (size_t)r0 * a0.ldqkv;
+  a.M = q.M[i];
+  a.pos0 = q.pos0[i];
+  a.lim_base = q.lim_base[i];
+  a.wbase = q.wbase[i];
+  a.wmask = q.wmask[i];
+  a.nch = q.nch[i];
+  a.kc = reinterpret_cast<char*>(a0.kc) + (size_t)q.slot[i] * a0.seq_stride;
+  a.vc = reinterpret_cast<char*>(a0.vc) + (size_t)q.slot[i] * a0.seq_stride;
+  if (a0.out) a.out = a0.out + (size_t)r0 * a0.Hq * HD;
+  if (a0.xo) a.xo = reinterpret_cast<char*>(a0.xo) + (size_t)r0 * a0.Hq * HD * 4;
+  return a;
+}
+// sequence of query block z of a batched launch (wave-uniform scan)
+__device__ __forceinline__ int att_seq_of(const AttnSeqs& q, int z) {
+  int i = 0;
+  while (i + 1 < q.n && z >= q.zs[i + 1]) ++i;
+  return i;
+}
+
+template <typename KT, typename WT, int HD, bool TREE = false>
+__global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
+  attention_body<KT, WT, HD, TREE>(a, blockIdx.z, blockIdx.z);
+}
+template <typename KT, typename WT, int HD>
+__global__ __launch_bounds__(ATT_THREADS) void k_attention_b(AttnArgs a0, AttnSeqs q) {
+  const int i = att_seq_of(q, blockIdx.z);
+  const AttnArgs a = att_for_seq<HD>(a0, q, i);
+  if ((int)blockIdx.x >= a.nch) return;               // whole workgroup: past this sequence's chunks
+  attention_body<KT, WT, HD, false>(a, blockIdx.z - q.zs[i], blockIdx.z);
+}
+
+
 // Merge of the chunk partials: one workgroup of HD threads per query
 // (blockIdx = (query in block, kv head, query block)).  Wave 0 reduces the
 // chunk statistics with lane = chunk (nch <= 64): M = max of the chunk
@@ -1852,16 +1924,16 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attention(AttnArgs a) {
 // chunk order and divides by L.  Every step depends on positions only.
 #define ATT_MERGE_MAXCH 64
 template <typename WT, int HD>
-__global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
+__device__ __forceinline__ void attn_merge_body(const AttnArgs& a, int z, int zp) {
   __shared__ float wgt[ATT_MERGE_MAXCH];
   __shared__ float st_s[2];
-  const int qi = blockIdx.x, kh = blockIdx.y, z = blockIdx.z;
+  const int qi = blockIdx.x, kh = blockIdx.y;
   const int G = a.Hq / a.Hkv;
   const int gq = z * ATT_QB + qi;
   if (gq >= G * a.M) return;                          // whole workgroup
   const int tid = threadIdx.x, lane = tid & 63;
   const int m = gq / G, h = kh * G + gq % G;
-  const float* pb = a.part + ((size_t)kh * a.nz_max + z) * a.nch_max * ATT_QB * (HD + 2) + (size_t)qi * (HD + 2);
+  const float* pb = a.part + ((size_t)kh * a.nz_max + zp) * a.nch_max * ATT_QB * (HD + 2) + (size_t)qi * (HD + 2);
   const size_t cstride = (size_t)ATT_QB * (HD + 2);
   // this thread's value partials, all chunks issued at once
   float pv[ATT_MERGE_MAXCH];
@@ -1906,6 +1978,15 @@ __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
   const float o = __fdiv_rn(acc, st_s[0]);
   if (a.xo) AF<WT>::store(a.xo, (size_t)m * a.Hq * HD, h * HD + tid, o);
   else a.out[(size_t)m * a.Hq * HD + (size_t)h * HD + tid] = o;
+}
+template <typename WT, int HD>
+__global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
+  attn_merge_body<WT, HD>(a, blockIdx.z, blockIdx.z);
+}
+template <typename WT, int HD>
+__global__ __launch_bounds__(HD) void k_attn_merge_b(AttnArgs a0, AttnSeqs q) {
+  const int i = att_seq_of(q, blockIdx.z);
+  attn_merge_body<WT, HD>(att_for_seq<HD>(a0, q, i), blockIdx.z - q.zs[i], blockIdx.z);
 }
 
 // ---------------------------------------------------------------- LM head reduce / accept
@@ -2308,6 +2389,64 @@ __global__ void k_gather_target(const float* __restrict__ hs, int rows_stride, i
   const int rr = res ? res->trow : row;
   const float* src = hs + ((size_t)l * rows_stride + rr) * d;
   for (int i = threadIdx.x; i < d; i += blockDim.x) target[(size_t)l * d + i] = src[i];
+}
+
+// ---------------------------------------------------------------- batches of independent sequences
+// Several sequences share one pass over the weights: each keeps its own
+// cache block, window, token slots (tok + seq * ts) and result block, and a
+// batched head writes the rows' results into one scratch block (bres) in
+// the pass's row order.  Every per-row step is the single-sequence one.
+
+// A batched draft step: row m (sequence seq[m], window slot slot[m]) gets
+// its argmax as the slot's drafted token and its top-1 probability in the
+// sequence's result block.
+struct BatchRows {
+  int n;
+  int seq[BATCH_ROWS_MAX], slot[BATCH_ROWS_MAX];
+};
+__global__ void k_draft_commit_b(const HeadRes* __restrict__ bres, BatchRows r, HeadRes* res, int32_t* tok, int ts) {
+  const int m = threadIdx.x;
+  if (m >= r.n) return;
+  const int s = r.seq[m], w = r.slot[m];
+  const int a = bres->argmax[m];
+  tok[(size_t)s * ts + w + 1] = a;
+  res[s].argmax[w] = a;
+  res[s].pmax[w] = bres->pmax[m];
+}
+
+// A batched verify pass: sequence seq[i] owns rows row0[i] .. row0[i] + k[i]
+// (pending token, then its k[i] drafts).  Greedy acceptance per sequence as
+// k_accept; trow is the pass row of the last accepted token.
+struct BatchSeqs {
+  int n;
+  int seq[ATT_SEQ_MAX], row0[ATT_SEQ_MAX], k[ATT_SEQ_MAX];
+};
+__global__ void k_accept_b(const HeadRes* __restrict__ bres, BatchSeqs b, HeadRes* res, int32_t* tok, int ts) {
+  const int i = threadIdx.x;
+  if (i >= b.n) return;
+  HeadRes* r = res + b.seq[i];
+  int32_t* t = tok + (size_t)b.seq[i] * ts;
+  const int32_t* am = bres->argmax + b.row0[i];
+  int n = 0;
+  while (n < b.k[i] && am[n] == t[n + 1]) ++n;
+  const int bonus = am[n];
+  r->n = n;
+  r->bonus = bonus;
+  r->trow = b.row0[i] + n;
+  for (int j = 0; j < n; ++j) r->emit[j] = t[j + 1];
+  r->emit[n] = bonus;
+  t[0] = bonus;
+}
+
+// the residual states of each sequence's trow into its layer-selection
+// target (blockIdx = (layer, sequence of the pass))
+__global__ void k_gather_target_b(const float* __restrict__ hs, int rows_stride, int d, const HeadRes* res,
+                                  BatchSeqs b, float* __restrict__ target, size_t tstride) {
+  const int l = blockIdx.x, i = blockIdx.y;
+  const int rr = res[b.seq[i]].trow;
+  const float* src = hs + ((size_t)l * rows_stride + rr) * d;
+  float* dst = target + (size_t)b.seq[i] * tstride + (size_t)l * d;
+  for (int j = threadIdx.x; j < d; j += blockDim.x) dst[j] = src[j];
 }
 
 // ---------------------------------------------------------------- layer-selection DP

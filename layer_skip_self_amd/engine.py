@@ -24,31 +24,35 @@ def _u8(a):
     return a, a.ctypes.data_as(C.POINTER(C.c_uint8))
 
 
-def make_config(shape, max_seq, max_rows=16, kv_dtype="f32"):
+def make_config(shape, max_seq, max_rows=16, kv_dtype="f32", max_seqs=1):
     """``kv_dtype``: "f32" (default) or "bf16".  A bf16 KV cache moves the
     Llama-3-8B-shaped logits ~8e-2 away from the exact result, a float32 one
-    ~2e-4, for ~2% more bytes per decoded token at 1.5K context."""
+    ~2e-4, for ~2% more bytes per decoded token at 1.5K context.
+    ``max_seqs``: independent sequences the engine holds (each its own KV
+    cache of ``max_seq`` positions)."""
     wdt = N.LSS_BF16 if shape.dtype == "bf16" else N.LSS_F32
     kdt = N.LSS_BF16 if kv_dtype == "bf16" else N.LSS_F32
     return N.lss_config(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim,
                         shape.ffn_dim, shape.vocab, float(shape.rope_theta), float(shape.rms_eps),
-                        wdt, int(max_seq), int(max_rows), kdt)
+                        wdt, int(max_seq), int(max_rows), kdt, int(max_seqs))
 
 
-def workspace_bytes(shape, max_seq, max_rows=16, kv_dtype="f32"):
-    cfg = make_config(shape, max_seq, max_rows, kv_dtype)
+def workspace_bytes(shape, max_seq, max_rows=16, kv_dtype="f32", max_seqs=1):
+    cfg = make_config(shape, max_seq, max_rows, kv_dtype, max_seqs)
     return int(N.load().lss_workspace_bytes(C.byref(cfg)))
 
 
 class Engine:
-    """One sequence on one GPU.  ``weights``: ``[(name, tensor)]`` in the
-    canonical order on the CUDA device (they are borrowed, not copied)."""
+    """One GPU engine holding ``max_seqs`` independent sequences (one by
+    default).  ``weights``: ``[(name, tensor)]`` in the canonical order on
+    the CUDA device (they are borrowed, not copied)."""
 
-    def __init__(self, shape, weights, max_seq, max_rows=16, stream=None, device="cuda", kv_dtype="f32"):
+    def __init__(self, shape, weights, max_seq, max_rows=16, stream=None, device="cuda", kv_dtype="f32",
+                 max_seqs=1):
         import torch
         self.lib = N.load()
         self.shape = shape
-        self.cfg = make_config(shape, max_seq, max_rows, kv_dtype)
+        self.cfg = make_config(shape, max_seq, max_rows, kv_dtype, max_seqs)
         self._tensors = [t for _, t in weights]
         n = len(self._tensors)
         nbytes = self.lib.lss_workspace_bytes(C.byref(self.cfg))
@@ -213,6 +217,61 @@ class Engine:
         self._check(self.lib.lss_generate(self.h, p, len(a), int(n_gen), C.byref(pol),
                                           out.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(st)), "lss_generate")
         return out.tolist(), {f: getattr(st, f) for f, _ in N.lss_stats._fields_}
+
+    # -------------------------------------------------------------- several sequences
+    def select(self, seq):
+        """Make sequence ``seq`` the one every single-sequence call acts on."""
+        self._check(self.lib.lss_seq_select(self.h, int(seq)), "lss_seq_select")
+
+    def batch_draft(self, seqs, masks, k, quant=0, exit_tau=0.0):
+        """Draft up to ``k[i]`` tokens for each sequence ``seqs[i]`` with
+        skip mask ``masks[i]``; returns the drafted token lists."""
+        n = len(seqs)
+        s, sp = _i32(seqs)
+        kk, kp = _i32(k)
+        m, mp = _u8(np.asarray(masks, dtype=np.uint8).reshape(n, self.shape.n_layers))
+        out = np.zeros((n, N.LSS_WINDOW_MAX), np.int32)
+        done = np.zeros(n, np.int32)
+        self._check(self.lib.lss_batch_draft(self.h, n, sp, mp, int(quant), kp, float(exit_tau),
+                                             out.ctypes.data_as(C.POINTER(C.c_int32)),
+                                             done.ctypes.data_as(C.POINTER(C.c_int32))), "lss_batch_draft")
+        return [out[i, :done[i]].tolist() for i in range(n)]
+
+    def batch_verify(self, seqs):
+        s, sp = _i32(seqs)
+        self._check(self.lib.lss_batch_verify(self.h, len(seqs), sp), "lss_batch_verify")
+
+    def batch_accept(self, seqs):
+        """Returns [(n_accepted, bonus, emitted tokens)] per sequence."""
+        n = len(seqs)
+        s, sp = _i32(seqs)
+        na = np.zeros(n, np.int32)
+        bo = np.zeros(n, np.int32)
+        acc = np.zeros((n, N.LSS_WINDOW_MAX + 1), np.int32)
+        self._check(self.lib.lss_batch_accept(self.h, n, sp, na.ctypes.data_as(C.POINTER(C.c_int32)),
+                                              bo.ctypes.data_as(C.POINTER(C.c_int32)),
+                                              acc.ctypes.data_as(C.POINTER(C.c_int32))), "lss_batch_accept")
+        return [(int(na[i]), int(bo[i]), acc[i, :na[i] + 1].tolist()) for i in range(n)]
+
+    def generate_batch(self, prompts, n_gen, policy):
+        """Decode every prompt (sequences 0 .. len(prompts) - 1) to ``n_gen``
+        tokens with ``policy`` applied per sequence; returns (token lists,
+        per-sequence stats dicts)."""
+        n = len(prompts)
+        lens = np.asarray([len(p) for p in prompts], np.int32)
+        flat, fp = _i32(np.concatenate([np.asarray(p, np.int32) for p in prompts]))
+        _, lp = _i32(lens)
+        self.set_sampling(policy.get("temperature", 0.0), policy.get("seed", 0))   # batches refuse sampling
+        if "decode_kernel" in policy:
+            self.set_decode_kernel(policy["decode_kernel"])
+        pol = make_policy(policy, self.shape.n_layers)
+        out = np.zeros((n, n_gen), np.int32)
+        st = (N.lss_stats * n)()
+        self._check(self.lib.lss_generate_batch(self.h, n, fp, lp, int(n_gen), C.byref(pol),
+                                                out.ctypes.data_as(C.POINTER(C.c_int32)), st),
+                    "lss_generate_batch")
+        stats = [{f: getattr(st[i], f) for f, _ in N.lss_stats._fields_} for i in range(n)]
+        return [out[i].tolist() for i in range(n)], stats
 
     # -------------------------------------------------------------- measurement
     EPILOGUES = {"qkv": 0, "resid": 1, "gate_up": 2, "lm_head": 3,

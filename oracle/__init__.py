@@ -33,7 +33,8 @@ Parity status per function is listed in each module header.
 from .model import (OracleModel, rms_norm, rope, silu, attend, quantize_row, argmax_first, quantize_weight_rows,
                     w8a8_accumulate, w8a8_project)
 from .decode import (DecodeState, layer_block, prefill, forward_row, ar_generate, draft, verify,
-                     accept, speculative_generate, Policy, top_b, draft_tree, verify_tree, accept_tree)
+                     accept, speculative_generate, batch_generate, Policy, top_b, draft_tree, verify_tree,
+                     accept_tree)
 from .clasp import clasp_dp, brute_force_skip, forward_with_mask_at_target
 from .dytc import (ALPHA, A_INIT, ema_update, fit_latency, predict_latency,
                    plan_cascade, update_cascade)
@@ -43,7 +44,7 @@ __all__ = [
     "OracleModel", "rms_norm", "rope", "silu", "attend", "quantize_row", "argmax_first",
     "quantize_weight_rows", "w8a8_accumulate", "w8a8_project",
     "DecodeState", "layer_block", "prefill", "forward_row", "ar_generate", "draft", "verify", "accept",
-    "speculative_generate", "Policy", "clasp_dp", "brute_force_skip", "top_b", "draft_tree", "verify_tree",
+    "speculative_generate", "batch_generate", "Policy", "clasp_dp", "brute_force_skip", "top_b", "draft_tree", "verify_tree",
     "accept_tree",
     "forward_with_mask_at_target", "ALPHA", "A_INIT", "ema_update", "fit_latency",
     "predict_latency", "plan_cascade", "update_cascade", "sampling",

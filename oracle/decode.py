@@ -541,3 +541,14 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None, state
         if log is not None:
             log.append(rec)
     return out[:G], records
+
+
+def batch_generate(model, prompts, G, policy):
+    """Several independent sequences decoded together (batch > 1): neither
+    page batches requests, so a batch is read as a set of sequences each
+    decoded exactly as on its own -- its own prompt, cache, drafts, layer
+    selection (CLaSp article, section 3, per sequence) and acceptance -- and
+    batching only shares the passes over the weights.  The oracle therefore
+    runs ``speculative_generate`` on every prompt in turn.  Returns
+    [(tokens, per-round records)] in prompt order."""
+    return [speculative_generate(model, np.asarray(p), G, policy) for p in prompts]

@@ -46,7 +46,8 @@ def test_workspace_size_and_invalid_configs():
     assert lss.workspace_bytes(sh, max_seq=1600, max_rows=16, kv_dtype="bf16") == nb - kv // 2
     lib = N.load()
     for field, bad in [("head_dim", 96), ("max_rows", 65), ("max_rows", 0), ("d_model", 8208),
-                       ("n_kv_heads", 5), ("dtype", 7), ("max_seq", 1), ("kv_dtype", 3)]:
+                       ("n_kv_heads", 5), ("dtype", 7), ("max_seq", 1), ("kv_dtype", 3), ("max_seqs", 65),
+                       ("max_seqs", -1)]:
         cfg = lss.make_config(sh, 1600, 16)
         setattr(cfg, field, bad)
         assert lib.lss_workspace_bytes(C.byref(cfg)) == 0, field
@@ -140,3 +141,14 @@ def test_load_weights_checks_names_and_sizes_without_gpu():
     rc = lib.lss_load_weights(C.byref(cfg), tensors(keep, numel), n - 1, C.c_void_p(0x100000), 1 << 30, None,
                               C.byref(h))
     assert rc == N.LSS_EINVAL
+
+
+def test_workspace_grows_by_one_cache_per_sequence():
+    """max_seqs sequences: one KV cache (keys and values), layer-selection
+    target, token slots and result block each, plus a few partials blocks."""
+    sh = lss_synth.SHAPES["llama3_8b"]
+    one = lss.workspace_bytes(sh, max_seq=1600, max_rows=64)
+    four = lss.workspace_bytes(sh, max_seq=1600, max_rows=64, max_seqs=4)
+    kv = 2 * 32 * 8 * 1600 * 128 * 4
+    assert one == lss.workspace_bytes(sh, max_seq=1600, max_rows=64, max_seqs=0)
+    assert 3 * kv < four - one < 3 * kv + 16 * 2**20
