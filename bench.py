@@ -93,6 +93,21 @@ WORKLOADS = {
                                         "tree_depth": 4, "decode_kernel": "mfma_verify"},
                                 desc="Llama-3-8B shape, prompt 1024, 512 generated, CLaSp DP skip 16 every 32 "
                                      "rounds, token tree of width 3 and depth 4 per round"),
+    # Batch > 1: eight independent sequences (seeded prompts of 1024 tokens,
+    # 256 generated each) decoded together, every sequence with the headline
+    # policy (its own CLaSp DP), or with one static skip set that lets all
+    # eight share each draft pass.  The AR leg decodes the same eight
+    # sequences batched.
+    "llama3_8b_batch8": dict(shape="llama3_8b", prompt=1024, gen=256, batch=8,
+                             policy={"mode": "dp", "k_max": 7, "n_skip": 16, "interval": 32, "exit_tau": 0.7,
+                                     "decode_kernel": "mfma_verify"},
+                             desc="Llama-3-8B shape, 8 sequences x (prompt 1024, 256 generated), each with "
+                                  "CLaSp DP skip 16 every 32 rounds, exit threshold 0.7, K <= 7"),
+    "llama3_8b_batch8_static": dict(shape="llama3_8b", prompt=1024, gen=256, batch=8,
+                                    policy={"mode": "static", "k_max": 4, "skip": tuple(range(1, 32, 2)),
+                                            "decode_kernel": "mfma"},
+                                    desc="Llama-3-8B shape, 8 sequences x (prompt 1024, 256 generated), static "
+                                         "skip of layers 1,3,..,31 shared by all, K 4"),
     "cascade_8b": dict(shape="llama3_8b", prompt=(128, 512, 2048), gen=256,
                        policy={"mode": "cascade", "k_max": 8, "interval": 32,
                                "levels": [(22, 4, False), (10, 0, True), (0, 0, True)]},
@@ -201,6 +216,80 @@ def recorded_traffic(bytes_per_launch):
     return None
 
 
+def bench_batch(args, wl, shape, dev):
+    """Batch > 1: wl["batch"] sequences decoded together (lss_generate_batch);
+    value = generated tokens of all sequences per second."""
+    import torch
+    import lss_synth
+    from layer_skip_self_amd import Engine
+    S, G = wl["batch"], (wl["gen"] if args.gen is None else args.gen)
+    weights = lss_synth.make_weights(shape, device=dev)
+    prompts = [lss_synth.make_prompt(shape, wl["prompt"], seed=shape.prompt_seed + i) for i in range(S)]
+    eng = Engine(shape, weights, max_seq=wl["prompt"] + G + 33, max_rows=64, max_seqs=S)
+    pol = dict(wl["policy"])
+    if args.decode_kernel:
+        pol["decode_kernel"] = args.decode_kernel
+    pol.setdefault("decode_kernel", "vector")
+
+    def run(p):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        toks, st = eng.generate_batch(prompts, G, p)
+        torch.cuda.synchronize()
+        return toks, st, time.perf_counter() - t
+
+    for _ in range(args.warmup):
+        run(pol)
+    eng.profile_kernel("gate_up", rows=0)
+    spec_t, toks, stats = 0.0, None, None
+    for _ in range(args.steps):
+        toks, stats, dt = run(pol)
+        spec_t += dt
+    k_ms, k_n, k_bytes = eng.profile_read()
+    eng.profile_kernel("gate_up", enable=False)
+    ar_pol = {"mode": "ar", "decode_kernel": pol["decode_kernel"]}
+    ar_t, ar_toks = 0.0, None
+    if args.ar_steps > 0:
+        run(ar_pol)
+        for _ in range(args.ar_steps):
+            ar_toks, _, dt = run(ar_pol)
+            ar_t += dt
+    step_s = spec_t / args.steps
+    value = S * G / step_s
+    ar_value = S * G * args.ar_steps / ar_t if args.ar_steps > 0 else None
+    rounds = sum(st["rounds"] for st in stats)
+    accepted = sum(st["accepted"] for st in stats)
+    drafted = sum(st["drafted"] for st in stats)
+    avg_us = 1e3 * k_ms / max(k_n, 1)
+    bpl = k_bytes / max(k_n, 1)
+    achieved = bpl / (avg_us * 1e-6) / 1e9 if k_n else None
+    out = {
+        "metric": "gen tokens/s @bs1 (Llama-3-8B shape), speedup vs AR, draft GEMV HBM GB/s",
+        "value": round(value, 3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * step_s, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": shape.dtype, "data": "synthetic (seeded random-init weights and uniform-random prompts)",
+        "config": {"workload": wl["desc"], "global_batch": S, "seq_len": wl["prompt"] + G,
+                   "parallelism": "none (1 GPU)"},
+        "speedup_vs_ar": round(value / ar_value, 4) if ar_value else None,
+        "ar_tokens_per_s": round(ar_value, 3) if ar_value else None,
+        "lossless": toks == ar_toks if ar_toks is not None else None,
+        "decoding": "greedy", "decode_kernel": pol["decode_kernel"],
+        "mean_accepted": round(accepted / max(rounds, 1), 4),
+        "drafted_per_round": round(drafted / max(rounds, 1), 4),
+        "rounds": rounds, "dp_runs": sum(st["dp_runs"] for st in stats),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gate/up projection + SwiGLU, every launch of the step (draft and verify rows of all "
+                      "sequences)",
+            "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None, "traffic": None,
+            "bytes_per_launch": int(bpl), "avg_launch_us": round(avg_us, 3), "launches": k_n,
+        },
+    }
+    eng.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,6 +320,8 @@ def main():
     shape = lss_synth.SHAPES[wl["shape"]]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if wl.get("batch"):
+        return bench_batch(args, wl, shape, dev)
     planted = ()
     if wl.get("planted"):
         rng = np.random.default_rng(shape.weight_seed)

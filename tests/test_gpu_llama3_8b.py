@@ -362,3 +362,28 @@ def test_mfma_decode_rows_8b(gpu8b, oracle8b, kind):
         assert sp == ar
     finally:
         eng.set_decode_kernel("vector")
+
+
+def test_batch_of_four_equals_single_sequence_runs_8b(gpu8b):
+    """Four sequences (the test prompt and three more, ragged lengths)
+    decoded together with the headline policy, each sequence with its own
+    DP: every sequence's tokens and round statistics equal its own
+    single-sequence run, and the batched AR decoding gives the same tokens."""
+    from layer_skip_self_amd import Engine
+    rng = np.random.default_rng(31)
+    prompts = [gpu8b["prompt"]] + [rng.integers(0, SHAPE.vocab, n).astype(np.int32) for n in (300, 177, 412)]
+    G = 40
+    pol = {"mode": "dp", "k_max": 8, "n_skip": 16, "interval": 4, "exit_tau": 0.7}
+    eng = Engine(SHAPE, gpu8b["w"], max_seq=MAX_SEQ, max_rows=64, max_seqs=4)
+    try:
+        toks, stats = eng.generate_batch(prompts, G, pol)
+        ar, _ = eng.generate_batch(prompts, G, {"mode": "ar"})
+    finally:
+        eng.close()
+    one = gpu8b["eng"]
+    for i, p in enumerate(prompts):
+        single, st = one.generate(p, G, pol)
+        print(f"sequence {i}: {stats[i]}")
+        assert toks[i] == single, i
+        assert stats[i] == st, i
+        assert ar[i] == single, i
