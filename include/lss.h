@@ -201,13 +201,18 @@ int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k);
 int lss_accept_and_rollback(lss_engine* e, int32_t* n_accepted, int32_t* bonus,
                             int32_t* accepted_out);
 
-/* CLaSp layer selection (section 3): skip exactly n_skip of the first
- * n_layers_eff layers (n_layers_eff <= n_layers; layers past it are marked
- * skipped, an early exit) by the batched cosine-similarity DP against the
- * target's full hidden states.  mask_out[n_layers] gets 1 = skip; score_out
- * (may be NULL) the final cosine similarity. */
-int lss_select_layers_dp(lss_engine* e, int32_t n_skip, int32_t n_layers_eff, uint8_t* mask_out,
-                         float* score_out);
+/* CLaSp layer selection (section 3): skip exactly n_skip of the n_layers
+ * layers by the batched cosine-similarity DP against the target's full
+ * hidden states (the last accepted token's; after prefill, the last prompt
+ * row's).  mask_out[n_layers] gets 1 = skip; score_out (may be NULL) the
+ * final cosine similarity.  LSS_EINVAL unless 0 <= n_skip <= n_layers. */
+int lss_select_layers_dp(lss_engine* e, int32_t n_skip, uint8_t* mask_out, float* score_out);
+/* The same DP over the first n_layers_eff layers only (n_layers_eff <=
+ * n_layers): the layers past it are marked skipped, an early exit (the
+ * CAS-Spec blog's draft levels with layer sparsity plus early exit,
+ * section 2.2). */
+int lss_select_layers_dp_exit(lss_engine* e, int32_t n_skip, int32_t n_layers_eff, uint8_t* mask_out,
+                              float* score_out);
 
 /* Committed sequence length p. */
 int32_t lss_seq_len(const lss_engine* e);

@@ -72,8 +72,9 @@ SIGNATURES = {
     "lss_verify": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32]),
     "lss_accept_and_rollback": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                                           C.POINTER(C.c_int32)]),
-    "lss_select_layers_dp": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_uint8),
-                                       C.POINTER(C.c_float)]),
+    "lss_select_layers_dp": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_uint8), C.POINTER(C.c_float)]),
+    "lss_select_layers_dp_exit": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_uint8),
+                                            C.POINTER(C.c_float)]),
     "lss_seq_len": (C.c_int32, [C.c_void_p]),
     "lss_set_sampling": (C.c_int, [C.c_void_p, C.c_float, C.c_uint64]),
     "lss_set_gemv_grid": (C.c_int, [C.c_void_p, C.c_int32]),

@@ -1470,7 +1470,12 @@ int lss_accept_and_rollback(lss_engine* e, int32_t* n_accepted, int32_t* bonus, 
   return LSS_OK;
 }
 
-int lss_select_layers_dp(lss_engine* e, int32_t S, int32_t Le, uint8_t* mask_out, float* score_out) {
+int lss_select_layers_dp(lss_engine* e, int32_t S, uint8_t* mask_out, float* score_out) {
+  if (!e) return LSS_EINVAL;
+  return lss_select_layers_dp_exit(e, S, e->cfg.n_layers, mask_out, score_out);
+}
+
+int lss_select_layers_dp_exit(lss_engine* e, int32_t S, int32_t Le, uint8_t* mask_out, float* score_out) {
   if (!e) return LSS_EINVAL;
   const auto& c = e->cfg;
   const int L = c.n_layers, d = c.d_model;
@@ -1929,12 +1934,12 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
     if (pol->mode == LSS_MODE_STATIC) {
       std::copy(pol->static_mask, pol->static_mask + L, masks[0].begin());
     } else if (pol->mode == LSS_MODE_DP) {
-      int r = lss_select_layers_dp(e, pol->n_skip, L, masks[0].data(), nullptr);
+      int r = lss_select_layers_dp(e, pol->n_skip, masks[0].data(), nullptr);
       if (r) return r;
       st.dp_runs++;
     } else if (pol->mode == LSS_MODE_CASCADE) {
       for (int v = 0; v < nlev; ++v) {
-        int r = lss_select_layers_dp(e, pol->level_skip[v] - pol->level_exit[v], L - pol->level_exit[v],
+        int r = lss_select_layers_dp_exit(e, pol->level_skip[v] - pol->level_exit[v], L - pol->level_exit[v],
                                      masks[v].data(), nullptr);
         if (r) return r;
         st.dp_runs++;
@@ -2042,7 +2047,7 @@ int lss_generate_batch(lss_engine* e, int32_t n, const int32_t* prompts, const i
   auto dp = [&](int i) -> int {
     int r = lss_seq_select(e, i);
     if (r) return r;
-    r = lss_select_layers_dp(e, pol->n_skip, L, masks.data() + (size_t)i * L, nullptr);
+    r = lss_select_layers_dp(e, pol->n_skip, masks.data() + (size_t)i * L, nullptr);
     if (r == LSS_OK) st[i].dp_runs++;
     return r;
   };

@@ -163,9 +163,12 @@ class Engine:
         L = self.shape.n_layers
         mask = np.zeros(L, np.uint8)
         score = C.c_float()
-        self._check(self.lib.lss_select_layers_dp(self.h, int(n_skip), int(L if n_layers_eff is None else n_layers_eff),
-                                                  mask.ctypes.data_as(C.POINTER(C.c_uint8)), C.byref(score)),
-                    "lss_select_layers_dp")
+        mp = mask.ctypes.data_as(C.POINTER(C.c_uint8))
+        if n_layers_eff is None:
+            self._check(self.lib.lss_select_layers_dp(self.h, int(n_skip), mp, C.byref(score)), "lss_select_layers_dp")
+        else:
+            self._check(self.lib.lss_select_layers_dp_exit(self.h, int(n_skip), int(n_layers_eff), mp, C.byref(score)),
+                        "lss_select_layers_dp_exit")
         return mask.tolist(), float(score.value)
 
     def calibrate_latency(self, prompt, seq_lens, depths, reps=5):
