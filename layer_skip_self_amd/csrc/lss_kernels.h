@@ -241,12 +241,94 @@ __device__ __forceinline__ void prep_vals(const float (&v)[PREP_PER_THREAD], int
   }
 }
 
+// Every load is issued unconditionally (elements past d read element d - 1
+// and are zeroed afterwards): a conditional load merged with a constant
+// makes the compiler wait for it at the merge, one round trip per element.
 template <typename T>
 __device__ __forceinline__ void load_vals(float (&v)[PREP_PER_THREAD], const T* src, int d) {
 #pragma unroll
   for (int j = 0; j < PREP_PER_THREAD; ++j) {
     const int i = threadIdx.x + j * PREP_THREADS;
-    v[j] = (i < d) ? ld_elem<T>(src, i) : 0.f;
+    v[j] = ld_elem<T>(src, min(i, d - 1));
+  }
+#pragma unroll
+  for (int j = 0; j < PREP_PER_THREAD; ++j)
+    if (threadIdx.x + j * PREP_THREADS >= d) v[j] = 0.f;
+}
+
+// The same for 16 consecutive columns c0 .. c0 + 15 held by one thread
+// (vector loads and stores): xo = x * g in the projection format and po =
+// the 16 columns' sum of squares, added in the order of sum16's lane tree
+// (pairs, then pairs of pairs, then the two quads of each half, then the
+// halves), so the result is the 16-lane form's bit for bit.
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+template <typename WT>
+__device__ __forceinline__ void prep16(const float (&x)[16], int c0, int d, const float* __restrict__ g, void* xo,
+                                       float* __restrict__ po, int m) {
+  if (xo) {
+    float y[16];
+    if (g) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 gg = *reinterpret_cast<const float4*>(g + c0 + 4 * q);
+        y[4 * q] = __fmul_rn(x[4 * q], gg.x);
+        y[4 * q + 1] = __fmul_rn(x[4 * q + 1], gg.y);
+        y[4 * q + 2] = __fmul_rn(x[4 * q + 2], gg.z);
+        y[4 * q + 3] = __fmul_rn(x[4 * q + 3], gg.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = x[i];
+    }
+    if constexpr (sizeof(WT) == 2) {
+      // blocks of 8: {8 bf16 hi, 8 bf16 lo}, 32 bytes per block
+      uint4* b = reinterpret_cast<uint4*>(reinterpret_cast<char*>(xo) + ((size_t)m * d + c0) * 4);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        float lo[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lo[i] = __fsub_rn(y[8 * k + i], bf2f(f2bf(y[8 * k + i])));
+        b[2 * k] = make_uint4(pack_bf2(y[8 * k], y[8 * k + 1]), pack_bf2(y[8 * k + 2], y[8 * k + 3]),
+                              pack_bf2(y[8 * k + 4], y[8 * k + 5]), pack_bf2(y[8 * k + 6], y[8 * k + 7]));
+        b[2 * k + 1] = make_uint4(pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(lo[4], lo[5]),
+                                  pack_bf2(lo[6], lo[7]));
+      }
+    } else {
+      float4* b = reinterpret_cast<float4*>(reinterpret_cast<float*>(xo) + (size_t)m * d + c0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) b[q] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+    }
+  }
+  if (po) {
+    float p2[8], p4[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p2[i] = __fadd_rn(__fmul_rn(x[2 * i], x[2 * i]), __fmul_rn(x[2 * i + 1], x[2 * i + 1]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p4[i] = __fadd_rn(p2[2 * i], p2[2 * i + 1]);
+    po[(size_t)m * (d >> 4) + (c0 >> 4)] = __fadd_rn(__fadd_rn(p4[0], p4[1]), __fadd_rn(p4[2], p4[3]));
+  }
+}
+// 16 consecutive values of a row of T (16-byte aligned) as float
+template <typename T> __device__ __forceinline__ void ld16(float (&x)[16], const T* src);
+template <> __device__ __forceinline__ void ld16<float>(float (&x)[16], const float* src) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = reinterpret_cast<const float4*>(src)[q];
+    x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+  }
+}
+template <> __device__ __forceinline__ void ld16<uint16_t>(float (&x)[16], const uint16_t* src) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint4 v = reinterpret_cast<const uint4*>(src)[q];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[8 * q + 2 * i] = __uint_as_float(w[i] << 16);
+      x[8 * q + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
   }
 }
 
@@ -255,24 +337,25 @@ __global__ __launch_bounds__(PREP_THREADS) void k_prep_rows(const float* __restr
                                                             const float* __restrict__ g, void* xo,
                                                             float* __restrict__ po) {
   const int m = blockIdx.x;
-  float v[PREP_PER_THREAD];
-  load_vals<float>(v, h + (size_t)m * ldh, d);
-  prep_vals<WT>(v, d, g, xo, po, m);
+  for (int c0 = threadIdx.x * 16; c0 < d; c0 += PREP_THREADS * 16) {
+    float x[16];
+    ld16<float>(x, h + (size_t)m * ldh + c0);
+    prep16<WT>(x, c0, d, g, xo, po, m);
+  }
 }
 
-// h[m][:] = E[tok[m]][:] (float32 residual stream) and its projection input.
+// h[m][:] = E[id][:] (float32 residual stream) and its projection input.
 template <typename WT>
 __device__ __forceinline__ void embed_body(const WT* __restrict__ E, int id, int d, float* __restrict__ h,
                                            const float* __restrict__ g, void* xo, float* __restrict__ po, int m) {
-  float v[PREP_PER_THREAD];
-  load_vals<WT>(v, E + (size_t)id * d, d);
-  float* hr = h + (size_t)m * d;
+  for (int c0 = threadIdx.x * 16; c0 < d; c0 += PREP_THREADS * 16) {
+    float x[16];
+    ld16<WT>(x, E + (size_t)id * d + c0);
+    float4* hr = reinterpret_cast<float4*>(h + (size_t)m * d + c0);
 #pragma unroll
-  for (int j = 0; j < PREP_PER_THREAD; ++j) {
-    const int i = threadIdx.x + j * PREP_THREADS;
-    if (i < d) hr[i] = v[j];
+    for (int q = 0; q < 4; ++q) hr[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+    prep16<WT>(x, c0, d, g, xo, po, m);
   }
-  prep_vals<WT>(v, d, g, xo, po, m);
 }
 template <typename WT>
 __global__ __launch_bounds__(PREP_THREADS) void k_embed(const WT* __restrict__ E, const int32_t* __restrict__ tok,
@@ -2020,13 +2103,22 @@ __global__ __launch_bounds__(HEAD_RED_THREADS) void k_head_reduce(const float* _
   // (tiles w = tid + j blockDim; vocabularies up to 16 x 1024 x 16 columns)
   float rm[HEAD_RED_REG], rl[HEAD_RED_REG];
   int ri[HEAD_RED_REG];
+  // (unconditional loads, tiles past ntile read the last one and are
+  // neutralized afterwards: see load_vals)
 #pragma unroll
   for (int j = 0; j < HEAD_RED_REG; ++j) {
-    const int w = threadIdx.x + j * HEAD_RED_THREADS;
-    rm[j] = w < ntile ? p[w * HEAD_PART] : -INFINITY;
-    ri[j] = w < ntile ? __float_as_int(p[w * HEAD_PART + 1]) : 0x7fffffff;
-    rl[j] = w < ntile ? p[w * HEAD_PART + 2] : 0.f;
+    const int w = min(threadIdx.x + j * HEAD_RED_THREADS, ntile - 1);
+    rm[j] = p[w * HEAD_PART];
+    ri[j] = __float_as_int(p[w * HEAD_PART + 1]);
+    rl[j] = p[w * HEAD_PART + 2];
   }
+#pragma unroll
+  for (int j = 0; j < HEAD_RED_REG; ++j)
+    if (threadIdx.x + j * HEAD_RED_THREADS >= ntile) {
+      rm[j] = -INFINITY;
+      ri[j] = 0x7fffffff;
+      rl[j] = 0.f;
+    }
 #pragma unroll
   for (int j = 0; j < HEAD_RED_REG; ++j) argmax_merge(mx, idx, rm[j], ri[j]);
   for (int w = threadIdx.x + HEAD_RED_REG * HEAD_RED_THREADS; w < ntile; w += blockDim.x)
@@ -2387,8 +2479,10 @@ __global__ void k_gather_target(const float* __restrict__ hs, int rows_stride, i
                                 int row, float* __restrict__ target) {
   const int l = blockIdx.x;
   const int rr = res ? res->trow : row;
-  const float* src = hs + ((size_t)l * rows_stride + rr) * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) target[(size_t)l * d + i] = src[i];
+  const float4* src = reinterpret_cast<const float4*>(hs + ((size_t)l * rows_stride + rr) * d);
+  float4* dst = reinterpret_cast<float4*>(target + (size_t)l * d);
+#pragma unroll 4
+  for (int i = threadIdx.x; i < d / 4; i += blockDim.x) dst[i] = src[i];   // d is a multiple of 16
 }
 
 // ---------------------------------------------------------------- batches of independent sequences
@@ -2444,9 +2538,10 @@ __global__ void k_gather_target_b(const float* __restrict__ hs, int rows_stride,
                                   BatchSeqs b, float* __restrict__ target, size_t tstride) {
   const int l = blockIdx.x, i = blockIdx.y;
   const int rr = res[b.seq[i]].trow;
-  const float* src = hs + ((size_t)l * rows_stride + rr) * d;
-  float* dst = target + (size_t)b.seq[i] * tstride + (size_t)l * d;
-  for (int j = threadIdx.x; j < d; j += blockDim.x) dst[j] = src[j];
+  const float4* src = reinterpret_cast<const float4*>(hs + ((size_t)l * rows_stride + rr) * d);
+  float4* dst = reinterpret_cast<float4*>(target + (size_t)b.seq[i] * tstride + (size_t)l * d);
+#pragma unroll 4
+  for (int j = threadIdx.x; j < d / 4; j += blockDim.x) dst[j] = src[j];
 }
 
 // ---------------------------------------------------------------- layer-selection DP
