@@ -286,6 +286,12 @@ def bench_batch(args, wl, shape, dev):
             "bytes_per_launch": int(bpl), "avg_launch_us": round(avg_us, 3), "launches": k_n,
         },
     }
+    if not args.no_cpu_baseline:
+        # the oracle decodes a batch as independent sequences, one after the
+        # other: its rate is the single-sequence rate of the same policy
+        cb = cpu_baseline(shape, weights, prompts[0], pol, args.cpu_tokens, min(args.cpu_prompt, wl["prompt"]))
+        cb["sample"] += "; the oracle decodes a batch's sequences one after another, so this is its batch rate too"
+        out["cpu_baseline"] = cb
     eng.close()
     print(json.dumps(out), flush=True)
 
