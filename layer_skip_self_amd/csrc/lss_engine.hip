@@ -243,7 +243,6 @@ struct lss_engine {
   float* target_all = nullptr;
   HeadRes *res_all = nullptr, *hres_all = nullptr;   // device / pinned host, nseq + 1 (the last: batched rows)
   std::vector<PassSeq> pass;                         // sequences of the running batched pass
-  bool pass_draft = false;
   // sequence state
   int p = 0;                  // committed length
   int win = 0;                // drafted tokens in the window
