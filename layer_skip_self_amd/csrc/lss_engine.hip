@@ -478,18 +478,20 @@ void vgemm_go(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t
   const dim3 grid(nwg), block(64 * (VG_WAVES + 1));
   launch_k(k_vgemm<EPI, TN, VG_ST>, grid, block, 0, s, t0, t1, g);
 }
-// tiles of 32 weight rows (half the activation loads per weight byte of
-// 16-row tiles) once there are at least this many such tiles per hundred
-// compute units: at the 8B shape the q/k/v projection (192 tiles, 0.75 per
-// unit) runs 18 % faster at one row and 27 % at 9 rows with 32-row tiles,
-// the 4096-row projections (128 tiles) 22 % slower
-#ifndef VG_TN32_MIN_TILES_PCT
-#define VG_TN32_MIN_TILES_PCT 75
-#endif
+// Tiles of 32 weight rows halve the activation loads per weight byte of
+// 16-row tiles but halve the workgroups.  Measured (one row / nine rows,
+// HIP events, interleaved A/B): 32-row tiles win where they give 0.75 to 1
+// tile per compute unit (q/k/v at 8B, 192 tiles: 13.2 against 15.9 us;
+// the 8192-row projections at 70B, 256 tiles: 51.6 against 54.8 us) and
+// for the LM head's thousands of tiles; 16-row tiles win below (the 4096-row
+// projections at 8B, 128 tiles) and above (q/k/v at 70B, 320 tiles: 39.2
+// against 44.6 us), where the extra workgroups keep more loads in flight.
+// gate/up holds two matrices per tile and always takes 16 rows.
 template <int EPI>
 void vgemm(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   if constexpr (EPI != EPI_SWIGLU) {
-    if (gl.ncu > 0 && (long)(g.N / 32) * 100 >= (long)VG_TN32_MIN_TILES_PCT * gl.ncu) {
+    const long t32 = g.N / 32, ncu = gl.ncu;
+    if (ncu > 0 && ((4 * t32 >= 3 * ncu && t32 <= ncu) || t32 >= 4 * ncu)) {
       vgemm_go<EPI, 32>(g, gl, s, t0, t1);
       return;
     }
