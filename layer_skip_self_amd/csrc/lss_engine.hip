@@ -450,19 +450,18 @@ void gemv_mt(const GemmArgs& ga, const GemvLaunch& gl, hipStream_t s, hipEvent_t
   }
 }
 
-// MFMA decode GEMM: one launch for all M <= 16 rows.  Tiles of 32 weight
-// rows where the launch walks tiles anyway (half the activation reads per
-// weight byte), 16 rows otherwise (more workgroups for the short
-// projections) and for gate/up (two weight matrices per tile).  The tile
-// width changes no output bit.
+// MFMA decode GEMM: one launch for all M <= 16 rows, tiles of 16 or 32
+// weight rows and 4 or 8 MFMA waves per workgroup by the rules below.  The
+// tile width changes no output bit; the wave count fixes the split of K and
+// is a function of the projection alone.
 #ifndef VG_ST
 #define VG_ST 2
 #endif
-template <int EPI, int TN>
+template <int EPI, int TN, int W>
 void vgemm_go(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   static const int occ = [] {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_vgemm<EPI, TN, VG_ST>, 64 * (VG_WAVES + 1), 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_vgemm<EPI, TN, VG_ST, W>, 64 * (W + 1), 0) !=
             hipSuccess || nb < 1)
       nb = 1;
     return nb;
@@ -475,8 +474,8 @@ void vgemm_go(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t
     const int per = (ntile + gl.ncu * occ - 1) / (gl.ncu * occ);
     nwg = (ntile + per - 1) / per;
   }
-  const dim3 grid(nwg), block(64 * (VG_WAVES + 1));
-  launch_k(k_vgemm<EPI, TN, VG_ST>, grid, block, 0, s, t0, t1, g);
+  const dim3 grid(nwg), block(64 * (W + 1));
+  launch_k(k_vgemm<EPI, TN, VG_ST, W>, grid, block, 0, s, t0, t1, g);
 }
 // Tiles of 32 weight rows halve the activation loads per weight byte of
 // 16-row tiles but halve the workgroups.  Measured (one row / nine rows,
@@ -487,16 +486,25 @@ void vgemm_go(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t
 // projections at 8B, 128 tiles) and above (q/k/v at 70B, 320 tiles: 39.2
 // against 44.6 us), where the extra workgroups keep more loads in flight.
 // gate/up holds two matrices per tile and always takes 16 rows.
+//
+// MFMA waves per workgroup: 8 for the q/k/v and gate/up projections of depth
+// K >= 8192 (70B: q/k/v 39.2 -> 35.3 us at one row, gate/up 151.7 -> 144.8
+// at one row and 166.2 -> 151.8 at nine), 4 otherwise (at K = 4096 every
+// projection, and at 70B the LM head, measured slower with 8).  The choice
+// depends on the projection only, never on the row count.
 template <int EPI>
 void vgemm(const GemmArgs& g, const GemvLaunch& gl, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  const bool w8 = g.K >= 8192 && (EPI == EPI_STORE || EPI == EPI_SWIGLU);
   if constexpr (EPI != EPI_SWIGLU) {
     const long t32 = g.N / 32, ncu = gl.ncu;
     if (ncu > 0 && ((4 * t32 >= 3 * ncu && t32 <= ncu) || t32 >= 4 * ncu)) {
-      vgemm_go<EPI, 32>(g, gl, s, t0, t1);
+      if (w8) vgemm_go<EPI, 32, 8>(g, gl, s, t0, t1);
+      else vgemm_go<EPI, 32, 4>(g, gl, s, t0, t1);
       return;
     }
   }
-  vgemm_go<EPI, 16>(g, gl, s, t0, t1);
+  if (w8) vgemm_go<EPI, 16, 8>(g, gl, s, t0, t1);
+  else vgemm_go<EPI, 16, 4>(g, gl, s, t0, t1);
 }
 
 // Prefill / layer-selection projection: 1/rms rows, split MFMA GEMM, split

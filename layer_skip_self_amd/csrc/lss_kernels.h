@@ -1128,7 +1128,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
 // operands of a unit come straight from L2 (rows < M only).
 //
 // Work split as in the vector GEMV: tiles of TN weight rows, a workgroup
-// walks a contiguous range of tiles, its VG_WAVES waves split K into fixed
+// walks a contiguous range of tiles, its W MFMA waves split K into fixed
 // contiguous ranges of 128-element pieces, and every wave walks the same
 // number of units per tile (units past its range are empty) with ST units
 // in flight across tile boundaries.  Per (n, m) the arithmetic is fixed by
@@ -1137,9 +1137,6 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
 // are added in wave order.  The MFMA's sum for one output does not depend
 // on the row's place in the operand or on the other rows, so a verify row
 // gets the bits of the greedy step at the same position.
-#ifndef VG_WAVES
-#define VG_WAVES 4                     // MFMA waves per workgroup (plus one epilogue wave)
-#endif
 #define VG_PB 256                      // bytes of one weight row per unit (128 bf16)
 #define VG_RS (VG_PB + 16)             // LDS row stride of the transposition buffer
 #define VG_MMAX 16
@@ -1190,16 +1187,18 @@ __device__ __forceinline__ void vg_load(VgUnit<NI, SUB>& U, const uint16_t* cons
   }
 }
 
-template <int EPI, int TN, int ST>
-__global__ __launch_bounds__(64 * (VG_WAVES + 1)) void k_vgemm(GemmArgs ga) {
+// W: MFMA waves per workgroup (plus one epilogue wave); it fixes how K is
+// split, so one projection always launches with the same W
+template <int EPI, int TN, int ST, int W>
+__global__ __launch_bounds__(64 * (W + 1)) void k_vgemm(GemmArgs ga) {
   constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int NB = TN / 16;                      // 16-column operand blocks per tile
   constexpr int NI = NACC * TN / 4;                // load instructions per unit
   constexpr int SUB = VG_PB / 64;                  // 32-k MFMA steps per unit
   constexpr int RPP = 64 / TN;                     // epilogue rows per pass of the epilogue wave
   static_assert(TN == 16 || TN == 32, "tile of 16 or 32 weight rows");
-  __shared__ __align__(16) char wl_s[VG_WAVES][NACC * TN * VG_RS];
-  __shared__ float part_s[2][VG_WAVES][NACC][VG_MMAX][TN];
+  __shared__ __align__(16) char wl_s[W][NACC * TN * VG_RS];
+  __shared__ float part_s[2][W][NACC][VG_MMAX][TN];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1209,7 +1208,7 @@ __global__ __launch_bounds__(64 * (VG_WAVES + 1)) void k_vgemm(GemmArgs ga) {
   const int te = (int)((long)(blockIdx.x + 1) * ntile / gridDim.x);
   if (tb >= te) return;                            // whole workgroup (grid <= tiles on the host)
 
-  if (wave == VG_WAVES) {
+  if (wave == W) {
     // ---- epilogue wave: the only wave that stores.  Loads and stores share
     // one counter on this chip, so a store among the MFMA waves' loads would
     // make every later wait for a load a wait for everything.
@@ -1281,7 +1280,7 @@ __global__ __launch_bounds__(64 * (VG_WAVES + 1)) void k_vgemm(GemmArgs ga) {
             for (int q = 0; q < NACC; ++q) {
               float v = part_s[par][0][q][m][ei];
 #pragma unroll
-              for (int w = 1; w < VG_WAVES; ++w) v = __fadd_rn(v, part_s[par][w][q][m][ei]);
+              for (int w = 1; w < W; ++w) v = __fadd_rn(v, part_s[par][w][q][m][ei]);
               y[q] = scaled ? __fmul_rn(v, sc[p]) : v;
             }
             proj_out<uint16_t, EPI>(ga, m, M, tile0 + ei, ei & 15, (tile0 + (ei & ~15)) / 16, n16, y[0],
@@ -1295,9 +1294,9 @@ __global__ __launch_bounds__(64 * (VG_WAVES + 1)) void k_vgemm(GemmArgs ga) {
 
   // ---- MFMA waves: loads, LDS transposition, MFMA; no global stores
   const int npc = (K + 127) >> 7;                  // 128-element pieces of a row
-  const int p0 = wave * npc / VG_WAVES;
-  const int np = (wave + 1) * npc / VG_WAVES - p0; // pieces of this wave
-  const int nmax = (npc + VG_WAVES - 1) / VG_WAVES;
+  const int p0 = wave * npc / W;
+  const int np = (wave + 1) * npc / W - p0;        // pieces of this wave
+  const int nmax = (npc + W - 1) / W;
   const int NUP = (nmax + ST - 1) / ST * ST;       // units per tile (every wave), a multiple of ST
   const int la = lane >> 4, lc = lane & 15;        // load role: row la of 4, 16-byte piece lc
   const int r = lane & 15, g = lane >> 4;          // operand role: row / column r, k group g
