@@ -37,7 +37,7 @@ from .decode import (DecodeState, layer_block, prefill, forward_row, ar_generate
                      accept_tree)
 from .clasp import clasp_dp, brute_force_skip, forward_with_mask_at_target
 from .dytc import (ALPHA, A_INIT, ema_update, fit_latency, predict_latency,
-                   plan_cascade, update_cascade)
+                   plan_cascade, update_cascade, plan_tree, update_tree, expected_tree)
 from . import sampling
 
 __all__ = [
@@ -47,5 +47,6 @@ __all__ = [
     "speculative_generate", "batch_generate", "Policy", "clasp_dp", "brute_force_skip", "top_b", "draft_tree", "verify_tree",
     "accept_tree",
     "forward_with_mask_at_target", "ALPHA", "A_INIT", "ema_update", "fit_latency",
-    "predict_latency", "plan_cascade", "update_cascade", "sampling",
+    "predict_latency", "plan_cascade", "update_cascade", "plan_tree", "update_tree", "expected_tree",
+    "sampling",
 ]

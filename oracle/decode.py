@@ -307,7 +307,7 @@ def top_b(z, B):
     return [int(i) for i in order[:B]]
 
 
-def draft_tree(model, st, skip, quant, B, D=1):
+def draft_tree(model, st, skip, quant, B, D=1, levels=None):
     """Token tree of width B and depth D, drafted by the skipped-layer model.
 
     The draft runs the pending token's row (position p) and proposes its B
@@ -316,8 +316,18 @@ def draft_tree(model, st, skip, quant, B, D=1):
     row of node j of a branch (position p + j) seeing the committed prefix,
     the pending token and that branch's earlier nodes only.  Returns (the
     branches [B][D], the draft's top-1 probability at the pending row); the
-    window holds the branches one after the other."""
-    z, _ = forward_row(model, st, st.t0, st.p, "draft", skip, quant)
+    window holds the branches one after the other.
+
+    levels: None (every depth drafted with ``skip``, ``quant``) or D pairs
+    (skip, quant): the draft level whose pass proposes the nodes of depth j
+    is levels[j - 1] (the pending token's row for j = 1, the rows of the
+    depth j - 1 nodes otherwise), a cascade routed into the tree.  A layer
+    sees the pending token and a branch's earlier nodes only where the
+    level of the pass over them ran that layer (the per-layer valid bits of
+    a chain window, by depth)."""
+    lv = [(skip, quant)] * D if levels is None else list(levels)
+    assert len(lv) == D
+    z, _ = forward_row(model, st, st.t0, st.p, "draft", lv[0][0], lv[0][1])
     firsts = top_b(z, B)
     root_valid = list(st.valid)                      # window slot 0: the pending token
     branches = []
@@ -325,7 +335,7 @@ def draft_tree(model, st, skip, quant, B, D=1):
         st.valid = list(root_valid)                  # another branch's nodes are invisible
         br = [c]
         for j in range(1, D):
-            zz, _ = forward_row(model, st, br[-1], st.p + j, "draft", skip, quant)
+            zz, _ = forward_row(model, st, br[-1], st.p + j, "draft", lv[j][0], lv[j][1])
             br.append(argmax_first(zz))
         branches.append(br)
     st.valid = list(root_valid)
@@ -425,7 +435,9 @@ class Policy:
     (``oracle.sampling``), 0: greedy; tree_width B > 0 (greedy, static or
     DP mask): every round drafts a token tree of width B and depth
     min(tree_depth, tokens still to emit) (``draft_tree``) instead of a
-    chain.
+    chain; with ``cascade``, tree_width is the largest width the router may
+    choose (``dytc.plan_tree``, row_cost its per-row-count cost factors,
+    None: 1), its levels drafting the tree's depths.
     """
     K: int = 4
     skip: tuple = ()
@@ -440,6 +452,7 @@ class Policy:
     seed: int = 0
     tree_width: int = 0
     tree_depth: int = 1
+    row_cost: tuple = None
 
     @property
     def sampling(self):
@@ -462,7 +475,7 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None, state
     prefill and again after every ``interval``-th verify round.
     """
     from .clasp import clasp_dp
-    from .dytc import A_INIT, plan_cascade, update_cascade, predict_latency
+    from .dytc import A_INIT, plan_cascade, update_cascade, predict_latency, plan_tree, update_tree
     L = model.L
     max_seq = max_seq or len(prompt) + G + WINDOW_MAX + 1
     sam = policy.sampling
@@ -489,6 +502,37 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None, state
     rounds = 0
     while len(out) < G:
         budget = G - len(out) - 1
+        if policy.cascade is not None and policy.tree_width:
+            depth = [L - sum(mk) for mk in masks]
+            t_hat = [predict_latency(policy.latency_beta, st.p, dp) for dp in depth]
+            t_ver = predict_latency(policy.latency_beta, st.p, L)
+            B, plan = plan_tree(a, t_hat, t_ver, policy.row_cost, policy.K, policy.tree_width)
+            levels = []         # depth order: most precise level first
+            for lev in reversed(range(len(masks))):
+                levels += [lev] * plan[lev]
+            levels = levels[:budget]
+            if levels:
+                draft_tree(model, st, None, None, B, len(levels),
+                           levels=[(masks[lev], policy.cascade[lev][2]) for lev in levels])
+                logits, states, branches, kv = verify_tree(model, st)
+                n, bonus, emitted = accept_tree(st, logits, states, branches, kv)
+                firsts = [br[0] for br in branches]
+                branch = firsts.index(emitted[0]) if n else -1
+            else:
+                logits, states, d = verify(model, st)
+                n, bonus, emitted = accept(st, logits, states, d, sam)
+                branch = -1
+            a = update_tree(a, levels, n, branch)
+            out += emitted
+            rounds += 1
+            rec = {"k": B * len(levels), "n": n, "bonus": bonus, "tree": True, "width": B,
+                   "levels": levels, "branch": branch, "a": list(a)}
+            records.append(rec)
+            if rounds % policy.interval == 0:
+                masks = select_masks()
+            if log is not None:
+                log.append(rec)
+            continue
         if policy.cascade is not None:
             depth = [L - sum(mk) for mk in masks]
             t_hat = [predict_latency(policy.latency_beta, st.p, dp) for dp in depth]

@@ -171,3 +171,95 @@ def test_some_run_accepts_deep_in_a_later_branch(tiny_model, tiny_prompt, ar):
                                              oracle.Policy(tree_width=3, tree_depth=3, skip=(1,)))
     assert toks == oracle.ar_generate(tiny_model, tiny_prompt, 48)
     assert any(r.get("branch", -1) >= 1 and r["n"] >= 2 for r in recs)
+
+
+# ---- the cascade routed into the tree (levels per depth)
+
+CASCADE = [(3, 1, False), (1, 0, True), (0, 0, True)]
+
+
+def test_mixed_level_branches_are_chain_drafts(tiny_model, tiny_prompt):
+    """A tree whose depths are drafted by different levels: branch 0 is the
+    chain window drafted one token per level in the same order (the pinned
+    chain draft with its per-layer valid bits), and every branch b continues
+    from its first node like that chain with the first token forced."""
+    m = tiny_model
+    lv = [([0, 0, 1, 0], True), ([1, 1, 1, 0], False), ([0, 1, 1, 1], False)]
+    st, _, _ = oracle.prefill(m, tiny_prompt, 64)
+    base = copy.deepcopy(st)
+    branches, _ = draft_tree(m, st, None, None, 3, 3, levels=lv)
+    sc = copy.deepcopy(base)
+    chain = []
+    for mask, q in lv:
+        toks, _ = oracle.draft(m, sc, mask, q, 1, 0.0)
+        chain += toks
+    assert branches[0] == chain
+    for br in branches:
+        sc = copy.deepcopy(base)
+        sc.window = []
+        z, _ = oracle.forward_row(m, sc, sc.t0, sc.p, "draft", lv[0][0], lv[0][1])
+        for j in range(1, 3):
+            z, _ = oracle.forward_row(m, sc, br[j - 1], sc.p + j, "draft", lv[j][0], lv[j][1])
+            assert br[j] == oracle.argmax_first(z)
+    # one level at every depth is the single-mask tree
+    st1 = copy.deepcopy(base)
+    st2 = copy.deepcopy(base)
+    b1, _ = draft_tree(m, st1, [0, 1, 1, 0], False, 2, 3)
+    b2, _ = draft_tree(m, st2, None, None, 2, 3, levels=[([0, 1, 1, 0], False)] * 3)
+    assert b1 == b2
+
+
+def test_mixed_level_visibility_follows_valid_bits(tiny_model, tiny_prompt):
+    """Layer 0 runs at depth 1 only: at depth 2 a level that runs layer 0
+    must not see the pending token's (never written) layer-0 key there.  The
+    node equals a chain draft where the same slots are invisible."""
+    m = tiny_model
+    lv = [([1, 0, 0, 0], False), ([0, 0, 0, 0], False)]
+    st, _, _ = oracle.prefill(m, tiny_prompt, 64)
+    branches, _ = draft_tree(m, st, None, None, 1, 2, levels=lv)
+    assert st.valid[0] == 0 and st.valid[1] == 1          # the pending token's bits (depth 1 level)
+    st2, _, _ = oracle.prefill(m, tiny_prompt, 64)
+    t1, _ = oracle.draft(m, st2, lv[0][0], False, 1, 0.0)
+    t2, _ = oracle.draft(m, st2, lv[1][0], False, 1, 0.0)
+    assert branches[0] == t1 + t2
+
+
+@pytest.mark.parametrize("bmax", [1, 2, 4])
+@pytest.mark.parametrize("beta", [(1.0, 0.0, 1.0), (10.0, 0.0, 0.2)])
+def test_tree_cascade_is_lossless(tiny_model, tiny_prompt, ar, bmax, beta):
+    pol = oracle.Policy(K=6, cascade=CASCADE, interval=5, tree_width=bmax, latency_beta=beta)
+    toks, recs = oracle.speculative_generate(tiny_model, tiny_prompt, G, pol)
+    assert toks == ar
+    for r in recs:
+        assert 1 <= r["width"] <= bmax and r["width"] * len(r["levels"]) <= 15
+        assert 0 <= r["n"] <= len(r["levels"])
+        assert r["levels"] == sorted(r["levels"], reverse=True)     # precise level first
+
+
+def test_width_one_tree_cascade_is_the_chain_cascade(tiny_model, tiny_prompt):
+    """b_max = 1 and no row costs: the same plans, drafts, acceptances and
+    EMA rates as the chain cascade, round for round."""
+    for beta in [(1.0, 0.0, 1.0), (10.0, 0.0, 0.2)]:
+        tt, rt = oracle.speculative_generate(tiny_model, tiny_prompt, G,
+                                             oracle.Policy(K=6, cascade=CASCADE, interval=5, tree_width=1,
+                                                           latency_beta=beta))
+        tc, rc = oracle.speculative_generate(tiny_model, tiny_prompt, G,
+                                             oracle.Policy(K=6, cascade=CASCADE, interval=5, latency_beta=beta))
+        assert tt == tc
+        assert [r["n"] for r in rt] == [r["n"] for r in rc]
+        assert [r["levels"] for r in rt] == [r["levels"] for r in rc]
+        assert [r["a"] for r in rt] == [r["a"] for r in rc]
+
+
+def test_tree_cascade_uses_width_and_row_costs(tiny_model, tiny_prompt, ar):
+    """Without row costs the router builds trees wider than 1; steep row
+    costs bring it back to width 1."""
+    pol = oracle.Policy(K=6, cascade=CASCADE, interval=5, tree_width=4, latency_beta=(10.0, 0.0, 0.2))
+    _, recs = oracle.speculative_generate(tiny_model, tiny_prompt, G, pol)
+    assert any(r["width"] > 1 for r in recs)
+    steep = tuple(float(r) for r in range(1, 17))
+    pol = oracle.Policy(K=6, cascade=CASCADE, interval=5, tree_width=4, latency_beta=(10.0, 0.0, 0.2),
+                        row_cost=steep)
+    toks, recs = oracle.speculative_generate(tiny_model, tiny_prompt, G, pol)
+    assert toks == ar
+    assert all(r["width"] == 1 for r in recs)
