@@ -184,6 +184,20 @@ int lss_draft(lss_engine* e, const uint8_t* skip_mask, int32_t quant, int32_t k,
 #define LSS_TREE_NODES_MAX 15
 int lss_draft_tree(lss_engine* e, const uint8_t* skip_mask, int32_t quant, int32_t B, int32_t D, int32_t* tokens_out);
 
+/* The same tree with a draft level per depth: the cascade's levels routed
+ * into the tree (CAS-Spec abstract, dynamic tree cascade; CAS-Spec blog
+ * section 2.2, levels).  The nodes of depth j (1 .. D) come from the pass
+ * with skip mask masks[(j - 1) * n_layers ..] (1 = skip) and quant
+ * quants[j - 1] (0, 1 or 2 as in lss_draft): the pending token's row for
+ * j = 1, the rows of the depth j - 1 nodes otherwise.  In a layer, a row
+ * sees the pending token and its branch's node i only where the pass over
+ * them ran that layer (per-layer valid bits by depth, as in a chain window
+ * drafted by several levels).  lss_draft_tree is this call with one level
+ * at every depth.  Errors as lss_draft_tree (LSS_EINVAL for a quant outside
+ * 0..2). */
+int lss_draft_tree_levels(lss_engine* e, const uint8_t* masks, const int32_t* quants, int32_t B, int32_t D,
+                          int32_t* tokens_out);
+
 /* Verify the window in one full-model pass over rows [t0, d1..dk] at
  * positions p..p+k (CLaSp section 3, verification).  drafts == NULL
  * verifies the pending window; otherwise the k host tokens replace it (a
@@ -287,8 +301,12 @@ typedef struct lss_policy {
   int32_t level_exit[LSS_LEVELS_MAX];  /* early-exit tail length per level */
   int32_t level_quant[LSS_LEVELS_MAX]; /* int8 activations per level */
   double beta[3];            /* CASCADE latency model b0 + b1*seq_len + b2*executed_layers */
-  int32_t tree_width;        /* STATIC / DP: > 0 drafts a width-B token tree per round (lss_draft_tree) */
-  int32_t tree_depth;        /* tree depth (0 or 1: depth 1), cut to the tokens still to emit per round */
+  int32_t tree_width;        /* STATIC / DP: > 0 drafts a width-B token tree per round (lss_draft_tree);
+                                CASCADE: > 0 routes the levels into a tree per round, width <= tree_width
+                                chosen by lss_router_plan_tree (lss_draft_tree_levels) */
+  int32_t tree_depth;        /* STATIC / DP tree depth (0 or 1: depth 1), cut to the tokens still to emit */
+  double row_cost[LSS_TREE_NODES_MAX + 1]; /* CASCADE trees: cost factor of a pass over r rows at index
+                                r - 1 (all 0: 1 for every row count) */
 } lss_policy;
 
 typedef struct lss_stats {
@@ -323,6 +341,26 @@ int lss_router_plan(const double* accept_rate, const double* t_hat, int32_t n_le
                     double t_verify, int32_t k_max, int32_t* plan_out);
 int lss_router_update(double* accept_rate, int32_t n_levels, const int32_t* slot_levels,
                       int32_t k, int32_t n_accepted);
+/* Tree routing (the abstract's dynamic tree cascade; our reading): a width
+ * B and draft lengths per level plan_out[n_levels] (index 0 = fastest) for
+ * a token tree whose depths are drafted precise level first.  Expected
+ * accepted nodes E = h (1 + sum_{j>=2} prod_{2<=m<=j} a_level(m)) with
+ * h = 1 - (1 - a_level(1))^B (B independent first candidates); predicted
+ * time = t_verify row_cost[B D] + the depth passes (the first over one row:
+ * t_hat row_cost[0], later ones over B rows: t_hat row_cost[B - 1]);
+ * row_cost NULL means 1.  Maximizes (E + 1) / time over 1 <= B <= b_max and
+ * totals D <= k_max with B D <= nodes_max; ties: fewer nodes, smaller
+ * width, then the order of lss_router_plan.  A total of 0 (width 1) is a
+ * greedy step.  update_tree: EMA update after a tree round whose depths had
+ * levels depth_levels[D] and n nodes accepted along branch `branch` (-1
+ * when n = 0): the first depth counts as accepted only for branch 0 (the
+ * draft's most likely token), later depths along the branch followed.
+ * LSS_EINVAL for sizes out of range. */
+int lss_router_plan_tree(const double* accept_rate, const double* t_hat, int32_t n_levels, double t_verify,
+                         const double* row_cost, int32_t k_max, int32_t b_max, int32_t nodes_max,
+                         int32_t* width_out, int32_t* plan_out);
+int lss_router_update_tree(double* accept_rate, int32_t n_levels, const int32_t* depth_levels, int32_t D,
+                           int32_t n_accepted, int32_t branch);
 int lss_latency_fit(const double* samples, int32_t n, double* beta_out);
 
 /* Measurement: time every launch of one GEMM family with HIP events on the

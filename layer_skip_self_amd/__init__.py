@@ -6,7 +6,7 @@ does not load the library; the first engine call does, and fails loudly if
 it has not been built.
 """
 from .engine import (Engine, LssError, make_config, workspace_bytes, router_plan, router_update,
-                     latency_fit, quantize_rows, make_policy)
+                     router_plan_tree, router_update_tree, latency_fit, quantize_rows, make_policy)
 
 __all__ = ["Engine", "LssError", "make_config", "workspace_bytes", "router_plan", "router_update",
-           "latency_fit", "quantize_rows", "make_policy"]
+           "router_plan_tree", "router_update_tree", "latency_fit", "quantize_rows", "make_policy"]

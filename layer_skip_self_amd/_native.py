@@ -39,7 +39,8 @@ class lss_policy(C.Structure):
                 ("n_skip", C.c_int32), ("interval", C.c_int32), ("n_levels", C.c_int32),
                 ("level_skip", C.c_int32 * LSS_LEVELS_MAX), ("level_exit", C.c_int32 * LSS_LEVELS_MAX),
                 ("level_quant", C.c_int32 * LSS_LEVELS_MAX), ("beta", C.c_double * 3),
-                ("tree_width", C.c_int32), ("tree_depth", C.c_int32)]
+                ("tree_width", C.c_int32), ("tree_depth", C.c_int32),
+                ("row_cost", C.c_double * (LSS_TREE_NODES_MAX + 1))]
 
 
 class lss_stats(C.Structure):
@@ -69,6 +70,8 @@ SIGNATURES = {
                             C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "lss_draft_tree": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint8), C.c_int32, C.c_int32, C.c_int32,
                                  C.POINTER(C.c_int32)]),
+    "lss_draft_tree_levels": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint8), C.POINTER(C.c_int32), C.c_int32,
+                                        C.c_int32, C.POINTER(C.c_int32)]),
     "lss_verify": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32]),
     "lss_accept_and_rollback": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                                           C.POINTER(C.c_int32)]),
@@ -88,6 +91,11 @@ SIGNATURES = {
                                   C.c_int32, C.POINTER(C.c_int32)]),
     "lss_router_update": (C.c_int, [C.POINTER(C.c_double), C.c_int32, C.POINTER(C.c_int32), C.c_int32,
                                     C.c_int32]),
+    "lss_router_plan_tree": (C.c_int, [C.POINTER(C.c_double), C.POINTER(C.c_double), C.c_int32, C.c_double,
+                                       C.POINTER(C.c_double), C.c_int32, C.c_int32, C.c_int32,
+                                       C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
+    "lss_router_update_tree": (C.c_int, [C.POINTER(C.c_double), C.c_int32, C.POINTER(C.c_int32), C.c_int32,
+                                         C.c_int32, C.c_int32]),
     "lss_latency_fit": (C.c_int, [C.POINTER(C.c_double), C.c_int32, C.POINTER(C.c_double)]),
     "lss_profile_kernel": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32]),
     "lss_profile_read": (C.c_int, [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_int64),

@@ -618,7 +618,7 @@ void attention(lss_engine* e, int l, int M, int mode, int pos0, int quant) {
   if (mode == MODE_CAUSAL) { a.lim_base = pos0 + 1; a.lim_step = 1; a.wbase = 0; a.wmask = 0; kmax = pos0 + M; }
   else if (mode == MODE_TREE) { a.lim_base = pos0 + 1; a.lim_step = 0; a.wbase = 0; a.wmask = 0; kmax = pos0 + M; }
   else if (mode == MODE_TREE_DRAFT) {             // last row's slot: pos0 + j + (b0 + M - 1) D
-    a.lim_base = pos0 + 1; a.lim_step = 0; a.wbase = 0; a.wmask = 0;
+    a.lim_base = pos0; a.lim_step = 0; a.wbase = pos0; a.wmask = e->valid[l];   // p + i by valid bit i
     kmax = pos0 + e->tree_step + (e->tree_b0 + M - 1) * e->tree_D + 1;
   }
   else if (mode == MODE_DRAFT) { a.lim_base = e->p; a.lim_step = 0; a.wbase = e->p; a.wmask = e->valid[l]; kmax = pos0 + 1; }
@@ -1329,52 +1329,65 @@ int lss_draft(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t k, floa
   return LSS_OK;
 }
 
-int lss_draft_tree(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t B, int32_t D, int32_t* tokens_out) {
+int lss_draft_tree_levels(lss_engine* e, const uint8_t* masks, const int32_t* quants, int32_t B, int32_t D,
+                          int32_t* tokens_out) {
   if (!e) return LSS_EINVAL;
   const GemvScope gv(e, true);
   const auto& c = e->cfg;
+  const int L = c.n_layers;
   if (!e->have_seq || e->pending_accept || e->win != 0)
     return fail(e, LSS_ESTATE, "draft_tree: needs a prefilled sequence, no pending accept and an empty window");
-  if (!mask || !tokens_out || B < 1 || B > TOPB_MAX || B > c.vocab || D < 1 || quant < 0 || quant > 2)
+  if (!masks || !quants || !tokens_out || B < 1 || B > TOPB_MAX || B > c.vocab || D < 1)
     return fail(e, LSS_EINVAL, "draft_tree: bad arguments (1 <= B <= 8, D >= 1)");
   if (e->inv_t > 0.f) return fail(e, LSS_EINVAL, "draft_tree: tree acceptance is greedy; sampling is on");
-  if (quant == 2 && e->w8.empty()) return fail(e, LSS_ESTATE, "draft_tree: int8 weights not attached");
   const long nodes = (long)B * D;
   if (nodes > LSS_TREE_NODES_MAX || nodes + 1 > c.max_rows || nodes > kWinMax)
     return fail(e, LSS_ECAPACITY, "draft_tree: B * D above LSS_TREE_NODES_MAX or max_rows - 1");
+  for (int j = 0; j < D; ++j) {
+    if (quants[j] < 0 || quants[j] > 2) return fail(e, LSS_EINVAL, "draft_tree: quant must be 0, 1 or 2");
+    if (quants[j] == 2 && e->w8.empty()) return fail(e, LSS_ESTATE, "draft_tree: int8 weights not attached");
+  }
   if (e->p + nodes + 1 > c.max_seq) return fail(e, LSS_ECAPACITY, "draft_tree: KV capacity exceeded");
   static_assert(LSS_TREE_NODES_MAX < ATT_TREE_NODES, "tree nodes must fit the attention kernel's node arrays");
-  // the draft row of the pending token (slot 0, position p), then its top B
-  // as the branches' first nodes (window slots 1 + b D)
-  embed(e, e->tok, 1, hs_row(e, 0, 0), next_gain(e, mask, -1));
+  static_assert(LSS_TREE_NODES_MAX < 32, "tree depths must fit the per-layer valid bits");
+  // the draft row of the pending token (slot 0, position p) with the first
+  // depth's level, then its top B as the branches' first nodes (window
+  // slots 1 + b D)
+  const uint8_t* m0 = masks;
+  embed(e, e->tok, 1, hs_row(e, 0, 0), next_gain(e, m0, -1));
   const float* h = hs_row(e, 0, 0);
-  for (int l = 0; l < c.n_layers; ++l) {
-    if (mask[l]) continue;
+  for (int l = 0; l < L; ++l) {
+    if (m0[l]) continue;
     e->valid[l] |= 1u;
-    layer_forward(e, l, 1, h, e->xa, e->pa, hs_row(e, l + 1, 0), next_gain(e, mask, l), MODE_DRAFT, e->p, quant);
+    layer_forward(e, l, 1, h, e->xa, e->pa, hs_row(e, l + 1, 0), next_gain(e, m0, l), MODE_DRAFT, e->p, quants[0]);
     h = hs_row(e, l + 1, 0);
   }
   head(e, 0, 1, 0, e->p, true);
   hipLaunchKernelGGL(k_topb, dim3(1), dim3(TOPB_THREADS), 0, e->stream, (const float*)e->logits, c.vocab, B, D, e->tok);
   // depth j = 1 .. D - 1: node j of branches b0 .. b0 + M - 1 (window slots
-  // 1 + b D + j - 1) through the draft, their argmax nodes j + 1.  Int8
-  // weights draft one row at a time, so one branch per pass there.
+  // 1 + b D + j - 1) through the level of depth j + 1, their argmax nodes
+  // j + 1.  A layer sees position p + i (the pending token, or node i of the
+  // row's branch) only where the pass over depth i ran it: valid bit i of
+  // the layer, set here for depth j.  Int8 weights draft one row at a time,
+  // so one branch per pass there.
   e->tree_D = D;
   auto step = [&](int j, int b0, int M) {
+    const uint8_t* mk = masks + (size_t)j * L;
     e->tree_step = j;
     e->tree_b0 = b0;
-    embed(e, e->tok + 1 + b0 * D + j - 1, M, hs_row(e, 0, 0), next_gain(e, mask, -1), D);
+    embed(e, e->tok + 1 + b0 * D + j - 1, M, hs_row(e, 0, 0), next_gain(e, mk, -1), D);
     const float* hh = hs_row(e, 0, 0);
-    for (int l = 0; l < c.n_layers; ++l) {
-      if (mask[l]) continue;
-      layer_forward(e, l, M, hh, e->xa, e->pa, hs_row(e, l + 1, 0), next_gain(e, mask, l), MODE_TREE_DRAFT, e->p,
-                    quant);
+    for (int l = 0; l < L; ++l) {
+      if (mk[l]) continue;
+      e->valid[l] |= 1u << j;
+      layer_forward(e, l, M, hh, e->xa, e->pa, hs_row(e, l + 1, 0), next_gain(e, mk, l), MODE_TREE_DRAFT, e->p,
+                    quants[j]);
       hh = hs_row(e, l + 1, 0);
     }
     head(e, 0, M, b0, e->p + j, true);
   };
   for (int j = 1; j < D; ++j) {
-    if (quant == 2)
+    if (quants[j] == 2)
       for (int b = 0; b < B; ++b) step(j, b, 1);
     else
       step(j, 0, B);
@@ -1390,6 +1403,16 @@ int lss_draft_tree(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t B,
   e->win = (int)nodes;
   e->tree = B;
   return LSS_OK;
+}
+
+int lss_draft_tree(lss_engine* e, const uint8_t* mask, int32_t quant, int32_t B, int32_t D, int32_t* tokens_out) {
+  if (!e) return LSS_EINVAL;
+  const int L = e->cfg.n_layers;
+  const bool ok = mask && D >= 1 && D <= kWinMax;
+  std::vector<uint8_t> masks(ok ? (size_t)D * L : 0);
+  std::vector<int32_t> quants(ok ? D : 0, quant);
+  for (int j = 0; ok && j < D; ++j) std::copy(mask, mask + L, masks.begin() + (size_t)j * L);
+  return lss_draft_tree_levels(e, ok ? masks.data() : nullptr, ok ? quants.data() : nullptr, B, D, tokens_out);
 }
 
 int lss_verify(lss_engine* e, const int32_t* drafts, int32_t k) {
@@ -1915,12 +1938,16 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
   if (pol->mode != LSS_MODE_AR && (pol->k_max < 0 || pol->k_max > std::min(kWinMax, c.max_rows - 1)))
     return fail(e, LSS_EINVAL, "generate: k_max out of range");
   if (pol->mode == LSS_MODE_STATIC && !pol->static_mask) return fail(e, LSS_EINVAL, "generate: static mask missing");
-  if (pol->tree_width < 0 || pol->tree_width > TOPB_MAX ||
-      (pol->tree_width > 0 && pol->mode != LSS_MODE_STATIC && pol->mode != LSS_MODE_DP))
-    return fail(e, LSS_EINVAL, "generate: tree_width must be 0..8 and needs the static or DP mode");
+  if (pol->tree_width < 0 || pol->tree_width > TOPB_MAX || (pol->tree_width > 0 && pol->mode == LSS_MODE_AR))
+    return fail(e, LSS_EINVAL, "generate: tree_width must be 0..8 and needs the static, DP or cascade mode");
   const int tree_depth = std::max(1, pol->tree_depth);   // 0: depth 1
-  if (pol->tree_width > 0 && (pol->tree_depth < 0 || (long)pol->tree_width * tree_depth > LSS_TREE_NODES_MAX))
+  if (pol->tree_width > 0 && pol->mode != LSS_MODE_CASCADE &&
+      (pol->tree_depth < 0 || (long)pol->tree_width * tree_depth > LSS_TREE_NODES_MAX))
     return fail(e, LSS_EINVAL, "generate: tree_depth must be >= 0 with tree_width * tree_depth <= 15");
+  bool row_cost_set = false;
+  for (int r = 0; r <= LSS_TREE_NODES_MAX; ++r) row_cost_set |= pol->row_cost[r] != 0.0;
+  for (int r = 0; row_cost_set && r <= LSS_TREE_NODES_MAX; ++r)
+    if (!(pol->row_cost[r] > 0.0)) return fail(e, LSS_EINVAL, "generate: row_cost entries must all be > 0 (or all 0)");
   if ((pol->mode == LSS_MODE_DP || pol->mode == LSS_MODE_CASCADE) && pol->interval < 1)
     return fail(e, LSS_EINVAL, "generate: interval < 1");
   if (pol->mode == LSS_MODE_CASCADE) {
@@ -1979,6 +2006,53 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
         rc = lss_draft(e, masks[0].data(), pol->quant, k, pol->exit_tau, toks.data(), &kd);
         if (rc) return rc;
       }
+    } else if (pol->mode == LSS_MODE_CASCADE && pol->tree_width > 0) {
+      // the levels routed into a token tree: width and k per level from the
+      // tree router, depths drafted precise level first
+      std::vector<double> t_hat(nlev);
+      for (int v = 0; v < nlev; ++v) {
+        int depth = 0;
+        for (int l = 0; l < L; ++l) depth += masks[v][l] ? 0 : 1;
+        t_hat[v] = router::predict(pol->beta, e->p, depth);
+      }
+      const double t_ver = router::predict(pol->beta, e->p, L);
+      std::vector<int32_t> plan(nlev);
+      int32_t B = 1;
+      router::plan_tree(acc_rate.data(), t_hat.data(), nlev, t_ver, row_cost_set ? pol->row_cost : nullptr,
+                        pol->k_max, pol->tree_width, std::min(LSS_TREE_NODES_MAX, c.max_rows - 1), &B, plan.data());
+      for (int v = nlev - 1; v >= 0; --v)
+        for (int i = 0; i < plan[v] && (int)slot_levels.size() < budget; ++i) slot_levels.push_back(v);
+      const int D = (int)slot_levels.size();
+      int branch = -1;
+      if (D > 0) {
+        std::vector<uint8_t> dm((size_t)D * L);
+        std::vector<int32_t> dq(D);
+        for (int j = 0; j < D; ++j) {
+          std::copy(masks[slot_levels[j]].begin(), masks[slot_levels[j]].end(), dm.begin() + (size_t)j * L);
+          dq[j] = pol->level_quant[slot_levels[j]];
+        }
+        rc = lss_draft_tree_levels(e, dm.data(), dq.data(), B, D, toks.data());
+        if (rc) return rc;
+      }
+      const int k = e->win;
+      rc = lss_verify(e, nullptr, k);
+      if (rc) return rc;
+      int n = 0, bonus = 0;
+      rc = lss_accept_and_rollback(e, &n, &bonus, acc.data());
+      if (rc) return rc;
+      if (n > 0)                                        // the branch followed: its first node was emitted
+        for (int b = 0; b < B; ++b)
+          if (toks[(size_t)b * D] == acc[0]) branch = b;
+      for (int i = 0; i <= n && emitted < n_gen; ++i) out[emitted++] = acc[i];
+      st.rounds++;
+      st.drafted += k;
+      st.accepted += n;
+      router::update_tree(acc_rate.data(), nlev, slot_levels.data(), D, n, branch);
+      if (st.rounds % pol->interval == 0) {
+        rc = select();
+        if (rc) return rc;
+      }
+      continue;
     } else if (pol->mode == LSS_MODE_CASCADE) {
       std::vector<double> t_hat(nlev);
       for (int v = 0; v < nlev; ++v) {
@@ -2166,6 +2240,27 @@ int lss_router_update(double* a, int32_t n_levels, const int32_t* slot_levels, i
   for (int i = 0; i < k; ++i)
     if (slot_levels[i] < 0 || slot_levels[i] >= n_levels) return LSS_EINVAL;
   router::update(a, n_levels, slot_levels, k, n);
+  return LSS_OK;
+}
+
+int lss_router_plan_tree(const double* a, const double* t_hat, int32_t n_levels, double t_verify,
+                         const double* row_cost, int32_t k_max, int32_t b_max, int32_t nodes_max,
+                         int32_t* width_out, int32_t* plan_out) {
+  if (!a || !t_hat || !plan_out || !width_out || n_levels < 1 || n_levels > LSS_LEVELS_MAX || k_max < 0 ||
+      k_max > kWinMax || b_max < 1 || b_max > TOPB_MAX || nodes_max < 1 || nodes_max > LSS_TREE_NODES_MAX)
+    return LSS_EINVAL;
+  router::plan_tree(a, t_hat, n_levels, t_verify, row_cost, k_max, b_max, nodes_max, width_out, plan_out);
+  return LSS_OK;
+}
+
+int lss_router_update_tree(double* a, int32_t n_levels, const int32_t* depth_levels, int32_t D, int32_t n,
+                           int32_t branch) {
+  if (!a || n_levels < 1 || n_levels > LSS_LEVELS_MAX || D < 0 || n < 0 || n > D || (D > 0 && !depth_levels) ||
+      branch < -1 || branch >= TOPB_MAX || (n > 0) != (branch >= 0))
+    return LSS_EINVAL;
+  for (int i = 0; i < D; ++i)
+    if (depth_levels[i] < 0 || depth_levels[i] >= n_levels) return LSS_EINVAL;
+  router::update_tree(a, n_levels, depth_levels, D, n, branch);
   return LSS_OK;
 }
 

@@ -1597,14 +1597,16 @@ __global__ __launch_bounds__(G8_THREADS) void k_gemv8(GemmArgs ga) {
 // nothing; each row's own key/value enters the merge directly.
 //
 // Tree launches (a token tree of width B and depth D; node (b, j) is the
-// j-th token of branch b, at position pos0 + j): a row of depth j sees
-// positions u <= pos0 + j, and inside the chunks that hold positions
-// pos0 + 1 .. pos0 + j its own branch's nodes 1..j stand in for the keys and
-// values there (per-row substitutes), so its scores, chunk partials and
-// merge are those of the plain step at pos0 + j after that branch's first j
-// tokens, bit for bit.  Nodes that are rows of the launch are rotated from
-// its projection output; a draft step's earlier nodes come from their cache
-// slots.
+// j-th token of branch b, at position pos0 + j): a verify row of depth j
+// sees positions u <= pos0 + j; a draft row of depth j sees the committed
+// prefix u < pos0 and pos0 + i (i <= j) where bit i of wmask is set (the
+// pass over depth i ran this layer: the levels of a cascade may differ by
+// depth).  Inside the chunks that hold positions pos0 + 1 .. pos0 + j the
+// row's own branch's nodes 1..j stand in for the keys and values there
+// (per-row substitutes), so its scores, chunk partials and merge are those
+// of the plain step at pos0 + j after that branch's first j tokens, bit for
+// bit.  Nodes that are rows of the launch are rotated from its projection
+// output; a draft step's earlier nodes come from their cache slots.
 #define ATT_CH 64
 #define ATT_QB 32
 #define ATT_THREADS 512
@@ -1900,7 +1902,10 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, int z, int zp)
         if (h2 == 1 && !has_c) break;                  // wave-uniform
         const int qi = h2 ? qc : qb;
         const int m = (q0 + qi) / G;
-        const int lim = TREE ? a.lim_base + att_tree_depth(a, m) : a.lim_base + m * a.lim_step;
+        // tree verify rows see p .. p + depth; tree draft rows the committed
+        // prefix, and p + i where the window bit i of the layer is set
+        const int lim = TREE ? (a.tree_step > 0 ? a.lim_base : a.lim_base + att_tree_depth(a, m))
+                             : a.lim_base + m * a.lim_step;
         const int wo = pos - a.wbase;
         const bool vis = pos < lim || (wo >= 0 && wo < 32 && ((a.wmask >> wo) & 1u));
         const float s = (vis && pos < a.max_seq) ? __fmul_rn(h2 ? dc : da, a.scale) : -INFINITY;

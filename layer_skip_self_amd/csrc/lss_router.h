@@ -17,5 +17,11 @@ double predict(const double* beta, int seq_len, int depth);
 void plan(const double* a, const double* t_hat, int n_levels, double t_verify, int k_max, int32_t* out);
 void update(double* a, int n_levels, const int32_t* slot_levels, int k, int n);
 bool fit(const double* samples, int n, double* beta);
+// tree routing: width and k per level of the next tree round (see
+// lss_router_plan_tree in lss.h); row_cost[r - 1] scales a pass over r rows
+// (nullptr: 1)
+void plan_tree(const double* a, const double* t_hat, int n_levels, double t_verify, const double* row_cost,
+               int k_max, int b_max, int nodes_max, int32_t* width_out, int32_t* out);
+void update_tree(double* a, int n_levels, const int32_t* depth_levels, int D, int n, int branch);
 
 }  // namespace router

@@ -134,14 +134,21 @@ class Engine:
                                        out.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(done)), "lss_draft")
         return out[:done.value].tolist()
 
-    def draft_tree(self, skip_mask, quant=0, B=2, D=1):
+    def draft_tree(self, skip_mask, quant=0, B=2, D=1, levels=None):
         """Token tree of width B and depth D: the draft's B most likely next
-        tokens, each extended greedily by D - 1 more.  Returns the branches
+        tokens, each extended greedily by D - 1 more.  ``levels``: D pairs
+        (skip mask, quant), the draft level of each depth (then
+        ``skip_mask`` and ``quant`` are ignored).  Returns the branches
         ([B][D] token lists)."""
-        m, mp = _u8(skip_mask)
         out = np.zeros(max(B * D, 1), np.int32)
-        self._check(self.lib.lss_draft_tree(self.h, mp, int(quant), int(B), int(D),
-                                            out.ctypes.data_as(C.POINTER(C.c_int32))), "lss_draft_tree")
+        op = out.ctypes.data_as(C.POINTER(C.c_int32))
+        if levels is None:
+            m, mp = _u8(skip_mask)
+            self._check(self.lib.lss_draft_tree(self.h, mp, int(quant), int(B), int(D), op), "lss_draft_tree")
+        else:
+            m, mp = _u8(np.asarray([lv[0] for lv in levels], np.uint8).reshape(-1))
+            q, qp = _i32([int(lv[1]) for lv in levels])
+            self._check(self.lib.lss_draft_tree_levels(self.h, mp, qp, int(B), int(D), op), "lss_draft_tree_levels")
         return [out[b * D:(b + 1) * D].tolist() for b in range(B)]
 
     def verify(self, drafts=None, k=None):
@@ -340,6 +347,10 @@ def make_policy(policy, n_layers):
         pol.beta[i] = float(beta[i])
     pol.tree_width = int(policy.get("tree_width", 0))
     pol.tree_depth = int(policy.get("tree_depth", 1))
+    rc = policy.get("row_cost")
+    if rc is not None:
+        for i, v in enumerate(rc):
+            pol.row_cost[i] = float(v)
     return pol
 
 
@@ -364,6 +375,34 @@ def router_update(accept_rate, slot_levels, n_accepted):
     rc = lib.lss_router_update(a, nl, lv, len(slot_levels), int(n_accepted))
     if rc != 0:
         raise LssError("lss_router_update", rc)
+    return list(a)
+
+
+def router_plan_tree(accept_rate, t_hat, t_verify, row_cost, k_max, b_max, nodes_max=N.LSS_TREE_NODES_MAX):
+    """(width, draft length per level) of the next tree round
+    (``lss_router_plan_tree``); row_cost None: 1 for every row count."""
+    lib = N.load()
+    nl = len(accept_rate)
+    a = (C.c_double * nl)(*accept_rate)
+    t = (C.c_double * nl)(*t_hat)
+    rcp = None if row_cost is None else (C.c_double * (N.LSS_TREE_NODES_MAX + 1))(*row_cost)
+    out = (C.c_int32 * nl)()
+    width = C.c_int32()
+    rc = lib.lss_router_plan_tree(a, t, nl, float(t_verify), rcp, int(k_max), int(b_max), int(nodes_max),
+                                  C.byref(width), out)
+    if rc != 0:
+        raise LssError("lss_router_plan_tree", rc)
+    return int(width.value), list(out)
+
+
+def router_update_tree(accept_rate, depth_levels, n_accepted, branch):
+    lib = N.load()
+    nl = len(accept_rate)
+    a = (C.c_double * nl)(*accept_rate)
+    lv = (C.c_int32 * max(1, len(depth_levels)))(*depth_levels)
+    rc = lib.lss_router_update_tree(a, nl, lv, len(depth_levels), int(n_accepted), int(branch))
+    if rc != 0:
+        raise LssError("lss_router_update_tree", rc)
     return list(a)
 
 

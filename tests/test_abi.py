@@ -95,6 +95,40 @@ def test_router_update_matches_oracle_bitwise():
         assert lss.router_update(a, levels, n) == oracle.update_cascade(a, levels, n)
 
 
+def test_router_plan_tree_matches_oracle():
+    """The tree router of the library against the oracle's, with and without
+    row costs (random, rounded and extreme rates; several node budgets)."""
+    rng = np.random.default_rng(17)
+    for i in range(300):
+        nl = int(rng.integers(1, 4))
+        a = list(rng.uniform(0, 1, nl))
+        if rng.uniform() < 0.2:
+            a = [float(round(x, 1)) for x in a]
+        t = list(rng.uniform(0.05, 1.0, nl))
+        tv = float(rng.uniform(0.5, 2.0))
+        k = int(rng.integers(0, 9))
+        bmax = int(rng.integers(1, 9))
+        nodes = int(rng.integers(1, 16))
+        rc = None if i % 2 else [1.0 + float(rng.uniform(0, 0.2)) * r for r in range(16)]
+        assert lss.router_plan_tree(a, t, tv, rc, k, bmax, nodes) == oracle.plan_tree(a, t, tv, rc, k, bmax, nodes)
+
+
+def test_router_update_tree_matches_oracle_bitwise():
+    rng = np.random.default_rng(18)
+    for _ in range(300):
+        nl = 3
+        a = list(rng.uniform(0, 1, nl))
+        D = int(rng.integers(0, 9))
+        levels = sorted((int(x) for x in rng.integers(0, nl, D)), reverse=True)
+        n = int(rng.integers(0, D + 1))
+        branch = int(rng.integers(0, 4)) if n else -1
+        assert lss.router_update_tree(a, levels, n, branch) == oracle.update_tree(a, levels, n, branch)
+    with pytest.raises(lss.LssError):
+        lss.router_update_tree([0.5], [0, 0], 1, -1)          # n > 0 needs the branch followed
+    with pytest.raises(lss.LssError):
+        lss.router_plan_tree([0.5], [0.1], 1.0, None, 8, 9)   # width above 8
+
+
 def test_latency_fit_matches_oracle():
     rng = np.random.default_rng(9)
     samples = [(s, d, 0.3 + 2e-4 * s + 0.04 * d + rng.normal(0, 0.01))

@@ -1,5 +1,7 @@
 """GPU parity of token-tree drafting (width B, depth D) on the 4-layer
 float32 model, and its losslessness at the 8B shape (in test_gpu_llama3_8b).
+Trees whose depths are drafted by different levels (the cascade routed into
+the tree) and the tree-cascade generation loop are checked the same way.
 
 Against the oracle: the emitted tokens, the rounds and accepted counts, the
 first round's branches (the draft's top B, each extended greedily) and the
@@ -169,7 +171,114 @@ def test_tree_error_paths(tiny):
     n, b, emitted = oracle.accept_tree(st, logits, states, oc, kv)
     assert got == (n, b, emitted)
     with pytest.raises(LssError):
+        eng.generate(prompt, 8, {"mode": "ar", "tree_width": 2})
+    with pytest.raises(LssError):
         eng.generate(prompt, 8, {"mode": "cascade", "k_max": 4, "tree_width": 2, "interval": 4,
-                                 "levels": [(2, 0, False)]})
+                                 "levels": [(2, 0, False)], "row_cost": [1.0, -1.0] + [1.0] * 14})
+    eng.prefill(prompt)
+    with pytest.raises(LssError):
+        eng.draft_tree(None, B=2, D=2, levels=[([0, 1, 1, 0], 0), ([0, 1, 1, 0], 3)])   # quant 3
     with pytest.raises(LssError):
         eng.generate(prompt, 8, {"mode": "static", "skip": (1,), "k_max": 1, "tree_width": 4, "tree_depth": 4})
+
+
+# ---- draft levels per depth, and the cascade routed into the tree
+
+LEVELS = [([0, 0, 1, 0], 1), ([1, 1, 1, 0], 0), ([0, 1, 1, 1], 0)]
+
+
+def _oracle_tree_rows(model, st, levels, branches):
+    """The oracle's draft rows of a tree: whether no row has a near-tie
+    (top-B at the root, top-1 along each branch), and each branch's last
+    draft row's logits (the pass over depth D - 1)."""
+    import copy
+    B = len(branches)
+    s0 = copy.deepcopy(st)
+    z, _ = oracle.forward_row(model, s0, s0.t0, s0.p, "draft", levels[0][0], levels[0][1])
+    srt = np.sort(z)[::-1]
+    ok = np.min(srt[:B] - srt[1:B + 1]) > 1e-5
+    root_valid = list(s0.valid)
+    last = []
+    for br in branches:
+        sb = copy.deepcopy(s0)
+        sb.valid = list(root_valid)
+        for j in range(1, len(br)):
+            zz, _ = oracle.forward_row(model, sb, br[j - 1], sb.p + j, "draft", levels[j][0], levels[j][1])
+            s2 = np.sort(zz)[::-1]
+            ok = ok and s2[0] - s2[1] > 1e-5
+        last.append(zz)
+    return ok, np.stack(last)
+
+
+@pytest.mark.parametrize("levels", [LEVELS, [([1, 0, 0, 0], 0), ([0, 0, 0, 0], 0)],
+                                    [([0, 1, 1, 0], 0), ([0, 1, 0, 1], 1), ([1, 0, 1, 0], 0), ([0, 0, 1, 1], 0)]],
+                         ids=["three_levels", "layer0_from_depth2", "four_levels"])
+def test_mixed_level_tree_matches_oracle(tiny, levels):
+    """Branches of a tree drafted by a level per depth, the last draft
+    pass's logits, the tree verify's logits and the acceptance, against the
+    oracle.  In the second case layer 0 runs from depth 2 only, so the
+    pending token's (unwritten) layer-0 key must stay invisible there: the
+    depth-2 draft rows' logits would move otherwise."""
+    eng, model, prompt = tiny["eng"], tiny["model"], tiny["prompt"]
+    B, D = 3, len(levels)
+    eng.prefill(prompt)
+    branches = eng.draft_tree(None, B=B, D=D, levels=levels)
+    zd = eng.read_logits(B)
+    st, _, _ = oracle.prefill(model, prompt, 256)
+    lv = [(m, bool(q)) for m, q in levels]
+    ref = oracle.draft_tree(model, st, None, None, B, D, levels=lv)[0]
+    st0, _, _ = oracle.prefill(model, prompt, 256)
+    ok, zlast = _oracle_tree_rows(model, st0, lv, ref)
+    assert ok
+    assert branches == ref
+    derr = float(np.max(np.abs(zd - zlast)))
+    print(f"last draft pass: max error {derr:.3g}")
+    assert derr <= 1e-4
+    eng.verify(k=B * D)
+    zg = eng.read_logits(1 + B * D)
+    logits, states, obr, kv = oracle.verify_tree(model, st)
+    assert float(np.max(np.abs(zg - logits))) <= 1e-4
+    n, b, emitted = oracle.accept_tree(st, logits, states, obr, kv)
+    assert eng.accept() == (n, b, emitted)
+
+
+def test_one_level_per_depth_is_the_single_mask_tree(tiny):
+    eng, prompt = tiny["eng"], tiny["prompt"]
+    mask = [0, 1, 1, 0]
+    out = []
+    for lv in (None, [(mask, 0)] * 3):
+        eng.prefill(prompt)
+        br = eng.draft_tree(mask, 0, 3, 3) if lv is None else eng.draft_tree(None, B=3, D=3, levels=lv)
+        eng.verify(k=9)
+        out.append((br, eng.read_logits(10), eng.accept()))
+    assert out[0][0] == out[1][0]
+    assert np.array_equal(out[0][1], out[1][1])
+    assert out[0][2] == out[1][2]
+
+
+CASCADE = [(3, 1, False), (1, 0, True), (0, 0, True)]
+
+
+@pytest.mark.parametrize("bmax,beta,steep", [(1, (1.0, 0.0, 1.0), False), (2, (1.0, 0.0, 1.0), False),
+                                             (4, (10.0, 0.0, 0.2), False), (4, (0.0, 0.0, 1.0), False),
+                                             (4, (10.0, 0.0, 0.2), True)])
+def test_tree_cascade_matches_oracle_and_greedy(tiny, bmax, beta, steep):
+    """The generation loop with the levels routed into trees: tokens equal
+    the greedy run and the oracle's, and so do the rounds, drafted nodes and
+    accepted counts (the router's plans and updates agree round for round)."""
+    eng = tiny["eng"]
+    rc = tuple(float(r) for r in range(1, 17)) if steep else None
+    gp = {"mode": "cascade", "k_max": 6, "interval": 5, "levels": CASCADE, "beta": beta, "tree_width": bmax}
+    if rc is not None:
+        gp["row_cost"] = rc
+    toks, st = eng.generate(tiny["prompt"], G, gp)
+    ref, recs = oracle.speculative_generate(tiny["model"], tiny["prompt"], G,
+                                            oracle.Policy(K=6, cascade=CASCADE, interval=5, tree_width=bmax,
+                                                          latency_beta=beta, row_cost=rc))
+    wide = sum(1 for r in recs if r["width"] > 1)
+    print(f"bmax {bmax} beta {beta} steep {steep}: {st}, {wide} rounds wider than 1")
+    assert toks == tiny["ar"]
+    assert toks == ref
+    assert st["rounds"] == len(recs)
+    assert st["accepted"] == sum(r["n"] for r in recs)
+    assert st["drafted"] == sum(r["k"] for r in recs)
