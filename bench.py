@@ -108,6 +108,16 @@ WORKLOADS = {
                                             "decode_kernel": "mfma"},
                                     desc="Llama-3-8B shape, 8 sequences x (prompt 1024, 256 generated), static "
                                          "skip of layers 1,3,..,31 shared by all, K 4"),
+    # The same levels routed into token trees of width <= 4 (the tree
+    # router prices each pass by its row count, factors measured on this
+    # engine's verify), verify rows on the MFMA GEMM.
+    "cascade_tree_8b": dict(shape="llama3_8b", prompt=(128, 512, 2048), gen=256,
+                            policy={"mode": "cascade", "k_max": 8, "interval": 32, "tree_width": 4,
+                                    "levels": [(22, 4, False), (10, 0, True), (0, 0, True)],
+                                    "decode_kernel": "mfma_verify"},
+                            desc="Llama-3-8B shape, CAS-Spec cascade levels as cascade_8b routed into token "
+                                 "trees (width <= 4, DyTC tree router with measured row costs), K <= 8, "
+                                 "prompts 128, 512, 2048 with 256 generated each"),
     "cascade_8b": dict(shape="llama3_8b", prompt=(128, 512, 2048), gen=256,
                        policy={"mode": "cascade", "k_max": 8, "interval": 32,
                                "levels": [(22, 4, False), (10, 0, True), (0, 0, True)]},
@@ -150,7 +160,8 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
                         cascade=list(policy["levels"]) if policy["mode"] == "cascade" else None,
                         latency_beta=tuple(policy.get("beta", (1.0, 0.0, 1.0))),
                         temperature=float(policy.get("temperature", 0.0)), seed=int(policy.get("seed", 0)),
-                        tree_width=int(policy.get("tree_width", 0)), tree_depth=int(policy.get("tree_depth", 1)))
+                        tree_width=int(policy.get("tree_width", 0)), tree_depth=int(policy.get("tree_depth", 1)),
+                        row_cost=tuple(policy["row_cost"]) if policy.get("row_cost") else None)
     sample = np.asarray(prompt[:n_prompt])
     t0 = time.perf_counter()
     toks, recs = oracle.speculative_generate(model, sample, n_tokens, pol)
@@ -358,10 +369,15 @@ def main():
         depths = sorted({L - lv[0] for lv in policy["levels"]} | {L})
         cal_lens = tuple(n for n in (128, 512, 1024, 2048) if n + 40 <= max_seq)
         cal_prompt = lss_synth.make_prompt(shape, max(cal_lens), seed=shape.prompt_seed + 99)
+        eng.set_decode_kernel(policy["decode_kernel"])
         beta, samples, err = eng.calibrate_latency(cal_prompt, cal_lens, depths)
         policy["beta"] = beta
         latency = {"beta": [float(b) for b in beta], "seq_lens": list(cal_lens), "depths": depths,
                    "samples": len(samples), "max_rel_err": round(err, 4)}
+        if policy.get("tree_width"):
+            rc = eng.calibrate_row_cost(cal_prompt[:min(cal_lens[-1], 1024)])
+            policy["row_cost"] = rc
+            latency["row_cost"] = [round(x, 4) for x in rc]
     runs = [(pol, i) for pol in policies for i in range(len(prompts))]   # (policy, prompt index)
 
     def run(pol, prompt):

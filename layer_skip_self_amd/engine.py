@@ -214,6 +214,32 @@ class Engine:
         err = max(abs(beta[0] + beta[1] * s + beta[2] * d - t) / t for s, d, t in samples)
         return beta, samples, err
 
+    def calibrate_row_cost(self, prompt, max_rows=16, reps=5, seed=0):
+        """Cost factors of a pass over r rows for the tree router
+        (``row_cost`` of a cascade tree policy): the median time of a
+        teacher-forced verify of r rows (the pending token and r - 1 seeded
+        random drafts) over the median one-row verify, r = 1 .. max_rows,
+        each timed with HIP events recorded on the engine stream after one
+        untimed repetition.  Returns the list of max_rows factors."""
+        import torch
+        rng = np.random.default_rng(seed)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        med = []
+        for r in range(1, max_rows + 1):
+            self.prefill(list(prompt))
+            times = []
+            for i in range(reps + 1):
+                drafts = rng.integers(0, self.shape.vocab, r - 1).astype(np.int32)
+                ev0.record(self.stream)
+                self.verify(drafts=drafts)
+                ev1.record(self.stream)
+                ev1.synchronize()
+                if i:
+                    times.append(ev0.elapsed_time(ev1))
+                self.accept()
+            med.append(float(np.median(times)))
+        return [m / med[0] for m in med]
+
     def generate(self, prompt, n_gen, policy):
         """Prefill + decoding of n_gen tokens under ``policy`` (``make_policy``;
         its ``temperature`` / ``seed`` select greedy decoding or sampling)."""

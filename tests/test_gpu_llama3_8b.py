@@ -55,13 +55,20 @@ def test_speculative_equals_greedy_bitwise_8b(gpu8b):
     eng, prompt = gpu8b["eng"], gpu8b["prompt"]
     G = 72
     ar, _ = eng.generate(prompt, G, {"mode": "ar"})
-    for pol in (BENCH_POLICY,
-                {"mode": "static", "k_max": 8, "skip": tuple(range(1, 32, 2)), "quant": True},
-                {"mode": "cascade", "k_max": 8, "interval": 16, "beta": (1.0, 0.0, 0.1),
-                 "levels": [(22, 4, False), (10, 0, True), (0, 0, True)]}):
-        toks, st = eng.generate(prompt, G, pol)
-        assert toks == ar, pol
-        assert 0 <= st["accepted"] <= st["drafted"]
+    cascade = {"mode": "cascade", "k_max": 8, "interval": 16, "beta": (1.0, 0.0, 0.1),
+               "levels": [(22, 4, False), (10, 0, True), (0, 0, True)]}
+    try:
+        for pol in (BENCH_POLICY,
+                    {"mode": "static", "k_max": 8, "skip": tuple(range(1, 32, 2)), "quant": True},
+                    cascade,
+                    dict(cascade, tree_width=4),                          # levels routed into trees
+                    dict(cascade, tree_width=3, decode_kernel="mfma_verify")):
+            toks, st = eng.generate(prompt, G, pol)
+            print(pol.get("tree_width", 0), st)
+            assert toks == ar, pol
+            assert 0 <= st["accepted"] <= st["drafted"]
+    finally:
+        eng.set_decode_kernel("vector")
 
 
 @pytest.mark.parametrize("grid", [0, 2])
