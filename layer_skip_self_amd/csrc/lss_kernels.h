@@ -1610,10 +1610,6 @@ __global__ __launch_bounds__(G8_THREADS) void k_gemv8(GemmArgs ga) {
 #define ATT_CH 64
 #define ATT_QB 32
 #define ATT_THREADS 512
-// row stride (floats) of the LDS key / value tile: 16-byte rows for vector
-// stores and score reads, rows 4 banks apart (a key per lane reads without
-// bank conflicts)
-#define ATT_LD (HD + 4)
 
 struct AttnArgs {
   const float* qkv; int ldqkv;     // [M][(Hq + 2 Hkv) hd] projection output
@@ -1703,106 +1699,66 @@ template <> __device__ __forceinline__ float4 ld4<uint16_t>(const uint16_t* p) {
                      __uint_as_float(v.y & 0xffff0000u));
 }
 
-// A 64-position tile of the layer cache for one kv head, issued as independent
-// 4-element loads (positions past the capacity read the last row; the
-// visibility mask never selects them).
-template <typename KT, int HD>
-struct AttTile {
-  static constexpr int NV = ATT_CH * HD / 4 / ATT_THREADS;   // float4 per thread
-  float4 v[NV];
-  __device__ __forceinline__ void load(const KT* cache, int u0, int max_seq) {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int f = threadIdx.x + j * ATT_THREADS;
-      const int u = f / (HD / 4), d4 = f % (HD / 4);
-      const int pos = min(u0 + u, max_seq - 1);
-      v[j] = ld4<KT>(cache + (size_t)pos * HD + d4 * 4);
-    }
-  }
-  __device__ __forceinline__ void store(float (*t)[ATT_LD]) const {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int f = threadIdx.x + j * ATT_THREADS;
-      const int u = f / (HD / 4), d4 = f % (HD / 4);
-      *reinterpret_cast<float4*>(&t[u][d4 * 4]) = v[j];
-    }
-  }
-};
+// Transposed sums over groups of 2^LB consecutive lanes (LB = 4: the 16-lane
+// rows; LB = 5: the 32-lane halves): the levels of wave_sum_t below LB.
+// Afterwards v[0] of lane l holds the group total of value wst_index<V>(l);
+// with V < 2^LB the last levels add whole copies, so the lanes whose index
+// in the group is below V hold every value once.
+template <int V, int LB> __device__ __forceinline__ void grp_sum_t(float (&v)[V]) {
+  static_assert(LB == 4 || LB == 5, "16- or 32-lane groups");
+  static_assert(V >= 1 && V <= (1 << LB) && (V & (V - 1)) == 0, "a power of two, at most the group size");
+  const int l = threadIdx.x & 63;
+  const int b2 = (l >> 2) & 1;
+  wst_dpp<LSS_DPP_XOR1, V, V>(v, ((l & 1) ^ b2) != 0);
+  wst_dpp<LSS_DPP_XOR2, (V >= 2 ? V / 2 : 1), V>(v, (((l >> 1) & 1) ^ b2) != 0);
+  wst_dpp<LSS_DPP_HMIRROR, (V >= 4 ? V / 4 : 1), V>(v, b2 != 0);
+  wst_dpp<LSS_DPP_ROR8, (V >= 8 ? V / 8 : 1), V>(v, ((l >> 3) & 1) != 0);
+  if constexpr (LB == 5) wst_swap<(V >= 16 ? V / 16 : 1), V, false>(v);
+}
 
-// Replace the tile rows that are rows of this launch by their own keys
-// (rotated) or values, rounded to the cache type; query block 0 also writes
-// them to the cache.  The first ATT_NR_J elements per thread come from
-// registers filled at kernel start (AttNew::load, so their reads overlap the
-// tile loads); any further ones (prefill blocks) are read here.
-#define ATT_NR_J 4
+// The chunk's keys and values stay in the registers they are loaded into:
+// thread t holds dims 4 (t % LPU) .. + 3 of positions t / LPU + UST j
+// (LPU = hd / 4 lanes per position, UST = 512 / LPU, j < NV), one coalesced
+// 16-byte load each.  Rows of this launch whose cache slot lies in the chunk
+// replace their key (rotated at the row's position) and value there, rounded
+// to the cache type; query block 0 writes them to the cache.
+//
+// Per query (row m, head h) and key position u of the chunk:
+//   score: each lane's 4-dim partial q.x k.x + q.y k.y + q.z k.z + q.w k.w
+//          (one FMA chain), then the fixed lane tree of grp_sum_t over the
+//          LPU lanes of the position; scaled by 1/sqrt(hd) where visible;
+//   chunk statistics: max and sum of exp(s - max) over the 64 positions by
+//          wave_max / wave_sum (lane = position);
+//   value sum, per dim: each thread's positions j = 0 .. NV - 1 in order
+//          (one FMA chain), then the lanes of a wave that hold the same dims
+//          (permlane swaps over lane bits 4 and 5 above LPU), then the 8
+//          waves' partials in wave order.
+// Queries run in groups of 4.  None of these orders depends on the rows in
+// the launch, the query block or the group a query falls in.
 template <typename KT, int HD>
-struct AttNew {
-  float xi[ATT_NR_J], xp[ATT_NR_J];   // key element and its rotation partner, or the value element
-  float2 c[ATT_NR_J];
-  int m0, n;                          // first launch row whose slot is in the chunk, elements (rows x HD)
-  __device__ __forceinline__ void load(const AttnArgs& a, int kh, int u0, bool is_v) {
-    // launch rows with a slot in [u0, u0 + ATT_CH): a contiguous range of rows
-    const int lo = a.self_kv ? 0 : att_first_row(a, u0);
-    const int hi = a.self_kv ? 0 : att_first_row(a, u0 + ATT_CH);
-    m0 = lo;
-    n = (hi - lo) * HD;
-    const int off = (is_v ? a.Hq + a.Hkv : a.Hq) + kh;
-#pragma unroll
-    for (int j = 0; j < ATT_NR_J; ++j) {
-      const int i = threadIdx.x + j * ATT_THREADS;
-      if (i < n) {
-        const int m = m0 + i / HD, dd = i % HD;
-        const float* x = a.qkv + (size_t)m * a.ldqkv + (size_t)off * HD;
-        xi[j] = x[dd];
-        if (!is_v) {
-          const bool low = dd < HD / 2;
-          const int pj = low ? dd + HD / 2 : dd - HD / 2;
-          xp[j] = x[pj];
-          c[j] = a.cs[(size_t)att_row_pos(a, m) * (HD / 2) + (low ? dd : pj)];
-        }
-      }
-    }
-  }
-  __device__ __forceinline__ void apply(float (*t)[ATT_LD], const AttnArgs& a, int kh, int u0, int z,
-                                        bool is_v) const {
-    if (n == 0) return;
-    KT* cache = reinterpret_cast<KT*>(is_v ? a.vc : a.kc) + (size_t)kh * a.max_seq * HD;
-#pragma unroll
-    for (int j = 0; j < ATT_NR_J; ++j) {
-      const int i = threadIdx.x + j * ATT_THREADS;
-      if (i < n) {
-        const int m = m0 + i / HD, dd = i % HD;
-        const int slot = att_row_slot(a, m);
-        float v = is_v ? xi[j] : rope_val(xi[j], xp[j], c[j], dd < HD / 2);
-        v = kv_round<KT>(v);
-        if (z == 0) st_elem<KT>(cache, (size_t)slot * HD + dd, v);
-        t[slot - u0][dd] = v;
-      }
-    }
-    const int off = (is_v ? a.Hq + a.Hkv : a.Hq) + kh;
-    for (int i = threadIdx.x + ATT_NR_J * ATT_THREADS; i < n; i += ATT_THREADS) {
-      const int m = m0 + i / HD, dd = i % HD;
-      const int slot = att_row_slot(a, m);
-      const float* x = a.qkv + (size_t)m * a.ldqkv + (size_t)off * HD;
-      const int rp = att_row_pos(a, m);
-      float v = is_v ? x[dd] : rope_elem(x, a.cs + (size_t)rp * (HD / 2), dd, HD / 2);
-      v = kv_round<KT>(v);
-      if (z == 0) st_elem<KT>(cache, (size_t)slot * HD + dd, v);
-      t[slot - u0][dd] = v;
-    }
-  }
+struct AttLayout {
+  static constexpr int LPU = HD / 4;                       // lanes per position
+  static constexpr int LB = LPU == 32 ? 5 : 4;
+  static constexpr int NV = ATT_CH * HD / 4 / ATT_THREADS;  // positions per thread
+  static constexpr int UST = ATT_THREADS / LPU;            // position stride of a thread
+  static constexpr int UPW = 64 / LPU;                      // positions per wave instruction
+  static_assert(LPU == 16 || LPU == 32, "head dim 64 or 128");
+  static_assert(NV * UST == ATT_CH, "a thread's positions cover the chunk");
 };
+#define ATT_QG 4
 
 // tree nodes (B D) a launch may hold
 #define ATT_TREE_NODES 16
 template <typename KT, typename WT, int HD, bool TREE>
 __device__ __forceinline__ void attention_body(const AttnArgs& a, int z, int zp) {
-  __shared__ __align__(16) float kv_s[ATT_CH][ATT_LD];
+  using LY = AttLayout<KT, HD>;
+  constexpr int LPU = LY::LPU, NV = LY::NV, UST = LY::UST, NW = ATT_THREADS / 64;
   __shared__ __align__(16) float q_s[ATT_QB][HD];
-  __shared__ float p_s[ATT_QB][ATT_CH];
+  __shared__ float s_s[ATT_QB][ATT_CH];                    // raw scores, then exp(s - max)
   __shared__ float st_s[ATT_QB][2];
-  __shared__ float own_s[TREE ? ATT_TREE_NODES : 1][TREE ? HD : 1];   // tree: node b D + j - 1's key
-  __shared__ float own_v[TREE ? ATT_TREE_NODES : 1][TREE ? HD : 1];   // and value
+  __shared__ __align__(16) float red_s[NW][ATT_QG][HD];    // per-wave value partials of a query group
+  __shared__ __align__(16) float own_s[TREE ? ATT_TREE_NODES : 1][TREE ? HD : 4];   // tree: node b D + j - 1's key
+  __shared__ __align__(16) float own_v[TREE ? ATT_TREE_NODES : 1][TREE ? HD : 4];   // and value
   // z: query block of the sequence, zp: its partials' slot in the launch
   const int c = blockIdx.x, kh = blockIdx.y;
   const int G = a.Hq / a.Hkv;
@@ -1810,16 +1766,51 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, int z, int zp)
   const int q0 = z * ATT_QB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int u0 = c * ATT_CH;
-  const KT* kc = reinterpret_cast<const KT*>(a.kc) + (size_t)kh * a.max_seq * HD;
-  const KT* vc = reinterpret_cast<const KT*>(a.vc) + (size_t)kh * a.max_seq * HD;
+  const int d4 = tid % LPU, ub = tid / LPU;              // dims 4 d4 .. 4 d4 + 3, positions ub + UST j
+  KT* kc = reinterpret_cast<KT*>(a.kc) + (size_t)kh * a.max_seq * HD;
+  KT* vc = reinterpret_cast<KT*>(a.vc) + (size_t)kh * a.max_seq * HD;
 
-  AttTile<KT, HD> kt, vt;
-  kt.load(kc, u0, a.max_seq);
-  vt.load(vc, u0, a.max_seq);
-  AttNew<KT, HD> nk, nv;                              // this launch's rows that fall in the chunk
-  nk.load(a, kh, u0, false);
-  nv.load(a, kh, u0, true);
-  // rotated queries of this block (only rows of real queries are read later)
+  // (1) keys and values of this thread's positions (clamped past the
+  // capacity: the visibility rule never selects those positions)
+  float4 kr[NV], vr[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const size_t o = (size_t)min(u0 + ub + UST * j, a.max_seq - 1) * HD + 4 * d4;
+    kr[j] = ld4<KT>(kc + o);
+    vr[j] = ld4<KT>(vc + o);
+  }
+  // (2) this launch's rows with a slot among them: their own key and value
+  if (!a.self_kv) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int s = u0 + ub + UST * j;
+      const int m = att_first_row(a, s);
+      if (m < a.M && att_row_slot(a, m) == s) {
+        const float* x = a.qkv + (size_t)m * a.ldqkv;
+        const int d = 4 * d4;
+        const bool low = d < HD / 2;
+        const int pd = low ? d + HD / 2 : d - HD / 2;
+        const float4 xk = *reinterpret_cast<const float4*>(x + (size_t)(a.Hq + kh) * HD + d);
+        const float4 xp = *reinterpret_cast<const float4*>(x + (size_t)(a.Hq + kh) * HD + pd);
+        const float4 xv = *reinterpret_cast<const float4*>(x + (size_t)(a.Hq + a.Hkv + kh) * HD + d);
+        const float2* cs = a.cs + (size_t)att_row_pos(a, m) * (HD / 2) + (low ? d : pd);
+        float4 k;
+        k.x = kv_round<KT>(rope_val(xk.x, xp.x, cs[0], low));
+        k.y = kv_round<KT>(rope_val(xk.y, xp.y, cs[1], low));
+        k.z = kv_round<KT>(rope_val(xk.z, xp.z, cs[2], low));
+        k.w = kv_round<KT>(rope_val(xk.w, xp.w, cs[3], low));
+        const float4 v = make_float4(kv_round<KT>(xv.x), kv_round<KT>(xv.y), kv_round<KT>(xv.z), kv_round<KT>(xv.w));
+        kr[j] = k;
+        vr[j] = v;
+        if (z == 0) {
+          const size_t o = (size_t)s * HD + d;
+          st_elem<KT>(kc, o, k.x); st_elem<KT>(kc, o + 1, k.y); st_elem<KT>(kc, o + 2, k.z); st_elem<KT>(kc, o + 3, k.w);
+          st_elem<KT>(vc, o, v.x); st_elem<KT>(vc, o + 1, v.y); st_elem<KT>(vc, o + 2, v.z); st_elem<KT>(vc, o + 3, v.w);
+        }
+      }
+    }
+  }
+  // (3) rotated queries of this block (only rows of real queries are read later)
   const int nqb = min(ATT_QB, nq - q0);
   for (int i = tid; i < nqb * HD; i += ATT_THREADS) {
     const int qi = i / HD, dd = i % HD;
@@ -1828,7 +1819,6 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, int z, int zp)
     const int pos = att_row_pos(a, m);
     q_s[qi][dd] = rope_elem(a.qkv + (size_t)m * a.ldqkv + (size_t)h * HD, a.cs + (size_t)pos * (HD / 2), dd, HD / 2);
   }
-  kt.store(kv_s);
   // tree: the keys and values of the nodes whose positions lie in this
   // chunk (rotated at their positions, rounded to the cache type)
   if constexpr (TREE) {
@@ -1861,105 +1851,120 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, int z, int zp)
     }
   }
   __syncthreads();
-  nk.apply(kv_s, a, kh, u0, z, false);
-  __syncthreads();
-  // scores: lane = key; each wave takes query pairs (qi, qi + 4) for
-  // qi = wave, wave + 8, ..., two independent dot-product chains per lane
-  {
-    const int u = lane, pos = u0 + u;
-    for (int qb = wave; qb < nqb; qb += 2 * (ATT_THREADS / 64)) {   // wave-uniform
-      const int qc = qb + ATT_THREADS / 64;
-      const bool has_c = qc < nqb;
-      const int qcc = has_c ? qc : qb;
-      float da = 0.f, dc = 0.f;
-      if constexpr (TREE) {
-        // positions pos0 + 1 .. pos0 + j of a depth-j row read its branch's
-        // nodes (same FMA order)
-        const int ma = (q0 + qb) / G, mc = (q0 + qcc) / G;
-        const int i = pos - a.pos0;
-        const bool sa = i >= 1 && i <= att_tree_depth(a, ma), sc = i >= 1 && i <= att_tree_depth(a, mc);
-        const float* ka = sa ? own_s[att_tree_branch(a, ma) * a.tree_D + i - 1] : kv_s[u];
-        const float* kc = sc ? own_s[att_tree_branch(a, mc) * a.tree_D + i - 1] : kv_s[u];
-#pragma unroll 8
-        for (int dd = 0; dd < HD; ++dd) {
-          da = fmaf(q_s[qb][dd], ka[dd], da);
-          dc = fmaf(q_s[qcc][dd], kc[dd], dc);
-        }
-      } else {
-#pragma unroll 4
-        for (int d4 = 0; d4 < HD / 4; ++d4) {
-          const float4 kv = *reinterpret_cast<const float4*>(&kv_s[u][d4 * 4]);
-          const float4 qa = *reinterpret_cast<const float4*>(&q_s[qb][d4 * 4]);
-          const float4 qc = *reinterpret_cast<const float4*>(&q_s[qcc][d4 * 4]);
-          da = fmaf(qa.x, kv.x, da); dc = fmaf(qc.x, kv.x, dc);
-          da = fmaf(qa.y, kv.y, da); dc = fmaf(qc.y, kv.y, dc);
-          da = fmaf(qa.z, kv.z, da); dc = fmaf(qc.z, kv.z, dc);
-          da = fmaf(qa.w, kv.w, da); dc = fmaf(qc.w, kv.w, dc);
-        }
-      }
+  // tree rows: positions pos0 + 1 .. pos0 + depth take the row's branch's
+  // nodes (node row index, or -1 for the cache tile)
+  auto node_of = [&](int m, int pos) -> int {
+    if constexpr (TREE) {
+      const int i = pos - a.pos0;
+      return (i >= 1 && i <= att_tree_depth(a, m)) ? att_tree_branch(a, m) * a.tree_D + i - 1 : -1;
+    } else {
+      return -1;
+    }
+  };
+  const int ngrp = (nqb + ATT_QG - 1) / ATT_QG;
+  // (4) raw scores, a group of 4 queries at a time
+  for (int g = 0; g < ngrp; ++g) {
+    float4 qv[ATT_QG];
+    int qm[ATT_QG];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        if (h2 == 1 && !has_c) break;                  // wave-uniform
-        const int qi = h2 ? qc : qb;
-        const int m = (q0 + qi) / G;
-        // tree verify rows see p .. p + depth; tree draft rows the committed
-        // prefix, and p + i where the window bit i of the layer is set
-        const int lim = TREE ? (a.tree_step > 0 ? a.lim_base : a.lim_base + att_tree_depth(a, m))
-                             : a.lim_base + m * a.lim_step;
-        const int wo = pos - a.wbase;
-        const bool vis = pos < lim || (wo >= 0 && wo < 32 && ((a.wmask >> wo) & 1u));
-        const float s = (vis && pos < a.max_seq) ? __fmul_rn(h2 ? dc : da, a.scale) : -INFINITY;
-        const float mx = wave_max(s);
-        const float e = (s == -INFINITY) ? 0.f : expf(__fsub_rn(s, mx));
-        const float l = wave_sum(e);
-        p_s[qi][u] = e;
-        if (lane == 0) { st_s[qi][0] = mx; st_s[qi][1] = l; }
+    for (int qi = 0; qi < ATT_QG; ++qi) {
+      const int qq = min(g * ATT_QG + qi, nqb - 1);
+      qv[qi] = *reinterpret_cast<const float4*>(&q_s[qq][4 * d4]);
+      qm[qi] = (q0 + qq) / G;
+    }
+    float sv[ATT_QG * NV];
+#pragma unroll
+    for (int qi = 0; qi < ATT_QG; ++qi)
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        float4 k = kr[j];
+        if constexpr (TREE) {
+          const int nd = node_of(qm[qi], u0 + ub + UST * j);
+          if (nd >= 0) k = *reinterpret_cast<const float4*>(&own_s[nd][4 * d4]);
+        }
+        float p = __fmul_rn(qv[qi].x, k.x);
+        p = fmaf(qv[qi].y, k.y, p);
+        p = fmaf(qv[qi].z, k.z, p);
+        p = fmaf(qv[qi].w, k.w, p);
+        sv[qi * NV + j] = p;
       }
+    grp_sum_t<ATT_QG * NV, LY::LB>(sv);
+    const int gl = lane % LPU;                             // lane in its position group
+    if (gl < ATT_QG * NV) {
+      const int idx = wst_index<ATT_QG * NV>(lane);
+      const int qi = idx / NV, j = idx % NV;
+      if (g * ATT_QG + qi < nqb) s_s[g * ATT_QG + qi][ub + UST * j] = sv[0];
     }
   }
   __syncthreads();
-  vt.store(kv_s);
+  // (5) chunk statistics per query (lane = position)
+  for (int qb = wave; qb < nqb; qb += NW) {                // wave-uniform
+    const int u = lane, pos = u0 + u;
+    const int m = (q0 + qb) / G;
+    const int lim = TREE ? (a.tree_step > 0 ? a.lim_base : a.lim_base + att_tree_depth(a, m))
+                         : a.lim_base + m * a.lim_step;
+    const int wo = pos - a.wbase;
+    const bool vis = pos < lim || (wo >= 0 && wo < 32 && ((a.wmask >> wo) & 1u));
+    const float s = (vis && pos < a.max_seq) ? __fmul_rn(s_s[qb][u], a.scale) : -INFINITY;
+    const float mx = wave_max(s);
+    const float e = (s == -INFINITY) ? 0.f : expf(__fsub_rn(s, mx));
+    const float l = wave_sum(e);
+    s_s[qb][u] = e;
+    if (lane == 0) { st_s[qb][0] = mx; st_s[qb][1] = l; }
+  }
   __syncthreads();
-  nv.apply(kv_s, a, kh, u0, z, true);
-  __syncthreads();
-  // value sums: outputs i and i + 256 of the (query, dim) grid per thread,
-  // two independent chains over the 64 keys
+  // (6) value sums, a group of 4 queries at a time
   float* part = a.part + (((size_t)kh * a.nz_max + zp) * a.nch_max + c) * ATT_QB * (HD + 2);
-  const int nout = nqb * HD;
-  for (int i0 = tid; i0 < nout; i0 += 2 * ATT_THREADS) {
-    const int i1 = i0 + ATT_THREADS;
-    const bool has1 = i1 < nout;
-    const int qa = i0 / HD, da = i0 % HD;
-    const int qc = has1 ? i1 / HD : qa, dc = has1 ? i1 % HD : da;
-    float acc0 = 0.f, acc1 = 0.f;
-    if constexpr (TREE) {
-      // keys u in [ulo, ulo + j - 1] of a depth-j row are its branch's nodes
-      // b D + (u - ulo)
-      const int ma = (q0 + qa) / G, mc = (q0 + qc) / G;
-      const int ulo = a.pos0 + 1 - u0;
-      const int uha = ulo + att_tree_depth(a, ma) - 1, uhc = ulo + att_tree_depth(a, mc) - 1;
-      const int kba = att_tree_branch(a, ma) * a.tree_D - ulo, kbc = att_tree_branch(a, mc) * a.tree_D - ulo;
-#pragma unroll 8
-      for (int u = 0; u < ATT_CH; ++u) {
-        const bool sa = u >= ulo && u <= uha, sc = u >= ulo && u <= uhc;
-        acc0 = fmaf(p_s[qa][u], sa ? own_v[sa ? kba + u : 0][da] : kv_s[u][da], acc0);
-        acc1 = fmaf(p_s[qc][u], sc ? own_v[sc ? kbc + u : 0][dc] : kv_s[u][dc], acc1);
+  for (int g = 0; g < ngrp; ++g) {
+    float acc[ATT_QG * 4];
+#pragma unroll
+    for (int qi = 0; qi < ATT_QG; ++qi) {
+      const int qq = min(g * ATT_QG + qi, nqb - 1);
+      const int m = (q0 + qq) / G;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int u = ub + UST * j;
+        const float p = s_s[qq][u];
+        float4 v = vr[j];
+        if constexpr (TREE) {
+          const int nd = node_of(m, u0 + u);
+          if (nd >= 0) v = *reinterpret_cast<const float4*>(&own_v[nd][4 * d4]);
+        }
+        float* o = acc + qi * 4;
+        o[0] = j == 0 ? __fmul_rn(p, v.x) : fmaf(p, v.x, o[0]);
+        o[1] = j == 0 ? __fmul_rn(p, v.y) : fmaf(p, v.y, o[1]);
+        o[2] = j == 0 ? __fmul_rn(p, v.z) : fmaf(p, v.z, o[2]);
+        o[3] = j == 0 ? __fmul_rn(p, v.w) : fmaf(p, v.w, o[3]);
       }
+    }
+    // lanes of the wave that hold the same dims: bit 5 (and bit 4 for hd 64)
+    int idx0;
+    if constexpr (LPU == 32) {
+      wst_swap<ATT_QG * 4, ATT_QG * 4, true>(acc);
+      idx0 = ((lane >> 5) & 1) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red_s[wave][(idx0 + i) / 4][4 * d4 + (idx0 + i) % 4] = acc[i];
     } else {
-#pragma unroll 8
-      for (int u = 0; u < ATT_CH; ++u) {
-        acc0 = fmaf(p_s[qa][u], kv_s[u][da], acc0);
-        acc1 = fmaf(p_s[qc][u], kv_s[u][dc], acc1);
+      wst_swap<ATT_QG * 4, ATT_QG * 4, false>(acc);
+      wst_swap<ATT_QG * 2, ATT_QG * 4, true>(acc);
+      idx0 = ((lane >> 4) & 1) * 8 + ((lane >> 5) & 1) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red_s[wave][(idx0 + i) / 4][4 * d4 + (idx0 + i) % 4] = acc[i];
+    }
+    __syncthreads();
+    for (int t = tid; t < ATT_QG * HD; t += ATT_THREADS) {
+      const int qi = t / HD, dd = t % HD;
+      const int qq = g * ATT_QG + qi;
+      if (qq < nqb) {
+        float v = red_s[0][qi][dd];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v = __fadd_rn(v, red_s[w][qi][dd]);
+        float* o = part + (size_t)qq * (HD + 2);
+        o[dd] = v;
+        if (dd == 0) { o[HD] = st_s[qq][0]; o[HD + 1] = st_s[qq][1]; }
       }
     }
-    float* o0 = part + (size_t)qa * (HD + 2);
-    o0[da] = acc0;
-    if (da == 0) { o0[HD] = st_s[qa][0]; o0[HD + 1] = st_s[qa][1]; }
-    if (has1) {
-      float* o1 = part + (size_t)qc * (HD + 2);
-      o1[dc] = acc1;
-      if (dc == 0) { o1[HD] = st_s[qc][0]; o1[HD + 1] = st_s[qc][1]; }
-    }
+    __syncthreads();
   }
 }
 
