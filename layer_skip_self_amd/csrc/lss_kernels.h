@@ -1964,7 +1964,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, int z, int zp)
         if (dd == 0) { o[HD] = st_s[qq][0]; o[HD + 1] = st_s[qq][1]; }
       }
     }
-    __syncthreads();
+    if (g + 1 < ngrp) __syncthreads();                   // red_s is rewritten by the next group
   }
 }
 
