@@ -193,8 +193,9 @@ int lss_draft_tree(lss_engine* e, const uint8_t* skip_mask, int32_t quant, int32
  * sees the pending token and its branch's node i only where the pass over
  * them ran that layer (per-layer valid bits by depth, as in a chain window
  * drafted by several levels).  lss_draft_tree is this call with one level
- * at every depth.  Errors as lss_draft_tree (LSS_EINVAL for a quant outside
- * 0..2). */
+ * at every depth.  masks and quants are host arrays of the caller, read
+ * during the call.  Errors as lss_draft_tree, plus LSS_EINVAL for a quant
+ * outside 0..2 and LSS_ESTATE for quant 2 without lss_attach_w8. */
 int lss_draft_tree_levels(lss_engine* e, const uint8_t* masks, const int32_t* quants, int32_t B, int32_t D,
                           int32_t* tokens_out);
 
