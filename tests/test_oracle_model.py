@@ -211,3 +211,26 @@ def test_int8_quant_bounds():
         assert np.all(err <= float(s) * 0.5 * (1 + 1e-5) + 1e-6 * np.abs(x))
         i = int(np.argmax(np.abs(x)))
         assert q[i] == (127 if x[i] > 0 else -127)
+
+
+def test_float32_oracle_tracks_float64_oracle(tiny_shape, tiny_weights_np, tiny_model, tiny_prompt):
+    """The large-shape tests use the oracle in float32 (the same code with
+    dtype float32); on the 4-layer model it stays within float32 rounding of
+    the float64 oracle pinned above: prefill logits and residual states, a
+    decode row, and the greedy tokens of a speculative run (where the float64
+    top-1/top-2 gap clears the float32 error)."""
+    m32 = oracle.OracleModel(tiny_shape, tiny_weights_np, dtype=np.float32)
+    st64, z64, s64 = oracle.prefill(tiny_model, tiny_prompt, 80)
+    st32, z32, s32 = oracle.prefill(m32, tiny_prompt, 80)
+    assert z32.dtype == np.float32
+    scale = float(np.max(np.abs(z64)))
+    assert np.max(np.abs(z32 - z64)) <= 1e-5 * scale
+    for a, b in zip(s32, s64):
+        assert np.max(np.abs(a - b)) <= 1e-5 * max(1.0, float(np.max(np.abs(b))))
+    assert st32.t0 == st64.t0
+    r64, _ = oracle.forward_row(tiny_model, st64, st64.t0, st64.p, "full")
+    r32, _ = oracle.forward_row(m32, st32, st32.t0, st32.p, "full")
+    assert np.max(np.abs(r32 - r64)) <= 1e-5 * float(np.max(np.abs(r64)))
+    t64, _ = oracle.speculative_generate(tiny_model, tiny_prompt, 24, oracle.Policy(K=3, skip=(1, 2)))
+    t32, _ = oracle.speculative_generate(m32, tiny_prompt, 24, oracle.Policy(K=3, skip=(1, 2)))
+    assert t32 == t64
