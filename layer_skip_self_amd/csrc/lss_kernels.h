@@ -834,10 +834,11 @@ __global__ __launch_bounds__(256) void k_pepi(GemmArgs ga, const float* __restri
 // no per-16-column partials: store, SwiGLU; more workgroups for the small
 // q/k/v launch), and a workgroup walks a contiguous
 // range of tiles (one tile when the grid has a workgroup per tile).  Its
-// GV_WAVES waves split the chunks of K into contiguous ranges (wave w: chunks
-// [w nc / W, (w + 1) nc / W)), and each wave walks every tile's rows in groups
-// of RG rows, the chunks of its range inside each group, RG x NACC 1 KB loads
-// per step with ST steps in flight.  The steps run on across tile
+// GV_WAVES waves take the chunks of K interleaved (wave w: chunks w, w + W,
+// w + 2 W, ..., so the waves of a step read W neighbouring chunks of the same
+// rows: 4-6 % faster than contiguous ranges per wave at K = 14336), and each
+// wave walks every tile's rows in groups of RG rows, its chunks inside each
+// group, RG x NACC 1 KB loads per step with ST steps in flight.  The steps run on across tile
 // boundaries: the first loads of the next tile are in flight while the wave
 // sums of the current tile go through LDS and its epilogue runs, so a
 // workgroup keeps the weight stream going from its first load to its last.
@@ -846,8 +847,8 @@ __global__ __launch_bounds__(256) void k_pepi(GemmArgs ga, const float* __restri
 // with its 8 (bf16) / 4 (float32) weights in fused multiply-adds.
 //
 // Per (weight row n, activation row m) the arithmetic is fixed by K alone:
-// lane l runs one FMA chain over k = c CH + l EPL + e for the chunks c of
-// its wave's range (ascending) and e ascending, the 64 lane values are
+// lane l runs one FMA chain over k = c CH + l EPL + e for its wave's chunks
+// c (ascending) and e ascending, the 64 lane values are
 // summed by the fixed tree of wave_sum, and the GV_WAVES wave sums are
 // added in wave order.  Nothing depends on M, on the tile or on the row group, so
 // a verify row gets the same bits as a one-row greedy step.  The lane sums of
@@ -923,8 +924,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int M = ga.M, K = ga.K;
   const int nc = (K + CH - 1) / CH;
-  const int c0 = wave * nc / GV_WAVES;
-  const int ncw = (wave + 1) * nc / GV_WAVES - c0;       // chunks of this wave (<= NCW)
+  const int ncw = (nc - wave + GV_WAVES - 1) / GV_WAVES;  // chunks of this wave: wave + GV_WAVES i (<= NCW)
   const int ntile = (ga.N + TR - 1) / TR;
   const int tb = (int)((long)blockIdx.x * ntile / gridDim.x);           // this workgroup's tiles [tb, te)
   const int te = (int)((long)(blockIdx.x + 1) * ntile / gridDim.x);
@@ -940,10 +940,10 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
     if constexpr (NACC == 2) wr[NACC - 1] = reinterpret_cast<const WT*>(ga.w2) + (size_t)tile0 * K;
     nrow = min(TR, ga.N - tile0);                          // rows of the tile inside N
   };
-  // weight step u of a tile = (row group u / NCW, chunk c0 + u % NCW)
+  // weight step u of a tile = (row group u / NCW, chunk wave + GV_WAVES (u % NCW))
   auto unit_load = [&](uint4 (&w)[RG][NACC], const WT* const (&wr)[NACC], int nrow, int u) {
     const int g = u / NCW, i = u % NCW;
-    const int k = min((c0 + i) * CH + kl, K - EPL);
+    const int k = min((wave + GV_WAVES * i) * CH + kl, K - EPL);
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
       const size_t ro = (size_t)min(g * RG + r, nrow - 1) * K + k;
@@ -956,7 +956,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
   uint4 xr[NCW][MB][AV];
 #pragma unroll
   for (int i = 0; i < NCW; ++i) {
-    const int k = min((c0 + min(i, max(ncw - 1, 0))) * CH + kl, K - EPL);
+    const int k = min((wave + GV_WAVES * min(i, max(ncw - 1, 0))) * CH + kl, K - EPL);
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       const uint4* pa = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(ga.A) +
@@ -985,7 +985,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(GemmArgs ga) {
   float x[NCW][MB][EPL];
 #pragma unroll
   for (int i = 0; i < NCW; ++i) {
-    const bool kv = (c0 + i) * CH + kl < K;
+    const bool kv = (wave + GV_WAVES * i) * CH + kl < K;
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       unpack_x<WT>(xr[i][m], x[i][m]);
