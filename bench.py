@@ -127,6 +127,12 @@ WORKLOADS = {
 }
 
 
+def progress(msg):
+    """One line on stderr as a piece of the benchmark finishes (stdout keeps
+    the single JSON result line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
     """Time the CPU oracle (float32, as it stands) on a bounded sample."""
     import numpy as np
@@ -148,6 +154,7 @@ def cpu_baseline(shape, w_gpu, prompt, policy, n_tokens, n_prompt):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         limiter, cores = None, threads
+    progress("CPU oracle baseline: widening the weights")
     w_host = [(n, t.to("cpu")) for n, t in w_gpu]
     model = oracle.OracleModel(shape, lss_synth.LazyF32(w_host), dtype=np.float32, cache_layers=True)
     for l in range(shape.n_layers):           # widen every weight once (setup, not timed)
@@ -247,7 +254,9 @@ def bench_batch(args, wl, shape, dev):
         t = time.perf_counter()
         toks, st = eng.generate_batch(prompts, G, p)
         torch.cuda.synchronize()
-        return toks, st, time.perf_counter() - t
+        dt = time.perf_counter() - t
+        progress(f"{p['mode']} batch run: {len(prompts)} sequences x {G} tokens in {dt:.2f} s")
+        return toks, st, dt
 
     for _ in range(args.warmup):
         run(pol)
@@ -350,6 +359,7 @@ def main():
     prompts = [lss_synth.make_prompt(shape, n, seed=shape.prompt_seed + i) for i, n in enumerate(lens)]
     G = wl["gen"] if args.gen is None else args.gen
     max_seq = max(lens) + G + 33
+    progress(f"weights of {wl['shape']} ready")
     eng = Engine(shape, weights, max_seq=max_seq, max_rows=64)
     policies = [dict(p) for p in (wl["policy"] if isinstance(wl["policy"], list) else [wl["policy"]])]
     for p in policies:
@@ -385,7 +395,9 @@ def main():
         t = time.perf_counter()
         toks, st = eng.generate(prompt, G, pol)
         torch.cuda.synchronize()
-        return toks, st, time.perf_counter() - t
+        dt = time.perf_counter() - t
+        progress(f"{pol['mode']} run: prompt {len(prompt)}, {G} tokens in {dt:.2f} s")
+        return toks, st, dt
 
     for _ in range(args.warmup):
         for pol, i in runs:
