@@ -332,3 +332,16 @@ def test_latency_calibration_fits_the_router_model(setup):
     # state is consistent afterwards: a fresh greedy run still matches the oracle
     toks, _ = eng.generate(prompt, 16, {"mode": "ar"})
     assert toks == setup["ref"][:16]
+
+
+def test_row_cost_calibration_structure(setup):
+    """Row-cost factors for the tree router (verify time of r rows over one
+    row, HIP events): one per row count, the first exactly 1, all finite and
+    positive; timing noise is not asserted.  The engine stays usable."""
+    eng, prompt = setup["eng"], setup["prompt"]
+    rc = eng.calibrate_row_cost(prompt[:24], max_rows=8, reps=3)
+    print("row costs", [round(x, 3) for x in rc])
+    assert len(rc) == 8 and rc[0] == 1.0
+    assert all(np.isfinite(x) and x > 0 for x in rc)
+    toks, _ = eng.generate(prompt, 16, {"mode": "ar"})
+    assert toks == setup["ref"][:16]
