@@ -289,6 +289,7 @@ int lss_read_dp_decisions(lss_engine* e, float* host_out);
 /* Draft policy of lss_generate. */
 enum lss_mode { LSS_MODE_AR = 0, LSS_MODE_STATIC = 1, LSS_MODE_DP = 2, LSS_MODE_CASCADE = 3 };
 #define LSS_LEVELS_MAX 4
+#define LSS_STOP_MAX 8
 typedef struct lss_policy {
   int32_t mode;              /* lss_mode */
   int32_t k_max;             /* draft tokens per round (cascade: total) */
@@ -308,6 +309,9 @@ typedef struct lss_policy {
   int32_t tree_depth;        /* STATIC / DP tree depth (0 or 1: depth 1), cut to the tokens still to emit */
   double row_cost[LSS_TREE_NODES_MAX + 1]; /* CASCADE trees: cost factor of a pass over r rows at index
                                 r - 1 (all 0: 1 for every row count) */
+  int32_t n_stop;            /* stop tokens (0: none, at most LSS_STOP_MAX): generation ends right after the
+                                first emitted token that is one of stop_tokens[0 .. n_stop) */
+  int32_t stop_tokens[LSS_STOP_MAX];
 } lss_policy;
 
 typedef struct lss_stats {
@@ -316,7 +320,13 @@ typedef struct lss_stats {
 
 /* Prefill `prompt`, then decode until n_gen tokens (t0 included) are
  * emitted into out_tokens[n_gen] with the given policy; LSS_MODE_AR is the
- * greedy autoregressive baseline (verify of the pending token alone). */
+ * greedy autoregressive baseline (verify of the pending token alone).  With
+ * stop tokens, decoding ends early right after the first emitted stop token
+ * (which is kept); stats->emitted is the number of tokens written.  Those
+ * tokens are the first ones of the run without stop tokens, so the output
+ * stays lossless.  The engine's committed sequence may then hold the rest
+ * of that round's accepted tokens.  LSS_EINVAL for n_stop outside
+ * [0, LSS_STOP_MAX] or a stop token outside the vocabulary. */
 int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t n_gen,
                  const lss_policy* policy, int32_t* out_tokens, lss_stats* stats);
 
@@ -325,8 +335,11 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
  * has n_gen tokens in out_tokens[i * n_gen ..]: every sequence runs the
  * policy's rounds as lss_generate would on its own (LSS_MODE_AR, STATIC, or
  * DP with its own layer selection), the rounds of all sequences batched.
- * stats[n_seqs] per sequence (may be NULL).  The cascade mode, trees,
- * sampling and the W8A8 draft are single-sequence only (LSS_EINVAL). */
+ * stats[n_seqs] per sequence (may be NULL).  Stop tokens end each
+ * sequence on its own as in lss_generate; a stopped sequence leaves the
+ * batch, and the rest of its out_tokens row is left untouched.  The cascade
+ * mode, trees, sampling and the W8A8 draft are single-sequence only
+ * (LSS_EINVAL). */
 int lss_generate_batch(lss_engine* e, int32_t n_seqs, const int32_t* prompts, const int32_t* prompt_lens,
                        int32_t n_gen, const lss_policy* policy, int32_t* out_tokens,
                        lss_stats* stats);

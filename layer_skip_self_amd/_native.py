@@ -14,6 +14,7 @@ LSS_ROWS_MAX = 64
 LSS_SEQS_MAX = 64
 LSS_BATCH_PASS_SEQS = 16
 LSS_LEVELS_MAX = 4
+LSS_STOP_MAX = 8
 LSS_ACCEPT_ROWS_MAX = 64
 LSS_ACCEPT_VOCAB_MAX = 262144
 
@@ -40,7 +41,8 @@ class lss_policy(C.Structure):
                 ("level_skip", C.c_int32 * LSS_LEVELS_MAX), ("level_exit", C.c_int32 * LSS_LEVELS_MAX),
                 ("level_quant", C.c_int32 * LSS_LEVELS_MAX), ("beta", C.c_double * 3),
                 ("tree_width", C.c_int32), ("tree_depth", C.c_int32),
-                ("row_cost", C.c_double * (LSS_TREE_NODES_MAX + 1))]
+                ("row_cost", C.c_double * (LSS_TREE_NODES_MAX + 1)),
+                ("n_stop", C.c_int32), ("stop_tokens", C.c_int32 * LSS_STOP_MAX)]
 
 
 class lss_stats(C.Structure):

@@ -967,6 +967,22 @@ int create_fail(int code, const std::string& msg) {
   return code;
 }
 
+// stop tokens of a generation policy: count and ids in range
+int check_stop(lss_engine* e, const lss_policy* pol, const char* what) {
+  if (pol->n_stop < 0 || pol->n_stop > LSS_STOP_MAX)
+    return fail(e, LSS_EINVAL, std::string(what) + ": n_stop must be in [0, LSS_STOP_MAX]");
+  for (int i = 0; i < pol->n_stop; ++i)
+    if (pol->stop_tokens[i] < 0 || pol->stop_tokens[i] >= e->cfg.vocab)
+      return fail(e, LSS_EINVAL, std::string(what) + ": stop token out of range");
+  return LSS_OK;
+}
+
+bool is_stop(const lss_policy* pol, int32_t tok) {
+  for (int i = 0; i < pol->n_stop; ++i)
+    if (pol->stop_tokens[i] == tok) return true;
+  return false;
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -1958,12 +1974,15 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
   }
   if ((long)n_prompt + n_gen + std::min(kWinMax, c.max_rows - 1) + 1 > c.max_seq)
     return fail(e, LSS_ECAPACITY, "generate: prompt + generation + window exceeds max_seq");
+  const int rc_stop = check_stop(e, pol, "generate");
+  if (rc_stop) return rc_stop;
   lss_stats st{};
   int32_t t0 = 0;
   int rc = lss_prefill(e, prompt, n_prompt, &t0);
   if (rc) return rc;
   int emitted = 0;
   out[emitted++] = t0;
+  bool stopped = is_stop(pol, t0);
   const int nlev = pol->mode == LSS_MODE_CASCADE ? pol->n_levels : 1;
   std::vector<std::vector<uint8_t>> masks(nlev, std::vector<uint8_t>(L, 0));
   auto select = [&]() -> int {
@@ -1990,7 +2009,7 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
   std::vector<double> acc_rate(nlev, router::kAInit);
   std::vector<int32_t> slot_levels;
   std::vector<int32_t> toks(64), acc(64);
-  while (emitted < n_gen) {
+  while (emitted < n_gen && !stopped) {
     const int budget = n_gen - emitted - 1;
     slot_levels.clear();
     if ((pol->mode == LSS_MODE_STATIC || pol->mode == LSS_MODE_DP) && pol->tree_width > 0) {
@@ -2043,12 +2062,12 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
       if (n > 0)                                        // the branch followed: its first node was emitted
         for (int b = 0; b < B; ++b)
           if (toks[(size_t)b * D] == acc[0]) branch = b;
-      for (int i = 0; i <= n && emitted < n_gen; ++i) out[emitted++] = acc[i];
+      for (int i = 0; i <= n && emitted < n_gen && !stopped; ++i) stopped = is_stop(pol, out[emitted++] = acc[i]);
       st.rounds++;
       st.drafted += k;
       st.accepted += n;
       router::update_tree(acc_rate.data(), nlev, slot_levels.data(), D, n, branch);
-      if (st.rounds % pol->interval == 0) {
+      if (!stopped && st.rounds % pol->interval == 0) {
         rc = select();
         if (rc) return rc;
       }
@@ -2080,13 +2099,13 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
     int n = 0, bonus = 0;
     rc = lss_accept_and_rollback(e, &n, &bonus, acc.data());
     if (rc) return rc;
-    for (int i = 0; i <= n && emitted < n_gen; ++i) out[emitted++] = acc[i];
+    for (int i = 0; i <= n && emitted < n_gen && !stopped; ++i) stopped = is_stop(pol, out[emitted++] = acc[i]);
     st.rounds++;
     st.drafted += k;
     st.accepted += n;
     if (pol->mode == LSS_MODE_CASCADE)
       router::update(acc_rate.data(), nlev, slot_levels.data(), (int)slot_levels.size(), n);
-    if ((pol->mode == LSS_MODE_DP || pol->mode == LSS_MODE_CASCADE) && st.rounds % pol->interval == 0) {
+    if (!stopped && (pol->mode == LSS_MODE_DP || pol->mode == LSS_MODE_CASCADE) && st.rounds % pol->interval == 0) {
       rc = select();
       if (rc) return rc;
     }
@@ -2114,10 +2133,13 @@ int lss_generate_batch(lss_engine* e, int32_t n, const int32_t* prompts, const i
   for (int i = 0; i < n; ++i)
     if (lens[i] < 1 || (long)lens[i] + n_gen + std::min(kWinMax, c.max_rows - 1) + 1 > c.max_seq)
       return fail(e, LSS_ECAPACITY, "generate_batch: a prompt is empty or prompt + generation + window exceeds max_seq");
+  const int rc_stop = check_stop(e, pol, "generate_batch");
+  if (rc_stop) return rc_stop;
   const int cur0 = e->cur;
   std::vector<int32_t> seqs(n);
   std::vector<uint8_t> masks((size_t)n * L, 0);
   std::vector<int> emitted(n, 0);
+  std::vector<uint8_t> stopped(n, 0);
   std::vector<lss_stats> st(n);
   int rc = LSS_OK;
   auto fin = [&](int r) {
@@ -2144,6 +2166,7 @@ int lss_generate_batch(lss_engine* e, int32_t n, const int32_t* prompts, const i
     off += lens[i];
     out[(size_t)i * n_gen] = t0;
     emitted[i] = 1;
+    stopped[i] = is_stop(pol, t0);
     if (pol->mode == LSS_MODE_STATIC) std::copy(pol->static_mask, pol->static_mask + L, masks.begin() + (size_t)i * L);
     if (pol->mode == LSS_MODE_DP && (rc = dp(i))) return fin(rc);
   }
@@ -2152,7 +2175,7 @@ int lss_generate_batch(lss_engine* e, int32_t n, const int32_t* prompts, const i
   for (;;) {
     act.clear();
     for (int i = 0; i < n; ++i)
-      if (emitted[i] < n_gen) act.push_back(i);
+      if (emitted[i] < n_gen && !stopped[i]) act.push_back(i);
     if (act.empty()) break;
     const int na_ = (int)act.size();
     std::fill(done.begin(), done.end(), 0);
@@ -2173,12 +2196,13 @@ int lss_generate_batch(lss_engine* e, int32_t n, const int32_t* prompts, const i
     if (rc) return fin(rc);
     for (int a = 0; a < na_; ++a) {
       const int i = act[a];
-      for (int j = 0; j <= na[a] && emitted[i] < n_gen; ++j)
-        out[(size_t)i * n_gen + emitted[i]++] = acc[(size_t)a * (LSS_WINDOW_MAX + 1) + j];
+      for (int j = 0; j <= na[a] && emitted[i] < n_gen && !stopped[i]; ++j)
+        stopped[i] = is_stop(pol, out[(size_t)i * n_gen + emitted[i]++] = acc[(size_t)a * (LSS_WINDOW_MAX + 1) + j]);
       st[i].rounds++;
       st[i].drafted += done[a];
       st[i].accepted += na[a];
-      if (pol->mode == LSS_MODE_DP && st[i].rounds % pol->interval == 0 && (rc = dp(i))) return fin(rc);
+      if (!stopped[i] && pol->mode == LSS_MODE_DP && st[i].rounds % pol->interval == 0 && (rc = dp(i)))
+        return fin(rc);
     }
   }
   for (int i = 0; i < n; ++i) {

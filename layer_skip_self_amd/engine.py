@@ -242,7 +242,9 @@ class Engine:
 
     def generate(self, prompt, n_gen, policy):
         """Prefill + decoding of n_gen tokens under ``policy`` (``make_policy``;
-        its ``temperature`` / ``seed`` select greedy decoding or sampling)."""
+        its ``temperature`` / ``seed`` select greedy decoding or sampling,
+        ``stop`` a tuple of token ids that end it early).  Returns (the
+        emitted tokens, stats)."""
         self.set_sampling(policy.get("temperature", 0.0), policy.get("seed", 0))
         if "decode_kernel" in policy:
             self.set_decode_kernel(policy["decode_kernel"])
@@ -252,7 +254,7 @@ class Engine:
         st = N.lss_stats()
         self._check(self.lib.lss_generate(self.h, p, len(a), int(n_gen), C.byref(pol),
                                           out.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(st)), "lss_generate")
-        return out.tolist(), {f: getattr(st, f) for f, _ in N.lss_stats._fields_}
+        return out[:st.emitted].tolist(), {f: getattr(st, f) for f, _ in N.lss_stats._fields_}
 
     # -------------------------------------------------------------- several sequences
     def select(self, seq):
@@ -307,7 +309,7 @@ class Engine:
                                                 out.ctypes.data_as(C.POINTER(C.c_int32)), st),
                     "lss_generate_batch")
         stats = [{f: getattr(st[i], f) for f, _ in N.lss_stats._fields_} for i in range(n)]
-        return [out[i].tolist() for i in range(n)], stats
+        return [out[i, :st[i].emitted].tolist() for i in range(n)], stats
 
     # -------------------------------------------------------------- measurement
     EPILOGUES = {"qkv": 0, "resid": 1, "gate_up": 2, "lm_head": 3,
@@ -377,6 +379,12 @@ def make_policy(policy, n_layers):
     if rc is not None:
         for i, v in enumerate(rc):
             pol.row_cost[i] = float(v)
+    stop = list(policy.get("stop", ()))
+    if len(stop) > N.LSS_STOP_MAX:
+        raise ValueError(f"at most {N.LSS_STOP_MAX} stop tokens")
+    pol.n_stop = len(stop)
+    for i, t in enumerate(stop):
+        pol.stop_tokens[i] = int(t)
     return pol
 
 

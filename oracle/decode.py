@@ -402,21 +402,37 @@ def accept_tree(st, logits, states, branches, kv):
     return n, bonus, emitted
 
 
-def ar_generate(model, prompt, G, max_seq=None, sampling=None, state_out=None):
+def _stopped(out, start, stop):
+    """Stop tokens: cut ``out`` right after the first stop token among
+    out[start:] (in place); True if there was one."""
+    for i in range(start, len(out)):
+        if out[i] in stop:
+            del out[i + 1:]
+            return True
+    return False
+
+
+def ar_generate(model, prompt, G, max_seq=None, sampling=None, state_out=None, stop=()):
     """Autoregressive decoding of G tokens (t0 included): greedy, or with
     ``sampling`` = (T, seed) the TARGET draw of every row's position.
-    ``state_out`` (a list) receives the decode state (its ``margins``)."""
+    ``state_out`` (a list) receives the decode state (its ``margins``).
+    ``stop``: token ids that end the decoding right after their first
+    occurrence (kept)."""
     max_seq = max_seq or len(prompt) + G + 1
     st, z, _ = prefill(model, prompt, max_seq, sampling=sampling)
     if state_out is not None:
         state_out.append(st)
     out = [st.t0]
+    if _stopped(out, 0, stop):
+        return out
     while len(out) < G:
         zz, s = forward_row(model, st, st.t0, st.p, "full")
         st.target_states, st.target_pos = s, st.p
         st.t0 = _pick(st, zz, sampling, smp.TARGET, st.p)
         st.p += 1
         out.append(st.t0)
+        if _stopped(out, len(out) - 1, stop):
+            break
     return out
 
 
@@ -437,7 +453,8 @@ class Policy:
     min(tree_depth, tokens still to emit) (``draft_tree``) instead of a
     chain; with ``cascade``, tree_width is the largest width the router may
     choose (``dytc.plan_tree``, row_cost its per-row-count cost factors,
-    None: 1), its levels drafting the tree's depths.
+    None: 1), its levels drafting the tree's depths.  stop: token ids that
+    end the decoding right after the first one emitted (kept).
     """
     K: int = 4
     skip: tuple = ()
@@ -453,6 +470,7 @@ class Policy:
     tree_width: int = 0
     tree_depth: int = 1
     row_cost: tuple = None
+    stop: tuple = ()
 
     @property
     def sampling(self):
@@ -484,6 +502,8 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None, state
         state_out.append(st)
     out = [st.t0]
     records = []
+    if _stopped(out, 0, policy.stop):
+        return out, records
 
     def select_masks():
         if policy.cascade is not None:
@@ -523,15 +543,18 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None, state
                 n, bonus, emitted = accept(st, logits, states, d, sam)
                 branch = -1
             a = update_tree(a, levels, n, branch)
+            start = len(out)
             out += emitted
             rounds += 1
             rec = {"k": B * len(levels), "n": n, "bonus": bonus, "tree": True, "width": B,
                    "levels": levels, "branch": branch, "a": list(a)}
             records.append(rec)
-            if rounds % policy.interval == 0:
-                masks = select_masks()
             if log is not None:
                 log.append(rec)
+            if _stopped(out, start, policy.stop):
+                break
+            if rounds % policy.interval == 0:
+                masks = select_masks()
             continue
         if policy.cascade is not None:
             depth = [L - sum(mk) for mk in masks]
@@ -551,16 +574,19 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None, state
             draft_tree(model, st, masks[0], policy.quant, policy.tree_width, depth)
             logits, states, branches, kv = verify_tree(model, st)
             n, bonus, emitted = accept_tree(st, logits, states, branches, kv)
+            start = len(out)
             out += emitted
             rounds += 1
             firsts = [br[0] for br in branches]
             rec = {"k": len(branches) * depth, "n": n, "bonus": bonus, "tree": True,
                    "branch": firsts.index(emitted[0]) if n else -1}
             records.append(rec)
-            if policy.dp_skip is not None and rounds % policy.interval == 0:
-                masks = select_masks()
             if log is not None:
                 log.append(rec)
+            if _stopped(out, start, policy.stop):
+                break
+            if policy.dp_skip is not None and rounds % policy.interval == 0:
+                masks = select_masks()
             continue
         else:
             kk = min(policy.K, budget)
@@ -572,6 +598,7 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None, state
             drafted_levels = None
         logits, states, d = verify(model, st)
         n, bonus, emitted = accept(st, logits, states, d, sam)
+        start = len(out)
         out += emitted
         rounds += 1
         rec = {"k": len(d), "n": n, "bonus": bonus}
@@ -580,10 +607,12 @@ def speculative_generate(model, prompt, G, policy, max_seq=None, log=None, state
             rec["levels"] = drafted_levels
             rec["a"] = list(a)
         records.append(rec)
-        if (policy.dp_skip is not None or policy.cascade is not None) and rounds % policy.interval == 0:
-            masks = select_masks()
         if log is not None:
             log.append(rec)
+        if _stopped(out, start, policy.stop):
+            break
+        if (policy.dp_skip is not None or policy.cascade is not None) and rounds % policy.interval == 0:
+            masks = select_masks()
     return out[:G], records
 
 

@@ -32,6 +32,42 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(N.SIGNATURES), set(names) ^ set(N.SIGNATURES)
 
 
+def test_struct_layouts_and_limits_match_the_header(tmp_path):
+    """The ctypes mirrors of the header's structs have the C compiler's field
+    offsets and sizes, and the binding's limits equal the header's defines."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = [N.lss_config, N.lss_tensor, N.lss_policy, N.lss_stats]
+    defines = sorted(set(re.findall(r"#define\s+(LSS_[A-Z_0-9]+)\s+\d+", open(HEADER).read())))
+    lines = ['#include <stdio.h>', '#include "lss.h"', "int main(void) {"]
+    for st in structs:
+        nm = st.__name__
+        lines.append(f'  printf("{nm} size %zu\\n", sizeof({nm}));')
+        for f in st._fields_:
+            lines.append(f'  printf("{nm}.{f[0]} %zu\\n", offsetof({nm}, {f[0]}));')
+    for d in defines:
+        lines.append(f'  printf("{d} %ld\\n", (long)({d}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                          check=True).stdout.splitlines())
+    for st in structs:
+        nm = st.__name__
+        assert int(got[f"{nm} size"]) == C.sizeof(st), nm
+        for f in st._fields_:
+            assert int(got[f"{nm}.{f[0]}"]) == getattr(st, f[0]).offset, (nm, f[0])
+    mirrored = [d for d in defines if hasattr(N, d)]
+    assert {"LSS_STOP_MAX", "LSS_LEVELS_MAX", "LSS_TREE_NODES_MAX", "LSS_WINDOW_MAX"} <= set(mirrored)
+    for d in mirrored:
+        assert int(got[d]) == getattr(N, d), d
+
+
 def test_null_engine_calls_are_rejected():
     lib = N.load()
     assert lib.lss_set_gemv_grid(None, 1) == N.LSS_EINVAL

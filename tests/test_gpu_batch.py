@@ -177,3 +177,29 @@ def test_bf16_batch_equals_single_sequence_runs(small, kernel):
     finally:
         small["eng"].set_decode_kernel("vector")
         small["one"].set_decode_kernel("vector")
+
+
+@pytest.mark.parametrize("name", ["ar", "dp_S2_I3"])
+def test_batch_stop_tokens_end_each_sequence_on_its_own(tiny, name):
+    """A stop token ends every sequence of a batch at its own first
+    occurrence: tokens, rounds and accepted counts equal the oracle's
+    single-sequence runs with the same stop token, and the GPU's own
+    single-sequence runs; sequences that never emit it run to the end."""
+    from dataclasses import replace
+    gp, op = POLICIES[name]
+    prompts = _prompts(tiny["sh"], 3)
+    full = oracle.batch_generate(tiny["model"], prompts, G, op)
+    t0 = full[0][0]
+    stop = (int(next(t0[j] for j in range(6, G) if t0[j] not in t0[:j])),)
+    toks, stats = tiny["eng"].generate_batch(prompts, G, dict(gp, stop=stop))
+    ref = oracle.batch_generate(tiny["model"], prompts, G, replace(op, stop=stop))
+    assert len(toks[0]) < G                                  # sequence 0 stops early
+    for i, p in enumerate(prompts):
+        rtoks, recs = ref[i]
+        single, sst = tiny["one"].generate(p, G, dict(gp, stop=stop))
+        assert toks[i] == rtoks == single, i
+        assert stats[i] == sst, i
+        assert stats[i]["emitted"] == len(rtoks), i
+        if name != "ar":
+            assert stats[i]["rounds"] == len(recs)
+            assert stats[i]["accepted"] == sum(r["n"] for r in recs)

@@ -345,3 +345,44 @@ def test_row_cost_calibration_structure(setup):
     assert all(np.isfinite(x) and x > 0 for x in rc)
     toks, _ = eng.generate(prompt, 16, {"mode": "ar"})
     assert toks == setup["ref"][:16]
+
+
+STOP_POLICIES = {
+    "ar": {"mode": "ar"},
+    "static_12_K4": POLICIES["static_12_K4"],
+    "dp_S2_I4": POLICIES["dp_S2_I4"],
+    "cascade": POLICIES["cascade"],
+    "tree_B3_D2": {"mode": "static", "k_max": 4, "skip": (1,), "tree_width": 3, "tree_depth": 2},
+    "cascade_tree": dict(POLICIES["cascade"], tree_width=2),
+}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", sorted(STOP_POLICIES))
+def test_stop_token_ends_generation_as_the_oracle(setup, name):
+    """With a stop token, the engine emits the oracle's greedy tokens up to
+    and including the stop token's first occurrence and nothing after it;
+    stats count exactly those tokens.  A stop token that never occurs
+    changes nothing."""
+    eng, prompt, ref = setup["eng"], setup["prompt"], setup["ref"]
+    i = next(j for j in range(7, G) if ref[j] not in ref[:j])
+    absent = next(t for t in range(setup["shape"].vocab) if t not in ref)
+    toks, stats = eng.generate(prompt, G, dict(STOP_POLICIES[name], stop=(absent, ref[i])))
+    assert toks == ref[:i + 1]
+    assert stats["emitted"] == i + 1
+    toks, stats = eng.generate(prompt, G, dict(STOP_POLICIES[name], stop=(absent,)))
+    assert toks == ref and stats["emitted"] == G
+
+
+@pytest.mark.gpu
+def test_stop_token_limits_and_first_token(setup):
+    from layer_skip_self_amd.engine import LssError
+    eng, prompt, ref = setup["eng"], setup["prompt"], setup["ref"]
+    toks, stats = eng.generate(prompt, G, {"mode": "static", "k_max": 4, "skip": (1,), "stop": (ref[0],)})
+    assert toks == ref[:1] and stats["emitted"] == 1 and stats["rounds"] == 0
+    with pytest.raises(LssError):
+        eng.generate(prompt, G, {"mode": "ar", "stop": (setup["shape"].vocab,)})
+    with pytest.raises(ValueError):
+        eng.generate(prompt, G, {"mode": "ar", "stop": tuple(range(9))})
+    toks, _ = eng.generate(prompt, 16, {"mode": "ar"})          # the engine is usable afterwards
+    assert toks == ref[:16]

@@ -106,3 +106,45 @@ def test_exit_threshold_stops_after_low_confidence_token(tiny_model, tiny_prompt
     assert len(toks) == 5
     for p in pm:
         assert 0.0 < p <= 1.0
+
+
+def _first_new_token(toks, lo):
+    """Index i >= lo of the first token that does not occur in toks[:i]."""
+    return next(i for i in range(lo, len(toks)) if toks[i] not in toks[:i])
+
+
+STOP_POLICIES = {
+    "static_skip_12_K4": oracle.Policy(K=4, skip=(1, 2)),
+    "clasp_dp_S2_I4": oracle.Policy(K=4, dp_skip=2, interval=4),
+    "tree_B3_D2": oracle.Policy(K=4, skip=(1,), tree_width=3, tree_depth=2),
+    "cascade": POLICIES["cascade"],
+    "cascade_tree": oracle.Policy(K=8, cascade=[(3, 1, False), (1, 0, True), (0, 0, True)], interval=5,
+                                  latency_beta=(0.1, 0.0, 0.05), tree_width=2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STOP_POLICIES))
+def test_stop_token_cuts_the_output_after_its_first_occurrence(name, tiny_model, tiny_prompt, ar_tokens):
+    """Decoding is deterministic and lossless, so ending it at a stop token
+    yields the greedy output up to and including that token's first
+    occurrence, for greedy decoding and every draft policy; a stop token
+    never emitted changes nothing."""
+    from dataclasses import replace
+    i = _first_new_token(ar_tokens, 7)
+    stop = (int(ar_tokens[i]),)
+    assert oracle.ar_generate(tiny_model, tiny_prompt, G, stop=stop) == ar_tokens[:i + 1]
+    pol = replace(STOP_POLICIES[name], stop=stop)
+    toks, recs = oracle.speculative_generate(tiny_model, tiny_prompt, G, pol)
+    assert toks == ar_tokens[:i + 1]
+    # the last round is the one that emitted the stop token
+    assert sum(r["n"] + 1 for r in recs[:-1]) < i <= sum(r["n"] + 1 for r in recs)
+    absent = next(t for t in range(tiny_model.V) if t not in ar_tokens)
+    toks, _ = oracle.speculative_generate(tiny_model, tiny_prompt, G, replace(pol, stop=(absent,)))
+    assert toks == ar_tokens
+
+
+def test_stop_token_equal_to_the_first_token(tiny_model, tiny_prompt, ar_tokens):
+    stop = (int(ar_tokens[0]),)
+    assert oracle.ar_generate(tiny_model, tiny_prompt, G, stop=stop) == ar_tokens[:1]
+    toks, recs = oracle.speculative_generate(tiny_model, tiny_prompt, G, oracle.Policy(K=4, skip=(1,), stop=stop))
+    assert toks == ar_tokens[:1] and recs == []
