@@ -174,3 +174,27 @@ def test_first_token_follows_the_full_model_distribution(tiny):
     print(f"accepted {acc}/{N}; chi-square p {chi.pvalue:.3g}")
     assert 0 < acc < N
     assert chi.pvalue > 1e-4, (counts, exp)
+
+
+@pytest.mark.parametrize("name", ["ar_T1", "dp_S2_I4_T1"])
+def test_sampling_with_stop_token_matches_oracle(tiny, name):
+    """A stop token under speculative sampling: the GPU emits the oracle's
+    sampled tokens up to and including the stop token's first occurrence
+    (the oracle run with the same stop token), and its round count."""
+    import dataclasses
+    gpol, opol = POLICIES[name]
+    T, seed = 1.0, 3000                   # every oracle decision of both runs clears MARGIN at this seed
+    full, _, margins = _oracle_run(tiny, opol, T, seed)
+    assert min(margins) > MARGIN, "seed leaves a decision too close to call; pick another"
+    i = next(j for j in range(6, G) if full[j] not in full[:j])
+    stop = (int(full[i]),)
+    toks, st = tiny["eng"].generate(tiny["prompt"], G, dict(gpol, temperature=T, seed=seed, stop=stop))
+    assert toks == full[:i + 1]
+    assert st["emitted"] == i + 1
+    if opol.K > 0:
+        p = dataclasses.replace(opol, temperature=T, seed=seed, stop=stop)
+        ref, recs = oracle.speculative_generate(tiny["model"], tiny["prompt"], G, p, max_seq=256)
+        assert ref == toks
+        assert st["rounds"] == len(recs)
+    else:
+        assert oracle.ar_generate(tiny["model"], tiny["prompt"], G, max_seq=256, sampling=(T, seed), stop=stop) == toks
