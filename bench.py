@@ -333,7 +333,7 @@ def main():
                     help="override the workload's decode-row kernel (A/B runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this engine runs one sequence on one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "the engine runs on one GPU; --gpus must be 1 "
                                    "(multi-GPU sharding is a design note only)"}))
         sys.exit(2)
 
