@@ -26,12 +26,15 @@ Sources (the pages this implements; no equations beyond two are printed there):
 Floating point: the oracle computes in float64 by default (``dtype``
 argument); the pages fix no precision.  Decisions that turn floating point
 into integers *inside the method* (int8 activation codes) are taken in
-float32, the precision the GPU kernels take them in.
+float32, the precision the GPU kernels take them in.  ``OracleModel(...,
+kv_dtype="bf16")`` models a KV cache that keeps keys and values rounded to
+bfloat16 (``round_bf16``, from their float32 values); the pages fix no cache
+precision either.
 
 Parity status per function is listed in each module header.
 """
-from .model import (OracleModel, rms_norm, rope, silu, attend, quantize_row, argmax_first, quantize_weight_rows,
-                    w8a8_accumulate, w8a8_project)
+from .model import (OracleModel, rms_norm, rope, silu, attend, quantize_row, argmax_first, round_bf16,
+                    quantize_weight_rows, w8a8_accumulate, w8a8_project)
 from .decode import (DecodeState, layer_block, prefill, forward_row, ar_generate, draft, verify,
                      accept, speculative_generate, batch_generate, Policy, top_b, draft_tree, verify_tree,
                      accept_tree)
@@ -41,7 +44,7 @@ from .dytc import (ALPHA, A_INIT, ema_update, fit_latency, predict_latency,
 from . import sampling
 
 __all__ = [
-    "OracleModel", "rms_norm", "rope", "silu", "attend", "quantize_row", "argmax_first",
+    "OracleModel", "rms_norm", "rope", "silu", "attend", "quantize_row", "argmax_first", "round_bf16",
     "quantize_weight_rows", "w8a8_accumulate", "w8a8_project",
     "DecodeState", "layer_block", "prefill", "forward_row", "ar_generate", "draft", "verify", "accept",
     "speculative_generate", "batch_generate", "Policy", "clasp_dp", "brute_force_skip", "top_b", "draft_tree", "verify_tree",

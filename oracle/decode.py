@@ -75,6 +75,9 @@ def layer_row(model, l, h, pos, st, mode, quant=False):
     mode "draft": writes its k, v at ``pos`` (a window slot) and sets the
                   layer's valid bit; attends to [0, p) plus valid window slots.
     mode "dp":    writes nothing; attends to [0, pos) plus its own k, v.
+    With a bf16 KV cache (``model.kv``) the stored keys and values are
+    rounded, and so are the row's own in modes "full" and "draft"; the own
+    k, v of a "dp" row enter unrounded, since they are never stored.
 
     quant: 0 full precision; 1 (or True) int8 activations (codes times
     scale) into the full-precision weights; 2 int8 activations and the
@@ -101,6 +104,8 @@ def layer_row(model, l, h, pos, st, mode, quant=False):
     v = proj("wv", x).reshape(m.Hkv, m.hd)
     q = rope(q, pos, m.theta)
     k = rope(k, pos, m.theta)
+    if mode in ("full", "draft"):       # the cache's values, used by the row itself too
+        k, v = m.kv(k), m.kv(v)
     if mode == "full":
         st.k[l, pos], st.v[l, pos] = k, v
         keys, vals = st.k[l, :pos + 1], st.v[l, :pos + 1]
@@ -159,6 +164,7 @@ def layer_block(model, l, H, st=None):
     Vv = (X @ lw["wv"].T).reshape(P, m.Hkv, m.hd)
     Q = np.stack([rope(Q[t], t, m.theta) for t in range(P)])
     K = np.stack([rope(K[t], t, m.theta) for t in range(P)])
+    K, Vv = m.kv(K), m.kv(Vv)           # the cache's values, used by the block's own rows too
     if st is not None:
         st.k[l, :P], st.v[l, :P] = K, Vv
     O = np.empty((P, m.Hq, m.hd), m.dt)

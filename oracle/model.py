@@ -17,7 +17,10 @@ Pins (tests/test_oracle_model.py): an independent float64 torch re-expression
 position 0 is the identity and preserves norms, a single key returns its
 value, equal scores average the values, zeroed output projections make a layer
 the identity, all-skipped gives head(norm(embedding))); hand-computed int8
-codes in tests/golden; incremental decode equals full recompute.
+codes in tests/golden; incremental decode equals full recompute.  The bf16
+KV cache option: ``round_bf16`` equals torch's float32 -> bfloat16
+conversion (ties included), and prefill plus every incremental step equal
+the torch re-expression with its keys and values converted the same way.
 """
 import numpy as np
 
@@ -30,10 +33,15 @@ class OracleModel:
     ``shape``: an object with the model-shape fields (n_layers, d_model, ...).
     """
 
-    def __init__(self, shape, weights, dtype=np.float64, cache_layers=None):
+    def __init__(self, shape, weights, dtype=np.float64, cache_layers=None, kv_dtype="f32"):
         self.shape = shape
         self.w = weights
         self.dt = np.dtype(dtype)
+        # "bf16": the KV cache holds keys and values rounded to bfloat16
+        # (``kv``); "f32": unrounded
+        if kv_dtype not in ("f32", "bf16"):
+            raise ValueError(kv_dtype)
+        self.kv_bf16 = kv_dtype == "bf16"
         self.L = shape.n_layers
         self.d = shape.d_model
         self.Hq = shape.n_heads
@@ -46,6 +54,10 @@ class OracleModel:
             cache_layers = shape.total_params() * self.dt.itemsize < 2e9
         self._cache = {} if cache_layers else None
         self._w8 = {} if cache_layers else None
+
+    def kv(self, x):
+        """The value the KV cache holds for key or value x."""
+        return round_bf16(x) if self.kv_bf16 else x
 
     def _get(self, name):
         if self._cache is not None and name in self._cache:
@@ -182,6 +194,15 @@ def w8a8_project(Q, S, x):
     acc = w8a8_accumulate(Q, q)
     c = (np.asarray(S, np.float32) * np.float32(sx)).astype(np.float32)
     return (acc.astype(np.float32) * c).astype(np.float32)
+
+
+def round_bf16(x):
+    """Nearest bfloat16 value (ties to even) of x taken as float32, in x's
+    dtype: bfloat16 keeps the top 16 bits of the float32 encoding."""
+    x = np.asarray(x)
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return r.view(np.float32).astype(x.dtype)
 
 
 def fake_quant(x, dt):

@@ -21,9 +21,10 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 # ---------------------------------------------------------------- torch re-expression
-def _torch_forward(shape, W, tokens):
+def _torch_forward(shape, W, tokens, kv_bf16=False):
     """Full causal forward of ``tokens`` in float64 torch; returns logits [P][V]
-    and residual states [L+1][P][d]."""
+    and residual states [L+1][P][d].  kv_bf16: keys (after RoPE) and values
+    pass through torch's float32 -> bfloat16 conversion first."""
     d64 = torch.float64
     tw = {k: torch.from_numpy(np.asarray(v, dtype=np.float64)) for k, v in W.items()}
     P = len(tokens)
@@ -48,6 +49,9 @@ def _torch_forward(shape, W, tokens):
         k = (x @ tw[p + "wk"].T).view(P, Hkv, hd)
         v = (x @ tw[p + "wv"].T).view(P, Hkv, hd)
         q, k = apply_rope(q), apply_rope(k)
+        if kv_bf16:
+            k = k.to(torch.float32).to(torch.bfloat16).to(d64)
+            v = v.to(torch.float32).to(torch.bfloat16).to(d64)
         rep = Hq // Hkv
         k = k.repeat_interleave(rep, dim=1)
         v = v.repeat_interleave(rep, dim=1)
@@ -83,6 +87,43 @@ def test_incremental_decode_matches_full_recompute(tiny_shape, tiny_weights_np, 
     for i in range(1, G):
         z, _ = oracle.forward_row(tiny_model, st, seq[P - 1 + i], P - 1 + i, "full")
         np.testing.assert_allclose(z, tz[P - 1 + i], rtol=0, atol=1e-9)
+
+
+def test_round_bf16_matches_torch_bfloat16():
+    """round_bf16 is torch's float32 -> bfloat16 conversion (round to
+    nearest, ties to even), also on exact ties and from float64 input."""
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(4000) * s for s in (1e-6, 1e-2, 1.0, 1e3)]).astype(np.float32)
+    hi = rng.integers(0, 0x7F7F, 2000, dtype=np.uint32) << 16       # finite magnitudes
+    ties = (hi | 0x8000).view(np.float32)                 # halfway between two bfloat16 values
+    ties = np.concatenate([ties, -ties])
+    for v in (x, ties):
+        ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
+        assert np.array_equal(oracle.round_bf16(v).view(np.uint32), ref.view(np.uint32))
+    x64 = rng.standard_normal(4000)
+    ref = torch.from_numpy(x64).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_bf16(x64), ref)
+
+
+def test_bf16_kv_cache_matches_torch_reexpression(tiny_shape, tiny_weights_np, tiny_prompt):
+    """With a bf16 KV cache, prefill and every incremental decode step equal
+    the torch re-expression whose keys and values go through torch's
+    bfloat16 conversion; the rounding does move the logits."""
+    model = oracle.OracleModel(tiny_shape, tiny_weights_np, kv_dtype="bf16")
+    G = 10
+    toks = oracle.ar_generate(model, tiny_prompt, G)
+    seq = list(tiny_prompt) + toks[:-1]
+    tz, ts = _torch_forward(tiny_shape, tiny_weights_np, seq, kv_bf16=True)
+    P = len(tiny_prompt)
+    st, z, states = oracle.prefill(model, tiny_prompt, 64)
+    np.testing.assert_allclose(z, tz[P - 1], rtol=0, atol=1e-9)
+    for l in range(tiny_shape.n_layers + 1):
+        np.testing.assert_allclose(states[l], ts[l][P - 1], rtol=0, atol=1e-9)
+    for i in range(1, G):
+        z, _ = oracle.forward_row(model, st, seq[P - 1 + i], P - 1 + i, "full")
+        np.testing.assert_allclose(z, tz[P - 1 + i], rtol=0, atol=1e-9)
+    tz32, _ = _torch_forward(tiny_shape, tiny_weights_np, seq)
+    assert np.max(np.abs(tz32 - tz)) > 1e-5
 
 
 def test_gqa_matches_torch_reexpression():
