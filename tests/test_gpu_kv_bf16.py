@@ -8,7 +8,8 @@ Checked against the oracle: prefill logits, greedy decode along the GPU's
 own tokens (the parity protocol's token rule), and teacher-forced verify
 rows.  Checked on the GPU alone: every verify row equals the greedy step at
 its position bit for bit, and speculative output equals greedy output for
-chain, DP and tree drafts."""
+chain, DP and tree drafts.  Batched sequences (the batched attention kernels
+on a bf16 cache) equal both the oracle's and the GPU's single-sequence runs."""
 import numpy as np
 import pytest
 
@@ -105,3 +106,26 @@ def test_speculative_equals_greedy(case, name):
     toks, st = eng.generate(prompt, G, POLICIES[name])
     assert toks == ar
     assert 0 <= st["accepted"] <= st["drafted"]
+
+
+def test_batched_sequences_with_bf16_cache(case):
+    """Three sequences decoded together with a bf16 cache (the batched
+    attention kernels on bf16 keys and values) equal the oracle's
+    single-sequence runs with the same cache, and the GPU's own single runs."""
+    from layer_skip_self_amd import Engine
+    shape = lss_synth.SHAPES[case["name"]]
+    w_gpu = [(n, t.to("cuda")) for n, t in lss_synth.make_weights(shape, device="cpu")]
+    rng = np.random.default_rng(17)
+    prompts = [rng.integers(0, shape.vocab, m).astype(np.int32) for m in (30, 17, 41)]
+    eng = Engine(shape, w_gpu, max_seq=120, max_rows=16, kv_dtype="bf16", max_seqs=3)
+    try:
+        for gp, op in (({"mode": "ar"}, oracle.Policy(K=0)),
+                       ({"mode": "static", "k_max": 4, "skip": (1,)}, oracle.Policy(K=4, skip=(1,)))):
+            toks, _ = eng.generate_batch(prompts, 24, gp)
+            ref = oracle.batch_generate(case["model"], prompts, 24, op)
+            for i, p in enumerate(prompts):
+                single, _ = case["eng"].generate(p, 24, gp)
+                assert toks[i] == single, (gp["mode"], i)
+                assert toks[i] == ref[i][0], (gp["mode"], i)
+    finally:
+        eng.close()
