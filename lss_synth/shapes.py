@@ -49,6 +49,12 @@ SHAPES = {
     # pieces, and some waves of a decode launch get no piece of K at all.
     "small_bf16": ModelShape("small_bf16", 3, 320, 5, 1, 64, 864, 1008, 1e4, "bf16",
                              weight_seed=11, prompt_seed=111),
+    # Medium float32 model for the float32 decode kernels at real depths: 2 L,
+    # d 1024, 8 q / 2 kv heads of 128 (GQA 4), SwiGLU 5632, vocab 4096.  Its
+    # FFN depth is 22 chunks of 1 KB of float32 weights, so the down
+    # projection's waves take 3 or 2 chunks each.
+    "medium_f32": ModelShape("medium_f32", 2, 1024, 8, 2, 128, 5632, 4096, 1e4, "f32",
+                             weight_seed=13, prompt_seed=113),
     # Llama-2-7B shape: 32 L, d 4096, 32 MHA heads, FFN 11008, vocab 32000.
     "llama2_7b": ModelShape("llama2_7b", 32, 4096, 32, 32, 128, 11008, 32000, 1e4, "bf16",
                             weight_seed=2, prompt_seed=102),
