@@ -2002,7 +2002,7 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
     }
     return LSS_OK;
   };
-  if (pol->mode != LSS_MODE_AR) {
+  if (pol->mode != LSS_MODE_AR && !stopped) {
     rc = select();
     if (rc) return rc;
   }
@@ -2168,7 +2168,7 @@ int lss_generate_batch(lss_engine* e, int32_t n, const int32_t* prompts, const i
     emitted[i] = 1;
     stopped[i] = is_stop(pol, t0);
     if (pol->mode == LSS_MODE_STATIC) std::copy(pol->static_mask, pol->static_mask + L, masks.begin() + (size_t)i * L);
-    if (pol->mode == LSS_MODE_DP && (rc = dp(i))) return fin(rc);
+    if (pol->mode == LSS_MODE_DP && !stopped[i] && (rc = dp(i))) return fin(rc);
   }
   std::vector<int32_t> act, dk, done(n), toks((size_t)n * LSS_WINDOW_MAX), na(n), acc((size_t)n * (LSS_WINDOW_MAX + 1));
   std::vector<uint8_t> dmask;

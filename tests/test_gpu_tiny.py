@@ -380,6 +380,8 @@ def test_stop_token_limits_and_first_token(setup):
     eng, prompt, ref = setup["eng"], setup["prompt"], setup["ref"]
     toks, stats = eng.generate(prompt, G, {"mode": "static", "k_max": 4, "skip": (1,), "stop": (ref[0],)})
     assert toks == ref[:1] and stats["emitted"] == 1 and stats["rounds"] == 0
+    toks, stats = eng.generate(prompt, G, {"mode": "dp", "k_max": 4, "n_skip": 2, "interval": 4, "stop": (ref[0],)})
+    assert toks == ref[:1] and stats["rounds"] == 0 and stats["dp_runs"] == 0      # no layer selection either
     with pytest.raises(LssError):
         eng.generate(prompt, G, {"mode": "ar", "stop": (setup["shape"].vocab,)})
     with pytest.raises(ValueError):
