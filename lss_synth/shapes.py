@@ -55,6 +55,11 @@ SHAPES = {
     # projection's waves take 3 or 2 chunks each.
     "medium_f32": ModelShape("medium_f32", 2, 1024, 8, 2, 128, 5632, 4096, 1e4, "f32",
                              weight_seed=13, prompt_seed=113),
+    # Wide float32 model, one layer: d 3072 (12 chunks of 1 KB: two chunk
+    # registers per wave) and FFN 14336 (56 chunks: eight, at most 2 rows per
+    # launch) for the remaining float32 GEMV variants.
+    "wide_f32": ModelShape("wide_f32", 1, 3072, 8, 2, 128, 14336, 4096, 1e4, "f32",
+                           weight_seed=17, prompt_seed=117),
     # Llama-2-7B shape: 32 L, d 4096, 32 MHA heads, FFN 11008, vocab 32000.
     "llama2_7b": ModelShape("llama2_7b", 32, 4096, 32, 32, 128, 11008, 32000, 1e4, "bf16",
                             weight_seed=2, prompt_seed=102),
