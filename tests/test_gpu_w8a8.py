@@ -34,7 +34,7 @@ def test_weight_quantizer_bitexact(dtype, rows, k):
     assert np.array_equal(s.cpu().numpy(), S)
 
 
-@pytest.mark.parametrize("n,k", [(64, 688), (6144, 4096), (4096, 14336), (256, 16)])
+@pytest.mark.parametrize("n,k", [(64, 688), (6144, 4096), (4096, 14336), (256, 16), (128, 28672)])
 def test_w8a8_gemv_bitexact(n, k):
     import torch
     from layer_skip_self_amd.engine import w8a8_gemv
@@ -55,7 +55,7 @@ def test_w8a8_gemv_bitexact(n, k):
     assert np.array_equal(got, ref), np.max(np.abs(got - ref))
 
 
-@pytest.mark.parametrize("n,k", [(64, 688), (6144, 4096), (4096, 14336), (256, 16)])
+@pytest.mark.parametrize("n,k", [(64, 688), (6144, 4096), (4096, 14336), (256, 16), (128, 8192), (64, 28672)])
 def test_w8a8_gemv_with_in_kernel_quantization_bitexact(n, k):
     """Every workgroup quantizes the float32 row itself (the draft's form):
     equal bit for bit to the oracle's w8a8_project (codes decided in float32
