@@ -394,3 +394,41 @@ def test_batch_of_four_equals_single_sequence_runs_8b(gpu8b):
         assert toks[i] == single, i
         assert stats[i] == st, i
         assert ar[i] == single, i
+
+
+def test_bf16_kv_cache_vs_oracle_8b(gpu8b, oracle8b):
+    """The bf16 KV cache at the 8B shape against the oracle with the same
+    cache (keys and values rounded to bfloat16): prefill logits and a
+    teacher-forced 4-row verify within the bf16 bound 2e-2.  (Against the
+    float32-cache oracle the same engine is 7.7e-2 away: that gap is the
+    cache's rounding.)  The oracle instance of this module is switched to
+    the bf16 cache for this test only, so that its float32 weights are not
+    held twice."""
+    import copy
+    from layer_skip_self_amd import Engine
+    model, prompt = oracle8b["model"], gpu8b["prompt"]
+    eng = Engine(SHAPE, gpu8b["w"], max_seq=MAX_SEQ, max_rows=64, kv_dtype="bf16")
+    model.kv_bf16 = True
+    try:
+        t0 = eng.prefill(prompt)
+        zg = eng.read_logits(1)[0].copy()
+        st, zo, _ = oracle.prefill(model, prompt, MAX_SEQ)
+        err0 = float(np.max(np.abs(zg - zo)))
+        toks, zs = [st.t0], []
+        so = copy.deepcopy(st)
+        for _ in range(4):
+            zz, _ = oracle.forward_row(model, so, toks[-1], so.p, "full")
+            so.p += 1
+            zs.append(zz)
+            toks.append(int(np.argmax(zz)))
+        eng.verify(drafts=toks[1:4])
+        zv = eng.read_logits(4)
+        eng.accept()
+        err1 = float(np.max(np.abs(zv - np.stack(zs))))
+    finally:
+        model.kv_bf16 = False
+        eng.close()
+    print(f"bf16 cache: prefill logits max-abs {err0:.3e}, 4-row verify {err1:.3e}; t0 {t0} vs {st.t0}")
+    assert err0 <= 2e-2 and err1 <= 2e-2
+    if oracle_gap(zo) >= 1e-2:
+        assert t0 == st.t0
