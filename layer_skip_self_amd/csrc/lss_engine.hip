@@ -2062,7 +2062,10 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
       if (n > 0)                                        // the branch followed: its first node was emitted
         for (int b = 0; b < B; ++b)
           if (toks[(size_t)b * D] == acc[0]) branch = b;
-      for (int i = 0; i <= n && emitted < n_gen && !stopped; ++i) stopped = is_stop(pol, out[emitted++] = acc[i]);
+      for (int i = 0; i <= n && emitted < n_gen && !stopped; ++i) {
+        out[emitted++] = acc[i];
+        stopped = is_stop(pol, acc[i]);
+      }
       st.rounds++;
       st.drafted += k;
       st.accepted += n;
@@ -2099,7 +2102,10 @@ int lss_generate(lss_engine* e, const int32_t* prompt, int32_t n_prompt, int32_t
     int n = 0, bonus = 0;
     rc = lss_accept_and_rollback(e, &n, &bonus, acc.data());
     if (rc) return rc;
-    for (int i = 0; i <= n && emitted < n_gen && !stopped; ++i) stopped = is_stop(pol, out[emitted++] = acc[i]);
+    for (int i = 0; i <= n && emitted < n_gen && !stopped; ++i) {
+      out[emitted++] = acc[i];
+      stopped = is_stop(pol, acc[i]);
+    }
     st.rounds++;
     st.drafted += k;
     st.accepted += n;
@@ -2196,8 +2202,11 @@ int lss_generate_batch(lss_engine* e, int32_t n, const int32_t* prompts, const i
     if (rc) return fin(rc);
     for (int a = 0; a < na_; ++a) {
       const int i = act[a];
-      for (int j = 0; j <= na[a] && emitted[i] < n_gen && !stopped[i]; ++j)
-        stopped[i] = is_stop(pol, out[(size_t)i * n_gen + emitted[i]++] = acc[(size_t)a * (LSS_WINDOW_MAX + 1) + j]);
+      for (int j = 0; j <= na[a] && emitted[i] < n_gen && !stopped[i]; ++j) {
+        const int32_t tk = acc[(size_t)a * (LSS_WINDOW_MAX + 1) + j];
+        out[(size_t)i * n_gen + emitted[i]++] = tk;
+        stopped[i] = is_stop(pol, tk);
+      }
       st[i].rounds++;
       st[i].drafted += done[a];
       st[i].accepted += na[a];
